@@ -1,0 +1,199 @@
+/*
+ * tok.h -- C ABI of the exact byte-level BPE tokenizer for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * One output contract for every call: the returned token IDs equal the full
+ * tokenization of the request text under one frozen configuration (TokTier,
+ * section 4 "Exactness contract" and Appendix A, Definition A.2; Delta
+ * Tokenizer, section 2 "Contract"; GraphTok, section 3 "Exactness requires the
+ * complete ordered token sequence").  A call that cannot honour the contract
+ * returns an error code and writes no partial answer the caller could mistake
+ * for a result: failures cost work, never exactness (TokTier, section 4).
+ *
+ * Configuration (fixed at tok_load):
+ *   - merges: n_merges ordered pairs (left, right) of token IDs, in rank order.
+ *     IDs 0..255 are the single bytes; merge r creates ID 256 + r.  Ranks are
+ *     keyed by the ordered ID pair (GraphTok, section 4: the lowest rank wins,
+ *     the leftmost pair on equal rank).
+ *   - pattern: the pre-tokenizer family, TOK_PAT_GPT2 or TOK_PAT_LLAMA3.
+ *     encode(x) = concatenation over the pre-tokenization pieces p of x, in
+ *     order, of bpe(bytes(p)) (TokTier, Appendix A, Definition A.2 and
+ *     Lemma A.3).
+ *
+ * Text is UTF-8.  Malformed input (overlong forms, surrogates, values above
+ * U+10FFFF, truncated or stray continuation bytes, a sequence cut by a document
+ * boundary) is rejected as a whole with TOK_E_UTF8 (GraphTok, section 6: byte
+ * input is validated before any tokenizer semantics apply).
+ *
+ * Threading: a context serves one caller at a time (GraphTok, section 5, one
+ * context per dispatcher).  Device-pointer calls enqueue their work on the
+ * given stream and return after that stream has completed it.
+ *
+ * Ownership: every pointer argument is owned by the caller and is not retained
+ * after the call returns; the context owns all of its device memory.
+ */
+#ifndef EXACT_BYTE_LEVEL_UTF8_TOK_H
+#define EXACT_BYTE_LEVEL_UTF8_TOK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tok_ctx tok_ctx;
+
+/* Status codes. */
+#define TOK_OK 0
+#define TOK_E_ARG 1        /* null pointer, non-monotone offsets, bad flag  */
+#define TOK_E_BADMERGES 2  /* operand >= 256 + rank, repeated pair, too many */
+#define TOK_E_PATTERN 3    /* pattern id not supported                      */
+#define TOK_E_UTF8 4       /* malformed UTF-8 anywhere in the input         */
+#define TOK_E_CAPACITY 5   /* output buffer too small; *n_out = required    */
+#define TOK_E_TOOLONG 6    /* input longer than TOK_MAX_BYTES               */
+#define TOK_E_DEVICE 7     /* a HIP runtime call failed                     */
+#define TOK_E_NOMEM 8      /* device or pinned host allocation failed       */
+#define TOK_E_SESSION 9    /* repair: stored IDs do not spell the old text  */
+
+/* Pre-tokenizer families. */
+#define TOK_PAT_GPT2 0   /* 's|'t|'re|'ve|'m|'ll|'d| ?L+| ?N+| ?[^\s L N]+|\s+(?!\S)|\s+ */
+#define TOK_PAT_LLAMA3 1 /* (?i:contractions)|[^\r\n L N]?L+|N{1,3}| ?[^\s L N]+[\r\n]*|\s*[\r\n]+|\s+(?!\S)|\s+ */
+
+/* Largest input of one call, in bytes (token counts and offsets are 32-bit
+ * on the device). */
+#define TOK_MAX_BYTES 0xFFFF0000ull
+/* Largest merge list: token IDs are 20-bit fields in the device tables. */
+#define TOK_MAX_MERGES 1040000ull
+
+/*
+ * tok_load -- validate a configuration and build its device tables.
+ *
+ * merges:   host array of 2 * n_merges uint32: (left, right) of merge r at
+ *           [2r, 2r+1].  Copied; the caller may free it on return.
+ * pattern:  TOK_PAT_GPT2 or TOK_PAT_LLAMA3.
+ * device:   HIP device ordinal the context runs on.
+ * out:      receives the context (NULL on error).
+ *
+ * Builds, on the device: the (left, right) -> rank open-addressing table, a
+ * direct byte-pair rank table, the token byte lengths, and a whole-piece
+ * table of vocabulary strings of 2..13 bytes whose own BPE is the single token
+ * (the "ignore_merges" shortcut of TokTier, section 4.3, applied only where it
+ * provably cannot change an ID: each string is checked by running the GPU
+ * merge kernels on it once at load).
+ *
+ * Errors: TOK_E_ARG (null out or merges with n_merges > 0), TOK_E_BADMERGES
+ * (left or right >= 256 + r, a repeated pair, n_merges > TOK_MAX_MERGES),
+ * TOK_E_PATTERN, TOK_E_DEVICE, TOK_E_NOMEM.
+ */
+int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, tok_ctx** out);
+
+/* Release the context and all its device and pinned memory.  NULL is a no-op. */
+void tok_free(tok_ctx* ctx);
+
+/* Static message for a status code. */
+const char* tok_strerror(int code);
+
+/*
+ * tok_encode -- exact encode of one request held in host memory.
+ *
+ * text, len: UTF-8 request (len may be 0; text may be NULL when len is 0).
+ * ids, cap:  host output buffer of cap int32.  cap >= len always suffices
+ *            (every token covers at least one byte).
+ * n_out:     receives the token count T (also on TOK_E_CAPACITY, where it is
+ *            the required cap; nothing is written to ids then).
+ *
+ * The text is staged through pinned memory to the context's stream; the
+ * pipeline runs on the device; the count and then the IDs come back.
+ * Errors: TOK_E_ARG, TOK_E_TOOLONG, TOK_E_UTF8 (*n_out = 0), TOK_E_CAPACITY,
+ * TOK_E_DEVICE, TOK_E_NOMEM.
+ */
+int tok_encode(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids, size_t cap,
+               size_t* n_out);
+
+/*
+ * tok_encode_dev -- as tok_encode with device-resident input and output: no
+ * host/device transfer of text or IDs (GraphTok, section 5, the device
+ * buffer handoff).  d_text: len bytes on the context's device; d_ids: cap
+ * int32 on the device; stream: hipStream_t to enqueue on (NULL = the
+ * context's own stream).  On TOK_E_CAPACITY the first cap IDs are written and
+ * *n_out is the full count; on TOK_E_UTF8 the content of d_ids is unspecified.
+ */
+int tok_encode_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, int32_t* d_ids, size_t cap,
+                   size_t* n_out, void* stream);
+
+/*
+ * tok_encode_batch -- encode n_docs independent documents in one pipeline
+ * pass (GraphTok, section 5 "Batch entry point"; TokTier, section 4.3,
+ * multi-document batches).  Document i is text[doc_off[i] .. doc_off[i+1]);
+ * documents are hard boundaries: no piece, code point or token spans two of
+ * them; an empty document yields no IDs.
+ *
+ * doc_off: host array of n_docs + 1 non-decreasing byte offsets with
+ *          doc_off[0] = 0 (the text length is doc_off[n_docs]).
+ * ids,cap: host output, concatenated IDs of all documents in order.
+ * out_off: host array of n_docs + 1: document i's IDs are
+ *          ids[out_off[i] .. out_off[i+1]).  out_off[n_docs] is the total.
+ * Errors: as tok_encode, plus TOK_E_ARG for offsets that decrease, do not
+ * start at 0, or n_docs == 0.  On TOK_E_CAPACITY out_off is filled and ids
+ * is untouched.
+ */
+int tok_encode_batch(tok_ctx* ctx, const uint8_t* text, const uint64_t* doc_off, size_t n_docs,
+                     int32_t* ids, size_t cap, uint64_t* out_off);
+
+/*
+ * tok_encode_batch_dev -- as tok_encode_batch with device-resident text,
+ * offsets (d_doc_off: n_docs + 1 uint64 on the device, validated on the
+ * device), IDs and output offsets (d_out_off: n_docs + 1 uint64).  n_out
+ * receives the total count.  stream as in tok_encode_dev.
+ */
+int tok_encode_batch_dev(tok_ctx* ctx, const uint8_t* d_text, const uint64_t* d_doc_off,
+                         size_t n_docs, int32_t* d_ids, size_t cap, uint64_t* d_out_off,
+                         size_t* n_out, void* stream);
+
+/*
+ * tok_pretokenize_dev -- the pre-tokenization stage alone, for split-level
+ * checks (TokTier, section 5.2, compares pieces before IDs).  Writes one
+ * uint16 per 16-byte chunk of d_text to d_flags (ceil(len / 16) words on the
+ * device): bit i of word c is set iff byte 16c + i starts a piece.  A
+ * document start always starts a piece.  d_doc_off / n_docs as in
+ * tok_encode_batch_dev, or NULL / 0 for one document.
+ */
+int tok_pretokenize_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len,
+                        const uint64_t* d_doc_off, size_t n_docs, uint16_t* d_flags, void* stream);
+
+/* Context facts. */
+typedef struct tok_info {
+  uint32_t pattern;
+  uint32_t n_merges;
+  uint32_t vocab_size;     /* 256 + n_merges                                 */
+  uint32_t max_token_len;  /* longest token, bytes                           */
+  uint32_t n_whole;        /* whole-piece table entries (self-encoding)      */
+  uint32_t n_not_self;     /* 2..13-byte vocab strings whose BPE differs     */
+  uint64_t config_hash;    /* FNV-1a over pattern and merges                 */
+} tok_info;
+
+int tok_get_info(const tok_ctx* ctx, tok_info* info);
+
+/*
+ * Token byte lengths, for host-side offset arithmetic: writes min(n,
+ * vocab_size) lengths to len_out (host).  Returns the vocabulary size.
+ */
+size_t tok_token_lengths(const tok_ctx* ctx, uint32_t* len_out, size_t n);
+
+/*
+ * Stage timing (GraphTok, section 7, per-stage profile).  With profiling on,
+ * every call records HIP events around each device stage on the stream it
+ * runs on; tok_stage_ms returns the last call's stage durations in ms:
+ * [0] counter reset, [1] pre-tokenization, [2] piece BPE, [3] long-piece BPE,
+ * [4] count scan + scatter, [5] document offsets.  Returns the number of
+ * stages written (at most n).
+ */
+int tok_set_profiling(tok_ctx* ctx, int on);
+int tok_stage_ms(const tok_ctx* ctx, float* ms, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_BYTE_LEVEL_UTF8_TOK_H */
