@@ -1,0 +1,205 @@
+"""Benchmark: exact encode of one 1,000,000-character request on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_1m|llama3_3m|batch64]
+
+One step = one tok_encode_dev call over the whole request (pre-tokenization,
+piece BPE, long-piece BPE, count scan + scatter), with the UTF-8 text already
+resident in HBM and the int32 IDs left in HBM.  W untimed steps, then exactly
+K timed steps between two device synchronizations.  Prints one JSON line:
+value = input MB/s (UTF-8 bytes / s / 1e6), ms_per_step = ms per request.
+
+Also reported, outside the headline value:
+  - roofline: the dominant kernel's algorithmic bytes per launch over its
+    average duration, timed with HIP events on the stream the kernels run on
+    during the timed steps, against the 8 TB/s HBM peak;
+  - complete_call: host bytes -> host int32 IDs through tok_encode (pinned
+    staging, both transfers), the PCIe-inclusive rate;
+  - cpu_baseline: the CPU oracle on the same request, single-threaded.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "ms per 1M-char request encode (input MB/s) + % HBM roofline, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (description, merges, pattern, generator seed, chars, docs)
+    "gpt2_1m": ("1M-char agent-transcript request, GPT-2-style pattern, 50K merges", "gpt2_50k", "gpt2", 2,
+                1_000_000, 1),
+    "llama3_3m": ("3M-char agent-transcript request, Llama-3-style pattern, 127,744 merges", "llama3_128k",
+                  "llama3", 3, 3_000_000, 1),
+    "batch64": ("64 requests x 500K chars, Llama-3-style pattern, 127,744 merges, one batch call",
+                "llama3_128k", "llama3", 40_000, 500_000, 64),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(stage: str, n_bytes: int, n_tokens: int) -> int:
+    """Bytes a stage must move through its interface buffers, once each."""
+    chunks = (n_bytes + 15) // 16
+    flags = 2 * chunks
+    if stage == "pretokenize":      # text in, piece-start flags out
+        return n_bytes + flags
+    if stage == "bpe":              # text and flags in, tokens and chunk counts out
+        return n_bytes + flags + 4 * n_tokens + 4 * chunks
+    if stage == "assemble":         # counts and staged tokens in, IDs and offsets out
+        return 4 * chunks * 2 + 8 * n_tokens
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2_1m", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the tokenizer runs on a single MI355X)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import exact_byte_level_utf8_amd as tk
+    from synth import textgen
+    from tests import vocab
+
+    desc, merges_name, pattern, seed, n_chars, n_docs = WORKLOADS[args.workload]
+    t0 = time.time()
+    if n_docs == 1:
+        text = textgen.mix_text(seed, n_chars).encode()
+        doc_off = None
+    else:
+        text, doc_off = textgen.pack_docs(textgen.batch_texts(seed, n_docs, n_chars))
+    n_bytes = len(text)
+    log(f"[bench] workload {args.workload}: {n_bytes} bytes generated in {time.time() - t0:.1f}s")
+
+    merges = vocab.merges(merges_name)
+    torch.cuda.set_device(0)
+    tok = tk.Tokenizer(merges, pattern, device=0)
+    stream = torch.cuda.current_stream()
+    d_text = torch.frombuffer(bytearray(text), dtype=torch.uint8).cuda()
+    d_ids = torch.empty(n_bytes, dtype=torch.int32, device="cuda")
+    if doc_off is not None:
+        d_off = torch.tensor(doc_off.astype(np.int64), device="cuda").view(torch.uint64)
+        d_out = torch.empty(n_docs + 1, dtype=torch.int64, device="cuda").view(torch.uint64)
+
+    def step() -> int:
+        if doc_off is None:
+            return tok.encode_dev(d_text, d_ids, stream=stream)
+        return tok.encode_batch_dev(d_text, d_off, d_ids, d_out, stream=stream)
+
+    for _ in range(args.warmup):
+        n_tokens = step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done: {n_tokens} tokens")
+
+    # timed region: K steps; HIP events inside the library time each stage on
+    # the same stream
+    tok.set_profiling(True)
+    stage_sum = np.zeros(len(tk.STAGES))
+    per_step = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        s0 = time.perf_counter()
+        n_tokens = step()
+        per_step.append(time.perf_counter() - s0)
+        stage_sum += np.asarray(tok.stage_ms())
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    tok.set_profiling(False)
+    ms_per_step = 1e3 * elapsed / args.steps
+    mbps = n_bytes * args.steps / elapsed / 1e6
+    stage_avg = stage_sum / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {mbps:.1f} MB/s")
+
+    stages = {name: round(float(v), 5) for name, v in zip(tk.STAGES, stage_avg)}
+    dom = max(("pretokenize", "bpe", "assemble"), key=lambda s: stages[s])
+    dom_ms = stages[dom]
+    alg = algorithmic_bytes(dom, n_bytes, n_tokens)
+    achieved = alg / (dom_ms * 1e-3) / 1e9 if dom_ms > 0 else 0.0
+
+    # complete call: host bytes in, host IDs out
+    cc = []
+    if doc_off is None:
+        for i in range(max(5, args.steps // 5)):
+            s0 = time.perf_counter()
+            ids_host = tok.encode(text)
+            cc.append(time.perf_counter() - s0)
+        assert len(ids_host) == n_tokens
+    complete = None
+    if cc:
+        med = statistics.median(cc)
+        complete = {"p50_ms": round(1e3 * med, 4), "mbps": round(n_bytes / med / 1e6, 1),
+                    "note": "tok_encode: pinned staging + H2D text + pipeline + D2H IDs"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        o = oracle.Oracle(merges, pattern)
+        if doc_off is None:
+            sample, what = text, f"the whole {n_bytes}-byte request, repeated"
+        else:
+            sample = text[int(doc_off[0]):int(doc_off[1])]
+            what = f"document 0 of the batch ({len(sample)} bytes), repeated"
+        reps, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and reps < 200:
+            s0 = time.perf_counter()
+            o.encode(sample)
+            t_cpu += time.perf_counter() - s0
+            reps += 1
+        cpu = {"value": round(len(sample) * reps / t_cpu / 1e6, 3), "unit": "MB/s", "cores": 1,
+               "kind": "oracle", "sample": f"{what} {reps} times, single thread ({t_cpu:.1f} s)"}
+        log(f"[bench] cpu oracle: {cpu['value']} MB/s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(mbps, 2),
+        "unit": "MB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "u8->int32",
+        "data": "synthetic (seeded generator, inputs resident in HBM)",
+        "config": {"workload": desc, "bytes": n_bytes, "chars": n_chars * n_docs, "docs": n_docs,
+                   "tokens": n_tokens, "merges": merges_name, "pattern": pattern, "seed": seed},
+        "latency_ms": {"p50": round(1e3 * statistics.median(per_step), 4),
+                       "p90": round(1e3 * float(np.percentile(per_step, 90)), 4),
+                       "p99": round(1e3 * float(np.percentile(per_step, 99)), 4)},
+        "stages_ms": stages,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6), "traffic": None,
+                     "algorithmic_bytes": alg, "avg_ms": dom_ms},
+        "complete_call": complete,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    tok.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,209 @@
+"""Python binding of the HIP tokenizer library (libtok.so, include/tok.h).
+
+Argument marshalling only: every step of the tokenizer runs in the library's
+HIP kernels.  Device-pointer calls take torch tensors (used only as device
+buffers) and enqueue on torch's current stream unless a stream is given.  The
+library must be built first (``python -m exact_byte_level_utf8_amd.build``);
+nothing here falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtok.so")
+
+PATTERNS = {"gpt2": 0, "llama3": 1}
+
+TOK_OK, TOK_E_ARG, TOK_E_BADMERGES, TOK_E_PATTERN, TOK_E_UTF8 = 0, 1, 2, 3, 4
+TOK_E_CAPACITY, TOK_E_TOOLONG, TOK_E_DEVICE, TOK_E_NOMEM, TOK_E_SESSION = 5, 6, 7, 8, 9
+
+# every function declared in include/tok.h
+EXPORTS = (
+    "tok_load", "tok_free", "tok_strerror", "tok_encode", "tok_encode_dev", "tok_encode_batch",
+    "tok_encode_batch_dev", "tok_pretokenize_dev", "tok_get_info", "tok_token_lengths",
+    "tok_set_profiling", "tok_stage_ms",
+)
+
+
+class TokError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {_strerror(code)} (code {code})")
+        self.code = code
+
+
+class TokInfo(ctypes.Structure):
+    _fields_ = [("pattern", ctypes.c_uint32), ("n_merges", ctypes.c_uint32),
+                ("vocab_size", ctypes.c_uint32), ("max_token_len", ctypes.c_uint32),
+                ("n_whole", ctypes.c_uint32), ("n_not_self", ctypes.c_uint32),
+                ("config_hash", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built: run python -m exact_byte_level_utf8_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        szp = ctypes.POINTER(ctypes.c_size_t)
+        L.tok_load.argtypes = [vp, sz, i32, i32, ctypes.POINTER(vp)]
+        L.tok_free.argtypes = [vp]
+        L.tok_free.restype = None
+        L.tok_strerror.argtypes = [i32]
+        L.tok_strerror.restype = ctypes.c_char_p
+        L.tok_encode.argtypes = [vp, vp, sz, vp, sz, szp]
+        L.tok_encode_dev.argtypes = [vp, vp, sz, vp, sz, szp, vp]
+        L.tok_encode_batch.argtypes = [vp, vp, vp, sz, vp, sz, vp]
+        L.tok_encode_batch_dev.argtypes = [vp, vp, sz, vp, sz, vp, sz, vp, szp, vp]
+        L.tok_pretokenize_dev.argtypes = [vp, vp, sz, vp, sz, vp, vp]
+        L.tok_get_info.argtypes = [vp, ctypes.POINTER(TokInfo)]
+        L.tok_token_lengths.argtypes = [vp, vp, sz]
+        L.tok_token_lengths.restype = sz
+        L.tok_set_profiling.argtypes = [vp, i32]
+        L.tok_stage_ms.argtypes = [vp, vp, i32]
+        for name in ("tok_load", "tok_encode", "tok_encode_dev", "tok_encode_batch",
+                     "tok_encode_batch_dev", "tok_pretokenize_dev", "tok_get_info",
+                     "tok_set_profiling", "tok_stage_ms"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _strerror(code: int) -> str:
+    try:
+        return lib().tok_strerror(code).decode()
+    except ImportError:
+        return "library not loaded"
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != TOK_OK:
+        raise TokError(rc, what)
+
+
+def _dev_ptr(t, dtype_name: str, what: str) -> int:
+    """Device pointer of a contiguous CUDA/HIP torch tensor of the given dtype."""
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if str(t.dtype) != f"torch.{dtype_name}":
+        raise ValueError(f"{what} must be {dtype_name}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+class Tokenizer:
+    """One loaded configuration (merge list + pre-tokenizer pattern) on one GPU."""
+
+    def __init__(self, merges, pattern: str | int, device: int = 0):
+        m = np.ascontiguousarray(np.asarray(merges, dtype=np.uint32).reshape(-1, 2))
+        pat = PATTERNS[pattern] if isinstance(pattern, str) else int(pattern)
+        h = ctypes.c_void_p()
+        _check(lib().tok_load(m.ctypes.data if m.size else None, m.shape[0], pat, device, ctypes.byref(h)),
+               "tok_load")
+        self._h = h
+        self.device = device
+        self.pattern = pat
+        self.n_merges = m.shape[0]
+
+    def close(self) -> None:
+        h = getattr(self, "_h", None)
+        if h:
+            lib().tok_free(h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ----------------------------------------------------------- host memory
+    def encode(self, text) -> np.ndarray:
+        b = text.encode("utf-8") if isinstance(text, str) else bytes(text)
+        ids = np.empty(max(len(b), 1), dtype=np.int32)
+        n = ctypes.c_size_t(0)
+        _check(lib().tok_encode(self._h, b, len(b), ids.ctypes.data, ids.size, ctypes.byref(n)), "tok_encode")
+        return ids[: n.value].copy()
+
+    def encode_batch(self, data: bytes, doc_off) -> tuple[np.ndarray, np.ndarray]:
+        off = np.ascontiguousarray(np.asarray(doc_off, dtype=np.uint64))
+        n_docs = off.size - 1
+        ids = np.empty(max(len(data), 1), dtype=np.int32)
+        out_off = np.zeros(n_docs + 1, dtype=np.uint64)
+        _check(lib().tok_encode_batch(self._h, data, off.ctypes.data, n_docs, ids.ctypes.data, ids.size,
+                                      out_off.ctypes.data), "tok_encode_batch")
+        return ids[: int(out_off[-1])].copy(), out_off
+
+    # --------------------------------------------------------- device memory
+    def encode_dev(self, d_text, d_ids, length: int | None = None, stream=None) -> int:
+        """Encode d_text[:length] (uint8 device tensor) into d_ids (int32); returns the count."""
+        n_bytes = d_text.numel() if length is None else int(length)
+        n = ctypes.c_size_t(0)
+        _check(lib().tok_encode_dev(self._h, _dev_ptr(d_text, "uint8", "text"), n_bytes,
+                                    _dev_ptr(d_ids, "int32", "ids"), d_ids.numel(), ctypes.byref(n),
+                                    _stream_handle(stream)), "tok_encode_dev")
+        return n.value
+
+    def encode_batch_dev(self, d_text, d_doc_off, d_ids, d_out_off, stream=None) -> int:
+        n = ctypes.c_size_t(0)
+        _check(lib().tok_encode_batch_dev(self._h, _dev_ptr(d_text, "uint8", "text"), d_text.numel(),
+                                          _dev_ptr(d_doc_off, "uint64", "doc_off"), d_doc_off.numel() - 1,
+                                          _dev_ptr(d_ids, "int32", "ids"), d_ids.numel(),
+                                          _dev_ptr(d_out_off, "uint64", "out_off"), ctypes.byref(n),
+                                          _stream_handle(stream)), "tok_encode_batch_dev")
+        return n.value
+
+    def pretokenize_dev(self, d_text, d_flags, d_doc_off=None, stream=None) -> None:
+        """Piece-start flag words (uint16 per 16 bytes) of d_text into d_flags."""
+        doc = _dev_ptr(d_doc_off, "uint64", "doc_off") if d_doc_off is not None else None
+        n_docs = d_doc_off.numel() - 1 if d_doc_off is not None else 0
+        _check(lib().tok_pretokenize_dev(self._h, _dev_ptr(d_text, "uint8", "text"), d_text.numel(), doc,
+                                         n_docs, _dev_ptr(d_flags, "int16", "flags"), _stream_handle(stream)),
+               "tok_pretokenize_dev")
+
+    # ---------------------------------------------------------------- facts
+    def info(self) -> dict:
+        i = TokInfo()
+        _check(lib().tok_get_info(self._h, ctypes.byref(i)), "tok_get_info")
+        return {f: getattr(i, f) for f, _ in TokInfo._fields_}
+
+    def token_lengths(self) -> np.ndarray:
+        v = lib().tok_token_lengths(self._h, None, 0)
+        out = np.zeros(v, dtype=np.uint32)
+        lib().tok_token_lengths(self._h, out.ctypes.data, v)
+        return out
+
+    def set_profiling(self, on: bool) -> None:
+        _check(lib().tok_set_profiling(self._h, int(bool(on))), "tok_set_profiling")
+
+    def stage_ms(self) -> list[float]:
+        out = (ctypes.c_float * 6)()
+        k = lib().tok_stage_ms(self._h, out, 6)
+        return list(out[:k])
+
+
+STAGES = ("reset", "pretokenize", "bpe", "bpe_long", "assemble", "doc_offsets")
+
+
+def flags_to_starts(flags: np.ndarray, n: int) -> np.ndarray:
+    """Byte offsets of the set bits of piece-start flag words (uint16 per 16 bytes)."""
+    w = np.asarray(flags, dtype=np.uint16)
+    bits = np.unpackbits(w.view(np.uint8), bitorder="little")
+    return np.flatnonzero(bits[:n]).astype(np.uint64)

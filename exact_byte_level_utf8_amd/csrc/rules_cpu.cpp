@@ -102,3 +102,8 @@ extern "C" int rules_cpu_pieces(const uint8_t* s, size_t n, const uint64_t* doc_
   *n_out = cnt;
   return 0;
 }
+
+#include "bpe_util.h"
+
+// The round selection of the long-piece merge kernel, exposed for tests.
+extern "C" uint64_t rules_cpu_select(uint64_t m, uint32_t carry) { return tok::select_leftmost(m, carry); }

@@ -10,6 +10,7 @@
 //   chunk_excl uint32[C]       exclusive prefix of chunk_cnt (output offsets)
 //   longs      uint4[C]        pieces longer than kShortMax bytes
 //   ws_sym/rk  uint32[N + 64]  merge workspace of long pieces, indexed by byte
+//   ws_sel     uint64[N + 64]  round selections of long pieces, indexed by byte
 //   scan_state uint64[G]       decoupled look-back state of the count scan
 //   ctr        Counters        status and device-side counts
 #pragma once
@@ -61,6 +62,7 @@ struct Bufs {
   uint4* longs;
   uint32_t* ws_sym;
   uint32_t* ws_rk;
+  uint64_t* ws_sel;
   unsigned long long* scan_state;
   Counters* ctr;
 };
@@ -86,7 +88,8 @@ __host__ __device__ inline uint32_t word_hash(uint64_t a, uint64_t b) {
 }
 
 // Kernel launchers (defined in the .hip files).
-void launch_reset(Bufs b, uint32_t n_tiles, hipStream_t s);
+void launch_reset(Bufs b, uint32_t n_tiles, const uint64_t* doc_off, uint32_t n_docs, uint64_t n,
+                  hipStream_t s);
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
                    int pattern, Bufs b, hipStream_t s);
 void launch_bpe(const uint8_t* text, uint64_t n, Tables t, Bufs b, hipStream_t s);

@@ -142,12 +142,14 @@ int tok_encode_batch(tok_ctx* ctx, const uint8_t* text, const uint64_t* doc_off,
                      int32_t* ids, size_t cap, uint64_t* out_off);
 
 /*
- * tok_encode_batch_dev -- as tok_encode_batch with device-resident text,
- * offsets (d_doc_off: n_docs + 1 uint64 on the device, validated on the
- * device), IDs and output offsets (d_out_off: n_docs + 1 uint64).  n_out
- * receives the total count.  stream as in tok_encode_dev.
+ * tok_encode_batch_dev -- as tok_encode_batch with device-resident text
+ * (d_text, len bytes), offsets (d_doc_off: n_docs + 1 uint64 on the device;
+ * the device checks d_doc_off[0] == 0, d_doc_off[n_docs] == len and that they
+ * never decrease, else TOK_E_ARG), IDs and output offsets (d_out_off: n_docs
+ * + 1 uint64 on the device).  n_out receives the total count.  stream as in
+ * tok_encode_dev.
  */
-int tok_encode_batch_dev(tok_ctx* ctx, const uint8_t* d_text, const uint64_t* d_doc_off,
+int tok_encode_batch_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const uint64_t* d_doc_off,
                          size_t n_docs, int32_t* d_ids, size_t cap, uint64_t* d_out_off,
                          size_t* n_out, void* stream);
 

@@ -1,0 +1,66 @@
+"""The C-ABI library builds, loads, exports every symbol include/tok.h
+declares, and validates configurations on the host (no GPU needed: every
+case here fails before any device work)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import exact_byte_level_utf8_amd as tk
+from tests import libs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "tok.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tok_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_binding_exports():
+    assert header_functions() == sorted(tk.EXPORTS)
+
+
+def test_library_exports_every_symbol():
+    libs.ensure_built()
+    out = subprocess.check_output(["nm", "-D", "--defined-only", tk.LIB_PATH], text=True)
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [f for f in header_functions() if f not in exported]
+    assert not missing, missing
+    L = tk.lib()
+    for f in header_functions():
+        assert getattr(L, f) is not None
+
+
+def _load(merges, pattern=0):
+    m = np.ascontiguousarray(np.asarray(merges, dtype=np.uint32).reshape(-1, 2))
+    h = ctypes.c_void_p()
+    rc = tk.lib().tok_load(m.ctypes.data if m.size else None, m.shape[0], pattern, 0, ctypes.byref(h))
+    return rc, h
+
+
+def test_load_rejects_bad_merges_and_pattern():
+    libs.ensure_built()
+    # operand not yet defined: merge 0 may only use bytes
+    assert _load([[256, 1]])[0] == tk.TOK_E_BADMERGES
+    assert _load([[97, 98], [97, 258]])[0] == tk.TOK_E_BADMERGES
+    # repeated pair
+    assert _load([[97, 98], [97, 98]])[0] == tk.TOK_E_BADMERGES
+    assert _load([[97, 98]], pattern=7)[0] == tk.TOK_E_PATTERN
+    h = ctypes.c_void_p()
+    assert tk.lib().tok_load(None, 3, 0, 0, ctypes.byref(h)) == tk.TOK_E_ARG
+    assert tk.lib().tok_load(None, 0, 0, 0, None) == tk.TOK_E_ARG
+
+
+def test_null_arguments():
+    libs.ensure_built()
+    L = tk.lib()
+    n = ctypes.c_size_t(5)
+    assert L.tok_encode(None, None, 0, None, 0, ctypes.byref(n)) == tk.TOK_E_ARG
+    assert L.tok_encode_batch(None, None, None, 0, None, 0, None) == tk.TOK_E_ARG
+    assert L.tok_strerror(tk.TOK_E_UTF8) == b"malformed UTF-8 input"
+    L.tok_free(None)

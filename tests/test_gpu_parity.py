@@ -1,0 +1,319 @@
+"""GPU parity: the HIP pipeline, called through the C ABI, against the CPU
+oracle, element by element.  Token IDs and piece offsets are integers, so the
+bar is bit-exact equality everywhere.
+
+Covers the five workload shapes (tiny ASCII, 1M-char request, 3M-char
+Llama-3-style request, a 64-document batch, and the seams that append repair
+creates), split-level parity of the pre-tokenizer alone (TokTier, section 5.2
+compares pieces before IDs), ragged sizes around the 16-byte chunk and 4 KiB
+tile, pieces long enough for the long-piece kernel (GraphTok, section 6.2:
+long pre-tokens, 10,000-character runs of one character), malformed UTF-8,
+capacity overflow, documents as hard boundaries, and stale state across calls
+of different sizes on one context (GraphTok, section 6.2: stale state across
+replays).
+"""
+import ctypes
+import random
+
+import numpy as np
+import pytest
+
+import exact_byte_level_utf8_amd as tk
+import oracle
+from synth import textgen
+from tests import libs, vocab
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+ALPHA = ["a", "b", "s", "t", "r", "e", "l", "d", "S", "ſ", "'", " ", "\n", "\r", "\t", "1", "2",
+         "!", ".", " ", "é", "中", "́", "\U0001F600", "\u0085"]
+
+
+def _pair(name):
+    merges_name, pattern = libs.CONFIGS[name]
+    m = vocab.merges(merges_name)
+    return tk.Tokenizer(m, pattern), oracle.Oracle(m, pattern), vocab.token_bytes(m)
+
+
+@pytest.fixture(scope="module")
+def cfg():
+    libs.ensure_built()
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return {name: _pair(name) for name in libs.CONFIGS}
+
+
+def dev_bytes(b: bytes):
+    return torch.frombuffer(bytearray(b), dtype=torch.uint8).cuda() if b else torch.empty(0, dtype=torch.uint8,
+                                                                                         device="cuda")
+
+
+def gpu_pieces(t: tk.Tokenizer, b: bytes, doc_off=None):
+    d = dev_bytes(b)
+    flags = torch.zeros((len(b) + 15) // 16 + 8, dtype=torch.int16, device="cuda")
+    doc = None if doc_off is None else torch.tensor(np.asarray(doc_off, dtype=np.int64), device="cuda").view(
+        torch.uint64)
+    t.pretokenize_dev(d, flags, doc)
+    torch.cuda.synchronize()
+    return tk.flags_to_starts(flags.cpu().numpy().view(np.uint16), len(b)).tolist()
+
+
+def gpu_encode_dev(t: tk.Tokenizer, b: bytes):
+    d = dev_bytes(b)
+    ids = torch.empty(max(len(b), 1), dtype=torch.int32, device="cuda")
+    n = t.encode_dev(d, ids)
+    torch.cuda.synchronize()
+    return ids[:n].cpu().numpy()
+
+
+def adversarial_texts():
+    rng = random.Random(2024)
+    rand = "".join("".join(rng.choice(ALPHA) for _ in range(rng.randint(1, 30))) + rng.choice(ALPHA)
+                   for _ in range(8000))
+    return [
+        rand,
+        "x" + "1" * 10001 + "y" + "22" * 3000,        # digit runs across tiles
+        "a" + " " * 9000 + "b" + " " * 5000,          # whitespace run across tiles, trailing run
+        "q\n" + " " * 6000 + "\n  z" + "\n" * 4097,   # CR/LF far apart inside one run
+        "!" + "\r\n" * 5000 + "  w\t\t x",            # CR/LF block after O spanning tiles
+        "it's " * 900 + "IT'S 'LL 'Re 'ſ 'x",        # contractions
+        "  \u0085 z" * 1500,                     # non-ASCII whitespace
+        "中文字" * 3000 + "😀" * 1200,               # multibyte letters and other
+    ]
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_split_parity(cfg, name):
+    t, o, _ = cfg[name]
+    for s in adversarial_texts() + [textgen.mix_text(91, 300_000)]:
+        b = s.encode()
+        got, want = gpu_pieces(t, b), o.pieces(b)
+        if got != want:
+            i = next(k for k in range(min(len(got), len(want))) if got[k] != want[k])
+            pytest.fail(f"{name}: first split difference at piece {i}: gpu {got[i]} oracle {want[i]}, "
+                        f"context {b[max(0, want[i] - 20):want[i] + 20]!r}")
+
+
+def test_load_info(cfg):
+    for name, (t, _, tokb) in cfg.items():
+        info = t.info()
+        assert info["vocab_size"] == len(tokb)
+        assert info["max_token_len"] == max(len(x) for x in tokb)
+        # every trained vocabulary string encodes to its own ID (checked by the
+        # oracle tests), so the load-time check must admit all 2..13-byte ones
+        assert info["n_not_self"] == 0, name
+        assert info["n_whole"] == sum(1 for x in tokb[256:] if 2 <= len(x) <= 13)
+        assert np.array_equal(t.token_lengths(), [len(x) for x in tokb])
+
+
+def _check(name, got, want, b, tokb):
+    if not np.array_equal(got, want):
+        n = min(len(got), len(want))
+        i = next((k for k in range(n) if got[k] != want[k]), n)
+        pytest.fail(f"{name}: {len(got)} vs {len(want)} tokens, first difference at {i}: "
+                    f"gpu {got[i:i + 5].tolist()} oracle {want[i:i + 5].tolist()}")
+
+
+@pytest.mark.parametrize("name,gen,seed,n_chars", [
+    ("tiny", "tiny", 1, 10_000),
+    ("gpt2", "mix", 2, 1_000_000),
+    ("llama3", "mix", 3, 3_000_000),
+])
+def test_workload_parity(cfg, name, gen, seed, n_chars):
+    t, o, tokb = cfg[name]
+    s = textgen.tiny_text(seed, n_chars) if gen == "tiny" else textgen.mix_text(seed, n_chars)
+    b = s.encode()
+    want = o.encode(b)
+    _check(name, t.encode(b), want, b, tokb)
+    _check(name, gpu_encode_dev(t, b), want, b, tokb)
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_adversarial_parity(cfg, name):
+    t, o, tokb = cfg[name]
+    for s in adversarial_texts():
+        b = s.encode()
+        _check(name, t.encode(b), o.encode(b), b, tokb)
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_ragged_sizes(cfg, name):
+    t, o, tokb = cfg[name]
+    base = textgen.mix_text(5, 40_000).encode()
+    for n in [1, 2, 3, 15, 16, 17, 31, 33, 63, 64, 65, 4095, 4096, 4097, 4160, 8191, 8192, 12289, 40_000]:
+        b = base[:n]
+        while b:
+            try:
+                b.decode()
+                break
+            except UnicodeDecodeError:
+                b = b[:-1]
+        _check(f"{name}[{n}]", t.encode(b), o.encode(b), b, tokb)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2", "llama3"])
+def test_long_pieces(cfg, name):
+    t, o, tokb = cfg[name]
+    rng = random.Random(7)
+    cases = []
+    for L in [33, 63, 64, 65, 100, 128, 129, 511, 512, 513, 4097, 10_000]:
+        cases += ["a" * L, " " * L + "x", "=" * L, "é" * L, "\n" * L + "x", "中" * L,
+                  "".join(rng.choice("abcdefghij") for _ in range(L)),
+                  "".join(rng.choice("aab") for _ in range(L)), "7" * L, "x" + "1" * L]
+    cases.append(" " + "ab" * 20000)
+    text = "|".join(cases)
+    b = text.encode()
+    _check(name, t.encode(b), o.encode(b), b, tokb)
+    for s in cases[::7]:
+        bb = s.encode()
+        _check(name, t.encode(bb), o.encode(bb), bb, tokb)
+
+
+def test_empty_and_tiny_inputs(cfg):
+    t, o, _ = cfg["gpt2"]
+    assert len(t.encode(b"")) == 0
+    for s in ["a", " ", "\n", "'", "'s", "é", "😀", "12", "a b", "  "]:
+        assert np.array_equal(t.encode(s.encode()), o.encode(s.encode())), s
+
+
+INVALID = [b"\xff", b"a\x80b", b"\xc3", b"ab\xc3", b"\xe0\x80\x80", b"\xed\xa0\x80", b"\xf4\x90\x80\x80",
+           b"\xc0\xaf", b"\xc1\xbf", b"\xf5\x80\x80\x80", b"\xe2\x82", b"\xe2\x28\xa1", b"\xf0\x9f\x98",
+           b"\x80", b"\xbf\xbf"]
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_invalid_utf8_rejected(cfg, name):
+    t, o, _ = cfg[name]
+    good = textgen.mix_text(8, 20_000).encode()
+    for bad in INVALID:
+        for b in (bad, good[:5000] + bad + good[5000:], good + bad):
+            with pytest.raises(UnicodeDecodeError):
+                o.encode(b)
+            with pytest.raises(tk.TokError) as e:
+                t.encode(b)
+            assert e.value.code == tk.TOK_E_UTF8, (bad, len(b))
+
+
+def test_capacity_overflow(cfg):
+    t, o, _ = cfg["gpt2"]
+    b = textgen.mix_text(9, 5000).encode()
+    want = o.encode(b)
+    d = dev_bytes(b)
+    ids = torch.full((10,), -1, dtype=torch.int32, device="cuda")
+    n = ctypes.c_size_t(0)
+    rc = tk.lib().tok_encode_dev(t._h, d.data_ptr(), len(b), ids.data_ptr(), 10, ctypes.byref(n),
+                                 torch.cuda.current_stream().cuda_stream)
+    assert rc == tk.TOK_E_CAPACITY and n.value == len(want)
+    assert np.array_equal(ids.cpu().numpy(), want[:10])
+    host = np.full(5, -1, dtype=np.int32)
+    rc = tk.lib().tok_encode(t._h, b, len(b), host.ctypes.data, 5, ctypes.byref(n))
+    assert rc == tk.TOK_E_CAPACITY and n.value == len(want)
+    assert (host == -1).all()
+
+
+def batch_docs():
+    docs = ["", "abc 123", "12", "345", "it'", "s fine", "tail   ", "\n  x", "", "中文", "😀😀", "",
+            "x" + "9" * 5000, "  \n", "\n\n", "'S", "'s", " ", "a" * 300]
+    docs += [textgen.mix_text(400 + i, 9000 + 1371 * i) for i in range(6)]
+    docs += [""]
+    return docs
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_batch_parity(cfg, name):
+    t, o, tokb = cfg[name]
+    data, off = textgen.pack_docs(batch_docs())
+    want_ids, want_off = o.encode_batch(data, off)
+    ids, out_off = t.encode_batch(data, off)
+    assert np.array_equal(out_off, want_off)
+    _check(name, ids, want_ids, data, tokb)
+    # split level with document boundaries
+    want_p = []
+    for i in range(len(off) - 1):
+        s, e = int(off[i]), int(off[i + 1])
+        want_p += [s + p for p in o.pieces(data[s:e])]
+    assert gpu_pieces(t, data, off) == want_p
+    # device-resident batch
+    d = dev_bytes(data)
+    d_off = torch.tensor(off.astype(np.int64), device="cuda").view(torch.uint64)
+    d_ids = torch.empty(len(data), dtype=torch.int32, device="cuda")
+    d_out = torch.empty(len(off), dtype=torch.int64, device="cuda").view(torch.uint64)
+    n = t.encode_batch_dev(d, d_off, d_ids, d_out)
+    torch.cuda.synchronize()
+    assert n == len(want_ids)
+    assert np.array_equal(d_ids[:n].cpu().numpy(), want_ids)
+    assert np.array_equal(d_out.view(torch.int64).cpu().numpy().astype(np.uint64), want_off)
+
+
+def test_batch_rejects_bad_offsets(cfg):
+    t, _, _ = cfg["gpt2"]
+    data = b"hello world"
+    for off in ([0, 5, 3, 11], [1, 11], [0, 5, 12]):
+        arr = np.asarray(off, dtype=np.uint64)
+        if off[-1] != len(data):
+            # the host entry takes the length from the last offset; the device
+            # entry checks it against the text it is given
+            d = dev_bytes(data)
+            d_off = torch.tensor(arr.astype(np.int64), device="cuda").view(torch.uint64)
+            d_ids = torch.empty(32, dtype=torch.int32, device="cuda")
+            d_out = torch.empty(len(off), dtype=torch.int64, device="cuda").view(torch.uint64)
+            with pytest.raises(tk.TokError) as e:
+                t.encode_batch_dev(d, d_off, d_ids, d_out)
+            assert e.value.code == tk.TOK_E_ARG
+        else:
+            with pytest.raises(tk.TokError) as e:
+                t.encode_batch(data, arr)
+            assert e.value.code == tk.TOK_E_ARG
+    with pytest.raises(tk.TokError):
+        t.encode_batch(data, np.asarray([1, 11], dtype=np.uint64))
+
+
+def test_batch_workload_sampled(cfg):
+    """64 documents of 500,000 characters in one call (the batch workload):
+    every document's tokens spell its bytes, and sampled documents equal the
+    oracle exactly."""
+    t, o, tokb = cfg["llama3"]
+    texts = textgen.batch_texts(40_000, 64, 500_000)
+    data, off = textgen.pack_docs(texts)
+    ids, out_off = t.encode_batch(data, off)
+    assert out_off[0] == 0 and np.all(np.diff(out_off.astype(np.int64)) > 0)
+    lens = np.asarray([len(x) for x in tokb], dtype=np.int64)
+    doc_bytes = np.add.reduceat(lens[ids], out_off[:-1].astype(np.int64))
+    assert np.array_equal(doc_bytes, np.diff(off.astype(np.int64)))
+    for i in (0, 17, 63):
+        s, e = int(off[i]), int(off[i + 1])
+        _check(f"doc {i}", ids[int(out_off[i]):int(out_off[i + 1])], o.encode(data[s:e]), data[s:e], tokb)
+
+
+def test_repair_seams(cfg):
+    """Seam shapes that append repair meets (a word cut mid-run, newline plus
+    spaces on both sides of the seam, a multibyte character's bytes at the
+    seam): the encode of the concatenation equals the oracle."""
+    t, o, tokb = cfg["gpt2"]
+    for seed in range(6):
+        old, suf = textgen.repair_case(100 + seed, 200 + seed, old_chars=20_000)
+        b = (old + suf).encode()
+        _check(f"seam {seed}", t.encode(b), o.encode(b), b, tokb)
+    for s in ["watch the staging pipe" + "line closely.", "x\n  " + "\n   y", "命" * 3 + "令"]:
+        b = s.encode()
+        _check(s, t.encode(b), o.encode(b), b, tokb)
+
+
+def test_stale_state_across_sizes(cfg):
+    t, o, tokb = cfg["llama3"]
+    small = "x12345 it's\n\n  fine".encode()
+    big = textgen.mix_text(12, 3_000_000).encode()
+    want_small, want_big = o.encode(small), o.encode(big)
+    for b, w in ((small, want_small), (big, want_big), (small, want_small), (big[:777], o.encode(big[:777])),
+                 (big, want_big)):
+        _check("stale", t.encode(b), w, b, tokb)
+        _check("stale-dev", gpu_encode_dev(t, b), w, b, tokb)
+
+
+def test_deterministic(cfg):
+    t, _, _ = cfg["gpt2"]
+    b = textgen.mix_text(13, 200_000).encode()
+    a = t.encode(b)
+    for _ in range(3):
+        assert np.array_equal(t.encode(b), a)

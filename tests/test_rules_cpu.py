@@ -1,0 +1,119 @@
+"""The piece-start rules of the pre-tokenization kernel (pretok_rules.h),
+built for the CPU, against the oracle's direct leftmost-first matcher; and the
+closed-form round selection of the long-piece merge kernel against a
+sequential definition.
+
+The CPU build runs the very rule functions and scan elements the kernel uses,
+sequentially over whole texts, so a rule mistake shows up here without a GPU;
+the kernel's scans and tile carries are covered by the GPU parity tests."""
+import ctypes
+import itertools
+import random
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_byte_level_utf8_amd import build as tkbuild
+from synth import textgen
+from tests import libs
+
+ALPHA = ["a", "b", "s", "t", "r", "e", "l", "d", "S", "ſ", "'", " ", "\n", "\r", "\t", "1", "2",
+         "!", ".", " ", "é", "中", "́", "\U0001F600", "\u0085"]
+
+
+@pytest.fixture(scope="module")
+def rules():
+    libs.ensure_built()
+    L = ctypes.CDLL(tkbuild.RULES_LIB)
+    L.rules_cpu_pieces.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.POINTER(ctypes.c_size_t)]
+    L.rules_cpu_select.restype = ctypes.c_uint64
+    L.rules_cpu_select.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
+    L.rules_cpu_class.argtypes = [ctypes.c_uint32]
+
+    def pieces(b: bytes, pat: int, doc_off=None):
+        out = np.zeros(max(len(b), 1), dtype=np.uint64)
+        n = ctypes.c_size_t()
+        off = None if doc_off is None else np.ascontiguousarray(doc_off, dtype=np.uint64)
+        rc = L.rules_cpu_pieces(b, len(b), None if off is None else off.ctypes.data,
+                                0 if off is None else off.size - 1, pat, out.ctypes.data, out.size,
+                                ctypes.byref(n))
+        assert rc == 0
+        return out[: n.value].tolist()
+
+    L.pieces = pieces
+    return L
+
+
+@pytest.fixture(scope="module")
+def orcs():
+    m = np.zeros((0, 2), dtype=np.uint32)
+    return [oracle.Oracle(m, "gpt2"), oracle.Oracle(m, "llama3")]
+
+
+def test_device_class_table_matches_oracle_table(rules):
+    rng = random.Random(0)
+    cps = list(range(0, 0x3400)) + rng.sample(range(0x3400, 0x110000), 60000)
+    for cp in cps:
+        if 0xD800 <= cp <= 0xDFFF:
+            continue
+        assert rules.rules_cpu_class(cp) == oracle.char_class(cp), hex(cp)
+
+
+@pytest.mark.parametrize("pat", [0, 1])
+def test_exhaustive_short_strings(rules, orcs, pat):
+    bad = []
+    for n in range(1, 5):
+        for tup in itertools.product(ALPHA, repeat=n):
+            b = "".join(tup).encode()
+            if rules.pieces(b, pat) != orcs[pat].pieces(b):
+                bad.append(b)
+    assert not bad, bad[:10]
+
+
+@pytest.mark.parametrize("pat", [0, 1])
+def test_random_strings(rules, orcs, pat):
+    rng = random.Random(11 + pat)
+    for _ in range(30000):
+        b = "".join(rng.choice(ALPHA) for _ in range(rng.randint(1, 48))).encode()
+        assert rules.pieces(b, pat) == orcs[pat].pieces(b), b
+
+
+@pytest.mark.parametrize("pat", [0, 1])
+def test_long_runs_and_workload(rules, orcs, pat):
+    texts = ["7" * 10001 + "x", "x" + " " * 5000 + "y", "a\n" + " " * 3000 + "\n  b", "!" + "\r\n" * 2000 + "  z",
+             "'s" * 1000, textgen.mix_text(77, 150_000)]
+    for t in texts:
+        b = t.encode()
+        assert rules.pieces(b, pat) == orcs[pat].pieces(b)
+
+
+def test_documents_are_hard_boundaries(rules, orcs):
+    docs = ["ab", "'s x", "12", "345", "\n", "\n  y", "", "  ", "!\n", "\nq"]
+    data = "".join(docs).encode()
+    off = np.cumsum([0] + [len(d.encode()) for d in docs])
+    for pat in (0, 1):
+        want = []
+        for d, s in zip(docs, off[:-1]):
+            want += [int(s) + p for p in orcs[pat].pieces(d.encode())]
+        assert rules.pieces(data, pat, off) == want
+
+
+def test_round_selection_closed_form(rules):
+    def ref(m, carry):
+        s, prev = 0, carry
+        for j in range(64):
+            take = (m >> j) & 1 and not prev
+            if take:
+                s |= 1 << j
+            prev = take
+        return s
+
+    rng = random.Random(3)
+    for _ in range(50000):
+        p = rng.choice([0.1, 0.5, 0.9, 0.99])
+        m = sum(1 << j for j in range(64) if rng.random() < p)
+        c = rng.randint(0, 1)
+        assert rules.rules_cpu_select(m, c) == ref(m, c)
