@@ -54,8 +54,10 @@ def algorithmic_bytes(stage: str, n_bytes: int, n_tokens: int) -> int:
     flags = 2 * chunks
     if stage == "pretokenize":      # text in, piece-start flags out
         return n_bytes + flags
-    if stage == "bpe":              # text and flags in, tokens and chunk counts out
+    if stage == "pieces":           # text and flags in, whole-piece tokens and chunk counts out
         return n_bytes + flags + 4 * n_tokens + 4 * chunks
+    if stage == "merge":            # bytes of the merged pieces in, their tokens out
+        return n_bytes + 4 * n_tokens
     if stage == "assemble":         # counts and staged tokens in, IDs and offsets out
         return 4 * chunks * 2 + 8 * n_tokens
     return 0
@@ -132,7 +134,7 @@ def main() -> int:
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {mbps:.1f} MB/s")
 
     stages = {name: round(float(v), 5) for name, v in zip(tk.STAGES, stage_avg)}
-    dom = max(("pretokenize", "bpe", "assemble"), key=lambda s: stages[s])
+    dom = max(("pretokenize", "pieces", "merge", "assemble"), key=lambda s: stages[s])
     dom_ms = stages[dom]
     alg = algorithmic_bytes(dom, n_bytes, n_tokens)
     achieved = alg / (dom_ms * 1e-3) / 1e9 if dom_ms > 0 else 0.0

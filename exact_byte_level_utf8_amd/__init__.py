@@ -199,7 +199,7 @@ class Tokenizer:
         return list(out[:k])
 
 
-STAGES = ("reset", "pretokenize", "bpe", "bpe_long", "assemble", "doc_offsets")
+STAGES = ("reset", "pretokenize", "pieces", "merge", "assemble", "doc_offsets")
 
 
 def flags_to_starts(flags: np.ndarray, n: int) -> np.ndarray:

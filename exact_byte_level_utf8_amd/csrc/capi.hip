@@ -120,9 +120,10 @@ struct tok_ctx {
   void free_scratch() {
     dfree(b.flags);
     dfree(b.staging);
+    dfree(b.cnt8);
     dfree(b.chunk_cnt);
     dfree(b.chunk_excl);
-    dfree(b.longs);
+    for (auto& l : b.list) dfree(l);
     dfree(b.ws_sym);
     dfree(b.ws_rk);
     dfree(b.ws_sel);
@@ -145,7 +146,10 @@ struct tok_ctx {
         hipMalloc((void**)&b.staging, (c + 64) * sizeof(int32_t)) != hipSuccess ||
         hipMalloc((void**)&b.chunk_cnt, chunks * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&b.chunk_excl, chunks * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.longs, chunks * sizeof(uint4)) != hipSuccess ||
+        hipMalloc((void**)&b.cnt8, c + 64) != hipSuccess ||
+        hipMalloc((void**)&b.list[0], (c / 2 + 64) * sizeof(uint2)) != hipSuccess ||
+        hipMalloc((void**)&b.list[1], (c / (kRowMax + 1) + 64) * sizeof(uint2)) != hipSuccess ||
+        hipMalloc((void**)&b.list[2], (c / (kWaveMax + 1) + 64) * sizeof(uint2)) != hipSuccess ||
         hipMalloc((void**)&b.ws_sym, (c + 64) * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&b.ws_rk, (c + 64) * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&b.ws_sel, (c + 64) * sizeof(uint64_t)) != hipSuccess ||
@@ -187,10 +191,8 @@ struct tok_ctx {
     if (prof) (void)hipEventRecord(ev[i], s);
   }
 
-  // Enqueue the pipeline over d_text[0..n) and wait for it.  flags_override:
-  // piece-start words prepared by the caller (the load-time vocabulary check
-  // skips pre-tokenization); out_flags: stop after pre-tokenization, with the
-  // flag words written there.
+  // Enqueue the pipeline over d_text[0..n) and wait for it.  out_flags: stop
+  // after pre-tokenization, with the flag words written there.
   int run(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, int32_t* out,
           uint64_t out_cap, uint64_t* out_off, hipStream_t s, bool words, uint16_t* out_flags,
           uint32_t* total) {
@@ -204,9 +206,9 @@ struct tok_ctx {
     launch_pretok(text, n, doc_off, n_docs, pattern, bb, s);
     mark(2, s);
     if (!out_flags) {
-      launch_bpe(text, n, t, bb, s);
+      launch_pieces(text, n, t, bb, s);
       mark(3, s);
-      launch_bpe_long(text, n, t, bb, s);
+      launch_merge(text, n, t, bb, s);
       mark(4, s);
       launch_assemble(n, out, out_cap, bb, s);
       mark(5, s);
@@ -243,8 +245,8 @@ struct tok_ctx {
     const uint32_t tiles = (uint32_t)((n + kTile - 1) / kTile);
     const Tables t = tables(false);
     launch_reset(b, tiles, nullptr, 0, n, stream);
-    launch_bpe(d_text, n, t, b, stream);
-    launch_bpe_long(d_text, n, t, b, stream);
+    launch_pieces(d_text, n, t, b, stream);
+    launch_merge(d_text, n, t, b, stream);
     launch_assemble(n, d_ids, n, b, stream);
     HIP_OK(hipGetLastError());
     HIP_OK(hipMemcpyAsync(h_ctr, d_ctr, sizeof(Counters), hipMemcpyDeviceToHost, stream));

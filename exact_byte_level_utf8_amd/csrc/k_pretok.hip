@@ -27,6 +27,14 @@ constexpr int kWin = kTile + 2 * kHalo;
 // per-byte flags in LDS
 constexpr uint8_t kBDoc = 1, kBOut = 2;
 
+// Padded LDS indexing.  Each thread walks 16 consecutive positions, so lanes
+// touch positions 16 apart; one pad word per 16 info words and four pad bytes
+// per 16 bytes spread those lanes over distinct banks.
+__device__ inline int IX(int k) { return k + (k >> 4); }
+__device__ inline int BX(int k) { return k + ((k >> 4) << 2); }
+constexpr int kWinI = kWin + kWin / 16 + 1;
+constexpr int kWinB = kWin + 4 * (kWin / 16) + 4;
+
 __device__ inline uint32_t dev_class(uint32_t cp) {
   if (cp < 0x80) return ascii_class(cp);
   if (cp >= 0x110000) return kO;
@@ -110,24 +118,24 @@ struct BwdOp {
 
 // previous code point's lead index in the window, same document, or -1
 __device__ inline int prev_lead(const uint32_t* info, const uint8_t* fl, int k) {
-  if (k < 0 || (fl[k] & kBDoc)) return -1;
+  if (k < 0 || (fl[BX(k)] & kBDoc)) return -1;
   int j = k - 1;
   for (int t = 0; t < 4 && j >= 0; ++t, --j) {
-    if (fl[j] & kBOut) return -1;
-    if (info[j] & kILead) return j;
+    if (fl[BX(j)] & kBOut) return -1;
+    if (info[IX(j)] & kILead) return j;
   }
   return -1;
 }
 
-__device__ inline uint32_t info_at(const uint32_t* info, int k) { return k < 0 ? kNone : info[k]; }
+__device__ inline uint32_t info_at(const uint32_t* info, int k) { return k < 0 ? kNone : info[IX(k)]; }
 
 template <int PATTERN>
 __global__ void __launch_bounds__(kThreads)
 pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off,
               uint32_t n_docs, uint16_t* __restrict__ flags, Counters* __restrict__ ctr) {
-  __shared__ uint8_t s_raw[kWin];
-  __shared__ uint8_t s_fl[kWin];
-  __shared__ uint32_t s_info[kWin];
+  __shared__ uint8_t s_raw[kWinB];
+  __shared__ uint8_t s_fl[kWinB];
+  __shared__ uint32_t s_info[kWinI];
   __shared__ uint32_t s_scan[kThreads / kWave];
   __shared__ uint32_t s_misc[4];
 
@@ -139,8 +147,8 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   for (int k = tid; k < kWin; k += kThreads) {
     const int64_t p = lo + k;
     const bool in = p >= 0 && p < sn;
-    s_raw[k] = in ? text[p] : 0;
-    s_fl[k] = in ? 0 : kBOut;
+    s_raw[BX(k)] = in ? text[p] : 0;
+    s_fl[BX(k)] = in ? 0 : kBOut;
   }
   if (doc_off && tid == 0) s_misc[0] = first_doc_at_or_after(doc_off, n_docs, lo < 0 ? 0 : (uint64_t)lo);
   __syncthreads();
@@ -148,30 +156,32 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     for (uint32_t d = s_misc[0] + tid; d <= n_docs; d += kThreads) {
       const uint64_t p = doc_off[d];
       if ((int64_t)p >= lo + kWin) break;
-      if ((int64_t)p >= lo && (int64_t)p < sn) s_fl[p - lo] |= kBDoc;  // equal offsets write equal bytes
+      if ((int64_t)p >= lo && (int64_t)p < sn) s_fl[BX(p - lo)] |= kBDoc;  // equal offsets write equal bytes
     }
   } else if (tid == 0 && lo <= 0 && sn > 0) {
-    s_fl[-lo] |= kBDoc;
+    s_fl[BX(-lo)] |= kBDoc;
   }
   __syncthreads();
 
   // decode every lead byte of the window into an info word
   for (int k = tid; k < kWin; k += kThreads) {
-    const uint8_t fl = s_fl[k];
+    const uint8_t fl = s_fl[BX(k)];
     uint32_t in = 0;
-    const uint32_t b = s_raw[k];
+    const uint32_t b = s_raw[BX(k)];
     if (!(fl & kBOut) && (b & 0xC0) != 0x80) {
       const uint32_t len = utf8_len(b);
       if (k + (int)len >= kWin) {
         in = kO | kILead | kIUndecoded | (len << kILenShift);
       } else {
-        const uint32_t cp = utf8_cp(&s_raw[k], len);
+        uint8_t sb[4];
+        for (uint32_t t = 0; t < 4; ++t) sb[t] = t < len ? s_raw[BX(k + (int)t)] : 0;
+        const uint32_t cp = utf8_cp(sb, len);
         in = make_info(cp, dev_class(cp), len, dev_fold_extra(cp));
-        if (s_fl[k + len] & (kBDoc | kBOut)) in |= kILastInDoc;
+        if (s_fl[BX(k + len)] & (kBDoc | kBOut)) in |= kILastInDoc;
       }
       if (fl & kBDoc) in |= kIDocStart;
     }
-    s_info[k] = in;
+    s_info[IX(k)] = in;
   }
 
   // UTF-8 validation of the tile's own bytes (Unicode Table 3-7, well-formed
@@ -179,21 +189,21 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   bool bad = false;
   for (int i = 0; i < kChunk; ++i) {
     const int k = kHalo + tid * kChunk + i;
-    if (s_fl[k] & kBOut) break;
-    const uint32_t b = s_raw[k];
+    if (s_fl[BX(k)] & kBOut) break;
+    const uint32_t b = s_raw[BX(k)];
     if (b < 0x80) continue;
     if ((b & 0xC0) == 0x80) {
-      if (s_fl[k] & kBDoc) { bad = true; continue; }
+      if (s_fl[BX(k)] & kBDoc) { bad = true; continue; }
       bool ok = false;
       for (int steps = 1; steps <= 3; ++steps) {
         const int j = k - steps;
-        if (s_fl[j] & kBOut) break;
-        const uint32_t rb = s_raw[j];
+        if (s_fl[BX(j)] & kBOut) break;
+        const uint32_t rb = s_raw[BX(j)];
         if ((rb & 0xC0) != 0x80) {
           ok = rb >= 0xC0 && utf8_len(rb) > (uint32_t)steps;
           break;
         }
-        if (s_fl[j] & kBDoc) break;
+        if (s_fl[BX(j)] & kBDoc) break;
       }
       bad |= !ok;
     } else {
@@ -201,9 +211,9 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
       const uint32_t len = utf8_len(b);
       for (uint32_t t = 1; t < len; ++t) {
         const int j = k + t;
-        if ((s_fl[j] & (kBOut | kBDoc)) || (s_raw[j] & 0xC0) != 0x80) bad = true;
+        if ((s_fl[BX(j)] & (kBOut | kBDoc)) || (s_raw[BX(j)] & 0xC0) != 0x80) bad = true;
       }
-      const uint32_t c1 = s_raw[k + 1];
+      const uint32_t c1 = s_raw[BX(k + 1)];
       if ((b == 0xE0 && c1 < 0xA0) || (b == 0xED && c1 > 0x9F) || (b == 0xF0 && c1 < 0x90) ||
           (b == 0xF4 && c1 > 0x8F))
         bad = true;
@@ -218,8 +228,8 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     if (tid == 0) {  // walk left through the halo until both forward aggregates reset
       uint32_t acc = kFwdId, done = 0;
       for (int k = kHalo - 1; k >= 0; --k) {
-        if (s_fl[k] & kBOut) { done = 1; break; }
-        const uint32_t in = s_info[k];
+        if (s_fl[BX(k)] & kBOut) { done = 1; break; }
+        const uint32_t in = s_info[IX(k)];
         if (in & kILead) {
           acc = fwd_comp(fwd_elem(in), acc);
           if (fwd_resolved(acc)) { done = 1; break; }
@@ -231,8 +241,8 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     if (tid == kWave) {  // walk right until the backward aggregate resets
       uint32_t acc = kBwdId, done = 0;
       for (int k = kHalo + kTile; k < kWin; ++k) {
-        if (s_fl[k] & kBOut) { done = 1; break; }
-        const uint32_t in = s_info[k];
+        if (s_fl[BX(k)] & kBOut) { done = 1; break; }
+        const uint32_t in = s_info[IX(k)];
         if (in & kILead) {
           if (in & kIUndecoded) break;
           acc = bwd_comp(acc, bwd_elem(in));
@@ -242,10 +252,11 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
       s_misc[3] = bwd_apply(acc, 0) | (done << 1);
     }
     __syncthreads();
-    carry_f = s_misc[1];
-    const bool fdone = s_misc[2] != 0;
-    carry_h = s_misc[3] & 1u;
-    const bool bdone = (s_misc[3] >> 1) & 1u;
+    carry_f = __builtin_amdgcn_readfirstlane(s_misc[1]);
+    const bool fdone = __builtin_amdgcn_readfirstlane(s_misc[2]) != 0;
+    const uint32_t m3 = __builtin_amdgcn_readfirstlane(s_misc[3]);
+    carry_h = m3 & 1u;
+    const bool bdone = (m3 >> 1) & 1u;
     __syncthreads();
     if (!fdone) {  // a run longer than the halo ends before the tile: reduce 4 KiB blocks
       uint32_t acc = kFwdId;
@@ -255,7 +266,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
         chunk_elems_global(text, n, doc_off, n_docs, start + (int64_t)tid * kChunk, &fe, &be);
         uint32_t tot;
         wg_excl_scan<kThreads>(fe, kFwdId, FwdOp(), s_scan, &tot);
-        acc = fwd_comp(tot, acc);
+        acc = __builtin_amdgcn_readfirstlane(fwd_comp(tot, acc));  // uniform loop exit
         if (fwd_resolved(acc) || start <= 0) break;
       }
       carry_f = fwd_apply(acc, 0);
@@ -267,7 +278,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
         chunk_elems_global(text, n, doc_off, n_docs, start + (int64_t)tid * kChunk, &fe, &be);
         uint32_t tot;
         wg_excl_suffix<kThreads>(be, kBwdId, BwdOp(), s_scan, &tot);
-        acc = bwd_comp(acc, tot);
+        acc = __builtin_amdgcn_readfirstlane(bwd_comp(acc, tot));  // uniform loop exit
         if ((acc & 1u) || start + kTile >= sn) break;
       }
       carry_h = bwd_apply(acc, 0);
@@ -280,7 +291,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   if (PATTERN == 1) {
     uint32_t fe = kFwdId, be = kBwdId;
     for (int i = 0; i < kChunk; ++i) {
-      const uint32_t in = s_info[k0 + i];
+      const uint32_t in = s_info[IX(k0 + i)];
       if (in & kILead) {
         fe = fwd_comp(fe, fwd_elem(in));
         be = bwd_comp(be, bwd_elem(in));
@@ -291,7 +302,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     fstate = fwd_apply(fpre, carry_f);
     uint32_t h = bwd_apply(bsuf, carry_h);
     for (int i = kChunk - 1; i >= 0; --i) {  // h to the right of each lead
-      const uint32_t in = s_info[k0 + i];
+      const uint32_t in = s_info[IX(k0 + i)];
       if (in & kILead) {
         hmask |= h << i;
         h = bwd_apply(bwd_elem(in), h);
@@ -302,7 +313,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   uint32_t word = 0;
   for (int i = 0; i < kChunk; ++i) {
     const int k = k0 + i;
-    const uint32_t c = s_info[k];
+    const uint32_t c = s_info[IX(k)];
     if (!(c & kILead)) continue;
     const int j1 = prev_lead(s_info, s_fl, k);
     const int j2 = prev_lead(s_info, s_fl, j1);
@@ -311,7 +322,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     const uint32_t p1 = info_at(s_info, j1), p2 = info_at(s_info, j2);
     const uint32_t p3 = info_at(s_info, j3), p4 = info_at(s_info, j4);
     const uint32_t len = (c >> kILenShift) & 7u;
-    const uint32_t n1 = (c & kILastInDoc) ? kNone : s_info[k + len];
+    const uint32_t n1 = (c & kILastInDoc) ? kNone : s_info[IX(k + len)];
     bool st;
     if (PATTERN == 0) {
       st = piece_start_gpt2(c, p1, p2, p3, p4, n1);

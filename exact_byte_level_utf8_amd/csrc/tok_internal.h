@@ -3,12 +3,16 @@
 // Data layout in HBM for one call over N input bytes (C = ceil(N / 16) chunks,
 // G = ceil(N / 4096) tiles):
 //   flags      uint16[C + 8]   bit i of word c: byte 16c + i starts a piece
-//   staging    int32[N + 64]   tokens of chunk c, contiguous from the chunk's
-//                              first piece start (they fit: a piece of b bytes
-//                              yields at most b tokens)
+//   staging    int32[N + 64]   tokens of the piece that starts at byte s, at
+//                              staging[s ..] (a piece of b bytes yields at most
+//                              b tokens, so every piece owns its slot)
+//   cnt8       uint8[N + 64]   token count of the piece that starts at byte s
+//                              (read only for pieces that are not the last of
+//                              their chunk, which are under 16 bytes)
 //   chunk_cnt  uint32[C]       tokens of the pieces that start in chunk c
 //   chunk_excl uint32[C]       exclusive prefix of chunk_cnt (output offsets)
-//   longs      uint4[C]        pieces longer than kShortMax bytes
+//   list1/2/3  uint2[...]      pieces left for merging: 2..16 bytes, 17..64
+//                              bytes, longer (start, length; 0 = not yet known)
 //   ws_sym/rk  uint32[N + 64]  merge workspace of long pieces, indexed by byte
 //   ws_sel     uint64[N + 64]  round selections of long pieces, indexed by byte
 //   scan_state uint64[G]       decoupled look-back state of the count scan
@@ -24,9 +28,10 @@ constexpr int kTile = 4096;          // bytes per workgroup tile
 constexpr int kThreads = 256;        // threads per workgroup
 constexpr int kChunk = 16;           // bytes per thread (one flag word)
 constexpr int kHalo = 64;            // context bytes loaded on each side of a tile
-constexpr int kShortMax = 32;        // longest piece merged in one lane's registers
 constexpr int kWordMax = 13;         // longest piece the whole-piece table holds
-constexpr int kLongWaves = 2048;     // resident waves of the long-piece kernel
+constexpr int kRowMax = 16;          // longest piece merged by one 16-lane row
+constexpr int kWaveMax = 64;         // longest piece merged by one wave in registers
+constexpr int kPieceTile = 1024;     // bytes per workgroup of the piece pass (4 per thread)
 constexpr uint32_t kNoRank = 0xFFFFFFFFu;
 constexpr uint64_t kEmptySlot = ~0ull;
 
@@ -38,9 +43,11 @@ enum : uint32_t { kStUtf8 = 1u, kStSpin = 2u, kStDocOff = 4u };
 
 struct Counters {
   uint32_t status;      // kSt* bits, OR-ed by kernels
-  uint32_t n_long;      // entries in the long-piece list
+  uint32_t n_list[3];   // entries in the merge lists (2..16, 17..64, longer)
+  uint32_t work;        // next merge work item
   uint32_t k3_ticket;   // tile ticket of the count scan
   uint32_t total;       // tokens in the output
+  uint32_t pad;
 };
 
 // Read-only device tables built by tok_load.
@@ -57,9 +64,10 @@ struct Tables {
 struct Bufs {
   uint16_t* flags;
   int32_t* staging;
+  uint8_t* cnt8;
   uint32_t* chunk_cnt;
   uint32_t* chunk_excl;
-  uint4* longs;
+  uint2* list[3];
   uint32_t* ws_sym;
   uint32_t* ws_rk;
   uint64_t* ws_sel;
@@ -92,8 +100,8 @@ void launch_reset(Bufs b, uint32_t n_tiles, const uint64_t* doc_off, uint32_t n_
                   hipStream_t s);
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
                    int pattern, Bufs b, hipStream_t s);
-void launch_bpe(const uint8_t* text, uint64_t n, Tables t, Bufs b, hipStream_t s);
-void launch_bpe_long(const uint8_t* text, uint64_t n, Tables t, Bufs b, hipStream_t s);
+void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, hipStream_t s);
+void launch_merge(const uint8_t* text, uint64_t n, Tables t, Bufs b, hipStream_t s);
 void launch_assemble(uint64_t n, int32_t* out, uint64_t cap, Bufs b, hipStream_t s);
 void launch_doc_offsets(uint64_t n, const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off,
                         Tables t, Bufs b, hipStream_t s);

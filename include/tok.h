@@ -187,8 +187,9 @@ size_t tok_token_lengths(const tok_ctx* ctx, uint32_t* len_out, size_t n);
  * Stage timing (GraphTok, section 7, per-stage profile).  With profiling on,
  * every call records HIP events around each device stage on the stream it
  * runs on; tok_stage_ms returns the last call's stage durations in ms:
- * [0] counter reset, [1] pre-tokenization, [2] piece BPE, [3] long-piece BPE,
- * [4] count scan + scatter, [5] document offsets.  Returns the number of
+ * [0] counter reset, [1] pre-tokenization, [2] piece pass (single bytes and
+ * whole-piece hits), [3] merge rounds of the remaining pieces, [4] count scan +
+ * scatter, [5] document offsets.  Returns the number of
  * stages written (at most n).
  */
 int tok_set_profiling(tok_ctx* ctx, int on);
