@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_1m|llama3_3m|batch64]
 
 One step = one tok_encode_dev call over the whole request (pre-tokenization,
-piece BPE, long-piece BPE, count scan + scatter), with the UTF-8 text already
+piece pass with merges, count scan + scatter), with the UTF-8 text already
 resident in HBM and the int32 IDs left in HBM.  W untimed steps, then exactly
 K timed steps between two device synchronizations.  Prints one JSON line:
 value = input MB/s (UTF-8 bytes / s / 1e6), ms_per_step = ms per request.
@@ -54,12 +54,10 @@ def algorithmic_bytes(stage: str, n_bytes: int, n_tokens: int) -> int:
     flags = 2 * chunks
     if stage == "pretokenize":      # text in, piece-start flags out
         return n_bytes + flags
-    if stage == "pieces":           # text and flags in, whole-piece tokens and chunk counts out
-        return n_bytes + flags + 4 * n_tokens + 4 * chunks
-    if stage == "merge":            # bytes of the merged pieces in, their tokens out
-        return n_bytes + 4 * n_tokens
-    if stage == "assemble":         # counts and staged tokens in, IDs and offsets out
-        return 4 * chunks * 2 + 8 * n_tokens
+    if stage == "pieces":           # text and flags in, each tile's run of int32 IDs out
+        return n_bytes + flags + 4 * n_tokens
+    if stage == "assemble":         # runs in, IDs out
+        return 8 * n_tokens
     return 0
 
 
@@ -71,6 +69,9 @@ def main() -> int:
     ap.add_argument("--workload", default="gpt2_1m", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run one device-to-device copy of this many MiB: a kernel of "
+                         "known traffic that scales the HBM byte counters of a profiler run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -128,13 +129,21 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     tok.set_profiling(False)
+    if args.copy_probe_mib > 0:
+        src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe_mib} MiB device-to-device")
+        del src, dst
     ms_per_step = 1e3 * elapsed / args.steps
     mbps = n_bytes * args.steps / elapsed / 1e6
     stage_avg = stage_sum / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {mbps:.1f} MB/s")
 
     stages = {name: round(float(v), 5) for name, v in zip(tk.STAGES, stage_avg)}
-    dom = max(("pretokenize", "pieces", "merge", "assemble"), key=lambda s: stages[s])
+    dom = max(("pretokenize", "pieces", "assemble"), key=lambda s: stages[s])
     dom_ms = stages[dom]
     alg = algorithmic_bytes(dom, n_bytes, n_tokens)
     achieved = alg / (dom_ms * 1e-3) / 1e9 if dom_ms > 0 else 0.0

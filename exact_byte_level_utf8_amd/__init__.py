@@ -194,12 +194,12 @@ class Tokenizer:
         _check(lib().tok_set_profiling(self._h, int(bool(on))), "tok_set_profiling")
 
     def stage_ms(self) -> list[float]:
-        out = (ctypes.c_float * 6)()
-        k = lib().tok_stage_ms(self._h, out, 6)
+        out = (ctypes.c_float * len(STAGES))()
+        k = lib().tok_stage_ms(self._h, out, len(STAGES))
         return list(out[:k])
 
 
-STAGES = ("reset", "pretokenize", "pieces", "merge", "assemble", "doc_offsets")
+STAGES = ("reset", "pretokenize", "pieces", "assemble")
 
 
 def flags_to_starts(flags: np.ndarray, n: int) -> np.ndarray:

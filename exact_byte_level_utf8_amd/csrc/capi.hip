@@ -64,7 +64,7 @@ void hfree(T*& p) {
   p = nullptr;
 }
 
-constexpr int kStages = 6;
+constexpr int kStages = 4;
 
 }  // namespace
 
@@ -79,10 +79,10 @@ struct tok_ctx {
 
   // device tables
   uint64_t* d_merge_slots = nullptr;
-  uint32_t merge_mask = 0;
+  uint32_t merge_buckets = 0;
   uint32_t* d_pair_rank = nullptr;
   uint64_t* d_word_slots = nullptr;
-  uint32_t word_mask = 0;
+  uint32_t word_buckets = 0;
   uint32_t* d_tok_len = nullptr;
 
   // scratch, grown on demand
@@ -109,10 +109,10 @@ struct tok_ctx {
   Tables tables(bool words = true) const {
     Tables t{};
     t.merge_slots = d_merge_slots;
-    t.merge_mask = merge_mask;
+    t.merge_buckets = merge_buckets;
     t.pair_rank = d_pair_rank;
     t.word_slots = words ? d_word_slots : nullptr;
-    t.word_mask = words ? word_mask : 0;
+    t.word_buckets = words ? word_buckets : 0;
     t.tok_len = d_tok_len;
     return t;
   }
@@ -120,10 +120,8 @@ struct tok_ctx {
   void free_scratch() {
     dfree(b.flags);
     dfree(b.staging);
-    dfree(b.cnt8);
-    dfree(b.chunk_cnt);
-    dfree(b.chunk_excl);
-    for (auto& l : b.list) dfree(l);
+    dfree(b.tile_cnt);
+    dfree(b.tile_first);
     dfree(b.ws_sym);
     dfree(b.ws_rk);
     dfree(b.ws_sel);
@@ -141,15 +139,11 @@ struct tok_ctx {
     (void)hipStreamSynchronize(stream);
     free_scratch();
     const uint64_t c = std::max<uint64_t>(next_pow2(n), 1u << 16);
-    const uint64_t chunks = c / kChunk, tiles = c / kTile;
+    const uint64_t chunks = c / kChunk, tiles = c / kPieceTile;
     if (hipMalloc((void**)&b.flags, (chunks + 8) * sizeof(uint16_t)) != hipSuccess ||
         hipMalloc((void**)&b.staging, (c + 64) * sizeof(int32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.chunk_cnt, chunks * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.chunk_excl, chunks * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.cnt8, c + 64) != hipSuccess ||
-        hipMalloc((void**)&b.list[0], (c / 2 + 64) * sizeof(uint2)) != hipSuccess ||
-        hipMalloc((void**)&b.list[1], (c / (kRowMax + 1) + 64) * sizeof(uint2)) != hipSuccess ||
-        hipMalloc((void**)&b.list[2], (c / (kWaveMax + 1) + 64) * sizeof(uint2)) != hipSuccess ||
+        hipMalloc((void**)&b.tile_cnt, tiles * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc((void**)&b.tile_first, tiles * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&b.ws_sym, (c + 64) * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&b.ws_rk, (c + 64) * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&b.ws_sel, (c + 64) * sizeof(uint64_t)) != hipSuccess ||
@@ -198,28 +192,24 @@ struct tok_ctx {
           uint32_t* total) {
     Bufs bb = b;
     if (out_flags) bb.flags = out_flags;
-    const uint32_t tiles = (uint32_t)((n + kTile - 1) / kTile);
+    const uint32_t tiles = (uint32_t)((n + kPieceTile - 1) / kPieceTile);
     const Tables t = tables(words);
     mark(0, s);
-    launch_reset(bb, tiles, doc_off, n_docs, n, s);
+    launch_reset(bb, tiles, doc_off, n_docs, n, out_flags ? nullptr : out_off, s);
     mark(1, s);
     launch_pretok(text, n, doc_off, n_docs, pattern, bb, s);
     mark(2, s);
     if (!out_flags) {
-      launch_pieces(text, n, t, bb, s);
+      launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s);
       mark(3, s);
-      launch_merge(text, n, t, bb, s);
+      launch_assemble(n, bb, out, out_cap, doc_off, n_docs, out_off, s);
       mark(4, s);
-      launch_assemble(n, out, out_cap, bb, s);
-      mark(5, s);
-      if (out_off) launch_doc_offsets(n, doc_off, n_docs, out_off, t, bb, s);
-      mark(6, s);
     }
     HIP_OK(hipGetLastError());
     HIP_OK(hipMemcpyAsync(h_ctr, d_ctr, sizeof(Counters), hipMemcpyDeviceToHost, s));
     HIP_OK(hipStreamSynchronize(s));
     if (prof) {
-      const int last = out_flags ? 2 : kStages;
+      const int last = out_flags ? 2 : kStages;  // pre-tokenization only: two stages
       for (int i = 0; i < kStages; ++i) {
         float ms = 0.f;
         if (i < last && hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) ms = 0.f;
@@ -242,12 +232,11 @@ struct tok_ctx {
     if (rc) return rc;
     HIP_OK(hipMemcpyAsync(d_text, h_bytes, n, hipMemcpyHostToDevice, stream));
     HIP_OK(hipMemcpyAsync(b.flags, flags.data(), flags.size() * 2, hipMemcpyHostToDevice, stream));
-    const uint32_t tiles = (uint32_t)((n + kTile - 1) / kTile);
+    const uint32_t tiles = (uint32_t)((n + kPieceTile - 1) / kPieceTile);
     const Tables t = tables(false);
-    launch_reset(b, tiles, nullptr, 0, n, stream);
-    launch_pieces(d_text, n, t, b, stream);
-    launch_merge(d_text, n, t, b, stream);
-    launch_assemble(n, d_ids, n, b, stream);
+    launch_reset(b, tiles, nullptr, 0, n, nullptr, stream);
+    launch_pieces(d_text, n, t, b, nullptr, 0, nullptr, stream);
+    launch_assemble(n, b, d_ids, n, nullptr, 0, nullptr, stream);
     HIP_OK(hipGetLastError());
     HIP_OK(hipMemcpyAsync(h_ctr, d_ctr, sizeof(Counters), hipMemcpyDeviceToHost, stream));
     HIP_OK(hipStreamSynchronize(stream));
@@ -314,6 +303,7 @@ int build_word_table(tok_ctx* ctx, const std::vector<std::vector<uint8_t>>& tok)
   ctx->n_not_self = (uint32_t)(cand.size() - self.size());
   if (self.empty()) return TOK_OK;
   const uint64_t slots = std::max<uint64_t>(next_pow2(2 * self.size()), 64);
+  const uint32_t bmask = (uint32_t)(slots / kBucket - 1);
   std::vector<uint64_t> tab(2 * slots, 0);
   for (uint32_t id : self) {
     const auto& s = tok[id];
@@ -321,14 +311,21 @@ int build_word_table(tok_ctx* ctx, const std::vector<std::vector<uint8_t>>& tok)
     for (size_t i = 0; i < s.size() && i < 8; ++i) a |= (uint64_t)s[i] << (8 * i);
     for (size_t i = 8; i < s.size(); ++i) bb |= (uint64_t)s[i] << (8 * (i - 8));
     bb |= (uint64_t)s.size() << 40;
-    uint32_t h = word_hash(a, bb) & (uint32_t)(slots - 1);
-    while (tab[2 * h + 1] != 0) h = (h + 1) & (uint32_t)(slots - 1);
-    tab[2 * h] = a;
-    tab[2 * h + 1] = bb | ((uint64_t)id << 44);
+    uint32_t h = word_hash(a, bb) & bmask;
+    for (bool placed = false; !placed; h = (h + 1) & bmask) {
+      for (uint32_t j = 0; j < kBucket && !placed; ++j) {
+        const size_t at = ((size_t)h * kBucket + j) * 2;
+        if (tab[at + 1] == 0) {
+          tab[at] = a;
+          tab[at + 1] = bb | ((uint64_t)id << 44);
+          placed = true;
+        }
+      }
+    }
   }
   HIP_OK(hipMalloc((void**)&ctx->d_word_slots, tab.size() * 8));
   HIP_OK(hipMemcpy(ctx->d_word_slots, tab.data(), tab.size() * 8, hipMemcpyHostToDevice));
-  ctx->word_mask = (uint32_t)(slots - 1);
+  ctx->word_buckets = bmask;
   return TOK_OK;
 }
 
@@ -358,7 +355,11 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
   if (pattern != TOK_PAT_GPT2 && pattern != TOK_PAT_LLAMA3) return TOK_E_PATTERN;
   if (n_merges > TOK_MAX_MERGES) return TOK_E_BADMERGES;
   // operands precede their merge, and each ordered pair has one rank
+  // open addressing over buckets of kBucket slots, at most half full; a key
+  // lives in the first bucket of its probe sequence with a free slot, taking
+  // the bucket's first free slot (lookups stop at a bucket with a free slot)
   const uint64_t slots = std::max<uint64_t>(next_pow2(2 * n_merges), 1024);
+  const uint32_t bmask = (uint32_t)(slots / kBucket - 1);
   std::vector<uint64_t> mtab(slots, kEmptySlot);
   std::vector<uint32_t> pr(65536, kNoRank);
   std::vector<std::vector<uint8_t>> tok(256 + n_merges);
@@ -367,12 +368,18 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
     const uint32_t a = merges[2 * r], bb = merges[2 * r + 1];
     if (a >= 256 + r || bb >= 256 + r) return TOK_E_BADMERGES;
     const uint64_t key = ((uint64_t)a << 20) | bb;
-    uint32_t h = merge_hash(a, bb) & (uint32_t)(slots - 1);
-    while (mtab[h] != kEmptySlot) {
-      if ((mtab[h] >> 24) == key) return TOK_E_BADMERGES;
-      h = (h + 1) & (uint32_t)(slots - 1);
+    uint32_t h = merge_hash(a, bb) & bmask;
+    for (bool placed = false; !placed; h = (h + 1) & bmask) {
+      for (uint32_t j = 0; j < kBucket && !placed; ++j) {
+        uint64_t& slot = mtab[(size_t)h * kBucket + j];
+        if (slot == kEmptySlot) {
+          slot = (key << 24) | r;
+          placed = true;
+        } else if ((slot >> 24) == key) {
+          return TOK_E_BADMERGES;  // the same ordered pair twice
+        }
+      }
     }
-    mtab[h] = (key << 24) | r;
     if ((a | bb) < 256) pr[(a << 8) | bb] = (uint32_t)r;
     tok[256 + r] = tok[a];
     tok[256 + r].insert(tok[256 + r].end(), tok[bb].begin(), tok[bb].end());
@@ -419,7 +426,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
             hipSuccess ||
         hipMemset(ctx->d_ctr, 0, sizeof(Counters)) != hipSuccess)
       break;
-    ctx->merge_mask = (uint32_t)(slots - 1);
+    ctx->merge_buckets = bmask;
     rc = build_word_table(ctx, tok);
   } while (false);
   if (rc != TOK_OK) {

@@ -5,26 +5,28 @@
 // lowest rank wins, the leftmost pair on equal rank, and the pair becomes ID
 // 256 + rank (GraphTok, section 4 "Warp-cooperative BPE").
 //
-// piece_kernel (one thread per 4 bytes): resolves the pieces that need no
-// merge loop -- a 1-byte piece is its byte's ID, and a 2..13-byte piece that is
-// a whole vocabulary string whose own BPE is that token (checked for every
-// string at load) is one probe of the whole-piece table (TokTier, "Exact GPU
-// Tokenization": whole-piece vocabulary hits) -- and appends every other piece
-// to one of three device work lists by length, with one atomic per wave.
-//
-// merge_kernel (persistent waves, items dealt round-robin): takes the long
-// list first, then the 17..64-byte list (one wave per piece, one symbol per
-// lane), then the 2..16-byte list (four pieces per wave, one 16-lane row each).
-// A round takes the row minimum of (rank, position), chooses every leftmost
-// non-overlapping occurrence of that pair value at once, compacts the row with
-// a lane permute, and re-probes only the pairs next to a merge (TokTier:
-// merging all leftmost non-overlapping occurrences of the minimum-rank pair
-// equals iterated single merges, and only pairs adjacent to a completed merge
-// are re-probed; GraphTok: a round takes every other pair of a chain).  Pieces
-// longer than 64 bytes run the same rounds over arrays in global memory.
-//
-// Every piece's tokens go to staging[start ..] and their count to cnt8[start];
-// each chunk's token total accumulates in chunk_cnt[start / 16].
+// piece_kernel: one workgroup per 1 KiB of piece starts, in two phases.
+//   1. One thread per 4 bytes resolves the pieces that need no merge loop: a
+//      1-byte piece is its byte's ID, and a 2..13-byte piece that is a whole
+//      vocabulary string whose own BPE is that token (checked for every string
+//      at load) is one probe of the whole-piece table (TokTier, "Exact GPU
+//      Tokenization": whole-piece vocabulary hits).  Every other piece goes to
+//      a work list in LDS by length.
+//   2. The workgroup's four waves merge the listed pieces: pieces longer than
+//      64 bytes first, then 17..64-byte pieces (one wave per piece, one symbol
+//      per lane), then 2..16-byte pieces (four per wave, one 16-lane row each).
+//      A round takes the row minimum of (rank, position), chooses every
+//      leftmost non-overlapping occurrence of that pair value at once,
+//      compacts the row with a lane permute, and re-probes only the pairs next
+//      to a merge (TokTier: merging all leftmost non-overlapping occurrences of
+//      the minimum-rank pair equals iterated single merges, and only pairs
+//      adjacent to a completed merge are re-probed; GraphTok: a round takes
+//      every other pair of a chain).  Pieces longer than 64 bytes run the same
+//      rounds over arrays in global memory.
+//   3. The tile's tokens are compacted in order (in LDS) and written as one
+//      run from the tile's first piece start, with the tile's count; the
+//      documents that start in the tile get their offsets within that run.
+//      The assembly kernel then places the runs (k_assemble.hip).
 #include "tok_internal.h"
 #include "bpe_util.h"
 #include "wg_scan.h"
@@ -32,15 +34,22 @@
 namespace tok {
 namespace {
 
+// Rank of the merge (a, b), or kNoRank.  Byte pairs come from a direct table;
+// other pairs from open addressing over buckets of kBucket slots, each bucket
+// read with two 16-byte loads.
 __device__ inline uint32_t merge_rank(const Tables& T, uint32_t a, uint32_t b) {
   if ((a | b) < 256u) return T.pair_rank[(a << 8) | b];
   const uint64_t key = ((uint64_t)a << 20) | b;
-  uint32_t h = merge_hash(a, b) & T.merge_mask;
-  for (uint32_t probe = 0; probe <= T.merge_mask; ++probe) {
-    const uint64_t s = T.merge_slots[h];
-    if (s == kEmptySlot) return kNoRank;
-    if ((s >> 24) == key) return (uint32_t)(s & 0xFFFFFFu);
-    h = (h + 1) & T.merge_mask;
+  uint32_t h = merge_hash(a, b) & T.merge_buckets;
+  for (uint32_t probe = 0; probe <= T.merge_buckets; ++probe) {
+    const ulonglong2* bk = reinterpret_cast<const ulonglong2*>(T.merge_slots + (size_t)h * kBucket);
+    const ulonglong2 s01 = bk[0], s23 = bk[1];
+    if ((s01.x >> 24) == key) return (uint32_t)(s01.x & 0xFFFFFFu);
+    if ((s01.y >> 24) == key) return (uint32_t)(s01.y & 0xFFFFFFu);
+    if ((s23.x >> 24) == key) return (uint32_t)(s23.x & 0xFFFFFFu);
+    if ((s23.y >> 24) == key) return (uint32_t)(s23.y & 0xFFFFFFu);
+    if (s23.y == kEmptySlot) return kNoRank;  // slots fill in order within a bucket
+    h = (h + 1) & T.merge_buckets;
   }
   return kNoRank;
 }
@@ -56,125 +65,64 @@ __device__ inline uint32_t word_lookup(const Tables& T, const uint8_t* p, uint32
     if (i < len) b |= (uint64_t)p[i] << (8 * (i - 8));
   b |= (uint64_t)len << 40;
   const ulonglong2* slots = reinterpret_cast<const ulonglong2*>(T.word_slots);
-  uint32_t h = word_hash(a, b) & T.word_mask;
-  for (uint32_t probe = 0; probe <= T.word_mask; ++probe) {
-    const ulonglong2 s = slots[h];
-    if (s.y == 0) return kNoRank;
-    if (s.x == a && (s.y & ((1ull << 44) - 1)) == b) return (uint32_t)(s.y >> 44);
-    h = (h + 1) & T.word_mask;
+  uint32_t h = word_hash(a, b) & T.word_buckets;
+  constexpr uint64_t kKeyMask = (1ull << 44) - 1;
+  for (uint32_t probe = 0; probe <= T.word_buckets; ++probe) {
+    const ulonglong2* bk = slots + (size_t)h * kBucket;
+    const ulonglong2 s0 = bk[0], s1 = bk[1], s2 = bk[2], s3 = bk[3];
+    if (s0.x == a && (s0.y & kKeyMask) == b) return (uint32_t)(s0.y >> 44);
+    if (s1.x == a && (s1.y & kKeyMask) == b) return (uint32_t)(s1.y >> 44);
+    if (s2.x == a && (s2.y & kKeyMask) == b) return (uint32_t)(s2.y >> 44);
+    if (s3.x == a && (s3.y & kKeyMask) == b) return (uint32_t)(s3.y >> 44);
+    if (s3.y == 0) return kNoRank;  // slots fill in order within a bucket
+    h = (h + 1) & T.word_buckets;
   }
   return kNoRank;
 }
 
-__global__ void __launch_bounds__(kThreads)
-piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B) {
-  constexpr int kChunksPerWg = kPieceTile / kChunk;  // 64
-  constexpr int kTextLds = kPieceTile + kWaveMax + 16;
-  constexpr int kFlagLds = kChunksPerWg + 6;
-  __shared__ uint8_t s_text[kTextLds];
-  __shared__ uint16_t s_flags[kFlagLds];
+// Row minimum over 16 lanes with DPP row rotations (every lane gets it).
+__device__ inline uint32_t row16_min(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));  // row_ror:2
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));  // row_ror:1
+  return v;
+}
 
-  const uint32_t tid = threadIdx.x, lane = tid & 63u;
-  const uint64_t base = (uint64_t)blockIdx.x * kPieceTile;
-  const uint64_t c0 = (uint64_t)blockIdx.x * kChunksPerWg;
-  const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
-  for (int k = tid; k < kTextLds; k += kThreads) {
-    const uint64_t p = base + k;
-    s_text[k] = p < n ? text[p] : 0;
-  }
-  for (int k = tid; k < kFlagLds; k += kThreads) {
-    const uint64_t c = c0 + k;
-    s_flags[k] = c < n_chunks ? B.flags[c] : 0;
-  }
-  __syncthreads();
-
-  const uint32_t lc = tid >> 2, q = tid & 3u;  // chunk within the workgroup, quarter of it
-  const uint64_t c = c0 + lc;
-  const uint32_t w = c < n_chunks ? s_flags[lc] : 0u;
-  const uint32_t mine = (w >> (4 * q)) & 15u;
-  uint32_t hits = 0, kinds = 0, lens = 0, packed = 0;
-#pragma unroll
-  for (uint32_t b = 0; b < 4; ++b) {
-    if (!((mine >> b) & 1u)) continue;
-    const uint32_t bit = 4 * q + b;
-    const uint64_t s = c * kChunk + bit;
-    uint64_t e = ~0ull;
-    const uint32_t above = w & ~((2u << bit) - 1u);
-    if (above) {
-      e = c * kChunk + __builtin_ctz(above);
-    } else {
-      for (uint32_t j = 1; j <= 4; ++j) {
-        const uint32_t wj = s_flags[lc + j];
-        if (wj) {
-          e = (c + j) * kChunk + __builtin_ctz(wj);
-          break;
-        }
-      }
-    }
-    if (e > n) e = n;
-    const uint64_t len = e - s;
-    const uint8_t* p = s_text + (s - base);
-    uint32_t id = kNoRank;
-    if (len == 1) id = p[0];
-    else if (len <= (uint64_t)kWordMax && T.word_slots) id = word_lookup(T, p, (uint32_t)len);
-    if (id != kNoRank) {
-      B.staging[s] = (int32_t)id;
-      B.cnt8[s] = 1;
-      ++hits;
-      continue;
-    }
-    const uint32_t list = len <= (uint64_t)kRowMax ? 0u : len <= (uint64_t)kWaveMax ? 1u : 2u;
-    kinds |= (list + 1) << (2 * b);
-    lens |= (list == 2 ? 0u : (uint32_t)len) << (8 * b);
-    packed += 1u << (10 * list);
-  }
-  // list slots: one atomic per wave and list, lanes take consecutive slots
-  const uint32_t incl = wave_incl_scan(packed, AddOp());
-  const uint32_t excl = incl - packed;
-  const uint32_t tot = __shfl(incl, 63, 64);
-  uint32_t b0 = 0, b1 = 0, b2 = 0;
-  if (lane == 63) {
-    if (tot & 1023u) b0 = atomicAdd(&B.ctr->n_list[0], tot & 1023u);
-    if ((tot >> 10) & 1023u) b1 = atomicAdd(&B.ctr->n_list[1], (tot >> 10) & 1023u);
-    if ((tot >> 20) & 1023u) b2 = atomicAdd(&B.ctr->n_list[2], (tot >> 20) & 1023u);
-  }
-  uint32_t slot0 = __shfl(b0, 63, 64) + (excl & 1023u);
-  uint32_t slot1 = __shfl(b1, 63, 64) + ((excl >> 10) & 1023u);
-  uint32_t slot2 = __shfl(b2, 63, 64) + ((excl >> 20) & 1023u);
-#pragma unroll
-  for (uint32_t b = 0; b < 4; ++b) {
-    const uint32_t kind = (kinds >> (2 * b)) & 3u;
-    if (!kind) continue;
-    const uint2 item = make_uint2((uint32_t)(c * kChunk + 4 * q + b), (lens >> (8 * b)) & 255u);
-    if (kind == 1) B.list[0][slot0++] = item;
-    else if (kind == 2) B.list[1][slot1++] = item;
-    else B.list[2][slot2++] = item;
-  }
-  hits += __shfl_xor(hits, 1, 64);
-  hits += __shfl_xor(hits, 2, 64);
-  if (q == 0 && c < n_chunks) B.chunk_cnt[c] = hits;
+__device__ inline uint32_t wave_min(uint32_t v) {
+  v = row16_min(v);
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
 // BPE of one piece per row of ROW lanes (ROW = 16: four pieces per wave; ROW =
 // 64: one piece per wave), one symbol per lane, in rounds.  Called by all 64
-// lanes; rows without a piece pass active = false.
+// lanes; rows without a piece pass active = false.  p: the piece's bytes;
+// tok_out / cnt_out: where its tokens and their count go; chunk_total: the
+// counter of the chunk the piece starts in (all three in LDS).
 template <int ROW>
-__device__ void merge_rows(const Tables& T, const uint8_t* __restrict__ text, uint64_t s, uint32_t len,
-                           bool active, const Bufs& B) {
+__device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool active, uint32_t* tok_out,
+                           uint8_t* cnt_out, uint32_t* chunk_total) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t k = lane & (ROW - 1);
   const uint32_t row_base = lane - k;
   const uint64_t row_bits = ROW == 64 ? ~0ull : (0xFFFFull << row_base);
   const uint64_t below = ((1ull << lane) - 1ull) & row_bits;
   uint32_t cur = active ? len : 0u;
-  uint32_t sym = k < cur ? (uint32_t)text[s + k] : 0u;
+  uint32_t sym = k < cur ? (uint32_t)p[k] : 0u;
   const uint32_t nx = __shfl_down(sym, 1, ROW);
   uint32_t rk = k + 1 < cur ? T.pair_rank[(sym << 8) | nx] : kNoRank;
   for (;;) {
     if (k + 1 >= cur) rk = kNoRank;
     uint32_t key = rk == kNoRank ? 0xFFFFFFFFu : ((rk << 6) | k);
-#pragma unroll
-    for (int d = ROW / 2; d >= 1; d >>= 1) key = min(key, (uint32_t)__shfl_xor(key, d, ROW));
+    key = row16_min(key);
+    if (ROW == 64) {
+      const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)key, 0),
+                             (uint32_t)__builtin_amdgcn_readlane((int)key, 16));
+      const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)key, 32),
+                             (uint32_t)__builtin_amdgcn_readlane((int)key, 48));
+      key = min(a, b);
+    }
     const bool live = key != 0xFFFFFFFFu;
     if (__ballot(live) == 0) break;
     const uint32_t r = key >> 6;
@@ -199,17 +147,11 @@ __device__ void merge_rows(const Tables& T, const uint8_t* __restrict__ text, ui
     rk = (uint32_t)__builtin_amdgcn_ds_permute((int)(dst << 2), (int)nrk);
     if (live) cur -= (uint32_t)__popcll(S & row_bits);
   }
-  if (active && k < cur) B.staging[s + k] = (int32_t)sym;
+  if (active && k < cur) tok_out[k] = sym;
   if (active && k == 0) {
-    B.cnt8[s] = (uint8_t)cur;
-    atomicAdd(&B.chunk_cnt[s / kChunk], cur);
+    *cnt_out = (uint8_t)cur;
+    atomicAdd(chunk_total, cur);
   }
-}
-
-__device__ inline uint32_t wave_min(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor(v, d, 64));
-  return v;
 }
 
 // Byte offset of the first piece start after s, or n.
@@ -234,9 +176,10 @@ __device__ inline uint64_t next_start(const uint16_t* flags, uint64_t n, uint64_
 
 // One wave merges a piece longer than 64 bytes with the same rounds, its
 // symbols and pair ranks in global memory (workspace indexed by the piece's
-// bytes, so pieces never share it), compacting in place.
+// bytes, so pieces never share it), compacting in place.  Its tokens stay in
+// ws_sym[s ..]; cnt_out gets 0 to mark the piece as long.
 __device__ void merge_long(const Tables& T, const uint8_t* __restrict__ text, uint64_t n, uint64_t s,
-                           const Bufs& B) {
+                           const Bufs& B, uint8_t* cnt_out, uint32_t* chunk_total) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   const uint64_t e = next_start(B.flags, n, s);
@@ -255,7 +198,7 @@ __device__ void merge_long(const Tables& T, const uint8_t* __restrict__ text, ui
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     uint32_t m = kNoRank;
     for (uint32_t k = lane; k + 1 < cur; k += 64) m = min(m, rk[k]);
-    m = __builtin_amdgcn_readfirstlane(wave_min(m));
+    m = wave_min(m);
     if (m == kNoRank) break;
     const uint32_t groups = (cur + 63) / 64;
     uint32_t carry = 0, chosen = 0;
@@ -304,52 +247,194 @@ __device__ void merge_long(const Tables& T, const uint8_t* __restrict__ text, ui
     }
     cur -= chosen;
   }
-  for (uint32_t k = lane; k < cur; k += 64) B.staging[s + k] = (int32_t)sym[k];
   if (lane == 0) {
-    B.cnt8[s] = (uint8_t)(cur < 255 ? cur : 255);  // only the chunk's last piece can be long
-    atomicAdd(&B.chunk_cnt[s / kChunk], cur);
+    *cnt_out = 0;  // marks a long piece: its tokens are in ws_sym
+    atomicAdd(chunk_total, cur);
   }
 }
 
-__global__ void __launch_bounds__(kThreads)
-merge_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B) {
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t n1 = B.ctr->n_list[0], n2 = B.ctr->n_list[1], n3 = B.ctr->n_list[2];
-  const uint32_t total = n3 + n2 + (n1 + 3) / 4;
-  // Items are dealt to waves round-robin, with every value that steers the
-  // loop in scalar registers: a work item taken by one lane and broadcast by a
-  // shuffle counts as divergent to the compiler, which then splits the loop
-  // per lane and separates the lanes of a wave.
-  const uint32_t wave = __builtin_amdgcn_readfirstlane((blockIdx.x * kThreads + threadIdx.x) >> 6);
-  const uint32_t n_waves = (gridDim.x * kThreads) >> 6;
-  for (uint32_t item = wave; item < total; item += n_waves) {
-    if (item < n3) {
-      merge_long(T, text, n, B.list[2][item].x, B);
-    } else if (item < n3 + n2) {
-      const uint2 it = B.list[1][item - n3];
-      merge_rows<64>(T, text, it.x, it.y, true, B);
+
+__global__ void __launch_bounds__(kPieceThreads)
+piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, const uint64_t* __restrict__ doc_off,
+             uint32_t n_docs, uint64_t* __restrict__ out_off) {
+  constexpr int kChunksPerWg = kPieceTile / kChunk;  // 64
+  constexpr int kPerChunk = kPieceThreads / kChunksPerWg;  // 8 threads per chunk
+  constexpr int kBytesPer = kChunk / kPerChunk;             // 2 bytes per thread
+  constexpr int kTextLds = kPieceTile + kWaveMax + 16;
+  constexpr int kFlagLds = kChunksPerWg + 6;
+  constexpr int kTokLds = kPieceTile + kWaveMax;
+  constexpr int kCap0 = kPieceTile / 2, kCap1 = kPieceTile / (kRowMax + 1) + 1;
+  constexpr int kCap2 = kPieceTile / (kWaveMax + 1) + 1;
+  constexpr uint32_t kWaves = kPieceThreads / kWave;
+  __shared__ uint8_t s_text[kTextLds];
+  __shared__ uint16_t s_flags[kFlagLds];
+  __shared__ uint32_t s_tok[kTokLds];
+  __shared__ uint32_t s_out[kTokLds];
+  __shared__ uint8_t s_cnt8[kPieceTile];
+  __shared__ uint32_t s_list0[kCap0], s_list1[kCap1], s_list2[kCap2];
+  __shared__ uint32_t s_cnt[kChunksPerWg], s_excl[kChunksPerWg];
+  __shared__ uint32_t s_n[3], s_first, s_total, s_doc0;
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63u;
+  if (tid < 3) s_n[tid] = 0;
+  const uint32_t tile = blockIdx.x;
+  const uint64_t base = (uint64_t)tile * kPieceTile;
+  const uint64_t c0 = (uint64_t)tile * kChunksPerWg;
+  const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
+  for (int k = tid; k < kTextLds; k += kPieceThreads) {
+    const uint64_t p = base + k;
+    s_text[k] = p < n ? text[p] : 0;
+  }
+  for (int k = tid; k < kFlagLds; k += kPieceThreads) {
+    const uint64_t c = c0 + k;
+    s_flags[k] = c < n_chunks ? B.flags[c] : 0;
+  }
+  __syncthreads();
+
+  // phase 1: single bytes and whole-piece hits; the rest goes to the lists
+  {
+    const uint32_t lc = tid / kPerChunk, q = tid % kPerChunk;
+    const uint64_t c = c0 + lc;
+    const uint32_t w = c < n_chunks ? s_flags[lc] : 0u;
+    const uint32_t mine = (w >> (kBytesPer * q)) & ((1u << kBytesPer) - 1u);
+    uint32_t hits = 0;
+#pragma unroll
+    for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
+      if (!((mine >> b) & 1u)) continue;
+      const uint32_t bit = kBytesPer * q + b;
+      const uint64_t s = c * kChunk + bit;
+      uint64_t e = ~0ull;
+      const uint32_t above = w & ~((2u << bit) - 1u);
+      if (above) {
+        e = c * kChunk + __builtin_ctz(above);
+      } else {
+        for (uint32_t j = 1; j <= 4; ++j) {
+          const uint32_t wj = s_flags[lc + j];
+          if (wj) {
+            e = (c + j) * kChunk + __builtin_ctz(wj);
+            break;
+          }
+        }
+      }
+      if (e > n) e = n;
+      const uint64_t len = e - s;
+      const uint32_t off = (uint32_t)(s - base);
+      const uint8_t* p = s_text + off;
+      uint32_t id = kNoRank;
+      if (len == 1) id = p[0];
+      else if (len <= (uint64_t)kWordMax && T.word_slots) id = word_lookup(T, p, (uint32_t)len);
+      if (id != kNoRank) {
+        s_tok[off] = id;
+        s_cnt8[off] = 1;
+        ++hits;
+      } else if (len <= (uint64_t)kRowMax) {
+        s_list0[atomicAdd(&s_n[0], 1u)] = off | ((uint32_t)len << 16);
+      } else if (len <= (uint64_t)kWaveMax) {
+        s_list1[atomicAdd(&s_n[1], 1u)] = off | ((uint32_t)len << 16);
+      } else {
+        s_list2[atomicAdd(&s_n[2], 1u)] = off;
+      }
+    }
+#pragma unroll
+    for (int d = 1; d < kPerChunk; d <<= 1) hits += __shfl_xor(hits, d, 64);
+    if (q == 0) s_cnt[lc] = hits;
+  }
+  __syncthreads();
+
+  // phase 2: the waves merge the listed pieces, longest first
+  const uint32_t n0 = __builtin_amdgcn_readfirstlane(s_n[0]);
+  const uint32_t n1 = __builtin_amdgcn_readfirstlane(s_n[1]);
+  const uint32_t n2 = __builtin_amdgcn_readfirstlane(s_n[2]);
+  const uint32_t items = n2 + n1 + (n0 + 3) / 4;
+  for (uint32_t item = __builtin_amdgcn_readfirstlane(tid / kWave); item < items; item += kWaves) {
+    if (item < n2) {
+      const uint32_t off = s_list2[item];
+      merge_long(T, text, n, base + off, B, &s_cnt8[off], &s_cnt[off / kChunk]);
+    } else if (item < n2 + n1) {
+      const uint32_t it = s_list1[item - n2];
+      const uint32_t off = it & 0xFFFFu;
+      merge_rows<64>(T, s_text + off, it >> 16, true, s_tok + off, &s_cnt8[off], &s_cnt[off / kChunk]);
     } else {
-      const uint32_t i = (item - n3 - n2) * 4 + (lane >> 4);
-      const bool act = i < n1;
-      const uint2 it = act ? B.list[0][i] : make_uint2(0u, 0u);
-      merge_rows<16>(T, text, it.x, it.y, act, B);
+      const uint32_t i = (item - n2 - n1) * 4 + (lane >> 4);
+      const bool act = i < n0;
+      const uint32_t it = act ? s_list0[i] : 0u;
+      const uint32_t off = it & 0xFFFFu;
+      merge_rows<16>(T, s_text + off, it >> 16, act, s_tok + off, &s_cnt8[off], &s_cnt[off / kChunk]);
+    }
+  }
+  __syncthreads();
+
+  // phase 3: the tile's tokens as one run from its first piece start
+  if (tid < (uint32_t)kChunksPerWg) {  // wave 0, all lanes
+    const uint32_t v = s_cnt[tid];
+    const uint32_t incl = wave_incl_scan(v, AddOp());
+    s_excl[tid] = incl - v;
+    const uint32_t total = __builtin_amdgcn_readlane((int)incl, 63);
+    const uint64_t has = __ballot(c0 + tid < n_chunks && s_flags[tid] != 0);
+    uint64_t first = base;
+    if (has) {
+      const uint32_t l = (uint32_t)__builtin_ctzll(has);
+      first = base + l * kChunk + __builtin_ctz((uint32_t)__builtin_amdgcn_readlane((int)s_flags[tid], (int)l));
+    }
+    if (tid == 0) {
+      s_total = total;
+      s_first = (uint32_t)first;
+      B.tile_cnt[tile] = total;
+      B.tile_first[tile] = (uint32_t)first;
+    }
+  }
+  if (doc_off && tid == kWave) s_doc0 = first_doc_at_or_after(doc_off, n_docs, base);
+  __syncthreads();
+  const uint32_t total = __builtin_amdgcn_readfirstlane(s_total);
+  const uint64_t first = __builtin_amdgcn_readfirstlane(s_first);
+  int32_t* run = B.staging + first;
+  const bool direct = n2 > 0;  // long pieces' tokens are in global memory: copy straight to the run
+
+  // one thread per chunk walks its pieces in order
+  if (tid < (uint32_t)kChunksPerWg && c0 + tid < n_chunks) {
+    uint32_t w = s_flags[tid];
+    const uint32_t cnt = s_cnt[tid], loc = s_excl[tid];
+    uint32_t done = 0;
+    while (w && done < cnt) {
+      const uint32_t off = tid * kChunk + __builtin_ctz(w);
+      w &= w - 1;
+      const uint32_t k = w ? s_cnt8[off] : cnt - done;  // the chunk's last piece takes the rest
+      const bool is_long = s_cnt8[off] == 0;
+      for (uint32_t j = 0; j < k; ++j) {
+        const uint32_t id = is_long ? B.ws_sym[base + off + j] : s_tok[off + j];
+        if (direct) run[loc + done + j] = (int32_t)id;
+        else s_out[loc + done + j] = id;
+      }
+      done += k;
+    }
+  }
+  __syncthreads();
+  if (!direct)
+    for (uint32_t i = tid; i < total; i += kPieceThreads) run[i] = (int32_t)s_out[i];
+
+  // offsets, within this tile's run, of the documents that start in the tile
+  if (doc_off) {
+    for (uint32_t d = s_doc0 + tid; d <= n_docs; d += kPieceThreads) {
+      const uint64_t p = doc_off[d];
+      if (p >= n || p >= base + kPieceTile) break;
+      const uint32_t off = (uint32_t)(p - base), lc = off / kChunk;
+      uint32_t before = s_flags[lc] & ((1u << (off % kChunk)) - 1u);
+      uint32_t loc = s_excl[lc];
+      while (before) {
+        loc += s_cnt8[lc * kChunk + __builtin_ctz(before)];
+        before &= before - 1;
+      }
+      out_off[d] = loc;
     }
   }
 }
 
 }  // namespace
 
-void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, hipStream_t s) {
+void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, const uint64_t* doc_off,
+                   uint32_t n_docs, uint64_t* out_off, hipStream_t s) {
   const uint32_t blocks = (uint32_t)((n + kPieceTile - 1) / kPieceTile);
-  if (blocks) piece_kernel<<<blocks, kThreads, 0, s>>>(text, n, t, b);
-}
-
-void launch_merge(const uint8_t* text, uint64_t n, Tables t, Bufs b, hipStream_t s) {
-  if (!n) return;
-  uint64_t blocks = (n + 1023) / 1024;
-  if (blocks < 16) blocks = 16;
-  if (blocks > 2048) blocks = 2048;
-  merge_kernel<<<(uint32_t)blocks, kThreads, 0, s>>>(text, n, t, b);
+  if (blocks) piece_kernel<<<blocks, kPieceThreads, 0, s>>>(text, n, t, b, doc_off, n_docs, out_off);
 }
 
 }  // namespace tok

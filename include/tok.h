@@ -187,10 +187,10 @@ size_t tok_token_lengths(const tok_ctx* ctx, uint32_t* len_out, size_t n);
  * Stage timing (GraphTok, section 7, per-stage profile).  With profiling on,
  * every call records HIP events around each device stage on the stream it
  * runs on; tok_stage_ms returns the last call's stage durations in ms:
- * [0] counter reset, [1] pre-tokenization, [2] piece pass (single bytes and
- * whole-piece hits), [3] merge rounds of the remaining pieces, [4] count scan +
- * scatter, [5] document offsets.  Returns the number of
- * stages written (at most n).
+ * [0] counter reset, [1] pre-tokenization, [2] piece pass (single bytes,
+ * whole-piece hits, merge rounds of the remaining pieces, one run of IDs per
+ * 1 KiB tile), [3] assembly (output offsets of the runs and their copy).
+ * Returns the number of stages written (at most n).
  */
 int tok_set_profiling(tok_ctx* ctx, int on);
 int tok_stage_ms(const tok_ctx* ctx, float* ms, int n);
