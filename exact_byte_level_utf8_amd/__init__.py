@@ -199,7 +199,7 @@ class Tokenizer:
         return list(out[:k])
 
 
-STAGES = ("reset", "pretokenize", "pieces", "assemble")
+STAGES = ("pretokenize", "pieces", "assemble")
 
 
 def flags_to_starts(flags: np.ndarray, n: int) -> np.ndarray:

@@ -5,12 +5,14 @@
 // section 5 "Runtime and asset loading" and "Device representation": the
 // host resolves every merge to token IDs and builds open-addressed device
 // tables at context construction).  Every encode call enqueues the whole
-// pipeline on one stream: counter reset -> pre-tokenization -> piece BPE ->
-// long-piece BPE -> count scan + scatter (-> document offsets), then reads the
-// 16-byte counter block back with the one synchronization of the call
-// (TokTier, "Exact GPU Tokenization": counts stay on the device and host
-// synchronizations drop to two per request; the host path adds one more for
-// the ID copy).
+// pipeline on one stream: pre-tokenization -> piece pass (whole-piece hits and
+// merge rounds, one run of IDs per tile) -> assembly (output offsets, copy,
+// document offsets).  The kernels write the call's results (total, error
+// reports) straight into a pinned, device-mapped counter block, so the call
+// needs one stream synchronization and no copy to learn its count (TokTier,
+// "Exact GPU Tokenization": counts stay on the device and host
+// synchronizations drop to a minimum per request; the host path adds one more
+// for the ID copy).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -64,7 +66,7 @@ void hfree(T*& p) {
   p = nullptr;
 }
 
-constexpr int kStages = 4;
+constexpr int kStages = 3;
 
 }  // namespace
 
@@ -88,7 +90,8 @@ struct tok_ctx {
   // scratch, grown on demand
   uint64_t cap = 0;  // input bytes the scratch covers
   Bufs b{};
-  Counters* d_ctr = nullptr;
+  Counters* d_ctr = nullptr;  // device address of h_ctr
+  uint64_t gen = 0;           // number of the last call
   uint8_t* d_text = nullptr;  // staging for host-memory calls
   int32_t* d_ids = nullptr;
   uint64_t doc_cap = 0;
@@ -122,10 +125,11 @@ struct tok_ctx {
     dfree(b.staging);
     dfree(b.tile_cnt);
     dfree(b.tile_first);
+    dfree(b.sum1);
+    dfree(b.sum2);
     dfree(b.ws_sym);
     dfree(b.ws_rk);
     dfree(b.ws_sel);
-    dfree(b.scan_state);
     dfree(d_text);
     dfree(d_ids);
     hfree(h_text);
@@ -147,7 +151,8 @@ struct tok_ctx {
         hipMalloc((void**)&b.ws_sym, (c + 64) * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&b.ws_rk, (c + 64) * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&b.ws_sel, (c + 64) * sizeof(uint64_t)) != hipSuccess ||
-        hipMalloc((void**)&b.scan_state, tiles * sizeof(unsigned long long)) != hipSuccess ||
+        hipMalloc((void**)&b.sum1, ((tiles >> kSum1Shift) + 1) * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc((void**)&b.sum2, ((tiles >> kSum2Shift) + 1) * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&d_text, c + 64) != hipSuccess ||
         hipMalloc((void**)&d_ids, (c + 64) * sizeof(int32_t)) != hipSuccess ||
         hipHostMalloc((void**)&h_text, c + 64, hipHostMallocDefault) != hipSuccess ||
@@ -192,35 +197,37 @@ struct tok_ctx {
           uint32_t* total) {
     Bufs bb = b;
     if (out_flags) bb.flags = out_flags;
-    const uint32_t tiles = (uint32_t)((n + kPieceTile - 1) / kPieceTile);
+    bb.gen = ++gen;
     const Tables t = tables(words);
     mark(0, s);
-    launch_reset(bb, tiles, doc_off, n_docs, n, out_flags ? nullptr : out_off, s);
-    mark(1, s);
-    launch_pretok(text, n, doc_off, n_docs, pattern, bb, s);
-    mark(2, s);
-    if (!out_flags) {
-      launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s);
-      mark(3, s);
-      launch_assemble(n, bb, out, out_cap, doc_off, n_docs, out_off, s);
-      mark(4, s);
+    if (n == 0) {  // only a batch of empty documents gets here
+      launch_empty_batch(bb, doc_off, n_docs, out_off, s);
+    } else {
+      launch_pretok(text, n, doc_off, n_docs, pattern, bb, s);
+      mark(1, s);
+      if (!out_flags) {
+        launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s);
+        mark(2, s);
+        launch_assemble(n, bb, out, out_cap, doc_off, n_docs, out_off, s);
+        mark(3, s);
+      }
     }
     HIP_OK(hipGetLastError());
-    HIP_OK(hipMemcpyAsync(h_ctr, d_ctr, sizeof(Counters), hipMemcpyDeviceToHost, s));
     HIP_OK(hipStreamSynchronize(s));
     if (prof) {
-      const int last = out_flags ? 2 : kStages;  // pre-tokenization only: two stages
+      const int last = n == 0 ? 0 : out_flags ? 1 : kStages;
       for (int i = 0; i < kStages; ++i) {
         float ms = 0.f;
         if (i < last && hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) ms = 0.f;
         stage_ms[i] = i < last ? ms : 0.f;
       }
     }
-    const uint32_t st = h_ctr->status;
-    if (st & kStDocOff) return TOK_E_ARG;
-    if (st & kStUtf8) return TOK_E_UTF8;
-    if (st & kStSpin) return TOK_E_DEVICE;
-    if (total) *total = h_ctr->total;
+    const volatile Counters* c = h_ctr;
+    if (c->err_docs == bb.gen) return TOK_E_ARG;
+    if (c->err_utf8 == bb.gen) return TOK_E_UTF8;
+    if (out_flags) return TOK_OK;
+    if (c->done != bb.gen) return TOK_E_DEVICE;
+    if (total) *total = c->total;
     return TOK_OK;
   }
 
@@ -232,16 +239,20 @@ struct tok_ctx {
     if (rc) return rc;
     HIP_OK(hipMemcpyAsync(d_text, h_bytes, n, hipMemcpyHostToDevice, stream));
     HIP_OK(hipMemcpyAsync(b.flags, flags.data(), flags.size() * 2, hipMemcpyHostToDevice, stream));
+    Bufs bb = b;
+    bb.gen = ++gen;
     const uint32_t tiles = (uint32_t)((n + kPieceTile - 1) / kPieceTile);
+    std::vector<uint32_t> zero((tiles >> kSum1Shift) + 1, 0);  // group sums start at zero
+    HIP_OK(hipMemcpyAsync(bb.sum1, zero.data(), zero.size() * 4, hipMemcpyHostToDevice, stream));
+    HIP_OK(hipMemcpyAsync(bb.sum2, zero.data(), ((tiles >> kSum2Shift) + 1) * 4, hipMemcpyHostToDevice, stream));
     const Tables t = tables(false);
-    launch_reset(b, tiles, nullptr, 0, n, nullptr, stream);
-    launch_pieces(d_text, n, t, b, nullptr, 0, nullptr, stream);
-    launch_assemble(n, b, d_ids, n, nullptr, 0, nullptr, stream);
+    launch_pieces(d_text, n, t, bb, nullptr, 0, nullptr, stream);
+    launch_assemble(n, bb, d_ids, n, nullptr, 0, nullptr, stream);
     HIP_OK(hipGetLastError());
-    HIP_OK(hipMemcpyAsync(h_ctr, d_ctr, sizeof(Counters), hipMemcpyDeviceToHost, stream));
     HIP_OK(hipStreamSynchronize(stream));
-    if (h_ctr->status) return TOK_E_DEVICE;
-    ids.resize(h_ctr->total);
+    const volatile Counters* c = h_ctr;
+    if (c->done != bb.gen) return TOK_E_DEVICE;
+    ids.resize(c->total);
     HIP_OK(hipMemcpy(ids.data(), d_ids, ids.size() * 4, hipMemcpyDeviceToHost));
     return TOK_OK;
   }
@@ -253,7 +264,6 @@ struct tok_ctx {
     dfree(d_pair_rank);
     dfree(d_word_slots);
     dfree(d_tok_len);
-    dfree(d_ctr);
     dfree(d_doc);
     dfree(d_outoff);
     hfree(h_doc);
@@ -415,8 +425,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
     if (hipMalloc((void**)&ctx->d_merge_slots, slots * 8) != hipSuccess ||
         hipMalloc((void**)&ctx->d_pair_rank, pr.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_tok_len, ctx->tok_len.size() * 4) != hipSuccess ||
-        hipMalloc((void**)&ctx->d_ctr, sizeof(Counters)) != hipSuccess ||
-        hipHostMalloc((void**)&ctx->h_ctr, sizeof(Counters), hipHostMallocDefault) != hipSuccess) {
+        hipHostMalloc((void**)&ctx->h_ctr, sizeof(Counters), hipHostMallocMapped) != hipSuccess) {
       rc = TOK_E_NOMEM;
       break;
     }
@@ -424,8 +433,10 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
         hipMemcpy(ctx->d_pair_rank, pr.data(), pr.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(ctx->d_tok_len, ctx->tok_len.data(), ctx->tok_len.size() * 4, hipMemcpyHostToDevice) !=
             hipSuccess ||
-        hipMemset(ctx->d_ctr, 0, sizeof(Counters)) != hipSuccess)
+        hipHostGetDevicePointer((void**)&ctx->d_ctr, ctx->h_ctr, 0) != hipSuccess)
       break;
+    std::memset(ctx->h_ctr, 0, sizeof(Counters));
+    ctx->b.ctr = ctx->d_ctr;
     ctx->merge_buckets = bmask;
     rc = build_word_table(ctx, tok);
   } while (false);

@@ -24,7 +24,8 @@
 //      every other pair of a chain).  Pieces longer than 64 bytes run the same
 //      rounds over arrays in global memory.
 //   3. The tile's tokens are compacted in order (in LDS) and written as one
-//      run from the tile's first piece start, with the tile's count; the
+//      run from the tile's first piece start, with the tile's count, which is
+//      also added to the sums of its groups of 64 and 4096 tiles; the
 //      documents that start in the tile get their offsets within that run.
 //      The assembly kernel then places the runs (k_assemble.hip).
 #include "tok_internal.h"
@@ -381,6 +382,8 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
       s_first = (uint32_t)first;
       B.tile_cnt[tile] = total;
       B.tile_first[tile] = (uint32_t)first;
+      atomicAdd(&B.sum1[tile >> kSum1Shift], total);
+      atomicAdd(&B.sum2[tile >> kSum2Shift], total);
     }
   }
   if (doc_off && tid == kWave) s_doc0 = first_doc_at_or_after(doc_off, n_docs, base);
@@ -417,6 +420,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
     for (uint32_t d = s_doc0 + tid; d <= n_docs; d += kPieceThreads) {
       const uint64_t p = doc_off[d];
       if (p >= n || p >= base + kPieceTile) break;
+      if (p < base) continue;  // only with unordered offsets, which the call rejects
       const uint32_t off = (uint32_t)(p - base), lc = off / kChunk;
       uint32_t before = s_flags[lc] & ((1u << (off % kChunk)) - 1u);
       uint32_t loc = s_excl[lc];

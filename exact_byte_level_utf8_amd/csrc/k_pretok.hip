@@ -124,7 +124,7 @@ __device__ inline uint32_t info_at(const uint32_t* info, int k) { return k < 0 ?
 template <int PATTERN>
 __global__ void __launch_bounds__(kThreads)
 pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off,
-              uint32_t n_docs, uint16_t* __restrict__ flags, Counters* __restrict__ ctr) {
+              uint32_t n_docs, Bufs B) {
   __shared__ uint8_t s_raw[kWin + 4];
   __shared__ uint8_t s_fl[kWin + 4];
   __shared__ uint32_t s_info[kWin];
@@ -133,6 +133,21 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
   const int64_t base = (int64_t)blockIdx.x * kPT;
+  uint16_t* __restrict__ flags = B.flags;
+  // per-call set-up for the later passes: clear the group sums of the tile
+  // counts, and check the batch's document offsets
+  if (tid == 0) {
+    const uint32_t tiles = gridDim.x;
+    if (blockIdx.x < ((tiles + 63u) >> kSum1Shift)) B.sum1[blockIdx.x] = 0;
+    if (blockIdx.x < ((tiles + 4095u) >> kSum2Shift)) B.sum2[blockIdx.x] = 0;
+    if (doc_off && blockIdx.x == 0 && (doc_off[0] != 0 || doc_off[n_docs] != n)) report(&B.ctr->err_docs, B.gen);
+  }
+  if (doc_off) {
+    bool bad_doc = false;
+    for (uint32_t d = blockIdx.x * kThreads + tid; d < n_docs; d += gridDim.x * kThreads)
+      bad_doc |= doc_off[d] > doc_off[d + 1];
+    if (bad_doc) report(&B.ctr->err_docs, B.gen);
+  }
   const int64_t lo = base - kHalo;
   const int64_t sn = (int64_t)n;
 
@@ -231,7 +246,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
         bad = true;
     }
   }
-  if (__ballot(bad) && lane == 0) atomicOr(&ctr->status, kStUtf8);
+  if (bad) report(&B.ctr->err_utf8, B.gen);
   __syncthreads();
 
   // Llama-3 style: run-aggregate states before (forward) and after (backward)
@@ -354,9 +369,9 @@ void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uin
   const uint32_t tiles = (uint32_t)((n + kPretokTile - 1) / kPretokTile);
   if (!tiles) return;
   if (pattern == 0)
-    pretok_kernel<0><<<tiles, kThreads, 0, s>>>(text, n, doc_off, n_docs, b.flags, b.ctr);
+    pretok_kernel<0><<<tiles, kThreads, 0, s>>>(text, n, doc_off, n_docs, b);
   else
-    pretok_kernel<1><<<tiles, kThreads, 0, s>>>(text, n, doc_off, n_docs, b.flags, b.ctr);
+    pretok_kernel<1><<<tiles, kThreads, 0, s>>>(text, n, doc_off, n_docs, b);
 }
 
 }  // namespace tok

@@ -8,11 +8,13 @@
 //                              tokens, so the tiles' runs never overlap)
 //   tile_cnt   uint32[G]       IDs of the pieces that start in tile t
 //   tile_first uint32[G]       byte offset of tile t's first piece start
+//   sum1       uint32[G / 64]  tile counts summed over aligned groups of 64 tiles
+//   sum2       uint32[G / 4096] the same over groups of 4096 tiles
 //   ws_sym/rk  uint32[N + 64]  merge workspace of pieces longer than 64 bytes,
 //                              indexed by byte (their final tokens stay there)
 //   ws_sel     uint64[N + 64]  their round selections, indexed by byte
-//   scan_state uint64[G]       decoupled look-back state of the tile counts
-//   ctr        Counters        status and device-side counts
+// and, in pinned host memory mapped into the device, one Counters block that
+// the host reads after its one synchronization of the call.
 // Everything else a tile needs (its bytes, piece lists, tokens, counts) lives
 // in LDS for the lifetime of its workgroup.
 #pragma once
@@ -38,15 +40,24 @@ constexpr uint32_t kBucket = 4;      // hash-table slots probed with one set of 
 // classes
 enum : uint32_t { kL = 0, kN = 1, kW = 2, kO = 3 };
 
-// status bits
-enum : uint32_t { kStUtf8 = 1u, kStSpin = 2u, kStDocOff = 4u };
-
+// Results of a call, written by the kernels into host memory.  Each call has
+// a number (gen, never 0); an error is reported by storing that number, so no
+// word needs clearing between calls and any number of workgroups may report.
 struct Counters {
-  uint32_t status;      // kSt* bits, OR-ed by kernels
-  uint32_t ticket;      // tile ticket of the assembly pass (dispatch order)
-  uint32_t total;       // tokens in the output
+  uint64_t err_utf8;  // gen of the last call that found malformed UTF-8
+  uint64_t err_docs;  // gen of the last call whose document offsets were invalid
+  uint64_t done;      // gen of the last call whose assembly finished
+  uint32_t total;     // tokens in the output of that call
   uint32_t reserved;
 };
+
+// Store a call number into the host-visible counters.
+__device__ inline void report(uint64_t* word, uint64_t gen) {
+  __hip_atomic_store(word, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+constexpr uint32_t kSum1Shift = 6;   // tiles per sum1 group: 64
+constexpr uint32_t kSum2Shift = 12;  // tiles per sum2 group: 4096
 
 // Read-only device tables built by tok_load.
 struct Tables {
@@ -64,11 +75,13 @@ struct Bufs {
   int32_t* staging;
   uint32_t* tile_cnt;
   uint32_t* tile_first;
+  uint32_t* sum1;
+  uint32_t* sum2;
   uint32_t* ws_sym;
   uint32_t* ws_rk;
   uint64_t* ws_sel;
-  unsigned long long* scan_state;
-  Counters* ctr;
+  Counters* ctr;  // device address of the host-mapped counters
+  uint64_t gen;   // this call's number
 };
 
 // Bucket of the merge pair (left, right): multiplicative hashing of the
@@ -97,8 +110,7 @@ __device__ inline uint32_t first_doc_at_or_after(const uint64_t* doc_off, uint32
 }
 
 // Kernel launchers (defined in the .hip files).
-void launch_reset(Bufs b, uint32_t n_tiles, const uint64_t* doc_off, uint32_t n_docs, uint64_t n,
-                  uint64_t* out_off, hipStream_t s);
+void launch_empty_batch(Bufs b, const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s);
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
                    int pattern, Bufs b, hipStream_t s);
 void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, const uint64_t* doc_off,

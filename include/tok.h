@@ -4,11 +4,13 @@
  *
  * One output contract for every call: the returned token IDs equal the full
  * tokenization of the request text under one frozen configuration (TokTier,
- * section 4 "Exactness contract" and Appendix A, Definition A.2; Delta
- * Tokenizer, section 2 "Contract"; GraphTok, section 3 "Exactness requires the
- * complete ordered token sequence").  A call that cannot honour the contract
- * returns an error code and writes no partial answer the caller could mistake
- * for a result: failures cost work, never exactness (TokTier, section 4).
+ * section 5.2 "Exactness" and Appendix A, Definition A.2; Delta Tokenizer, the
+ * contract shared by all of its request paths; GraphTok, section 3
+ * "Background", where exactness means the complete ordered ID sequence).  A
+ * call that cannot honour the contract returns an error code and writes no
+ * partial answer the caller could mistake for a result: a failure costs work,
+ * never exactness (TokTier, section 3, the repair search may miss a boundary
+ * but never accepts a wrong one).
  *
  * Configuration (fixed at tok_load):
  *   - merges: n_merges ordered pairs (left, right) of token IDs, in rank order.
@@ -22,12 +24,15 @@
  *
  * Text is UTF-8.  Malformed input (overlong forms, surrogates, values above
  * U+10FFFF, truncated or stray continuation bytes, a sequence cut by a document
- * boundary) is rejected as a whole with TOK_E_UTF8 (GraphTok, section 6: byte
- * input is validated before any tokenizer semantics apply).
+ * boundary) is rejected as a whole with TOK_E_UTF8: the pages define
+ * tokenization over Unicode text, so a byte string that is not UTF-8 has no
+ * reference result to match.
  *
- * Threading: a context serves one caller at a time (GraphTok, section 5, one
- * context per dispatcher).  Device-pointer calls enqueue their work on the
- * given stream and return after that stream has completed it.
+ * Threading: a context serves one caller at a time (GraphTok, section 5
+ * "Implementation", one context per dispatcher).  Device-pointer calls enqueue
+ * their work on the given stream and return after that stream has completed
+ * it; the call's count and error status come back through pinned host memory
+ * written by the kernels, so a call costs one stream synchronization.
  *
  * Ownership: every pointer argument is owned by the caller and is not retained
  * after the call returns; the context owns all of its device memory.
@@ -78,7 +83,7 @@ typedef struct tok_ctx tok_ctx;
  * Builds, on the device: the (left, right) -> rank open-addressing table, a
  * direct byte-pair rank table, the token byte lengths, and a whole-piece
  * table of vocabulary strings of 2..13 bytes whose own BPE is the single token
- * (the "ignore_merges" shortcut of TokTier, section 4.3, applied only where it
+ * (the whole-vocabulary-hit shortcut of TokTier, section 4 "GPU BPE", applied only where it
  * provably cannot change an ID: each string is checked by running the GPU
  * merge kernels on it once at load).
  *
@@ -124,8 +129,8 @@ int tok_encode_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, int32_t* d_i
 
 /*
  * tok_encode_batch -- encode n_docs independent documents in one pipeline
- * pass (GraphTok, section 5 "Batch entry point"; TokTier, section 4.3,
- * multi-document batches).  Document i is text[doc_off[i] .. doc_off[i+1]);
+ * pass (GraphTok, section 5 "Implementation", the batch entry point; TokTier,
+ * section 4 "GPU BPE", multi-document batches).  Document i is text[doc_off[i] .. doc_off[i+1]);
  * documents are hard boundaries: no piece, code point or token spans two of
  * them; an empty document yields no IDs.
  *
@@ -184,12 +189,13 @@ int tok_get_info(const tok_ctx* ctx, tok_info* info);
 size_t tok_token_lengths(const tok_ctx* ctx, uint32_t* len_out, size_t n);
 
 /*
- * Stage timing (GraphTok, section 7, per-stage profile).  With profiling on,
- * every call records HIP events around each device stage on the stream it
- * runs on; tok_stage_ms returns the last call's stage durations in ms:
- * [0] counter reset, [1] pre-tokenization, [2] piece pass (single bytes,
- * whole-piece hits, merge rounds of the remaining pieces, one run of IDs per
- * 1 KiB tile), [3] assembly (output offsets of the runs and their copy).
+ * Stage timing (GraphTok, section 6.11, the per-stage profile).  With
+ * profiling on, every call records HIP events around each device stage on the
+ * stream it runs on; tok_stage_ms returns the last call's stage durations in
+ * ms: [0] pre-tokenization (with the per-call set-up of the later passes),
+ * [1] piece pass (single bytes, whole-piece hits, merge rounds of the
+ * remaining pieces, one run of IDs per 1 KiB tile), [2] assembly (output
+ * offsets of the runs and their copy).
  * Returns the number of stages written (at most n).
  */
 int tok_set_profiling(tok_ctx* ctx, int on);
