@@ -41,6 +41,9 @@ WORKLOADS = {
                   "llama3", 3, 3_000_000, 1),
     "batch64": ("64 requests x 500K chars, Llama-3-style pattern, 127,744 merges, one batch call",
                 "llama3_128k", "llama3", 40_000, 500_000, 64),
+    # append repair: stored 1M-char context + 1,400-char appends (a latency, not a bench headline)
+    "repair": ("tok_repair: 1M-char stored context + 1,400-char append, GPT-2-style pattern, 50K merges",
+               "gpt2_50k", "gpt2", 2, 1_000_000, 1),
 }
 
 
@@ -58,6 +61,43 @@ def algorithmic_bytes(stage: str, n_bytes: int, n_tokens: int) -> int:
         return n_bytes + flags + 4 * n_tokens
     if stage == "assemble":         # runs in, IDs out
         return 8 * n_tokens
+    return 0
+
+
+def bench_repair(args, desc, merges_name, pattern, seed, n_chars) -> int:
+    """Latency of tok_repair over seeded appends (host text and IDs, one GPU window encode per call)."""
+    import torch
+
+    import exact_byte_level_utf8_amd as tk
+    from synth import textgen
+    from tests import vocab
+
+    torch.cuda.set_device(0)
+    tok = tk.Tokenizer(vocab.merges(merges_name), pattern, device=0)
+    base = textgen.mix_text(seed, n_chars)
+    lat, full, widen = [], 0, 0
+    for i in range(args.warmup + args.steps):
+        old, suf = textgen.repair_case(seed, 70_000 + i, old_text=base, append_chars=1_400)
+        ob, text = old.encode(), (old + suf).encode()
+        sess = tok.encode(ob)
+        s0 = time.perf_counter()
+        ids, info = tok.repair(sess, text, len(ob))
+        dt = time.perf_counter() - s0
+        if i >= args.warmup:
+            lat.append(dt)
+            full += info["full"]
+            widen += info["widenings"]
+    p50 = statistics.median(lat)
+    out = {"metric": "tok_repair latency (ms, P50)", "value": round(1e3 * p50, 4), "unit": "ms", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+           "latency_ms": {"p50": round(1e3 * p50, 4), "p90": round(1e3 * float(np.percentile(lat, 90)), 4),
+                          "p99": round(1e3 * float(np.percentile(lat, 99)), 4)},
+           "full_encodes": full, "widenings": widen, "dtype": "u8->int32",
+           "data": "synthetic (seeded generator; host text and IDs)",
+           "config": {"workload": desc, "context_chars": n_chars, "append_chars": 1400, "merges": merges_name,
+                      "pattern": pattern, "seed": seed}}
+    print(json.dumps(out), flush=True)
+    tok.close()
     return 0
 
 
@@ -85,6 +125,8 @@ def main() -> int:
     from tests import vocab
 
     desc, merges_name, pattern, seed, n_chars, n_docs = WORKLOADS[args.workload]
+    if args.workload == "repair":
+        return bench_repair(args, desc, merges_name, pattern, seed, n_chars)
     t0 = time.time()
     if n_docs == 1:
         text = textgen.mix_text(seed, n_chars).encode()

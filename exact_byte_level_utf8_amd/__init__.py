@@ -24,8 +24,8 @@ TOK_E_CAPACITY, TOK_E_TOOLONG, TOK_E_DEVICE, TOK_E_NOMEM, TOK_E_SESSION = 5, 6, 
 # every function declared in include/tok.h
 EXPORTS = (
     "tok_load", "tok_free", "tok_strerror", "tok_encode", "tok_encode_dev", "tok_encode_batch",
-    "tok_encode_batch_dev", "tok_pretokenize_dev", "tok_get_info", "tok_token_lengths",
-    "tok_set_profiling", "tok_stage_ms",
+    "tok_encode_batch_dev", "tok_pretokenize_dev", "tok_repair", "tok_sync_boundary", "tok_get_info",
+    "tok_token_lengths", "tok_set_profiling", "tok_stage_ms",
 )
 
 
@@ -40,6 +40,11 @@ class TokInfo(ctypes.Structure):
                 ("vocab_size", ctypes.c_uint32), ("max_token_len", ctypes.c_uint32),
                 ("n_whole", ctypes.c_uint32), ("n_not_self", ctypes.c_uint32),
                 ("config_hash", ctypes.c_uint64)]
+
+
+class RepairInfo(ctypes.Structure):
+    _fields_ = [("window_start", ctypes.c_uint64), ("splice_byte", ctypes.c_uint64),
+                ("kept", ctypes.c_uint64), ("widenings", ctypes.c_uint32), ("full", ctypes.c_uint32)]
 
 
 _lib = None
@@ -64,14 +69,16 @@ def lib() -> ctypes.CDLL:
         L.tok_encode_batch.argtypes = [vp, vp, vp, sz, vp, sz, vp]
         L.tok_encode_batch_dev.argtypes = [vp, vp, sz, vp, sz, vp, sz, vp, szp, vp]
         L.tok_pretokenize_dev.argtypes = [vp, vp, sz, vp, sz, vp, vp]
+        L.tok_repair.argtypes = [vp, vp, sz, sz, vp, sz, sz, szp, ctypes.POINTER(RepairInfo)]
+        L.tok_sync_boundary.argtypes = [i32, ctypes.c_uint32, ctypes.c_uint32]
         L.tok_get_info.argtypes = [vp, ctypes.POINTER(TokInfo)]
         L.tok_token_lengths.argtypes = [vp, vp, sz]
         L.tok_token_lengths.restype = sz
         L.tok_set_profiling.argtypes = [vp, i32]
         L.tok_stage_ms.argtypes = [vp, vp, i32]
         for name in ("tok_load", "tok_encode", "tok_encode_dev", "tok_encode_batch",
-                     "tok_encode_batch_dev", "tok_pretokenize_dev", "tok_get_info",
-                     "tok_set_profiling", "tok_stage_ms"):
+                     "tok_encode_batch_dev", "tok_pretokenize_dev", "tok_repair", "tok_sync_boundary",
+                     "tok_get_info", "tok_set_profiling", "tok_stage_ms"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -87,6 +94,12 @@ def _strerror(code: int) -> str:
 def _check(rc: int, what: str) -> None:
     if rc != TOK_OK:
         raise TokError(rc, what)
+
+
+def sync_boundary(pattern: str | int, prev_cp: int, cp: int) -> bool:
+    """tok_sync_boundary: is prev_cp -> cp a synchronizing transition?"""
+    pat = PATTERNS[pattern] if isinstance(pattern, str) else int(pattern)
+    return bool(lib().tok_sync_boundary(pat, prev_cp, cp))
 
 
 def _dev_ptr(t, dtype_name: str, what: str) -> int:
@@ -150,6 +163,28 @@ class Tokenizer:
         _check(lib().tok_encode_batch(self._h, data, off.ctypes.data, n_docs, ids.ctypes.data, ids.size,
                                       out_off.ctypes.data), "tok_encode_batch")
         return ids[: int(out_off[-1])].copy(), out_off
+
+    def repair(self, session_ids, text: bytes, old_len: int) -> tuple[np.ndarray, dict]:
+        """tok_repair: IDs of ``text`` from the IDs of ``text[:old_len]``.
+
+        Returns (ids, info); the input array is not modified (the splice happens
+        in a copy of it).
+        """
+        b = bytes(text)
+        sess = np.asarray(session_ids, dtype=np.int32)
+        cap = sess.size + (len(b) - old_len) + 64
+        while True:
+            buf = np.zeros(max(cap, 1), dtype=np.int32)
+            buf[: sess.size] = sess
+            n = ctypes.c_size_t(0)
+            info = RepairInfo()
+            rc = lib().tok_repair(self._h, buf.ctypes.data, sess.size, buf.size, b, old_len, len(b),
+                                  ctypes.byref(n), ctypes.byref(info))
+            if rc == TOK_E_CAPACITY and n.value > cap:
+                cap = n.value
+                continue
+            _check(rc, "tok_repair")
+            return buf[: n.value].copy(), {f: getattr(info, f) for f, _ in RepairInfo._fields_}
 
     # --------------------------------------------------------- device memory
     def encode_dev(self, d_text, d_ids, length: int | None = None, stream=None) -> int:

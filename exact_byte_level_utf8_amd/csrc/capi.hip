@@ -21,258 +21,9 @@
 #include <new>
 #include <vector>
 
-#include "../../include/tok.h"
-#include "tok_internal.h"
+#include "ctx.h"
 
 using namespace tok;
-
-namespace {
-
-#define HIP_OK(expr)                       \
-  do {                                     \
-    if ((expr) != hipSuccess) {            \
-      (void)hipGetLastError();             \
-      return TOK_E_DEVICE;                 \
-    }                                      \
-  } while (0)
-
-uint64_t next_pow2(uint64_t x) {
-  uint64_t p = 1;
-  while (p < x) p <<= 1;
-  return p;
-}
-
-struct DeviceGuard {
-  int prev = -1;
-  explicit DeviceGuard(int dev) {
-    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
-    if (prev != dev) (void)hipSetDevice(dev);
-  }
-  ~DeviceGuard() {
-    int cur = -1;
-    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
-  }
-};
-
-template <typename T>
-void dfree(T*& p) {
-  if (p) (void)hipFree((void*)p);
-  p = nullptr;
-}
-
-template <typename T>
-void hfree(T*& p) {
-  if (p) (void)hipHostFree((void*)p);
-  p = nullptr;
-}
-
-constexpr int kStages = 3;
-
-}  // namespace
-
-struct tok_ctx {
-  int device = 0;
-  int pattern = 0;
-  uint32_t n_merges = 0;
-  uint32_t max_tok_len = 1;
-  uint32_t n_whole = 0, n_not_self = 0;
-  uint64_t config_hash = 0;
-  std::vector<uint32_t> tok_len;  // host copy
-
-  // device tables
-  uint64_t* d_merge_slots = nullptr;
-  uint32_t merge_buckets = 0;
-  uint32_t* d_pair_rank = nullptr;
-  uint64_t* d_word_slots = nullptr;
-  uint32_t word_buckets = 0;
-  uint32_t* d_tok_len = nullptr;
-
-  // scratch, grown on demand
-  uint64_t cap = 0;  // input bytes the scratch covers
-  Bufs b{};
-  Counters* d_ctr = nullptr;  // device address of h_ctr
-  uint64_t gen = 0;           // number of the last call
-  uint8_t* d_text = nullptr;  // staging for host-memory calls
-  int32_t* d_ids = nullptr;
-  uint64_t doc_cap = 0;
-  uint64_t* d_doc = nullptr;
-  uint64_t* d_outoff = nullptr;
-
-  // pinned host memory
-  uint8_t* h_text = nullptr;
-  int32_t* h_ids = nullptr;
-  uint64_t* h_doc = nullptr;
-  Counters* h_ctr = nullptr;
-
-  hipStream_t stream = nullptr;
-  bool prof = false;
-  hipEvent_t ev[kStages + 1] = {};
-  float stage_ms[kStages] = {};
-
-  Tables tables(bool words = true) const {
-    Tables t{};
-    t.merge_slots = d_merge_slots;
-    t.merge_buckets = merge_buckets;
-    t.pair_rank = d_pair_rank;
-    t.word_slots = words ? d_word_slots : nullptr;
-    t.word_buckets = words ? word_buckets : 0;
-    t.tok_len = d_tok_len;
-    return t;
-  }
-
-  void free_scratch() {
-    dfree(b.flags);
-    dfree(b.staging);
-    dfree(b.tile_cnt);
-    dfree(b.tile_first);
-    dfree(b.sum1);
-    dfree(b.sum2);
-    dfree(b.ws_sym);
-    dfree(b.ws_rk);
-    dfree(b.ws_sel);
-    dfree(d_text);
-    dfree(d_ids);
-    hfree(h_text);
-    hfree(h_ids);
-    cap = 0;
-  }
-
-  // Make the scratch cover n input bytes (capacity grows in powers of two).
-  int ensure(uint64_t n) {
-    if (n <= cap && b.flags) return TOK_OK;
-    (void)hipStreamSynchronize(stream);
-    free_scratch();
-    const uint64_t c = std::max<uint64_t>(next_pow2(n), 1u << 16);
-    const uint64_t chunks = c / kChunk, tiles = c / kPieceTile;
-    if (hipMalloc((void**)&b.flags, (chunks + 8) * sizeof(uint16_t)) != hipSuccess ||
-        hipMalloc((void**)&b.staging, (c + 64) * sizeof(int32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.tile_cnt, tiles * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.tile_first, tiles * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.ws_sym, (c + 64) * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.ws_rk, (c + 64) * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.ws_sel, (c + 64) * sizeof(uint64_t)) != hipSuccess ||
-        hipMalloc((void**)&b.sum1, ((tiles >> kSum1Shift) + 1) * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.sum2, ((tiles >> kSum2Shift) + 1) * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&d_text, c + 64) != hipSuccess ||
-        hipMalloc((void**)&d_ids, (c + 64) * sizeof(int32_t)) != hipSuccess ||
-        hipHostMalloc((void**)&h_text, c + 64, hipHostMallocDefault) != hipSuccess ||
-        hipHostMalloc((void**)&h_ids, (c + 64) * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
-      (void)hipGetLastError();
-      free_scratch();
-      return TOK_E_NOMEM;
-    }
-    b.ctr = d_ctr;
-    cap = c;
-    return TOK_OK;
-  }
-
-  int ensure_docs(uint64_t n_docs) {
-    if (n_docs + 1 <= doc_cap && d_doc) return TOK_OK;
-    (void)hipStreamSynchronize(stream);
-    dfree(d_doc);
-    dfree(d_outoff);
-    hfree(h_doc);
-    const uint64_t c = std::max<uint64_t>(next_pow2(n_docs + 1), 64);
-    if (hipMalloc((void**)&d_doc, c * 8) != hipSuccess || hipMalloc((void**)&d_outoff, c * 8) != hipSuccess ||
-        hipHostMalloc((void**)&h_doc, c * 8, hipHostMallocDefault) != hipSuccess) {
-      (void)hipGetLastError();
-      dfree(d_doc);
-      dfree(d_outoff);
-      hfree(h_doc);
-      doc_cap = 0;
-      return TOK_E_NOMEM;
-    }
-    doc_cap = c;
-    return TOK_OK;
-  }
-
-  void mark(int i, hipStream_t s) {
-    if (prof) (void)hipEventRecord(ev[i], s);
-  }
-
-  // Enqueue the pipeline over d_text[0..n) and wait for it.  out_flags: stop
-  // after pre-tokenization, with the flag words written there.
-  int run(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, int32_t* out,
-          uint64_t out_cap, uint64_t* out_off, hipStream_t s, bool words, uint16_t* out_flags,
-          uint32_t* total) {
-    Bufs bb = b;
-    if (out_flags) bb.flags = out_flags;
-    bb.gen = ++gen;
-    const Tables t = tables(words);
-    mark(0, s);
-    if (n == 0) {  // only a batch of empty documents gets here
-      launch_empty_batch(bb, doc_off, n_docs, out_off, s);
-    } else {
-      launch_pretok(text, n, doc_off, n_docs, pattern, bb, s);
-      mark(1, s);
-      if (!out_flags) {
-        launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s);
-        mark(2, s);
-        launch_assemble(n, bb, out, out_cap, doc_off, n_docs, out_off, s);
-        mark(3, s);
-      }
-    }
-    HIP_OK(hipGetLastError());
-    HIP_OK(hipStreamSynchronize(s));
-    if (prof) {
-      const int last = n == 0 ? 0 : out_flags ? 1 : kStages;
-      for (int i = 0; i < kStages; ++i) {
-        float ms = 0.f;
-        if (i < last && hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) ms = 0.f;
-        stage_ms[i] = i < last ? ms : 0.f;
-      }
-    }
-    const volatile Counters* c = h_ctr;
-    if (c->err_docs == bb.gen) return TOK_E_ARG;
-    if (c->err_utf8 == bb.gen) return TOK_E_UTF8;
-    if (out_flags) return TOK_OK;
-    if (c->done != bb.gen) return TOK_E_DEVICE;
-    if (total) *total = c->total;
-    return TOK_OK;
-  }
-
-  // Run only the merge stages over pieces given by host-built flag words (the
-  // load-time self-encoding check of vocabulary strings).
-  int run_pieces(const uint8_t* h_bytes, uint64_t n, const std::vector<uint16_t>& flags,
-                 std::vector<int32_t>& ids) {
-    int rc = ensure(n);
-    if (rc) return rc;
-    HIP_OK(hipMemcpyAsync(d_text, h_bytes, n, hipMemcpyHostToDevice, stream));
-    HIP_OK(hipMemcpyAsync(b.flags, flags.data(), flags.size() * 2, hipMemcpyHostToDevice, stream));
-    Bufs bb = b;
-    bb.gen = ++gen;
-    const uint32_t tiles = (uint32_t)((n + kPieceTile - 1) / kPieceTile);
-    std::vector<uint32_t> zero((tiles >> kSum1Shift) + 1, 0);  // group sums start at zero
-    HIP_OK(hipMemcpyAsync(bb.sum1, zero.data(), zero.size() * 4, hipMemcpyHostToDevice, stream));
-    HIP_OK(hipMemcpyAsync(bb.sum2, zero.data(), ((tiles >> kSum2Shift) + 1) * 4, hipMemcpyHostToDevice, stream));
-    const Tables t = tables(false);
-    launch_pieces(d_text, n, t, bb, nullptr, 0, nullptr, stream);
-    launch_assemble(n, bb, d_ids, n, nullptr, 0, nullptr, stream);
-    HIP_OK(hipGetLastError());
-    HIP_OK(hipStreamSynchronize(stream));
-    const volatile Counters* c = h_ctr;
-    if (c->done != bb.gen) return TOK_E_DEVICE;
-    ids.resize(c->total);
-    HIP_OK(hipMemcpy(ids.data(), d_ids, ids.size() * 4, hipMemcpyDeviceToHost));
-    return TOK_OK;
-  }
-
-  ~tok_ctx() {
-    if (stream) (void)hipStreamSynchronize(stream);
-    free_scratch();
-    dfree(d_merge_slots);
-    dfree(d_pair_rank);
-    dfree(d_word_slots);
-    dfree(d_tok_len);
-    dfree(d_doc);
-    dfree(d_outoff);
-    hfree(h_doc);
-    hfree(h_ctr);
-    for (auto& e : ev)
-      if (e) (void)hipEventDestroy(e);
-    if (stream) (void)hipStreamDestroy(stream);
-  }
-};
 
 namespace {
 
@@ -400,10 +151,15 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
   ctx->pattern = pattern;
   ctx->n_merges = (uint32_t)n_merges;
   ctx->tok_len.resize(tok.size());
+  ctx->tok_off.resize(tok.size() + 1);
+  ctx->tok_off[0] = 0;
   for (size_t i = 0; i < tok.size(); ++i) {
     ctx->tok_len[i] = (uint32_t)tok[i].size();
     ctx->max_tok_len = std::max(ctx->max_tok_len, ctx->tok_len[i]);
+    ctx->tok_off[i + 1] = ctx->tok_off[i] + tok[i].size();
   }
+  ctx->tok_bytes.reserve(ctx->tok_off.back());
+  for (const auto& t : tok) ctx->tok_bytes.insert(ctx->tok_bytes.end(), t.begin(), t.end());
   uint64_t h = 0xCBF29CE484222325ull;  // FNV-1a over pattern and merges
   auto fnv = [&](const void* p, size_t n) {
     const uint8_t* c = (const uint8_t*)p;

@@ -1,0 +1,253 @@
+// Append repair: tok_repair, and its splice certificate tok_sync_boundary.
+//
+// A session keeps the IDs of its text A.  When text B is appended, only a
+// window at the seam is encoded again: the last w code points of A plus B
+// (TokTier, section 3, windowed repair; Delta Tokenizer, reference-identical
+// tokenization of session deltas).  The fresh records (byte offset, ID) of the
+// window are matched against the stored records; a run of equal records is
+// accepted if it contains a stable pre-tokenization boundary, and the result
+// is the stored IDs up to the end of that run followed by the fresh IDs after
+// it (TokTier, Appendix A: Definition A.4 splice certificate, Theorem A.5,
+// Corollary A.6 -- splicing at the end of the equal run is interchangeable
+// with splicing at the boundary inside it).  If no run qualifies the window
+// doubles, at most five times, and then the whole text is encoded.  A miss
+// costs work, never a different ID.
+//
+// The stable boundary used here is a synchronizing transition: a byte b where
+// the class changes between the code point x before b and y at b such that,
+// for every left context, the pieces from b on are the pieces of the text
+// from b alone, b starts a piece, and the pieces before b do not depend on
+// anything after y.  Then the stored pieces before b are those of A + B, and
+// the window's pieces from b on are those of A + B.  The sets below follow
+// from the two pattern families (they list exactly the transitions where a
+// character before b can join the piece at b, or the piece before b can take
+// characters from b on); tests derive them independently by brute force from
+// the CPU oracle's matcher.
+//
+//   GPT-2 style: every class change, except after U+0020 (the optional space
+//   joins the next run) and apostrophe -> s t r v m l d (a contraction may
+//   begin there; the match is case-sensitive).
+//   Llama-3 style: every class change, except whitespace -> letter unless the
+//   whitespace is CR or LF (one non-CR/LF char prefixes a letter run),
+//   U+0020 -> other (the optional space), other -> letter (one other char
+//   prefixes a letter run, or a contraction), and other -> CR/LF (the other
+//   piece takes trailing CR/LF).
+//
+// Work per call is O(w + |B|): the stored IDs are walked back from the end
+// through the token byte lengths, never from the start of the session.
+#include "ctx.h"
+#include "pretok_rules.h"
+
+namespace {
+
+#define TOK_CLS_QUAL static
+#include "uniclass.inc"
+#undef TOK_CLS_QUAL
+
+uint32_t host_class(uint32_t cp) {
+  if (cp < 0x80) return ascii_class(cp);
+  if (cp < 0x10000) return (kClsBmp[cp >> 2] >> (2 * (cp & 3u))) & 3u;
+  if (cp >= 0x110000) return kO;
+  const uint32_t blk = kClsBlock[cp >> 8];
+  return (kClsBits[blk * 64 + ((cp & 255u) >> 2)] >> (2 * (cp & 3u))) & 3u;
+}
+
+bool is_cont(uint8_t b) { return (b & 0xC0) == 0x80; }
+
+// Code point whose lead byte is t[i] (the text is valid UTF-8 around i).
+uint32_t cp_at(const uint8_t* t, uint64_t n, uint64_t i) {
+  const uint32_t b0 = t[i];
+  if (b0 < 0x80) return b0;
+  const uint32_t len = b0 >= 0xF0 ? 4 : b0 >= 0xE0 ? 3 : 2;
+  uint32_t cp = b0 & (0x7Fu >> len);
+  for (uint32_t k = 1; k < len && i + k < n; ++k) cp = (cp << 6) | (t[i + k] & 0x3Fu);
+  return cp;
+}
+
+// Lead byte of the code point that ends just before byte i (i > 0).
+uint64_t prev_lead(const uint8_t* t, uint64_t i) {
+  uint64_t j = i - 1;
+  while (j > 0 && is_cont(t[j])) --j;
+  return j;
+}
+
+// Byte offset of the w-th code point before byte `end` (0 if there are fewer).
+uint64_t back_code_points(const uint8_t* t, uint64_t end, uint64_t w) {
+  uint64_t i = end, seen = 0;
+  while (i > 0 && seen < w) {
+    --i;
+    if (!is_cont(t[i])) ++seen;
+  }
+  return i;
+}
+
+// Byte offset of the code point that lies w code points after byte `start`
+// (`end` if there are fewer).
+uint64_t fwd_code_points(const uint8_t* t, uint64_t start, uint64_t end, uint64_t w) {
+  uint64_t i = start, seen = 0;
+  while (i < end) {
+    if (!is_cont(t[i])) {
+      if (seen == w) return i;
+      ++seen;
+    }
+    ++i;
+  }
+  return end;
+}
+
+bool sync_transition(int pattern, uint32_t x, uint32_t y) {
+  const uint32_t cx = host_class(x), cy = host_class(y);
+  if (cx == cy) return false;
+  const bool x_crlf = x == 0x0D || x == 0x0A, y_crlf = y == 0x0D || y == 0x0A;
+  if (pattern == TOK_PAT_GPT2) {
+    if (x == 0x20) return false;
+    // apostrophe before a letter that can begin a (case-sensitive) contraction
+    if (x == 0x27 && (y == 's' || y == 't' || y == 'r' || y == 'v' || y == 'm' || y == 'l' || y == 'd'))
+      return false;
+    return true;
+  }
+  if (cx == kW && cy == kL && !x_crlf) return false;
+  if (x == 0x20 && cy == kO) return false;
+  if (cx == kO && cy == kL) return false;
+  if (cx == kO && y_crlf) return false;
+  return true;
+}
+
+struct Rec {
+  uint64_t off;  // byte offset of the token in the text
+  size_t idx;    // index in its sequence (session or window)
+  int32_t id;
+};
+
+constexpr uint64_t kFirstWindow = 512;  // code points
+constexpr uint32_t kMaxWidenings = 5;
+constexpr uint64_t kMarginCodePoints = 8;
+
+}  // namespace
+
+extern "C" {
+
+int tok_sync_boundary(int pattern, uint32_t prev_cp, uint32_t cp) {
+  if (pattern != TOK_PAT_GPT2 && pattern != TOK_PAT_LLAMA3) return 0;
+  return sync_transition(pattern, prev_cp, cp) ? 1 : 0;
+}
+
+int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap, const uint8_t* text,
+               size_t old_len, size_t new_len, size_t* n_out, tok_repair_info* info) {
+  if (!ctx || !n_out || (!text && new_len) || (!session_ids && (cap || n_session)) || old_len > new_len ||
+      n_session > cap)
+    return TOK_E_ARG;
+  *n_out = 0;
+  tok_repair_info scratch{};
+  tok_repair_info& inf = info ? *info : scratch;
+  inf = tok_repair_info{};
+  if (new_len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
+  if ((old_len == 0) != (n_session == 0)) return TOK_E_SESSION;
+  if (new_len == old_len) {  // nothing appended: the stored IDs are the answer
+    *n_out = n_session;
+    inf.kept = n_session;
+    inf.splice_byte = old_len;
+    return TOK_OK;
+  }
+
+  // stored records, walked back from the end of the session as far as needed
+  std::vector<Rec> stored;  // in reverse order of offset
+  uint64_t pos = old_len;
+  size_t j = n_session;
+  const size_t vocab = ctx->tok_len.size();
+  auto walk_to = [&](uint64_t target) -> int {
+    while (pos > target && j > 0) {
+      const int32_t id = session_ids[j - 1];
+      if (id < 0 || (size_t)id >= vocab) return TOK_E_SESSION;
+      const uint32_t L = ctx->tok_len[(size_t)id];
+      if (L > pos) return TOK_E_SESSION;
+      pos -= L;
+      --j;
+      if (std::memcmp(&ctx->tok_bytes[ctx->tok_off[(size_t)id]], text + pos, L) != 0) return TOK_E_SESSION;
+      stored.push_back(Rec{pos, j, id});
+    }
+    return pos > target ? TOK_E_SESSION : TOK_OK;  // the IDs must cover the stored text
+  };
+
+  std::vector<int32_t> fresh;
+  uint64_t w = kFirstWindow;
+  for (uint32_t widen = 0; widen <= kMaxWidenings; ++widen, w *= 2) {
+    inf.widenings = widen;
+    const uint64_t ws = back_code_points(text, old_len, w);
+    if (ws == 0) break;  // the window would be the whole text
+    int rc = walk_to(ws);
+    if (rc) return rc;
+    const uint64_t wlen = new_len - ws;
+    fresh.resize(wlen);
+    size_t nf = 0;
+    rc = tok_encode(ctx, text + ws, wlen, fresh.data(), wlen, &nf);
+    if (rc) return rc;
+    const uint64_t margin = fwd_code_points(text, ws, new_len, kMarginCodePoints);
+
+    // match stored records (offset >= ws) against the window's records
+    size_t si = stored.size();  // stored[si - 1] is the first stored record at or after ws
+    while (si > 0 && stored[si - 1].off < ws) --si;
+    uint64_t fo = ws;  // offset of fresh[k]
+    size_t k = 0;
+    bool found = false;
+    size_t keep_s = 0, keep_f = 0;
+    uint64_t splice = 0;
+    while (si > 0 && k < nf) {
+      const Rec& s = stored[si - 1];
+      if (s.off < fo) {
+        --si;
+        continue;
+      }
+      if (fo < s.off) {
+        fo += ctx->tok_len[(size_t)fresh[k++]];
+        continue;
+      }
+      if (s.id != fresh[k]) {
+        --si;
+        fo += ctx->tok_len[(size_t)fresh[k++]];
+        continue;
+      }
+      // an equal run starts here; extend it
+      const uint64_t r0 = s.off;
+      uint64_t r1 = r0;
+      size_t m = 0;
+      bool certified = false;
+      size_t last_s = 0, last_f = 0;
+      while (si > 0 && k < nf && stored[si - 1].off == fo && stored[si - 1].id == fresh[k]) {
+        const uint64_t b = fo;
+        if (b >= margin && b < old_len &&
+            sync_transition(ctx->pattern, cp_at(text, new_len, prev_lead(text, b)), cp_at(text, new_len, b)))
+          certified = true;
+        last_s = stored[si - 1].idx;
+        last_f = k;
+        r1 = fo + ctx->tok_len[(size_t)fresh[k]];
+        fo = r1;
+        ++k;
+        --si;
+        ++m;
+      }
+      const bool gates = m >= 2 && r1 - r0 > ctx->max_tok_len;
+      if (certified && gates) {  // keep the last certified run
+        found = true;
+        keep_s = last_s + 1;
+        keep_f = last_f + 1;
+        splice = r1;
+      }
+    }
+    if (!found) continue;
+    const size_t total = keep_s + (nf - keep_f);
+    *n_out = total;
+    inf.window_start = ws;
+    inf.splice_byte = splice;
+    inf.kept = keep_s;
+    if (total > cap) return TOK_E_CAPACITY;
+    std::memcpy(session_ids + keep_s, fresh.data() + keep_f, (nf - keep_f) * sizeof(int32_t));
+    return TOK_OK;
+  }
+
+  // no certified splice: encode the whole text
+  inf.full = 1;
+  return tok_encode(ctx, text, new_len, session_ids, cap, n_out);
+}
+
+}  // extern "C"

@@ -6,14 +6,14 @@
 // rules and the scan algebra against the oracle's direct matcher on the CPU.
 // Not part of the tokenizer: the library never calls it.
 //
-// Built with g++ (no HIP): __device__ is defined away so that the device class
-// table compiles as ordinary constant arrays.
+// Built with g++ (no HIP): TOK_CLS_QUAL is empty, so the class table compiles
+// as ordinary constant arrays.
 #include <cstddef>
 #include <cstdint>
 #include <vector>
 
 #define TOK_HD
-#define __device__
+#define TOK_CLS_QUAL
 #include "pretok_rules.h"
 #include "uniclass.inc"
 

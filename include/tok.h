@@ -169,6 +169,59 @@ int tok_encode_batch_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
 int tok_pretokenize_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len,
                         const uint64_t* d_doc_off, size_t n_docs, uint16_t* d_flags, void* stream);
 
+/*
+ * tok_repair -- exact encode of a session after an append, from the session's
+ * stored IDs (TokTier, section 3, windowed repair with a splice certificate,
+ * and Appendix A, Definition A.4, Theorem A.5, Corollary A.6; Delta Tokenizer,
+ * reference-identical tokenization of session deltas).
+ *
+ * text:        host bytes text[0 .. new_len): the stored text A =
+ *              text[0 .. old_len) followed by the appended text B.
+ * session_ids: host array of cap int32; on entry session_ids[0 .. n_session)
+ *              must equal the encode of A; on success session_ids[0 .. *n_out)
+ *              equals the encode of A + B, spliced in place (a prefix of the
+ *              stored IDs is left untouched).
+ * info:        optional; receives where the accepted window started, the splice
+ *              byte, the number of stored IDs kept, the window doublings and
+ *              whether the whole text was encoded.
+ *
+ * The last w code points of A plus B are encoded on the device (w = 512,
+ * doubling up to five times); a run of equal (offset, ID) records of the
+ * stored and the fresh encode is accepted if it holds at least two tokens,
+ * spans more bytes than the longest token and contains, at least 8 code points
+ * into the window, a synchronizing transition (tok_sync_boundary); the
+ * result is the stored IDs up to the end of the last such run followed by the
+ * fresh IDs.  Without such a run the whole text is encoded.  Work is O(w +
+ * |B|): the stored IDs are walked back from their end through the token byte
+ * lengths.
+ *
+ * Errors: TOK_E_ARG (null pointers, old_len > new_len, n_session > cap),
+ * TOK_E_TOOLONG, TOK_E_SESSION (the walked-back stored IDs do not spell the
+ * tail of A, or do not cover it, or exactly one of old_len and n_session is
+ * 0), TOK_E_UTF8, TOK_E_CAPACITY (*n_out = required cap; session_ids is
+ * unchanged), TOK_E_DEVICE, TOK_E_NOMEM.
+ */
+typedef struct tok_repair_info {
+  uint64_t window_start;  /* first byte of the accepted window (0 after a full encode) */
+  uint64_t splice_byte;   /* end of the accepted equal run                          */
+  uint64_t kept;          /* stored IDs kept                                        */
+  uint32_t widenings;     /* window doublings done                                  */
+  uint32_t full;          /* 1 if the whole text was encoded                        */
+} tok_repair_info;
+
+int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap, const uint8_t* text,
+               size_t old_len, size_t new_len, size_t* n_out, tok_repair_info* info);
+
+/*
+ * tok_sync_boundary -- 1 if a byte where code point prev_cp is followed by
+ * code point cp is a synchronizing transition of the pattern family: a class
+ * change such that, for any text before it, the pieces from that byte on are
+ * those of the text from that byte alone, and the pieces before it do not
+ * depend on the text after cp (the stable boundary of TokTier, section 3 and
+ * Appendix A).  No context needed; never touches the device.
+ */
+int tok_sync_boundary(int pattern, uint32_t prev_cp, uint32_t cp);
+
 /* Context facts. */
 typedef struct tok_info {
   uint32_t pattern;

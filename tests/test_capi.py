@@ -62,5 +62,7 @@ def test_null_arguments():
     n = ctypes.c_size_t(5)
     assert L.tok_encode(None, None, 0, None, 0, ctypes.byref(n)) == tk.TOK_E_ARG
     assert L.tok_encode_batch(None, None, None, 0, None, 0, None) == tk.TOK_E_ARG
+    assert L.tok_repair(None, None, 0, 0, None, 0, 0, ctypes.byref(n), None) == tk.TOK_E_ARG
+    assert L.tok_sync_boundary(7, 97, 32) == 0  # unknown pattern
     assert L.tok_strerror(tk.TOK_E_UTF8) == b"malformed UTF-8 input"
     L.tok_free(None)
