@@ -27,15 +27,16 @@ using namespace tok;
 
 namespace {
 
-// Build the whole-piece table from the vocabulary strings of 2..13 bytes
-// that the merge kernels encode to their own single token.
+// Build the whole-piece tables from the vocabulary strings of 2..28 bytes
+// that the merge kernels encode to their own single token: 2..13-byte keys in
+// 16-byte slots, 14..28-byte keys in 32-byte slots.
 int build_word_table(tok_ctx* ctx, const std::vector<std::vector<uint8_t>>& tok) {
   std::vector<uint32_t> cand;
   std::vector<uint8_t> blob;
   std::vector<uint16_t> flags;
   for (uint32_t id = 256; id < tok.size(); ++id) {
     const size_t L = tok[id].size();
-    if (L < 2 || L > (size_t)kWordMax) continue;
+    if (L < 2 || L > (size_t)kLongMax) continue;
     const uint64_t pos = blob.size();
     if (flags.size() * kChunk <= pos) flags.resize(pos / kChunk + 1, 0);
     flags[pos / kChunk] |= (uint16_t)(1u << (pos % kChunk));
@@ -47,7 +48,7 @@ int build_word_table(tok_ctx* ctx, const std::vector<std::vector<uint8_t>>& tok)
   std::vector<int32_t> ids;
   int rc = ctx->run_pieces(blob.data(), blob.size(), flags, ids);
   if (rc) return rc;
-  std::vector<uint32_t> self;
+  std::vector<uint32_t> self_short, self_long;
   size_t k = 0;
   for (uint32_t id : cand) {
     const size_t L = tok[id].size();
@@ -58,35 +59,64 @@ int build_word_table(tok_ctx* ctx, const std::vector<std::vector<uint8_t>>& tok)
       ++used;
     }
     if (got != L) return TOK_E_DEVICE;  // token lengths must tile each string
-    if (one && used == 1) self.push_back(id);
+    if (one && used == 1) (L <= (size_t)kWordMax ? self_short : self_long).push_back(id);
   }
-  ctx->n_whole = (uint32_t)self.size();
-  ctx->n_not_self = (uint32_t)(cand.size() - self.size());
-  if (self.empty()) return TOK_OK;
-  const uint64_t slots = std::max<uint64_t>(next_pow2(2 * self.size()), 64);
-  const uint32_t bmask = (uint32_t)(slots / kBucket - 1);
-  std::vector<uint64_t> tab(2 * slots, 0);
-  for (uint32_t id : self) {
-    const auto& s = tok[id];
-    uint64_t a = 0, bb = 0;
-    for (size_t i = 0; i < s.size() && i < 8; ++i) a |= (uint64_t)s[i] << (8 * i);
-    for (size_t i = 8; i < s.size(); ++i) bb |= (uint64_t)s[i] << (8 * (i - 8));
-    bb |= (uint64_t)s.size() << 40;
-    uint32_t h = word_hash(a, bb) & bmask;
-    for (bool placed = false; !placed; h = (h + 1) & bmask) {
-      for (uint32_t j = 0; j < kBucket && !placed; ++j) {
-        const size_t at = ((size_t)h * kBucket + j) * 2;
-        if (tab[at + 1] == 0) {
-          tab[at] = a;
-          tab[at + 1] = bb | ((uint64_t)id << 44);
-          placed = true;
+  ctx->n_whole = (uint32_t)(self_short.size() + self_long.size());
+  ctx->n_not_self = (uint32_t)(cand.size() - ctx->n_whole);
+  auto key_bytes = [&](const std::vector<uint8_t>& s, size_t from, size_t to) {
+    uint64_t v = 0;
+    for (size_t i = from; i < s.size() && i < to; ++i) v |= (uint64_t)s[i] << (8 * (i - from));
+    return v;
+  };
+  if (!self_short.empty()) {
+    const uint64_t slots = std::max<uint64_t>(next_pow2(2 * self_short.size()), 64);
+    const uint32_t bmask = (uint32_t)(slots / kBucket - 1);
+    std::vector<uint64_t> tab(2 * slots, 0);
+    for (uint32_t id : self_short) {
+      const auto& s = tok[id];
+      const uint64_t a = key_bytes(s, 0, 8), bb = key_bytes(s, 8, 13) | ((uint64_t)s.size() << 40);
+      uint32_t h = word_hash(a, bb) & bmask;
+      for (bool placed = false; !placed; h = (h + 1) & bmask) {
+        for (uint32_t j = 0; j < kBucket && !placed; ++j) {
+          const size_t at = ((size_t)h * kBucket + j) * 2;
+          if (tab[at + 1] == 0) {
+            tab[at] = a;
+            tab[at + 1] = bb | ((uint64_t)id << 44);
+            placed = true;
+          }
         }
       }
     }
+    HIP_OK(hipMalloc((void**)&ctx->d_word_slots, tab.size() * 8));
+    HIP_OK(hipMemcpy(ctx->d_word_slots, tab.data(), tab.size() * 8, hipMemcpyHostToDevice));
+    ctx->word_buckets = bmask;
   }
-  HIP_OK(hipMalloc((void**)&ctx->d_word_slots, tab.size() * 8));
-  HIP_OK(hipMemcpy(ctx->d_word_slots, tab.data(), tab.size() * 8, hipMemcpyHostToDevice));
-  ctx->word_buckets = bmask;
+  if (!self_long.empty()) {
+    const uint64_t slots = std::max<uint64_t>(next_pow2(2 * self_long.size()), 64);
+    const uint32_t bmask = (uint32_t)(slots / kBucket - 1);
+    std::vector<uint64_t> tab(4 * slots, 0);
+    for (uint32_t id : self_long) {
+      const auto& s = tok[id];
+      const uint64_t k0 = key_bytes(s, 0, 8), k1 = key_bytes(s, 8, 16), k2 = key_bytes(s, 16, 24);
+      const uint64_t k3 = key_bytes(s, 24, 28) | ((uint64_t)s.size() << 32);
+      uint32_t h = long_hash(k0, k1, k2, k3) & bmask;
+      for (bool placed = false; !placed; h = (h + 1) & bmask) {
+        for (uint32_t j = 0; j < kBucket && !placed; ++j) {
+          const size_t at = ((size_t)h * kBucket + j) * 4;
+          if (tab[at + 3] == 0) {
+            tab[at] = k0;
+            tab[at + 1] = k1;
+            tab[at + 2] = k2;
+            tab[at + 3] = k3 | ((uint64_t)id << 37);
+            placed = true;
+          }
+        }
+      }
+    }
+    HIP_OK(hipMalloc((void**)&ctx->d_long_slots, tab.size() * 8));
+    HIP_OK(hipMemcpy(ctx->d_long_slots, tab.data(), tab.size() * 8, hipMemcpyHostToDevice));
+    ctx->long_buckets = bmask;
+  }
   return TOK_OK;
 }
 

@@ -10,7 +10,7 @@
 #include <cstring>
 #include <vector>
 
-#include "../../include/tok.h"
+#include "tok.h"
 #include "tok_internal.h"
 
 using namespace tok;  // internal header of the library's host sources only
@@ -72,6 +72,8 @@ struct tok_ctx {
   uint32_t* d_pair_rank = nullptr;
   uint64_t* d_word_slots = nullptr;
   uint32_t word_buckets = 0;
+  uint64_t* d_long_slots = nullptr;
+  uint32_t long_buckets = 0;
   uint32_t* d_tok_len = nullptr;
 
   // scratch, grown on demand
@@ -103,6 +105,8 @@ struct tok_ctx {
     t.pair_rank = d_pair_rank;
     t.word_slots = words ? d_word_slots : nullptr;
     t.word_buckets = words ? word_buckets : 0;
+    t.long_slots = words ? d_long_slots : nullptr;
+    t.long_buckets = words ? long_buckets : 0;
     t.tok_len = d_tok_len;
     return t;
   }
@@ -250,6 +254,7 @@ struct tok_ctx {
     dfree(d_merge_slots);
     dfree(d_pair_rank);
     dfree(d_word_slots);
+    dfree(d_long_slots);
     dfree(d_tok_len);
     dfree(d_doc);
     dfree(d_outoff);

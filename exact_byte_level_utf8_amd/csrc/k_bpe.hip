@@ -6,12 +6,12 @@
 // 256 + rank (GraphTok, section 4 "Warp-cooperative BPE").
 //
 // piece_kernel: one workgroup per 1 KiB of piece starts, in two phases.
-//   1. One thread per 4 bytes resolves the pieces that need no merge loop: a
-//      1-byte piece is its byte's ID, and a 2..13-byte piece that is a whole
+//   1. One thread per 2 bytes resolves the pieces that need no merge loop: a
+//      1-byte piece is its byte's ID, and a 2..28-byte piece that is a whole
 //      vocabulary string whose own BPE is that token (checked for every string
-//      at load) is one probe of the whole-piece table (TokTier, "Exact GPU
-//      Tokenization": whole-piece vocabulary hits).  Every other piece goes to
-//      a work list in LDS by length.
+//      at load) is one probe of a whole-piece table (TokTier, section 4 "GPU
+//      BPE": whole-piece vocabulary hits).  Every other piece goes to a work
+//      list in LDS by length.
 //   2. The workgroup's four waves merge the listed pieces: pieces longer than
 //      64 bytes first, then 17..64-byte pieces (one wave per piece, one symbol
 //      per lane), then 2..16-byte pieces (four per wave, one 16-lane row each).
@@ -55,16 +55,29 @@ __device__ inline uint32_t merge_rank(const Tables& T, uint32_t a, uint32_t b) {
   return kNoRank;
 }
 
-// Whole-piece probe: token ID of the bytes p[0..len), 2 <= len <= 13, or kNoRank.
-__device__ inline uint32_t word_lookup(const Tables& T, const uint8_t* p, uint32_t len) {
-  uint64_t a = 0, b = 0;
+// NW dwords holding the LDS bytes text[off .. off + 4 NW), read with NW + 1
+// aligned dword loads and byte funnel shifts; bytes at or past len are zero.
+template <int NW>
+__device__ inline void key_words(const uint8_t* text, uint32_t off, uint32_t len, uint32_t (&w)[NW]) {
+  const uint32_t* a = reinterpret_cast<const uint32_t*>(text) + (off >> 2);
+  const uint32_t sh = off & 3u;
+  uint32_t d[NW + 1];
 #pragma unroll
-  for (uint32_t i = 0; i < 8; ++i)
-    if (i < len) a |= (uint64_t)p[i] << (8 * i);
+  for (int i = 0; i <= NW; ++i) d[i] = a[i];
 #pragma unroll
-  for (uint32_t i = 8; i < (uint32_t)kWordMax; ++i)
-    if (i < len) b |= (uint64_t)p[i] << (8 * (i - 8));
-  b |= (uint64_t)len << 40;
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t v = __builtin_amdgcn_alignbyte(d[i + 1], d[i], sh);
+    const int valid = (int)len - 4 * i;  // bytes of this word inside the piece
+    w[i] = valid >= 4 ? v : valid <= 0 ? 0u : v & ((1u << (8 * valid)) - 1u);
+  }
+}
+
+// Whole-piece probe of a 2..13-byte piece at text[off]: its token ID, or kNoRank.
+__device__ inline uint32_t word_lookup(const Tables& T, const uint8_t* text, uint32_t off, uint32_t len) {
+  uint32_t w[4];
+  key_words<4>(text, off, len, w);
+  const uint64_t a = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+  const uint64_t b = ((uint64_t)w[2] | ((uint64_t)(w[3] & 0xFFu) << 32)) | ((uint64_t)len << 40);
   const ulonglong2* slots = reinterpret_cast<const ulonglong2*>(T.word_slots);
   uint32_t h = word_hash(a, b) & T.word_buckets;
   constexpr uint64_t kKeyMask = (1ull << 44) - 1;
@@ -77,6 +90,33 @@ __device__ inline uint32_t word_lookup(const Tables& T, const uint8_t* p, uint32
     if (s3.x == a && (s3.y & kKeyMask) == b) return (uint32_t)(s3.y >> 44);
     if (s3.y == 0) return kNoRank;  // slots fill in order within a bucket
     h = (h + 1) & T.word_buckets;
+  }
+  return kNoRank;
+}
+
+// Whole-piece probe of a 14..28-byte piece at text[off]: its token ID, or
+// kNoRank.  A bucket is four 32-byte slots, one 128-byte line.
+__device__ inline uint32_t long_lookup(const Tables& T, const uint8_t* text, uint32_t off, uint32_t len) {
+  uint32_t w[7];
+  key_words<7>(text, off, len, w);
+  const uint64_t k0 = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+  const uint64_t k1 = (uint64_t)w[2] | ((uint64_t)w[3] << 32);
+  const uint64_t k2 = (uint64_t)w[4] | ((uint64_t)w[5] << 32);
+  const uint64_t k3 = (uint64_t)w[6] | ((uint64_t)len << 32);
+  const ulonglong2* slots = reinterpret_cast<const ulonglong2*>(T.long_slots);
+  uint32_t h = long_hash(k0, k1, k2, k3) & T.long_buckets;
+  constexpr uint64_t kKeyMask = (1ull << 37) - 1;
+  for (uint32_t probe = 0; probe <= T.long_buckets; ++probe) {
+    const ulonglong2* bk = slots + (size_t)h * kBucket * 2;
+    uint64_t last = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kBucket; ++j) {
+      const ulonglong2 lo = bk[2 * j], hi = bk[2 * j + 1];
+      if (lo.x == k0 && lo.y == k1 && hi.x == k2 && (hi.y & kKeyMask) == k3) return (uint32_t)(hi.y >> 37);
+      last = hi.y;
+    }
+    if (last == 0) return kNoRank;  // slots fill in order within a bucket
+    h = (h + 1) & T.long_buckets;
   }
   return kNoRank;
 }
@@ -255,7 +295,7 @@ __device__ void merge_long(const Tables& T, const uint8_t* __restrict__ text, ui
 }
 
 
-__global__ void __launch_bounds__(kPieceThreads)
+__global__ void __launch_bounds__(kPieceThreads, 8)
 piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, const uint64_t* __restrict__ doc_off,
              uint32_t n_docs, uint64_t* __restrict__ out_off) {
   constexpr int kChunksPerWg = kPieceTile / kChunk;  // 64
@@ -264,20 +304,23 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   constexpr int kTextLds = kPieceTile + kWaveMax + 16;
   constexpr int kFlagLds = kChunksPerWg + 6;
   constexpr int kTokLds = kPieceTile + kWaveMax;
-  constexpr int kCap0 = kPieceTile / 2, kCap1 = kPieceTile / (kRowMax + 1) + 1;
-  constexpr int kCap2 = kPieceTile / (kWaveMax + 1) + 1;
-  constexpr uint32_t kWaves = kPieceThreads / kWave;
-  __shared__ uint8_t s_text[kTextLds];
+  // pieces of 2..16 bytes in four length classes (13-16, 9-12, 5-8, 2-4),
+  // merged longest class first; a class of minimum length L holds at most
+  // 1024 / L pieces
+  constexpr int kCapA = kPieceTile / 13 + 1, kCapB = kPieceTile / 9 + 1, kCapC = kPieceTile / 5 + 1;
+  constexpr int kCapD = kPieceTile / 2;
+  constexpr int kCap1 = kPieceTile / (kRowMax + 1) + 1, kCap2 = kPieceTile / (kWaveMax + 1) + 1;
+  __shared__ __attribute__((aligned(16))) uint8_t s_text[kTextLds];
   __shared__ uint16_t s_flags[kFlagLds];
   __shared__ uint32_t s_tok[kTokLds];
-  __shared__ uint32_t s_out[kTokLds];
   __shared__ uint8_t s_cnt8[kPieceTile];
-  __shared__ uint32_t s_list0[kCap0], s_list1[kCap1], s_list2[kCap2];
+  __shared__ uint32_t s_la[kCapA], s_lb[kCapB], s_lc[kCapC], s_ld[kCapD], s_list1[kCap1], s_list2[kCap2];
   __shared__ uint32_t s_cnt[kChunksPerWg], s_excl[kChunksPerWg];
-  __shared__ uint32_t s_n[3], s_first, s_total, s_doc0;
+  __shared__ uint32_t s_n[6], s_next, s_first, s_total, s_doc0;
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
-  if (tid < 3) s_n[tid] = 0;
+  if (tid < 6) s_n[tid] = 0;
+  if (tid == 0) s_next = 0;
   const uint32_t tile = blockIdx.x;
   const uint64_t base = (uint64_t)tile * kPieceTile;
   const uint64_t c0 = (uint64_t)tile * kChunksPerWg;
@@ -292,17 +335,18 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   }
   __syncthreads();
 
-  // phase 1: single bytes and whole-piece hits; the rest goes to the lists
+  // phase 1: single bytes and whole-piece hits; the rest goes to the lists.
+  // Thread (lc, q) owns bytes 2q, 2q + 1 of chunk lc.
+  const uint32_t lc = tid / kPerChunk, q = tid % kPerChunk;
+  const uint32_t w = c0 + lc < n_chunks ? s_flags[lc] : 0u;
+  const uint32_t mine = (w >> (kBytesPer * q)) & ((1u << kBytesPer) - 1u);
   {
-    const uint32_t lc = tid / kPerChunk, q = tid % kPerChunk;
-    const uint64_t c = c0 + lc;
-    const uint32_t w = c < n_chunks ? s_flags[lc] : 0u;
-    const uint32_t mine = (w >> (kBytesPer * q)) & ((1u << kBytesPer) - 1u);
     uint32_t hits = 0;
 #pragma unroll
     for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
       if (!((mine >> b) & 1u)) continue;
       const uint32_t bit = kBytesPer * q + b;
+      const uint64_t c = c0 + lc;
       const uint64_t s = c * kChunk + bit;
       uint64_t e = ~0ull;
       const uint32_t above = w & ~((2u << bit) - 1u);
@@ -323,17 +367,25 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
       const uint8_t* p = s_text + off;
       uint32_t id = kNoRank;
       if (len == 1) id = p[0];
-      else if (len <= (uint64_t)kWordMax && T.word_slots) id = word_lookup(T, p, (uint32_t)len);
+      else if (len <= (uint64_t)kWordMax && T.word_slots) id = word_lookup(T, s_text, off, (uint32_t)len);
+      else if (len <= (uint64_t)kLongMax && T.long_slots) id = long_lookup(T, s_text, off, (uint32_t)len);
+      const uint32_t item = off | ((uint32_t)len << 16);
       if (id != kNoRank) {
         s_tok[off] = id;
         s_cnt8[off] = 1;
         ++hits;
-      } else if (len <= (uint64_t)kRowMax) {
-        s_list0[atomicAdd(&s_n[0], 1u)] = off | ((uint32_t)len << 16);
-      } else if (len <= (uint64_t)kWaveMax) {
-        s_list1[atomicAdd(&s_n[1], 1u)] = off | ((uint32_t)len << 16);
+      } else if (len > (uint64_t)kWaveMax) {
+        s_list2[atomicAdd(&s_n[5], 1u)] = off;
+      } else if (len > (uint64_t)kRowMax) {
+        s_list1[atomicAdd(&s_n[4], 1u)] = item;
+      } else if (len >= 13) {
+        s_la[atomicAdd(&s_n[0], 1u)] = item;
+      } else if (len >= 9) {
+        s_lb[atomicAdd(&s_n[1], 1u)] = item;
+      } else if (len >= 5) {
+        s_lc[atomicAdd(&s_n[2], 1u)] = item;
       } else {
-        s_list2[atomicAdd(&s_n[2], 1u)] = off;
+        s_ld[atomicAdd(&s_n[3], 1u)] = item;
       }
     }
 #pragma unroll
@@ -342,25 +394,41 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   }
   __syncthreads();
 
-  // phase 2: the waves merge the listed pieces, longest first
-  const uint32_t n0 = __builtin_amdgcn_readfirstlane(s_n[0]);
-  const uint32_t n1 = __builtin_amdgcn_readfirstlane(s_n[1]);
-  const uint32_t n2 = __builtin_amdgcn_readfirstlane(s_n[2]);
-  const uint32_t items = n2 + n1 + (n0 + 3) / 4;
-  for (uint32_t item = __builtin_amdgcn_readfirstlane(tid / kWave); item < items; item += kWaves) {
-    if (item < n2) {
-      const uint32_t off = s_list2[item];
-      merge_long(T, text, n, base + off, B, &s_cnt8[off], &s_cnt[off / kChunk]);
-    } else if (item < n2 + n1) {
-      const uint32_t it = s_list1[item - n2];
-      const uint32_t off = it & 0xFFFFu;
-      merge_rows<64>(T, s_text + off, it >> 16, true, s_tok + off, &s_cnt8[off], &s_cnt[off / kChunk]);
-    } else {
-      const uint32_t i = (item - n2 - n1) * 4 + (lane >> 4);
-      const bool act = i < n0;
-      const uint32_t it = act ? s_list0[i] : 0u;
-      const uint32_t off = it & 0xFFFFu;
-      merge_rows<16>(T, s_text + off, it >> 16, act, s_tok + off, &s_cnt8[off], &s_cnt[off / kChunk]);
+  // phase 2: the waves take items in order, longest pieces first: pieces
+  // over 64 bytes, then 17..64 bytes (a wave each), then groups of four
+  // 2..16-byte pieces by length class (a 16-lane row each).  The item index
+  // comes from an LDS counter through readfirstlane, so every branch on it
+  // is uniform across the wave.
+  {
+    const uint32_t n2 = __builtin_amdgcn_readfirstlane(s_n[5]);
+    const uint32_t n1 = __builtin_amdgcn_readfirstlane(s_n[4]);
+    const uint32_t ca = __builtin_amdgcn_readfirstlane(s_n[0]), cb = __builtin_amdgcn_readfirstlane(s_n[1]);
+    const uint32_t cc = __builtin_amdgcn_readfirstlane(s_n[2]), cd = __builtin_amdgcn_readfirstlane(s_n[3]);
+    const uint32_t ea = n2 + n1 + (ca + 3) / 4, eb = ea + (cb + 3) / 4, ec = eb + (cc + 3) / 4;
+    const uint32_t items = ec + (cd + 3) / 4;
+    for (;;) {
+      // every lane adds 1, so a grab moves the counter by 64
+      const uint32_t item = __builtin_amdgcn_readfirstlane(atomicAdd(&s_next, 1u)) / (uint32_t)kWave;
+      if (item >= items) break;
+      if (item < n2) {
+        const uint32_t off = s_list2[item];
+        merge_long(T, text, n, base + off, B, &s_cnt8[off], &s_cnt[off / kChunk]);
+      } else if (item < n2 + n1) {
+        const uint32_t it = s_list1[item - n2];
+        const uint32_t off = it & 0xFFFFu;
+        merge_rows<64>(T, s_text + off, it >> 16, true, s_tok + off, &s_cnt8[off], &s_cnt[off / kChunk]);
+      } else {
+        // length class of the item: bounds and counts are wave-uniform
+        const bool ia = item < ea, ib = !ia && item < eb, ic = !ia && !ib && item < ec;
+        const uint32_t first = ia ? n2 + n1 : ib ? ea : ic ? eb : ec;
+        const uint32_t cnt = ia ? ca : ib ? cb : ic ? cc : cd;
+        const uint32_t* lst = ia ? s_la : ib ? s_lb : ic ? s_lc : s_ld;
+        const uint32_t i = (item - first) * 4 + (lane >> 4);
+        const bool act = i < cnt;
+        const uint32_t it = act ? lst[i] : 0u;
+        const uint32_t off = it & 0xFFFFu;
+        merge_rows<16>(T, s_text + off, it >> 16, act, s_tok + off, &s_cnt8[off], &s_cnt[off / kChunk]);
+      }
     }
   }
   __syncthreads();
@@ -388,32 +456,40 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   }
   if (doc_off && tid == kWave) s_doc0 = first_doc_at_or_after(doc_off, n_docs, base);
   __syncthreads();
-  const uint32_t total = __builtin_amdgcn_readfirstlane(s_total);
-  const uint64_t first = __builtin_amdgcn_readfirstlane(s_first);
-  int32_t* run = B.staging + first;
-  const bool direct = n2 > 0;  // long pieces' tokens are in global memory: copy straight to the run
 
-  // one thread per chunk walks its pieces in order
-  if (tid < (uint32_t)kChunksPerWg && c0 + tid < n_chunks) {
-    uint32_t w = s_flags[tid];
-    const uint32_t cnt = s_cnt[tid], loc = s_excl[tid];
-    uint32_t done = 0;
-    while (w && done < cnt) {
-      const uint32_t off = tid * kChunk + __builtin_ctz(w);
-      w &= w - 1;
-      const uint32_t k = w ? s_cnt8[off] : cnt - done;  // the chunk's last piece takes the rest
-      const bool is_long = s_cnt8[off] == 0;
-      for (uint32_t j = 0; j < k; ++j) {
-        const uint32_t id = is_long ? B.ws_sym[base + off + j] : s_tok[off + j];
-        if (direct) run[loc + done + j] = (int32_t)id;
-        else s_out[loc + done + j] = id;
+  // every thread writes the tokens of the pieces that start in its two bytes:
+  // its position in the run is its chunk's offset plus the counts of the
+  // earlier pieces of the chunk (a scan over the chunk's eight threads).  A
+  // piece longer than 64 bytes is its chunk's last piece; its count is what
+  // the chunk's total leaves, and its tokens are in the long-piece workspace.
+  {
+    int32_t* run = B.staging + __builtin_amdgcn_readfirstlane(s_first);
+    uint32_t own = 0;
+#pragma unroll
+    for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b)
+      if ((mine >> b) & 1u) own += s_cnt8[lc * kChunk + kBytesPer * q + b];
+    uint32_t incl = own;
+#pragma unroll
+    for (int d = 1; d < kPerChunk; d <<= 1) {
+      const uint32_t up = __shfl_up(incl, d, kPerChunk);
+      if (q >= (uint32_t)d) incl += up;
+    }
+    uint32_t at = s_excl[lc] + (incl - own);
+    const uint32_t chunk_end = s_excl[lc] + s_cnt[lc];
+#pragma unroll
+    for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
+      if (!((mine >> b) & 1u)) continue;
+      const uint32_t off = lc * kChunk + kBytesPer * q + b;
+      const uint32_t k = s_cnt8[off];
+      if (k == 0) {  // long piece
+        for (uint32_t j = 0; at + j < chunk_end; ++j) run[at + j] = (int32_t)B.ws_sym[base + off + j];
+        at = chunk_end;
+      } else {
+        for (uint32_t j = 0; j < k; ++j) run[at + j] = (int32_t)s_tok[off + j];
+        at += k;
       }
-      done += k;
     }
   }
-  __syncthreads();
-  if (!direct)
-    for (uint32_t i = tid; i < total; i += kPieceThreads) run[i] = (int32_t)s_out[i];
 
   // offsets, within this tile's run, of the documents that start in the tile
   if (doc_off) {
@@ -421,11 +497,11 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
       const uint64_t p = doc_off[d];
       if (p >= n || p >= base + kPieceTile) break;
       if (p < base) continue;  // only with unordered offsets, which the call rejects
-      const uint32_t off = (uint32_t)(p - base), lc = off / kChunk;
-      uint32_t before = s_flags[lc] & ((1u << (off % kChunk)) - 1u);
-      uint32_t loc = s_excl[lc];
+      const uint32_t off = (uint32_t)(p - base), lc2 = off / kChunk;
+      uint32_t before = s_flags[lc2] & ((1u << (off % kChunk)) - 1u);
+      uint32_t loc = s_excl[lc2];
       while (before) {
-        loc += s_cnt8[lc * kChunk + __builtin_ctz(before)];
+        loc += s_cnt8[lc2 * kChunk + __builtin_ctz(before)];
         before &= before - 1;
       }
       out_off[d] = loc;

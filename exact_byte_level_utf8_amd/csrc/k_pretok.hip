@@ -108,28 +108,27 @@ struct BwdOp {
   __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return bwd_comp(a, b); }
 };
 
-// previous code point's lead index in the window, same document, or -1
-__device__ inline int prev_lead(const uint32_t* info, const uint8_t* fl, int k) {
-  if (k < 0 || (fl[k] & kBDoc)) return -1;
-  int j = k - 1;
-  for (int t = 0; t < 4 && j >= 0; ++t, --j) {
-    if (fl[j] & kBOut) return -1;
-    if (info[j] & kILead) return j;
-  }
-  return -1;
+// Bytes b .. b + 3 of an LDS byte array read as one word: two aligned word
+// loads and a byte funnel shift.
+__device__ inline uint32_t lds_word(const uint32_t* a, uint32_t b) {
+  return __builtin_amdgcn_alignbyte(a[(b >> 2) + 1], a[b >> 2], b & 3u);
 }
 
-__device__ inline uint32_t info_at(const uint32_t* info, int k) { return k < 0 ? kNone : info[k]; }
+__device__ inline bool is_cont(uint32_t byte) { return (byte & 0xC0u) == 0x80u; }
 
 template <int PATTERN>
 __global__ void __launch_bounds__(kThreads)
 pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off,
               uint32_t n_docs, Bufs B) {
-  __shared__ uint8_t s_raw[kWin + 4];
-  __shared__ uint8_t s_fl[kWin + 4];
+  // window byte k (k in [-4, kWin + 12)) lives at byte 4 + k of s_raw / s_fl
+  constexpr int kGuard = 4, kBytes = kWin + 16;
+  __shared__ uint32_t s_raw32[kBytes / 4];
+  __shared__ uint32_t s_fl32[kBytes / 4];
   __shared__ uint32_t s_info[kWin];
   __shared__ uint32_t s_scan[kThreads / kWave];
   __shared__ uint32_t s_misc[4];
+  uint8_t* s_raw = reinterpret_cast<uint8_t*>(s_raw32);
+  uint8_t* s_fl = reinterpret_cast<uint8_t*>(s_fl32);
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
   const int64_t base = (int64_t)blockIdx.x * kPT;
@@ -151,11 +150,11 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   const int64_t lo = base - kHalo;
   const int64_t sn = (int64_t)n;
 
-  for (int k = tid; k < kWin + 4; k += kThreads) {
-    const int64_t p = lo + k;
+  for (int g = tid; g < kBytes; g += kThreads) {
+    const int64_t p = lo + g - kGuard;
     const bool in = p >= 0 && p < sn;
-    s_raw[k] = in ? text[p] : 0;
-    s_fl[k] = in ? 0 : kBOut;
+    s_raw[g] = in ? text[p] : 0;
+    s_fl[g] = in ? 0 : kBOut;
   }
   if (doc_off && tid == 0) s_misc[0] = first_doc_at_or_after(doc_off, n_docs, lo < 0 ? 0 : (uint64_t)lo);
   __syncthreads();
@@ -163,88 +162,93 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     for (uint32_t d = s_misc[0] + tid; d <= n_docs; d += kThreads) {
       const uint64_t p = doc_off[d];
       if ((int64_t)p >= lo + kWin) break;
-      if ((int64_t)p >= lo && (int64_t)p < sn) s_fl[p - lo] |= kBDoc;  // equal offsets write equal bytes
+      if ((int64_t)p >= lo && (int64_t)p < sn) s_fl[p - lo + kGuard] |= kBDoc;  // equal offsets write equal bytes
     }
   } else if (tid == 0 && lo <= 0 && sn > 0) {
-    s_fl[-lo] |= kBDoc;
+    s_fl[kGuard - lo] |= kBDoc;
   }
   __syncthreads();
 
-  // decode every lead byte of the window; all class lookups of a thread are
-  // issued before any is used
+  // decode every window position into an info word, without branches: the
+  // bytes of a position and the four before it come from word reads; class
+  // lookups of all rounds are issued before any is used
   {
-    uint32_t cps[kWinRounds], lens[kWinRounds], pre[kWinRounds];
+    uint32_t cps[kWinRounds], pre[kWinRounds];
 #pragma unroll
     for (int j = 0; j < kWinRounds; ++j) {
-      const int k = tid + j * kThreads;
-      cps[j] = 0;
-      lens[j] = 0;
-      pre[j] = 0;
-      if (k < kWin) {
-        const uint8_t fl = s_fl[k];
-        const uint32_t b = s_raw[k];
-        if (!(fl & kBOut) && (b & 0xC0) != 0x80) {
-          const uint32_t len = utf8_len(b);
-          lens[j] = len;
-          pre[j] = kILead | ((fl & kBDoc) ? kIDocStart : 0u);
-          if (k + (int)len >= kWin) {
-            pre[j] |= kIUndecoded;
-          } else {
-            cps[j] = utf8_cp(b, s_raw[k + 1], s_raw[k + 2], s_raw[k + 3], len);
-            if (s_fl[k + len] & (kBDoc | kBOut)) pre[j] |= kILastInDoc;
-          }
-        }
-      }
+      const int k = min((int)(tid + j * kThreads), kWin - 1);  // positions past the window repeat the last one
+      const uint32_t g = (uint32_t)(k + kGuard);
+      const uint32_t cur = lds_word(s_raw32, g), prv = lds_word(s_raw32, g - 4u);
+      const uint64_t fl = (uint64_t)lds_word(s_fl32, g) | ((uint64_t)lds_word(s_fl32, g + 4u) << 32);
+      const uint32_t fprv = lds_word(s_fl32, g - 4u);
+      const uint32_t b0 = cur & 0xFFu, b1 = (cur >> 8) & 0xFFu, b2 = (cur >> 16) & 0xFFu, b3 = cur >> 24;
+      const uint32_t fl0 = (uint32_t)fl & 0xFFu;
+      const bool lead = !(fl0 & kBOut) & !is_cont(b0);
+      const uint32_t len = 1u + (b0 >= 0xC0u) + (b0 >= 0xE0u) + (b0 >= 0xF0u);
+      const bool undecoded = k + (int)len >= kWin;
+      const uint32_t c2 = ((b0 & 0x1Fu) << 6) | (b1 & 0x3Fu);
+      const uint32_t c3 = ((b0 & 0x0Fu) << 12) | ((b1 & 0x3Fu) << 6) | (b2 & 0x3Fu);
+      const uint32_t c4 = ((b0 & 0x07u) << 18) | ((b1 & 0x3Fu) << 12) | ((b2 & 0x3Fu) << 6) | (b3 & 0x3Fu);
+      cps[j] = len == 1u ? b0 : len == 2u ? c2 : len == 3u ? c3 : c4;
+      const bool last = ((uint32_t)(fl >> (8u * len)) & (kBDoc | kBOut)) != 0;
+      // bytes back to the previous code point's lead (bytes k-1 .. k-4 are
+      // prv bytes 3 .. 0); none at a document start or before the text
+      const bool q1 = is_cont(prv >> 24), q2 = is_cont((prv >> 16) & 0xFFu), q3 = is_cont((prv >> 8) & 0xFFu);
+      uint32_t d = !q1 ? 1u : !q2 ? 2u : !q3 ? 3u : 4u;
+      const uint32_t fback = (fprv >> (8u * (4u - d))) & 0xFFu;
+      if ((fl0 & kBDoc) | ((fback & kBOut) != 0)) d = 0;
+      uint32_t pr = kILead | (len << kILenShift) | ((fl0 & kBDoc) ? kIDocStart : 0u) | (d << kIPrevShift);
+      pr |= undecoded ? kIUndecoded : last ? kILastInDoc : 0u;
+      pre[j] = lead && k == (int)(tid + j * kThreads) ? pr : 0u;
     }
     uint32_t cls[kWinRounds];
 #pragma unroll
-    for (int j = 0; j < kWinRounds; ++j) cls[j] = dev_class(cps[j]);
+    for (int j = 0; j < kWinRounds; ++j) {
+      const uint32_t cp = cps[j];
+      const uint32_t bmp = kClsBmp[min(cp, 0xFFFFu) >> 2];
+      cls[j] = cp < 0x80u ? ascii_class(cp) : (bmp >> (2u * (cp & 3u))) & 3u;
+    }
+#pragma unroll
+    for (int j = 0; j < kWinRounds; ++j)
+      if (cps[j] >= 0x10000u) cls[j] = dev_class(cps[j]);  // rare: two-level table above the BMP
 #pragma unroll
     for (int j = 0; j < kWinRounds; ++j) {
       const int k = tid + j * kThreads;
       if (k >= kWin) continue;
+      const uint32_t cp = cps[j], p = pre[j];
       uint32_t in = 0;
-      if (pre[j] & kIUndecoded) in = kO | (lens[j] << kILenShift) | pre[j];
-      else if (pre[j]) in = make_info(cps[j], cls[j], lens[j], dev_fold_extra(cps[j])) | pre[j];
+      if (p & kIUndecoded) in = kO | p;
+      else if (p) in = make_info(cp, cls[j], 0u, cp == 0x17Fu ? (uint32_t)kCodeS : 0u) | p;
       s_info[k] = in;
     }
   }
 
   // UTF-8 validation of the tile's own bytes (Unicode Table 3-7, well-formed
-  // byte sequences); a sequence may not cross a document boundary
+  // byte sequences), from the lead side: every sequence that starts in the
+  // tile has a lead in C2..F4 (or is ASCII), its continuation bytes in the
+  // same document, the second-byte ranges of E0 ED F0 F4, and no
+  // continuation byte after it; no document starts with a continuation byte.
+  // Together these leave no stray or missing continuation byte anywhere.
   bool bad = false;
 #pragma unroll
   for (int j = 0; j < kRounds; ++j) {
-    const int k = kHalo + tid + j * kThreads;
-    if (s_fl[k] & kBOut) continue;
-    const uint32_t b = s_raw[k];
-    if (b < 0x80) continue;
-    if ((b & 0xC0) == 0x80) {
-      if (s_fl[k] & kBDoc) { bad = true; continue; }
-      bool ok = false;
-      for (int steps = 1; steps <= 3; ++steps) {
-        const int jj = k - steps;
-        if (s_fl[jj] & kBOut) break;
-        const uint32_t rb = s_raw[jj];
-        if ((rb & 0xC0) != 0x80) {
-          ok = rb >= 0xC0 && utf8_len(rb) > (uint32_t)steps;
-          break;
-        }
-        if (s_fl[jj] & kBDoc) break;
-      }
-      bad |= !ok;
-    } else {
-      if (b < 0xC2 || b > 0xF4) { bad = true; continue; }
-      const uint32_t len = utf8_len(b);
-      for (uint32_t t = 1; t < len; ++t) {
-        const int jj = k + t;
-        if ((s_fl[jj] & (kBOut | kBDoc)) || (s_raw[jj] & 0xC0) != 0x80) bad = true;
-      }
-      const uint32_t c1 = s_raw[k + 1];
-      if ((b == 0xE0 && c1 < 0xA0) || (b == 0xED && c1 > 0x9F) || (b == 0xF0 && c1 < 0x90) ||
-          (b == 0xF4 && c1 > 0x8F))
-        bad = true;
+    const uint32_t g = (uint32_t)(kHalo + tid + j * kThreads + kGuard);
+    const uint64_t raw = (uint64_t)lds_word(s_raw32, g) | ((uint64_t)lds_word(s_raw32, g + 4u) << 32);
+    const uint64_t fl = (uint64_t)lds_word(s_fl32, g) | ((uint64_t)lds_word(s_fl32, g + 4u) << 32);
+    const uint32_t b0 = (uint32_t)raw & 0xFFu, b1 = (uint32_t)(raw >> 8) & 0xFFu, f0 = (uint32_t)fl & 0xFFu;
+    const uint32_t len = 1u + (b0 >= 0xC0u) + (b0 >= 0xE0u) + (b0 >= 0xF0u);
+    bool ok = b0 < 0x80u || (b0 >= 0xC2u && b0 <= 0xF4u);
+#pragma unroll
+    for (uint32_t t = 1; t < 4; ++t) {
+      const uint32_t bt = (uint32_t)(raw >> (8 * t)) & 0xFFu, ft = (uint32_t)(fl >> (8 * t)) & 0xFFu;
+      ok &= t >= len || (is_cont(bt) && !(ft & (kBOut | kBDoc)));
     }
+    ok &= !(b0 == 0xE0u && b1 < 0xA0u) & !(b0 == 0xEDu && b1 > 0x9Fu) & !(b0 == 0xF0u && b1 < 0x90u) &
+          !(b0 == 0xF4u && b1 > 0x8Fu);
+    const uint32_t bn = (uint32_t)(raw >> (8 * len)) & 0xFFu, fn = (uint32_t)(fl >> (8 * len)) & 0xFFu;
+    ok &= (fn & (kBOut | kBDoc)) || !is_cont(bn);
+    const bool cont = is_cont(b0);
+    bad |= !(f0 & kBOut) && (cont ? (f0 & kBDoc) != 0 : !ok);
   }
   if (bad) report(&B.ctr->err_utf8, B.gen);
   __syncthreads();
@@ -258,7 +262,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     if (tid == 0) {  // walk left through the halo until both forward aggregates reset
       uint32_t acc = kFwdId, done = 0;
       for (int k = kHalo - 1; k >= 0; --k) {
-        if (s_fl[k] & kBOut) { done = 1; break; }
+        if (s_fl[k + kGuard] & kBOut) { done = 1; break; }
         const uint32_t in = s_info[k];
         if (in & kILead) {
           acc = fwd_comp(fwd_elem(in), acc);
@@ -271,7 +275,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     if (tid == kWave) {  // walk right until the backward aggregate resets
       uint32_t acc = kBwdId, done = 0;
       for (int k = kHalo + kPT; k < kWin; ++k) {
-        if (s_fl[k] & kBOut) { done = 1; break; }
+        if (s_fl[k + kGuard] & kBOut) { done = 1; break; }
         const uint32_t in = s_info[k];
         if (in & kILead) {
           if (in & kIUndecoded) break;
@@ -334,24 +338,30 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     }
   }
 
+  // the piece-start predicate at every tile position: the previous code
+  // points come from the back distances stored in the info words (four
+  // chained LDS reads), the next one from the code point's length
 #pragma unroll
   for (int j = 0; j < kRounds; ++j) {
     const int k = kHalo + tid + j * kThreads;
     const uint32_t c = s_info[k];
-    bool st = false;
-    if (c & kILead) {
-      const int j1 = prev_lead(s_info, s_fl, k);
-      const int j2 = prev_lead(s_info, s_fl, j1);
-      const int j3 = prev_lead(s_info, s_fl, j2);
-      const int j4 = prev_lead(s_info, s_fl, j3);
-      const uint32_t p1 = info_at(s_info, j1), p2 = info_at(s_info, j2);
-      const uint32_t p3 = info_at(s_info, j3), p4 = info_at(s_info, j4);
-      const uint32_t len = (c >> kILenShift) & 7u;
-      const uint32_t n1 = (c & kILastInDoc) ? kNone : s_info[k + len];
-      st = PATTERN == 0 ? piece_start_gpt2(c, p1, p2, p3, p4, n1)
-                        : piece_start_llama3(c, p1, p2, p3, p4, n1, fst[j] & 3u, (fst[j] >> 2) & 1u,
-                                             hst[j] & 1u);
+    uint32_t p[4];
+    uint32_t at = (uint32_t)k, cur = c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t d = is_none(cur) ? 0u : (cur >> kIPrevShift) & 7u;
+      at -= d;
+      const uint32_t v = s_info[at];
+      cur = d ? v : kNone;
+      p[i] = cur;
     }
+    const uint32_t len = (c >> kILenShift) & 7u;
+    const uint32_t nx = s_info[k + len];
+    const uint32_t n1 = (c & kILastInDoc) ? kNone : nx;
+    const bool rule = PATTERN == 0 ? piece_start_gpt2(c, p[0], p[1], p[2], p[3], n1)
+                                   : piece_start_llama3(c, p[0], p[1], p[2], p[3], n1, fst[j] & 3u,
+                                                        (fst[j] >> 2) & 1u, hst[j] & 1u);
+    const bool st = (c & kILead) && rule;
     // this wave holds 64 consecutive positions: four flag words
     const uint64_t m = __ballot(st);
     const uint64_t p0 = (uint64_t)base + (uint64_t)j * kThreads + wv * kWave;

@@ -38,6 +38,7 @@ enum : uint32_t {
   kIUndecoded = 1u << 16,  // lead whose continuation bytes lie outside the loaded window
   kILenShift = 17,         // bits 17-19: UTF-8 length of the code point
   kILastInDoc = 1u << 20,  // the next code point starts another document (or the text ends)
+  kIPrevShift = 21,        // bits 21-23: bytes back to the previous code point of the document (0: none)
 };
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
@@ -49,71 +50,70 @@ TOK_HD inline bool has(uint32_t i, uint32_t bit) { return i != kNone && (i & bit
 TOK_HD inline uint32_t exact_code(uint32_t i) { return (i >> kIExactShift) & 15u; }
 TOK_HD inline uint32_t fold_code(uint32_t i) { return (i >> kIFoldShift) & 15u; }
 
+// Letter codes of 'a'..'z' as nibbles: letters a..p in kLetterLo, q..z in
+// kLetterHi (0 = not a contraction letter).
+constexpr uint64_t letter_nibbles(char first, char last) {
+  uint64_t v = 0;
+  for (char ch = first; ch <= last; ++ch) {
+    const uint64_t code = ch == 's' ? kCodeS : ch == 't' ? kCodeT : ch == 'r' ? kCodeR : ch == 'e' ? kCodeE
+                        : ch == 'v' ? kCodeV : ch == 'm' ? kCodeM : ch == 'l' ? kCodeL : ch == 'd' ? kCodeD : 0;
+    v |= code << (4 * (ch - first));
+  }
+  return v;
+}
+constexpr uint64_t kLetterLo = letter_nibbles('a', 'p'), kLetterHi = letter_nibbles('q', 'z');
+
 // Letter code of an ASCII code point, case-sensitive (lowercase only).
 TOK_HD inline uint32_t ascii_letter_code(uint32_t cp) {
-  switch (cp) {
-    case 's': return kCodeS;
-    case 't': return kCodeT;
-    case 'r': return kCodeR;
-    case 'e': return kCodeE;
-    case 'v': return kCodeV;
-    case 'm': return kCodeM;
-    case 'l': return kCodeL;
-    case 'd': return kCodeD;
-    default: return 0;
-  }
+  const uint32_t t = cp - 'a';
+  if (t >= 26u) return 0;
+  return (uint32_t)((t < 16u ? kLetterLo >> (4 * t) : kLetterHi >> (4 * (t - 16u))) & 15u);
 }
 
 // Class of an ASCII code point: letters L, digits N, TAB..CR and space W.
 TOK_HD inline uint32_t ascii_class(uint32_t cp) {
-  if ((cp | 0x20u) - 'a' < 26u) return 0;  // L
-  if (cp - '0' < 10u) return 1;            // N
-  if (cp == ' ' || (cp >= 9 && cp <= 13)) return 2;  // W
-  return 3;                                 // O
+  const bool l = (cp | 0x20u) - 'a' < 26u, d = cp - '0' < 10u, w = cp == ' ' || cp - 9u < 5u;
+  return l ? 0u : d ? 1u : w ? 2u : 3u;
 }
 
 // Info word of one decoded code point (class from the caller's table).
 TOK_HD inline uint32_t make_info(uint32_t cp, uint32_t cls, uint32_t len, uint32_t fold_extra_code) {
   uint32_t i = cls | kILead | (len << kILenShift);
-  if (cp == 0x0D || cp == 0x0A) i |= kICrlf;
-  if (cp == 0x20) i |= kISpace;
-  if (cp == 0x27) i |= kIApos;
-  if (cp < 0x80) {
-    uint32_t ex = ascii_letter_code(cp);
-    uint32_t fo = ascii_letter_code(cp | 0x20u);
-    if ((cp | 0x20u) - 'a' >= 26u) fo = 0;
-    i |= ex << kIExactShift;
-    i |= fo << kIFoldShift;
-  } else {
-    i |= fold_extra_code << kIFoldShift;
-  }
+  i |= (cp == 0x0D || cp == 0x0A) ? kICrlf : 0u;
+  i |= cp == 0x20 ? kISpace : 0u;
+  i |= cp == 0x27 ? kIApos : 0u;
+  const bool ascii_letter = cp < 0x80 && (cp | 0x20u) - 'a' < 26u;
+  i |= (cp < 0x80 ? ascii_letter_code(cp) : 0u) << kIExactShift;
+  i |= (ascii_letter ? ascii_letter_code(cp | 0x20u) : cp < 0x80 ? 0u : fold_extra_code) << kIFoldShift;
   return i;
 }
 
-// The apostrophe before code point q (q = the code point before the
-// apostrophe, or none) stands alone at a piece start: its other-class run has
-// length one (q is not O) and no space attaches it to the left (q is not
-// U+0020).  Only then is the contraction alternative tried at the apostrophe.
+// The predicates below are flat boolean algebra (no early returns), so the
+// kernel evaluates them without divergent branches.  kNone has every bit set,
+// so each test that can see "no code point" checks for it first.
+
+// The apostrophe after code point q (q = the code point before it, or none)
+// stands alone at a piece start: its other-class run has length one (q is not
+// O) and no space attaches it to the left (q is not U+0020).  Only then is
+// the contraction alternative tried at the apostrophe.
 TOK_HD inline bool apos_at_piece_start(uint32_t q) {
-  return is_none(q) || (cls_of(q) != 3 && !(q & kISpace));
+  return is_none(q) | ((cls_of(q) != 3u) & !(q & kISpace));
 }
 
+constexpr uint32_t kOneLetter = (1u << kCodeS) | (1u << kCodeT) | (1u << kCodeM) | (1u << kCodeD);
+constexpr uint32_t kTwoLetter = (1u << kCodeR) | (1u << kCodeV) | (1u << kCodeL);
+
 // Length in code points (1 or 2) of the contraction suffix that begins with
-// code point a followed by b (b may be none), or 0.  The alternatives are
-// tried in the order s t re ve m ll d; their first letters differ, so at most
-// one applies.
+// code point a followed by b (either may be none), or 0.  The alternatives
+// are tried in the order s t re ve m ll d; their first letters differ, so at
+// most one applies.
 TOK_HD inline uint32_t contraction_len(uint32_t a, uint32_t b, bool fold) {
-  uint32_t ca = fold ? fold_code(a) : exact_code(a);
-  switch (ca) {
-    case kCodeS: case kCodeT: case kCodeM: case kCodeD: return 1;
-    case kCodeR: case kCodeV: case kCodeL: {
-      if (is_none(b)) return 0;
-      uint32_t cb = fold ? fold_code(b) : exact_code(b);
-      uint32_t want = ca == kCodeL ? kCodeL : kCodeE;
-      return cb == want ? 2 : 0;
-    }
-    default: return 0;
-  }
+  const uint32_t ca = is_none(a) ? 0u : fold ? fold_code(a) : exact_code(a);
+  const uint32_t cb = is_none(b) ? 0u : fold ? fold_code(b) : exact_code(b);
+  const uint32_t want = ca == kCodeL ? kCodeL : kCodeE;
+  const bool one = (kOneLetter >> ca) & 1u;
+  const bool two = ((kTwoLetter >> ca) & 1u) & (cb == want);
+  return one ? 1u : two ? 2u : 0u;
 }
 
 // Code point j lies inside a letter run (p1 is a letter).  It starts a piece
@@ -121,35 +121,30 @@ TOK_HD inline uint32_t contraction_len(uint32_t a, uint32_t b, bool fold) {
 // precedes the run: "'x" + j or "'xy" + j.
 TOK_HD inline bool contraction_split(uint32_t p1, uint32_t p2, uint32_t p3, uint32_t p4, bool fold) {
   // one-letter suffix: p2 = apostrophe, p1 = the letter (p1 starts the run)
-  if (has(p2, kIApos) && apos_at_piece_start(p3) && contraction_len(p1, kNone, fold) == 1)
-    return true;
+  const bool one = !is_none(p2) & ((p2 & kIApos) != 0) & apos_at_piece_start(p3) &
+                   (contraction_len(p1, kNone, fold) == 1u);
   // two-letter suffix: p3 = apostrophe, p2 p1 = the letters
-  if (has(p3, kIApos) && !is_none(p2) && cls_of(p2) == 0 && apos_at_piece_start(p4) &&
-      contraction_len(p2, p1, fold) == 2)
-    return true;
-  return false;
+  const bool two = !is_none(p3) & ((p3 & kIApos) != 0) & !is_none(p2) & (cls_of(p2) == 0u) &
+                   apos_at_piece_start(p4) & (contraction_len(p2, p1, fold) == 2u);
+  return one | two;
 }
 
 // GPT-2 style: 's|'t|'re|'ve|'m|'ll|'d | ?L+ | ?N+ | ?[^\s L N]+ | \s+(?!\S) | \s+
 // c = this code point, p1..p4 = the previous ones, n1 = the next one.
 TOK_HD inline bool piece_start_gpt2(uint32_t c, uint32_t p1, uint32_t p2, uint32_t p3, uint32_t p4,
                                     uint32_t n1) {
-  if (is_none(p1)) return true;  // document start
   const uint32_t k = cls_of(c), k1 = cls_of(p1);
-  if (k == 2) {
-    // a whitespace run [s, e) is one piece at the end of the text, else
-    // [s, e-1) and then e-1 alone (the lookahead gives back one char)
-    if (k1 != 2) return true;
-    return !is_none(n1) && cls_of(n1) != 2;
-  }
-  if (k1 == k) {  // inside a letter, digit or other run
-    return k == 0 && contraction_split(p1, p2, p3, p4, false);
-  }
-  // run start: an immediately preceding U+0020 attaches to the run
-  if (p1 & kISpace) return false;
-  if (k == 0 && (p1 & kIApos) && apos_at_piece_start(p2) && contraction_len(c, n1, false))
-    return false;  // the letters belong to the contraction piece
-  return true;
+  // whitespace: a run [s, e) is one piece at the end of the text, else
+  // [s, e-1) and then e-1 alone (the lookahead gives back one char)
+  const bool w = (k1 != 2u) | (!is_none(n1) & (cls_of(n1) != 2u));
+  // inside a letter, digit or other run
+  const bool same = (k == 0u) & contraction_split(p1, p2, p3, p4, false);
+  // run start: an immediately preceding U+0020 attaches to the run, and the
+  // letters after a stand-alone apostrophe belong to its contraction
+  const bool contr = (k == 0u) & ((p1 & kIApos) != 0) & apos_at_piece_start(p2) &
+                     (contraction_len(c, n1, false) != 0u);
+  const bool start = !(p1 & kISpace) & !contr;
+  return is_none(p1) | (k == 2u ? w : k1 == k ? same : start);
 }
 
 // Llama-3 style:
@@ -161,30 +156,23 @@ TOK_HD inline bool piece_start_gpt2(uint32_t c, uint32_t p1, uint32_t p2, uint32
 // h: a CR or LF follows c inside its whitespace run.
 TOK_HD inline bool piece_start_llama3(uint32_t c, uint32_t p1, uint32_t p2, uint32_t p3, uint32_t p4,
                                       uint32_t n1, uint32_t nmod3, bool g, bool h) {
-  if (is_none(p1)) return true;
   const uint32_t k = cls_of(c), k1 = cls_of(p1);
-  switch (k) {
-    case 1:  // digits: groups of three from the run start
-      return nmod3 == 0;
-    case 0:  // letters
-      if (k1 == 0) return contraction_split(p1, p2, p3, p4, true);
-      if ((p1 & kICrlf) || k1 == 1) return true;
-      if (k1 == 2) return false;  // one non-CR/LF space char is the optional prefix
-      // k1 == O: a lone O char at a piece start is the prefix (or a contraction)
-      return !apos_at_piece_start(p2);
-    case 3:  // other
-      if (k1 == 3) return false;
-      return !(p1 & kISpace);
-    default:  // whitespace
-      if (c & kICrlf) {
-        if (k1 != 2) return k1 != 3;  // after O the CR/LF block joins the O piece
-        return false;                 // \s*[\r\n]+ runs to the last CR/LF of the run
-      }
-      if (k1 != 2) return true;
-      // first char after the last CR/LF of the run, or the run's entry point
-      if (p1 & kICrlf) return is_none(n1) || !h || g;
-      return !is_none(n1) && cls_of(n1) != 2;  // e-1 before a non-space run
-  }
+  const bool crlf1 = (p1 & kICrlf) != 0;
+  // digits: groups of three from the run start
+  const bool d = nmod3 == 0u;
+  // letters: one non-CR/LF space char before the run is its optional prefix,
+  // and so is a lone O char at a piece start (or its contraction)
+  const bool l = k1 == 0u ? contraction_split(p1, p2, p3, p4, true)
+                          : (crlf1 | (k1 == 1u)) ? true : k1 == 2u ? false : !apos_at_piece_start(p2);
+  // other: U+0020 before the run attaches to it
+  const bool o = (k1 != 3u) & !(p1 & kISpace);
+  // whitespace: after O the CR/LF block joins the O piece; \s*[\r\n]+ runs to
+  // the last CR/LF of the run; then the first char after it, or the run's
+  // entry point; e-1 before a non-space run
+  const bool w = (c & kICrlf) ? (k1 != 2u) & (k1 != 3u)
+                              : (k1 != 2u) | (crlf1 ? (is_none(n1) | !h | g)
+                                                     : (!is_none(n1) & (cls_of(n1) != 2u)));
+  return is_none(p1) | (k == 0u ? l : k == 1u ? d : k == 2u ? w : o);
 }
 
 // ---- run aggregates of the Llama-3 style as scans over (reset, value) maps --

@@ -27,7 +27,8 @@ namespace tok {
 constexpr int kThreads = 256;        // threads per pre-tokenization workgroup
 constexpr int kChunk = 16;           // bytes per flag word
 constexpr int kHalo = 64;            // context bytes loaded on each side of a tile
-constexpr int kWordMax = 13;         // longest piece the whole-piece table holds
+constexpr int kWordMax = 13;         // longest piece the short whole-piece table holds
+constexpr int kLongMax = 28;         // longest piece the long whole-piece table holds
 constexpr int kRowMax = 16;          // longest piece merged by one 16-lane row
 constexpr int kWaveMax = 64;         // longest piece merged by one wave in registers
 constexpr int kPretokTile = 1024;    // bytes per workgroup of the pre-tokenization pass
@@ -66,6 +67,8 @@ struct Tables {
   const uint32_t* pair_rank;    // [256 * 256] rank of byte pair (a, b), or kNoRank
   const uint64_t* word_slots;   // 2 x uint64 per slot, see word_hash()
   uint32_t word_buckets;        // buckets - 1; word_slots == nullptr disables the table
+  const uint64_t* long_slots;   // 4 x uint64 per slot, see long_hash()
+  uint32_t long_buckets;        // buckets - 1; long_slots == nullptr disables the table
   const uint32_t* tok_len;      // bytes of each token ID
 };
 
@@ -96,6 +99,14 @@ __host__ __device__ inline uint32_t merge_hash(uint32_t left, uint32_t right) {
 // token ID in bits 44..63 of b.
 __host__ __device__ inline uint32_t word_hash(uint64_t a, uint64_t b) {
   return (uint32_t)(((a ^ (b * 0x9E3779B97F4A7C15ull)) * 0xC2B2AE3D27D4EB4Full) >> 32);
+}
+
+// Whole-piece key of a byte string of 14..28 bytes: k0, k1, k2 = bytes 0..23
+// (little endian), k3 = bytes 24..27 (zero padded) | len << 32.  A stored
+// slot adds the token ID in bits 37..63 of k3.
+__host__ __device__ inline uint32_t long_hash(uint64_t k0, uint64_t k1, uint64_t k2, uint64_t k3) {
+  const uint64_t h = (k0 ^ (k1 * 0x9E3779B97F4A7C15ull)) * 0xC2B2AE3D27D4EB4Full ^ (k2 + (k3 << 7));
+  return (uint32_t)((h * 0xFF51AFD7ED558CCDull) >> 32);
 }
 
 // First index d in [0, n_docs] with doc_off[d] >= x (n_docs + 1 if none).

@@ -81,8 +81,8 @@ typedef struct tok_ctx tok_ctx;
  * out:      receives the context (NULL on error).
  *
  * Builds, on the device: the (left, right) -> rank open-addressing table, a
- * direct byte-pair rank table, the token byte lengths, and a whole-piece
- * table of vocabulary strings of 2..13 bytes whose own BPE is the single token
+ * direct byte-pair rank table, the token byte lengths, and whole-piece
+ * tables of vocabulary strings of 2..28 bytes whose own BPE is the single token
  * (the whole-vocabulary-hit shortcut of TokTier, section 4 "GPU BPE", applied only where it
  * provably cannot change an ID: each string is checked by running the GPU
  * merge kernels on it once at load).
@@ -229,7 +229,7 @@ typedef struct tok_info {
   uint32_t vocab_size;     /* 256 + n_merges                                 */
   uint32_t max_token_len;  /* longest token, bytes                           */
   uint32_t n_whole;        /* whole-piece table entries (self-encoding)      */
-  uint32_t n_not_self;     /* 2..13-byte vocab strings whose BPE differs     */
+  uint32_t n_not_self;     /* 2..28-byte vocab strings whose BPE differs     */
   uint64_t config_hash;    /* FNV-1a over pattern and merges                 */
 } tok_info;
 

@@ -101,9 +101,9 @@ def test_load_info(cfg):
         assert info["vocab_size"] == len(tokb)
         assert info["max_token_len"] == max(len(x) for x in tokb)
         # every trained vocabulary string encodes to its own ID (checked by the
-        # oracle tests), so the load-time check must admit all 2..13-byte ones
+        # oracle tests), so the load-time check must admit all 2..28-byte ones
         assert info["n_not_self"] == 0, name
-        assert info["n_whole"] == sum(1 for x in tokb[256:] if 2 <= len(x) <= 13)
+        assert info["n_whole"] == sum(1 for x in tokb[256:] if 2 <= len(x) <= 28)
         assert np.array_equal(t.token_lengths(), [len(x) for x in tokb])
 
 
