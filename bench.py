@@ -47,6 +47,41 @@ WORKLOADS = {
 }
 
 
+# dominant-stage kernel and the sources its code comes from (for matching
+# committed counter summaries to the kernel that produced them)
+CSRC = os.path.join(ROOT, "exact_byte_level_utf8_amd", "csrc")
+STAGE_KERNELS = {
+    "pretokenize": ("pretok_kernel", ["k_pretok.hip", "pretok_rules.h", "wg_scan.h", "tok_internal.h", "uniclass.inc"]),
+    "pieces": ("piece_kernel", ["k_bpe.hip", "bpe_util.h", "wg_scan.h", "tok_internal.h"]),
+    "assemble": ("assemble_kernel", ["k_assemble.hip", "wg_scan.h", "tok_internal.h"]),
+}
+
+
+def source_digest(stage: str) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in STAGE_KERNELS[stage][1]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, stage: str):
+    """HBM bytes per launch of the stage's kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by a copy of known
+    size), or None when there is none or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    k = rec.get("kernels", {}).get(STAGE_KERNELS[stage][0])
+    if not k or k.get("source_sha256") != source_digest(stage):
+        return None
+    return int(k["bytes_per_launch"])
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -244,7 +279,8 @@ def main() -> int:
                        "p99": round(1e3 * float(np.percentile(per_step, 99)), 4)},
         "stages_ms": stages,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6),
+                     "traffic": measured_traffic(args.workload, dom),
                      "algorithmic_bytes": alg, "avg_ms": dom_ms},
         "complete_call": complete,
         "cpu_baseline": cpu,

@@ -39,7 +39,7 @@ assemble_kernel(uint64_t n, Bufs B, int32_t* __restrict__ out, uint64_t cap, con
   } else if (tid < 128u) {
     if (t_lo + (tid - 64u) < tile) part += B.tile_cnt[t_lo + (tid - 64u)];
   }
-  part = wave_incl_scan(part, AddOp());
+  part = wave_incl_scan(part, AddOp(), 0u);
   if (lane == 63u) s_part[tid >> 6] = part;
   __syncthreads();
   const uint32_t base = __builtin_amdgcn_readfirstlane(s_part[0] + s_part[1] + s_part[2] + s_part[3]);

@@ -72,6 +72,24 @@ __device__ inline void key_words(const uint8_t* text, uint32_t off, uint32_t len
   }
 }
 
+// Short whole-piece table: the token ID of key (a, b), probing from bucket h
+// on, or kNoRank.
+__device__ inline uint32_t word_probe_from(const Tables& T, uint64_t a, uint64_t b, uint32_t h) {
+  const ulonglong2* slots = reinterpret_cast<const ulonglong2*>(T.word_slots);
+  constexpr uint64_t kKeyMask = (1ull << 44) - 1;
+  for (uint32_t probe = 0; probe <= T.word_buckets; ++probe) {
+    const ulonglong2* bk = slots + (size_t)h * kBucket;
+    const ulonglong2 s0 = bk[0], s1 = bk[1], s2 = bk[2], s3 = bk[3];
+    if (s0.x == a && (s0.y & kKeyMask) == b) return (uint32_t)(s0.y >> 44);
+    if (s1.x == a && (s1.y & kKeyMask) == b) return (uint32_t)(s1.y >> 44);
+    if (s2.x == a && (s2.y & kKeyMask) == b) return (uint32_t)(s2.y >> 44);
+    if (s3.x == a && (s3.y & kKeyMask) == b) return (uint32_t)(s3.y >> 44);
+    if (s3.y == 0) return kNoRank;  // slots fill in order within a bucket
+    h = (h + 1) & T.word_buckets;
+  }
+  return kNoRank;
+}
+
 // Whole-piece probe of a 2..13-byte piece at text[off]: its token ID, or kNoRank.
 __device__ inline uint32_t word_lookup(const Tables& T, const uint8_t* text, uint32_t off, uint32_t len) {
   uint32_t w[4];
@@ -130,6 +148,20 @@ __device__ inline uint32_t row16_min(uint32_t v) {
   return v;
 }
 
+// Value of lane + 1 (next) and lane + 2 (next2) of the same row of ROW lanes,
+// by DPP: row_shl inside a 16-lane row, wave_shl across the wave.  Lanes whose
+// source lies past the row get 0 (callers never use those).
+template <int ROW>
+__device__ inline uint32_t row_next(uint32_t v) {
+  if (ROW == 16) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x101, 0xF, 0xF, false);  // row_shl:1
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xF, 0xF, false);                  // wave_shl:1
+}
+template <int ROW>
+__device__ inline uint32_t row_next2(uint32_t v) {
+  if (ROW == 16) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x102, 0xF, 0xF, false);  // row_shl:2
+  return row_next<64>(row_next<64>(v));
+}
+
 __device__ inline uint32_t wave_min(uint32_t v) {
   v = row16_min(v);
   return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
@@ -151,7 +183,7 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
   const uint64_t below = ((1ull << lane) - 1ull) & row_bits;
   uint32_t cur = active ? len : 0u;
   uint32_t sym = k < cur ? (uint32_t)p[k] : 0u;
-  const uint32_t nx = __shfl_down(sym, 1, ROW);
+  const uint32_t nx = row_next<ROW>(sym);
   uint32_t rk = k + 1 < cur ? T.pair_rank[(sym << 8) | nx] : kNoRank;
   for (;;) {
     if (k + 1 >= cur) rk = kNoRank;
@@ -171,8 +203,8 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
     const bool chose = (S >> lane) & 1ull;
     const bool gone = k > 0 && ((S >> (lane - 1)) & 1ull);
     const uint32_t nsym = chose ? 256u + r : sym;
-    const uint32_t n1 = __shfl_down(nsym, 1, ROW);
-    const uint32_t n2 = __shfl_down(nsym, 2, ROW);
+    const uint32_t n1 = row_next<ROW>(nsym);
+    const uint32_t n2 = row_next2<ROW>(nsym);
     uint32_t nrk = rk;
     if (live && !gone && k < cur) {
       const uint32_t kn = chose ? k + 2 : k + 1;  // next surviving position
@@ -316,7 +348,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   __shared__ uint8_t s_cnt8[kPieceTile];
   __shared__ uint32_t s_la[kCapA], s_lb[kCapB], s_lc[kCapC], s_ld[kCapD], s_list1[kCap1], s_list2[kCap2];
   __shared__ uint32_t s_cnt[kChunksPerWg], s_excl[kChunksPerWg];
-  __shared__ uint32_t s_n[6], s_next, s_first, s_total, s_doc0;
+  __shared__ uint32_t s_n[6], s_next, s_first, s_doc0;
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   if (tid < 6) s_n[tid] = 0;
@@ -341,48 +373,80 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   const uint32_t w = c0 + lc < n_chunks ? s_flags[lc] : 0u;
   const uint32_t mine = (w >> (kBytesPer * q)) & ((1u << kBytesPer) - 1u);
   {
+    // ends: the next piece start in this chunk, else in the next four chunks
+    // (a piece with no start within 64 bytes is long, or runs to the end)
+    const uint64_t c = c0 + lc;
+    const uint32_t w1 = s_flags[lc + 1], w2 = s_flags[lc + 2], w3 = s_flags[lc + 3], w4 = s_flags[lc + 4];
+    const uint32_t far = w1 ? 16u + __builtin_ctz(w1) : w2 ? 32u + __builtin_ctz(w2)
+                       : w3 ? 48u + __builtin_ctz(w3) : w4 ? 64u + __builtin_ctz(w4) : 0xFFFFu;
+    bool has[kBytesPer];
+    uint32_t len[kBytesPer], off[kBytesPer], id[kBytesPer];
+#pragma unroll
+    for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
+      const uint32_t bit = kBytesPer * q + b;
+      const uint32_t above = w & ~((2u << bit) - 1u);
+      const uint32_t endrel = above ? (uint32_t)__builtin_ctz(above) : far;
+      const uint64_t s0 = c * kChunk + bit;
+      const uint64_t e = min(endrel == 0xFFFFu ? ~0ull : c * kChunk + endrel, n);
+      has[b] = (mine >> b) & 1u;
+      len[b] = has[b] ? (uint32_t)min(e - s0, (uint64_t)0xFFFF) : 0u;
+      off[b] = (uint32_t)(s0 - base);
+      id[b] = len[b] == 1u ? (uint32_t)s_text[off[b]] : kNoRank;
+    }
+    // short whole-piece table: both candidates' first buckets are loaded
+    // before either is compared, so their latencies overlap
+    if (T.word_slots) {
+      constexpr uint64_t kKeyMask = (1ull << 44) - 1;
+      const ulonglong2* slots = reinterpret_cast<const ulonglong2*>(T.word_slots);
+      uint64_t ka[kBytesPer], kb[kBytesPer];
+      uint32_t h[kBytesPer];
+      ulonglong2 x[kBytesPer][4];
+#pragma unroll
+      for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
+        const bool want = len[b] >= 2u && len[b] <= (uint32_t)kWordMax;
+        uint32_t wd[4];
+        key_words<4>(s_text, off[b], len[b], wd);
+        ka[b] = (uint64_t)wd[0] | ((uint64_t)wd[1] << 32);
+        kb[b] = ((uint64_t)wd[2] | ((uint64_t)(wd[3] & 0xFFu) << 32)) | ((uint64_t)len[b] << 40);
+        h[b] = want ? word_hash(ka[b], kb[b]) & T.word_buckets : 0u;
+        const ulonglong2* bk = slots + (size_t)h[b] * kBucket;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[b][i] = bk[i];
+      }
+#pragma unroll
+      for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
+        if (!(len[b] >= 2u && len[b] <= (uint32_t)kWordMax)) continue;
+        uint32_t got = kNoRank;
+#pragma unroll
+        for (int i = 3; i >= 0; --i)
+          if (x[b][i].x == ka[b] && (x[b][i].y & kKeyMask) == kb[b]) got = (uint32_t)(x[b][i].y >> 44);
+        if (got == kNoRank && x[b][3].y != 0)  // bucket full: keep probing (rare)
+          got = word_probe_from(T, ka[b], kb[b], (h[b] + 1) & T.word_buckets);
+        id[b] = got;
+      }
+    }
+#pragma unroll
+    for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b)
+      if (T.long_slots && len[b] > (uint32_t)kWordMax && len[b] <= (uint32_t)kLongMax)
+        id[b] = long_lookup(T, s_text, off[b], len[b]);
     uint32_t hits = 0;
 #pragma unroll
     for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
-      if (!((mine >> b) & 1u)) continue;
-      const uint32_t bit = kBytesPer * q + b;
-      const uint64_t c = c0 + lc;
-      const uint64_t s = c * kChunk + bit;
-      uint64_t e = ~0ull;
-      const uint32_t above = w & ~((2u << bit) - 1u);
-      if (above) {
-        e = c * kChunk + __builtin_ctz(above);
-      } else {
-        for (uint32_t j = 1; j <= 4; ++j) {
-          const uint32_t wj = s_flags[lc + j];
-          if (wj) {
-            e = (c + j) * kChunk + __builtin_ctz(wj);
-            break;
-          }
-        }
-      }
-      if (e > n) e = n;
-      const uint64_t len = e - s;
-      const uint32_t off = (uint32_t)(s - base);
-      const uint8_t* p = s_text + off;
-      uint32_t id = kNoRank;
-      if (len == 1) id = p[0];
-      else if (len <= (uint64_t)kWordMax && T.word_slots) id = word_lookup(T, s_text, off, (uint32_t)len);
-      else if (len <= (uint64_t)kLongMax && T.long_slots) id = long_lookup(T, s_text, off, (uint32_t)len);
-      const uint32_t item = off | ((uint32_t)len << 16);
-      if (id != kNoRank) {
-        s_tok[off] = id;
-        s_cnt8[off] = 1;
+      if (!has[b]) continue;
+      const uint32_t item = off[b] | (len[b] << 16);
+      if (id[b] != kNoRank) {
+        s_tok[off[b]] = id[b];
+        s_cnt8[off[b]] = 1;
         ++hits;
-      } else if (len > (uint64_t)kWaveMax) {
-        s_list2[atomicAdd(&s_n[5], 1u)] = off;
-      } else if (len > (uint64_t)kRowMax) {
+      } else if (len[b] > (uint32_t)kWaveMax) {
+        s_list2[atomicAdd(&s_n[5], 1u)] = off[b];
+      } else if (len[b] > (uint32_t)kRowMax) {
         s_list1[atomicAdd(&s_n[4], 1u)] = item;
-      } else if (len >= 13) {
+      } else if (len[b] >= 13u) {
         s_la[atomicAdd(&s_n[0], 1u)] = item;
-      } else if (len >= 9) {
+      } else if (len[b] >= 9u) {
         s_lb[atomicAdd(&s_n[1], 1u)] = item;
-      } else if (len >= 5) {
+      } else if (len[b] >= 5u) {
         s_lc[atomicAdd(&s_n[2], 1u)] = item;
       } else {
         s_ld[atomicAdd(&s_n[3], 1u)] = item;
@@ -436,7 +500,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   // phase 3: the tile's tokens as one run from its first piece start
   if (tid < (uint32_t)kChunksPerWg) {  // wave 0, all lanes
     const uint32_t v = s_cnt[tid];
-    const uint32_t incl = wave_incl_scan(v, AddOp());
+    const uint32_t incl = wave_incl_scan(v, AddOp(), 0u);
     s_excl[tid] = incl - v;
     const uint32_t total = __builtin_amdgcn_readlane((int)incl, 63);
     const uint64_t has = __ballot(c0 + tid < n_chunks && s_flags[tid] != 0);
@@ -446,7 +510,6 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
       first = base + l * kChunk + __builtin_ctz((uint32_t)__builtin_amdgcn_readlane((int)s_flags[tid], (int)l));
     }
     if (tid == 0) {
-      s_total = total;
       s_first = (uint32_t)first;
       B.tile_cnt[tile] = total;
       B.tile_first[tile] = (uint32_t)first;

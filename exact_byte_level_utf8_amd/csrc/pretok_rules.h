@@ -90,7 +90,12 @@ TOK_HD inline uint32_t make_info(uint32_t cp, uint32_t cls, uint32_t len, uint32
 
 // The predicates below are flat boolean algebra (no early returns), so the
 // kernel evaluates them without divergent branches.  kNone has every bit set,
-// so each test that can see "no code point" checks for it first.
+// so each test that can see "no code point" checks for it first.  Bitwise &
+// and | on bools are deliberate: they keep both sides evaluated, branch-free.
+#if defined(__clang__)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wbitwise-instead-of-logical"
+#endif
 
 // The apostrophe after code point q (q = the code point before it, or none)
 // stands alone at a piece start: its other-class run has length one (q is not
@@ -174,6 +179,10 @@ TOK_HD inline bool piece_start_llama3(uint32_t c, uint32_t p1, uint32_t p2, uint
                                                      : (!is_none(n1) & (cls_of(n1) != 2u)));
   return is_none(p1) | (k == 0u ? l : k == 1u ? d : k == 2u ? w : o);
 }
+
+#if defined(__clang__)
+#pragma clang diagnostic pop
+#endif
 
 // ---- run aggregates of the Llama-3 style as scans over (reset, value) maps --
 //

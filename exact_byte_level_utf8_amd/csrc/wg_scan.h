@@ -12,28 +12,47 @@ constexpr int kWave = 64;
 
 __device__ inline uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
 
-// inclusive prefix over the lanes of one wave
+// Value of lane i - D (prefix direction) or i + D (suffix direction) of the
+// same 16-lane row, by DPP row_shr / row_shl; lanes whose source lies outside
+// the row get `id`.
+template <int D>
+__device__ inline uint32_t row_from_below(uint32_t v, uint32_t id) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x110 + D, 0xF, 0xF, false);  // row_shr:D
+}
+template <int D>
+__device__ inline uint32_t row_from_above(uint32_t v, uint32_t id) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x100 + D, 0xF, 0xF, false);  // row_shl:D
+}
+
+// inclusive prefix over the lanes of one wave: in-row steps by DPP, then the
+// totals of the lower rows (read as scalars) in front.  id: the identity.
 template <typename Op>
-__device__ inline uint32_t wave_incl_scan(uint32_t v, Op op) {
-  const uint32_t lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t o = __shfl_up(v, d, kWave);
-    if (lane >= (uint32_t)d) v = op(o, v);
-  }
-  return v;
+__device__ inline uint32_t wave_incl_scan(uint32_t v, Op op, uint32_t id) {
+  v = op(row_from_below<1>(v, id), v);
+  v = op(row_from_below<2>(v, id), v);
+  v = op(row_from_below<4>(v, id), v);
+  v = op(row_from_below<8>(v, id), v);
+  const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 15), r1 = __builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 47);
+  const uint32_t row = lane_id() >> 4;
+  const uint32_t b1 = r0, b2 = op(r0, r1), b3 = op(b2, r2);
+  const uint32_t before = row == 0 ? id : row == 1 ? b1 : row == 2 ? b2 : b3;
+  return op(before, v);
 }
 
 // inclusive suffix over the lanes of one wave: op(e_i, op(e_{i+1}, ...))
 template <typename Op>
-__device__ inline uint32_t wave_incl_suffix(uint32_t v, Op op) {
-  const uint32_t lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t o = __shfl_down(v, d, kWave);
-    if (lane + d < (uint32_t)kWave) v = op(v, o);
-  }
-  return v;
+__device__ inline uint32_t wave_incl_suffix(uint32_t v, Op op, uint32_t id) {
+  v = op(v, row_from_above<1>(v, id));
+  v = op(v, row_from_above<2>(v, id));
+  v = op(v, row_from_above<4>(v, id));
+  v = op(v, row_from_above<8>(v, id));
+  const uint32_t r1 = __builtin_amdgcn_readlane((int)v, 16), r2 = __builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = __builtin_amdgcn_readlane((int)v, 48);
+  const uint32_t row = lane_id() >> 4;
+  const uint32_t a2 = r3, a1 = op(r2, r3), a0 = op(r1, a1);
+  const uint32_t after = row == 3 ? id : row == 2 ? a2 : row == 1 ? a1 : a0;
+  return op(v, after);
 }
 
 // Exclusive prefix over the workgroup (blockDim.x = NT, a multiple of 64),
@@ -44,7 +63,7 @@ __device__ inline uint32_t wg_excl_scan(uint32_t v, uint32_t id, Op op, uint32_t
                                         uint32_t* total) {
   constexpr int NW = NT / kWave;
   const uint32_t lane = lane_id(), w = threadIdx.x / kWave;
-  const uint32_t incl = wave_incl_scan(v, op);
+  const uint32_t incl = wave_incl_scan(v, op, id);
   if (lane == kWave - 1) scratch[w] = incl;
   __syncthreads();
   uint32_t before = id;
@@ -52,8 +71,9 @@ __device__ inline uint32_t wg_excl_scan(uint32_t v, uint32_t id, Op op, uint32_t
   uint32_t all = id;
 #pragma unroll
   for (int i = 0; i < NW; ++i) all = op(all, scratch[i]);
-  uint32_t excl = __shfl_up(incl, 1, kWave);
-  excl = lane == 0 ? before : op(before, excl);
+  // lane i - 1 across the whole wave (wave_shr:1); lane 0 takes the identity
+  const uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)incl, 0x138, 0xF, 0xF, false);
+  const uint32_t excl = lane == 0 ? before : op(before, prev);
   __syncthreads();  // scratch may be reused right after
   if (total) *total = all;
   return excl;
@@ -66,7 +86,7 @@ __device__ inline uint32_t wg_excl_suffix(uint32_t v, uint32_t id, Op op, uint32
                                           uint32_t* total) {
   constexpr int NW = NT / kWave;
   const uint32_t lane = lane_id(), w = threadIdx.x / kWave;
-  const uint32_t incl = wave_incl_suffix(v, op);
+  const uint32_t incl = wave_incl_suffix(v, op, id);
   if (lane == 0) scratch[w] = incl;
   __syncthreads();
   uint32_t after = id;
@@ -74,8 +94,9 @@ __device__ inline uint32_t wg_excl_suffix(uint32_t v, uint32_t id, Op op, uint32
   uint32_t all = id;
 #pragma unroll
   for (int i = NW - 1; i >= 0; --i) all = op(scratch[i], all);
-  uint32_t excl = __shfl_down(incl, 1, kWave);
-  excl = lane == kWave - 1 ? after : op(excl, after);
+  // lane i + 1 across the whole wave (wave_shl:1); lane 63 takes the identity
+  const uint32_t next = (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)incl, 0x130, 0xF, 0xF, false);
+  const uint32_t excl = lane == kWave - 1 ? after : op(next, after);
   __syncthreads();
   if (total) *total = all;
   return excl;
