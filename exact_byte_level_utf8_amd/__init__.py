@@ -225,8 +225,10 @@ class Tokenizer:
         lib().tok_token_lengths(self._h, out.ctypes.data, v)
         return out
 
-    def set_profiling(self, on: bool) -> None:
-        _check(lib().tok_set_profiling(self._h, int(bool(on))), "tok_set_profiling")
+    def set_profiling(self, stages=True) -> None:
+        """stages: True for every stage, False for none, or a bit mask (bit i = STAGES[i])."""
+        mask = (1 << len(STAGES)) - 1 if stages is True else 0 if stages is False else int(stages)
+        _check(lib().tok_set_profiling(self._h, mask), "tok_set_profiling")
 
     def stage_ms(self) -> list[float]:
         out = (ctypes.c_float * len(STAGES))()

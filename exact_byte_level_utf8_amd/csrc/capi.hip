@@ -368,9 +368,9 @@ size_t tok_token_lengths(const tok_ctx* ctx, uint32_t* len_out, size_t n) {
   return v;
 }
 
-int tok_set_profiling(tok_ctx* ctx, int on) {
-  if (!ctx) return TOK_E_ARG;
-  ctx->prof = on != 0;
+int tok_set_profiling(tok_ctx* ctx, int stages) {
+  if (!ctx || stages < 0) return TOK_E_ARG;
+  ctx->prof = (uint32_t)stages & TOK_STAGES_ALL;
   return TOK_OK;
 }
 

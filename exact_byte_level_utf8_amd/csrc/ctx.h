@@ -94,7 +94,7 @@ struct tok_ctx {
   Counters* h_ctr = nullptr;
 
   hipStream_t stream = nullptr;
-  bool prof = false;
+  uint32_t prof = 0;  // bit i: time stage i with events
   hipEvent_t ev[kStages + 1] = {};
   float stage_ms[kStages] = {};
 
@@ -177,8 +177,11 @@ struct tok_ctx {
     return TOK_OK;
   }
 
+  // event i separates stage i - 1 from stage i; it is recorded when either
+  // neighbouring stage is timed
   void mark(int i, hipStream_t s) {
-    if (prof) (void)hipEventRecord(ev[i], s);
+    const uint32_t need = (prof >> i) | (i > 0 ? prof >> (i - 1) : 0u);
+    if (need & 1u) (void)hipEventRecord(ev[i], s);
   }
 
   // Enqueue the pipeline over d_text[0..n) and wait for it.  out_flags: stop
@@ -209,8 +212,9 @@ struct tok_ctx {
       const int last = n == 0 ? 0 : out_flags ? 1 : kStages;
       for (int i = 0; i < kStages; ++i) {
         float ms = 0.f;
-        if (i < last && hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) ms = 0.f;
-        stage_ms[i] = i < last ? ms : 0.f;
+        const bool timed = i < last && ((prof >> i) & 1u);
+        if (timed && hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) ms = 0.f;
+        stage_ms[i] = timed ? ms : 0.f;
       }
     }
     const volatile Counters* c = h_ctr;

@@ -72,24 +72,6 @@ __device__ inline void key_words(const uint8_t* text, uint32_t off, uint32_t len
   }
 }
 
-// Short whole-piece table: the token ID of key (a, b), probing from bucket h
-// on, or kNoRank.
-__device__ inline uint32_t word_probe_from(const Tables& T, uint64_t a, uint64_t b, uint32_t h) {
-  const ulonglong2* slots = reinterpret_cast<const ulonglong2*>(T.word_slots);
-  constexpr uint64_t kKeyMask = (1ull << 44) - 1;
-  for (uint32_t probe = 0; probe <= T.word_buckets; ++probe) {
-    const ulonglong2* bk = slots + (size_t)h * kBucket;
-    const ulonglong2 s0 = bk[0], s1 = bk[1], s2 = bk[2], s3 = bk[3];
-    if (s0.x == a && (s0.y & kKeyMask) == b) return (uint32_t)(s0.y >> 44);
-    if (s1.x == a && (s1.y & kKeyMask) == b) return (uint32_t)(s1.y >> 44);
-    if (s2.x == a && (s2.y & kKeyMask) == b) return (uint32_t)(s2.y >> 44);
-    if (s3.x == a && (s3.y & kKeyMask) == b) return (uint32_t)(s3.y >> 44);
-    if (s3.y == 0) return kNoRank;  // slots fill in order within a bucket
-    h = (h + 1) & T.word_buckets;
-  }
-  return kNoRank;
-}
-
 // Whole-piece probe of a 2..13-byte piece at text[off]: its token ID, or kNoRank.
 __device__ inline uint32_t word_lookup(const Tables& T, const uint8_t* text, uint32_t off, uint32_t len) {
   uint32_t w[4];
@@ -369,10 +351,10 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
 
   // phase 1: single bytes and whole-piece hits; the rest goes to the lists.
   // Thread (lc, q) owns bytes 2q, 2q + 1 of chunk lc.
-  const uint32_t lc = tid / kPerChunk, q = tid % kPerChunk;
-  const uint32_t w = c0 + lc < n_chunks ? s_flags[lc] : 0u;
-  const uint32_t mine = (w >> (kBytesPer * q)) & ((1u << kBytesPer) - 1u);
   {
+    const uint32_t lc = tid / kPerChunk, q = tid % kPerChunk;
+    const uint32_t w = c0 + lc < n_chunks ? s_flags[lc] : 0u;
+    const uint32_t mine = (w >> (kBytesPer * q)) & ((1u << kBytesPer) - 1u);
     // ends: the next piece start in this chunk, else in the next four chunks
     // (a piece with no start within 64 bytes is long, or runs to the end)
     const uint64_t c = c0 + lc;
@@ -393,38 +375,11 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
       off[b] = (uint32_t)(s0 - base);
       id[b] = len[b] == 1u ? (uint32_t)s_text[off[b]] : kNoRank;
     }
-    // short whole-piece table: both candidates' first buckets are loaded
-    // before either is compared, so their latencies overlap
-    if (T.word_slots) {
-      constexpr uint64_t kKeyMask = (1ull << 44) - 1;
-      const ulonglong2* slots = reinterpret_cast<const ulonglong2*>(T.word_slots);
-      uint64_t ka[kBytesPer], kb[kBytesPer];
-      uint32_t h[kBytesPer];
-      ulonglong2 x[kBytesPer][4];
+    // whole-piece tables: 2..13-byte pieces in the short table, 14..28 in the long one
 #pragma unroll
-      for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
-        const bool want = len[b] >= 2u && len[b] <= (uint32_t)kWordMax;
-        uint32_t wd[4];
-        key_words<4>(s_text, off[b], len[b], wd);
-        ka[b] = (uint64_t)wd[0] | ((uint64_t)wd[1] << 32);
-        kb[b] = ((uint64_t)wd[2] | ((uint64_t)(wd[3] & 0xFFu) << 32)) | ((uint64_t)len[b] << 40);
-        h[b] = want ? word_hash(ka[b], kb[b]) & T.word_buckets : 0u;
-        const ulonglong2* bk = slots + (size_t)h[b] * kBucket;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[b][i] = bk[i];
-      }
-#pragma unroll
-      for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
-        if (!(len[b] >= 2u && len[b] <= (uint32_t)kWordMax)) continue;
-        uint32_t got = kNoRank;
-#pragma unroll
-        for (int i = 3; i >= 0; --i)
-          if (x[b][i].x == ka[b] && (x[b][i].y & kKeyMask) == kb[b]) got = (uint32_t)(x[b][i].y >> 44);
-        if (got == kNoRank && x[b][3].y != 0)  // bucket full: keep probing (rare)
-          got = word_probe_from(T, ka[b], kb[b], (h[b] + 1) & T.word_buckets);
-        id[b] = got;
-      }
-    }
+    for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b)
+      if (T.word_slots && len[b] >= 2u && len[b] <= (uint32_t)kWordMax)
+        id[b] = word_lookup(T, s_text, off[b], len[b]);
 #pragma unroll
     for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b)
       if (T.long_slots && len[b] > (uint32_t)kWordMax && len[b] <= (uint32_t)kLongMax)
@@ -527,6 +482,14 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   // the chunk's total leaves, and its tokens are in the long-piece workspace.
   {
     int32_t* run = B.staging + __builtin_amdgcn_readfirstlane(s_first);
+    // this thread's piece starts, read again from LDS rather than kept live
+    // across the merge phase (the empty asm keeps the compiler from reusing,
+    // and so spilling, addresses computed before it)
+    uint32_t t3 = threadIdx.x;
+    __asm__ volatile("" : "+v"(t3));
+    const uint32_t lc = t3 / kPerChunk, q = t3 % kPerChunk;
+    const uint32_t w = c0 + lc < n_chunks ? s_flags[lc] : 0u;
+    const uint32_t mine = (w >> (kBytesPer * q)) & ((1u << kBytesPer) - 1u);
     uint32_t own = 0;
 #pragma unroll
     for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b)

@@ -242,16 +242,23 @@ int tok_get_info(const tok_ctx* ctx, tok_info* info);
 size_t tok_token_lengths(const tok_ctx* ctx, uint32_t* len_out, size_t n);
 
 /*
- * Stage timing (GraphTok, section 6.11, the per-stage profile).  With
- * profiling on, every call records HIP events around each device stage on the
- * stream it runs on; tok_stage_ms returns the last call's stage durations in
- * ms: [0] pre-tokenization (with the per-call set-up of the later passes),
- * [1] piece pass (single bytes, whole-piece hits, merge rounds of the
- * remaining pieces, one run of IDs per 1 KiB tile), [2] assembly (output
- * offsets of the runs and their copy).
- * Returns the number of stages written (at most n).
+ * Stage timing (GraphTok, section 6.11, the per-stage profile).
+ * tok_set_profiling(ctx, stages): stages is a bit mask of the stages to time
+ * (0 = off); every later call records HIP events around each of them on the
+ * stream it runs on (two events per isolated stage, shared between adjacent
+ * ones).  tok_stage_ms writes the last call's stage durations in ms, 0 for
+ * stages not timed: [0] pre-tokenization (with the per-call set-up of the
+ * later passes), [1] piece pass (single bytes, whole-piece hits, merge
+ * rounds of the remaining pieces, one run of IDs per 1 KiB tile), [2]
+ * assembly (output offsets of the runs and their copy).  Returns the number
+ * of stages written (at most n).  tok_set_profiling: TOK_E_ARG for a null
+ * context or a negative mask.
  */
-int tok_set_profiling(tok_ctx* ctx, int on);
+#define TOK_STAGE_PRETOK 1
+#define TOK_STAGE_PIECES 2
+#define TOK_STAGE_ASSEMBLE 4
+#define TOK_STAGES_ALL 7
+int tok_set_profiling(tok_ctx* ctx, int stages);
 int tok_stage_ms(const tok_ctx* ctx, float* ms, int n);
 
 #ifdef __cplusplus

@@ -317,3 +317,22 @@ def test_deterministic(cfg):
     a = t.encode(b)
     for _ in range(3):
         assert np.array_equal(t.encode(b), a)
+
+
+def test_stage_timing_mask(cfg):
+    """tok_set_profiling takes a stage mask: only the chosen stages get durations."""
+    t, o, tokb = cfg["gpt2"]
+    b = textgen.mix_text(14, 50_000).encode()
+    d = dev_bytes(b)
+    ids = torch.empty(len(b), dtype=torch.int32, device="cuda")
+    t.set_profiling(True)
+    t.encode_dev(d, ids)
+    ms = t.stage_ms()
+    assert len(ms) == len(tk.STAGES) and all(x > 0 for x in ms)
+    t.set_profiling(1 << tk.STAGES.index("pieces"))
+    n = t.encode_dev(d, ids)
+    ms = t.stage_ms()
+    assert ms[tk.STAGES.index("pieces")] > 0
+    assert all(x == 0 for i, x in enumerate(ms) if i != tk.STAGES.index("pieces"))
+    t.set_profiling(False)
+    _check("timed", ids[:n].cpu().numpy(), o.encode(b), b, tokb)
