@@ -117,7 +117,7 @@ __device__ inline uint32_t lds_word(const uint32_t* a, uint32_t b) {
 __device__ inline bool is_cont(uint32_t byte) { return (byte & 0xC0u) == 0x80u; }
 
 template <int PATTERN>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 6)
 pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off,
               uint32_t n_docs, Bufs B) {
   // window byte k (k in [-4, kWin + 12)) lives at byte 4 + k of s_raw / s_fl
@@ -125,8 +125,9 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   __shared__ uint32_t s_raw32[kBytes / 4];
   __shared__ uint32_t s_fl32[kBytes / 4];
   __shared__ uint32_t s_info[kWin];
-  __shared__ uint32_t s_scan[kThreads / kWave];
+  __shared__ uint32_t s_scan[kThreads / kWave], s_scan2[kThreads / kWave];
   __shared__ uint32_t s_misc[4];
+  __shared__ uint32_t s_agg[PATTERN == 1 ? kPT / 4 : 1];  // Llama-3 run states, a byte per tile position
   uint8_t* s_raw = reinterpret_cast<uint8_t*>(s_raw32);
   uint8_t* s_fl = reinterpret_cast<uint8_t*>(s_fl32);
 
@@ -254,52 +255,49 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   __syncthreads();
 
   // Llama-3 style: run-aggregate states before (forward) and after (backward)
-  // every tile position
-  uint32_t fst[kRounds], hst[kRounds];
-#pragma unroll
-  for (int j = 0; j < kRounds; ++j) fst[j] = hst[j] = 0;
+  // every tile position.  Thread t composes the elements of the four
+  // consecutive positions 4t .. 4t+3; one workgroup pass turns the per-thread
+  // compositions into exclusive prefixes (forward) and suffixes (backward);
+  // the carries into the tile come from wave reductions over the halos, or,
+  // for a run longer than a halo, from 4 KiB blocks in global memory.  The
+  // states go to LDS, one byte per position: n | g << 2 | h << 3.
   if (PATTERN == 1) {
-    if (tid == 0) {  // walk left through the halo until both forward aggregates reset
-      uint32_t acc = kFwdId, done = 0;
-      for (int k = kHalo - 1; k >= 0; --k) {
-        if (s_fl[k + kGuard] & kBOut) { done = 1; break; }
-        const uint32_t in = s_info[k];
-        if (in & kILead) {
-          acc = fwd_comp(fwd_elem(in), acc);
-          if (fwd_resolved(acc)) { done = 1; break; }
+    uint32_t carry_f, carry_h;
+    bool fdone, bdone;
+    {
+      // halo carries: wave 0 composes the 64 positions left of the tile,
+      // wave 1 the 64 right of it (identity past an undecoded lead)
+      if (wv == 0) {
+        const uint32_t in = s_info[lane];
+        const uint32_t acc = __builtin_amdgcn_readlane(
+            (int)wave_incl_scan((in & kILead) ? fwd_elem(in) : kFwdId, FwdOp(), kFwdId), 63);
+        if (lane == 0) {
+          s_misc[1] = fwd_apply(acc, 0);
+          s_misc[2] = fwd_resolved(acc) || lo <= 0;
         }
+      } else if (wv == 1) {
+        const uint32_t in = s_info[kHalo + kPT + lane];
+        const uint64_t und = __ballot((in & kIUndecoded) != 0);
+        const bool past = und && lane >= (uint32_t)__builtin_ctzll(und);
+        const uint32_t e = ((in & kILead) && !past) ? bwd_elem(in) : kBwdId;
+        const uint32_t acc = __builtin_amdgcn_readlane((int)wave_incl_suffix(e, BwdOp(), kBwdId), 0);
+        if (lane == 0) s_misc[3] = bwd_apply(acc, 0) | ((acc & 1u) << 1);
       }
-      s_misc[1] = fwd_apply(acc, 0);
-      s_misc[2] = done;
-    }
-    if (tid == kWave) {  // walk right until the backward aggregate resets
-      uint32_t acc = kBwdId, done = 0;
-      for (int k = kHalo + kPT; k < kWin; ++k) {
-        if (s_fl[k + kGuard] & kBOut) { done = 1; break; }
-        const uint32_t in = s_info[k];
-        if (in & kILead) {
-          if (in & kIUndecoded) break;
-          acc = bwd_comp(acc, bwd_elem(in));
-          if (acc & 1u) { done = 1; break; }
-        }
-      }
-      s_misc[3] = bwd_apply(acc, 0) | (done << 1);
     }
     __syncthreads();
-    uint32_t carry_f = __builtin_amdgcn_readfirstlane(s_misc[1]);
-    const bool fdone = __builtin_amdgcn_readfirstlane(s_misc[2]) != 0;
+    carry_f = __builtin_amdgcn_readfirstlane(s_misc[1]);
+    fdone = __builtin_amdgcn_readfirstlane(s_misc[2]) != 0;
     const uint32_t m3 = __builtin_amdgcn_readfirstlane(s_misc[3]);
-    uint32_t carry_h = m3 & 1u;
-    const bool bdone = (m3 >> 1) & 1u;
-    __syncthreads();
+    carry_h = m3 & 1u;
+    bdone = (m3 >> 1) & 1u;
     if (!fdone) {  // a run longer than the halo ends before the tile: reduce 4 KiB blocks
       uint32_t acc = kFwdId;
       for (int64_t end = base;; end -= kThreads * kChunk) {
         const int64_t start = end - kThreads * kChunk;
-        uint32_t fe, be;
-        chunk_elems_global(text, n, doc_off, n_docs, start + (int64_t)tid * kChunk, &fe, &be);
+        uint32_t fe2, be2;
+        chunk_elems_global(text, n, doc_off, n_docs, start + (int64_t)tid * kChunk, &fe2, &be2);
         uint32_t tot;
-        wg_excl_scan<kThreads>(fe, kFwdId, FwdOp(), s_scan, &tot);
+        wg_excl_scan<kThreads>(fe2, kFwdId, FwdOp(), s_scan, &tot);
         acc = __builtin_amdgcn_readfirstlane(fwd_comp(tot, acc));  // uniform loop exit
         if (fwd_resolved(acc) || start <= 0) break;
       }
@@ -308,34 +306,61 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     if (!bdone) {
       uint32_t acc = kBwdId;
       for (int64_t start = base + kPT;; start += kThreads * kChunk) {
-        uint32_t fe, be;
-        chunk_elems_global(text, n, doc_off, n_docs, start + (int64_t)tid * kChunk, &fe, &be);
+        uint32_t fe2, be2;
+        chunk_elems_global(text, n, doc_off, n_docs, start + (int64_t)tid * kChunk, &fe2, &be2);
         uint32_t tot;
-        wg_excl_suffix<kThreads>(be, kBwdId, BwdOp(), s_scan, &tot);
+        wg_excl_suffix<kThreads>(be2, kBwdId, BwdOp(), s_scan, &tot);
         acc = __builtin_amdgcn_readfirstlane(bwd_comp(acc, tot));  // uniform loop exit
         if ((acc & 1u) || start + kThreads * kChunk >= sn) break;
       }
       carry_h = bwd_apply(acc, 0);
     }
-    // forward: rounds in position order; backward: rounds in reverse order
+    // per-thread compositions of four consecutive positions, then the
+    // workgroup prefix (forward) and suffix (backward) of them
+    const uint4 q4 = reinterpret_cast<const uint4*>(s_info + kHalo)[tid];
+    const uint32_t in4[4] = {q4.x, q4.y, q4.z, q4.w};
+    uint32_t fe[4], be[4];
 #pragma unroll
-    for (int j = 0; j < kRounds; ++j) {
-      const uint32_t in = s_info[kHalo + tid + j * kThreads];
-      uint32_t tot;
-      const uint32_t pre = wg_excl_scan<kThreads>((in & kILead) ? fwd_elem(in) : kFwdId, kFwdId, FwdOp(),
-                                                  s_scan, &tot);
-      fst[j] = fwd_apply(pre, carry_f);
-      carry_f = fwd_apply(tot, carry_f);
+    for (int i = 0; i < 4; ++i) {
+      fe[i] = (in4[i] & kILead) ? fwd_elem(in4[i]) : kFwdId;
+      be[i] = (in4[i] & kILead) ? bwd_elem(in4[i]) : kBwdId;
+    }
+    const uint32_t fcomp = fwd_comp(fwd_comp(fwd_comp(fe[0], fe[1]), fe[2]), fe[3]);
+    const uint32_t bcomp = bwd_comp(bwd_comp(bwd_comp(be[0], be[1]), be[2]), be[3]);
+    const uint32_t finc = wave_incl_scan(fcomp, FwdOp(), kFwdId);
+    const uint32_t binc = wave_incl_suffix(bcomp, BwdOp(), kBwdId);
+    if (lane == kWave - 1) s_scan[wv] = finc;
+    if (lane == 0) s_scan2[wv] = binc;
+    __syncthreads();
+    uint32_t wbefore = kFwdId, wafter = kBwdId;
+#pragma unroll
+    for (uint32_t i = 0; i < (uint32_t)(kThreads / kWave); ++i) {
+      if (i < wv) wbefore = fwd_comp(wbefore, s_scan[i]);
     }
 #pragma unroll
-    for (int j = kRounds - 1; j >= 0; --j) {
-      const uint32_t in = s_info[kHalo + tid + j * kThreads];
-      uint32_t tot;
-      const uint32_t suf = wg_excl_suffix<kThreads>((in & kILead) ? bwd_elem(in) : kBwdId, kBwdId, BwdOp(),
-                                                    s_scan, &tot);
-      hst[j] = bwd_apply(suf, carry_h);
-      carry_h = bwd_apply(tot, carry_h);
+    for (int i = kThreads / kWave - 1; i >= 0; --i) {
+      if ((uint32_t)i > wv) wafter = bwd_comp(s_scan2[i], wafter);
     }
+    const uint32_t fprev = (uint32_t)__builtin_amdgcn_update_dpp((int)kFwdId, (int)finc, 0x138, 0xF, 0xF, false);
+    const uint32_t bnext = (uint32_t)__builtin_amdgcn_update_dpp((int)kBwdId, (int)binc, 0x130, 0xF, 0xF, false);
+    const uint32_t pre = fwd_comp(wbefore, lane == 0 ? kFwdId : fprev);         // elements before position 4t
+    const uint32_t suf = bwd_comp(lane == kWave - 1 ? kBwdId : bnext, wafter);  // elements after 4t + 3
+    // states of the four positions
+    uint32_t st4[4];
+    uint32_t acc = pre;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st4[i] = fwd_apply(acc, carry_f);
+      acc = fwd_comp(acc, fe[i]);
+    }
+    acc = suf;
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      st4[i] |= bwd_apply(acc, carry_h) << 3;
+      acc = bwd_comp(be[i], acc);
+    }
+    s_agg[tid] = st4[0] | (st4[1] << 8) | (st4[2] << 16) | (st4[3] << 24);
+    __syncthreads();
   }
 
   // the piece-start predicate at every tile position: the previous code
@@ -358,9 +383,11 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     const uint32_t len = (c >> kILenShift) & 7u;
     const uint32_t nx = s_info[k + len];
     const uint32_t n1 = (c & kILastInDoc) ? kNone : nx;
+    uint32_t agg = 0;
+    if (PATTERN == 1) agg = reinterpret_cast<const uint8_t*>(s_agg)[k - kHalo];
     const bool rule = PATTERN == 0 ? piece_start_gpt2(c, p[0], p[1], p[2], p[3], n1)
-                                   : piece_start_llama3(c, p[0], p[1], p[2], p[3], n1, fst[j] & 3u,
-                                                        (fst[j] >> 2) & 1u, hst[j] & 1u);
+                                   : piece_start_llama3(c, p[0], p[1], p[2], p[3], n1, agg & 3u, (agg >> 2) & 1u,
+                                                        (agg >> 3) & 1u);
     const bool st = (c & kILead) && rule;
     // this wave holds 64 consecutive positions: four flag words
     const uint64_t m = __ballot(st);
