@@ -309,11 +309,12 @@ __device__ void merge_long(const Tables& T, const uint8_t* __restrict__ text, ui
 }
 
 
-__global__ void __launch_bounds__(kPieceThreads, 8)
+template <int NT>
+__global__ void __launch_bounds__(NT, 8)
 piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, const uint64_t* __restrict__ doc_off,
              uint32_t n_docs, uint64_t* __restrict__ out_off) {
   constexpr int kChunksPerWg = kPieceTile / kChunk;  // 64
-  constexpr int kPerChunk = kPieceThreads / kChunksPerWg;  // 8 threads per chunk
+  constexpr int kPerChunk = NT / kChunksPerWg;  // threads per chunk
   constexpr int kBytesPer = kChunk / kPerChunk;             // 2 bytes per thread
   constexpr int kTextLds = kPieceTile + kWaveMax + 16;
   constexpr int kFlagLds = kChunksPerWg + 6;
@@ -339,11 +340,11 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   const uint64_t base = (uint64_t)tile * kPieceTile;
   const uint64_t c0 = (uint64_t)tile * kChunksPerWg;
   const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
-  for (int k = tid; k < kTextLds; k += kPieceThreads) {
+  for (int k = tid; k < kTextLds; k += NT) {
     const uint64_t p = base + k;
     s_text[k] = p < n ? text[p] : 0;
   }
-  for (int k = tid; k < kFlagLds; k += kPieceThreads) {
+  for (int k = tid; k < kFlagLds; k += NT) {
     const uint64_t c = c0 + k;
     s_flags[k] = c < n_chunks ? B.flags[c] : 0;
   }
@@ -519,7 +520,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
 
   // offsets, within this tile's run, of the documents that start in the tile
   if (doc_off) {
-    for (uint32_t d = s_doc0 + tid; d <= n_docs; d += kPieceThreads) {
+    for (uint32_t d = s_doc0 + tid; d <= n_docs; d += NT) {
       const uint64_t p = doc_off[d];
       if (p >= n || p >= base + kPieceTile) break;
       if (p < base) continue;  // only with unordered offsets, which the call rejects
@@ -540,7 +541,14 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
 void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, const uint64_t* doc_off,
                    uint32_t n_docs, uint64_t* out_off, hipStream_t s) {
   const uint32_t blocks = (uint32_t)((n + kPieceTile - 1) / kPieceTile);
-  if (blocks) piece_kernel<<<blocks, kPieceThreads, 0, s>>>(text, n, t, b, doc_off, n_docs, out_off);
+  if (!blocks) return;
+  // up to one tile per workgroup slot of the device (four 512-thread
+  // workgroups per CU) every tile starts at once with 8 waves; larger inputs
+  // use 4-wave workgroups, so twice as many tiles are in flight per CU
+  if (blocks <= kPieceSmallGrid)
+    piece_kernel<512><<<blocks, 512, 0, s>>>(text, n, t, b, doc_off, n_docs, out_off);
+  else
+    piece_kernel<256><<<blocks, 256, 0, s>>>(text, n, t, b, doc_off, n_docs, out_off);
 }
 
 }  // namespace tok

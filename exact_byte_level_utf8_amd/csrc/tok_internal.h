@@ -33,7 +33,7 @@ constexpr int kRowMax = 16;          // longest piece merged by one 16-lane row
 constexpr int kWaveMax = 64;         // longest piece merged by one wave in registers
 constexpr int kPretokTile = 1024;    // bytes per workgroup of the pre-tokenization pass
 constexpr int kPieceTile = 1024;     // bytes per workgroup of the piece pass
-constexpr int kPieceThreads = 512;   // threads per piece-pass workgroup (2 bytes each)
+constexpr uint32_t kPieceSmallGrid = 1024;  // piece-pass grids up to this use 512-thread workgroups
 constexpr uint32_t kNoRank = 0xFFFFFFFFu;
 constexpr uint64_t kEmptySlot = ~0ull;
 constexpr uint32_t kBucket = 4;      // hash-table slots probed with one set of loads
