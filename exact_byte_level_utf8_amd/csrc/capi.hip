@@ -206,7 +206,11 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
     if (hipSetDevice(device) != hipSuccess) break;
     if (hipStreamCreateWithFlags(&ctx->stream, hipStreamNonBlocking) != hipSuccess) break;
     bool ok = true;
-    for (auto& e : ctx->ev) ok = ok && hipEventCreate(&e) == hipSuccess;
+    // timing-only events: no system-scope fence (no cache write-back and
+    // invalidation around the timed kernels)
+    for (int i = 0; i < kStages; ++i)
+      ok = ok && hipEventCreateWithFlags(&ctx->ev0[i], hipEventDisableSystemFence) == hipSuccess &&
+           hipEventCreateWithFlags(&ctx->ev1[i], hipEventDisableSystemFence) == hipSuccess;
     if (!ok) break;
     if (hipMalloc((void**)&ctx->d_merge_slots, slots * 8) != hipSuccess ||
         hipMalloc((void**)&ctx->d_pair_rank, pr.size() * 4) != hipSuccess ||

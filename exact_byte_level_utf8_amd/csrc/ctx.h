@@ -95,7 +95,7 @@ struct tok_ctx {
 
   hipStream_t stream = nullptr;
   uint32_t prof = 0;  // bit i: time stage i with events
-  hipEvent_t ev[kStages + 1] = {};
+  hipEvent_t ev0[kStages] = {}, ev1[kStages] = {};  // start / end of each stage's kernel
   float stage_ms[kStages] = {};
 
   Tables tables(bool words = true) const {
@@ -177,12 +177,9 @@ struct tok_ctx {
     return TOK_OK;
   }
 
-  // event i separates stage i - 1 from stage i; it is recorded when either
-  // neighbouring stage is timed
-  void mark(int i, hipStream_t s) {
-    const uint32_t need = (prof >> i) | (i > 0 ? prof >> (i - 1) : 0u);
-    if (need & 1u) (void)hipEventRecord(ev[i], s);
-  }
+  // start and end events for stage i when it is timed, else none
+  hipEvent_t e0(int i) const { return (prof >> i) & 1u ? ev0[i] : nullptr; }
+  hipEvent_t e1(int i) const { return (prof >> i) & 1u ? ev1[i] : nullptr; }
 
   // Enqueue the pipeline over d_text[0..n) and wait for it.  out_flags: stop
   // after pre-tokenization, with the flag words written there.
@@ -193,17 +190,13 @@ struct tok_ctx {
     if (out_flags) bb.flags = out_flags;
     bb.gen = ++gen;
     const Tables t = tables(words);
-    mark(0, s);
     if (n == 0) {  // only a batch of empty documents gets here
       launch_empty_batch(bb, doc_off, n_docs, out_off, s);
     } else {
-      launch_pretok(text, n, doc_off, n_docs, pattern, bb, s);
-      mark(1, s);
+      launch_pretok(text, n, doc_off, n_docs, pattern, bb, s, e0(0), e1(0));
       if (!out_flags) {
-        launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s);
-        mark(2, s);
-        launch_assemble(n, bb, out, out_cap, doc_off, n_docs, out_off, s);
-        mark(3, s);
+        launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s, e0(1), e1(1));
+        launch_assemble(n, bb, out, out_cap, doc_off, n_docs, out_off, s, e0(2), e1(2));
       }
     }
     HIP_OK(hipGetLastError());
@@ -213,7 +206,7 @@ struct tok_ctx {
       for (int i = 0; i < kStages; ++i) {
         float ms = 0.f;
         const bool timed = i < last && ((prof >> i) & 1u);
-        if (timed && hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) ms = 0.f;
+        if (timed && hipEventElapsedTime(&ms, ev0[i], ev1[i]) != hipSuccess) ms = 0.f;
         stage_ms[i] = timed ? ms : 0.f;
       }
     }
@@ -264,8 +257,10 @@ struct tok_ctx {
     dfree(d_outoff);
     hfree(h_doc);
     hfree(h_ctr);
-    for (auto& e : ev)
-      if (e) (void)hipEventDestroy(e);
+    for (int i = 0; i < kStages; ++i) {
+      if (ev0[i]) (void)hipEventDestroy(ev0[i]);
+      if (ev1[i]) (void)hipEventDestroy(ev1[i]);
+    }
     if (stream) (void)hipStreamDestroy(stream);
   }
 };

@@ -88,9 +88,10 @@ __global__ void empty_batch_kernel(Bufs B, const uint64_t* __restrict__ doc_off,
 }  // namespace
 
 void launch_assemble(uint64_t n, Bufs b, int32_t* out, uint64_t cap, const uint64_t* doc_off,
-                     uint32_t n_docs, uint64_t* out_off, hipStream_t s) {
+                     uint32_t n_docs, uint64_t* out_off, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const uint32_t tiles = (uint32_t)((n + kPieceTile - 1) / kPieceTile);
-  if (tiles) assemble_kernel<<<tiles, kAsmThreads, 0, s>>>(n, b, out, cap, doc_off, n_docs, out_off);
+  if (tiles)
+    launch_on(assemble_kernel, dim3(tiles), dim3(kAsmThreads), s, e0, e1, n, b, out, cap, doc_off, n_docs, out_off);
 }
 
 void launch_empty_batch(Bufs b, const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s) {

@@ -539,16 +539,16 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
 }  // namespace
 
 void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, const uint64_t* doc_off,
-                   uint32_t n_docs, uint64_t* out_off, hipStream_t s) {
+                   uint32_t n_docs, uint64_t* out_off, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const uint32_t blocks = (uint32_t)((n + kPieceTile - 1) / kPieceTile);
   if (!blocks) return;
   // up to one tile per workgroup slot of the device (four 512-thread
   // workgroups per CU) every tile starts at once with 8 waves; larger inputs
   // use 4-wave workgroups, so twice as many tiles are in flight per CU
   if (blocks <= kPieceSmallGrid)
-    piece_kernel<512><<<blocks, 512, 0, s>>>(text, n, t, b, doc_off, n_docs, out_off);
+    launch_on(piece_kernel<512>, dim3(blocks), dim3(512), s, e0, e1, text, n, t, b, doc_off, n_docs, out_off);
   else
-    piece_kernel<256><<<blocks, 256, 0, s>>>(text, n, t, b, doc_off, n_docs, out_off);
+    launch_on(piece_kernel<256>, dim3(blocks), dim3(256), s, e0, e1, text, n, t, b, doc_off, n_docs, out_off);
 }
 
 }  // namespace tok

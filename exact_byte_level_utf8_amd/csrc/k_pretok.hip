@@ -402,13 +402,13 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
 }  // namespace
 
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
-                   int pattern, Bufs b, hipStream_t s) {
+                   int pattern, Bufs b, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const uint32_t tiles = (uint32_t)((n + kPretokTile - 1) / kPretokTile);
   if (!tiles) return;
   if (pattern == 0)
-    pretok_kernel<0><<<tiles, kThreads, 0, s>>>(text, n, doc_off, n_docs, b);
+    launch_on(pretok_kernel<0>, dim3(tiles), dim3(kThreads), s, e0, e1, text, n, doc_off, n_docs, b);
   else
-    pretok_kernel<1><<<tiles, kThreads, 0, s>>>(text, n, doc_off, n_docs, b);
+    launch_on(pretok_kernel<1>, dim3(tiles), dim3(kThreads), s, e0, e1, text, n, doc_off, n_docs, b);
 }
 
 }  // namespace tok

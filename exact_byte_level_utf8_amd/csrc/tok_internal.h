@@ -120,13 +120,26 @@ __device__ inline uint32_t first_doc_at_or_after(const uint64_t* doc_off, uint32
   return lo;
 }
 
-// Kernel launchers (defined in the .hip files).
+// Launch kernel k on stream s, between event records e0 and e1 when the
+// stage is timed.
+template <typename... KArgs, typename... Args>
+inline void launch_on(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
+                      Args... args) {
+  if (e0) (void)hipEventRecord(e0, s);
+  k<<<grid, block, 0, s>>>(args...);
+  if (e1) (void)hipEventRecord(e1, s);
+}
+
+// Kernel launchers (defined in the .hip files); e0 / e1: optional events
+// around the stage's kernel.
 void launch_empty_batch(Bufs b, const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s);
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
-                   int pattern, Bufs b, hipStream_t s);
+                   int pattern, Bufs b, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, const uint64_t* doc_off,
-                   uint32_t n_docs, uint64_t* out_off, hipStream_t s);
+                   uint32_t n_docs, uint64_t* out_off, hipStream_t s, hipEvent_t e0 = nullptr,
+                   hipEvent_t e1 = nullptr);
 void launch_assemble(uint64_t n, Bufs b, int32_t* out, uint64_t cap, const uint64_t* doc_off,
-                     uint32_t n_docs, uint64_t* out_off, hipStream_t s);
+                     uint32_t n_docs, uint64_t* out_off, hipStream_t s, hipEvent_t e0 = nullptr,
+                     hipEvent_t e1 = nullptr);
 
 }  // namespace tok

@@ -244,9 +244,9 @@ size_t tok_token_lengths(const tok_ctx* ctx, uint32_t* len_out, size_t n);
 /*
  * Stage timing (GraphTok, section 6.11, the per-stage profile).
  * tok_set_profiling(ctx, stages): stages is a bit mask of the stages to time
- * (0 = off); every later call records HIP events around each of them on the
- * stream it runs on (two events per isolated stage, shared between adjacent
- * ones).  tok_stage_ms writes the last call's stage durations in ms, 0 for
+ * (0 = off); in every later call a pair of HIP events brackets the kernel of
+ * each timed stage on the stream it runs on (timing-only events, without a
+ * system-scope fence).  tok_stage_ms writes the last call's stage durations in ms, 0 for
  * stages not timed: [0] pre-tokenization (with the per-call set-up of the
  * later passes), [1] piece pass (single bytes, whole-piece hits, merge
  * rounds of the remaining pieces, one run of IDs per 1 KiB tile), [2]
