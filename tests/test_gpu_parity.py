@@ -118,7 +118,9 @@ def _check(name, got, want, b, tokb):
 @pytest.mark.parametrize("name,gen,seed,n_chars", [
     ("tiny", "tiny", 1, 10_000),
     ("gpt2", "mix", 2, 1_000_000),
+    ("gpt2", "mix", 21, 2_500_000),   # more tiles than one device generation: 4-wave piece workgroups
     ("llama3", "mix", 3, 3_000_000),
+    ("llama3", "mix", 31, 700_000),   # fewer tiles than one generation: 8-wave piece workgroups
 ])
 def test_workload_parity(cfg, name, gen, seed, n_chars):
     t, o, tokb = cfg[name]
@@ -141,7 +143,8 @@ def test_adversarial_parity(cfg, name):
 def test_ragged_sizes(cfg, name):
     t, o, tokb = cfg[name]
     base = textgen.mix_text(5, 40_000).encode()
-    for n in [1, 2, 3, 15, 16, 17, 31, 33, 63, 64, 65, 4095, 4096, 4097, 4160, 8191, 8192, 12289, 40_000]:
+    for n in [1, 2, 3, 15, 16, 17, 31, 33, 63, 64, 65, 1023, 1024, 1025, 2047, 2048, 4095, 4096, 4097, 4160,
+              8191, 8192, 12289, 40_000]:
         b = base[:n]
         while b:
             try:
@@ -336,3 +339,39 @@ def test_stage_timing_mask(cfg):
     assert all(x == 0 for i, x in enumerate(ms) if i != tk.STAGES.index("pieces"))
     t.set_profiling(False)
     _check("timed", ids[:n].cpu().numpy(), o.encode(b), b, tokb)
+
+
+def test_all_empty_batch(cfg):
+    """Every document empty: no tile runs; offsets are all zero (host and device
+    entry), and a nonzero offset in an empty text is rejected on the device."""
+    t, _, _ = cfg["llama3"]
+    off = np.zeros(6, dtype=np.uint64)
+    ids, out_off = t.encode_batch(b"", off)
+    assert len(ids) == 0 and (out_off == 0).all()
+    d = torch.empty(0, dtype=torch.uint8, device="cuda")
+    d_ids = torch.empty(1, dtype=torch.int32, device="cuda")
+    for good, arr in ((True, off), (False, np.array([0, 0, 1, 0], dtype=np.uint64))):
+        d_off = torch.tensor(arr.astype(np.int64), device="cuda").view(torch.uint64)
+        d_out = torch.full((len(arr),), 7, dtype=torch.int64, device="cuda").view(torch.uint64)
+        if good:
+            assert t.encode_batch_dev(d, d_off, d_ids, d_out) == 0
+            assert (d_out.view(torch.int64).cpu().numpy() == 0).all()
+        else:
+            with pytest.raises(tk.TokError) as e:
+                t.encode_batch_dev(d, d_off, d_ids, d_out)
+            assert e.value.code == tk.TOK_E_ARG
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_many_tiny_documents(cfg, name):
+    """Thousands of 0..5-byte documents: many document starts per tile and per
+    16-byte chunk, and more documents than threads in a workgroup."""
+    t, o, tokb = cfg[name]
+    rng = random.Random(77)
+    alpha = ["a", "b", " ", "1", "'", "s", "\n", "é", ".", "😀"]
+    docs = ["".join(rng.choice(alpha) for _ in range(rng.randint(0, 3))) for _ in range(6000)]
+    data, off = textgen.pack_docs(docs)
+    want_ids, want_off = o.encode_batch(data, off)
+    ids, out_off = t.encode_batch(data, off)
+    assert np.array_equal(out_off, want_off)
+    _check(name, ids, want_ids, data, tokb)
