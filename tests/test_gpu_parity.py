@@ -375,3 +375,36 @@ def test_many_tiny_documents(cfg, name):
     ids, out_off = t.encode_batch(data, off)
     assert np.array_equal(out_off, want_off)
     _check(name, ids, want_ids, data, tokb)
+
+
+FUZZ_ALPHA = (list("abcdefghijklmnopqrstuvwxyzSTRVMLD") + list("0123456789") + [" ", "  ", "\t", "\n", "\r",
+              "\r\n", " ", "\u0085", " ", "　"] + list(".,;:!?'\"()[]{}<>=+-*/\\|&^%$#@~`_") +
+              ["é", "ß", "ſ", "Ω", "中", "文", "ひ", "한", "́", "²", "½", "Ⅳ", "😀", "🧪", "\U0001F1FA"])
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_random_texts(cfg, name):
+    """Seeded random texts over a rich alphabet (letters, contraction letters in
+    both cases, digits, every whitespace kind, punctuation, accents, CJK,
+    combining marks, other number forms, emoji), with runs, as one batch and as
+    single requests."""
+    t, o, tokb = cfg[name]
+    rng = random.Random(1234 if name == "gpt2" else 4321)
+    docs = []
+    for _ in range(400):
+        n = rng.choice([0, 1, 2, 5, 17, 64, 300, 1500, 5000])
+        parts = []
+        while len(parts) < n:
+            tok = rng.choice(FUZZ_ALPHA)
+            parts.append(tok * rng.choice([1, 1, 1, 2, 3, 8, 70]))
+        docs.append("".join(parts))
+    data, off = textgen.pack_docs(docs)
+    want_ids, want_off = o.encode_batch(data, off)
+    ids, out_off = t.encode_batch(data, off)
+    assert np.array_equal(out_off, want_off)
+    _check(name, ids, want_ids, data, tokb)
+    for s in docs[:60]:
+        b = s.encode()
+        _check(name, t.encode(b), o.encode(b), b, tokb)
+    whole = "".join(docs).encode()
+    _check(name, t.encode(whole), o.encode(whole), whole, tokb)
