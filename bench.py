@@ -17,6 +17,8 @@ Also reported, outside the headline value:
     the committed rocprofv3 summary when it matches the kernel's sources;
   - complete_call: host bytes -> host int32 IDs through tok_encode (pinned
     staging, both transfers), the PCIe-inclusive rate;
+  - graph_ab: median call time without stage timing, eager launches against
+    a replayed HIP graph of the same call (tok_set_graph);
   - cpu_baseline: the CPU oracle on the same request, single-threaded.
 """
 from __future__ import annotations
@@ -247,6 +249,28 @@ def main() -> int:
         complete = {"p50_ms": round(1e3 * med, 4), "mbps": round(n_bytes / med / 1e6, 1),
                     "note": "tok_encode: pinned staging + H2D text + pipeline + D2H IDs"}
 
+    # graph replay A/B (outside the timed region): the same step without stage
+    # timing, three launches per call against one replayed graph per call
+    def median_step(k: int) -> float:
+        v = []
+        for _ in range(k):
+            s0 = time.perf_counter()
+            assert step() == n_tokens
+            v.append(time.perf_counter() - s0)
+        return statistics.median(v)
+
+    k_ab = max(20, args.steps)
+    eager_p50 = median_step(k_ab)
+    tok.set_graph(True)
+    step()
+    step()  # the second call of a shape captures its graph
+    graph_p50 = median_step(k_ab)
+    graphs_held = tok.graph_count()
+    tok.set_graph(False)
+    graph_ab = {"eager_p50_ms": round(1e3 * eager_p50, 4), "graph_p50_ms": round(1e3 * graph_p50, 4),
+                "graphs": graphs_held, "steps": k_ab}
+    log(f"[bench] graph A/B: {graph_ab}")
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -291,6 +315,7 @@ def main() -> int:
                      "traffic": measured_traffic(args.workload, dom),
                      "algorithmic_bytes": alg, "avg_ms": dom_ms},
         "complete_call": complete,
+        "graph_ab": graph_ab,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

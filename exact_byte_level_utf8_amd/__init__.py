@@ -25,7 +25,7 @@ TOK_E_CAPACITY, TOK_E_TOOLONG, TOK_E_DEVICE, TOK_E_NOMEM, TOK_E_SESSION = 5, 6, 
 EXPORTS = (
     "tok_load", "tok_free", "tok_strerror", "tok_encode", "tok_encode_dev", "tok_encode_batch",
     "tok_encode_batch_dev", "tok_pretokenize_dev", "tok_repair", "tok_sync_boundary", "tok_get_info",
-    "tok_token_lengths", "tok_set_profiling", "tok_stage_ms",
+    "tok_token_lengths", "tok_set_graph", "tok_graph_count", "tok_set_profiling", "tok_stage_ms",
 )
 
 
@@ -74,11 +74,14 @@ def lib() -> ctypes.CDLL:
         L.tok_get_info.argtypes = [vp, ctypes.POINTER(TokInfo)]
         L.tok_token_lengths.argtypes = [vp, vp, sz]
         L.tok_token_lengths.restype = sz
+        L.tok_set_graph.argtypes = [vp, i32]
+        L.tok_graph_count.argtypes = [vp]
+        L.tok_graph_count.restype = sz
         L.tok_set_profiling.argtypes = [vp, i32]
         L.tok_stage_ms.argtypes = [vp, vp, i32]
         for name in ("tok_load", "tok_encode", "tok_encode_dev", "tok_encode_batch",
                      "tok_encode_batch_dev", "tok_pretokenize_dev", "tok_repair", "tok_sync_boundary",
-                     "tok_get_info", "tok_set_profiling", "tok_stage_ms"):
+                     "tok_get_info", "tok_set_graph", "tok_set_profiling", "tok_stage_ms"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -224,6 +227,13 @@ class Tokenizer:
         out = np.zeros(v, dtype=np.uint32)
         lib().tok_token_lengths(self._h, out.ctypes.data, v)
         return out
+
+    def set_graph(self, on: bool = True) -> None:
+        """Replay a captured HIP graph for call shapes met before (tok_set_graph)."""
+        _check(lib().tok_set_graph(self._h, 1 if on else 0), "tok_set_graph")
+
+    def graph_count(self) -> int:
+        return int(lib().tok_graph_count(self._h))
 
     def set_profiling(self, stages=True) -> None:
         """stages: True for every stage, False for none, or a bit mask (bit i = STAGES[i])."""

@@ -204,7 +204,9 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
   int rc = TOK_E_DEVICE;
   do {
     if (hipSetDevice(device) != hipSuccess) break;
-    if (hipStreamCreateWithFlags(&ctx->stream, hipStreamNonBlocking) != hipSuccess) break;
+    // a blocking stream: ordered with the legacy default stream, on which
+    // callers that pass no stream usually produced the input
+    if (hipStreamCreate(&ctx->stream) != hipSuccess) break;
     bool ok = true;
     // timing-only events: no system-scope fence (no cache write-back and
     // invalidation around the timed kernels)
@@ -371,6 +373,17 @@ size_t tok_token_lengths(const tok_ctx* ctx, uint32_t* len_out, size_t n) {
   if (len_out) std::memcpy(len_out, ctx->tok_len.data(), std::min(n, v) * 4);
   return v;
 }
+
+int tok_set_graph(tok_ctx* ctx, int on) {
+  if (!ctx || on < 0 || on > 1) return TOK_E_ARG;
+  DeviceGuard g(ctx->device);
+  (void)hipStreamSynchronize(ctx->stream);
+  ctx->graph_mode = on == 1;
+  if (!ctx->graph_mode) ctx->drop_graphs();
+  return TOK_OK;
+}
+
+size_t tok_graph_count(const tok_ctx* ctx) { return ctx ? ctx->graphs.size() : 0; }
 
 int tok_set_profiling(tok_ctx* ctx, int stages) {
   if (!ctx || stages < 0) return TOK_E_ARG;

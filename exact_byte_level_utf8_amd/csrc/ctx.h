@@ -55,6 +55,32 @@ inline void hfree(T*& p) {
 
 constexpr int kStages = 3;
 
+// Key of a captured pipeline: every argument baked into its kernel launches.
+struct GraphKey {
+  const uint8_t* text;
+  uint64_t n;
+  const uint64_t* doc_off;
+  uint32_t n_docs;
+  int32_t* out;
+  uint64_t out_cap;
+  uint64_t* out_off;
+  hipStream_t s;
+  bool words;
+  bool operator==(const GraphKey& o) const {
+    return text == o.text && n == o.n && doc_off == o.doc_off && n_docs == o.n_docs && out == o.out &&
+           out_cap == o.out_cap && out_off == o.out_off && s == o.s && words == o.words;
+  }
+};
+
+struct GraphEntry {
+  GraphKey key;
+  hipGraphExec_t exec;
+  uint64_t gen;   // the call number baked into the graph's status reports
+  uint64_t used;  // last use, for eviction
+};
+
+constexpr size_t kMaxGraphs = 8;
+
 struct tok_ctx {
   int device = 0;
   int pattern = 0;
@@ -98,6 +124,18 @@ struct tok_ctx {
   hipEvent_t ev0[kStages] = {}, ev1[kStages] = {};  // start / end of each stage's kernel
   float stage_ms[kStages] = {};
 
+  // graph replay (off by default): one captured pipeline per call shape
+  bool graph_mode = false;
+  std::vector<GraphEntry> graphs;
+  std::vector<GraphKey> seen;  // shapes met once, not captured yet
+  uint64_t graph_tick = 0;
+
+  void drop_graphs() {
+    for (auto& g : graphs) (void)hipGraphExecDestroy(g.exec);
+    graphs.clear();
+    seen.clear();
+  }
+
   Tables tables(bool words = true) const {
     Tables t{};
     t.merge_slots = d_merge_slots;
@@ -112,6 +150,7 @@ struct tok_ctx {
   }
 
   void free_scratch() {
+    drop_graphs();  // their launches point into the scratch
     dfree(b.flags);
     dfree(b.staging);
     dfree(b.tile_cnt);
@@ -160,6 +199,7 @@ struct tok_ctx {
   int ensure_docs(uint64_t n_docs) {
     if (n_docs + 1 <= doc_cap && d_doc) return TOK_OK;
     (void)hipStreamSynchronize(stream);
+    drop_graphs();
     dfree(d_doc);
     dfree(d_outoff);
     hfree(h_doc);
@@ -181,23 +221,85 @@ struct tok_ctx {
   hipEvent_t e0(int i) const { return (prof >> i) & 1u ? ev0[i] : nullptr; }
   hipEvent_t e1(int i) const { return (prof >> i) & 1u ? ev1[i] : nullptr; }
 
-  // Enqueue the pipeline over d_text[0..n) and wait for it.  out_flags: stop
-  // after pre-tokenization, with the flag words written there.
-  int run(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, int32_t* out,
-          uint64_t out_cap, uint64_t* out_off, hipStream_t s, bool words, uint16_t* out_flags,
-          uint32_t* total) {
-    Bufs bb = b;
-    if (out_flags) bb.flags = out_flags;
-    bb.gen = ++gen;
+  // The three stages of one call, enqueued on s (eagerly or under capture).
+  void enqueue(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, int32_t* out,
+               uint64_t out_cap, uint64_t* out_off, hipStream_t s, const Bufs& bb, bool words,
+               uint16_t* out_flags) {
     const Tables t = tables(words);
     if (n == 0) {  // only a batch of empty documents gets here
       launch_empty_batch(bb, doc_off, n_docs, out_off, s);
-    } else {
-      launch_pretok(text, n, doc_off, n_docs, pattern, bb, s, e0(0), e1(0));
-      if (!out_flags) {
-        launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s, e0(1), e1(1));
-        launch_assemble(n, bb, out, out_cap, doc_off, n_docs, out_off, s, e0(2), e1(2));
+      return;
+    }
+    launch_pretok(text, n, doc_off, n_docs, pattern, bb, s, e0(0), e1(0));
+    if (out_flags) return;
+    launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s, e0(1), e1(1));
+    launch_assemble(n, bb, out, out_cap, doc_off, n_docs, out_off, s, e0(2), e1(2));
+  }
+
+  // The captured pipeline for this call shape: found, or captured now on s
+  // with a fresh call number when the shape was met before.  nullptr for a
+  // shape met for the first time (it runs eagerly, so one-off shapes pay no
+  // capture) or when capture fails.
+  GraphEntry* graph_for(const GraphKey& k) {
+    for (auto& g : graphs)
+      if (g.key == k) {
+        g.used = ++graph_tick;
+        return &g;
       }
+    auto it = std::find(seen.begin(), seen.end(), k);
+    if (it == seen.end()) {
+      if (seen.size() >= 2 * kMaxGraphs) seen.erase(seen.begin());
+      seen.push_back(k);
+      return nullptr;
+    }
+    seen.erase(it);
+    Bufs bb = b;
+    bb.gen = ++gen;
+    hipGraph_t gr = nullptr;
+    hipGraphExec_t ex = nullptr;
+    if (hipStreamBeginCapture(k.s, hipStreamCaptureModeThreadLocal) != hipSuccess) return nullptr;
+    enqueue(k.text, k.n, k.doc_off, k.n_docs, k.out, k.out_cap, k.out_off, k.s, bb, k.words, nullptr);
+    const bool captured = hipStreamEndCapture(k.s, &gr) == hipSuccess && gr;
+    const bool made = captured && hipGraphInstantiate(&ex, gr, nullptr, nullptr, 0) == hipSuccess;
+    if (gr) (void)hipGraphDestroy(gr);
+    if (!made) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    if (graphs.size() >= kMaxGraphs) {
+      auto lru = std::min_element(graphs.begin(), graphs.end(),
+                                  [](const GraphEntry& a, const GraphEntry& c) { return a.used < c.used; });
+      (void)hipGraphExecDestroy(lru->exec);
+      graphs.erase(lru);
+    }
+    graphs.push_back(GraphEntry{k, ex, bb.gen, ++graph_tick});
+    return &graphs.back();
+  }
+
+  // Enqueue the pipeline over d_text[0..n) and wait for it.  out_flags: stop
+  // after pre-tokenization, with the flag words written there.  In graph mode
+  // a call without stage timing replays the pipeline captured for its shape;
+  // the status words are cleared first, since every replay reports the call
+  // number that was captured.
+  int run(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, int32_t* out,
+          uint64_t out_cap, uint64_t* out_off, hipStream_t s, bool words, uint16_t* out_flags,
+          uint32_t* total) {
+    volatile Counters* c = h_ctr;
+    uint64_t call = 0;
+    GraphEntry* g = nullptr;
+    if (graph_mode && !prof && !out_flags && n > 0)
+      g = graph_for(GraphKey{text, n, doc_off, n_docs, out, out_cap, out_off, s, words});
+    if (g) {
+      call = g->gen;
+      c->err_utf8 = 0;
+      c->err_docs = 0;
+      c->done = 0;
+      HIP_OK(hipGraphLaunch(g->exec, s));
+    } else {
+      Bufs bb = b;
+      if (out_flags) bb.flags = out_flags;
+      bb.gen = call = ++gen;
+      enqueue(text, n, doc_off, n_docs, out, out_cap, out_off, s, bb, words, out_flags);
     }
     HIP_OK(hipGetLastError());
     HIP_OK(hipStreamSynchronize(s));
@@ -210,11 +312,10 @@ struct tok_ctx {
         stage_ms[i] = timed ? ms : 0.f;
       }
     }
-    const volatile Counters* c = h_ctr;
-    if (c->err_docs == bb.gen) return TOK_E_ARG;
-    if (c->err_utf8 == bb.gen) return TOK_E_UTF8;
+    if (c->err_docs == call) return TOK_E_ARG;
+    if (c->err_utf8 == call) return TOK_E_UTF8;
     if (out_flags) return TOK_OK;
-    if (c->done != bb.gen) return TOK_E_DEVICE;
+    if (c->done != call) return TOK_E_DEVICE;
     if (total) *total = c->total;
     return TOK_OK;
   }
@@ -247,7 +348,7 @@ struct tok_ctx {
 
   ~tok_ctx() {
     if (stream) (void)hipStreamSynchronize(stream);
-    free_scratch();
+    free_scratch();  // and the captured graphs
     dfree(d_merge_slots);
     dfree(d_pair_rank);
     dfree(d_word_slots);

@@ -121,7 +121,8 @@ int tok_encode(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids, size
  * host/device transfer of text or IDs (GraphTok, section 5, the device
  * buffer handoff).  d_text: len bytes on the context's device; d_ids: cap
  * int32 on the device; stream: hipStream_t to enqueue on (NULL = the
- * context's own stream).  On TOK_E_CAPACITY the first cap IDs are written and
+ * context's own stream, a blocking stream: it runs after work queued before
+ * the call on the legacy default stream).  On TOK_E_CAPACITY the first cap IDs are written and
  * *n_out is the full count; on TOK_E_UTF8 the content of d_ids is unspecified.
  */
 int tok_encode_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, int32_t* d_ids, size_t cap,
@@ -254,6 +255,24 @@ size_t tok_token_lengths(const tok_ctx* ctx, uint32_t* len_out, size_t n);
  * of stages written (at most n).  tok_set_profiling: TOK_E_ARG for a null
  * context or a negative mask.
  */
+/*
+ * Graph replay (GraphTok, section 4 "Design", graph-resident execution, and
+ * section 5 "Implementation", captured execution).  tok_set_graph(ctx, 1)
+ * turns it on: a call whose shape -- text and output pointers, sizes,
+ * document offsets, stream -- was met before replays one HIP graph of the
+ * three kernels captured for that shape, instead of three launches; a shape
+ * met for the first time runs eagerly.  At most 8 graphs are held (least
+ * recently used evicted); growing the context's buffers drops them all, and
+ * so does tok_set_graph(ctx, 0), the default.  Calls with stage timing on,
+ * tok_pretokenize_dev and empty batches always run eagerly.  Results are the
+ * same either way.  A replay reuses the launch geometry of its shape, so
+ * graphs are keyed by exact size rather than by power-of-two capacity class.
+ * tok_set_graph: TOK_E_ARG for a null context or on outside {0, 1}.
+ * tok_graph_count: the number of graphs held (0 for a null context).
+ */
+int tok_set_graph(tok_ctx* ctx, int on);
+size_t tok_graph_count(const tok_ctx* ctx);
+
 #define TOK_STAGE_PRETOK 1
 #define TOK_STAGE_PIECES 2
 #define TOK_STAGE_ASSEMBLE 4

@@ -65,4 +65,7 @@ def test_null_arguments():
     assert L.tok_repair(None, None, 0, 0, None, 0, 0, ctypes.byref(n), None) == tk.TOK_E_ARG
     assert L.tok_sync_boundary(7, 97, 32) == 0  # unknown pattern
     assert L.tok_strerror(tk.TOK_E_UTF8) == b"malformed UTF-8 input"
+    assert L.tok_set_graph(None, 1) == tk.TOK_E_ARG
+    assert L.tok_graph_count(None) == 0
+    assert L.tok_set_profiling(None, 1) == tk.TOK_E_ARG
     L.tok_free(None)
