@@ -5,14 +5,16 @@
 // lowest rank wins, the leftmost pair on equal rank, and the pair becomes ID
 // 256 + rank (GraphTok, section 4 "Warp-cooperative BPE").
 //
-// piece_kernel: one workgroup per 1 KiB of piece starts, in two phases.
+// piece_kernel: one workgroup per 1 KiB of piece starts, in three phases.
 //   1. One thread per 2 bytes resolves the pieces that need no merge loop: a
 //      1-byte piece is its byte's ID, and a 2..28-byte piece that is a whole
 //      vocabulary string whose own BPE is that token (checked for every string
 //      at load) is one probe of a whole-piece table (TokTier, section 4 "GPU
-//      BPE": whole-piece vocabulary hits).  Every other piece goes to a work
+//      BPE": whole-piece vocabulary hits).  The probes are first compacted
+//      into lists in LDS, one per table, and then run one per lane, so a wave
+//      waits for one memory round trip.  Every other piece goes to a work
 //      list in LDS by length.
-//   2. The workgroup's four waves merge the listed pieces: pieces longer than
+//   2. The workgroup's waves merge the listed pieces: pieces longer than
 //      64 bytes first, then 17..64-byte pieces (one wave per piece, one symbol
 //      per lane), then 2..16-byte pieces (four per wave, one 16-lane row each).
 //      A round takes the row minimum of (rank, position), chooses every
@@ -309,6 +311,32 @@ __device__ void merge_long(const Tables& T, const uint8_t* __restrict__ text, ui
 }
 
 
+constexpr uint32_t kXcds = 8;    // XCDs of the device; workgroups are dealt to them in turn
+constexpr uint32_t kXcdCus = 32;  // compute units per XCD
+constexpr uint32_t kLine = 128;   // L2 line bytes
+
+// Read one dword of every L2 line of this workgroup's share of a read-only
+// table, so that the merge rounds find the table in this XCD's L2 (each XCD
+// has its own L2, and every kernel starts with it cold).  The workgroups that
+// run at once on one XCD split the table between them; a thread reads at most
+// `most` lines.  Returns the xor of what it read, so that the loads are kept.
+template <int NT>
+__device__ inline uint32_t touch_lines(const void* table, uint64_t bytes, uint32_t most) {
+  constexpr uint32_t kAtOnce = kXcdCus * (2048 / NT);  // resident workgroups per XCD at 8 waves per SIMD
+  const uint32_t lines = (uint32_t)((bytes + kLine - 1) / kLine);
+  const uint32_t on_xcd = min((gridDim.x + kXcds - 1) / kXcds, kAtOnce);
+  const uint32_t share = (lines + on_xcd - 1) / on_xcd;
+  const uint32_t lo = (blockIdx.x / kXcds % on_xcd) * share;
+  const uint32_t hi = min(lo + share, lines);
+  const uint8_t* t = static_cast<const uint8_t*>(table);
+  uint32_t x = 0;
+  for (uint32_t i = 0; i < most; ++i) {
+    const uint32_t l = lo + i * NT + threadIdx.x;
+    if (l < hi) x ^= *reinterpret_cast<const uint32_t*>(t + (size_t)l * kLine);
+  }
+  return x;
+}
+
 template <int NT>
 __global__ void __launch_bounds__(NT, 8)
 piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, const uint64_t* __restrict__ doc_off,
@@ -317,6 +345,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   constexpr int kPerChunk = NT / kChunksPerWg;  // threads per chunk
   constexpr int kBytesPer = kChunk / kPerChunk;             // 2 bytes per thread
   constexpr int kTextLds = kPieceTile + kWaveMax + 16;
+  static_assert(kTextLds % 4 == 0, "the tile bytes are loaded as dwords");
   constexpr int kFlagLds = kChunksPerWg + 6;
   constexpr int kTokLds = kPieceTile + kWaveMax;
   // pieces of 2..16 bytes in four length classes (13-16, 9-12, 5-8, 2-4),
@@ -330,27 +359,62 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   __shared__ uint32_t s_tok[kTokLds];
   __shared__ uint8_t s_cnt8[kPieceTile];
   __shared__ uint32_t s_la[kCapA], s_lb[kCapB], s_lc[kCapC], s_ld[kCapD], s_list1[kCap1], s_list2[kCap2];
+  // probe lists of 2..13-byte and 14..28-byte pieces
+  __shared__ uint32_t s_probe_s[kPieceTile / 2], s_probe_l[kPieceTile / (kWordMax + 1) + 1];
   __shared__ uint32_t s_cnt[kChunksPerWg], s_excl[kChunksPerWg];
-  __shared__ uint32_t s_n[6], s_next, s_first, s_doc0;
+  __shared__ uint32_t s_n[8], s_next, s_first, s_doc0;
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
-  if (tid < 6) s_n[tid] = 0;
+  if (tid < 8) s_n[tid] = 0;
   if (tid == 0) s_next = 0;
   const uint32_t tile = blockIdx.x;
   const uint64_t base = (uint64_t)tile * kPieceTile;
   const uint64_t c0 = (uint64_t)tile * kChunksPerWg;
   const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
-  for (int k = tid; k < kTextLds; k += NT) {
-    const uint64_t p = base + k;
-    s_text[k] = p < n ? text[p] : 0;
+  // tile bytes as dwords (all loads in flight before the first wait); bytes
+  // past the text are zero
+  {
+    constexpr int kTextWords = kTextLds / 4;
+    const bool aligned = (reinterpret_cast<uintptr_t>(text) & 3u) == 0;
+    uint32_t* s_text32 = reinterpret_cast<uint32_t*>(s_text);
+#pragma unroll
+    for (int r = 0; r < (kTextWords + NT - 1) / NT; ++r) {
+      const int k = r * NT + (int)tid;
+      if (k < kTextWords) {
+        const uint64_t p = base + 4u * (uint32_t)k;
+        uint32_t v = 0;
+        if (aligned && p + 4 <= n) {
+          v = *reinterpret_cast<const uint32_t*>(text + p);
+        } else {
+          for (uint32_t i = 0; i < 4; ++i)
+            if (p + i < n) v |= (uint32_t)text[p + i] << (8 * i);
+        }
+        s_text32[k] = v;
+      }
+    }
   }
   for (int k = tid; k < kFlagLds; k += NT) {
     const uint64_t c = c0 + k;
     s_flags[k] = c < n_chunks ? B.flags[c] : 0;
   }
+  // the merge and byte-pair tables into this XCD's L2 while phase 1 runs
+  const uint32_t warm = touch_lines<NT>(T.merge_slots, (uint64_t)(T.merge_buckets + 1) * kBucket * 8, 2) ^
+                        touch_lines<NT>(T.pair_rank, 256u * 256u * 4u, 1);
   __syncthreads();
 
-  // phase 1: single bytes and whole-piece hits; the rest goes to the lists.
+  // a piece that needs the merge loop goes to the list of its length class
+  auto list_piece = [&](uint32_t item) {
+    const uint32_t len = item >> 16;
+    if (len > (uint32_t)kWaveMax) s_list2[atomicAdd(&s_n[5], 1u)] = item & 0xFFFFu;
+    else if (len > (uint32_t)kRowMax) s_list1[atomicAdd(&s_n[4], 1u)] = item;
+    else if (len >= 13u) s_la[atomicAdd(&s_n[0], 1u)] = item;
+    else if (len >= 9u) s_lb[atomicAdd(&s_n[1], 1u)] = item;
+    else if (len >= 5u) s_lc[atomicAdd(&s_n[2], 1u)] = item;
+    else s_ld[atomicAdd(&s_n[3], 1u)] = item;
+  };
+
+  // phase 1a: a single byte is its own ID; a 2..28-byte piece goes to the
+  // probe list of its whole-piece table, a longer one to the merge lists.
   // Thread (lc, q) owns bytes 2q, 2q + 1 of chunk lc.
   {
     const uint32_t lc = tid / kPerChunk, q = tid % kPerChunk;
@@ -362,56 +426,57 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
     const uint32_t w1 = s_flags[lc + 1], w2 = s_flags[lc + 2], w3 = s_flags[lc + 3], w4 = s_flags[lc + 4];
     const uint32_t far = w1 ? 16u + __builtin_ctz(w1) : w2 ? 32u + __builtin_ctz(w2)
                        : w3 ? 48u + __builtin_ctz(w3) : w4 ? 64u + __builtin_ctz(w4) : 0xFFFFu;
-    bool has[kBytesPer];
-    uint32_t len[kBytesPer], off[kBytesPer], id[kBytesPer];
+    uint32_t hits = 0;
 #pragma unroll
     for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
+      if (!((mine >> b) & 1u)) continue;
       const uint32_t bit = kBytesPer * q + b;
       const uint32_t above = w & ~((2u << bit) - 1u);
       const uint32_t endrel = above ? (uint32_t)__builtin_ctz(above) : far;
       const uint64_t s0 = c * kChunk + bit;
       const uint64_t e = min(endrel == 0xFFFFu ? ~0ull : c * kChunk + endrel, n);
-      has[b] = (mine >> b) & 1u;
-      len[b] = has[b] ? (uint32_t)min(e - s0, (uint64_t)0xFFFF) : 0u;
-      off[b] = (uint32_t)(s0 - base);
-      id[b] = len[b] == 1u ? (uint32_t)s_text[off[b]] : kNoRank;
-    }
-    // whole-piece tables: 2..13-byte pieces in the short table, 14..28 in the long one
-#pragma unroll
-    for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b)
-      if (T.word_slots && len[b] >= 2u && len[b] <= (uint32_t)kWordMax)
-        id[b] = word_lookup(T, s_text, off[b], len[b]);
-#pragma unroll
-    for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b)
-      if (T.long_slots && len[b] > (uint32_t)kWordMax && len[b] <= (uint32_t)kLongMax)
-        id[b] = long_lookup(T, s_text, off[b], len[b]);
-    uint32_t hits = 0;
-#pragma unroll
-    for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
-      if (!has[b]) continue;
-      const uint32_t item = off[b] | (len[b] << 16);
-      if (id[b] != kNoRank) {
-        s_tok[off[b]] = id[b];
-        s_cnt8[off[b]] = 1;
+      const uint32_t len = (uint32_t)min(e - s0, (uint64_t)0xFFFF);
+      const uint32_t off = (uint32_t)(s0 - base);
+      const uint32_t item = off | (len << 16);
+      if (len == 1u) {
+        s_tok[off] = s_text[off];
+        s_cnt8[off] = 1;
         ++hits;
-      } else if (len[b] > (uint32_t)kWaveMax) {
-        s_list2[atomicAdd(&s_n[5], 1u)] = off[b];
-      } else if (len[b] > (uint32_t)kRowMax) {
-        s_list1[atomicAdd(&s_n[4], 1u)] = item;
-      } else if (len[b] >= 13u) {
-        s_la[atomicAdd(&s_n[0], 1u)] = item;
-      } else if (len[b] >= 9u) {
-        s_lb[atomicAdd(&s_n[1], 1u)] = item;
-      } else if (len[b] >= 5u) {
-        s_lc[atomicAdd(&s_n[2], 1u)] = item;
+      } else if (T.word_slots && len <= (uint32_t)kWordMax) {
+        s_probe_s[atomicAdd(&s_n[6], 1u)] = item;
+      } else if (T.long_slots && len <= (uint32_t)kLongMax) {
+        s_probe_l[atomicAdd(&s_n[7], 1u)] = item;
       } else {
-        s_ld[atomicAdd(&s_n[3], 1u)] = item;
+        list_piece(item);
       }
     }
 #pragma unroll
     for (int d = 1; d < kPerChunk; d <<= 1) hits += __shfl_xor(hits, d, 64);
     if (q == 0) s_cnt[lc] = hits;
   }
+  __syncthreads();
+
+  // phase 1b: one whole-piece probe per lane, all in flight at once.  The
+  // long-table probes start at a wave boundary, so a wave probes one table.
+  {
+    const uint32_t ns = s_n[6], nl = s_n[7];
+    const uint32_t l0 = (ns + kWave - 1) & ~(uint32_t)(kWave - 1);
+    for (uint32_t t = tid; t < l0 + nl; t += NT) {
+      const bool lng = t >= l0;
+      if (!lng && t >= ns) continue;
+      const uint32_t item = lng ? s_probe_l[t - l0] : s_probe_s[t];
+      const uint32_t off = item & 0xFFFFu, len = item >> 16;
+      const uint32_t id = lng ? long_lookup(T, s_text, off, len) : word_lookup(T, s_text, off, len);
+      if (id != kNoRank) {
+        s_tok[off] = id;
+        s_cnt8[off] = 1;
+        atomicAdd(&s_cnt[off / kChunk], 1u);
+      } else {
+        list_piece(item);
+      }
+    }
+  }
+  __asm__ volatile("" : : "v"(warm));  // keeps the table reads; they have arrived by now
   __syncthreads();
 
   // phase 2: the waves take items in order, longest pieces first: pieces
