@@ -15,8 +15,9 @@
 //      waits for one memory round trip.  Every other piece goes to a work
 //      list in LDS by length.
 //   2. The workgroup's waves merge the listed pieces: pieces longer than
-//      64 bytes first, then 17..64-byte pieces (one wave per piece, one symbol
-//      per lane), then 2..16-byte pieces (four per wave, one 16-lane row each).
+//      64 bytes first, then 33..64-byte pieces (one wave per piece, one symbol
+//      per lane), then 17..32-byte pieces (two per wave, one 32-lane row
+//      each), then 2..16-byte pieces (four per wave, one 16-lane row each).
 //      A round takes the row minimum of (rank, position), chooses every
 //      leftmost non-overlapping occurrence of that pair value at once,
 //      compacts the row with a lane permute, and re-probes only the pairs next
@@ -152,8 +153,22 @@ __device__ inline uint32_t wave_min(uint32_t v) {
              min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
 }
 
+// Set bits of the wave mask x in this lane's row of ROW lanes (row_base: the
+// row's first lane), all of them or only those below lane k of the row; the
+// counts come from the lane number, so no per-lane 64-bit mask stays live.
+template <int ROW>
+__device__ inline uint32_t row_count(uint64_t x, uint32_t row_base) {
+  if (ROW == 64) return (uint32_t)__popcll(x);
+  return (uint32_t)__popc((uint32_t)(x >> row_base) & (ROW == 32 ? 0xFFFFFFFFu : (1u << ROW) - 1u));
+}
+template <int ROW>
+__device__ inline uint32_t row_count_below(uint64_t x, uint32_t row_base, uint32_t k) {
+  if (ROW == 64) return __builtin_amdgcn_mbcnt_hi((uint32_t)(x >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)x, 0u));
+  return (uint32_t)__popc((uint32_t)(x >> row_base) & ((1u << k) - 1u));
+}
+
 // BPE of one piece per row of ROW lanes (ROW = 16: four pieces per wave; ROW =
-// 64: one piece per wave), one symbol per lane, in rounds.  Called by all 64
+// 32: two; ROW = 64: one), one symbol per lane, in rounds.  Called by all 64
 // lanes; rows without a piece pass active = false.  p: the piece's bytes;
 // tok_out / cnt_out: where its tokens and their count go; chunk_total: the
 // counter of the chunk the piece starts in (all three in LDS).
@@ -163,8 +178,6 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t k = lane & (ROW - 1);
   const uint32_t row_base = lane - k;
-  const uint64_t row_bits = ROW == 64 ? ~0ull : (0xFFFFull << row_base);
-  const uint64_t below = ((1ull << lane) - 1ull) & row_bits;
   uint32_t cur = active ? len : 0u;
   uint32_t sym = k < cur ? (uint32_t)p[k] : 0u;
   const uint32_t nx = row_next<ROW>(sym);
@@ -179,6 +192,12 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
       const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)key, 32),
                              (uint32_t)__builtin_amdgcn_readlane((int)key, 48));
       key = min(a, b);
+    } else if (ROW == 32) {
+      const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)key, 0),
+                             (uint32_t)__builtin_amdgcn_readlane((int)key, 16));
+      const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)key, 32),
+                             (uint32_t)__builtin_amdgcn_readlane((int)key, 48));
+      key = lane < 32u ? a : b;
     }
     const bool live = key != 0xFFFFFFFFu;
     if (__ballot(live) == 0) break;
@@ -198,11 +217,11 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
         nrk = (chose || chose_n) ? merge_rank(T, nsym, chose ? n2 : n1) : rk;
       }
     }
-    const uint32_t nk = k - (uint32_t)__popcll((S << 1) & below);
+    const uint32_t nk = k - row_count_below<ROW>(S << 1, row_base, k);
     const uint32_t dst = !live ? lane : ((gone || k >= cur) ? row_base + ROW - 1 : row_base + nk);
     sym = (uint32_t)__builtin_amdgcn_ds_permute((int)(dst << 2), (int)nsym);
     rk = (uint32_t)__builtin_amdgcn_ds_permute((int)(dst << 2), (int)nrk);
-    if (live) cur -= (uint32_t)__popcll(S & row_bits);
+    if (live) cur -= row_count<ROW>(S, row_base);
   }
   if (active && k < cur) tok_out[k] = sym;
   if (active && k == 0) {
@@ -353,19 +372,21 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   // 1024 / L pieces
   constexpr int kCapA = kPieceTile / 13 + 1, kCapB = kPieceTile / 9 + 1, kCapC = kPieceTile / 5 + 1;
   constexpr int kCapD = kPieceTile / 2;
-  constexpr int kCap1 = kPieceTile / (kRowMax + 1) + 1, kCap2 = kPieceTile / (kWaveMax + 1) + 1;
+  constexpr int kCapH = kPieceTile / (kRowMax + 1) + 1, kCap1 = kPieceTile / (kHalfMax + 1) + 1;
+  constexpr int kCap2 = kPieceTile / (kWaveMax + 1) + 1;
   __shared__ __attribute__((aligned(16))) uint8_t s_text[kTextLds];
   __shared__ uint16_t s_flags[kFlagLds];
   __shared__ uint32_t s_tok[kTokLds];
   __shared__ uint8_t s_cnt8[kPieceTile];
-  __shared__ uint32_t s_la[kCapA], s_lb[kCapB], s_lc[kCapC], s_ld[kCapD], s_list1[kCap1], s_list2[kCap2];
+  __shared__ uint32_t s_la[kCapA], s_lb[kCapB], s_lc[kCapC], s_ld[kCapD];
+  __shared__ uint32_t s_lh[kCapH], s_list1[kCap1], s_list2[kCap2];
   // probe lists of 2..13-byte and 14..28-byte pieces
   __shared__ uint32_t s_probe_s[kPieceTile / 2], s_probe_l[kPieceTile / (kWordMax + 1) + 1];
   __shared__ uint32_t s_cnt[kChunksPerWg], s_excl[kChunksPerWg];
-  __shared__ uint32_t s_n[8], s_next, s_first, s_doc0;
+  __shared__ uint32_t s_n[9], s_next, s_first, s_doc0;
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
-  if (tid < 8) s_n[tid] = 0;
+  if (tid < 9) s_n[tid] = 0;
   if (tid == 0) s_next = 0;
   const uint32_t tile = blockIdx.x;
   const uint64_t base = (uint64_t)tile * kPieceTile;
@@ -406,7 +427,8 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   auto list_piece = [&](uint32_t item) {
     const uint32_t len = item >> 16;
     if (len > (uint32_t)kWaveMax) s_list2[atomicAdd(&s_n[5], 1u)] = item & 0xFFFFu;
-    else if (len > (uint32_t)kRowMax) s_list1[atomicAdd(&s_n[4], 1u)] = item;
+    else if (len > (uint32_t)kHalfMax) s_list1[atomicAdd(&s_n[4], 1u)] = item;
+    else if (len > (uint32_t)kRowMax) s_lh[atomicAdd(&s_n[8], 1u)] = item;
     else if (len >= 13u) s_la[atomicAdd(&s_n[0], 1u)] = item;
     else if (len >= 9u) s_lb[atomicAdd(&s_n[1], 1u)] = item;
     else if (len >= 5u) s_lc[atomicAdd(&s_n[2], 1u)] = item;
@@ -454,6 +476,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
     for (int d = 1; d < kPerChunk; d <<= 1) hits += __shfl_xor(hits, d, 64);
     if (q == 0) s_cnt[lc] = hits;
   }
+  __asm__ volatile("" : : "v"(warm));  // keeps the table reads; they arrive with the tile bytes
   __syncthreads();
 
   // phase 1b: one whole-piece probe per lane, all in flight at once.  The
@@ -476,20 +499,22 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
       }
     }
   }
-  __asm__ volatile("" : : "v"(warm));  // keeps the table reads; they have arrived by now
   __syncthreads();
 
   // phase 2: the waves take items in order, longest pieces first: pieces
-  // over 64 bytes, then 17..64 bytes (a wave each), then groups of four
-  // 2..16-byte pieces by length class (a 16-lane row each).  The item index
-  // comes from an LDS counter through readfirstlane, so every branch on it
-  // is uniform across the wave.
+  // over 64 bytes, then 33..64 bytes (a wave each), then pairs of 17..32-byte
+  // pieces (a 32-lane row each), then groups of four 2..16-byte pieces by
+  // length class (a 16-lane row each).  The item index comes from an LDS
+  // counter through readfirstlane, so every branch on it is uniform across
+  // the wave.
   {
     const uint32_t n2 = __builtin_amdgcn_readfirstlane(s_n[5]);
     const uint32_t n1 = __builtin_amdgcn_readfirstlane(s_n[4]);
+    const uint32_t nh = __builtin_amdgcn_readfirstlane(s_n[8]);
     const uint32_t ca = __builtin_amdgcn_readfirstlane(s_n[0]), cb = __builtin_amdgcn_readfirstlane(s_n[1]);
     const uint32_t cc = __builtin_amdgcn_readfirstlane(s_n[2]), cd = __builtin_amdgcn_readfirstlane(s_n[3]);
-    const uint32_t ea = n2 + n1 + (ca + 3) / 4, eb = ea + (cb + 3) / 4, ec = eb + (cc + 3) / 4;
+    const uint32_t eh = n2 + n1 + (nh + 1) / 2;
+    const uint32_t ea = eh + (ca + 3) / 4, eb = ea + (cb + 3) / 4, ec = eb + (cc + 3) / 4;
     const uint32_t items = ec + (cd + 3) / 4;
     for (;;) {
       // every lane adds 1, so a grab moves the counter by 64
@@ -502,10 +527,16 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
         const uint32_t it = s_list1[item - n2];
         const uint32_t off = it & 0xFFFFu;
         merge_rows<64>(T, s_text + off, it >> 16, true, s_tok + off, &s_cnt8[off], &s_cnt[off / kChunk]);
+      } else if (item < eh) {
+        const uint32_t i = (item - n2 - n1) * 2 + (lane >> 5);
+        const bool act = i < nh;
+        const uint32_t it = act ? s_lh[i] : 0u;
+        const uint32_t off = it & 0xFFFFu;
+        merge_rows<32>(T, s_text + off, it >> 16, act, s_tok + off, &s_cnt8[off], &s_cnt[off / kChunk]);
       } else {
         // length class of the item: bounds and counts are wave-uniform
         const bool ia = item < ea, ib = !ia && item < eb, ic = !ia && !ib && item < ec;
-        const uint32_t first = ia ? n2 + n1 : ib ? ea : ic ? eb : ec;
+        const uint32_t first = ia ? eh : ib ? ea : ic ? eb : ec;
         const uint32_t cnt = ia ? ca : ib ? cb : ic ? cc : cd;
         const uint32_t* lst = ia ? s_la : ib ? s_lb : ic ? s_lc : s_ld;
         const uint32_t i = (item - first) * 4 + (lane >> 4);

@@ -30,6 +30,7 @@ constexpr int kHalo = 64;            // context bytes loaded on each side of a t
 constexpr int kWordMax = 13;         // longest piece the short whole-piece table holds
 constexpr int kLongMax = 28;         // longest piece the long whole-piece table holds
 constexpr int kRowMax = 16;          // longest piece merged by one 16-lane row
+constexpr int kHalfMax = 32;         // longest piece merged by one 32-lane row
 constexpr int kWaveMax = 64;         // longest piece merged by one wave in registers
 constexpr int kPretokTile = 1024;    // bytes per workgroup of the pre-tokenization pass
 constexpr int kPieceTile = 1024;     // bytes per workgroup of the piece pass
