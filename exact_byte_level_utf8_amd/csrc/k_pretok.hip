@@ -2,7 +2,7 @@
 // run aggregates and the piece-start predicate, one 1 KiB tile per workgroup.
 //
 // Each workgroup loads its tile plus 64 bytes of context on each side into LDS
-// with coalesced byte loads, decodes every code point once into an info word
+// with coalesced dword loads, decodes every code point once into an info word
 // (class and the few character flags the rules test), and evaluates the
 // run-local rules of pretok_rules.h at every code point of the tile (TokTier,
 // "Exact GPU Tokenization"; GraphTok, section 4 "Parallel tokenizer
@@ -68,11 +68,20 @@ __device__ void chunk_elems_global(const uint8_t* text, uint64_t n, const uint64
                                    uint32_t n_docs, int64_t x, uint32_t* fe, uint32_t* be) {
   uint32_t b[20];
   uint32_t edge = 0;  // bit i: a document starts at x + i, or x + i >= n
+  if (x >= 0 && x + 20 <= (int64_t)n && (reinterpret_cast<uintptr_t>(text + x) & 3u) == 0) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(text + x);  // five loads in flight at once
+    uint32_t d[5];
 #pragma unroll
-  for (int i = 0; i < 20; ++i) {
-    const int64_t p = x + i;
-    b[i] = (p >= 0 && p < (int64_t)n) ? text[p] : 0u;
-    if (p >= (int64_t)n) edge |= 1u << i;
+    for (int i = 0; i < 5; ++i) d[i] = w[i];
+#pragma unroll
+    for (int i = 0; i < 20; ++i) b[i] = (d[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 20; ++i) {
+      const int64_t p = x + i;
+      b[i] = (p >= 0 && p < (int64_t)n) ? text[p] : 0u;
+      if (p >= (int64_t)n) edge |= 1u << i;
+    }
   }
   if (doc_off) {
     uint32_t d = first_doc_at_or_after(doc_off, n_docs, x < 0 ? 0 : (uint64_t)x);
@@ -122,6 +131,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
               uint32_t n_docs, Bufs B) {
   // window byte k (k in [-4, kWin + 12)) lives at byte 4 + k of s_raw / s_fl
   constexpr int kGuard = 4, kBytes = kWin + 16;
+  static_assert(kBytes % 4 == 0 && (kHalo + kGuard) % 4 == 0, "the window is loaded as aligned dwords");
   __shared__ uint32_t s_raw32[kBytes / 4];
   __shared__ uint32_t s_fl32[kBytes / 4];
   __shared__ uint32_t s_info[kWin];
@@ -151,11 +161,35 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   const int64_t lo = base - kHalo;
   const int64_t sn = (int64_t)n;
 
-  for (int g = tid; g < kBytes; g += kThreads) {
-    const int64_t p = lo + g - kGuard;
-    const bool in = p >= 0 && p < sn;
-    s_raw[g] = in ? text[p] : 0;
-    s_fl[g] = in ? 0 : kBOut;
+  // the window as dwords, every load in flight before the first wait; bytes
+  // outside the text are 0 and flagged kBOut
+  {
+    constexpr int kWords = kBytes / 4, kR = (kWords + kThreads - 1) / kThreads;
+    const bool aligned = (reinterpret_cast<uintptr_t>(text) & 3u) == 0;
+    uint32_t v[kR], f[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int64_t p = lo - kGuard + 4 * (r * kThreads + (int)tid);
+      v[r] = 0;
+      f[r] = 0;
+      if (aligned && p >= 0 && p + 4 <= sn) {
+        v[r] = *reinterpret_cast<const uint32_t*>(text + p);
+      } else {
+        for (int i = 0; i < 4; ++i) {
+          const bool in = p + i >= 0 && p + i < sn;
+          v[r] |= in ? (uint32_t)text[p + i] << (8 * i) : 0u;
+          f[r] |= in ? 0u : (uint32_t)kBOut << (8 * i);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int w = r * kThreads + (int)tid;
+      if (w < kWords) {
+        s_raw32[w] = v[r];
+        s_fl32[w] = f[r];
+      }
+    }
   }
   if (doc_off && tid == 0) s_misc[0] = first_doc_at_or_after(doc_off, n_docs, lo < 0 ? 0 : (uint64_t)lo);
   __syncthreads();
