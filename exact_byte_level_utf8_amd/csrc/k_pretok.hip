@@ -6,18 +6,19 @@
 // (class and the few character flags the rules test), and evaluates the
 // run-local rules of pretok_rules.h at every code point of the tile (TokTier,
 // "Exact GPU Tokenization"; GraphTok, section 4 "Parallel tokenizer
-// frontends").  Positions are dealt to lanes interleaved (position j * 256 +
-// thread), so a wave touches 64 consecutive LDS entries at every step and a
-// wave ballot yields four flag words at once: bit i of word c is set iff byte
+// frontends").  Positions are dealt to lanes interleaved (position j * NT +
+// thread, with NT = 512 threads for grids of up to 1024 tiles and 256 above),
+// so a wave touches 64 consecutive LDS entries at every step and a wave
+// ballot yields four flag words at once: bit i of word c is set iff byte
 // 16c + i starts a piece.
 //
 // The Llama-3 style needs three run aggregates whose runs may cross the tile
-// edge.  They are (reset, value) scan elements: four workgroup scans in
-// position order combine the tile's elements, and the carry into the tile is
-// found by walking the LDS halo; a run longer than the halo (a long digit or
-// whitespace run) falls back to reducing 4 KiB blocks from global memory until
-// the run ends, which costs time only on such input and keeps the result
-// exact.
+// edge.  They are (reset, value) scan elements: one workgroup pass of wave
+// scans combines the tile's elements, and the carries into the tile are wave
+// reductions over the LDS halos; a run longer than the halo (a long digit or
+// whitespace run) falls back to reducing blocks of 16 bytes per thread from
+// global memory until the run ends, which costs time only on such input and
+// keeps the result exact.
 #include "tok_internal.h"
 #include "pretok_rules.h"
 #include "wg_scan.h"
@@ -28,8 +29,6 @@ namespace {
 
 constexpr int kPT = kPretokTile;          // tile bytes
 constexpr int kWin = kPT + 2 * kHalo;     // LDS window bytes
-constexpr int kRounds = kPT / kThreads;   // tile positions per thread
-constexpr int kWinRounds = (kWin + kThreads - 1) / kThreads;
 // per-byte flags in LDS
 constexpr uint8_t kBDoc = 1, kBOut = 2;
 
@@ -125,17 +124,21 @@ __device__ inline uint32_t lds_word(const uint32_t* a, uint32_t b) {
 
 __device__ inline bool is_cont(uint32_t byte) { return (byte & 0xC0u) == 0x80u; }
 
-template <int PATTERN>
-__global__ void __launch_bounds__(kThreads, 6)
+template <int PATTERN, int NT>
+__global__ void __launch_bounds__(NT, NT >= 512 ? 8 : 6)
 pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off,
               uint32_t n_docs, Bufs B) {
+  constexpr int kRounds = kPT / NT;                    // tile positions per thread
+  constexpr int kPer = kRounds;                        // consecutive positions per thread in the aggregate pass
+  static_assert(kPer == 2 || kPer == 4, "aggregate states are packed as 2 or 4 bytes per thread");
+  constexpr int kWinRounds = (kWin + NT - 1) / NT;     // window positions per thread
   // window byte k (k in [-4, kWin + 12)) lives at byte 4 + k of s_raw / s_fl
   constexpr int kGuard = 4, kBytes = kWin + 16;
   static_assert(kBytes % 4 == 0 && (kHalo + kGuard) % 4 == 0, "the window is loaded as aligned dwords");
   __shared__ uint32_t s_raw32[kBytes / 4];
   __shared__ uint32_t s_fl32[kBytes / 4];
   __shared__ uint32_t s_info[kWin];
-  __shared__ uint32_t s_scan[kThreads / kWave], s_scan2[kThreads / kWave];
+  __shared__ uint32_t s_scan[NT / kWave], s_scan2[NT / kWave];
   __shared__ uint32_t s_misc[4];
   __shared__ uint32_t s_agg[PATTERN == 1 ? kPT / 4 : 1];  // Llama-3 run states, a byte per tile position
   uint8_t* s_raw = reinterpret_cast<uint8_t*>(s_raw32);
@@ -154,7 +157,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   }
   if (doc_off) {
     bool bad_doc = false;
-    for (uint32_t d = blockIdx.x * kThreads + tid; d < n_docs; d += gridDim.x * kThreads)
+    for (uint32_t d = blockIdx.x * NT + tid; d < n_docs; d += gridDim.x * NT)
       bad_doc |= doc_off[d] > doc_off[d + 1];
     if (bad_doc) report(&B.ctr->err_docs, B.gen);
   }
@@ -164,12 +167,12 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   // the window as dwords, every load in flight before the first wait; bytes
   // outside the text are 0 and flagged kBOut
   {
-    constexpr int kWords = kBytes / 4, kR = (kWords + kThreads - 1) / kThreads;
+    constexpr int kWords = kBytes / 4, kR = (kWords + NT - 1) / NT;
     const bool aligned = (reinterpret_cast<uintptr_t>(text) & 3u) == 0;
     uint32_t v[kR], f[kR];
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
-      const int64_t p = lo - kGuard + 4 * (r * kThreads + (int)tid);
+      const int64_t p = lo - kGuard + 4 * (r * NT + (int)tid);
       v[r] = 0;
       f[r] = 0;
       if (aligned && p >= 0 && p + 4 <= sn) {
@@ -184,7 +187,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
-      const int w = r * kThreads + (int)tid;
+      const int w = r * NT + (int)tid;
       if (w < kWords) {
         s_raw32[w] = v[r];
         s_fl32[w] = f[r];
@@ -194,7 +197,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   if (doc_off && tid == 0) s_misc[0] = first_doc_at_or_after(doc_off, n_docs, lo < 0 ? 0 : (uint64_t)lo);
   __syncthreads();
   if (doc_off) {
-    for (uint32_t d = s_misc[0] + tid; d <= n_docs; d += kThreads) {
+    for (uint32_t d = s_misc[0] + tid; d <= n_docs; d += NT) {
       const uint64_t p = doc_off[d];
       if ((int64_t)p >= lo + kWin) break;
       if ((int64_t)p >= lo && (int64_t)p < sn) s_fl[p - lo + kGuard] |= kBDoc;  // equal offsets write equal bytes
@@ -211,7 +214,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     uint32_t cps[kWinRounds], pre[kWinRounds];
 #pragma unroll
     for (int j = 0; j < kWinRounds; ++j) {
-      const int k = min((int)(tid + j * kThreads), kWin - 1);  // positions past the window repeat the last one
+      const int k = min((int)(tid + j * NT), kWin - 1);  // positions past the window repeat the last one
       const uint32_t g = (uint32_t)(k + kGuard);
       const uint32_t cur = lds_word(s_raw32, g), prv = lds_word(s_raw32, g - 4u);
       const uint64_t fl = (uint64_t)lds_word(s_fl32, g) | ((uint64_t)lds_word(s_fl32, g + 4u) << 32);
@@ -234,7 +237,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
       if ((fl0 & kBDoc) | ((fback & kBOut) != 0)) d = 0;
       uint32_t pr = kILead | (len << kILenShift) | ((fl0 & kBDoc) ? kIDocStart : 0u) | (d << kIPrevShift);
       pr |= undecoded ? kIUndecoded : last ? kILastInDoc : 0u;
-      pre[j] = lead && k == (int)(tid + j * kThreads) ? pr : 0u;
+      pre[j] = lead && k == (int)(tid + j * NT) ? pr : 0u;
     }
     uint32_t cls[kWinRounds];
 #pragma unroll
@@ -248,7 +251,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
       if (cps[j] >= 0x10000u) cls[j] = dev_class(cps[j]);  // rare: two-level table above the BMP
 #pragma unroll
     for (int j = 0; j < kWinRounds; ++j) {
-      const int k = tid + j * kThreads;
+      const int k = tid + j * NT;
       if (k >= kWin) continue;
       const uint32_t cp = cps[j], p = pre[j];
       uint32_t in = 0;
@@ -267,7 +270,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   bool bad = false;
 #pragma unroll
   for (int j = 0; j < kRounds; ++j) {
-    const uint32_t g = (uint32_t)(kHalo + tid + j * kThreads + kGuard);
+    const uint32_t g = (uint32_t)(kHalo + tid + j * NT + kGuard);
     const uint64_t raw = (uint64_t)lds_word(s_raw32, g) | ((uint64_t)lds_word(s_raw32, g + 4u) << 32);
     const uint64_t fl = (uint64_t)lds_word(s_fl32, g) | ((uint64_t)lds_word(s_fl32, g + 4u) << 32);
     const uint32_t b0 = (uint32_t)raw & 0xFFu, b1 = (uint32_t)(raw >> 8) & 0xFFu, f0 = (uint32_t)fl & 0xFFu;
@@ -289,11 +292,12 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   __syncthreads();
 
   // Llama-3 style: run-aggregate states before (forward) and after (backward)
-  // every tile position.  Thread t composes the elements of the four
-  // consecutive positions 4t .. 4t+3; one workgroup pass turns the per-thread
+  // every tile position.  Thread t composes the elements of the kPer
+  // consecutive positions kPer t ..; one workgroup pass turns the per-thread
   // compositions into exclusive prefixes (forward) and suffixes (backward);
   // the carries into the tile come from wave reductions over the halos, or,
-  // for a run longer than a halo, from 4 KiB blocks in global memory.  The
+  // for a run longer than a halo, from blocks of 16 bytes per thread in
+  // global memory.  The
   // states go to LDS, one byte per position: n | g << 2 | h << 3.
   if (PATTERN == 1) {
     uint32_t carry_f, carry_h;
@@ -324,14 +328,14 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     const uint32_t m3 = __builtin_amdgcn_readfirstlane(s_misc[3]);
     carry_h = m3 & 1u;
     bdone = (m3 >> 1) & 1u;
-    if (!fdone) {  // a run longer than the halo ends before the tile: reduce 4 KiB blocks
+    if (!fdone) {  // a run longer than the halo ends before the tile: reduce blocks from global memory
       uint32_t acc = kFwdId;
-      for (int64_t end = base;; end -= kThreads * kChunk) {
-        const int64_t start = end - kThreads * kChunk;
+      for (int64_t end = base;; end -= NT * kChunk) {
+        const int64_t start = end - NT * kChunk;
         uint32_t fe2, be2;
         chunk_elems_global(text, n, doc_off, n_docs, start + (int64_t)tid * kChunk, &fe2, &be2);
         uint32_t tot;
-        wg_excl_scan<kThreads>(fe2, kFwdId, FwdOp(), s_scan, &tot);
+        wg_excl_scan<NT>(fe2, kFwdId, FwdOp(), s_scan, &tot);
         acc = __builtin_amdgcn_readfirstlane(fwd_comp(tot, acc));  // uniform loop exit
         if (fwd_resolved(acc) || start <= 0) break;
       }
@@ -339,28 +343,31 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     }
     if (!bdone) {
       uint32_t acc = kBwdId;
-      for (int64_t start = base + kPT;; start += kThreads * kChunk) {
+      for (int64_t start = base + kPT;; start += NT * kChunk) {
         uint32_t fe2, be2;
         chunk_elems_global(text, n, doc_off, n_docs, start + (int64_t)tid * kChunk, &fe2, &be2);
         uint32_t tot;
-        wg_excl_suffix<kThreads>(be2, kBwdId, BwdOp(), s_scan, &tot);
+        wg_excl_suffix<NT>(be2, kBwdId, BwdOp(), s_scan, &tot);
         acc = __builtin_amdgcn_readfirstlane(bwd_comp(acc, tot));  // uniform loop exit
-        if ((acc & 1u) || start + kThreads * kChunk >= sn) break;
+        if ((acc & 1u) || start + NT * kChunk >= sn) break;
       }
       carry_h = bwd_apply(acc, 0);
     }
-    // per-thread compositions of four consecutive positions, then the
+    // per-thread compositions of kPer consecutive positions, then the
     // workgroup prefix (forward) and suffix (backward) of them
-    const uint4 q4 = reinterpret_cast<const uint4*>(s_info + kHalo)[tid];
-    const uint32_t in4[4] = {q4.x, q4.y, q4.z, q4.w};
-    uint32_t fe[4], be[4];
+    uint32_t fe[kPer], be[kPer];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fe[i] = (in4[i] & kILead) ? fwd_elem(in4[i]) : kFwdId;
-      be[i] = (in4[i] & kILead) ? bwd_elem(in4[i]) : kBwdId;
+    for (int i = 0; i < kPer; ++i) {
+      const uint32_t in = s_info[kHalo + tid * kPer + i];
+      fe[i] = (in & kILead) ? fwd_elem(in) : kFwdId;
+      be[i] = (in & kILead) ? bwd_elem(in) : kBwdId;
     }
-    const uint32_t fcomp = fwd_comp(fwd_comp(fwd_comp(fe[0], fe[1]), fe[2]), fe[3]);
-    const uint32_t bcomp = bwd_comp(bwd_comp(bwd_comp(be[0], be[1]), be[2]), be[3]);
+    uint32_t fcomp = fe[0], bcomp = be[0];
+#pragma unroll
+    for (int i = 1; i < kPer; ++i) {
+      fcomp = fwd_comp(fcomp, fe[i]);
+      bcomp = bwd_comp(bcomp, be[i]);
+    }
     const uint32_t finc = wave_incl_scan(fcomp, FwdOp(), kFwdId);
     const uint32_t binc = wave_incl_suffix(bcomp, BwdOp(), kBwdId);
     if (lane == kWave - 1) s_scan[wv] = finc;
@@ -368,32 +375,36 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     __syncthreads();
     uint32_t wbefore = kFwdId, wafter = kBwdId;
 #pragma unroll
-    for (uint32_t i = 0; i < (uint32_t)(kThreads / kWave); ++i) {
+    for (uint32_t i = 0; i < (uint32_t)(NT / kWave); ++i) {
       if (i < wv) wbefore = fwd_comp(wbefore, s_scan[i]);
     }
 #pragma unroll
-    for (int i = kThreads / kWave - 1; i >= 0; --i) {
+    for (int i = NT / kWave - 1; i >= 0; --i) {
       if ((uint32_t)i > wv) wafter = bwd_comp(s_scan2[i], wafter);
     }
     const uint32_t fprev = (uint32_t)__builtin_amdgcn_update_dpp((int)kFwdId, (int)finc, 0x138, 0xF, 0xF, false);
     const uint32_t bnext = (uint32_t)__builtin_amdgcn_update_dpp((int)kBwdId, (int)binc, 0x130, 0xF, 0xF, false);
-    const uint32_t pre = fwd_comp(wbefore, lane == 0 ? kFwdId : fprev);         // elements before position 4t
-    const uint32_t suf = bwd_comp(lane == kWave - 1 ? kBwdId : bnext, wafter);  // elements after 4t + 3
-    // states of the four positions
-    uint32_t st4[4];
+    const uint32_t pre = fwd_comp(wbefore, lane == 0 ? kFwdId : fprev);         // elements before this thread's positions
+    const uint32_t suf = bwd_comp(lane == kWave - 1 ? kBwdId : bnext, wafter);  // elements after them
+    // states of this thread's positions
+    uint32_t st[kPer];
     uint32_t acc = pre;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st4[i] = fwd_apply(acc, carry_f);
+    for (int i = 0; i < kPer; ++i) {
+      st[i] = fwd_apply(acc, carry_f);
       acc = fwd_comp(acc, fe[i]);
     }
     acc = suf;
 #pragma unroll
-    for (int i = 3; i >= 0; --i) {
-      st4[i] |= bwd_apply(acc, carry_h) << 3;
+    for (int i = kPer - 1; i >= 0; --i) {
+      st[i] |= bwd_apply(acc, carry_h) << 3;
       acc = bwd_comp(be[i], acc);
     }
-    s_agg[tid] = st4[0] | (st4[1] << 8) | (st4[2] << 16) | (st4[3] << 24);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) packed |= st[i] << (8 * i);
+    if (kPer == 4) s_agg[tid] = packed;
+    else reinterpret_cast<uint16_t*>(s_agg)[tid] = (uint16_t)packed;
     __syncthreads();
   }
 
@@ -402,7 +413,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   // chained LDS reads), the next one from the code point's length
 #pragma unroll
   for (int j = 0; j < kRounds; ++j) {
-    const int k = kHalo + tid + j * kThreads;
+    const int k = kHalo + tid + j * NT;
     const uint32_t c = s_info[k];
     uint32_t p[4];
     uint32_t at = (uint32_t)k, cur = c;
@@ -425,7 +436,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     const bool st = (c & kILead) && rule;
     // this wave holds 64 consecutive positions: four flag words
     const uint64_t m = __ballot(st);
-    const uint64_t p0 = (uint64_t)base + (uint64_t)j * kThreads + wv * kWave;
+    const uint64_t p0 = (uint64_t)base + (uint64_t)j * NT + wv * kWave;
     if (lane < 4) {
       const uint64_t cw = p0 / kChunk + lane;
       if (cw * kChunk < n) flags[cw] = (uint16_t)(m >> (16 * lane));
@@ -439,10 +450,16 @@ void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uin
                    int pattern, Bufs b, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const uint32_t tiles = (uint32_t)((n + kPretokTile - 1) / kPretokTile);
   if (!tiles) return;
-  if (pattern == 0)
-    launch_on(pretok_kernel<0>, dim3(tiles), dim3(kThreads), s, e0, e1, text, n, doc_off, n_docs, b);
-  else
-    launch_on(pretok_kernel<1>, dim3(tiles), dim3(kThreads), s, e0, e1, text, n, doc_off, n_docs, b);
+  // up to one tile per workgroup slot of the device, 8 waves per tile; larger
+  // inputs use 4-wave workgroups, which pack the CUs better
+  const bool small = tiles <= (uint32_t)kPretokSmallGrid;
+  if (pattern == 0) {
+    if (small) launch_on(pretok_kernel<0, 512>, dim3(tiles), dim3(512), s, e0, e1, text, n, doc_off, n_docs, b);
+    else launch_on(pretok_kernel<0, 256>, dim3(tiles), dim3(256), s, e0, e1, text, n, doc_off, n_docs, b);
+  } else {
+    if (small) launch_on(pretok_kernel<1, 512>, dim3(tiles), dim3(512), s, e0, e1, text, n, doc_off, n_docs, b);
+    else launch_on(pretok_kernel<1, 256>, dim3(tiles), dim3(256), s, e0, e1, text, n, doc_off, n_docs, b);
+  }
 }
 
 }  // namespace tok

@@ -24,7 +24,7 @@
 
 namespace tok {
 
-constexpr int kThreads = 256;        // threads per pre-tokenization workgroup
+constexpr int kPretokSmallGrid = 1024;  // largest pre-tokenization grid run with 8-wave workgroups
 constexpr int kChunk = 16;           // bytes per flag word
 constexpr int kHalo = 64;            // context bytes loaded on each side of a tile
 constexpr int kWordMax = 13;         // longest piece the short whole-piece table holds

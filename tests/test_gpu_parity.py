@@ -155,6 +155,29 @@ def test_ragged_sizes(cfg, name):
         _check(f"{name}[{n}]", t.encode(b), o.encode(b), b, tokb)
 
 
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+@pytest.mark.parametrize("total", [700_000, 1_600_000])
+def test_long_runs_in_large_input(cfg, name, total):
+    """Runs far longer than the pre-tokenizer's 64-byte halo, spread over an
+    input of fewer than 1024 tiles (8-wave workgroups) and of more (4-wave
+    workgroups): the run carries then come from blocks in global memory."""
+    t, o, tokb = cfg[name]
+    filler = textgen.mix_text(41, 300_000)
+    runs = ["7" * 30_000, " " * 20_000, "\r\n" * 9_000, "x" + "\n" * 12_000 + "  y", "!" + " " * 9_000 + "\r\nz",
+            "12" * 7_000, "\t " * 5_000 + "w"]
+    parts, size, k = [], 0, 0
+    while size < total:
+        a = (k * 37_813) % 250_000
+        piece = filler[a:a + 30_000 + 1_111 * (k % 5)] + runs[k % len(runs)]
+        parts.append(piece)
+        size += len(piece)
+        k += 1
+    b = "".join(parts).encode()
+    want = o.encode(b)
+    _check(f"{name}[{len(b)}]", t.encode(b), want, b, tokb)
+    _check(f"{name}[{len(b)}] dev", gpu_encode_dev(t, b), want, b, tokb)
+
+
 @pytest.mark.parametrize("name", ["tiny", "gpt2", "llama3"])
 def test_long_pieces(cfg, name):
     t, o, tokb = cfg[name]
