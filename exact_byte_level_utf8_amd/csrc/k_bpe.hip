@@ -38,24 +38,43 @@
 namespace tok {
 namespace {
 
-// Rank of the merge (a, b), or kNoRank.  Byte pairs come from a direct table;
-// other pairs from open addressing over buckets of kBucket slots, each bucket
-// read with two 16-byte loads.
+// Rank held by one merge-table slot, or kNoRank.  A slot is left << 44 |
+// right << 24 | rank, so its high dword is left << 12 | right >> 8 (khi) and
+// the top byte of its low dword is right & 0xFF (klo); an empty slot (all
+// ones) never matches, since token IDs stay below 2^20 - 1 (TOK_MAX_MERGES)
+// and khi is then never all ones.
+__device__ inline uint32_t slot_rank(ulonglong2 two, int which, uint32_t khi, uint32_t klo) {
+  const uint64_t v = which ? two.y : two.x;
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  return hi == khi && (lo >> 24) == klo ? (lo & 0xFFFFFFu) : kNoRank;
+}
+
+__device__ inline uint32_t bucket_rank(ulonglong2 s01, ulonglong2 s23, uint32_t khi, uint32_t klo) {
+  return min(min(slot_rank(s01, 0, khi, klo), slot_rank(s01, 1, khi, klo)),
+             min(slot_rank(s23, 0, khi, klo), slot_rank(s23, 1, khi, klo)));
+}
+
+// Rank of the merge (a, b), or kNoRank, for a pair next to a merge: a or b is
+// a merged token (>= 256), so the byte-pair table never applies.  Open
+// addressing over buckets of kBucket slots, each read with two 16-byte loads;
+// the first bucket is compared without branches, and only a full first
+// bucket without the key goes on to the next ones.
 __device__ inline uint32_t merge_rank(const Tables& T, uint32_t a, uint32_t b) {
-  if ((a | b) < 256u) return T.pair_rank[(a << 8) | b];
-  const uint64_t key = ((uint64_t)a << 20) | b;
+  const uint32_t khi = (a << 12) | (b >> 8), klo = b & 0xFFu;
   uint32_t h = merge_hash(a, b) & T.merge_buckets;
-  for (uint32_t probe = 0; probe <= T.merge_buckets; ++probe) {
-    const ulonglong2* bk = reinterpret_cast<const ulonglong2*>(T.merge_slots + (size_t)h * kBucket);
-    const ulonglong2 s01 = bk[0], s23 = bk[1];
-    if ((s01.x >> 24) == key) return (uint32_t)(s01.x & 0xFFFFFFu);
-    if ((s01.y >> 24) == key) return (uint32_t)(s01.y & 0xFFFFFFu);
-    if ((s23.x >> 24) == key) return (uint32_t)(s23.x & 0xFFFFFFu);
-    if ((s23.y >> 24) == key) return (uint32_t)(s23.y & 0xFFFFFFu);
-    if (s23.y == kEmptySlot) return kNoRank;  // slots fill in order within a bucket
-    h = (h + 1) & T.merge_buckets;
+  const ulonglong2* bk = reinterpret_cast<const ulonglong2*>(T.merge_slots + (size_t)h * kBucket);
+  const ulonglong2 s01 = bk[0], s23 = bk[1];
+  uint32_t r = bucket_rank(s01, s23, khi, klo);
+  if (r == kNoRank && s23.y != kEmptySlot) {  // slots fill in order within a bucket
+    for (uint32_t probe = 1; probe <= T.merge_buckets; ++probe) {
+      h = (h + 1) & T.merge_buckets;
+      bk = reinterpret_cast<const ulonglong2*>(T.merge_slots + (size_t)h * kBucket);
+      const ulonglong2 t01 = bk[0], t23 = bk[1];
+      r = bucket_rank(t01, t23, khi, klo);
+      if (r != kNoRank || t23.y == kEmptySlot) break;
+    }
   }
-  return kNoRank;
+  return r;
 }
 
 // NW dwords holding the LDS bytes text[off .. off + 4 NW), read with NW + 1
@@ -208,15 +227,13 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
     const uint32_t nsym = chose ? 256u + r : sym;
     const uint32_t n1 = row_next<ROW>(nsym);
     const uint32_t n2 = row_next2<ROW>(nsym);
-    uint32_t nrk = rk;
-    if (live && !gone && k < cur) {
-      const uint32_t kn = chose ? k + 2 : k + 1;  // next surviving position
-      nrk = kNoRank;
-      if (kn < cur) {
-        const bool chose_n = (S >> (row_base + kn)) & 1ull;
-        nrk = (chose || chose_n) ? merge_rank(T, nsym, chose ? n2 : n1) : rk;
-      }
-    }
+    // the pair starting at this symbol after the round: gone past the end,
+    // new next to a merge (one probe), or unchanged
+    const uint32_t kn = chose ? k + 2 : k + 1;  // next surviving position
+    const bool here = live && !gone && k < cur;
+    const bool chose_n = kn < cur && ((S >> ((row_base + kn) & 63u)) & 1ull);
+    uint32_t nrk = here && kn >= cur ? kNoRank : rk;
+    if (here && kn < cur && (chose || chose_n)) nrk = merge_rank(T, nsym, chose ? n2 : n1);
     const uint32_t nk = k - row_count_below<ROW>(S << 1, row_base, k);
     const uint32_t dst = !live ? lane : ((gone || k >= cur) ? row_base + ROW - 1 : row_base + nk);
     sym = (uint32_t)__builtin_amdgcn_ds_permute((int)(dst << 2), (int)nsym);
