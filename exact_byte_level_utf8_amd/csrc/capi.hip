@@ -153,6 +153,9 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
   const uint32_t bmask = (uint32_t)(slots / kBucket - 1);
   std::vector<uint64_t> mtab(slots, kEmptySlot);
   std::vector<uint32_t> pr(65536, kNoRank);
+  // per token: lowest rank of a merge taking it as right operand (x), as
+  // left operand (y); kNoRank for none
+  std::vector<uint32_t> tmin(2 * (256 + n_merges), kNoRank);
   std::vector<std::vector<uint8_t>> tok(256 + n_merges);
   for (uint32_t i = 0; i < 256; ++i) tok[i] = {(uint8_t)i};
   for (size_t r = 0; r < n_merges; ++r) {
@@ -172,6 +175,8 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
       }
     }
     if ((a | bb) < 256) pr[(a << 8) | bb] = (uint32_t)r;
+    tmin[2 * (size_t)bb] = std::min(tmin[2 * (size_t)bb], (uint32_t)r);
+    tmin[2 * (size_t)a + 1] = std::min(tmin[2 * (size_t)a + 1], (uint32_t)r);
     tok[256 + r] = tok[a];
     tok[256 + r].insert(tok[256 + r].end(), tok[bb].begin(), tok[bb].end());
   }
@@ -217,6 +222,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
     if (hipMalloc((void**)&ctx->d_merge_slots, slots * 8) != hipSuccess ||
         hipMalloc((void**)&ctx->d_pair_rank, pr.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_tok_len, ctx->tok_len.size() * 4) != hipSuccess ||
+        hipMalloc((void**)&ctx->d_tok_min, tmin.size() * 4) != hipSuccess ||
         hipHostMalloc((void**)&ctx->h_ctr, sizeof(Counters), hipHostMallocMapped) != hipSuccess) {
       rc = TOK_E_NOMEM;
       break;
@@ -225,6 +231,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
         hipMemcpy(ctx->d_pair_rank, pr.data(), pr.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(ctx->d_tok_len, ctx->tok_len.data(), ctx->tok_len.size() * 4, hipMemcpyHostToDevice) !=
             hipSuccess ||
+        hipMemcpy(ctx->d_tok_min, tmin.data(), tmin.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipHostGetDevicePointer((void**)&ctx->d_ctr, ctx->h_ctr, 0) != hipSuccess)
       break;
     std::memset(ctx->h_ctr, 0, sizeof(Counters));

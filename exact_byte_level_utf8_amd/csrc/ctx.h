@@ -101,6 +101,7 @@ struct tok_ctx {
   uint64_t* d_long_slots = nullptr;
   uint32_t long_buckets = 0;
   uint32_t* d_tok_len = nullptr;
+  uint2* d_tok_min = nullptr;
 
   // scratch, grown on demand
   uint64_t cap = 0;  // input bytes the scratch covers
@@ -146,6 +147,7 @@ struct tok_ctx {
     t.long_slots = words ? d_long_slots : nullptr;
     t.long_buckets = words ? long_buckets : 0;
     t.tok_len = d_tok_len;
+    t.tok_min = d_tok_min;
     return t;
   }
 
@@ -354,6 +356,7 @@ struct tok_ctx {
     dfree(d_word_slots);
     dfree(d_long_slots);
     dfree(d_tok_len);
+    dfree(d_tok_min);
     dfree(d_doc);
     dfree(d_outoff);
     hfree(h_doc);

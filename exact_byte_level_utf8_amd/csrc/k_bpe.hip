@@ -35,6 +35,8 @@
 #include "bpe_util.h"
 #include "wg_scan.h"
 
+#pragma clang diagnostic ignored "-Wbitwise-instead-of-logical"
+
 namespace tok {
 namespace {
 
@@ -186,11 +188,40 @@ __device__ inline uint32_t row_count_below(uint64_t x, uint32_t row_base, uint32
   return (uint32_t)__popc((uint32_t)(x >> row_base) & ((1u << k) - 1u));
 }
 
+// Value of lane k + D (row_up) or k - D (row_down) of the same row of ROW
+// lanes, or kNoRank where that lane lies outside the row.
+template <int ROW, int D>
+__device__ inline uint32_t row_up(uint32_t v, uint32_t k) {
+  if (ROW == 16) return (uint32_t)__builtin_amdgcn_update_dpp((int)kNoRank, (int)v, 0x100 + D, 0xF, 0xF, false);
+  uint32_t x = v;
+#pragma unroll
+  for (int i = 0; i < D; ++i) x = (uint32_t)__builtin_amdgcn_update_dpp((int)kNoRank, (int)x, 0x130, 0xF, 0xF, false);
+  return k + D < (uint32_t)ROW ? x : kNoRank;
+}
+template <int ROW, int D>
+__device__ inline uint32_t row_down(uint32_t v, uint32_t k) {
+  if (ROW == 16) return (uint32_t)__builtin_amdgcn_update_dpp((int)kNoRank, (int)v, 0x110 + D, 0xF, 0xF, false);
+  uint32_t x = v;
+#pragma unroll
+  for (int i = 0; i < D; ++i) x = (uint32_t)__builtin_amdgcn_update_dpp((int)kNoRank, (int)x, 0x138, 0xF, 0xF, false);
+  return k >= (uint32_t)D ? x : kNoRank;
+}
+
 // BPE of one piece per row of ROW lanes (ROW = 16: four pieces per wave; ROW =
 // 32: two; ROW = 64: one), one symbol per lane, in rounds.  Called by all 64
 // lanes; rows without a piece pass active = false.  p: the piece's bytes;
 // tok_out / cnt_out: where its tokens and their count go; chunk_total: the
 // counter of the chunk the piece starts in (all three in LDS).
+//
+// A round merges every pair of the row's lowest rank and every sheltered
+// pair (x, y) of rank r: walking left from x over at most two pairs ranked
+// above r reaches a token that no merge ranked below r takes as its right
+// operand (x itself counts), or the piece start, and likewise to the right
+// of y with left operands.  No merge ranked below r can then reach x or y, so
+// textbook BPE merges (x, y) before anything changes them; adjacent merged
+// pairs always share one rank, and runs of them keep the leftmost
+// non-overlapping pairs.  Each lane carries its token's lowest ranks as right
+// operand (ml) and as left operand (mr).
 template <int ROW>
 __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool active, uint32_t* tok_out,
                            uint8_t* cnt_out, uint32_t* chunk_total) {
@@ -201,8 +232,11 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
   uint32_t sym = k < cur ? (uint32_t)p[k] : 0u;
   const uint32_t nx = row_next<ROW>(sym);
   uint32_t rk = k + 1 < cur ? T.pair_rank[(sym << 8) | nx] : kNoRank;
+  const uint2 m0 = T.tok_min[sym];
+  uint32_t ml = m0.x, mr = m0.y;
   for (;;) {
     if (k + 1 >= cur) rk = kNoRank;
+    if (k >= cur) ml = mr = kNoRank;
     uint32_t key = rk == kNoRank ? 0xFFFFFFFFu : ((rk << 6) | k);
     key = row16_min(key);
     if (ROW == 64) {
@@ -220,11 +254,28 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
     }
     const bool live = key != 0xFFFFFFFFu;
     if (__ballot(live) == 0) break;
-    const uint32_t r = key >> 6;
-    const uint64_t S = select_leftmost(__ballot(live && rk == r), 0);
+    const uint32_t low = key >> 6;
+    // shelter of the pair (k, k + 1).  The neighbours' values are read with
+    // every lane active (a DPP read from an inactive lane yields the
+    // fallback, which would pass for "no rank") and combined without
+    // branches.
+    const uint32_t rl1 = row_down<ROW, 1>(rk, k), rl2 = row_down<ROW, 2>(rk, k);
+    const uint32_t ml1 = row_down<ROW, 1>(ml, k), ml2 = row_down<ROW, 2>(ml, k);
+    const uint32_t rr1 = row_up<ROW, 1>(rk, k), rr2 = row_up<ROW, 2>(rk, k);
+    const uint32_t mr1 = row_up<ROW, 1>(mr, k), mr2 = row_up<ROW, 2>(mr, k), mr3 = row_up<ROW, 3>(mr, k);
+    const bool left = (ml > rk) | ((rl1 > rk) & ((ml1 > rk) | ((rl2 > rk) & (ml2 > rk))));
+    const bool right = (mr1 > rk) | ((rr1 > rk) & ((mr2 > rk) | ((rr2 > rk) & (mr3 > rk))));
+    const bool take = (rk != kNoRank) & ((rk == low) | (left & right));
+    const uint64_t S = select_leftmost(__ballot(take), 0);
     const bool chose = (S >> lane) & 1ull;
     const bool gone = k > 0 && ((S >> (lane - 1)) & 1ull);
-    const uint32_t nsym = chose ? 256u + r : sym;
+    const uint32_t nsym = chose ? 256u + rk : sym;
+    uint32_t nml = ml, nmr = mr;
+    if (chose) {
+      const uint2 m = T.tok_min[nsym];
+      nml = m.x;
+      nmr = m.y;
+    }
     const uint32_t n1 = row_next<ROW>(nsym);
     const uint32_t n2 = row_next2<ROW>(nsym);
     // the pair starting at this symbol after the round: gone past the end,
@@ -238,6 +289,8 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
     const uint32_t dst = !live ? lane : ((gone || k >= cur) ? row_base + ROW - 1 : row_base + nk);
     sym = (uint32_t)__builtin_amdgcn_ds_permute((int)(dst << 2), (int)nsym);
     rk = (uint32_t)__builtin_amdgcn_ds_permute((int)(dst << 2), (int)nrk);
+    ml = (uint32_t)__builtin_amdgcn_ds_permute((int)(dst << 2), (int)nml);
+    mr = (uint32_t)__builtin_amdgcn_ds_permute((int)(dst << 2), (int)nmr);
     if (live) cur -= row_count<ROW>(S, row_base);
   }
   if (active && k < cur) tok_out[k] = sym;
@@ -566,19 +619,23 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   }
   __syncthreads();
 
-  // phase 3: the tile's tokens as one run from its first piece start
-  if (tid < (uint32_t)kChunksPerWg) {  // wave 0, all lanes
-    const uint32_t v = s_cnt[tid];
+  // phase 3: the tile's tokens as one run from its first piece start (the
+  // thread index again through an empty asm, so that no address computed
+  // before the merge phase is kept, and spilled, across it)
+  uint32_t t2 = threadIdx.x;
+  __asm__ volatile("" : "+v"(t2));
+  if (t2 < (uint32_t)kChunksPerWg) {  // wave 0, all lanes
+    const uint32_t v = s_cnt[t2];
     const uint32_t incl = wave_incl_scan(v, AddOp(), 0u);
-    s_excl[tid] = incl - v;
+    s_excl[t2] = incl - v;
     const uint32_t total = __builtin_amdgcn_readlane((int)incl, 63);
-    const uint64_t has = __ballot(c0 + tid < n_chunks && s_flags[tid] != 0);
+    const uint64_t has = __ballot(c0 + t2 < n_chunks && s_flags[t2] != 0);
     uint64_t first = base;
     if (has) {
       const uint32_t l = (uint32_t)__builtin_ctzll(has);
-      first = base + l * kChunk + __builtin_ctz((uint32_t)__builtin_amdgcn_readlane((int)s_flags[tid], (int)l));
+      first = base + l * kChunk + __builtin_ctz((uint32_t)__builtin_amdgcn_readlane((int)s_flags[t2], (int)l));
     }
-    if (tid == 0) {
+    if (t2 == 0) {
       s_first = (uint32_t)first;
       B.tile_cnt[tile] = total;
       B.tile_first[tile] = (uint32_t)first;

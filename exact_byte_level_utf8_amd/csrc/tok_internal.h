@@ -71,6 +71,7 @@ struct Tables {
   const uint64_t* long_slots;   // 4 x uint64 per slot, see long_hash()
   uint32_t long_buckets;        // buckets - 1; long_slots == nullptr disables the table
   const uint32_t* tok_len;      // bytes of each token ID
+  const uint2* tok_min;         // per token: lowest rank of a merge taking it as right operand (x), as left (y)
 };
 
 // Per-call device buffers.
