@@ -180,7 +180,7 @@ __device__ inline uint32_t wave_min(uint32_t v) {
 template <int ROW>
 __device__ inline uint32_t row_count(uint64_t x, uint32_t row_base) {
   if (ROW == 64) return (uint32_t)__popcll(x);
-  return (uint32_t)__popc((uint32_t)(x >> row_base) & (ROW == 32 ? 0xFFFFFFFFu : (1u << ROW) - 1u));
+  return (uint32_t)__popc((uint32_t)(x >> row_base) & (ROW >= 32 ? 0xFFFFFFFFu : (1u << (ROW & 31)) - 1u));
 }
 template <int ROW>
 __device__ inline uint32_t row_count_below(uint64_t x, uint32_t row_base, uint32_t k) {

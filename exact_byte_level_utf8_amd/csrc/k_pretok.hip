@@ -34,7 +34,7 @@ constexpr uint8_t kBDoc = 1, kBOut = 2;
 
 __device__ inline uint32_t dev_class(uint32_t cp) {
   if (cp < 0x80) return ascii_class(cp);
-  if (cp < 0x10000) return (kClsBmp[cp >> 2] >> (2 * (cp & 3u))) & 3u;
+  if (cp < TOK_CLS_LOW) return (kClsLow[cp >> 2] >> (2 * (cp & 3u))) & 3u;
   if (cp >= 0x110000) return kO;
   const uint32_t blk = kClsBlock[cp >> 8];
   return (kClsBits[blk * 64 + ((cp & 255u) >> 2)] >> (2 * (cp & 3u))) & 3u;
@@ -209,7 +209,8 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
 
   // decode every window position into an info word, without branches: the
   // bytes of a position and the four before it come from word reads; class
-  // lookups of all rounds are issued before any is used
+  // lookups of all rounds (one direct table up to U+1FFFF, so emoji too) are
+  // issued before any is used
   {
     uint32_t cps[kWinRounds], pre[kWinRounds];
 #pragma unroll
@@ -243,12 +244,12 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
 #pragma unroll
     for (int j = 0; j < kWinRounds; ++j) {
       const uint32_t cp = cps[j];
-      const uint32_t bmp = kClsBmp[min(cp, 0xFFFFu) >> 2];
-      cls[j] = cp < 0x80u ? ascii_class(cp) : (bmp >> (2u * (cp & 3u))) & 3u;
+      const uint32_t low = kClsLow[min(cp, (uint32_t)TOK_CLS_LOW - 1u) >> 2];
+      cls[j] = cp < 0x80u ? ascii_class(cp) : (low >> (2u * (cp & 3u))) & 3u;
     }
 #pragma unroll
     for (int j = 0; j < kWinRounds; ++j)
-      if (cps[j] >= 0x10000u) cls[j] = dev_class(cps[j]);  // rare: two-level table above the BMP
+      if (cps[j] >= (uint32_t)TOK_CLS_LOW) cls[j] = dev_class(cps[j]);  // rare: two-level table above U+1FFFF
 #pragma unroll
     for (int j = 0; j < kWinRounds; ++j) {
       const int k = tid + j * NT;

@@ -46,7 +46,7 @@ namespace {
 
 uint32_t host_class(uint32_t cp) {
   if (cp < 0x80) return ascii_class(cp);
-  if (cp < 0x10000) return (kClsBmp[cp >> 2] >> (2 * (cp & 3u))) & 3u;
+  if (cp < TOK_CLS_LOW) return (kClsLow[cp >> 2] >> (2 * (cp & 3u))) & 3u;
   if (cp >= 0x110000) return kO;
   const uint32_t blk = kClsBlock[cp >> 8];
   return (kClsBits[blk * 64 + ((cp & 255u) >> 2)] >> (2 * (cp & 3u))) & 3u;
