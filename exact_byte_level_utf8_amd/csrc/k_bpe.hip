@@ -232,7 +232,11 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
   uint32_t sym = k < cur ? (uint32_t)p[k] : 0u;
   const uint32_t nx = row_next<ROW>(sym);
   uint32_t rk = k + 1 < cur ? T.pair_rank[(sym << 8) | nx] : kNoRank;
-  const uint2 m0 = T.tok_min[sym];
+  // held across the rounds (the empty asm keeps the compiler from reloading
+  // it from the kernel arguments in every round)
+  const uint2* __restrict__ tok_min = T.tok_min;
+  __asm__ volatile("" : "+s"(tok_min));
+  const uint2 m0 = tok_min[sym];
   uint32_t ml = m0.x, mr = m0.y;
   for (;;) {
     if (k + 1 >= cur) rk = kNoRank;
@@ -272,7 +276,7 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
     const uint32_t nsym = chose ? 256u + rk : sym;
     uint32_t nml = ml, nmr = mr;
     if (chose) {
-      const uint2 m = T.tok_min[nsym];
+      const uint2 m = tok_min[nsym];
       nml = m.x;
       nmr = m.y;
     }
