@@ -24,7 +24,7 @@ TOK_E_CAPACITY, TOK_E_TOOLONG, TOK_E_DEVICE, TOK_E_NOMEM, TOK_E_SESSION = 5, 6, 
 # every function declared in include/tok.h
 EXPORTS = (
     "tok_load", "tok_free", "tok_strerror", "tok_encode", "tok_encode_dev", "tok_encode_batch",
-    "tok_encode_batch_dev", "tok_pretokenize_dev", "tok_repair", "tok_sync_boundary", "tok_get_info",
+    "tok_encode_batch_dev", "tok_encode_spans_dev", "tok_encode_spans", "tok_pretokenize_dev", "tok_repair", "tok_sync_boundary", "tok_get_info",
     "tok_token_lengths", "tok_set_graph", "tok_graph_count", "tok_set_profiling", "tok_stage_ms",
 )
 
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.tok_encode_dev.argtypes = [vp, vp, sz, vp, sz, szp, vp]
         L.tok_encode_batch.argtypes = [vp, vp, vp, sz, vp, sz, vp]
         L.tok_encode_batch_dev.argtypes = [vp, vp, sz, vp, sz, vp, sz, vp, szp, vp]
+        L.tok_encode_spans_dev.argtypes = [vp, vp, sz, vp, sz, vp, vp, sz, vp, szp, vp]
+        L.tok_encode_spans.argtypes = [vp, vp, sz, vp, vp, sz, szp]
         L.tok_pretokenize_dev.argtypes = [vp, vp, sz, vp, sz, vp, vp]
         L.tok_repair.argtypes = [vp, vp, sz, sz, vp, sz, sz, szp, ctypes.POINTER(RepairInfo)]
         L.tok_sync_boundary.argtypes = [i32, ctypes.c_uint32, ctypes.c_uint32]
@@ -80,7 +82,7 @@ def lib() -> ctypes.CDLL:
         L.tok_set_profiling.argtypes = [vp, i32]
         L.tok_stage_ms.argtypes = [vp, vp, i32]
         for name in ("tok_load", "tok_encode", "tok_encode_dev", "tok_encode_batch",
-                     "tok_encode_batch_dev", "tok_pretokenize_dev", "tok_repair", "tok_sync_boundary",
+                     "tok_encode_batch_dev", "tok_encode_spans_dev", "tok_encode_spans", "tok_encode_spans_dev", "tok_encode_spans", "tok_pretokenize_dev", "tok_repair", "tok_sync_boundary",
                      "tok_get_info", "tok_set_graph", "tok_set_profiling", "tok_stage_ms"):
             getattr(L, name).restype = i32
         _lib = L
@@ -106,10 +108,11 @@ def sync_boundary(pattern: str | int, prev_cp: int, cp: int) -> bool:
 
 
 def _dev_ptr(t, dtype_name: str, what: str) -> int:
-    """Device pointer of a contiguous CUDA/HIP torch tensor of the given dtype."""
+    """Device pointer of a contiguous CUDA/HIP torch tensor of the given dtype
+    (dtype_name may list alternatives separated by '|')."""
     if not t.is_cuda:
         raise ValueError(f"{what} must be a device tensor")
-    if str(t.dtype) != f"torch.{dtype_name}":
+    if str(t.dtype) not in [f"torch.{d}" for d in dtype_name.split("|")]:
         raise ValueError(f"{what} must be {dtype_name}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
@@ -158,6 +161,16 @@ class Tokenizer:
         _check(lib().tok_encode(self._h, b, len(b), ids.ctypes.data, ids.size, ctypes.byref(n)), "tok_encode")
         return ids[: n.value].copy()
 
+    def encode_spans(self, text) -> tuple[np.ndarray, np.ndarray]:
+        """tok_encode_spans: (ids, spans), spans[k] = byte where token k starts."""
+        b = text.encode("utf-8") if isinstance(text, str) else bytes(text)
+        ids = np.empty(max(len(b), 1), dtype=np.int32)
+        spans = np.empty(max(len(b), 1), dtype=np.uint32)
+        n = ctypes.c_size_t(0)
+        _check(lib().tok_encode_spans(self._h, b, len(b), ids.ctypes.data, spans.ctypes.data, ids.size,
+                                      ctypes.byref(n)), "tok_encode_spans")
+        return ids[: n.value].copy(), spans[: n.value].copy()
+
     def encode_batch(self, data: bytes, doc_off) -> tuple[np.ndarray, np.ndarray]:
         off = np.ascontiguousarray(np.asarray(doc_off, dtype=np.uint64))
         n_docs = off.size - 1
@@ -189,6 +202,17 @@ class Tokenizer:
             _check(rc, "tok_repair")
             return buf[: n.value].copy(), {f: getattr(info, f) for f, _ in RepairInfo._fields_}
 
+    def repair_into(self, buf: np.ndarray, n_session: int, text: bytes, old_len: int) -> tuple[int, dict]:
+        """tok_repair in place on a caller-owned int32 buffer: buf[:n_session] holds the IDs of
+        text[:old_len]; on return buf[:n] holds the IDs of text.  Returns (n, info)."""
+        if buf.dtype != np.int32 or not buf.flags.c_contiguous:
+            raise ValueError("buf must be a contiguous int32 array")
+        n = ctypes.c_size_t(0)
+        info = RepairInfo()
+        _check(lib().tok_repair(self._h, buf.ctypes.data, n_session, buf.size, text, old_len, len(text),
+                                ctypes.byref(n), ctypes.byref(info)), "tok_repair")
+        return n.value, {f: getattr(info, f) for f, _ in RepairInfo._fields_}
+
     # --------------------------------------------------------- device memory
     def encode_dev(self, d_text, d_ids, length: int | None = None, stream=None) -> int:
         """Encode d_text[:length] (uint8 device tensor) into d_ids (int32); returns the count."""
@@ -206,6 +230,24 @@ class Tokenizer:
                                           _dev_ptr(d_ids, "int32", "ids"), d_ids.numel(),
                                           _dev_ptr(d_out_off, "uint64", "out_off"), ctypes.byref(n),
                                           _stream_handle(stream)), "tok_encode_batch_dev")
+        return n.value
+
+    def encode_spans_dev(self, d_text, d_ids, d_spans, d_doc_off=None, d_out_off=None, length: int | None = None,
+                         stream=None) -> int:
+        """tok_encode_spans_dev: IDs into d_ids (int32) and each token's first byte into d_spans
+        (uint32 tensor, or int32 holding uint32 offsets); with d_doc_off (uint64) a batch, whose
+        per-document output offsets go to d_out_off (uint64).  Returns the count."""
+        n_bytes = d_text.numel() if length is None else int(length)
+        if d_spans.numel() < d_ids.numel():
+            raise ValueError("spans must hold as many entries as ids")
+        doc = _dev_ptr(d_doc_off, "uint64", "doc_off") if d_doc_off is not None else None
+        n_docs = d_doc_off.numel() - 1 if d_doc_off is not None else 0
+        oo = _dev_ptr(d_out_off, "uint64", "out_off") if d_out_off is not None else None
+        n = ctypes.c_size_t(0)
+        _check(lib().tok_encode_spans_dev(self._h, _dev_ptr(d_text, "uint8", "text"), n_bytes, doc, n_docs,
+                                          _dev_ptr(d_ids, "int32", "ids"), _dev_ptr(d_spans, "int32|uint32", "spans"),
+                                          d_ids.numel(), oo, ctypes.byref(n), _stream_handle(stream)),
+               "tok_encode_spans_dev")
         return n.value
 
     def pretokenize_dev(self, d_text, d_flags, d_doc_off=None, stream=None) -> None:

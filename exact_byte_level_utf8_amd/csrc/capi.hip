@@ -265,7 +265,7 @@ int tok_encode_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, int32_t* d_i
   if (rc) return rc;
   hipStream_t s = stream ? (hipStream_t)stream : ctx->stream;
   uint32_t total = 0;
-  rc = ctx->run(d_text, len, nullptr, 0, d_ids, cap, nullptr, s, true, nullptr, &total);
+  rc = ctx->run(d_text, len, nullptr, 0, d_ids, nullptr, cap, nullptr, s, true, nullptr, &total);
   if (rc) return rc;
   *n_out = total;
   return total > cap ? TOK_E_CAPACITY : TOK_OK;
@@ -283,7 +283,7 @@ int tok_encode(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids, size
   std::memcpy(ctx->h_text, text, len);
   HIP_OK(hipMemcpyAsync(ctx->d_text, ctx->h_text, len, hipMemcpyHostToDevice, s));
   uint32_t total = 0;
-  rc = ctx->run(ctx->d_text, len, nullptr, 0, ctx->d_ids, len, nullptr, s, true, nullptr, &total);
+  rc = ctx->run(ctx->d_text, len, nullptr, 0, ctx->d_ids, nullptr, len, nullptr, s, true, nullptr, &total);
   if (rc) return rc;
   *n_out = total;
   if (total > cap) return TOK_E_CAPACITY;
@@ -306,7 +306,7 @@ int tok_encode_batch_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
   if (rc) return rc;
   hipStream_t s = stream ? (hipStream_t)stream : ctx->stream;
   uint32_t total = 0;
-  rc = ctx->run(d_text, len, d_doc_off, (uint32_t)n_docs, d_ids, cap, d_out_off, s, true, nullptr, &total);
+  rc = ctx->run(d_text, len, d_doc_off, (uint32_t)n_docs, d_ids, nullptr, cap, d_out_off, s, true, nullptr, &total);
   if (rc) return rc;
   *n_out = total;
   return total > cap ? TOK_E_CAPACITY : TOK_OK;
@@ -334,7 +334,7 @@ int tok_encode_batch(tok_ctx* ctx, const uint8_t* text, const uint64_t* doc_off,
   std::memcpy(ctx->h_doc, doc_off, (n_docs + 1) * 8);
   HIP_OK(hipMemcpyAsync(ctx->d_doc, ctx->h_doc, (n_docs + 1) * 8, hipMemcpyHostToDevice, s));
   uint32_t total = 0;
-  rc = ctx->run(ctx->d_text, len, ctx->d_doc, (uint32_t)n_docs, ctx->d_ids, len, ctx->d_outoff, s, true,
+  rc = ctx->run(ctx->d_text, len, ctx->d_doc, (uint32_t)n_docs, ctx->d_ids, nullptr, len, ctx->d_outoff, s, true,
                 nullptr, &total);
   if (rc) return rc;
   HIP_OK(hipMemcpyAsync(ctx->h_doc, ctx->d_outoff, (n_docs + 1) * 8, hipMemcpyDeviceToHost, s));
@@ -344,6 +344,53 @@ int tok_encode_batch(tok_ctx* ctx, const uint8_t* text, const uint64_t* doc_off,
   std::memcpy(out_off, ctx->h_doc, (n_docs + 1) * 8);
   if (total > cap) return TOK_E_CAPACITY;
   if (total) std::memcpy(ids, ctx->h_ids, (size_t)total * 4);
+  return TOK_OK;
+}
+
+int tok_encode_spans_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const uint64_t* d_doc_off,
+                         size_t n_docs, int32_t* d_ids, uint32_t* d_spans, size_t cap, uint64_t* d_out_off,
+                         size_t* n_out, void* stream) {
+  if (!ctx || !n_out || (!d_text && len) || (cap && (!d_ids || !d_spans)) || n_docs >= 0xFFFFFFFFu ||
+      (d_doc_off && (n_docs == 0 || !d_out_off)))
+    return TOK_E_ARG;
+  *n_out = 0;
+  if (len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
+  if (len == 0 && !d_doc_off) return TOK_OK;
+  DeviceGuard g(ctx->device);
+  int rc = ctx->ensure(len ? len : 1);
+  if (rc) return rc;
+  hipStream_t s = stream ? (hipStream_t)stream : ctx->stream;
+  uint32_t total = 0;
+  rc = ctx->run(d_text, len, d_doc_off, d_doc_off ? (uint32_t)n_docs : 0, d_ids, d_spans, cap,
+                d_doc_off ? d_out_off : nullptr, s, true, nullptr, &total);
+  if (rc) return rc;
+  *n_out = total;
+  return total > cap ? TOK_E_CAPACITY : TOK_OK;
+}
+
+int tok_encode_spans(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids, uint32_t* spans, size_t cap,
+                     size_t* n_out) {
+  if (!ctx || !n_out || (!text && len) || (cap && (!ids || !spans))) return TOK_E_ARG;
+  *n_out = 0;
+  if (len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
+  if (len == 0) return TOK_OK;
+  DeviceGuard g(ctx->device);
+  int rc = ctx->ensure(len);
+  if (!rc) rc = ctx->ensure_spans();
+  if (rc) return rc;
+  hipStream_t s = ctx->stream;
+  std::memcpy(ctx->h_text, text, len);
+  HIP_OK(hipMemcpyAsync(ctx->d_text, ctx->h_text, len, hipMemcpyHostToDevice, s));
+  uint32_t total = 0;
+  rc = ctx->run(ctx->d_text, len, nullptr, 0, ctx->d_ids, ctx->d_spans, len, nullptr, s, true, nullptr, &total);
+  if (rc) return rc;
+  *n_out = total;
+  if (total > cap) return TOK_E_CAPACITY;
+  HIP_OK(hipMemcpyAsync(ctx->h_ids, ctx->d_ids, (size_t)total * 4, hipMemcpyDeviceToHost, s));
+  HIP_OK(hipMemcpyAsync(ctx->h_spans, ctx->d_spans, (size_t)total * 4, hipMemcpyDeviceToHost, s));
+  HIP_OK(hipStreamSynchronize(s));
+  std::memcpy(ids, ctx->h_ids, (size_t)total * 4);
+  std::memcpy(spans, ctx->h_spans, (size_t)total * 4);
   return TOK_OK;
 }
 
@@ -358,7 +405,7 @@ int tok_pretokenize_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const u
   int rc = ctx->ensure(len);
   if (rc) return rc;
   hipStream_t s = stream ? (hipStream_t)stream : ctx->stream;
-  return ctx->run(d_text, len, d_doc_off, (uint32_t)(d_doc_off ? n_docs : 0), nullptr, 0, nullptr, s, true,
+  return ctx->run(d_text, len, d_doc_off, (uint32_t)(d_doc_off ? n_docs : 0), nullptr, nullptr, 0, nullptr, s, true,
                   d_flags, nullptr);
 }
 

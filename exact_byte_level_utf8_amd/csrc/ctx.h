@@ -62,13 +62,14 @@ struct GraphKey {
   const uint64_t* doc_off;
   uint32_t n_docs;
   int32_t* out;
+  uint32_t* spans;
   uint64_t out_cap;
   uint64_t* out_off;
   hipStream_t s;
   bool words;
   bool operator==(const GraphKey& o) const {
     return text == o.text && n == o.n && doc_off == o.doc_off && n_docs == o.n_docs && out == o.out &&
-           out_cap == o.out_cap && out_off == o.out_off && s == o.s && words == o.words;
+           spans == o.spans && out_cap == o.out_cap && out_off == o.out_off && s == o.s && words == o.words;
   }
 };
 
@@ -110,6 +111,7 @@ struct tok_ctx {
   uint64_t gen = 0;           // number of the last call
   uint8_t* d_text = nullptr;  // staging for host-memory calls
   int32_t* d_ids = nullptr;
+  uint32_t* d_spans = nullptr;  // span staging of host-memory calls, made on first use
   uint64_t doc_cap = 0;
   uint64_t* d_doc = nullptr;
   uint64_t* d_outoff = nullptr;
@@ -117,6 +119,7 @@ struct tok_ctx {
   // pinned host memory
   uint8_t* h_text = nullptr;
   int32_t* h_ids = nullptr;
+  uint32_t* h_spans = nullptr;
   uint64_t* h_doc = nullptr;
   Counters* h_ctr = nullptr;
 
@@ -164,8 +167,10 @@ struct tok_ctx {
     dfree(b.ws_sel);
     dfree(d_text);
     dfree(d_ids);
+    dfree(d_spans);
     hfree(h_text);
     hfree(h_ids);
+    hfree(h_spans);
     cap = 0;
   }
 
@@ -198,6 +203,19 @@ struct tok_ctx {
     return TOK_OK;
   }
 
+  // Span staging for host-memory calls, sized like d_ids (after ensure()).
+  int ensure_spans() {
+    if (d_spans) return TOK_OK;
+    if (hipMalloc((void**)&d_spans, (cap + 64) * sizeof(uint32_t)) != hipSuccess ||
+        hipHostMalloc((void**)&h_spans, (cap + 64) * sizeof(uint32_t), hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      dfree(d_spans);
+      hfree(h_spans);
+      return TOK_E_NOMEM;
+    }
+    return TOK_OK;
+  }
+
   int ensure_docs(uint64_t n_docs) {
     if (n_docs + 1 <= doc_cap && d_doc) return TOK_OK;
     (void)hipStreamSynchronize(stream);
@@ -225,7 +243,7 @@ struct tok_ctx {
 
   // The three stages of one call, enqueued on s (eagerly or under capture).
   void enqueue(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, int32_t* out,
-               uint64_t out_cap, uint64_t* out_off, hipStream_t s, const Bufs& bb, bool words,
+               uint32_t* spans, uint64_t out_cap, uint64_t* out_off, hipStream_t s, const Bufs& bb, bool words,
                uint16_t* out_flags) {
     const Tables t = tables(words);
     if (n == 0) {  // only a batch of empty documents gets here
@@ -235,7 +253,7 @@ struct tok_ctx {
     launch_pretok(text, n, doc_off, n_docs, pattern, bb, s, e0(0), e1(0));
     if (out_flags) return;
     launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s, e0(1), e1(1));
-    launch_assemble(n, bb, out, out_cap, doc_off, n_docs, out_off, s, e0(2), e1(2));
+    launch_assemble(n, bb, out, spans, d_tok_len, out_cap, doc_off, n_docs, out_off, s, e0(2), e1(2));
   }
 
   // The captured pipeline for this call shape: found, or captured now on s
@@ -260,7 +278,7 @@ struct tok_ctx {
     hipGraph_t gr = nullptr;
     hipGraphExec_t ex = nullptr;
     if (hipStreamBeginCapture(k.s, hipStreamCaptureModeThreadLocal) != hipSuccess) return nullptr;
-    enqueue(k.text, k.n, k.doc_off, k.n_docs, k.out, k.out_cap, k.out_off, k.s, bb, k.words, nullptr);
+    enqueue(k.text, k.n, k.doc_off, k.n_docs, k.out, k.spans, k.out_cap, k.out_off, k.s, bb, k.words, nullptr);
     const bool captured = hipStreamEndCapture(k.s, &gr) == hipSuccess && gr;
     const bool made = captured && hipGraphInstantiate(&ex, gr, nullptr, nullptr, 0) == hipSuccess;
     if (gr) (void)hipGraphDestroy(gr);
@@ -284,13 +302,13 @@ struct tok_ctx {
   // the status words are cleared first, since every replay reports the call
   // number that was captured.
   int run(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, int32_t* out,
-          uint64_t out_cap, uint64_t* out_off, hipStream_t s, bool words, uint16_t* out_flags,
+          uint32_t* spans, uint64_t out_cap, uint64_t* out_off, hipStream_t s, bool words, uint16_t* out_flags,
           uint32_t* total) {
     volatile Counters* c = h_ctr;
     uint64_t call = 0;
     GraphEntry* g = nullptr;
     if (graph_mode && !prof && !out_flags && n > 0)
-      g = graph_for(GraphKey{text, n, doc_off, n_docs, out, out_cap, out_off, s, words});
+      g = graph_for(GraphKey{text, n, doc_off, n_docs, out, spans, out_cap, out_off, s, words});
     if (g) {
       call = g->gen;
       c->err_utf8 = 0;
@@ -301,7 +319,7 @@ struct tok_ctx {
       Bufs bb = b;
       if (out_flags) bb.flags = out_flags;
       bb.gen = call = ++gen;
-      enqueue(text, n, doc_off, n_docs, out, out_cap, out_off, s, bb, words, out_flags);
+      enqueue(text, n, doc_off, n_docs, out, spans, out_cap, out_off, s, bb, words, out_flags);
     }
     HIP_OK(hipGetLastError());
     HIP_OK(hipStreamSynchronize(s));
@@ -338,7 +356,7 @@ struct tok_ctx {
     HIP_OK(hipMemcpyAsync(bb.sum2, zero.data(), ((tiles >> kSum2Shift) + 1) * 4, hipMemcpyHostToDevice, stream));
     const Tables t = tables(false);
     launch_pieces(d_text, n, t, bb, nullptr, 0, nullptr, stream);
-    launch_assemble(n, bb, d_ids, n, nullptr, 0, nullptr, stream);
+    launch_assemble(n, bb, d_ids, nullptr, nullptr, n, nullptr, 0, nullptr, stream);
     HIP_OK(hipGetLastError());
     HIP_OK(hipStreamSynchronize(stream));
     const volatile Counters* c = h_ctr;

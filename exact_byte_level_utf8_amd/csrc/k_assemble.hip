@@ -10,6 +10,13 @@
 // restores document order and writes the result), and the documents that
 // start in the tile get their output offsets.  The last tile publishes the
 // total.
+//
+// With span export on, each ID also gets the byte where its token starts
+// (TokTier, section 7 "Session-state construction" and Appendix E, "Route C:
+// GPU full tokenization with span export": gather each token's byte length,
+// a cumulative sum gives the offsets).  A tile's run covers the text
+// contiguously from its first piece start, so the offsets are that byte plus
+// a workgroup scan of the lengths along the run: no scan crosses tiles.
 #include "tok_internal.h"
 #include "wg_scan.h"
 
@@ -18,10 +25,13 @@ namespace {
 
 constexpr uint32_t kAsmThreads = 256;
 
+template <bool SPANS>
 __global__ void __launch_bounds__(kAsmThreads)
-assemble_kernel(uint64_t n, Bufs B, int32_t* __restrict__ out, uint64_t cap, const uint64_t* __restrict__ doc_off,
+assemble_kernel(uint64_t n, Bufs B, int32_t* __restrict__ out, uint32_t* __restrict__ spans,
+                const uint32_t* __restrict__ tok_len, uint64_t cap, const uint64_t* __restrict__ doc_off,
                 uint32_t n_docs, uint64_t* __restrict__ out_off) {
   __shared__ uint32_t s_part[kAsmThreads / kWave];
+  __shared__ uint32_t s_scan[kAsmThreads / kWave];
   __shared__ uint32_t s_doc0;
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   const uint32_t tile = blockIdx.x;
@@ -44,9 +54,27 @@ assemble_kernel(uint64_t n, Bufs B, int32_t* __restrict__ out, uint64_t cap, con
   __syncthreads();
   const uint32_t base = __builtin_amdgcn_readfirstlane(s_part[0] + s_part[1] + s_part[2] + s_part[3]);
   const uint32_t cnt = __builtin_amdgcn_readfirstlane(B.tile_cnt[tile]);
-  const int32_t* run = B.staging + B.tile_first[tile];
-  for (uint32_t i = tid; i < cnt; i += kAsmThreads)
-    if ((uint64_t)base + i < cap) out[base + i] = run[i];
+  const uint32_t first = __builtin_amdgcn_readfirstlane(B.tile_first[tile]);
+  const int32_t* run = B.staging + first;
+  if constexpr (SPANS) {
+    // uniform trip count: the scan inside holds barriers
+    uint32_t at = first;
+    for (uint32_t i0 = 0; i0 < cnt; i0 += kAsmThreads) {
+      const uint32_t i = i0 + tid;
+      const int32_t id = i < cnt ? run[i] : 0;
+      const uint32_t len = i < cnt ? tok_len[id] : 0u;
+      uint32_t chunk = 0;
+      const uint32_t before = wg_excl_scan<kAsmThreads>(len, 0u, AddOp(), s_scan, &chunk);
+      if (i < cnt && (uint64_t)base + i < cap) {
+        out[base + i] = id;
+        spans[base + i] = at + before;
+      }
+      at += chunk;
+    }
+  } else {
+    for (uint32_t i = tid; i < cnt; i += kAsmThreads)
+      if ((uint64_t)base + i < cap) out[base + i] = run[i];
+  }
   if (last && tid == 0) {
     B.ctr->total = base + cnt;
     __threadfence_system();
@@ -87,11 +115,17 @@ __global__ void empty_batch_kernel(Bufs B, const uint64_t* __restrict__ doc_off,
 
 }  // namespace
 
-void launch_assemble(uint64_t n, Bufs b, int32_t* out, uint64_t cap, const uint64_t* doc_off,
-                     uint32_t n_docs, uint64_t* out_off, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+void launch_assemble(uint64_t n, Bufs b, int32_t* out, uint32_t* spans, const uint32_t* tok_len, uint64_t cap,
+                     const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s, hipEvent_t e0,
+                     hipEvent_t e1) {
   const uint32_t tiles = (uint32_t)((n + kPieceTile - 1) / kPieceTile);
-  if (tiles)
-    launch_on(assemble_kernel, dim3(tiles), dim3(kAsmThreads), s, e0, e1, n, b, out, cap, doc_off, n_docs, out_off);
+  if (!tiles) return;
+  if (spans)
+    launch_on(assemble_kernel<true>, dim3(tiles), dim3(kAsmThreads), s, e0, e1, n, b, out, spans, tok_len, cap,
+              doc_off, n_docs, out_off);
+  else
+    launch_on(assemble_kernel<false>, dim3(tiles), dim3(kAsmThreads), s, e0, e1, n, b, out, spans, tok_len, cap,
+              doc_off, n_docs, out_off);
 }
 
 void launch_empty_batch(Bufs b, const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s) {

@@ -140,8 +140,10 @@ void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uin
 void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, const uint64_t* doc_off,
                    uint32_t n_docs, uint64_t* out_off, hipStream_t s, hipEvent_t e0 = nullptr,
                    hipEvent_t e1 = nullptr);
-void launch_assemble(uint64_t n, Bufs b, int32_t* out, uint64_t cap, const uint64_t* doc_off,
-                     uint32_t n_docs, uint64_t* out_off, hipStream_t s, hipEvent_t e0 = nullptr,
-                     hipEvent_t e1 = nullptr);
+// spans: optional uint32 per output ID, the byte where its token starts
+// (tok_len is read only when spans is set).
+void launch_assemble(uint64_t n, Bufs b, int32_t* out, uint32_t* spans, const uint32_t* tok_len, uint64_t cap,
+                     const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s,
+                     hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 }  // namespace tok

@@ -160,6 +160,37 @@ int tok_encode_batch_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
                          size_t* n_out, void* stream);
 
 /*
+ * tok_encode_spans_dev -- tok_encode_dev / tok_encode_batch_dev that also
+ * exports, for every ID, the byte where its token starts (span export:
+ * TokTier, section 7 "Session-state construction" and Appendix E, "Route C:
+ * GPU full tokenization with span export": each ID's token byte length is
+ * gathered and a cumulative sum gives the offsets, on the device).
+ *
+ * d_doc_off, n_docs: as tok_encode_batch_dev (then d_out_off receives the
+ *            per-document output offsets), or NULL / 0 for one request
+ *            (d_out_off is then ignored and may be NULL).
+ * d_ids, d_spans, cap: device arrays of cap int32 IDs and cap uint32 byte
+ *            offsets.  d_spans[k] counts from the start of d_text (in a batch
+ *            too, not from the document's start); token k covers
+ *            d_text[d_spans[k] .. d_spans[k] + its byte length), and the
+ *            tokens of a document tile it without gaps.
+ * Errors, stream, capacity: as tok_encode_dev (on TOK_E_CAPACITY the first
+ * cap IDs and offsets are written).
+ */
+int tok_encode_spans_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const uint64_t* d_doc_off,
+                         size_t n_docs, int32_t* d_ids, uint32_t* d_spans, size_t cap, uint64_t* d_out_off,
+                         size_t* n_out, void* stream);
+
+/*
+ * tok_encode_spans -- tok_encode with span export into host memory: ids and
+ * spans are host arrays of cap entries; spans[k] is the byte of text where
+ * token k starts.  Errors as tok_encode (on TOK_E_CAPACITY neither array is
+ * written).
+ */
+int tok_encode_spans(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids, uint32_t* spans, size_t cap,
+                     size_t* n_out);
+
+/*
  * tok_pretokenize_dev -- the pre-tokenization stage alone, for split-level
  * checks (TokTier, section 5.2, compares pieces before IDs).  Writes one
  * uint16 per 16-byte chunk of d_text to d_flags (ceil(len / 16) words on the

@@ -52,6 +52,8 @@ def lib():
             fn.restype = ctypes.c_int
         L.orc_encode_batch.argtypes = [vp, u8p, vp, sz, vp, sz, vp]
         L.orc_encode_batch.restype = ctypes.c_int
+        L.orc_encode_batch_spans.argtypes = [vp, u8p, vp, sz, vp, vp, sz, vp]
+        L.orc_encode_batch_spans.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -134,3 +136,26 @@ class Oracle:
         if rc:
             raise OracleError(f"encode_batch failed (code {rc})")
         return out[: int(out_off[-1])].copy(), out_off
+
+    def encode_batch_spans(self, data: bytes, doc_off) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """(ids, spans, out_off): spans[k] is the byte of data where token k starts, tracked
+        through the merges themselves (a merged token starts where its left operand did)."""
+        off = np.ascontiguousarray(np.asarray(doc_off, dtype=np.uint64))
+        n_docs = off.size - 1
+        out = np.zeros(max(len(data), 1), dtype=np.int32)
+        spans = np.zeros(max(len(data), 1), dtype=np.uint64)
+        out_off = np.zeros(n_docs + 1, dtype=np.uint64)
+        rc = lib().orc_encode_batch_spans(self._h, data, off.ctypes.data, n_docs, out.ctypes.data,
+                                          spans.ctypes.data, out.size, out_off.ctypes.data)
+        if rc == 1:
+            raise UnicodeDecodeError("utf-8", data, 0, len(data), "invalid UTF-8 (oracle)")
+        if rc:
+            raise OracleError(f"encode_batch_spans failed (code {rc})")
+        t = int(out_off[-1])
+        return out[:t].copy(), spans[:t].copy(), out_off
+
+    def encode_spans(self, text) -> tuple[np.ndarray, np.ndarray]:
+        """(ids, spans) of one text: spans[k] is the byte where token k starts."""
+        b = self._bytes(text)
+        ids, spans, _ = self.encode_batch_spans(b, [0, len(b)])
+        return ids, spans

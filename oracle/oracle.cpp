@@ -233,8 +233,15 @@ struct Oracle {
   std::map<std::pair<uint32_t, uint32_t>, uint32_t> rank;  // (left, right) -> rank
 };
 
-void bpe(const Oracle& o, const uint8_t* b, size_t n, std::vector<int32_t>& out) {
+// Textbook BPE of one piece.  at, when given, receives the byte offset within
+// the piece where each output token starts: a merged token starts where its
+// left operand did (the span export of TokTier, section 7: per-token byte
+// offsets next to the IDs).
+void bpe(const Oracle& o, const uint8_t* b, size_t n, std::vector<int32_t>& out,
+         std::vector<size_t>* at = nullptr) {
   std::vector<uint32_t> sym(b, b + n);
+  std::vector<size_t> start(n);
+  for (size_t i = 0; i < n; ++i) start[i] = i;
   for (;;) {
     size_t best_j = 0;
     uint32_t best_r = UINT32_MAX;
@@ -248,21 +255,29 @@ void bpe(const Oracle& o, const uint8_t* b, size_t n, std::vector<int32_t>& out)
     if (best_r == UINT32_MAX) break;
     sym[best_j] = 256u + best_r;
     sym.erase(sym.begin() + long(best_j) + 1);
+    start.erase(start.begin() + long(best_j) + 1);
   }
   for (uint32_t s : sym) out.push_back(int32_t(s));
+  if (at) at->insert(at->end(), start.begin(), start.end());
 }
 
-int encode_one(const Oracle& o, const uint8_t* s, size_t n, std::vector<int32_t>& out) {
+// spans, when given, receives each token's first byte, counted from s.
+int encode_one(const Oracle& o, const uint8_t* s, size_t n, std::vector<int32_t>& out,
+               std::vector<uint64_t>* spans = nullptr) {
   Text t;
   std::vector<size_t> offs;
   if (!decode_utf8(s, n, t.cp, offs)) return ORC_UTF8;
   t.cls.resize(t.cp.size());
   for (size_t i = 0; i < t.cp.size(); ++i) t.cls[i] = class_of(t.cp[i]);
   std::vector<size_t> st = pretokenize(t, o.pattern);
+  std::vector<size_t> at;
   for (size_t k = 0; k < st.size(); ++k) {
     size_t a = offs[st[k]];
     size_t e = offs[k + 1 < st.size() ? st[k + 1] : t.cp.size()];
-    bpe(o, s + a, e - a, out);
+    at.clear();
+    bpe(o, s + a, e - a, out, spans ? &at : nullptr);
+    if (spans)
+      for (size_t x : at) spans->push_back(a + x);
   }
   return ORC_OK;
 }
@@ -330,20 +345,31 @@ int orc_encode(void* h, const uint8_t* text, size_t len, int32_t* ids, size_t ca
   return ORC_OK;
 }
 
-// Each document [doc_off[i], doc_off[i+1]) is encoded on its own.
-int orc_encode_batch(void* h, const uint8_t* text, const uint64_t* doc_off, size_t n_docs,
-                     int32_t* ids, size_t cap, uint64_t* out_off) {
+// Each document [doc_off[i], doc_off[i+1]) is encoded on its own.  spans
+// (optional, cap entries): each token's first byte in text.
+int orc_encode_batch_spans(void* h, const uint8_t* text, const uint64_t* doc_off, size_t n_docs,
+                           int32_t* ids, uint64_t* spans, size_t cap, uint64_t* out_off) {
   std::vector<int32_t> out;
+  std::vector<uint64_t> sp;
   out_off[0] = 0;
   for (size_t d = 0; d < n_docs; ++d) {
     if (doc_off[d + 1] < doc_off[d]) return ORC_ARG;
-    int rc = encode_one(*static_cast<Oracle*>(h), text + doc_off[d], doc_off[d + 1] - doc_off[d], out);
+    const size_t before = sp.size();
+    int rc = encode_one(*static_cast<Oracle*>(h), text + doc_off[d], doc_off[d + 1] - doc_off[d], out,
+                        spans ? &sp : nullptr);
     if (rc) return rc;
+    for (size_t k = before; k < sp.size(); ++k) sp[k] += doc_off[d];
     out_off[d + 1] = out.size();
   }
   if (out.size() > cap) return ORC_CAP;
   if (!out.empty()) memcpy(ids, out.data(), out.size() * 4);
+  if (spans && !sp.empty()) memcpy(spans, sp.data(), sp.size() * 8);
   return ORC_OK;
+}
+
+int orc_encode_batch(void* h, const uint8_t* text, const uint64_t* doc_off, size_t n_docs,
+                     int32_t* ids, size_t cap, uint64_t* out_off) {
+  return orc_encode_batch_spans(h, text, doc_off, n_docs, ids, nullptr, cap, out_off);
 }
 
 }  // extern "C"

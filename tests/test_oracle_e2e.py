@@ -118,3 +118,41 @@ def test_trainer_reproduces_artifact():
 def test_vocab_strings_unique(name):
     tok = vocab.token_bytes(vocab.merges(name))
     assert len(set(tok)) == len(tok)
+
+
+def _spans_from_bytes(ids, tok, start=0):
+    """Token start bytes as the running sum of the tokens' byte lengths (the
+    gather-and-cumulative-sum reading of span export, TokTier, Appendix E,
+    "Route C: GPU full tokenization with span export")."""
+    lens = np.array([len(tok[i]) for i in ids], dtype=np.uint64)
+    return start + np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.uint64) if len(ids) else lens
+
+
+def test_spans_follow_the_merges(gpt2, llama):
+    """The oracle tracks where each token starts through the merges themselves;
+    pinned here against the token byte strings: every span slices the text to
+    exactly its token's bytes, and the spans are the running sum of lengths."""
+    for (o, tok), seed in ((gpt2, 2), (llama, 3)):
+        b = textgen.mix_text(seed + 70, 50_000).encode()
+        ids, sp = o.encode_spans(b)
+        assert np.array_equal(ids, o.encode(b))
+        assert np.array_equal(sp, _spans_from_bytes(ids, tok))
+        ends = list(sp[1:]) + [len(b)]
+        assert all(b[int(s):int(e)] == tok[i] for s, e, i in zip(sp, ends, ids))
+    ids, sp = gpt2[0].encode_spans(b"")
+    assert len(ids) == 0 and len(sp) == 0
+
+
+def test_batch_spans_are_absolute(llama):
+    """Batch spans count from the start of the concatenated text; every
+    document's first token starts at the document's first byte."""
+    o, tok = llama
+    docs = ["", "abc 123", "中文 x", "", "it's\r\n  ok", textgen.mix_text(91, 2000)]
+    data = "".join(docs).encode()
+    off = np.cumsum([0] + [len(d.encode()) for d in docs]).astype(np.uint64)
+    ids, sp, out_off = o.encode_batch_spans(data, off)
+    for d in range(len(docs)):
+        a, z = int(out_off[d]), int(out_off[d + 1])
+        want_ids = o.encode(docs[d].encode())
+        assert np.array_equal(ids[a:z], want_ids)
+        assert np.array_equal(sp[a:z], _spans_from_bytes(want_ids, tok, int(off[d])))
