@@ -54,6 +54,8 @@ def lib():
         L.orc_encode_batch.restype = ctypes.c_int
         L.orc_encode_batch_spans.argtypes = [vp, u8p, vp, sz, vp, vp, sz, vp]
         L.orc_encode_batch_spans.restype = ctypes.c_int
+        L.orc_encode_added.argtypes = [vp, u8p, vp, sz, vp, u8p, sz, vp, sz, ctypes.POINTER(sz)]
+        L.orc_encode_added.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -159,3 +161,21 @@ class Oracle:
         b = self._bytes(text)
         ids, spans, _ = self.encode_batch_spans(b, [0, len(b)])
         return ids, spans
+
+    def encode_added(self, text, literals) -> np.ndarray:
+        """Encode with added-token literals: literals is a list of (bytes, id); the leftmost,
+        longest literal is taken at each position and the text between literals is encoded
+        segment by segment."""
+        b = self._bytes(text)
+        blob = b"".join(x for x, _ in literals)
+        off = np.cumsum([0] + [len(x) for x, _ in literals]).astype(np.uint64)
+        lid = np.asarray([i for _, i in literals] or [0], dtype=np.int32)
+        out = np.zeros(max(len(b), 1), dtype=np.int32)
+        n = ctypes.c_size_t(0)
+        rc = lib().orc_encode_added(self._h, blob, off.ctypes.data, len(literals), lid.ctypes.data, b, len(b),
+                                    out.ctypes.data, out.size, ctypes.byref(n))
+        if rc == 1:
+            raise UnicodeDecodeError("utf-8", b, 0, len(b), "invalid UTF-8 (oracle)")
+        if rc:
+            raise OracleError(f"encode_added failed (code {rc})")
+        return out[: n.value].copy()

@@ -372,4 +372,52 @@ int orc_encode_batch(void* h, const uint8_t* text, const uint64_t* doc_off, size
   return orc_encode_batch_spans(h, text, doc_off, n_docs, ids, nullptr, cap, out_off);
 }
 
+// Added-token literals (TokTier, section 4 "Single-request path": a
+// leftmost-longest literal pass extracts the added tokens before the
+// tokenizer family handles the remaining segments; GraphTok, section 4
+// "Design": added entries take precedence over pre-tokenization and only the
+// unmatched regions reach it).  Literal i is lit[lit_off[i] .. lit_off[i+1])
+// with ID lit_id[i].  A cursor walks the text byte by byte: where one or more
+// literals match, the longest is taken, its ID emitted and the cursor moved
+// past it; the text between two taken literals is one segment, encoded on its
+// own by encode_one.  Malformed UTF-8 anywhere rejects the whole text.
+int orc_encode_added(void* h, const uint8_t* lit, const uint64_t* lit_off, size_t n_lit, const int32_t* lit_id,
+                     const uint8_t* text, size_t len, int32_t* ids, size_t cap, size_t* n_out) {
+  const Oracle& o = *static_cast<Oracle*>(h);
+  *n_out = 0;
+  {
+    Text t;
+    std::vector<size_t> offs;
+    if (!decode_utf8(text, len, t.cp, offs)) return ORC_UTF8;
+  }
+  std::vector<int32_t> out;
+  size_t seg = 0, p = 0;
+  while (p < len) {
+    size_t best_len = 0;
+    int32_t best_id = 0;
+    for (size_t i = 0; i < n_lit; ++i) {
+      const size_t L = lit_off[i + 1] - lit_off[i];
+      if (L > best_len && p + L <= len && memcmp(text + p, lit + lit_off[i], L) == 0) {
+        best_len = L;
+        best_id = lit_id[i];
+      }
+    }
+    if (best_len == 0) {
+      ++p;
+      continue;
+    }
+    int rc = encode_one(o, text + seg, p - seg, out);
+    if (rc) return rc;
+    out.push_back(best_id);
+    p += best_len;
+    seg = p;
+  }
+  int rc = encode_one(o, text + seg, len - seg, out);
+  if (rc) return rc;
+  *n_out = out.size();
+  if (out.size() > cap) return ORC_CAP;
+  if (!out.empty()) memcpy(ids, out.data(), out.size() * 4);
+  return ORC_OK;
+}
+
 }  // extern "C"
