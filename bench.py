@@ -1,6 +1,6 @@
 """Benchmark: exact encode of one 1,000,000-character request on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_1m|llama3_3m|batch64]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_1m|llama3_3m|batch64|chat_1m|repair]
 
 One step = one tok_encode_dev call over the whole request (pre-tokenization,
 piece pass with merges, count scan + scatter), with the UTF-8 text already
@@ -50,6 +50,9 @@ WORKLOADS = {
                   "llama3", 3, 3_000_000, 1),
     "batch64": ("64 requests x 500K chars, Llama-3-style pattern, 127,744 merges, one batch call",
                 "llama3_128k", "llama3", 40_000, 500_000, 64),
+    # chat transcript with added-token markers taken ahead of the pattern (tok_set_added_tokens)
+    "chat_1m": ("1M-char chat transcript with 5 added-token markers, GPT-2-style pattern, 50K merges",
+                "gpt2_50k", "gpt2", 7, 1_000_000, 1),
     # append repair: stored 1M-char context + 1,400-char appends (a latency, not a bench headline)
     "repair": ("tok_repair: 1M-char stored context + 1,400-char append, GPT-2-style pattern, 50K merges",
                "gpt2_50k", "gpt2", 2, 1_000_000, 1),
@@ -64,6 +67,17 @@ STAGE_KERNELS = {
     "pieces": ("piece_kernel", ["k_bpe.hip", "bpe_util.h", "wg_scan.h", "tok_internal.h"]),
     "assemble": ("assemble_kernel", ["k_assemble.hip", "wg_scan.h", "tok_internal.h"]),
 }
+
+
+CHAT_MARKERS = ["<|im_start|>", "<|im_end|>", "<|endoftext|>", "<|tool_call|>", "<|im_sep|>"]
+
+
+def request_text(workload: str, seed: int, n_chars: int) -> bytes:
+    from synth import textgen
+
+    if workload == "chat_1m":
+        return textgen.chat_text(seed, n_chars, CHAT_MARKERS).encode()
+    return textgen.mix_text(seed, n_chars).encode()
 
 
 def source_digest(stage: str) -> str:
@@ -180,7 +194,7 @@ def main() -> int:
         return bench_repair(args, desc, merges_name, pattern, seed, n_chars)
     t0 = time.time()
     if n_docs == 1:
-        text = textgen.mix_text(seed, n_chars).encode()
+        text = request_text(args.workload, seed, n_chars)
         doc_off = None
     else:
         text, doc_off = textgen.pack_docs(textgen.batch_texts(seed, n_docs, n_chars))
@@ -190,6 +204,10 @@ def main() -> int:
     merges = vocab.merges(merges_name)
     torch.cuda.set_device(0)
     tok = tk.Tokenizer(merges, pattern, device=0)
+    literals = None
+    if args.workload == "chat_1m":
+        literals = [(m.encode(), 256 + len(merges) + i) for i, m in enumerate(CHAT_MARKERS)]
+        tok.set_added_tokens(literals)
     stream = torch.cuda.current_stream()
     d_text = torch.frombuffer(bytearray(text), dtype=torch.uint8).cuda()
     d_ids = torch.empty(n_bytes, dtype=torch.int32, device="cuda")
@@ -275,7 +293,7 @@ def main() -> int:
     fresh = None
     n_fresh = args.fresh if args.fresh >= 0 else (4 if doc_off is None else 0)
     if n_fresh > 0 and doc_off is None:
-        texts = [textgen.mix_text(seed + 1000 * (k + 1), n_chars).encode() for k in range(n_fresh)]
+        texts = [request_text(args.workload, seed + 1000 * (k + 1), n_chars) for k in range(n_fresh)]
         d_texts = [torch.frombuffer(bytearray(t), dtype=torch.uint8).cuda() for t in texts]
         d_fids = torch.empty(max(len(t) for t in texts), dtype=torch.int32, device="cuda")
         torch.cuda.synchronize()
@@ -305,14 +323,16 @@ def main() -> int:
             return tok.encode_spans_dev(d_text, d_ids, d_spans, stream=stream)
         return tok.encode_spans_dev(d_text, d_ids, d_spans, d_off, d_out, stream=stream)
 
-    span_step()
-    sv = []
-    for _ in range(k_ab):
-        s0 = time.perf_counter()
-        assert span_step() == n_tokens
-        sv.append(time.perf_counter() - s0)
-    span_export = {"p50_ms": round(1e3 * statistics.median(sv), 4), "steps": k_ab,
-                   "note": "tok_encode_spans_dev: IDs plus each token's first byte, device-resident"}
+    span_export = None
+    if literals is None:  # span export refuses added-token literals
+        span_step()
+        sv = []
+        for _ in range(k_ab):
+            s0 = time.perf_counter()
+            assert span_step() == n_tokens
+            sv.append(time.perf_counter() - s0)
+        span_export = {"p50_ms": round(1e3 * statistics.median(sv), 4), "steps": k_ab,
+                       "note": "tok_encode_spans_dev: IDs plus each token's first byte, device-resident"}
     del d_spans
     eager_p50 = median_step(k_ab)
     tok.set_graph(True)
@@ -338,7 +358,7 @@ def main() -> int:
         reps, t_cpu = 0, 0.0
         while t_cpu < args.cpu_seconds and reps < 200:
             s0 = time.perf_counter()
-            o.encode(sample)
+            o.encode(sample) if literals is None else o.encode_added(sample, literals)
             t_cpu += time.perf_counter() - s0
             reps += 1
         cpu = {"value": round(len(sample) * reps / t_cpu / 1e6, 3), "unit": "MB/s", "cores": 1,
@@ -358,7 +378,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "u8->int32",
         "data": "synthetic (seeded generator, inputs resident in HBM)",
-        "config": {"workload": desc, "bytes": n_bytes, "chars": n_chars * n_docs, "docs": n_docs,
+        "config": {"workload": desc, "bytes": n_bytes,
+                   "chars": len(text.decode("utf-8")) if doc_off is None else n_chars * n_docs, "docs": n_docs,
                    "tokens": n_tokens, "merges": merges_name, "pattern": pattern, "seed": seed},
         "latency_ms": {"p50": round(1e3 * statistics.median(per_step), 4),
                        "p90": round(1e3 * float(np.percentile(per_step, 90)), 4),

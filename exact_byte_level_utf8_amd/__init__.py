@@ -20,12 +20,13 @@ PATTERNS = {"gpt2": 0, "llama3": 1}
 
 TOK_OK, TOK_E_ARG, TOK_E_BADMERGES, TOK_E_PATTERN, TOK_E_UTF8 = 0, 1, 2, 3, 4
 TOK_E_CAPACITY, TOK_E_TOOLONG, TOK_E_DEVICE, TOK_E_NOMEM, TOK_E_SESSION = 5, 6, 7, 8, 9
+TOK_E_UNSUPPORTED = 10
 
 # every function declared in include/tok.h
 EXPORTS = (
     "tok_load", "tok_free", "tok_strerror", "tok_encode", "tok_encode_dev", "tok_encode_batch",
     "tok_encode_batch_dev", "tok_encode_spans_dev", "tok_encode_spans", "tok_pretokenize_dev", "tok_repair", "tok_sync_boundary", "tok_get_info",
-    "tok_token_lengths", "tok_set_graph", "tok_graph_count", "tok_set_profiling", "tok_stage_ms",
+    "tok_token_lengths", "tok_set_added_tokens", "tok_set_graph", "tok_graph_count", "tok_set_profiling", "tok_stage_ms",
 )
 
 
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
         L.tok_get_info.argtypes = [vp, ctypes.POINTER(TokInfo)]
         L.tok_token_lengths.argtypes = [vp, vp, sz]
         L.tok_token_lengths.restype = sz
+        L.tok_set_added_tokens.argtypes = [vp, vp, vp, sz, vp]
         L.tok_set_graph.argtypes = [vp, i32]
         L.tok_graph_count.argtypes = [vp]
         L.tok_graph_count.restype = sz
@@ -83,7 +85,7 @@ def lib() -> ctypes.CDLL:
         L.tok_stage_ms.argtypes = [vp, vp, i32]
         for name in ("tok_load", "tok_encode", "tok_encode_dev", "tok_encode_batch",
                      "tok_encode_batch_dev", "tok_encode_spans_dev", "tok_encode_spans", "tok_encode_spans_dev", "tok_encode_spans", "tok_pretokenize_dev", "tok_repair", "tok_sync_boundary",
-                     "tok_get_info", "tok_set_graph", "tok_set_profiling", "tok_stage_ms"):
+                     "tok_get_info", "tok_set_added_tokens", "tok_set_graph", "tok_set_profiling", "tok_stage_ms"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -269,6 +271,15 @@ class Tokenizer:
         out = np.zeros(v, dtype=np.uint32)
         lib().tok_token_lengths(self._h, out.ctypes.data, v)
         return out
+
+    def set_added_tokens(self, literals) -> None:
+        """tok_set_added_tokens: literals is a list of (bytes or str, id); [] removes them."""
+        lits = [(x.encode("utf-8") if isinstance(x, str) else bytes(x), int(i)) for x, i in literals]
+        blob = b"".join(x for x, _ in lits)
+        off = np.cumsum([0] + [len(x) for x, _ in lits]).astype(np.uint64)
+        ids = np.asarray([i for _, i in lits] or [0], dtype=np.int32)
+        _check(lib().tok_set_added_tokens(self._h, blob if lits else None, off.ctypes.data if lits else None,
+                                          len(lits), ids.ctypes.data if lits else None), "tok_set_added_tokens")
 
     def set_graph(self, on: bool = True) -> None:
         """Replay a captured HIP graph for call shapes met before (tok_set_graph)."""

@@ -136,6 +136,7 @@ const char* tok_strerror(int code) {
     case TOK_E_DEVICE: return "HIP device error";
     case TOK_E_NOMEM: return "out of memory";
     case TOK_E_SESSION: return "session IDs do not match the old text";
+    case TOK_E_UNSUPPORTED: return "call not supported with added-token literals set";
     default: return "unknown error";
   }
 }
@@ -265,7 +266,8 @@ int tok_encode_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, int32_t* d_i
   if (rc) return rc;
   hipStream_t s = stream ? (hipStream_t)stream : ctx->stream;
   uint32_t total = 0;
-  rc = ctx->run(d_text, len, nullptr, 0, d_ids, nullptr, cap, nullptr, s, true, nullptr, &total);
+  rc = ctx->n_lit ? ctx->run_added(d_text, len, d_ids, cap, s, &total)
+                  : ctx->run(d_text, len, nullptr, 0, d_ids, nullptr, cap, nullptr, s, true, nullptr, &total);
   if (rc) return rc;
   *n_out = total;
   return total > cap ? TOK_E_CAPACITY : TOK_OK;
@@ -283,7 +285,8 @@ int tok_encode(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids, size
   std::memcpy(ctx->h_text, text, len);
   HIP_OK(hipMemcpyAsync(ctx->d_text, ctx->h_text, len, hipMemcpyHostToDevice, s));
   uint32_t total = 0;
-  rc = ctx->run(ctx->d_text, len, nullptr, 0, ctx->d_ids, nullptr, len, nullptr, s, true, nullptr, &total);
+  rc = ctx->n_lit ? ctx->run_added(ctx->d_text, len, ctx->d_ids, len, s, &total)
+                  : ctx->run(ctx->d_text, len, nullptr, 0, ctx->d_ids, nullptr, len, nullptr, s, true, nullptr, &total);
   if (rc) return rc;
   *n_out = total;
   if (total > cap) return TOK_E_CAPACITY;
@@ -299,6 +302,7 @@ int tok_encode_batch_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
   if (!ctx || !n_out || !d_doc_off || !d_out_off || n_docs == 0 || n_docs >= 0xFFFFFFFFu ||
       (!d_text && len) || (!d_ids && cap))
     return TOK_E_ARG;
+  if (ctx->n_lit) return TOK_E_UNSUPPORTED;
   *n_out = 0;
   if (len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
   DeviceGuard g(ctx->device);
@@ -315,6 +319,7 @@ int tok_encode_batch_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
 int tok_encode_batch(tok_ctx* ctx, const uint8_t* text, const uint64_t* doc_off, size_t n_docs,
                      int32_t* ids, size_t cap, uint64_t* out_off) {
   if (!ctx || !doc_off || !out_off || n_docs == 0 || n_docs >= 0xFFFFFFFFu) return TOK_E_ARG;
+  if (ctx->n_lit) return TOK_E_UNSUPPORTED;
   if (doc_off[0] != 0) return TOK_E_ARG;
   for (size_t d = 0; d < n_docs; ++d)
     if (doc_off[d + 1] < doc_off[d]) return TOK_E_ARG;
@@ -353,6 +358,7 @@ int tok_encode_spans_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
   if (!ctx || !n_out || (!d_text && len) || (cap && (!d_ids || !d_spans)) || n_docs >= 0xFFFFFFFFu ||
       (d_doc_off && (n_docs == 0 || !d_out_off)))
     return TOK_E_ARG;
+  if (ctx->n_lit) return TOK_E_UNSUPPORTED;
   *n_out = 0;
   if (len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
   if (len == 0 && !d_doc_off) return TOK_OK;
@@ -371,6 +377,7 @@ int tok_encode_spans_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
 int tok_encode_spans(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids, uint32_t* spans, size_t cap,
                      size_t* n_out) {
   if (!ctx || !n_out || (!text && len) || (cap && (!ids || !spans))) return TOK_E_ARG;
+  if (ctx->n_lit) return TOK_E_UNSUPPORTED;
   *n_out = 0;
   if (len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
   if (len == 0) return TOK_OK;
@@ -407,6 +414,93 @@ int tok_pretokenize_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const u
   hipStream_t s = stream ? (hipStream_t)stream : ctx->stream;
   return ctx->run(d_text, len, d_doc_off, (uint32_t)(d_doc_off ? n_docs : 0), nullptr, nullptr, 0, nullptr, s, true,
                   d_flags, nullptr);
+}
+
+int tok_set_added_tokens(tok_ctx* ctx, const uint8_t* bytes, const uint64_t* off, size_t n, const int32_t* ids) {
+  if (!ctx || (n && (!bytes || !off || !ids)) || n > kLitMaxCount) return TOK_E_ARG;
+  DeviceGuard g(ctx->device);
+  (void)hipStreamSynchronize(ctx->stream);
+  ctx->free_lit_tables();
+  if (n == 0) return TOK_OK;
+  if (off[0] != 0) return TOK_E_ARG;
+  std::vector<std::vector<uint8_t>> lit(n);
+  for (size_t i = 0; i < n; ++i) {
+    if (off[i + 1] <= off[i] || off[i + 1] - off[i] > (uint64_t)kLitMax || ids[i] < 0) return TOK_E_ARG;
+    lit[i].assign(bytes + off[i], bytes + off[i + 1]);
+  }
+  // each literal is whole UTF-8 (so it starts and ends on code-point
+  // boundaries of any valid text), and no string is given twice
+  for (const auto& x : lit) {
+    size_t i = 0;
+    while (i < x.size()) {
+      const uint32_t b0 = x[i];
+      const uint32_t len = b0 < 0x80 ? 1 : (b0 >= 0xC2 && b0 < 0xE0) ? 2 : (b0 >= 0xE0 && b0 < 0xF0) ? 3
+                                                                       : (b0 >= 0xF0 && b0 < 0xF5) ? 4 : 0;
+      if (!len || i + len > x.size()) return TOK_E_UTF8;
+      uint32_t cp = b0 & (0x7Fu >> len);
+      for (uint32_t k = 1; k < len; ++k) {
+        if ((x[i + k] & 0xC0) != 0x80) return TOK_E_UTF8;
+        cp = (cp << 6) | (x[i + k] & 0x3Fu);
+      }
+      if ((len == 3 && (cp < 0x800 || (cp >= 0xD800 && cp < 0xE000))) || (len == 4 && (cp < 0x10000 || cp > 0x10FFFF)))
+        return TOK_E_UTF8;
+      i += len;
+    }
+  }
+  {
+    std::vector<size_t> idx(n);
+    for (size_t i = 0; i < n; ++i) idx[i] = i;
+    std::sort(idx.begin(), idx.end(), [&](size_t a, size_t c) { return lit[a] < lit[c]; });
+    for (size_t i = 1; i < n; ++i)
+      if (lit[idx[i]] == lit[idx[i - 1]]) return TOK_E_ARG;
+  }
+  std::vector<uint32_t> first(8, 0), key2(65536, 0);
+  std::vector<int32_t> key1(256, -1);
+  std::vector<uint16_t> order;
+  std::vector<std::vector<uint16_t>> groups(65536);
+  for (size_t i = 0; i < n; ++i) {
+    const uint32_t b0 = lit[i][0];
+    first[b0 >> 5] |= 1u << (b0 & 31u);
+    if (lit[i].size() == 1) key1[b0] = (int32_t)i;
+    else groups[b0 | ((uint32_t)lit[i][1] << 8)].push_back((uint16_t)i);
+  }
+  for (uint32_t k = 0; k < 65536; ++k) {
+    auto& gk = groups[k];
+    if (gk.empty()) continue;
+    std::sort(gk.begin(), gk.end(), [&](uint16_t a, uint16_t c) { return lit[a].size() > lit[c].size(); });
+    key2[k] = ((uint32_t)order.size() << 16) | (uint32_t)gk.size();
+    order.insert(order.end(), gk.begin(), gk.end());
+  }
+  std::vector<uint8_t> blob;
+  std::vector<uint32_t> loff(n + 1, 0);
+  for (size_t i = 0; i < n; ++i) {
+    blob.insert(blob.end(), lit[i].begin(), lit[i].end());
+    loff[i + 1] = (uint32_t)blob.size();
+  }
+  if (hipMalloc((void**)&ctx->d_lit_bytes, blob.size()) != hipSuccess ||
+      hipMalloc((void**)&ctx->d_lit_off, loff.size() * 4) != hipSuccess ||
+      hipMalloc((void**)&ctx->d_lit_ids, n * 4) != hipSuccess ||
+      hipMalloc((void**)&ctx->d_lit_key2, key2.size() * 4) != hipSuccess ||
+      hipMalloc((void**)&ctx->d_lit_order, std::max<size_t>(order.size(), 1) * 2) != hipSuccess ||
+      hipMalloc((void**)&ctx->d_lit_key1, key1.size() * 4) != hipSuccess ||
+      hipMalloc((void**)&ctx->d_lit_first, first.size() * 4) != hipSuccess) {
+    (void)hipGetLastError();
+    ctx->free_lit_tables();
+    return TOK_E_NOMEM;
+  }
+  if (hipMemcpy(ctx->d_lit_bytes, blob.data(), blob.size(), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(ctx->d_lit_off, loff.data(), loff.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(ctx->d_lit_ids, ids, n * 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(ctx->d_lit_key2, key2.data(), key2.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+      (order.size() && hipMemcpy(ctx->d_lit_order, order.data(), order.size() * 2, hipMemcpyHostToDevice) != hipSuccess) ||
+      hipMemcpy(ctx->d_lit_key1, key1.data(), key1.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(ctx->d_lit_first, first.data(), first.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipGetLastError();
+    ctx->free_lit_tables();
+    return TOK_E_DEVICE;
+  }
+  ctx->n_lit = (uint32_t)n;
+  return TOK_OK;
 }
 
 int tok_get_info(const tok_ctx* ctx, tok_info* info) {

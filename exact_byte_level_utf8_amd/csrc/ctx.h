@@ -104,6 +104,18 @@ struct tok_ctx {
   uint32_t* d_tok_len = nullptr;
   uint2* d_tok_min = nullptr;
 
+  // added-token literals (tok_set_added_tokens); n_lit == 0: none
+  uint32_t n_lit = 0;
+  uint8_t* d_lit_bytes = nullptr;
+  uint32_t* d_lit_off = nullptr;
+  int32_t* d_lit_ids = nullptr;
+  uint32_t* d_lit_key2 = nullptr;
+  uint16_t* d_lit_order = nullptr;
+  int32_t* d_lit_key1 = nullptr;
+  uint32_t* d_lit_first = nullptr;
+  LitBufs lb{};
+  uint64_t lit_cap = 0;  // input bytes lb covers
+
   // scratch, grown on demand
   uint64_t cap = 0;  // input bytes the scratch covers
   Bufs b{};
@@ -165,6 +177,7 @@ struct tok_ctx {
     dfree(b.ws_sym);
     dfree(b.ws_rk);
     dfree(b.ws_sel);
+    free_lit_bufs();
     dfree(d_text);
     dfree(d_ids);
     dfree(d_spans);
@@ -200,6 +213,91 @@ struct tok_ctx {
     }
     b.ctr = d_ctr;
     cap = c;
+    return TOK_OK;
+  }
+
+  void free_lit_tables() {
+    dfree(d_lit_bytes);
+    dfree(d_lit_off);
+    dfree(d_lit_ids);
+    dfree(d_lit_key2);
+    dfree(d_lit_order);
+    dfree(d_lit_key1);
+    dfree(d_lit_first);
+    n_lit = 0;
+  }
+
+  void free_lit_bufs() {
+    dfree(lb.cand);
+    dfree(lb.tile_cnt);
+    dfree(lb.tile_base);
+    dfree(lb.sel);
+    dfree(lb.doc_off);
+    dfree(lb.out_off);
+    dfree(lb.fin);
+    dfree(lb.misc);
+    dfree(lb.ids);
+    lit_cap = 0;
+  }
+
+  Literals literals() const {
+    return Literals{d_lit_bytes, d_lit_off, d_lit_ids, d_lit_key2, d_lit_order, d_lit_key1, d_lit_first, n_lit};
+  }
+
+  // Buffers of the literal pass for the current capacity (after ensure()).
+  int ensure_lit_bufs() {
+    if (lit_cap == cap && lb.cand) return TOK_OK;
+    free_lit_bufs();
+    const uint64_t tiles = cap / kLitTile;
+    if (hipMalloc((void**)&lb.cand, cap * 8) != hipSuccess ||
+        hipMalloc((void**)&lb.tile_cnt, tiles * 4) != hipSuccess ||
+        hipMalloc((void**)&lb.tile_base, tiles * 4) != hipSuccess ||
+        hipMalloc((void**)&lb.sel, cap * 8) != hipSuccess ||
+        hipMalloc((void**)&lb.doc_off, (2 * cap + 2) * 8) != hipSuccess ||
+        hipMalloc((void**)&lb.out_off, (2 * cap + 2) * 8) != hipSuccess ||
+        hipMalloc((void**)&lb.fin, (2 * cap + 2) * 4) != hipSuccess ||
+        hipMalloc((void**)&lb.misc, 16) != hipSuccess ||
+        hipMalloc((void**)&lb.ids, (cap + 64) * 4) != hipSuccess) {
+      (void)hipGetLastError();
+      free_lit_bufs();
+      return TOK_E_NOMEM;
+    }
+    lit_cap = cap;
+    return TOK_OK;
+  }
+
+  // Encode with the added-token literals: the literal pass, one
+  // synchronization to learn how many literals it took, then the pipeline
+  // over the 2k + 1 parts and the insertion of the literal IDs (or, with no
+  // literal in the text, the plain pipeline straight into out).
+  int run_added(const uint8_t* text, uint64_t n, int32_t* out, uint64_t out_cap, hipStream_t s, uint32_t* total) {
+    int rc = ensure_lit_bufs();
+    if (rc) return rc;
+    volatile Counters* c = h_ctr;
+    const uint64_t call = ++gen;
+    launch_literal_pass(text, n, literals(), lb, d_ctr, call, s);
+    HIP_OK(hipGetLastError());
+    HIP_OK(hipStreamSynchronize(s));
+    if (c->lit_done != call) return TOK_E_DEVICE;
+    const uint32_t k = c->lits;
+    if (k == 0) return run(text, n, nullptr, 0, out, nullptr, out_cap, nullptr, s, true, nullptr, total);
+    Bufs bb = b;
+    const uint64_t call2 = bb.gen = ++gen;
+    enqueue(text, n, lb.doc_off, 2 * k + 1, lb.ids, nullptr, n, lb.out_off, s, bb, true, nullptr);
+    launch_literal_insert(n, k, literals(), lb, out, out_cap, d_ctr, call2, s);
+    HIP_OK(hipGetLastError());
+    HIP_OK(hipStreamSynchronize(s));
+    if (prof) {
+      for (int i = 0; i < kStages; ++i) {
+        float ms = 0.f;
+        if (((prof >> i) & 1u) && hipEventElapsedTime(&ms, ev0[i], ev1[i]) != hipSuccess) ms = 0.f;
+        stage_ms[i] = ((prof >> i) & 1u) ? ms : 0.f;
+      }
+    }
+    if (c->err_docs == call2) return TOK_E_DEVICE;  // the parts are well formed by construction
+    if (c->err_utf8 == call2) return TOK_E_UTF8;
+    if (c->done != call2 || c->ins_done != call2) return TOK_E_DEVICE;
+    *total = c->total;
     return TOK_OK;
   }
 
@@ -375,6 +473,7 @@ struct tok_ctx {
     dfree(d_long_slots);
     dfree(d_tok_len);
     dfree(d_tok_min);
+    free_lit_tables();
     dfree(d_doc);
     dfree(d_outoff);
     hfree(h_doc);

@@ -1,0 +1,202 @@
+// Added-token literals: a leftmost-longest literal pass ahead of the pattern
+// (TokTier, section 4 "Single-request path": added and special tokens are
+// literal strings reserved as single IDs, extracted by a leftmost-longest pass
+// before the tokenizer family handles the remaining segments; GraphTok,
+// section 4 "Design": a device lookup first finds the literals, emits their
+// IDs directly and passes only the unmatched regions to the family predicate).
+//
+//   lit_match_kernel   one 1 KiB tile per workgroup: at every byte, the
+//                      longest literal that starts there (a 256-bit first-byte
+//                      mask rejects most bytes at once; candidates of two or
+//                      more bytes are grouped by their first two bytes, longest
+//                      first); each tile writes its matches in position order.
+//   lit_select_kernel  one workgroup: the matches of all tiles in order; when
+//                      no match overlaps the next one every match is taken,
+//                      else one lane keeps, in order, each match that starts at
+//                      or after the end of the last one kept (the cursor scan
+//                      of the definition, over the matches only).  The taken
+//                      literals cut the text into 2k + 1 parts: segment,
+//                      literal, segment, ..., segment.
+// The parts then run through the usual pipeline as documents, which are hard
+// boundaries for code points, pieces and merges, exactly as the segments
+// between literals must be.  Then:
+//   lit_insert_kernel  one workgroup: output offsets of the parts, where a
+//                      literal part counts one ID; writes the literal IDs.
+//   lit_scatter_kernel every ID of a segment part to its final place; the IDs
+//                      the pipeline made from a literal's own bytes are dropped.
+#include "tok_internal.h"
+#include "wg_scan.h"
+
+namespace tok {
+namespace {
+
+constexpr uint32_t kMatchThreads = 256;  // 4 consecutive positions per thread
+constexpr uint32_t kSelThreads = 1024;
+constexpr uint32_t kScatterThreads = 256;
+
+__device__ inline uint32_t lit_len(const Literals& L, uint32_t li) { return L.off[li + 1] - L.off[li]; }
+
+// The longest literal that starts at byte p of text[0, n), or -1.
+__device__ inline int32_t literal_at(const uint8_t* __restrict__ text, uint64_t n, uint64_t p, const Literals& L) {
+  const uint32_t b0 = text[p];
+  if (!((L.first[b0 >> 5] >> (b0 & 31u)) & 1u)) return -1;
+  if (p + 1 < n) {
+    const uint32_t e = L.key2[b0 | ((uint32_t)text[p + 1] << 8)];
+    const uint32_t start = e >> 16, cnt = e & 0xFFFFu;
+    for (uint32_t c = 0; c < cnt; ++c) {  // longest first: the first full match is the longest
+      const uint32_t li = L.order[start + c];
+      const uint32_t a = L.off[li], len = L.off[li + 1] - a;
+      if (p + len > n) continue;
+      uint32_t k = 2;
+      while (k < len && text[p + k] == L.bytes[a + k]) ++k;
+      if (k == len) return (int32_t)li;
+    }
+  }
+  return L.key1[b0];
+}
+
+__global__ void __launch_bounds__(kMatchThreads)
+lit_match_kernel(const uint8_t* __restrict__ text, uint64_t n, Literals L, LitBufs lb) {
+  __shared__ uint32_t s_scan[kMatchThreads / kWave];
+  const uint32_t tile = blockIdx.x, tid = threadIdx.x;
+  const uint64_t p0 = (uint64_t)tile * kLitTile + 4u * tid;
+  int32_t m[4];
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m[j] = p0 + j < n ? literal_at(text, n, p0 + j, L) : -1;
+    c += m[j] >= 0 ? 1u : 0u;
+  }
+  uint32_t tot = 0;
+  uint32_t at = wg_excl_scan<kMatchThreads>(c, 0u, AddOp(), s_scan, &tot);
+  uint64_t* out = lb.cand + (uint64_t)tile * kLitTile;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (m[j] >= 0) out[at++] = ((p0 + j) << 32) | (uint32_t)m[j];
+  if (tid == 0) lb.tile_cnt[tile] = tot;
+}
+
+__global__ void __launch_bounds__(kSelThreads)
+lit_select_kernel(uint64_t n, uint32_t tiles, Literals L, LitBufs lb, Counters* ctr, uint64_t gen) {
+  __shared__ uint32_t s_scan[kSelThreads / kWave];
+  __shared__ uint32_t s_over, s_kept;
+  const uint32_t tid = threadIdx.x;
+  if (tid == 0) s_over = 0;
+  // matches before each tile (uniform trip count: the scan holds barriers)
+  uint32_t carry = 0;
+  for (uint32_t t0 = 0; t0 < tiles; t0 += kSelThreads) {
+    const uint32_t t = t0 + tid;
+    const uint32_t v = t < tiles ? lb.tile_cnt[t] : 0u;
+    uint32_t tot = 0;
+    const uint32_t ex = wg_excl_scan<kSelThreads>(v, 0u, AddOp(), s_scan, &tot);
+    if (t < tiles) lb.tile_base[t] = carry + ex;
+    carry += tot;
+  }
+  const uint32_t K = carry;
+  __syncthreads();
+  for (uint32_t t = tid; t < tiles; t += kSelThreads) {
+    const uint32_t c = lb.tile_cnt[t], b = lb.tile_base[t];
+    for (uint32_t j = 0; j < c; ++j) lb.sel[b + j] = lb.cand[(uint64_t)t * kLitTile + j];
+  }
+  __syncthreads();
+  bool over = false;
+  for (uint32_t i = tid; i + 1 < K; i += kSelThreads) {
+    const uint64_t a = lb.sel[i], b = lb.sel[i + 1];
+    over |= (a >> 32) + lit_len(L, (uint32_t)a) > (b >> 32);
+  }
+  if (over) s_over = 1u;
+  __syncthreads();
+  uint32_t k = K;
+  if (s_over) {  // uniform: an LDS word read after a barrier
+    if (tid == 0) {
+      uint64_t end = 0;
+      uint32_t w = 0;
+      for (uint32_t i = 0; i < K; ++i) {
+        const uint64_t a = lb.sel[i];
+        if ((a >> 32) >= end) {
+          lb.sel[w++] = a;
+          end = (a >> 32) + lit_len(L, (uint32_t)a);
+        }
+      }
+      s_kept = w;
+    }
+    __syncthreads();
+    k = s_kept;
+  }
+  for (uint32_t i = tid; i < k; i += kSelThreads) {
+    const uint64_t a = lb.sel[i];
+    lb.doc_off[2 * i + 1] = a >> 32;
+    lb.doc_off[2 * i + 2] = (a >> 32) + lit_len(L, (uint32_t)a);
+  }
+  if (tid == 0) {
+    lb.doc_off[0] = 0;
+    lb.doc_off[2 * (uint64_t)k + 1] = n;
+    lb.misc[1] = k;
+    ctr->lits = k;
+    __threadfence_system();
+    report(&ctr->lit_done, gen);
+  }
+}
+
+__global__ void __launch_bounds__(kSelThreads)
+lit_insert_kernel(Literals L, LitBufs lb, uint32_t k, int32_t* __restrict__ out, uint64_t cap, Counters* ctr,
+                  uint64_t gen) {
+  __shared__ uint32_t s_scan[kSelThreads / kWave];
+  const uint32_t tid = threadIdx.x, parts = 2 * k + 1;
+  uint32_t carry = 0;
+  for (uint32_t i0 = 0; i0 < parts; i0 += kSelThreads) {
+    const uint32_t i = i0 + tid;
+    uint32_t v = 0;
+    if (i < parts) v = (i & 1u) ? 1u : (uint32_t)(lb.out_off[i + 1] - lb.out_off[i]);
+    uint32_t tot = 0;
+    const uint32_t ex = wg_excl_scan<kSelThreads>(v, 0u, AddOp(), s_scan, &tot);
+    if (i < parts) {
+      const uint32_t at = carry + ex;
+      lb.fin[i] = at;
+      if ((i & 1u) && at < cap) out[at] = L.ids[(uint32_t)lb.sel[i >> 1]];
+    }
+    carry += tot;
+  }
+  if (tid == 0) {
+    lb.misc[0] = (uint32_t)lb.out_off[parts];
+    ctr->total = carry;
+    __threadfence_system();
+    report(&ctr->ins_done, gen);
+  }
+}
+
+__global__ void __launch_bounds__(kScatterThreads)
+lit_scatter_kernel(LitBufs lb, uint32_t k, int32_t* __restrict__ out, uint64_t cap) {
+  const uint32_t parts = 2 * k + 1;
+  const uint32_t T = lb.misc[0];
+  for (uint32_t t = blockIdx.x * kScatterThreads + threadIdx.x; t < T; t += gridDim.x * kScatterThreads) {
+    // the part holding pipeline token t: the last i with out_off[i] <= t
+    uint32_t lo = 0, hi = parts - 1;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi + 1) >> 1;
+      if (lb.out_off[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    if (lo & 1u) continue;  // made from a literal's own bytes: replaced by its ID
+    const uint64_t at = (uint64_t)lb.fin[lo] + (t - (uint32_t)lb.out_off[lo]);
+    if (at < cap) out[at] = lb.ids[t];
+  }
+}
+
+}  // namespace
+
+void launch_literal_pass(const uint8_t* text, uint64_t n, Literals L, LitBufs lb, Counters* ctr, uint64_t gen,
+                         hipStream_t s) {
+  const uint32_t tiles = (uint32_t)((n + kLitTile - 1) / kLitTile);
+  lit_match_kernel<<<tiles, kMatchThreads, 0, s>>>(text, n, L, lb);
+  lit_select_kernel<<<1, kSelThreads, 0, s>>>(n, tiles, L, lb, ctr, gen);
+}
+
+void launch_literal_insert(uint64_t n, uint32_t k, Literals L, LitBufs lb, int32_t* out, uint64_t cap,
+                           Counters* ctr, uint64_t gen, hipStream_t s) {
+  lit_insert_kernel<<<1, kSelThreads, 0, s>>>(L, lb, k, out, cap, ctr, gen);
+  const uint32_t blocks = (uint32_t)std::min<uint64_t>((n + kScatterThreads - 1) / kScatterThreads, 8192);
+  lit_scatter_kernel<<<blocks, kScatterThreads, 0, s>>>(lb, k, out, cap);
+}
+
+}  // namespace tok

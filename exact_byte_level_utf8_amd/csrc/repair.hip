@@ -143,6 +143,10 @@ int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap,
   inf = tok_repair_info{};
   if (new_len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
   if ((old_len == 0) != (n_session == 0)) return TOK_E_SESSION;
+  if (ctx->n_lit) {  // the splice certificate knows nothing of literals: encode the whole text
+    inf.full = 1;
+    return tok_encode(ctx, text, new_len, session_ids, cap, n_out);
+  }
   if (new_len == old_len) {  // nothing appended: the stored IDs are the answer
     *n_out = n_session;
     inf.kept = n_session;

@@ -50,7 +50,9 @@ struct Counters {
   uint64_t err_docs;  // gen of the last call whose document offsets were invalid
   uint64_t done;      // gen of the last call whose assembly finished
   uint32_t total;     // tokens in the output of that call
-  uint32_t reserved;
+  uint32_t lits;      // added-token literals taken by the last literal pass
+  uint64_t lit_done;  // gen of the last call whose literal selection finished
+  uint64_t ins_done;  // gen of the last call whose literal insertion finished
 };
 
 // Store a call number into the host-visible counters.
@@ -132,8 +134,41 @@ inline void launch_on(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
   if (e1) (void)hipEventRecord(e1, s);
 }
 
+// Device tables of the added-token literals (set by tok_set_added_tokens).
+struct Literals {
+  const uint8_t* bytes;   // literal i is bytes[off[i] .. off[i + 1])
+  const uint32_t* off;
+  const int32_t* ids;
+  const uint32_t* key2;   // [65536] by first two bytes: (first << 16 | count) into order, longest first
+  const uint16_t* order;  // literal indices of two or more bytes, grouped by key2
+  const int32_t* key1;    // [256] the one-byte literal of each byte, or -1
+  const uint32_t* first;  // [8] bit b: some literal starts with byte b
+  uint32_t n;
+};
+
+// Per-call buffers of the literal pass (sized by the context's capacity).
+struct LitBufs {
+  uint64_t* cand;       // per tile: up to kLitTile (position << 32 | literal) in position order
+  uint32_t* tile_cnt;   // candidates found in each tile
+  uint32_t* tile_base;  // candidates before each tile
+  uint64_t* sel;        // taken literals, in order
+  uint64_t* doc_off;    // 2k + 2 offsets: segment, literal, segment, ..., segment
+  uint64_t* out_off;    // their output offsets from the pipeline
+  uint32_t* fin;        // final output offset of each of those 2k + 1 parts
+  uint32_t* misc;       // [0]: tokens the pipeline produced, [1]: literals taken
+  int32_t* ids;         // the pipeline's output, before the literal IDs go in
+};
+
+constexpr int kLitTile = 1024;  // bytes per workgroup of the literal match
+constexpr int kLitMax = 64;     // longest added-token literal, bytes
+constexpr uint32_t kLitMaxCount = 4096;
+
 // Kernel launchers (defined in the .hip files); e0 / e1: optional events
 // around the stage's kernel.
+void launch_literal_pass(const uint8_t* text, uint64_t n, Literals L, LitBufs lb, Counters* ctr, uint64_t gen,
+                         hipStream_t s);
+void launch_literal_insert(uint64_t n, uint32_t k, Literals L, LitBufs lb, int32_t* out, uint64_t cap,
+                           Counters* ctr, uint64_t gen, hipStream_t s);
 void launch_empty_batch(Bufs b, const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s);
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
                    int pattern, Bufs b, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);

@@ -60,6 +60,7 @@ typedef struct tok_ctx tok_ctx;
 #define TOK_E_DEVICE 7     /* a HIP runtime call failed                     */
 #define TOK_E_NOMEM 8      /* device or pinned host allocation failed       */
 #define TOK_E_SESSION 9    /* repair: stored IDs do not spell the old text  */
+#define TOK_E_UNSUPPORTED 10 /* call not supported with added-token literals */
 
 /* Pre-tokenizer families. */
 #define TOK_PAT_GPT2 0   /* 's|'t|'re|'ve|'m|'ll|'d| ?L+| ?N+| ?[^\s L N]+|\s+(?!\S)|\s+ */
@@ -253,6 +254,37 @@ int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap,
  * Appendix A).  No context needed; never touches the device.
  */
 int tok_sync_boundary(int pattern, uint32_t prev_cp, uint32_t cp);
+
+/*
+ * tok_set_added_tokens -- added-token literals (special tokens such as
+ * "<|endoftext|>") that take precedence over the pattern (TokTier, section 4
+ * "Single-request path": a leftmost-longest literal pass extracts added and
+ * special tokens before the tokenizer family handles the remaining segments;
+ * GraphTok, section 4 "Design": added entries take precedence over ordinary
+ * pre-tokenization, their IDs are emitted directly and only the unmatched
+ * regions reach the family predicate).
+ *
+ * Literal i is bytes[off[i] .. off[i+1]) (off: n + 1 non-decreasing host
+ * offsets, off[0] = 0) with token ID ids[i] >= 0 (any value; usually at or
+ * above the vocabulary size).  Each literal is 1..64 bytes of well-formed
+ * UTF-8; no string twice; n <= 4096.  n = 0 removes the literals.
+ *
+ * Afterwards tok_encode and tok_encode_dev scan the text left to right: at the
+ * first position where some literal matches, the longest one there is taken
+ * and its ID emitted, and the scan goes on after it; each segment between
+ * taken literals is encoded as a request of its own (its pieces and merges
+ * never reach across a literal).  Literals are matched on the raw bytes, with
+ * no whitespace stripping, word-boundary or normalization options.  The cost
+ * is one more synchronization per call (the literal pass reports how many
+ * literals it took).  tok_repair then always encodes the whole text (its
+ * splice certificate does not cover literals).  The batch and span calls
+ * return TOK_E_UNSUPPORTED while literals are set.
+ *
+ * Errors: TOK_E_ARG (null pointers, a length of 0 or over 64, a negative ID, a
+ * repeated string, n > 4096), TOK_E_UTF8 (a literal is not well-formed UTF-8),
+ * TOK_E_NOMEM, TOK_E_DEVICE.  On error no literals are set.
+ */
+int tok_set_added_tokens(tok_ctx* ctx, const uint8_t* bytes, const uint64_t* off, size_t n, const int32_t* ids);
 
 /* Context facts. */
 typedef struct tok_info {

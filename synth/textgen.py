@@ -375,6 +375,26 @@ def prose_text(seed: int, n_chars: int) -> str:
     return "".join(parts)[:n_chars]
 
 
+def chat_text(seed: int, n_chars: int, markers: list[str]) -> str:
+    """Chat-transcript shape of about ``n_chars`` characters: turns of the mix
+    wrapped in the given marker strings, chosen by the seed (turn open, role
+    line, body, turn close).  The markers are whatever literal strings the
+    caller wants to find in the text; nothing here knows what they mean."""
+    g = _MixGen(seed)
+    roles = ["system", "user", "assistant", "tool"]
+    parts: list[str] = []
+    total = 0
+    while total < n_chars:
+        u = g.s.u()
+        kind = "prose" if u < 0.4 else ("code" if u < 0.8 else "json")
+        open_m = markers[g.s.randint(0, len(markers) - 1)]
+        close_m = markers[g.s.randint(0, len(markers) - 1)]
+        t = open_m + roles[g.s.randint(0, 3)] + "\n" + g.block(kind) + close_m + ("\n" if g.s.u() < 0.7 else "")
+        parts.append(t)
+        total += len(t)
+    return "".join(parts)
+
+
 # ----------------------------------------------------------------- workloads
 
 def batch_texts(base_seed: int, n_docs: int, n_chars: int) -> list[str]:

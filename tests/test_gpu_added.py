@@ -1,0 +1,202 @@
+"""GPU parity of the added-token literal pass (tok_set_added_tokens, then
+tok_encode / tok_encode_dev) against the oracle's literal pass, bit-exact.
+
+Covers chat-transcript text with marker literals on both pattern families at
+the 1M-character size, literals that also occur inside ordinary code (many
+matches per tile), overlapping literal sets (the selection's ordered path),
+literals at the text's ends, back to back and across 1 KiB tiles, a 64-byte
+literal, one-byte and multibyte literals, text without any occurrence,
+capacity overflow, malformed UTF-8, invalid literal sets, removal, the calls
+that refuse literals, and the hand-worked cases of
+tests/golden/added_tokens.json (tiny merge tables, run last).
+"""
+import json
+import os
+import random
+
+import numpy as np
+import pytest
+
+import exact_byte_level_utf8_amd as tk
+import oracle
+from synth import textgen
+from tests import libs, vocab
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+MARKERS = ["<|im_start|>", "<|im_end|>", "<|endoftext|>", "<|tool_call|>", "<|im_sep|>"]
+
+
+@pytest.fixture(scope="module")
+def cfg():
+    libs.ensure_built()
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    out = {}
+    for name, (merges_name, pattern) in libs.CONFIGS.items():
+        m = vocab.merges(merges_name)
+        out[name] = (tk.Tokenizer(m, pattern), oracle.Oracle(m, pattern), len(m) + 256)
+    return out
+
+
+def lits_from(strings, base):
+    return [(s.encode() if isinstance(s, str) else s, base + i) for i, s in enumerate(strings)]
+
+
+def dev_encode(t, b: bytes, cap=None):
+    d = torch.frombuffer(bytearray(b), dtype=torch.uint8).cuda() if b else torch.empty(0, dtype=torch.uint8,
+                                                                                     device="cuda")
+    ids = torch.full((max(len(b), 1) if cap is None else cap,), -7, dtype=torch.int32, device="cuda")
+    n = t.encode_dev(d, ids)
+    torch.cuda.synchronize()
+    return ids[:n].cpu().numpy()
+
+
+def same(what, got, want):
+    got, want = np.asarray(got), np.asarray(want)
+    if got.shape != want.shape or not np.array_equal(got, want):
+        n = min(len(got), len(want))
+        i = next((k for k in range(n) if got[k] != want[k]), n)
+        pytest.fail(f"{what}: {len(got)} vs {len(want)} IDs, first difference at {i}: "
+                    f"gpu {got[i:i + 6].tolist()} oracle {want[i:i + 6].tolist()}")
+
+
+def check(t, o, b, lits, what):
+    want = o.encode_added(b, lits)
+    same(f"{what} host", t.encode(b), want)
+    same(f"{what} dev", dev_encode(t, b), want)
+    return want
+
+
+@pytest.mark.parametrize("name,seed,n_chars", [("gpt2", 7, 1_000_000), ("llama3", 8, 1_000_000),
+                                               ("tiny", 9, 20_000)])
+def test_chat_workload(cfg, name, seed, n_chars):
+    t, o, v = cfg[name]
+    lits = lits_from(MARKERS, v)
+    b = textgen.chat_text(seed, n_chars, MARKERS).encode()
+    t.set_added_tokens(lits)
+    try:
+        want = check(t, o, b, lits, name)
+        assert sum(1 for i in want if i >= v) > n_chars // 2000
+    finally:
+        t.set_added_tokens([])
+    same(f"{name} cleared", t.encode(b), o.encode(b))
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_literals_inside_code(cfg, name):
+    """Literals that the code blocks contain all the time (operators, a
+    keyword, a multibyte letter): thousands of matches, many per tile."""
+    t, o, v = cfg[name]
+    lits = lits_from(["=>", "==", "return", "->", "é", "self.", "\n    "], v)
+    b = textgen.mix_text(17, 300_000).encode()
+    t.set_added_tokens(lits)
+    try:
+        check(t, o, b, lits, name)
+    finally:
+        t.set_added_tokens([])
+
+
+def test_overlapping_literals(cfg):
+    t, o, v = cfg["gpt2"]
+    rng = random.Random(5)
+    sets = [["ab", "ba", "aba", "bab"], ["aa", "aaa"], ["a b", " b ", "b a"], ["<|", "|>", "<|x|>", "|x"]]
+    for strings in sets:
+        lits = lits_from(strings, v)
+        t.set_added_tokens(lits)
+        try:
+            alpha = sorted(set("".join(strings))) + ["x", "\n"]
+            for k in range(3):
+                b = "".join(rng.choice(alpha) for _ in range(20_000)).encode()
+                check(t, o, b, lits, f"{strings} #{k}")
+            check(t, o, (strings[0] * 30_000).encode(), lits, f"{strings} run")
+        finally:
+            t.set_added_tokens([])
+
+
+def test_edges(cfg):
+    t, o, v = cfg["llama3"]
+    long_lit = "<|" + "x" * 60 + "|>"
+    assert len(long_lit) == 64
+    strings = ["<|eot|>", "<|e", "§", "中文", "😀", long_lit, "\r\n"]
+    lits = lits_from(strings, v)
+    filler = textgen.mix_text(3, 5000)
+    cases = ["", "<|eot|>", "<|eot|><|eot|>", "<|eot|>abc", "abc<|eot|>", "§§§", "a§b", "中文中文x", "😀 😀",
+             long_lit, long_lit[:-1], "x" + long_lit + "y", "it's\r\n\r\n ok", "<|e<|eot|>",
+             filler[:1020] + "<|eot|>" + filler[1020:3000],        # a literal across the 1 KiB tile edge
+             filler[:1023] + "§" + filler[1023:2100] + long_lit,   # a 2-byte literal at the edge
+             filler + "<|eot|>" * 300]
+    t.set_added_tokens(lits)
+    try:
+        for s in cases:
+            check(t, o, s.encode(), lits, repr(s[:30]))
+        with pytest.raises(tk.TokError) as e:
+            t.encode(b"ok <|eot|> \xff")
+        assert e.value.code == tk.TOK_E_UTF8
+        # capacity: the count comes back, the first cap IDs are right
+        b = (filler[:2000] + "<|eot|>").encode()
+        want = o.encode_added(b, lits)
+        cap = len(want) - 3
+        d = torch.frombuffer(bytearray(b), dtype=torch.uint8).cuda()
+        ids = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+        with pytest.raises(tk.TokError) as e:
+            t.encode_dev(d, ids)
+        assert e.value.code == tk.TOK_E_CAPACITY
+        torch.cuda.synchronize()
+        same("first cap IDs", ids.cpu().numpy(), want[:cap])
+    finally:
+        t.set_added_tokens([])
+
+
+def test_no_occurrence_and_refusals(cfg):
+    t, o, v = cfg["gpt2"]
+    b = textgen.mix_text(21, 200_000).encode()
+    lits = lits_from(["<|endoftext|>"], v)
+    t.set_added_tokens(lits)
+    try:
+        same("no occurrence", dev_encode(t, b), o.encode(b))
+        data, off = textgen.pack_docs(["a<|endoftext|>", "b"])
+        with pytest.raises(tk.TokError) as e:
+            t.encode_batch(data, off)
+        assert e.value.code == tk.TOK_E_UNSUPPORTED
+        with pytest.raises(tk.TokError) as e:
+            t.encode_spans(b"a<|endoftext|>")
+        assert e.value.code == tk.TOK_E_UNSUPPORTED
+        # repair encodes the whole text and still equals the literal pass
+        old = textgen.mix_text(22, 20_000) + "<|endoftext|>"
+        new = old + "<|endoftext|> and more"
+        sess = t.encode(old.encode())
+        same("session", sess, o.encode_added(old.encode(), lits))
+        ids, info = t.repair(sess, new.encode(), len(old.encode()))
+        assert info["full"] == 1
+        same("repair", ids, o.encode_added(new.encode(), lits))
+    finally:
+        t.set_added_tokens([])
+    same("cleared", t.encode(b"a<|endoftext|>"), o.encode(b"a<|endoftext|>"))
+
+
+def test_invalid_literal_sets(cfg):
+    t, o, v = cfg["gpt2"]
+    for bad, code in [([(b"", 1)], tk.TOK_E_ARG), ([(b"x" * 65, 1)], tk.TOK_E_ARG), ([(b"ab", -1)], tk.TOK_E_ARG),
+                      ([(b"ab", 1), (b"ab", 2)], tk.TOK_E_ARG), ([(b"\xff", 1)], tk.TOK_E_UTF8),
+                      ([(b"\xe4\xb8", 1)], tk.TOK_E_UTF8), ([(b"\xed\xa0\x80", 1)], tk.TOK_E_UTF8)]:
+        with pytest.raises(tk.TokError) as e:
+            t.set_added_tokens(bad)
+        assert e.value.code == code, bad
+    same("nothing set", t.encode(b"ab"), o.encode(b"ab"))
+
+
+def test_hand_worked_cases():
+    libs.ensure_built()
+    cases = json.load(open(os.path.join(HERE, "golden", "added_tokens.json")))["cases"]
+    for c in cases:
+        m = np.asarray(c["merges"], dtype=np.uint32).reshape(-1, 2)
+        t = tk.Tokenizer(m, c["pattern"])
+        t.set_added_tokens([(s, i) for s, i in c["literals"]])
+        b = c["text"].encode()
+        assert t.encode(b).tolist() == c["ids"], c["why"]
+        if b:
+            assert dev_encode(t, b).tolist() == c["ids"], c["why"]
+        t.close()
