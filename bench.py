@@ -135,18 +135,25 @@ def bench_repair(args, desc, merges_name, pattern, seed, n_chars) -> int:
     torch.cuda.set_device(0)
     tok = tk.Tokenizer(vocab.merges(merges_name), pattern, device=0)
     base = textgen.mix_text(seed, n_chars)
-    lat, full, widen = [], 0, 0
+    lat, dlat, full, widen = [], [], 0, 0
     for i in range(args.warmup + args.steps):
         old, suf = textgen.repair_case(seed, 70_000 + i, old_text=base, append_chars=1_400)
         ob, text = old.encode(), (old + suf).encode()
         sess = tok.encode(ob)
         buf = np.zeros(sess.size + len(text) - len(ob) + 64, dtype=np.int32)
         buf[: sess.size] = sess
+        d_sess = torch.from_numpy(buf).cuda()  # the same session, kept on the device
+        torch.cuda.synchronize()
         s0 = time.perf_counter()
         n, info = tok.repair_into(buf, sess.size, text, len(ob))
         dt = time.perf_counter() - s0
+        s0 = time.perf_counter()
+        dn, dinfo = tok.repair_dev(d_sess, sess.size, text, len(ob))
+        ddt = time.perf_counter() - s0
+        assert dn == n and dinfo == info
         if i >= args.warmup:
             lat.append(dt)
+            dlat.append(ddt)
             full += info["full"]
             widen += info["widenings"]
     p50 = statistics.median(lat)
@@ -154,6 +161,9 @@ def bench_repair(args, desc, merges_name, pattern, seed, n_chars) -> int:
            "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
            "latency_ms": {"p50": round(1e3 * p50, 4), "p90": round(1e3 * float(np.percentile(lat, 90)), 4),
                           "p99": round(1e3 * float(np.percentile(lat, 99)), 4)},
+           "device_session_ms": {"p50": round(1e3 * statistics.median(dlat), 4),
+                                 "p90": round(1e3 * float(np.percentile(dlat, 90)), 4),
+                                 "note": "tok_repair_dev: session IDs in device memory, match and splice on the device"},
            "full_encodes": full, "widenings": widen, "dtype": "u8->int32",
            "data": "synthetic (seeded generator; host text and IDs)",
            "config": {"workload": desc, "context_chars": n_chars, "append_chars": 1400, "merges": merges_name,

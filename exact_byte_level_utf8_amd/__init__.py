@@ -25,7 +25,8 @@ TOK_E_UNSUPPORTED = 10
 # every function declared in include/tok.h
 EXPORTS = (
     "tok_load", "tok_free", "tok_strerror", "tok_encode", "tok_encode_dev", "tok_encode_batch",
-    "tok_encode_batch_dev", "tok_encode_spans_dev", "tok_encode_spans", "tok_pretokenize_dev", "tok_repair", "tok_sync_boundary", "tok_get_info",
+    "tok_encode_batch_dev", "tok_encode_spans_dev", "tok_encode_spans", "tok_pretokenize_dev", "tok_repair",
+    "tok_repair_dev", "tok_sync_boundary", "tok_get_info",
     "tok_token_lengths", "tok_set_added_tokens", "tok_set_graph", "tok_graph_count", "tok_set_profiling", "tok_stage_ms",
 )
 
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.tok_encode_spans.argtypes = [vp, vp, sz, vp, vp, sz, szp]
         L.tok_pretokenize_dev.argtypes = [vp, vp, sz, vp, sz, vp, vp]
         L.tok_repair.argtypes = [vp, vp, sz, sz, vp, sz, sz, szp, ctypes.POINTER(RepairInfo)]
+        L.tok_repair_dev.argtypes = [vp, vp, sz, sz, vp, sz, sz, szp, ctypes.POINTER(RepairInfo)]
         L.tok_sync_boundary.argtypes = [i32, ctypes.c_uint32, ctypes.c_uint32]
         L.tok_get_info.argtypes = [vp, ctypes.POINTER(TokInfo)]
         L.tok_token_lengths.argtypes = [vp, vp, sz]
@@ -83,9 +85,10 @@ def lib() -> ctypes.CDLL:
         L.tok_graph_count.restype = sz
         L.tok_set_profiling.argtypes = [vp, i32]
         L.tok_stage_ms.argtypes = [vp, vp, i32]
-        for name in ("tok_load", "tok_encode", "tok_encode_dev", "tok_encode_batch",
-                     "tok_encode_batch_dev", "tok_encode_spans_dev", "tok_encode_spans", "tok_encode_spans_dev", "tok_encode_spans", "tok_pretokenize_dev", "tok_repair", "tok_sync_boundary",
-                     "tok_get_info", "tok_set_added_tokens", "tok_set_graph", "tok_set_profiling", "tok_stage_ms"):
+        for name in ("tok_load", "tok_encode", "tok_encode_dev", "tok_encode_batch", "tok_encode_batch_dev",
+                     "tok_encode_spans_dev", "tok_encode_spans", "tok_pretokenize_dev", "tok_repair",
+                     "tok_repair_dev", "tok_sync_boundary", "tok_get_info", "tok_set_added_tokens",
+                     "tok_set_graph", "tok_set_profiling", "tok_stage_ms"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -213,6 +216,17 @@ class Tokenizer:
         info = RepairInfo()
         _check(lib().tok_repair(self._h, buf.ctypes.data, n_session, buf.size, text, old_len, len(text),
                                 ctypes.byref(n), ctypes.byref(info)), "tok_repair")
+        return n.value, {f: getattr(info, f) for f, _ in RepairInfo._fields_}
+
+    def repair_dev(self, d_session, n_session: int, text: bytes, old_len: int) -> tuple[int, dict]:
+        """tok_repair_dev: d_session (int32 device tensor, its size is the capacity) holds the IDs of
+        text[:old_len] in its first n_session entries; on return the first n hold the IDs of text.
+        Returns (n, info)."""
+        n = ctypes.c_size_t(0)
+        info = RepairInfo()
+        _check(lib().tok_repair_dev(self._h, _dev_ptr(d_session, "int32", "session"), n_session,
+                                    d_session.numel(), text, old_len, len(text), ctypes.byref(n),
+                                    ctypes.byref(info)), "tok_repair_dev")
         return n.value, {f: getattr(info, f) for f, _ in RepairInfo._fields_}
 
     # --------------------------------------------------------- device memory

@@ -104,6 +104,10 @@ struct tok_ctx {
   uint32_t* d_tok_len = nullptr;
   uint2* d_tok_min = nullptr;
 
+  // every token's bytes on the device, made on first use (device repair)
+  uint8_t* d_tok_bytes = nullptr;
+  uint64_t* d_tok_off = nullptr;
+
   // added-token literals (tok_set_added_tokens); n_lit == 0: none
   uint32_t n_lit = 0;
   uint8_t* d_lit_bytes = nullptr;
@@ -301,6 +305,25 @@ struct tok_ctx {
     return TOK_OK;
   }
 
+  int ensure_tok_bytes() {
+    if (d_tok_bytes) return TOK_OK;
+    if (hipMalloc((void**)&d_tok_bytes, tok_bytes.size() + 64) != hipSuccess ||
+        hipMalloc((void**)&d_tok_off, tok_off.size() * 8) != hipSuccess) {
+      (void)hipGetLastError();
+      dfree(d_tok_bytes);
+      dfree(d_tok_off);
+      return TOK_E_NOMEM;
+    }
+    if (hipMemcpy(d_tok_bytes, tok_bytes.data(), tok_bytes.size(), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(d_tok_off, tok_off.data(), tok_off.size() * 8, hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipGetLastError();
+      dfree(d_tok_bytes);
+      dfree(d_tok_off);
+      return TOK_E_DEVICE;
+    }
+    return TOK_OK;
+  }
+
   // Span staging for host-memory calls, sized like d_ids (after ensure()).
   int ensure_spans() {
     if (d_spans) return TOK_OK;
@@ -474,6 +497,8 @@ struct tok_ctx {
     dfree(d_tok_len);
     dfree(d_tok_min);
     free_lit_tables();
+    dfree(d_tok_bytes);
+    dfree(d_tok_off);
     dfree(d_doc);
     dfree(d_outoff);
     hfree(h_doc);

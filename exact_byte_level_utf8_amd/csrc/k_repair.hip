@@ -1,0 +1,191 @@
+// Device side of append repair over a session kept in device memory
+// (tok_repair_dev): after the window [ws, new_len) is encoded with span
+// export, one workgroup matches the window's (byte offset, ID) records
+// against the stored ones, picks the splice and writes it into the session
+// buffer, so the IDs never cross to the host (TokTier, section 3, windowed
+// repair with a splice certificate; Appendix A, Definition A.4, Theorem A.5,
+// Corollary A.6; "Delta-aware routing" and Appendix E, the match and splice moved onto
+// the device).  The decisions are those of the host repair, record for
+// record:
+//   - stored records: walked back from the session's end through the token
+//     byte lengths (a suffix scan) until they cover [ws, old_len); each must
+//     spell its bytes of the text, else the session does not match;
+//   - a window record is equal when a stored record starts at the same byte
+//     with the same ID; runs of consecutive equal records are the candidates;
+//   - a run qualifies with at least two records, more bytes than the longest
+//     token, and a record starting at a synchronizing transition at least
+//     8 code points into the window and before old_len;
+//   - the last qualifying run is kept: stored IDs up to its end, then the
+//     window's IDs after it.
+#include "tok_internal.h"
+#include "pretok_rules.h"
+#include "sync_rules.h"
+#include "wg_scan.h"
+#include "uniclass.inc"
+
+namespace tok {
+namespace {
+
+constexpr uint32_t kRpThreads = 1024;
+
+__device__ inline uint32_t rp_class(uint32_t cp) {
+  if (cp < 0x80) return ascii_class(cp);
+  if (cp < TOK_CLS_LOW) return (kClsLow[cp >> 2] >> (2 * (cp & 3u))) & 3u;
+  if (cp >= 0x110000) return kO;
+  const uint32_t blk = kClsBlock[cp >> 8];
+  return (kClsBits[blk * 64 + ((cp & 255u) >> 2)] >> (2 * (cp & 3u))) & 3u;
+}
+
+// Code point whose lead byte is at index i of w[0, n) (valid UTF-8 there).
+__device__ inline uint32_t rp_cp(const uint8_t* w, uint64_t n, uint64_t i) {
+  const uint32_t b0 = w[i];
+  if (b0 < 0x80) return b0;
+  const uint32_t len = b0 >= 0xF0 ? 4 : b0 >= 0xE0 ? 3 : 2;
+  uint32_t cp = b0 & (0x7Fu >> len);
+  for (uint32_t k = 1; k < len && i + k < n; ++k) cp = (cp << 6) | (w[i + k] & 0x3Fu);
+  return cp;
+}
+
+struct MaxOp {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+
+// Stored record whose first byte is `off`, as its distance r from the
+// session's end (st_off[r] falls as r grows), or -1.
+__device__ inline int32_t find_stored(const uint32_t* st_off, uint32_t n_st, uint64_t off) {
+  uint32_t lo = 0, hi = n_st;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (st_off[mid] > off) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo < n_st && st_off[lo] == off ? (int32_t)lo : -1;
+}
+
+__global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) {
+  __shared__ uint32_t s_scan[kRpThreads / kWave];
+  __shared__ uint32_t s_bad, s_nst, s_best, s_F;
+  const uint32_t tid = threadIdx.x;
+  if (tid == 0) {
+    s_bad = 0;
+    s_nst = 0xFFFFFFFFu;
+    s_best = 0;
+    s_F = *(volatile const uint32_t*)A.fresh_total;  // host-mapped: one read
+  }
+  __syncthreads();
+  const uint32_t F = s_F;
+  const uint64_t wn = A.new_len - A.ws0;  // bytes in the device window
+  const uint64_t need = A.old_len - A.ws;  // stored bytes to cover
+
+  // stored records, from the session's end: r-th from the end has session
+  // index n_session - 1 - r and starts at old_len - (bytes of the last r + 1)
+  uint32_t carry = 0;
+  for (uint32_t r0 = 0;; r0 += kRpThreads) {  // uniform: s_nst and carry are shared
+    const uint32_t r = r0 + tid;
+    const bool have = r < A.n_session;
+    int32_t id = have ? A.session[A.n_session - 1 - r] : 0;
+    const bool id_ok = id >= 0 && (uint32_t)id < A.vocab;
+    const uint32_t len = have && id_ok ? A.tok_len[id] : 0u;
+    uint32_t tot = 0;
+    const uint32_t before = wg_excl_scan<kRpThreads>(len, 0u, AddOp(), s_scan, &tot);
+    const uint64_t s_end = (uint64_t)carry + before;  // bytes after this record
+    if (have && s_end < need) {                       // the record reaches into [ws, old_len)
+      bool bad = !id_ok || s_end + len > A.old_len;
+      if (!bad) {
+        const uint64_t off = A.old_len - s_end - len;
+        A.st_off[r] = (uint32_t)off;
+        const uint8_t* tb = A.tok_bytes + A.tok_off[id];
+        for (uint32_t k = 0; k < len && !bad; ++k) bad = tb[k] != A.win[off - A.ws0 + k];
+        if (s_end + len >= need) atomicMin(&s_nst, r + 1);
+      }
+      if (bad) s_bad = 1u;
+    }
+    carry += tot;
+    __syncthreads();
+    const bool stop = s_bad || s_nst != 0xFFFFFFFFu || r0 + kRpThreads >= A.n_session;
+    __syncthreads();  // every lane has read the shared words before the next pass may write them
+    if (stop) break;
+  }
+  const uint32_t n_st = s_nst;
+  if (s_bad || n_st == 0xFFFFFFFFu) {  // IDs that do not spell the text, or do not cover it
+    if (tid == 0) {
+      A.out->status = kRepairSession;
+      __threadfence_system();
+      report(&A.out->gen, A.gen);
+    }
+    return;
+  }
+
+  // equal records, runs, certificates; best = 1 + the last qualifying run end
+  auto equal_at = [&](int64_t k) -> bool {
+    if (k < 0 || k >= (int64_t)F) return false;
+    const uint64_t off = A.ws + A.fspan[k];
+    const int32_t r = find_stored(A.st_off, n_st, off);
+    return r >= 0 && A.session[A.n_session - 1 - (uint32_t)r] == A.fresh[k];
+  };
+  uint32_t c_start = 0, c_cert = 0;  // 1 + index of the last run start / certified record so far
+  for (uint32_t k0 = 0; k0 < F; k0 += kRpThreads) {
+    const uint32_t k = k0 + tid;
+    const bool eq = equal_at(k);
+    const bool start = eq && !equal_at((int64_t)k - 1);
+    const bool end = eq && !equal_at((int64_t)k + 1);
+    bool cert = false;
+    uint64_t off = 0;
+    if (eq) {
+      off = A.ws + A.fspan[k];
+      if (off >= A.margin && off < A.old_len) {
+        const uint64_t i = off - A.ws0;
+        uint64_t j = i - 1;
+        while (j > 0 && (A.win[j] & 0xC0u) == 0x80u) --j;
+        const uint32_t x = rp_cp(A.win, wn, j), y = rp_cp(A.win, wn, i);
+        cert = sync_transition_of(A.gpt2 != 0, x, rp_class(x), y, rp_class(y));
+      }
+    }
+    uint32_t t1 = 0, t2 = 0;
+    const uint32_t ls = MaxOp()(c_start, wg_excl_scan<kRpThreads>(start ? k + 1 : 0u, 0u, MaxOp(), s_scan, &t1));
+    const uint32_t lc = MaxOp()(c_cert, wg_excl_scan<kRpThreads>(cert ? k + 1 : 0u, 0u, MaxOp(), s_scan, &t2));
+    if (end) {
+      const uint32_t s = start ? k + 1 : ls;  // 1 + index of this run's first record
+      const uint32_t c = cert ? k + 1 : lc;
+      const uint32_t m = k + 2 - s;
+      const uint64_t bytes = off + A.tok_len[A.fresh[k]] - (A.ws + A.fspan[s - 1]);
+      if (c >= s && m >= 2 && bytes > A.max_tok_len) atomicMax(&s_best, k + 1);
+    }
+    c_start = MaxOp()(c_start, t1);
+    c_cert = MaxOp()(c_cert, t2);
+  }
+  __syncthreads();
+  const uint32_t best = s_best;
+  if (best == 0) {
+    if (tid == 0) {
+      A.out->status = kRepairNone;
+      __threadfence_system();
+      report(&A.out->gen, A.gen);
+    }
+    return;
+  }
+  const uint32_t kl = best - 1;
+  const uint64_t end_off = A.ws + A.fspan[kl] + A.tok_len[A.fresh[kl]];
+  const int32_t r = find_stored(A.st_off, n_st, A.ws + A.fspan[kl]);
+  const uint64_t keep_s = A.n_session - (uint32_t)r;  // stored IDs through the run's last record
+  const uint64_t total = keep_s + (F - best);
+  if (total <= A.cap)
+    for (uint32_t i = tid; i < F - best; i += kRpThreads) A.session[keep_s + i] = A.fresh[best + i];
+  __syncthreads();
+  if (tid == 0) {
+    A.out->status = total <= A.cap ? kRepairSpliced : kRepairCapacity;
+    A.out->total = total;
+    A.out->kept = keep_s;
+    A.out->splice = end_off;
+    __threadfence_system();
+    report(&A.out->gen, A.gen);
+  }
+}
+
+}  // namespace
+
+void launch_repair_match(const RepairArgs& a, hipStream_t s) {
+  repair_match_kernel<<<1, kRpThreads, 0, s>>>(a);
+}
+
+}  // namespace tok

@@ -13,30 +13,13 @@
 // doubles, at most five times, and then the whole text is encoded.  A miss
 // costs work, never a different ID.
 //
-// The stable boundary used here is a synchronizing transition: a byte b where
-// the class changes between the code point x before b and y at b such that,
-// for every left context, the pieces from b on are the pieces of the text
-// from b alone, b starts a piece, and the pieces before b do not depend on
-// anything after y.  Then the stored pieces before b are those of A + B, and
-// the window's pieces from b on are those of A + B.  The sets below follow
-// from the two pattern families (they list exactly the transitions where a
-// character before b can join the piece at b, or the piece before b can take
-// characters from b on); tests derive them independently by brute force from
-// the CPU oracle's matcher.
-//
-//   GPT-2 style: every class change, except after U+0020 (the optional space
-//   joins the next run) and apostrophe -> s t r v m l d (a contraction may
-//   begin there; the match is case-sensitive).
-//   Llama-3 style: every class change, except whitespace -> letter unless the
-//   whitespace is CR or LF (one non-CR/LF char prefixes a letter run),
-//   U+0020 -> other (the optional space), other -> letter (one other char
-//   prefixes a letter run, or a contraction), and other -> CR/LF (the other
-//   piece takes trailing CR/LF).
+// The stable boundary used here is a synchronizing transition (sync_rules.h).
 //
 // Work per call is O(w + |B|): the stored IDs are walked back from the end
 // through the token byte lengths, never from the start of the session.
 #include "ctx.h"
 #include "pretok_rules.h"
+#include "sync_rules.h"
 
 namespace {
 
@@ -96,21 +79,7 @@ uint64_t fwd_code_points(const uint8_t* t, uint64_t start, uint64_t end, uint64_
 }
 
 bool sync_transition(int pattern, uint32_t x, uint32_t y) {
-  const uint32_t cx = host_class(x), cy = host_class(y);
-  if (cx == cy) return false;
-  const bool x_crlf = x == 0x0D || x == 0x0A, y_crlf = y == 0x0D || y == 0x0A;
-  if (pattern == TOK_PAT_GPT2) {
-    if (x == 0x20) return false;
-    // apostrophe before a letter that can begin a (case-sensitive) contraction
-    if (x == 0x27 && (y == 's' || y == 't' || y == 'r' || y == 'v' || y == 'm' || y == 'l' || y == 'd'))
-      return false;
-    return true;
-  }
-  if (cx == kW && cy == kL && !x_crlf) return false;
-  if (x == 0x20 && cy == kO) return false;
-  if (cx == kO && cy == kL) return false;
-  if (cx == kO && y_crlf) return false;
-  return true;
+  return sync_transition_of(pattern == TOK_PAT_GPT2, x, host_class(x), y, host_class(y));
 }
 
 struct Rec {
@@ -252,6 +221,103 @@ int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap,
   // no certified splice: encode the whole text
   inf.full = 1;
   return tok_encode(ctx, text, new_len, session_ids, cap, n_out);
+}
+
+int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_t cap, const uint8_t* text,
+                   size_t old_len, size_t new_len, size_t* n_out, tok_repair_info* info) {
+  if (!ctx || !n_out || (!text && new_len) || (!d_session_ids && (cap || n_session)) || old_len > new_len ||
+      n_session > cap)
+    return TOK_E_ARG;
+  *n_out = 0;
+  tok_repair_info scratch{};
+  tok_repair_info& inf = info ? *info : scratch;
+  inf = tok_repair_info{};
+  if (new_len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
+  if ((old_len == 0) != (n_session == 0)) return TOK_E_SESSION;
+  if (new_len == old_len) {
+    *n_out = n_session;
+    inf.kept = n_session;
+    inf.splice_byte = old_len;
+    return TOK_OK;
+  }
+  DeviceGuard g(ctx->device);
+  hipStream_t s = ctx->stream;
+  volatile Counters* c = ctx->h_ctr;
+  if (!ctx->n_lit) {
+    int rc = ctx->ensure_tok_bytes();
+    if (rc) return rc;
+    const uint64_t pad = (ctx->max_tok_len + 3u) & ~3ull;  // keeps the window start word-aligned
+    uint64_t w = kFirstWindow;
+    for (uint32_t widen = 0; widen <= kMaxWidenings; ++widen, w *= 2) {
+      inf.widenings = widen;
+      const uint64_t ws = back_code_points(text, old_len, w);
+      if (ws == 0) break;  // the window would be the whole text
+      const uint64_t ws0 = ws > pad ? ws - pad : 0;
+      const uint64_t margin = fwd_code_points(text, ws, new_len, kMarginCodePoints);
+      const uint64_t wlen = new_len - ws;
+      rc = ctx->ensure(new_len - ws0);
+      if (!rc) rc = ctx->ensure_spans();
+      if (rc) return rc;
+      std::memcpy(ctx->h_text, text + ws0, new_len - ws0);
+      HIP_OK(hipMemcpyAsync(ctx->d_text, ctx->h_text, new_len - ws0, hipMemcpyHostToDevice, s));
+      Bufs bb = ctx->b;
+      const uint64_t call = bb.gen = ++ctx->gen;
+      ctx->enqueue(ctx->d_text + (ws - ws0), wlen, nullptr, 0, ctx->d_ids, ctx->d_spans, wlen, nullptr, s, bb, true,
+                   nullptr);
+      RepairArgs a{};
+      a.win = ctx->d_text;
+      a.ws0 = ws0;
+      a.ws = ws;
+      a.margin = margin;
+      a.old_len = old_len;
+      a.new_len = new_len;
+      a.fresh = ctx->d_ids;
+      a.fspan = ctx->d_spans;
+      a.fresh_total = &ctx->d_ctr->total;
+      a.session = d_session_ids;
+      a.n_session = n_session;
+      a.cap = cap;
+      a.tok_len = ctx->d_tok_len;
+      a.tok_bytes = ctx->d_tok_bytes;
+      a.tok_off = ctx->d_tok_off;
+      a.vocab = (uint32_t)ctx->tok_len.size();
+      a.max_tok_len = ctx->max_tok_len;
+      a.gpt2 = ctx->pattern == TOK_PAT_GPT2 ? 1 : 0;
+      a.st_off = ctx->b.ws_rk;  // free once the window encode is done
+      a.out = &ctx->d_ctr->rp;
+      a.gen = call;
+      launch_repair_match(a, s);
+      HIP_OK(hipGetLastError());
+      HIP_OK(hipStreamSynchronize(s));
+      if (c->err_utf8 == call) return TOK_E_UTF8;
+      if (c->done != call || c->rp.gen != call) return TOK_E_DEVICE;
+      const uint32_t st = c->rp.status;
+      if (st == kRepairSession) return TOK_E_SESSION;
+      if (st == kRepairNone) continue;
+      *n_out = c->rp.total;
+      inf.window_start = ws;
+      inf.splice_byte = c->rp.splice;
+      inf.kept = c->rp.kept;
+      return st == kRepairSpliced ? TOK_OK : TOK_E_CAPACITY;
+    }
+  }
+  // no certified splice (or literals set): encode the whole text, then
+  // replace the session if it fits
+  inf.full = 1;
+  int rc = ctx->ensure(new_len);
+  if (rc) return rc;
+  std::memcpy(ctx->h_text, text, new_len);
+  HIP_OK(hipMemcpyAsync(ctx->d_text, ctx->h_text, new_len, hipMemcpyHostToDevice, s));
+  uint32_t total = 0;
+  rc = ctx->n_lit ? ctx->run_added(ctx->d_text, new_len, ctx->d_ids, new_len, s, &total)
+                  : ctx->run(ctx->d_text, new_len, nullptr, 0, ctx->d_ids, nullptr, new_len, nullptr, s, true, nullptr,
+                             &total);
+  if (rc) return rc;
+  *n_out = total;
+  if (total > cap) return TOK_E_CAPACITY;
+  HIP_OK(hipMemcpyAsync(d_session_ids, ctx->d_ids, (size_t)total * 4, hipMemcpyDeviceToDevice, s));
+  HIP_OK(hipStreamSynchronize(s));
+  return TOK_OK;
 }
 
 }  // extern "C"

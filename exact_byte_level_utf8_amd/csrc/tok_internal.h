@@ -42,6 +42,17 @@ constexpr uint32_t kBucket = 4;      // hash-table slots probed with one set of 
 // classes
 enum : uint32_t { kL = 0, kN = 1, kW = 2, kO = 3 };
 
+// Result of the device repair's match and splice.
+enum : uint32_t { kRepairSpliced = 1, kRepairNone = 2, kRepairSession = 3, kRepairCapacity = 4 };
+struct RepairOut {
+  uint64_t gen;     // call number of the last match that finished
+  uint32_t status;  // kRepair*
+  uint32_t pad;
+  uint64_t total;   // IDs of the repaired session (spliced or capacity)
+  uint64_t kept;    // stored IDs kept
+  uint64_t splice;  // byte where the window's IDs take over
+};
+
 // Results of a call, written by the kernels into host memory.  Each call has
 // a number (gen, never 0); an error is reported by storing that number, so no
 // word needs clearing between calls and any number of workgroups may report.
@@ -53,6 +64,7 @@ struct Counters {
   uint32_t lits;      // added-token literals taken by the last literal pass
   uint64_t lit_done;  // gen of the last call whose literal selection finished
   uint64_t ins_done;  // gen of the last call whose literal insertion finished
+  RepairOut rp;       // the last device repair match
 };
 
 // Store a call number into the host-visible counters.
@@ -159,6 +171,25 @@ struct LitBufs {
   int32_t* ids;         // the pipeline's output, before the literal IDs go in
 };
 
+// Arguments of the device repair's match and splice (one workgroup).
+struct RepairArgs {
+  const uint8_t* win;  // text[ws0, new_len) on the device
+  uint64_t ws0, ws, margin, old_len, new_len;
+  const int32_t* fresh;          // IDs of the window text[ws, new_len)
+  const uint32_t* fspan;         // their first bytes, counted from ws
+  const uint32_t* fresh_total;   // how many (the window encode's count word)
+  int32_t* session;              // stored IDs on the device, spliced in place
+  uint64_t n_session, cap;
+  const uint32_t* tok_len;
+  const uint8_t* tok_bytes;      // token t is tok_bytes[tok_off[t] .. + tok_len[t])
+  const uint64_t* tok_off;
+  uint32_t vocab, max_tok_len;
+  int gpt2;                      // 1: GPT-2 style family, 0: Llama-3 style
+  uint32_t* st_off;              // scratch: first byte of the r-th stored record from the end
+  RepairOut* out;                // host-mapped result
+  uint64_t gen;
+};
+
 constexpr int kLitTile = 1024;  // bytes per workgroup of the literal match
 constexpr int kLitMax = 64;     // longest added-token literal, bytes
 constexpr uint32_t kLitMaxCount = 4096;
@@ -169,6 +200,7 @@ void launch_literal_pass(const uint8_t* text, uint64_t n, Literals L, LitBufs lb
                          hipStream_t s);
 void launch_literal_insert(uint64_t n, uint32_t k, Literals L, LitBufs lb, int32_t* out, uint64_t cap,
                            Counters* ctr, uint64_t gen, hipStream_t s);
+void launch_repair_match(const RepairArgs& a, hipStream_t s);
 void launch_empty_batch(Bufs b, const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s);
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
                    int pattern, Bufs b, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);

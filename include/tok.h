@@ -246,6 +246,35 @@ int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap,
                size_t old_len, size_t new_len, size_t* n_out, tok_repair_info* info);
 
 /*
+ * tok_repair_dev -- tok_repair for a session whose IDs live in device memory
+ * (TokTier, section 3 and Appendix A as for tok_repair; "Delta-aware routing" and
+ * Appendix E: the match and splice run on the device, so the IDs never cross
+ * to the host).
+ *
+ * d_session_ids: device array of cap int32 (the context's device); on entry
+ *                d_session_ids[0 .. n_session) must equal the encode of
+ *                text[0 .. old_len); on success d_session_ids[0 .. *n_out)
+ *                equals the encode of text[0 .. new_len), spliced in place.
+ * text:          host bytes text[0 .. new_len), as for tok_repair.
+ *
+ * Each attempt copies the window text[ws - (longest token, rounded up to 4
+ * bytes) .. new_len) to the device, encodes text[ws .. new_len) with span
+ * export, and one workgroup then walks the stored IDs back from their end
+ * through the token byte lengths (checking that they spell the text),
+ * matches the (byte offset, ID) records, picks the splice exactly as
+ * tok_repair does and writes the window's IDs after it: one synchronization
+ * per attempt.  The window widening, the gates and the full-encode fallback
+ * are tok_repair's; with added-token literals set the whole text is encoded.
+ * Runs on the context's own stream, ordered after work on the legacy default
+ * stream.
+ *
+ * Errors: as tok_repair; on TOK_E_CAPACITY (*n_out = required cap) and on
+ * every other error the session IDs are left unchanged.
+ */
+int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_t cap, const uint8_t* text,
+                   size_t old_len, size_t new_len, size_t* n_out, tok_repair_info* info);
+
+/*
  * tok_sync_boundary -- 1 if a byte where code point prev_cp is followed by
  * code point cp is a synchronizing transition of the pattern family: a class
  * change such that, for any text before it, the pieces from that byte on are

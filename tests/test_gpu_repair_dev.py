@@ -1,0 +1,151 @@
+"""Append repair over a session kept in device memory (tok_repair_dev): the
+match and splice run in one workgroup on the device.  The result must equal
+the oracle's full encode of the whole text, and every decision (kept IDs,
+splice byte, window start, widenings, fallback) must equal the host repair's
+(tok_repair), which runs the same rules on the host.  The stored IDs handed
+in are the oracle's encode of the stored text.
+
+Covers the session-append workload (1,000,000-character context, seeded
+log-normal appends, 30% starting mid-word or mid-whitespace), seam shapes of
+both families, widening and the full-encode fallback, stored IDs that do not
+spell the text or do not cover it, capacity overflow (session untouched), an
+empty session, and added-token literals (whole-text encode).
+"""
+import numpy as np
+import pytest
+
+import exact_byte_level_utf8_amd as tk
+import oracle
+from synth import textgen
+from tests import libs, vocab
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+SEAMS = [
+    ("The staging pipe", "line holds"),
+    ("one two three\n   ", "\n   four"),
+    ("x = 1;\n    ", "    y = 2"),
+    ("it'", "s fine and they'll go"),
+    ("it", "'s fine"),
+    ("count 12345", "6789 items"),
+    ("done.\r", "\n\nnext"),
+    ("tail   ", "   more"),
+    ("emoji \U0001F600", "\U0001F600 and more"),
+    ("end", ""),
+]
+
+
+@pytest.fixture(scope="module")
+def cfg():
+    libs.ensure_built()
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    out = {}
+    for name in ("gpt2", "llama3"):
+        merges_name, pattern = libs.CONFIGS[name]
+        m = vocab.merges(merges_name)
+        out[name] = (tk.Tokenizer(m, pattern), oracle.Oracle(m, pattern))
+    return out
+
+
+def dev_repair(t, sess, text: bytes, old_len: int, cap=None):
+    sess = np.asarray(sess, dtype=np.int32)
+    cap = len(sess) + (len(text) - old_len) + 64 if cap is None else cap
+    buf = torch.full((max(cap, 1),), -5, dtype=torch.int32)
+    buf[: len(sess)] = torch.from_numpy(sess)
+    d = buf.cuda()
+    torch.cuda.synchronize()
+    n, info = t.repair_dev(d, len(sess), text, old_len)
+    return d.cpu().numpy()[:n], info, d
+
+
+def check(t, o, old: bytes, app: bytes, what: str):
+    sess = o.encode(old)
+    want = o.encode(old + app)
+    got, info, _ = dev_repair(t, sess, old + app, len(old))
+    assert np.array_equal(got, want), f"{what}: device repair differs from the full encode ({info})"
+    h_ids, h_info = t.repair(sess, old + app, len(old))
+    assert h_info == info, f"{what}: device {info} vs host {h_info}"
+    if info["full"] == 0:
+        assert np.array_equal(got[: info["kept"]], np.asarray(sess)[: info["kept"]])
+    return info
+
+
+def test_session_append_workload(cfg):
+    t, o = cfg["gpt2"]
+    base = textgen.mix_text(500, 1_000_000)
+    full = 0
+    for seed in range(24):
+        old, suf = textgen.repair_case(500, 9_000 + seed, old_text=base)
+        info = check(t, o, old.encode(), suf.encode(), f"append seed {seed}")
+        full += info["full"]
+    assert full == 0
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_seam_shapes(cfg, name):
+    t, o = cfg[name]
+    ctx = textgen.mix_text(501, 4_000)
+    for left, right in SEAMS:
+        check(t, o, (ctx + left).encode(), right.encode(), f"{left!r}|{right!r}")
+        check(t, o, left.encode(), right.encode(), f"short {left!r}|{right!r}")
+
+
+def test_llama3_appends(cfg):
+    t, o = cfg["llama3"]
+    base = textgen.mix_text(510, 200_000)
+    for seed in range(10):
+        old, suf = textgen.repair_case(510, 9_500 + seed, old_text=base)
+        check(t, o, old.encode(), suf.encode(), f"llama3 append {seed}")
+
+
+def test_widening_and_fallback(cfg):
+    t, o = cfg["gpt2"]
+    ctx = textgen.mix_text(502, 3_000)
+    info = check(t, o, (ctx + " " + "a" * 3_000).encode(), b"b and c", "widen")
+    assert info["full"] == 0 and info["widenings"] >= 3
+    info = check(t, o, (ctx + " " + "a" * 20_000).encode(), b"b", "fallback")
+    assert info["full"] == 1
+
+
+def test_session_errors_leave_the_session_alone(cfg):
+    t, o = cfg["gpt2"]
+    old = textgen.mix_text(503, 5_000).encode()
+    app = b" appended words"
+    sess = np.asarray(o.encode(old), dtype=np.int32)
+    bad = sess.copy()
+    bad[-1] = (bad[-1] + 1) % t.info()["vocab_size"]
+    for ids in (bad, sess[:-3], np.concatenate([sess[:-1], [t.info()["vocab_size"] + 5]]).astype(np.int32)):
+        with pytest.raises(tk.TokError) as e:
+            dev_repair(t, ids, old + app, len(old))
+        assert e.value.code == tk.TOK_E_SESSION
+    # capacity: reported, session untouched
+    app = textgen.prose_text(505, 600).encode()
+    cap = len(sess)
+    buf = torch.from_numpy(sess.copy()).cuda()
+    with pytest.raises(tk.TokError) as e:
+        t.repair_dev(buf, len(sess), old + app, len(old))
+    assert e.value.code == tk.TOK_E_CAPACITY
+    assert np.array_equal(buf.cpu().numpy(), sess)
+    assert cap == buf.numel()
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_empty_session_and_literals(cfg, name):
+    t, o = cfg[name]
+    app = "Fresh session text, 42 words.\n".encode()
+    got, info, _ = dev_repair(t, [], app, 0)
+    assert np.array_equal(got, o.encode(app)) and info["full"] == 1
+    v = t.info()["vocab_size"]
+    lits = [(b"<|endoftext|>", v), (b"<|im_end|>", v + 1)]
+    t.set_added_tokens(lits)
+    try:
+        old = (textgen.mix_text(506, 3000) + "<|im_end|>").encode()
+        new = old + b"<|endoftext|> more"
+        sess = o.encode_added(old, lits)
+        got, info, _ = dev_repair(t, sess, new, len(old))
+        assert info["full"] == 1
+        assert np.array_equal(got, o.encode_added(new, lits))
+    finally:
+        t.set_added_tokens([])
