@@ -90,19 +90,41 @@ def source_digest(stage: str) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, stage: str):
-    """HBM bytes per launch of the stage's kernel from the committed rocprofv3
-    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by a copy of known
-    size), or None when there is none or the kernel's sources changed since."""
+def profiled(workload: str, stage: str, field: str):
+    """A per-launch figure of the stage's kernel from the committed rocprofv3
+    counter summary (bytes_per_launch: FETCH_SIZE + WRITE_SIZE, each scaled by
+    a copy of known size; valu_wave_instr: SQ_INSTS_VALU), or None when there
+    is none or the kernel's sources changed since."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
     k = rec.get("kernels", {}).get(STAGE_KERNELS[stage][0])
-    if not k or k.get("source_sha256") != source_digest(stage):
+    if not k or k.get("source_sha256") != source_digest(stage) or field not in k:
         return None
-    return int(k["bytes_per_launch"])
+    return int(k[field])
+
+
+def measured_traffic(workload: str, stage: str):
+    return profiled(workload, stage, "bytes_per_launch")
+
+
+# VALU issue peak: 256 CUs x 4 SIMDs, each SIMD issuing one wave64 vector
+# instruction per 4 cycles (16 lanes per cycle) at 2.4 GHz
+VALU_PEAK_G = 256 * 4 * 2.4e9 / 4 / 1e9
+
+
+def valu_issue(workload: str, stage: str, avg_ms: float):
+    """Vector-instruction issue rate of the kernel: its counted wave64 VALU
+    instructions per launch (committed counter summary) over the live average
+    duration, against the chip's issue peak."""
+    v = profiled(workload, stage, "valu_wave_instr")
+    if v is None or avg_ms <= 0:
+        return None
+    g = v / (avg_ms * 1e-3) / 1e9
+    return {"achieved": round(g, 1), "peak": round(VALU_PEAK_G, 1), "unit": "G wave64 VALU instr/s",
+            "frac": round(g / VALU_PEAK_G, 4), "instr_per_launch": v}
 
 
 def log(*a):
@@ -398,7 +420,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6),
                      "traffic": measured_traffic(args.workload, dom),
-                     "algorithmic_bytes": alg, "avg_ms": dom_ms},
+                     "algorithmic_bytes": alg, "avg_ms": dom_ms,
+                     "valu_issue": valu_issue(args.workload, dom, dom_ms)},
         "complete_call": complete,
         "graph_ab": graph_ab,
         "span_export": span_export,
