@@ -212,9 +212,16 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   // lookups of all rounds (one direct table up to U+1FFFF, so emoji too) are
   // issued before any is used
   {
+    // the last round covers only the window's tail: a wave wholly past the
+    // window skips it (a scalar branch), instead of decoding clamped copies
+    const uint32_t wv_s = __builtin_amdgcn_readfirstlane(wv);
+    auto live = [&](int j) { return j + 1 < kWinRounds || (int)(wv_s * kWave) + j * NT < kWin; };
     uint32_t cps[kWinRounds], pre[kWinRounds];
 #pragma unroll
     for (int j = 0; j < kWinRounds; ++j) {
+      cps[j] = 0;
+      pre[j] = 0;
+      if (!live(j)) continue;
       const int k = min((int)(tid + j * NT), kWin - 1);  // positions past the window repeat the last one
       const uint32_t g = (uint32_t)(k + kGuard);
       const uint32_t cur = lds_word(s_raw32, g), prv = lds_word(s_raw32, g - 4u);
@@ -243,17 +250,19 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     uint32_t cls[kWinRounds];
 #pragma unroll
     for (int j = 0; j < kWinRounds; ++j) {
+      cls[j] = kO;
+      if (!live(j)) continue;
       const uint32_t cp = cps[j];
       const uint32_t low = kClsLow[min(cp, (uint32_t)TOK_CLS_LOW - 1u) >> 2];
       cls[j] = cp < 0x80u ? ascii_class(cp) : (low >> (2u * (cp & 3u))) & 3u;
     }
 #pragma unroll
     for (int j = 0; j < kWinRounds; ++j)
-      if (cps[j] >= (uint32_t)TOK_CLS_LOW) cls[j] = dev_class(cps[j]);  // rare: two-level table above U+1FFFF
+      if (live(j) && cps[j] >= (uint32_t)TOK_CLS_LOW) cls[j] = dev_class(cps[j]);  // rare: two-level table above U+1FFFF
 #pragma unroll
     for (int j = 0; j < kWinRounds; ++j) {
       const int k = tid + j * NT;
-      if (k >= kWin) continue;
+      if (!live(j) || k >= kWin) continue;
       const uint32_t cp = cps[j], p = pre[j];
       uint32_t in = 0;
       if (p & kIUndecoded) in = kO | p;
@@ -273,6 +282,9 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   for (int j = 0; j < kRounds; ++j) {
     const uint32_t g = (uint32_t)(kHalo + tid + j * NT + kGuard);
     const uint64_t raw = (uint64_t)lds_word(s_raw32, g) | ((uint64_t)lds_word(s_raw32, g + 4u) << 32);
+    // a wave whose positions and the four bytes after each are all ASCII is
+    // well formed there (bytes outside the text read as 0): skip the checks
+    if (__ballot((raw & 0x8080808080ull) != 0) == 0) continue;
     const uint64_t fl = (uint64_t)lds_word(s_fl32, g) | ((uint64_t)lds_word(s_fl32, g + 4u) << 32);
     const uint32_t b0 = (uint32_t)raw & 0xFFu, b1 = (uint32_t)(raw >> 8) & 0xFFu, f0 = (uint32_t)fl & 0xFFu;
     const uint32_t len = 1u + (b0 >= 0xC0u) + (b0 >= 0xE0u) + (b0 >= 0xF0u);
