@@ -280,6 +280,7 @@ int tok_encode(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids, size
   if (len == 0) return TOK_OK;
   DeviceGuard g(ctx->device);
   int rc = ctx->ensure(len);
+  if (!rc) rc = ctx->ensure_host();
   if (rc) return rc;
   hipStream_t s = ctx->stream;
   std::memcpy(ctx->h_text, text, len);
@@ -328,6 +329,7 @@ int tok_encode_batch(tok_ctx* ctx, const uint8_t* text, const uint64_t* doc_off,
   if (len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
   DeviceGuard g(ctx->device);
   int rc = ctx->ensure(len ? len : 1);
+  if (!rc) rc = ctx->ensure_host();
   if (rc) return rc;
   rc = ctx->ensure_docs(n_docs);
   if (rc) return rc;
@@ -383,6 +385,7 @@ int tok_encode_spans(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids
   if (len == 0) return TOK_OK;
   DeviceGuard g(ctx->device);
   int rc = ctx->ensure(len);
+  if (!rc) rc = ctx->ensure_host();
   if (!rc) rc = ctx->ensure_spans();
   if (rc) return rc;
   hipStream_t s = ctx->stream;

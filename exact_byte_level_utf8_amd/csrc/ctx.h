@@ -206,11 +206,7 @@ struct tok_ctx {
         hipMalloc((void**)&b.ws_rk, (c + 64) * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&b.ws_sel, (c + 64) * sizeof(uint64_t)) != hipSuccess ||
         hipMalloc((void**)&b.sum1, ((tiles >> kSum1Shift) + 1) * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.sum2, ((tiles >> kSum2Shift) + 1) * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&d_text, c + 64) != hipSuccess ||
-        hipMalloc((void**)&d_ids, (c + 64) * sizeof(int32_t)) != hipSuccess ||
-        hipHostMalloc((void**)&h_text, c + 64, hipHostMallocDefault) != hipSuccess ||
-        hipHostMalloc((void**)&h_ids, (c + 64) * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
+        hipMalloc((void**)&b.sum2, ((tiles >> kSum2Shift) + 1) * sizeof(uint32_t)) != hipSuccess) {
       (void)hipGetLastError();
       free_scratch();
       return TOK_E_NOMEM;
@@ -270,25 +266,20 @@ struct tok_ctx {
     return TOK_OK;
   }
 
-  // Encode with the added-token literals: the literal pass, one
-  // synchronization to learn how many literals it took, then the pipeline
-  // over the 2k + 1 parts and the insertion of the literal IDs (or, with no
-  // literal in the text, the plain pipeline straight into out).
+  // Encode with the added-token literals: the literal pass, the pipeline
+  // over the 2k + 1 parts (segment, literal, ..., segment) as documents whose
+  // count the kernels read on the device, and the insertion of the literal
+  // IDs, all enqueued at once; one synchronization.
   int run_added(const uint8_t* text, uint64_t n, int32_t* out, uint64_t out_cap, hipStream_t s, uint32_t* total) {
     int rc = ensure_lit_bufs();
     if (rc) return rc;
     volatile Counters* c = h_ctr;
-    const uint64_t call = ++gen;
-    launch_literal_pass(text, n, literals(), lb, d_ctr, call, s);
-    HIP_OK(hipGetLastError());
-    HIP_OK(hipStreamSynchronize(s));
-    if (c->lit_done != call) return TOK_E_DEVICE;
-    const uint32_t k = c->lits;
-    if (k == 0) return run(text, n, nullptr, 0, out, nullptr, out_cap, nullptr, s, true, nullptr, total);
     Bufs bb = b;
-    const uint64_t call2 = bb.gen = ++gen;
-    enqueue(text, n, lb.doc_off, 2 * k + 1, lb.ids, nullptr, n, lb.out_off, s, bb, true, nullptr);
-    launch_literal_insert(n, k, literals(), lb, out, out_cap, d_ctr, call2, s);
+    const uint64_t call = bb.gen = ++gen;
+    bb.n_docs_dev = lb.misc + 2;
+    launch_literal_pass(text, n, literals(), lb, d_ctr, call, s);
+    enqueue(text, n, lb.doc_off, 1, lb.ids, nullptr, n, lb.out_off, s, bb, true, nullptr);
+    launch_literal_insert(n, literals(), lb, out, out_cap, d_ctr, call, s);
     HIP_OK(hipGetLastError());
     HIP_OK(hipStreamSynchronize(s));
     if (prof) {
@@ -298,9 +289,9 @@ struct tok_ctx {
         stage_ms[i] = ((prof >> i) & 1u) ? ms : 0.f;
       }
     }
-    if (c->err_docs == call2) return TOK_E_DEVICE;  // the parts are well formed by construction
-    if (c->err_utf8 == call2) return TOK_E_UTF8;
-    if (c->done != call2 || c->ins_done != call2) return TOK_E_DEVICE;
+    if (c->err_docs == call) return TOK_E_DEVICE;  // the parts are well formed by construction
+    if (c->err_utf8 == call) return TOK_E_UTF8;
+    if (c->lit_done != call || c->done != call || c->ins_done != call) return TOK_E_DEVICE;
     *total = c->total;
     return TOK_OK;
   }
@@ -320,6 +311,25 @@ struct tok_ctx {
       dfree(d_tok_bytes);
       dfree(d_tok_off);
       return TOK_E_DEVICE;
+    }
+    return TOK_OK;
+  }
+
+  // Staging of host-memory calls (device copies of the text and IDs, pinned
+  // host buffers), sized like the scratch (after ensure()); calls on device
+  // buffers never allocate it.
+  int ensure_host() {
+    if (d_text) return TOK_OK;
+    if (hipMalloc((void**)&d_text, cap + 64) != hipSuccess ||
+        hipMalloc((void**)&d_ids, (cap + 64) * sizeof(int32_t)) != hipSuccess ||
+        hipHostMalloc((void**)&h_text, cap + 64, hipHostMallocDefault) != hipSuccess ||
+        hipHostMalloc((void**)&h_ids, (cap + 64) * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      dfree(d_text);
+      dfree(d_ids);
+      hfree(h_text);
+      hfree(h_ids);
+      return TOK_E_NOMEM;
     }
     return TOK_OK;
   }
@@ -466,6 +476,7 @@ struct tok_ctx {
   int run_pieces(const uint8_t* h_bytes, uint64_t n, const std::vector<uint16_t>& flags,
                  std::vector<int32_t>& ids) {
     int rc = ensure(n);
+    if (!rc) rc = ensure_host();
     if (rc) return rc;
     HIP_OK(hipMemcpyAsync(d_text, h_bytes, n, hipMemcpyHostToDevice, stream));
     HIP_OK(hipMemcpyAsync(b.flags, flags.data(), flags.size() * 2, hipMemcpyHostToDevice, stream));

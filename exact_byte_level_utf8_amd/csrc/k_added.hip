@@ -17,9 +17,10 @@
 //                      of the definition, over the matches only).  The taken
 //                      literals cut the text into 2k + 1 parts: segment,
 //                      literal, segment, ..., segment.
-// The parts then run through the usual pipeline as documents, which are hard
-// boundaries for code points, pieces and merges, exactly as the segments
-// between literals must be.  Then:
+// The parts then run through the usual pipeline as documents (their count
+// read on the device, so the host enqueues everything without waiting),
+// which are hard boundaries for code points, pieces and merges, exactly as
+// the segments between literals must be.  Then:
 //   lit_insert_kernel  one workgroup: output offsets of the parts, where a
 //                      literal part counts one ID; writes the literal IDs.
 //   lit_scatter_kernel every ID of a segment part to its final place; the IDs
@@ -132,6 +133,7 @@ lit_select_kernel(uint64_t n, uint32_t tiles, Literals L, LitBufs lb, Counters* 
     lb.doc_off[0] = 0;
     lb.doc_off[2 * (uint64_t)k + 1] = n;
     lb.misc[1] = k;
+    lb.misc[2] = 2 * k + 1;  // the parts, read by the pipeline as its document count
     ctr->lits = k;
     __threadfence_system();
     report(&ctr->lit_done, gen);
@@ -139,9 +141,9 @@ lit_select_kernel(uint64_t n, uint32_t tiles, Literals L, LitBufs lb, Counters* 
 }
 
 __global__ void __launch_bounds__(kSelThreads)
-lit_insert_kernel(Literals L, LitBufs lb, uint32_t k, int32_t* __restrict__ out, uint64_t cap, Counters* ctr,
-                  uint64_t gen) {
+lit_insert_kernel(Literals L, LitBufs lb, int32_t* __restrict__ out, uint64_t cap, Counters* ctr, uint64_t gen) {
   __shared__ uint32_t s_scan[kSelThreads / kWave];
+  const uint32_t k = lb.misc[1];
   const uint32_t tid = threadIdx.x, parts = 2 * k + 1;
   uint32_t carry = 0;
   for (uint32_t i0 = 0; i0 < parts; i0 += kSelThreads) {
@@ -166,8 +168,8 @@ lit_insert_kernel(Literals L, LitBufs lb, uint32_t k, int32_t* __restrict__ out,
 }
 
 __global__ void __launch_bounds__(kScatterThreads)
-lit_scatter_kernel(LitBufs lb, uint32_t k, int32_t* __restrict__ out, uint64_t cap) {
-  const uint32_t parts = 2 * k + 1;
+lit_scatter_kernel(LitBufs lb, int32_t* __restrict__ out, uint64_t cap) {
+  const uint32_t parts = 2 * lb.misc[1] + 1;
   const uint32_t T = lb.misc[0];
   for (uint32_t t = blockIdx.x * kScatterThreads + threadIdx.x; t < T; t += gridDim.x * kScatterThreads) {
     // the part holding pipeline token t: the last i with out_off[i] <= t
@@ -192,11 +194,11 @@ void launch_literal_pass(const uint8_t* text, uint64_t n, Literals L, LitBufs lb
   lit_select_kernel<<<1, kSelThreads, 0, s>>>(n, tiles, L, lb, ctr, gen);
 }
 
-void launch_literal_insert(uint64_t n, uint32_t k, Literals L, LitBufs lb, int32_t* out, uint64_t cap,
-                           Counters* ctr, uint64_t gen, hipStream_t s) {
-  lit_insert_kernel<<<1, kSelThreads, 0, s>>>(L, lb, k, out, cap, ctr, gen);
+void launch_literal_insert(uint64_t n, Literals L, LitBufs lb, int32_t* out, uint64_t cap, Counters* ctr,
+                           uint64_t gen, hipStream_t s) {
+  lit_insert_kernel<<<1, kSelThreads, 0, s>>>(L, lb, out, cap, ctr, gen);
   const uint32_t blocks = (uint32_t)std::min<uint64_t>((n + kScatterThreads - 1) / kScatterThreads, 8192);
-  lit_scatter_kernel<<<blocks, kScatterThreads, 0, s>>>(lb, k, out, cap);
+  lit_scatter_kernel<<<blocks, kScatterThreads, 0, s>>>(lb, out, cap);
 }
 
 }  // namespace tok

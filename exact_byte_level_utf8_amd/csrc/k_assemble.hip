@@ -33,6 +33,7 @@ assemble_kernel(uint64_t n, Bufs B, int32_t* __restrict__ out, uint32_t* __restr
   __shared__ uint32_t s_part[kAsmThreads / kWave];
   __shared__ uint32_t s_scan[kAsmThreads / kWave];
   __shared__ uint32_t s_doc0;
+  if (B.n_docs_dev) n_docs = *B.n_docs_dev;
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   const uint32_t tile = blockIdx.x;
   const bool last = tile == gridDim.x - 1;

@@ -459,6 +459,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   __shared__ uint32_t s_cnt[kChunksPerWg], s_excl[kChunksPerWg];
   __shared__ uint32_t s_n[9], s_next, s_first, s_doc0;
 
+  if (B.n_docs_dev) n_docs = *B.n_docs_dev;
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   if (tid < 9) s_n[tid] = 0;
   if (tid == 0) s_next = 0;

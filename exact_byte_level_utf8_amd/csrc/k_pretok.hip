@@ -144,6 +144,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   uint8_t* s_raw = reinterpret_cast<uint8_t*>(s_raw32);
   uint8_t* s_fl = reinterpret_cast<uint8_t*>(s_fl32);
 
+  if (B.n_docs_dev) n_docs = *B.n_docs_dev;
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
   const int64_t base = (int64_t)blockIdx.x * kPT;
   uint16_t* __restrict__ flags = B.flags;

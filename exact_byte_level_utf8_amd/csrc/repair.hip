@@ -256,6 +256,7 @@ int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_
       const uint64_t margin = fwd_code_points(text, ws, new_len, kMarginCodePoints);
       const uint64_t wlen = new_len - ws;
       rc = ctx->ensure(new_len - ws0);
+      if (!rc) rc = ctx->ensure_host();
       if (!rc) rc = ctx->ensure_spans();
       if (rc) return rc;
       std::memcpy(ctx->h_text, text + ws0, new_len - ws0);
@@ -305,6 +306,7 @@ int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_
   // replace the session if it fits
   inf.full = 1;
   int rc = ctx->ensure(new_len);
+  if (!rc) rc = ctx->ensure_host();
   if (rc) return rc;
   std::memcpy(ctx->h_text, text, new_len);
   HIP_OK(hipMemcpyAsync(ctx->d_text, ctx->h_text, new_len, hipMemcpyHostToDevice, s));

@@ -303,9 +303,10 @@ int tok_sync_boundary(int pattern, uint32_t prev_cp, uint32_t cp);
  * and its ID emitted, and the scan goes on after it; each segment between
  * taken literals is encoded as a request of its own (its pieces and merges
  * never reach across a literal).  Literals are matched on the raw bytes, with
- * no whitespace stripping, word-boundary or normalization options.  The cost
- * is one more synchronization per call (the literal pass reports how many
- * literals it took).  tok_repair then always encodes the whole text (its
+ * no whitespace stripping, word-boundary or normalization options.  The
+ * literal pass and the insertion of the literal IDs run on the device in the
+ * same stream as the pipeline (still one synchronization per call).
+ * tok_repair then always encodes the whole text (its
  * splice certificate does not cover literals).  The batch and span calls
  * return TOK_E_UNSUPPORTED while literals are set.
  *
