@@ -132,7 +132,7 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   constexpr int kPer = kRounds;                        // consecutive positions per thread in the aggregate pass
   static_assert(kPer == 2 || kPer == 4, "aggregate states are packed as 2 or 4 bytes per thread");
   constexpr int kWinRounds = (kWin + NT - 1) / NT;     // window positions per thread
-  // window byte k (k in [-4, kWin + 12)) lives at byte 4 + k of s_raw / s_fl
+  // window byte k (k in [-4, kWin + 12)) lives at byte 4 + k of s_raw32 / s_fl32 (as bytes)
   constexpr int kGuard = 4, kBytes = kWin + 16;
   static_assert(kBytes % 4 == 0 && (kHalo + kGuard) % 4 == 0, "the window is loaded as aligned dwords");
   __shared__ uint32_t s_raw32[kBytes / 4];
@@ -141,7 +141,6 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   __shared__ uint32_t s_scan[NT / kWave], s_scan2[NT / kWave];
   __shared__ uint32_t s_misc[4];
   __shared__ uint32_t s_agg[PATTERN == 1 ? kPT / 4 : 1];  // Llama-3 run states, a byte per tile position
-  uint8_t* s_raw = reinterpret_cast<uint8_t*>(s_raw32);
   uint8_t* s_fl = reinterpret_cast<uint8_t*>(s_fl32);
 
   if (B.n_docs_dev) n_docs = *B.n_docs_dev;
