@@ -459,7 +459,6 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   __shared__ uint32_t s_cnt[kChunksPerWg], s_excl[kChunksPerWg];
   __shared__ uint32_t s_n[9], s_next, s_first, s_doc0;
 
-  if (B.n_docs_dev) n_docs = *B.n_docs_dev;
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   if (tid < 9) s_n[tid] = 0;
   if (tid == 0) s_next = 0;
@@ -648,7 +647,8 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
       atomicAdd(&B.sum2[tile >> kSum2Shift], total);
     }
   }
-  if (doc_off && tid == kWave) s_doc0 = first_doc_at_or_after(doc_off, n_docs, base);
+  if (doc_off && tid == kWave)
+    s_doc0 = first_doc_at_or_after(doc_off, B.n_docs_dev ? *B.n_docs_dev : n_docs, base);
   __syncthreads();
 
   // every thread writes the tokens of the pieces that start in its two bytes:
@@ -695,7 +695,8 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
 
   // offsets, within this tile's run, of the documents that start in the tile
   if (doc_off) {
-    for (uint32_t d = s_doc0 + tid; d <= n_docs; d += NT) {
+    const uint32_t nd = B.n_docs_dev ? *B.n_docs_dev : n_docs;  // the count read on the device, if given
+    for (uint32_t d = s_doc0 + tid; d <= nd; d += NT) {
       const uint64_t p = doc_off[d];
       if (p >= n || p >= base + kPieceTile) break;
       if (p < base) continue;  // only with unordered offsets, which the call rejects
