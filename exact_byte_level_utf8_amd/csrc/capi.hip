@@ -360,7 +360,7 @@ int tok_encode_spans_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
   if (!ctx || !n_out || (!d_text && len) || (cap && (!d_ids || !d_spans)) || n_docs >= 0xFFFFFFFFu ||
       (d_doc_off && (n_docs == 0 || !d_out_off)))
     return TOK_E_ARG;
-  if (ctx->n_lit) return TOK_E_UNSUPPORTED;
+  if (ctx->n_lit && d_doc_off) return TOK_E_UNSUPPORTED;
   *n_out = 0;
   if (len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
   if (len == 0 && !d_doc_off) return TOK_OK;
@@ -369,8 +369,9 @@ int tok_encode_spans_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
   if (rc) return rc;
   hipStream_t s = stream ? (hipStream_t)stream : ctx->stream;
   uint32_t total = 0;
-  rc = ctx->run(d_text, len, d_doc_off, d_doc_off ? (uint32_t)n_docs : 0, d_ids, d_spans, cap,
-                d_doc_off ? d_out_off : nullptr, s, true, nullptr, &total);
+  rc = ctx->n_lit ? ctx->run_added(d_text, len, d_ids, cap, s, &total, d_spans)
+                  : ctx->run(d_text, len, d_doc_off, d_doc_off ? (uint32_t)n_docs : 0, d_ids, d_spans, cap,
+                             d_doc_off ? d_out_off : nullptr, s, true, nullptr, &total);
   if (rc) return rc;
   *n_out = total;
   return total > cap ? TOK_E_CAPACITY : TOK_OK;
@@ -379,7 +380,6 @@ int tok_encode_spans_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
 int tok_encode_spans(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids, uint32_t* spans, size_t cap,
                      size_t* n_out) {
   if (!ctx || !n_out || (!text && len) || (cap && (!ids || !spans))) return TOK_E_ARG;
-  if (ctx->n_lit) return TOK_E_UNSUPPORTED;
   *n_out = 0;
   if (len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
   if (len == 0) return TOK_OK;
@@ -392,7 +392,9 @@ int tok_encode_spans(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids
   std::memcpy(ctx->h_text, text, len);
   HIP_OK(hipMemcpyAsync(ctx->d_text, ctx->h_text, len, hipMemcpyHostToDevice, s));
   uint32_t total = 0;
-  rc = ctx->run(ctx->d_text, len, nullptr, 0, ctx->d_ids, ctx->d_spans, len, nullptr, s, true, nullptr, &total);
+  rc = ctx->n_lit ? ctx->run_added(ctx->d_text, len, ctx->d_ids, len, s, &total, ctx->d_spans)
+                  : ctx->run(ctx->d_text, len, nullptr, 0, ctx->d_ids, ctx->d_spans, len, nullptr, s, true, nullptr,
+                             &total);
   if (rc) return rc;
   *n_out = total;
   if (total > cap) return TOK_E_CAPACITY;

@@ -237,6 +237,7 @@ struct tok_ctx {
     dfree(lb.fin);
     dfree(lb.misc);
     dfree(lb.ids);
+    dfree(lb.spans);
     lit_cap = 0;
   }
 
@@ -257,7 +258,8 @@ struct tok_ctx {
         hipMalloc((void**)&lb.out_off, (2 * cap + 2) * 8) != hipSuccess ||
         hipMalloc((void**)&lb.fin, (2 * cap + 2) * 4) != hipSuccess ||
         hipMalloc((void**)&lb.misc, 16) != hipSuccess ||
-        hipMalloc((void**)&lb.ids, (cap + 64) * 4) != hipSuccess) {
+        hipMalloc((void**)&lb.ids, (cap + 64) * 4) != hipSuccess ||
+        hipMalloc((void**)&lb.spans, (cap + 64) * 4) != hipSuccess) {
       (void)hipGetLastError();
       free_lit_bufs();
       return TOK_E_NOMEM;
@@ -269,8 +271,10 @@ struct tok_ctx {
   // Encode with the added-token literals: the literal pass, the pipeline
   // over the 2k + 1 parts (segment, literal, ..., segment) as documents whose
   // count the kernels read on the device, and the insertion of the literal
-  // IDs, all enqueued at once; one synchronization.
-  int run_added(const uint8_t* text, uint64_t n, int32_t* out, uint64_t out_cap, hipStream_t s, uint32_t* total) {
+  // IDs, all enqueued at once; one synchronization.  spans (optional): each
+  // ID's first byte.
+  int run_added(const uint8_t* text, uint64_t n, int32_t* out, uint64_t out_cap, hipStream_t s, uint32_t* total,
+                uint32_t* spans = nullptr) {
     int rc = ensure_lit_bufs();
     if (rc) return rc;
     volatile Counters* c = h_ctr;
@@ -278,8 +282,8 @@ struct tok_ctx {
     const uint64_t call = bb.gen = ++gen;
     bb.n_docs_dev = lb.misc + 2;
     launch_literal_pass(text, n, literals(), lb, d_ctr, call, s);
-    enqueue(text, n, lb.doc_off, 1, lb.ids, nullptr, n, lb.out_off, s, bb, true, nullptr);
-    launch_literal_insert(n, literals(), lb, out, out_cap, d_ctr, call, s);
+    enqueue(text, n, lb.doc_off, 1, lb.ids, spans ? lb.spans : nullptr, n, lb.out_off, s, bb, true, nullptr);
+    launch_literal_insert(n, literals(), lb, out, spans, out_cap, d_ctr, call, s);
     HIP_OK(hipGetLastError());
     HIP_OK(hipStreamSynchronize(s));
     if (prof) {

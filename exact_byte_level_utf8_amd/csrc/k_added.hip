@@ -25,6 +25,9 @@
 //                      literal part counts one ID; writes the literal IDs.
 //   lit_scatter_kernel every ID of a segment part to its final place; the IDs
 //                      the pipeline made from a literal's own bytes are dropped.
+// With span export the pipeline also gives each segment token's first byte
+// (counted from the start of the text, as the parts are), the literal's first
+// byte goes with its ID, and the scatter moves both.
 #include "tok_internal.h"
 #include "wg_scan.h"
 
@@ -141,7 +144,8 @@ lit_select_kernel(uint64_t n, uint32_t tiles, Literals L, LitBufs lb, Counters* 
 }
 
 __global__ void __launch_bounds__(kSelThreads)
-lit_insert_kernel(Literals L, LitBufs lb, int32_t* __restrict__ out, uint64_t cap, Counters* ctr, uint64_t gen) {
+lit_insert_kernel(Literals L, LitBufs lb, int32_t* __restrict__ out, uint32_t* __restrict__ spans, uint64_t cap,
+                  Counters* ctr, uint64_t gen) {
   __shared__ uint32_t s_scan[kSelThreads / kWave];
   const uint32_t k = lb.misc[1];
   const uint32_t tid = threadIdx.x, parts = 2 * k + 1;
@@ -155,7 +159,10 @@ lit_insert_kernel(Literals L, LitBufs lb, int32_t* __restrict__ out, uint64_t ca
     if (i < parts) {
       const uint32_t at = carry + ex;
       lb.fin[i] = at;
-      if ((i & 1u) && at < cap) out[at] = L.ids[(uint32_t)lb.sel[i >> 1]];
+      if ((i & 1u) && at < cap) {
+        out[at] = L.ids[(uint32_t)lb.sel[i >> 1]];
+        if (spans) spans[at] = (uint32_t)lb.doc_off[i];  // the literal starts its part
+      }
     }
     carry += tot;
   }
@@ -168,7 +175,7 @@ lit_insert_kernel(Literals L, LitBufs lb, int32_t* __restrict__ out, uint64_t ca
 }
 
 __global__ void __launch_bounds__(kScatterThreads)
-lit_scatter_kernel(LitBufs lb, int32_t* __restrict__ out, uint64_t cap) {
+lit_scatter_kernel(LitBufs lb, int32_t* __restrict__ out, uint32_t* __restrict__ spans, uint64_t cap) {
   const uint32_t parts = 2 * lb.misc[1] + 1;
   const uint32_t T = lb.misc[0];
   for (uint32_t t = blockIdx.x * kScatterThreads + threadIdx.x; t < T; t += gridDim.x * kScatterThreads) {
@@ -181,7 +188,10 @@ lit_scatter_kernel(LitBufs lb, int32_t* __restrict__ out, uint64_t cap) {
     }
     if (lo & 1u) continue;  // made from a literal's own bytes: replaced by its ID
     const uint64_t at = (uint64_t)lb.fin[lo] + (t - (uint32_t)lb.out_off[lo]);
-    if (at < cap) out[at] = lb.ids[t];
+    if (at < cap) {
+      out[at] = lb.ids[t];
+      if (spans) spans[at] = lb.spans[t];
+    }
   }
 }
 
@@ -194,11 +204,11 @@ void launch_literal_pass(const uint8_t* text, uint64_t n, Literals L, LitBufs lb
   lit_select_kernel<<<1, kSelThreads, 0, s>>>(n, tiles, L, lb, ctr, gen);
 }
 
-void launch_literal_insert(uint64_t n, Literals L, LitBufs lb, int32_t* out, uint64_t cap, Counters* ctr,
-                           uint64_t gen, hipStream_t s) {
-  lit_insert_kernel<<<1, kSelThreads, 0, s>>>(L, lb, out, cap, ctr, gen);
+void launch_literal_insert(uint64_t n, Literals L, LitBufs lb, int32_t* out, uint32_t* spans, uint64_t cap,
+                           Counters* ctr, uint64_t gen, hipStream_t s) {
+  lit_insert_kernel<<<1, kSelThreads, 0, s>>>(L, lb, out, spans, cap, ctr, gen);
   const uint32_t blocks = (uint32_t)std::min<uint64_t>((n + kScatterThreads - 1) / kScatterThreads, 8192);
-  lit_scatter_kernel<<<blocks, kScatterThreads, 0, s>>>(lb, out, cap);
+  lit_scatter_kernel<<<blocks, kScatterThreads, 0, s>>>(lb, out, spans, cap);
 }
 
 }  // namespace tok

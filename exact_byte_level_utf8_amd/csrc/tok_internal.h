@@ -170,6 +170,7 @@ struct LitBufs {
   uint32_t* fin;        // final output offset of each of those 2k + 1 parts
   uint32_t* misc;       // [0]: tokens the pipeline produced, [1]: literals taken k, [2]: parts 2k + 1
   int32_t* ids;         // the pipeline's output, before the literal IDs go in
+  uint32_t* spans;      // with span export: the first byte of each of those IDs
 };
 
 // Arguments of the device repair's match and splice (one workgroup).
@@ -199,8 +200,8 @@ constexpr uint32_t kLitMaxCount = 4096;
 // around the stage's kernel.
 void launch_literal_pass(const uint8_t* text, uint64_t n, Literals L, LitBufs lb, Counters* ctr, uint64_t gen,
                          hipStream_t s);
-void launch_literal_insert(uint64_t n, Literals L, LitBufs lb, int32_t* out, uint64_t cap, Counters* ctr,
-                           uint64_t gen, hipStream_t s);
+void launch_literal_insert(uint64_t n, Literals L, LitBufs lb, int32_t* out, uint32_t* spans, uint64_t cap,
+                           Counters* ctr, uint64_t gen, hipStream_t s);
 void launch_repair_match(const RepairArgs& a, hipStream_t s);
 void launch_empty_batch(Bufs b, const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s);
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,

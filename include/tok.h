@@ -307,8 +307,11 @@ int tok_sync_boundary(int pattern, uint32_t prev_cp, uint32_t cp);
  * literal pass and the insertion of the literal IDs run on the device in the
  * same stream as the pipeline (still one synchronization per call).
  * tok_repair then always encodes the whole text (its
- * splice certificate does not cover literals).  The batch and span calls
- * return TOK_E_UNSUPPORTED while literals are set.
+ * splice certificate does not cover literals).  Span export of one request
+ * (tok_encode_spans, tok_encode_spans_dev without document offsets) covers
+ * literals: a literal's span is its first byte.  The batch calls, and
+ * tok_encode_spans_dev with document offsets, return TOK_E_UNSUPPORTED while
+ * literals are set.
  *
  * Errors: TOK_E_ARG (null pointers, a length of 0 or over 64, a negative ID, a
  * repeated string, n > 4096), TOK_E_UTF8 (a literal is not well-formed UTF-8),

@@ -7,7 +7,9 @@ matches per tile), overlapping literal sets (the selection's ordered path),
 literals at the text's ends, back to back and across 1 KiB tiles, a 64-byte
 literal, one-byte and multibyte literals, text without any occurrence,
 capacity overflow, malformed UTF-8, invalid literal sets, removal, the calls
-that refuse literals, and the hand-worked cases of
+that refuse literals, span export with literals (token starts tile the text:
+the running sum of the token byte lengths, a literal counting its own
+length), and the hand-worked cases of
 tests/golden/added_tokens.json (tiny merge tables, run last).
 """
 import json
@@ -161,9 +163,6 @@ def test_no_occurrence_and_refusals(cfg):
         with pytest.raises(tk.TokError) as e:
             t.encode_batch(data, off)
         assert e.value.code == tk.TOK_E_UNSUPPORTED
-        with pytest.raises(tk.TokError) as e:
-            t.encode_spans(b"a<|endoftext|>")
-        assert e.value.code == tk.TOK_E_UNSUPPORTED
         # repair encodes the whole text and still equals the literal pass
         old = textgen.mix_text(22, 20_000) + "<|endoftext|>"
         new = old + "<|endoftext|> and more"
@@ -175,6 +174,43 @@ def test_no_occurrence_and_refusals(cfg):
     finally:
         t.set_added_tokens([])
     same("cleared", t.encode(b"a<|endoftext|>"), o.encode(b"a<|endoftext|>"))
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_spans_with_literals(cfg, name):
+    t, o, v = cfg[name]
+    lits = lits_from(MARKERS + ["§", "=>"], v)
+    tokb = vocab.token_bytes(vocab.merges(libs.CONFIGS[name][0]))
+    t.set_added_tokens(lits)
+    try:
+        for seed, n_chars in ((31, 300_000), (32, 5_000)):
+            b = textgen.chat_text(seed, n_chars, MARKERS).encode()
+            b = b.replace(b" = ", b" => ", 50).replace(b"a", "§".encode(), 30)
+            want = o.encode_added(b, lits)
+            lit_len = {i: len(x) for x, i in lits}
+            lens = np.asarray([lit_len[i] if i >= v else len(tokb[i]) for i in want], dtype=np.uint64)
+            want_sp = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.uint64)
+            assert int(lens.sum()) == len(b)
+            ids, sp = t.encode_spans(b)
+            same(f"{name} ids", ids, want)
+            same(f"{name} spans", sp.astype(np.uint64), want_sp)
+            d = torch.frombuffer(bytearray(b), dtype=torch.uint8).cuda()
+            d_ids = torch.full((len(b),), -7, dtype=torch.int32, device="cuda")
+            d_sp = torch.full((len(b),), -7, dtype=torch.int32, device="cuda")
+            n = t.encode_spans_dev(d, d_ids, d_sp)
+            torch.cuda.synchronize()
+            same(f"{name} dev ids", d_ids[:n].cpu().numpy(), want)
+            same(f"{name} dev spans", d_sp[:n].cpu().numpy().view(np.uint32).astype(np.uint64), want_sp)
+        data, off = textgen.pack_docs(["a<|im_end|>", "b"])
+        d = torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda()
+        d_off = torch.tensor(off.astype(np.int64), device="cuda").view(torch.uint64)
+        d_out = torch.zeros(len(off), dtype=torch.int64, device="cuda").view(torch.uint64)
+        d_ids = torch.empty(len(data), dtype=torch.int32, device="cuda")
+        with pytest.raises(tk.TokError) as e:
+            t.encode_spans_dev(d, d_ids, d_ids.clone(), d_off, d_out)
+        assert e.value.code == tk.TOK_E_UNSUPPORTED
+    finally:
+        t.set_added_tokens([])
 
 
 def test_invalid_literal_sets(cfg):
