@@ -136,7 +136,6 @@ const char* tok_strerror(int code) {
     case TOK_E_DEVICE: return "HIP device error";
     case TOK_E_NOMEM: return "out of memory";
     case TOK_E_SESSION: return "session IDs do not match the old text";
-    case TOK_E_UNSUPPORTED: return "call not supported with added-token literals set";
     default: return "unknown error";
   }
 }
@@ -266,7 +265,7 @@ int tok_encode_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, int32_t* d_i
   if (rc) return rc;
   hipStream_t s = stream ? (hipStream_t)stream : ctx->stream;
   uint32_t total = 0;
-  rc = ctx->n_lit ? ctx->run_added(d_text, len, d_ids, cap, s, &total)
+  rc = ctx->n_lit ? ctx->run_added(d_text, len, nullptr, 0, d_ids, cap, nullptr, s, &total)
                   : ctx->run(d_text, len, nullptr, 0, d_ids, nullptr, cap, nullptr, s, true, nullptr, &total);
   if (rc) return rc;
   *n_out = total;
@@ -286,7 +285,7 @@ int tok_encode(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids, size
   std::memcpy(ctx->h_text, text, len);
   HIP_OK(hipMemcpyAsync(ctx->d_text, ctx->h_text, len, hipMemcpyHostToDevice, s));
   uint32_t total = 0;
-  rc = ctx->n_lit ? ctx->run_added(ctx->d_text, len, ctx->d_ids, len, s, &total)
+  rc = ctx->n_lit ? ctx->run_added(ctx->d_text, len, nullptr, 0, ctx->d_ids, len, nullptr, s, &total)
                   : ctx->run(ctx->d_text, len, nullptr, 0, ctx->d_ids, nullptr, len, nullptr, s, true, nullptr, &total);
   if (rc) return rc;
   *n_out = total;
@@ -303,7 +302,6 @@ int tok_encode_batch_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
   if (!ctx || !n_out || !d_doc_off || !d_out_off || n_docs == 0 || n_docs >= 0xFFFFFFFFu ||
       (!d_text && len) || (!d_ids && cap))
     return TOK_E_ARG;
-  if (ctx->n_lit) return TOK_E_UNSUPPORTED;
   *n_out = 0;
   if (len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
   DeviceGuard g(ctx->device);
@@ -311,7 +309,9 @@ int tok_encode_batch_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
   if (rc) return rc;
   hipStream_t s = stream ? (hipStream_t)stream : ctx->stream;
   uint32_t total = 0;
-  rc = ctx->run(d_text, len, d_doc_off, (uint32_t)n_docs, d_ids, nullptr, cap, d_out_off, s, true, nullptr, &total);
+  rc = ctx->n_lit && len ? ctx->run_added(d_text, len, d_doc_off, (uint32_t)n_docs, d_ids, cap, d_out_off, s, &total)
+                         : ctx->run(d_text, len, d_doc_off, (uint32_t)n_docs, d_ids, nullptr, cap, d_out_off, s, true,
+                                    nullptr, &total);
   if (rc) return rc;
   *n_out = total;
   return total > cap ? TOK_E_CAPACITY : TOK_OK;
@@ -320,7 +320,6 @@ int tok_encode_batch_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
 int tok_encode_batch(tok_ctx* ctx, const uint8_t* text, const uint64_t* doc_off, size_t n_docs,
                      int32_t* ids, size_t cap, uint64_t* out_off) {
   if (!ctx || !doc_off || !out_off || n_docs == 0 || n_docs >= 0xFFFFFFFFu) return TOK_E_ARG;
-  if (ctx->n_lit) return TOK_E_UNSUPPORTED;
   if (doc_off[0] != 0) return TOK_E_ARG;
   for (size_t d = 0; d < n_docs; ++d)
     if (doc_off[d + 1] < doc_off[d]) return TOK_E_ARG;
@@ -341,8 +340,10 @@ int tok_encode_batch(tok_ctx* ctx, const uint8_t* text, const uint64_t* doc_off,
   std::memcpy(ctx->h_doc, doc_off, (n_docs + 1) * 8);
   HIP_OK(hipMemcpyAsync(ctx->d_doc, ctx->h_doc, (n_docs + 1) * 8, hipMemcpyHostToDevice, s));
   uint32_t total = 0;
-  rc = ctx->run(ctx->d_text, len, ctx->d_doc, (uint32_t)n_docs, ctx->d_ids, nullptr, len, ctx->d_outoff, s, true,
-                nullptr, &total);
+  rc = ctx->n_lit && len ? ctx->run_added(ctx->d_text, len, ctx->d_doc, (uint32_t)n_docs, ctx->d_ids, len,
+                                           ctx->d_outoff, s, &total)
+                         : ctx->run(ctx->d_text, len, ctx->d_doc, (uint32_t)n_docs, ctx->d_ids, nullptr, len,
+                                    ctx->d_outoff, s, true, nullptr, &total);
   if (rc) return rc;
   HIP_OK(hipMemcpyAsync(ctx->h_doc, ctx->d_outoff, (n_docs + 1) * 8, hipMemcpyDeviceToHost, s));
   if (total <= cap && total)
@@ -360,7 +361,6 @@ int tok_encode_spans_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
   if (!ctx || !n_out || (!d_text && len) || (cap && (!d_ids || !d_spans)) || n_docs >= 0xFFFFFFFFu ||
       (d_doc_off && (n_docs == 0 || !d_out_off)))
     return TOK_E_ARG;
-  if (ctx->n_lit && d_doc_off) return TOK_E_UNSUPPORTED;
   *n_out = 0;
   if (len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
   if (len == 0 && !d_doc_off) return TOK_OK;
@@ -369,7 +369,8 @@ int tok_encode_spans_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, const 
   if (rc) return rc;
   hipStream_t s = stream ? (hipStream_t)stream : ctx->stream;
   uint32_t total = 0;
-  rc = ctx->n_lit ? ctx->run_added(d_text, len, d_ids, cap, s, &total, d_spans)
+  rc = ctx->n_lit && len ? ctx->run_added(d_text, len, d_doc_off, d_doc_off ? (uint32_t)n_docs : 0, d_ids, cap,
+                                           d_doc_off ? d_out_off : nullptr, s, &total, d_spans)
                   : ctx->run(d_text, len, d_doc_off, d_doc_off ? (uint32_t)n_docs : 0, d_ids, d_spans, cap,
                              d_doc_off ? d_out_off : nullptr, s, true, nullptr, &total);
   if (rc) return rc;
@@ -392,7 +393,7 @@ int tok_encode_spans(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids
   std::memcpy(ctx->h_text, text, len);
   HIP_OK(hipMemcpyAsync(ctx->d_text, ctx->h_text, len, hipMemcpyHostToDevice, s));
   uint32_t total = 0;
-  rc = ctx->n_lit ? ctx->run_added(ctx->d_text, len, ctx->d_ids, len, s, &total, ctx->d_spans)
+  rc = ctx->n_lit ? ctx->run_added(ctx->d_text, len, nullptr, 0, ctx->d_ids, len, nullptr, s, &total, ctx->d_spans)
                   : ctx->run(ctx->d_text, len, nullptr, 0, ctx->d_ids, ctx->d_spans, len, nullptr, s, true, nullptr,
                              &total);
   if (rc) return rc;

@@ -118,7 +118,8 @@ struct tok_ctx {
   int32_t* d_lit_key1 = nullptr;
   uint32_t* d_lit_first = nullptr;
   LitBufs lb{};
-  uint64_t lit_cap = 0;  // input bytes lb covers
+  uint64_t lit_cap = 0;   // input bytes lb covers
+  uint64_t lit_docs = 0;  // documents lb covers
 
   // scratch, grown on demand
   uint64_t cap = 0;  // input bytes the scratch covers
@@ -232,31 +233,40 @@ struct tok_ctx {
     dfree(lb.tile_cnt);
     dfree(lb.tile_base);
     dfree(lb.sel);
-    dfree(lb.doc_off);
+    dfree(lb.cut);
+    dfree(lb.part_lit);
+    dfree(lb.doc_part);
     dfree(lb.out_off);
     dfree(lb.fin);
     dfree(lb.misc);
     dfree(lb.ids);
     dfree(lb.spans);
     lit_cap = 0;
+    lit_docs = 0;
   }
 
   Literals literals() const {
     return Literals{d_lit_bytes, d_lit_off, d_lit_ids, d_lit_key2, d_lit_order, d_lit_key1, d_lit_first, n_lit};
   }
 
-  // Buffers of the literal pass for the current capacity (after ensure()).
-  int ensure_lit_bufs() {
-    if (lit_cap == cap && lb.cand) return TOK_OK;
+  // Buffers of the literal pass for the current capacity and n_docs
+  // documents (after ensure()): at most cap literals, so at most n_docs +
+  // 2 cap parts.
+  int ensure_lit_bufs(uint64_t n_docs) {
+    if (lit_cap == cap && n_docs <= lit_docs && lb.cand) return TOK_OK;
     free_lit_bufs();
     const uint64_t tiles = cap / kLitTile;
+    const uint64_t docs = std::max<uint64_t>(next_pow2(n_docs), 64);
+    const uint64_t parts = docs + 2 * cap;
     if (hipMalloc((void**)&lb.cand, cap * 8) != hipSuccess ||
         hipMalloc((void**)&lb.tile_cnt, tiles * 4) != hipSuccess ||
         hipMalloc((void**)&lb.tile_base, tiles * 4) != hipSuccess ||
         hipMalloc((void**)&lb.sel, cap * 8) != hipSuccess ||
-        hipMalloc((void**)&lb.doc_off, (2 * cap + 2) * 8) != hipSuccess ||
-        hipMalloc((void**)&lb.out_off, (2 * cap + 2) * 8) != hipSuccess ||
-        hipMalloc((void**)&lb.fin, (2 * cap + 2) * 4) != hipSuccess ||
+        hipMalloc((void**)&lb.cut, (parts + 2) * 8) != hipSuccess ||
+        hipMalloc((void**)&lb.part_lit, (parts + 2) * 4) != hipSuccess ||
+        hipMalloc((void**)&lb.doc_part, (docs + 2) * 4) != hipSuccess ||
+        hipMalloc((void**)&lb.out_off, (parts + 2) * 8) != hipSuccess ||
+        hipMalloc((void**)&lb.fin, (parts + 2) * 4) != hipSuccess ||
         hipMalloc((void**)&lb.misc, 16) != hipSuccess ||
         hipMalloc((void**)&lb.ids, (cap + 64) * 4) != hipSuccess ||
         hipMalloc((void**)&lb.spans, (cap + 64) * 4) != hipSuccess) {
@@ -265,25 +275,27 @@ struct tok_ctx {
       return TOK_E_NOMEM;
     }
     lit_cap = cap;
+    lit_docs = docs;
     return TOK_OK;
   }
 
-  // Encode with the added-token literals: the literal pass, the pipeline
-  // over the 2k + 1 parts (segment, literal, ..., segment) as documents whose
-  // count the kernels read on the device, and the insertion of the literal
-  // IDs, all enqueued at once; one synchronization.  spans (optional): each
-  // ID's first byte.
-  int run_added(const uint8_t* text, uint64_t n, int32_t* out, uint64_t out_cap, hipStream_t s, uint32_t* total,
-                uint32_t* spans = nullptr) {
-    int rc = ensure_lit_bufs();
+  // Encode with the added-token literals: the literal pass (matches never
+  // cross a document boundary), the pipeline over the parts as documents
+  // whose count the kernels read on the device, and the insertion of the
+  // literal IDs, all enqueued at once; one synchronization.  doc_off /
+  // n_docs / out_off: the caller's documents and their output offsets, or
+  // nullptr for one request.  spans (optional): each ID's first byte.
+  int run_added(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, int32_t* out,
+                uint64_t out_cap, uint64_t* out_off, hipStream_t s, uint32_t* total, uint32_t* spans = nullptr) {
+    int rc = ensure_lit_bufs(doc_off ? n_docs : 1);
     if (rc) return rc;
     volatile Counters* c = h_ctr;
     Bufs bb = b;
     const uint64_t call = bb.gen = ++gen;
     bb.n_docs_dev = lb.misc + 2;
-    launch_literal_pass(text, n, literals(), lb, d_ctr, call, s);
-    enqueue(text, n, lb.doc_off, 1, lb.ids, spans ? lb.spans : nullptr, n, lb.out_off, s, bb, true, nullptr);
-    launch_literal_insert(n, literals(), lb, out, spans, out_cap, d_ctr, call, s);
+    launch_literal_pass(text, n, doc_off, n_docs, literals(), lb, d_ctr, call, s);
+    enqueue(text, n, lb.cut, 1, lb.ids, spans ? lb.spans : nullptr, n, lb.out_off, s, bb, true, nullptr);
+    launch_literal_insert(n, literals(), lb, out, spans, out_cap, out_off, d_ctr, call, s);
     HIP_OK(hipGetLastError());
     HIP_OK(hipStreamSynchronize(s));
     if (prof) {
@@ -293,7 +305,7 @@ struct tok_ctx {
         stage_ms[i] = ((prof >> i) & 1u) ? ms : 0.f;
       }
     }
-    if (c->err_docs == call) return TOK_E_DEVICE;  // the parts are well formed by construction
+    if (c->err_docs == call) return TOK_E_ARG;  // the caller's document offsets (the parts are well formed)
     if (c->err_utf8 == call) return TOK_E_UTF8;
     if (c->lit_done != call || c->done != call || c->ins_done != call) return TOK_E_DEVICE;
     *total = c->total;

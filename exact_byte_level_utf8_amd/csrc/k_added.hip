@@ -40,17 +40,24 @@ constexpr uint32_t kScatterThreads = 256;
 
 __device__ inline uint32_t lit_len(const Literals& L, uint32_t li) { return L.off[li + 1] - L.off[li]; }
 
-// The longest literal that starts at byte p of text[0, n), or -1.
-__device__ inline int32_t literal_at(const uint8_t* __restrict__ text, uint64_t n, uint64_t p, const Literals& L) {
+// The longest literal that starts at byte p of text[0, n) and ends by the end
+// of p's document, or -1.
+__device__ inline int32_t literal_at(const uint8_t* __restrict__ text, uint64_t n, uint64_t p, const Literals& L,
+                                     const uint64_t* __restrict__ doc_off, uint32_t n_docs) {
   const uint32_t b0 = text[p];
   if (!((L.first[b0 >> 5] >> (b0 & 31u)) & 1u)) return -1;
-  if (p + 1 < n) {
+  uint64_t lim = n;  // a literal never reaches into the next document
+  if (doc_off) {
+    const uint32_t d = first_doc_at_or_after(doc_off, n_docs, p + 1);
+    if (d <= n_docs) lim = min(lim, doc_off[d]);
+  }
+  if (p + 1 < lim) {
     const uint32_t e = L.key2[b0 | ((uint32_t)text[p + 1] << 8)];
     const uint32_t start = e >> 16, cnt = e & 0xFFFFu;
     for (uint32_t c = 0; c < cnt; ++c) {  // longest first: the first full match is the longest
       const uint32_t li = L.order[start + c];
       const uint32_t a = L.off[li], len = L.off[li + 1] - a;
-      if (p + len > n) continue;
+      if (p + len > lim) continue;
       uint32_t k = 2;
       while (k < len && text[p + k] == L.bytes[a + k]) ++k;
       if (k == len) return (int32_t)li;
@@ -60,7 +67,8 @@ __device__ inline int32_t literal_at(const uint8_t* __restrict__ text, uint64_t 
 }
 
 __global__ void __launch_bounds__(kMatchThreads)
-lit_match_kernel(const uint8_t* __restrict__ text, uint64_t n, Literals L, LitBufs lb) {
+lit_match_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off, uint32_t n_docs,
+                 Literals L, LitBufs lb) {
   __shared__ uint32_t s_scan[kMatchThreads / kWave];
   const uint32_t tile = blockIdx.x, tid = threadIdx.x;
   const uint64_t p0 = (uint64_t)tile * kLitTile + 4u * tid;
@@ -68,7 +76,7 @@ lit_match_kernel(const uint8_t* __restrict__ text, uint64_t n, Literals L, LitBu
   uint32_t c = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    m[j] = p0 + j < n ? literal_at(text, n, p0 + j, L) : -1;
+    m[j] = p0 + j < n ? literal_at(text, n, p0 + j, L, doc_off, n_docs) : -1;
     c += m[j] >= 0 ? 1u : 0u;
   }
   uint32_t tot = 0;
@@ -81,11 +89,22 @@ lit_match_kernel(const uint8_t* __restrict__ text, uint64_t n, Literals L, LitBu
 }
 
 __global__ void __launch_bounds__(kSelThreads)
-lit_select_kernel(uint64_t n, uint32_t tiles, Literals L, LitBufs lb, Counters* ctr, uint64_t gen) {
+lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_off, uint32_t n_docs, Literals L,
+                  LitBufs lb, Counters* ctr, uint64_t gen) {
   __shared__ uint32_t s_scan[kSelThreads / kWave];
-  __shared__ uint32_t s_over, s_kept;
+  __shared__ uint32_t s_over, s_kept, s_bad;
   const uint32_t tid = threadIdx.x;
-  if (tid == 0) s_over = 0;
+  if (tid == 0) {
+    s_over = 0;
+    s_bad = 0;
+  }
+  // the caller's documents (one document [0, n) without offsets): the
+  // pipeline sees only the parts, so their offsets are checked here
+  const uint32_t nd = doc_off ? n_docs : 1u;
+  auto D = [&](uint32_t d) -> uint64_t { return doc_off ? doc_off[d] : (d == 0 ? 0ull : n); };
+  bool bad = false;
+  for (uint32_t d = tid; d < nd; d += kSelThreads) bad |= D(d) > D(d + 1);
+  if (tid == 0) bad |= D(0) != 0 || D(nd) != n;
   // matches before each tile (uniform trip count: the scan holds barriers)
   uint32_t carry = 0;
   for (uint32_t t0 = 0; t0 < tiles; t0 += kSelThreads) {
@@ -96,6 +115,7 @@ lit_select_kernel(uint64_t n, uint32_t tiles, Literals L, LitBufs lb, Counters* 
     if (t < tiles) lb.tile_base[t] = carry + ex;
     carry += tot;
   }
+  if (bad) s_bad = 1u;
   const uint32_t K = carry;
   __syncthreads();
   for (uint32_t t = tid; t < tiles; t += kSelThreads) {
@@ -110,8 +130,11 @@ lit_select_kernel(uint64_t n, uint32_t tiles, Literals L, LitBufs lb, Counters* 
   }
   if (over) s_over = 1u;
   __syncthreads();
-  uint32_t k = K;
-  if (s_over) {  // uniform: an LDS word read after a barrier
+  // malformed offsets: report, and fall back to one part with no literal
+  // (the call fails; everything below stays in bounds)
+  const bool bad_docs = s_bad != 0;
+  uint32_t k = bad_docs ? 0u : K;
+  if (!bad_docs && s_over) {  // uniform: LDS words read after a barrier
     if (tid == 0) {
       uint64_t end = 0;
       uint32_t w = 0;
@@ -127,17 +150,57 @@ lit_select_kernel(uint64_t n, uint32_t tiles, Literals L, LitBufs lb, Counters* 
     __syncthreads();
     k = s_kept;
   }
-  for (uint32_t i = tid; i < k; i += kSelThreads) {
-    const uint64_t a = lb.sel[i];
-    lb.doc_off[2 * i + 1] = a >> 32;
-    lb.doc_off[2 * i + 2] = (a >> 32) + lit_len(L, (uint32_t)a);
+  // cut points: the document boundaries merged with each literal's start and
+  // end.  A boundary comes before a literal starting on it and after a
+  // literal ending on it; literals never straddle a boundary.
+  //   index of start j = 2j + #{d : D(d) <= S_j}
+  //   index of end j   = 2j + 1 + #{d : D(d) < E_j}
+  //   index of D(d)    = d + 2 #{j : S_j < D(d)}
+  const uint32_t nb = bad_docs ? 1u : nd;  // boundaries 0..nb
+  auto Db = [&](uint32_t d) -> uint64_t { return bad_docs ? (d == 0 ? 0ull : n) : D(d); };
+  const uint32_t parts = nb + 2 * k;
+  for (uint32_t i = tid; i < parts; i += kSelThreads) lb.part_lit[i] = -1;
+  __syncthreads();
+  for (uint32_t j = tid; j < k; j += kSelThreads) {
+    const uint64_t a = lb.sel[j];
+    const uint64_t S = a >> 32, E = S + lit_len(L, (uint32_t)a);
+    uint32_t lo = 0, hi = nb + 1;  // #{d : D(d) <= S}
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (Db(mid) <= S) lo = mid + 1;
+      else hi = mid;
+    }
+    const uint32_t is = 2 * j + lo;
+    lo = 0;
+    hi = nb + 1;  // #{d : D(d) < E}
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (Db(mid) < E) lo = mid + 1;
+      else hi = mid;
+    }
+    const uint32_t ie = 2 * j + 1 + lo;
+    lb.cut[is] = S;
+    lb.cut[ie] = E;
+    lb.part_lit[is] = (int32_t)j;
+  }
+  for (uint32_t d = tid; d <= nb; d += kSelThreads) {
+    const uint64_t x = Db(d);
+    uint32_t lo = 0, hi = k;  // #{j : S_j < x}
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if ((lb.sel[mid] >> 32) < x) lo = mid + 1;
+      else hi = mid;
+    }
+    const uint32_t id = d + 2 * lo;
+    lb.cut[id] = x;
+    lb.doc_part[d] = id;
   }
   if (tid == 0) {
-    lb.doc_off[0] = 0;
-    lb.doc_off[2 * (uint64_t)k + 1] = n;
     lb.misc[1] = k;
-    lb.misc[2] = 2 * k + 1;  // the parts, read by the pipeline as its document count
+    lb.misc[2] = parts;  // read by the pipeline as its document count
+    lb.misc[3] = nb;
     ctr->lits = k;
+    if (bad_docs) report(&ctr->err_docs, gen);
     __threadfence_system();
     report(&ctr->lit_done, gen);
   }
@@ -145,27 +208,32 @@ lit_select_kernel(uint64_t n, uint32_t tiles, Literals L, LitBufs lb, Counters* 
 
 __global__ void __launch_bounds__(kSelThreads)
 lit_insert_kernel(Literals L, LitBufs lb, int32_t* __restrict__ out, uint32_t* __restrict__ spans, uint64_t cap,
-                  Counters* ctr, uint64_t gen) {
+                  uint64_t* __restrict__ out_off, Counters* ctr, uint64_t gen) {
   __shared__ uint32_t s_scan[kSelThreads / kWave];
-  const uint32_t k = lb.misc[1];
-  const uint32_t tid = threadIdx.x, parts = 2 * k + 1;
+  const uint32_t tid = threadIdx.x, parts = lb.misc[2], nb = lb.misc[3];
   uint32_t carry = 0;
   for (uint32_t i0 = 0; i0 < parts; i0 += kSelThreads) {
     const uint32_t i = i0 + tid;
+    const int32_t lj = i < parts ? lb.part_lit[i] : -1;
     uint32_t v = 0;
-    if (i < parts) v = (i & 1u) ? 1u : (uint32_t)(lb.out_off[i + 1] - lb.out_off[i]);
+    if (i < parts) v = lj >= 0 ? 1u : (uint32_t)(lb.out_off[i + 1] - lb.out_off[i]);
     uint32_t tot = 0;
     const uint32_t ex = wg_excl_scan<kSelThreads>(v, 0u, AddOp(), s_scan, &tot);
     if (i < parts) {
       const uint32_t at = carry + ex;
       lb.fin[i] = at;
-      if ((i & 1u) && at < cap) {
-        out[at] = L.ids[(uint32_t)lb.sel[i >> 1]];
-        if (spans) spans[at] = (uint32_t)lb.doc_off[i];  // the literal starts its part
+      if (lj >= 0 && at < cap) {
+        out[at] = L.ids[(uint32_t)lb.sel[lj]];
+        if (spans) spans[at] = (uint32_t)lb.cut[i];  // the literal starts its part
       }
     }
     carry += tot;
   }
+  if (tid == 0) lb.fin[parts] = carry;
+  __syncthreads();
+  // each document's output offset: that of its first part
+  if (out_off)
+    for (uint32_t d = tid; d <= nb; d += kSelThreads) out_off[d] = lb.fin[lb.doc_part[d]];
   if (tid == 0) {
     lb.misc[0] = (uint32_t)lb.out_off[parts];
     ctr->total = carry;
@@ -176,7 +244,7 @@ lit_insert_kernel(Literals L, LitBufs lb, int32_t* __restrict__ out, uint32_t* _
 
 __global__ void __launch_bounds__(kScatterThreads)
 lit_scatter_kernel(LitBufs lb, int32_t* __restrict__ out, uint32_t* __restrict__ spans, uint64_t cap) {
-  const uint32_t parts = 2 * lb.misc[1] + 1;
+  const uint32_t parts = lb.misc[2];
   const uint32_t T = lb.misc[0];
   for (uint32_t t = blockIdx.x * kScatterThreads + threadIdx.x; t < T; t += gridDim.x * kScatterThreads) {
     // the part holding pipeline token t: the last i with out_off[i] <= t
@@ -186,7 +254,7 @@ lit_scatter_kernel(LitBufs lb, int32_t* __restrict__ out, uint32_t* __restrict__
       if (lb.out_off[mid] <= t) lo = mid;
       else hi = mid - 1;
     }
-    if (lo & 1u) continue;  // made from a literal's own bytes: replaced by its ID
+    if (lb.part_lit[lo] >= 0) continue;  // made from a literal's own bytes: replaced by its ID
     const uint64_t at = (uint64_t)lb.fin[lo] + (t - (uint32_t)lb.out_off[lo]);
     if (at < cap) {
       out[at] = lb.ids[t];
@@ -197,16 +265,16 @@ lit_scatter_kernel(LitBufs lb, int32_t* __restrict__ out, uint32_t* __restrict__
 
 }  // namespace
 
-void launch_literal_pass(const uint8_t* text, uint64_t n, Literals L, LitBufs lb, Counters* ctr, uint64_t gen,
-                         hipStream_t s) {
+void launch_literal_pass(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, Literals L,
+                         LitBufs lb, Counters* ctr, uint64_t gen, hipStream_t s) {
   const uint32_t tiles = (uint32_t)((n + kLitTile - 1) / kLitTile);
-  lit_match_kernel<<<tiles, kMatchThreads, 0, s>>>(text, n, L, lb);
-  lit_select_kernel<<<1, kSelThreads, 0, s>>>(n, tiles, L, lb, ctr, gen);
+  lit_match_kernel<<<tiles, kMatchThreads, 0, s>>>(text, n, doc_off, n_docs, L, lb);
+  lit_select_kernel<<<1, kSelThreads, 0, s>>>(n, tiles, doc_off, n_docs, L, lb, ctr, gen);
 }
 
 void launch_literal_insert(uint64_t n, Literals L, LitBufs lb, int32_t* out, uint32_t* spans, uint64_t cap,
-                           Counters* ctr, uint64_t gen, hipStream_t s) {
-  lit_insert_kernel<<<1, kSelThreads, 0, s>>>(L, lb, out, spans, cap, ctr, gen);
+                           uint64_t* out_off, Counters* ctr, uint64_t gen, hipStream_t s) {
+  lit_insert_kernel<<<1, kSelThreads, 0, s>>>(L, lb, out, spans, cap, out_off, ctr, gen);
   const uint32_t blocks = (uint32_t)std::min<uint64_t>((n + kScatterThreads - 1) / kScatterThreads, 8192);
   lit_scatter_kernel<<<blocks, kScatterThreads, 0, s>>>(lb, out, spans, cap);
 }

@@ -311,7 +311,7 @@ int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_
   std::memcpy(ctx->h_text, text, new_len);
   HIP_OK(hipMemcpyAsync(ctx->d_text, ctx->h_text, new_len, hipMemcpyHostToDevice, s));
   uint32_t total = 0;
-  rc = ctx->n_lit ? ctx->run_added(ctx->d_text, new_len, ctx->d_ids, new_len, s, &total)
+  rc = ctx->n_lit ? ctx->run_added(ctx->d_text, new_len, nullptr, 0, ctx->d_ids, new_len, nullptr, s, &total)
                   : ctx->run(ctx->d_text, new_len, nullptr, 0, ctx->d_ids, nullptr, new_len, nullptr, s, true, nullptr,
                              &total);
   if (rc) return rc;

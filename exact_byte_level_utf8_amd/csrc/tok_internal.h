@@ -159,19 +159,27 @@ struct Literals {
   uint32_t n;
 };
 
-// Per-call buffers of the literal pass (sized by the context's capacity).
+// Per-call buffers of the literal pass (sized by the context's capacity and
+// document count).  The k taken literals cut the caller's documents into
+// parts: each literal is a part, and so is each stretch between two cuts.
 struct LitBufs {
   uint64_t* cand;       // per tile: up to kLitTile (position << 32 | literal) in position order
   uint32_t* tile_cnt;   // candidates found in each tile
   uint32_t* tile_base;  // candidates before each tile
   uint64_t* sel;        // taken literals, in order
-  uint64_t* doc_off;    // 2k + 2 offsets: segment, literal, segment, ..., segment
-  uint64_t* out_off;    // their output offsets from the pipeline
-  uint32_t* fin;        // final output offset of each of those 2k + 1 parts
-  uint32_t* misc;       // [0]: tokens the pipeline produced, [1]: literals taken k, [2]: parts 2k + 1
+  uint64_t* cut;        // parts + 1 cut points: document boundaries, literal starts and ends, merged
+  int32_t* part_lit;    // per part: the taken literal it is, or -1
+  uint32_t* doc_part;   // per document boundary: its index among the cut points
+  uint64_t* out_off;    // the parts' output offsets from the pipeline
+  uint32_t* fin;        // final output offset of each part (and the total)
+  uint32_t* misc;       // [0] tokens the pipeline produced, [1] literals taken k, [2] parts, [3] documents
   int32_t* ids;         // the pipeline's output, before the literal IDs go in
   uint32_t* spans;      // with span export: the first byte of each of those IDs
 };
+
+constexpr int kLitTile = 1024;  // bytes per workgroup of the literal match
+constexpr int kLitMax = 64;     // longest added-token literal, bytes
+constexpr uint32_t kLitMaxCount = 4096;
 
 // Arguments of the device repair's match and splice (one workgroup).
 struct RepairArgs {
@@ -192,16 +200,12 @@ struct RepairArgs {
   uint64_t gen;
 };
 
-constexpr int kLitTile = 1024;  // bytes per workgroup of the literal match
-constexpr int kLitMax = 64;     // longest added-token literal, bytes
-constexpr uint32_t kLitMaxCount = 4096;
-
 // Kernel launchers (defined in the .hip files); e0 / e1: optional events
 // around the stage's kernel.
-void launch_literal_pass(const uint8_t* text, uint64_t n, Literals L, LitBufs lb, Counters* ctr, uint64_t gen,
-                         hipStream_t s);
+void launch_literal_pass(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, Literals L,
+                         LitBufs lb, Counters* ctr, uint64_t gen, hipStream_t s);
 void launch_literal_insert(uint64_t n, Literals L, LitBufs lb, int32_t* out, uint32_t* spans, uint64_t cap,
-                           Counters* ctr, uint64_t gen, hipStream_t s);
+                           uint64_t* out_off, Counters* ctr, uint64_t gen, hipStream_t s);
 void launch_repair_match(const RepairArgs& a, hipStream_t s);
 void launch_empty_batch(Bufs b, const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s);
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,

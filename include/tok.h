@@ -60,7 +60,6 @@ typedef struct tok_ctx tok_ctx;
 #define TOK_E_DEVICE 7     /* a HIP runtime call failed                     */
 #define TOK_E_NOMEM 8      /* device or pinned host allocation failed       */
 #define TOK_E_SESSION 9    /* repair: stored IDs do not spell the old text  */
-#define TOK_E_UNSUPPORTED 10 /* call not supported with added-token literals */
 
 /* Pre-tokenizer families. */
 #define TOK_PAT_GPT2 0   /* 's|'t|'re|'ve|'m|'ll|'d| ?L+| ?N+| ?[^\s L N]+|\s+(?!\S)|\s+ */
@@ -298,7 +297,7 @@ int tok_sync_boundary(int pattern, uint32_t prev_cp, uint32_t cp);
  * above the vocabulary size).  Each literal is 1..64 bytes of well-formed
  * UTF-8; no string twice; n <= 4096.  n = 0 removes the literals.
  *
- * Afterwards tok_encode and tok_encode_dev scan the text left to right: at the
+ * Afterwards every encode call scans the text left to right: at the
  * first position where some literal matches, the longest one there is taken
  * and its ID emitted, and the scan goes on after it; each segment between
  * taken literals is encoded as a request of its own (its pieces and merges
@@ -307,11 +306,9 @@ int tok_sync_boundary(int pattern, uint32_t prev_cp, uint32_t cp);
  * literal pass and the insertion of the literal IDs run on the device in the
  * same stream as the pipeline (still one synchronization per call).
  * tok_repair then always encodes the whole text (its
- * splice certificate does not cover literals).  Span export of one request
- * (tok_encode_spans, tok_encode_spans_dev without document offsets) covers
- * literals: a literal's span is its first byte.  The batch calls, and
- * tok_encode_spans_dev with document offsets, return TOK_E_UNSUPPORTED while
- * literals are set.
+ * splice certificate does not cover literals).  The batch calls apply the
+ * pass within each document (a literal never spans two documents), and span
+ * export covers literals (a literal's span is its first byte).
  *
  * Errors: TOK_E_ARG (null pointers, a length of 0 or over 64, a negative ID, a
  * repeated string, n > 4096), TOK_E_UTF8 (a literal is not well-formed UTF-8),

@@ -6,8 +6,9 @@ the 1M-character size, literals that also occur inside ordinary code (many
 matches per tile), overlapping literal sets (the selection's ordered path),
 literals at the text's ends, back to back and across 1 KiB tiles, a 64-byte
 literal, one-byte and multibyte literals, text without any occurrence,
-capacity overflow, malformed UTF-8, invalid literal sets, removal, the calls
-that refuse literals, span export with literals (token starts tile the text:
+capacity overflow, malformed UTF-8, invalid literal sets, removal, batches
+(literals within each document, never across a boundary; per-document
+offsets; spans), span export with literals (token starts tile the text:
 the running sum of the token byte lengths, a literal counting its own
 length), and the hand-worked cases of
 tests/golden/added_tokens.json (tiny merge tables, run last).
@@ -152,17 +153,13 @@ def test_edges(cfg):
         t.set_added_tokens([])
 
 
-def test_no_occurrence_and_refusals(cfg):
+def test_no_occurrence_and_repair(cfg):
     t, o, v = cfg["gpt2"]
     b = textgen.mix_text(21, 200_000).encode()
     lits = lits_from(["<|endoftext|>"], v)
     t.set_added_tokens(lits)
     try:
         same("no occurrence", dev_encode(t, b), o.encode(b))
-        data, off = textgen.pack_docs(["a<|endoftext|>", "b"])
-        with pytest.raises(tk.TokError) as e:
-            t.encode_batch(data, off)
-        assert e.value.code == tk.TOK_E_UNSUPPORTED
         # repair encodes the whole text and still equals the literal pass
         old = textgen.mix_text(22, 20_000) + "<|endoftext|>"
         new = old + "<|endoftext|> and more"
@@ -201,14 +198,6 @@ def test_spans_with_literals(cfg, name):
             torch.cuda.synchronize()
             same(f"{name} dev ids", d_ids[:n].cpu().numpy(), want)
             same(f"{name} dev spans", d_sp[:n].cpu().numpy().view(np.uint32).astype(np.uint64), want_sp)
-        data, off = textgen.pack_docs(["a<|im_end|>", "b"])
-        d = torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda()
-        d_off = torch.tensor(off.astype(np.int64), device="cuda").view(torch.uint64)
-        d_out = torch.zeros(len(off), dtype=torch.int64, device="cuda").view(torch.uint64)
-        d_ids = torch.empty(len(data), dtype=torch.int32, device="cuda")
-        with pytest.raises(tk.TokError) as e:
-            t.encode_spans_dev(d, d_ids, d_ids.clone(), d_off, d_out)
-        assert e.value.code == tk.TOK_E_UNSUPPORTED
     finally:
         t.set_added_tokens([])
 
@@ -222,6 +211,91 @@ def test_invalid_literal_sets(cfg):
             t.set_added_tokens(bad)
         assert e.value.code == code, bad
     same("nothing set", t.encode(b"ab"), o.encode(b"ab"))
+
+
+BATCH_DOCS = ["", "a<|im_end|>", "<|im_start|>user\nhi", "", "<|im", "_end|>tail", "x" * 5000 + "<|im_sep|>",
+              "<|endoftext|>", "<|endoftext|><|endoftext|>", "§=>§", "no literal here", "", "<|tool_call|>"]
+
+
+def batch_expect(o, docs, lits, v, tokb):
+    ids, spans, out_off = [], [], [0]
+    lit_len = {i: len(x) for x, i in lits}
+    base = 0
+    for dtext in docs:
+        b = dtext.encode()
+        got = o.encode_added(b, lits).tolist()
+        lens = [lit_len[i] if i >= v else len(tokb[i]) for i in got]
+        at = base
+        for L in lens:
+            spans.append(at)
+            at += L
+        assert at == base + len(b)
+        ids += got
+        out_off.append(len(ids))
+        base += len(b)
+    return np.asarray(ids, dtype=np.int32), np.asarray(spans, dtype=np.uint64), np.asarray(out_off, dtype=np.uint64)
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_batch_with_literals(cfg, name):
+    """Each document gets its own literal pass: "<|im" + "_end|>" in two
+    documents is no literal; per-document output offsets and spans as the
+    oracle's per-document encode."""
+    t, o, v = cfg[name]
+    lits = lits_from(MARKERS + ["§", "=>"], v)
+    tokb = vocab.token_bytes(vocab.merges(libs.CONFIGS[name][0]))
+    docs = BATCH_DOCS + [textgen.chat_text(60 + i, 6000 + 977 * i, MARKERS) for i in range(5)] + [""]
+    data, off = textgen.pack_docs(docs)
+    want_ids, want_sp, want_off = batch_expect(o, docs, lits, v, tokb)
+    t.set_added_tokens(lits)
+    try:
+        ids, out_off = t.encode_batch(data, off)
+        same(f"{name} batch out_off", out_off, want_off)
+        same(f"{name} batch ids", ids, want_ids)
+        d = torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda()
+        d_off = torch.tensor(off.astype(np.int64), device="cuda").view(torch.uint64)
+        d_out = torch.zeros(len(off), dtype=torch.int64, device="cuda").view(torch.uint64)
+        d_ids = torch.full((len(data),), -7, dtype=torch.int32, device="cuda")
+        n = t.encode_batch_dev(d, d_off, d_ids, d_out)
+        torch.cuda.synchronize()
+        same(f"{name} batch dev ids", d_ids[:n].cpu().numpy(), want_ids)
+        same(f"{name} batch dev out_off", d_out.view(torch.int64).cpu().numpy().astype(np.uint64), want_off)
+        d_sp = torch.full((len(data),), -7, dtype=torch.int32, device="cuda")
+        d_out.zero_()
+        n = t.encode_spans_dev(d, d_ids, d_sp, d_off, d_out)
+        torch.cuda.synchronize()
+        same(f"{name} batch spans ids", d_ids[:n].cpu().numpy(), want_ids)
+        same(f"{name} batch spans", d_sp[:n].cpu().numpy().view(np.uint32).astype(np.uint64), want_sp)
+        same(f"{name} batch spans out_off", d_out.view(torch.int64).cpu().numpy().astype(np.uint64), want_off)
+        # malformed offsets are rejected on the device
+        bad = torch.tensor(np.asarray([0, 5, 3, len(data)], dtype=np.int64), device="cuda").view(torch.uint64)
+        with pytest.raises(tk.TokError) as e:
+            t.encode_batch_dev(d, bad, d_ids, torch.zeros(4, dtype=torch.int64, device="cuda").view(torch.uint64))
+        assert e.value.code == tk.TOK_E_ARG
+    finally:
+        t.set_added_tokens([])
+
+
+def test_batch_workload_with_literals(cfg):
+    """64 chat transcripts of 200,000 characters in one batch call: sampled
+    documents equal the oracle; every document's IDs cover its bytes."""
+    t, o, v = cfg["llama3"]
+    lits = lits_from(MARKERS, v)
+    tokb = vocab.token_bytes(vocab.merges(libs.CONFIGS["llama3"][0]))
+    docs = [textgen.chat_text(7000 + i, 200_000, MARKERS) for i in range(64)]
+    data, off = textgen.pack_docs(docs)
+    t.set_added_tokens(lits)
+    try:
+        ids, out_off = t.encode_batch(data, off)
+    finally:
+        t.set_added_tokens([])
+    lit_len = {i: len(x) for x, i in lits}
+    lens = np.asarray([lit_len[i] if i >= v else len(tokb[i]) for i in ids.tolist()], dtype=np.int64)
+    doc_bytes = np.add.reduceat(lens, out_off[:-1].astype(np.int64))
+    assert np.array_equal(doc_bytes, np.diff(off.astype(np.int64)))
+    for i in (0, 33, 63):
+        a, z = int(out_off[i]), int(out_off[i + 1])
+        same(f"doc {i}", ids[a:z], o.encode_added(docs[i].encode(), lits))
 
 
 def test_hand_worked_cases():
