@@ -15,8 +15,9 @@ Also reported, outside the headline value:
     warm-up steps time every stage to find it and give stages_ms), against the
     8 TB/s HBM peak, with the counter-measured HBM traffic of that kernel from
     the committed rocprofv3 summary when it matches the kernel's sources;
-  - complete_call: host bytes -> host int32 IDs through tok_encode (pinned
-    staging, both transfers), the PCIe-inclusive rate;
+  - complete_call: host bytes -> host int32 IDs through tok_encode (or
+    tok_encode_batch for the batch; pinned staging, both transfers), the
+    PCIe-inclusive rate;
   - graph_ab: median call time without stage timing, eager launches against
     a replayed HIP graph of the same call (tok_set_graph);
   - fresh_inputs: median call time over distinct seeded requests of the same
@@ -110,9 +111,10 @@ def measured_traffic(workload: str, stage: str):
     return profiled(workload, stage, "bytes_per_launch")
 
 
-# VALU issue peak: 256 CUs x 4 SIMDs, each SIMD issuing one wave64 vector
-# instruction per 4 cycles (16 lanes per cycle) at 2.4 GHz
-VALU_PEAK_G = 256 * 4 * 2.4e9 / 4 / 1e9
+# VALU issue peak: the published fp32 vector peak, 157.3 TFLOP/s = 256 CUs x
+# 4 SIMDs x 32 lanes x 2 flops (FMA) x 2.4 GHz, is one wave64 instruction per
+# 2 cycles per SIMD: 1228.8 G wave64 instructions/s
+VALU_PEAK_G = 256 * 4 * 2.4e9 / 2 / 1e9
 
 
 def valu_issue(workload: str, stage: str, avg_ms: float):
@@ -298,17 +300,15 @@ def main() -> int:
 
     # complete call: host bytes in, host IDs out
     cc = []
-    if doc_off is None:
-        for i in range(max(5, args.steps // 5)):
-            s0 = time.perf_counter()
-            ids_host = tok.encode(text)
-            cc.append(time.perf_counter() - s0)
-        assert len(ids_host) == n_tokens
-    complete = None
-    if cc:
-        med = statistics.median(cc)
-        complete = {"p50_ms": round(1e3 * med, 4), "mbps": round(n_bytes / med / 1e6, 1),
-                    "note": "tok_encode: pinned staging + H2D text + pipeline + D2H IDs"}
+    for i in range(max(5, args.steps // 5)):
+        s0 = time.perf_counter()
+        ids_host = tok.encode(text) if doc_off is None else tok.encode_batch(text, doc_off)[0]
+        cc.append(time.perf_counter() - s0)
+    assert len(ids_host) == n_tokens
+    med = statistics.median(cc)
+    call = "tok_encode" if doc_off is None else "tok_encode_batch"
+    complete = {"p50_ms": round(1e3 * med, 4), "mbps": round(n_bytes / med / 1e6, 1),
+                "note": f"{call}: pinned staging + H2D text + pipeline + D2H IDs"}
 
     # graph replay A/B (outside the timed region): the same step without stage
     # timing, three launches per call against one replayed graph per call

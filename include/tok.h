@@ -196,7 +196,8 @@ int tok_encode_spans(tok_ctx* ctx, const uint8_t* text, size_t len, int32_t* ids
  * uint16 per 16-byte chunk of d_text to d_flags (ceil(len / 16) words on the
  * device): bit i of word c is set iff byte 16c + i starts a piece.  A
  * document start always starts a piece.  d_doc_off / n_docs as in
- * tok_encode_batch_dev, or NULL / 0 for one document.
+ * tok_encode_batch_dev, or NULL / 0 for one document.  Added-token literals
+ * are not applied here: this is the pattern's stage alone.
  */
 int tok_pretokenize_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len,
                         const uint64_t* d_doc_off, size_t n_docs, uint16_t* d_flags, void* stream);
