@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -72,3 +73,11 @@ def test_null_arguments():
     assert L.tok_encode_spans(None, None, 0, None, None, 0, ctypes.byref(n)) == tk.TOK_E_ARG
     assert L.tok_encode_spans_dev(None, None, 0, None, 0, None, None, 0, None, ctypes.byref(n), None) == tk.TOK_E_ARG
     L.tok_free(None)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus 2 exits with a message and no work."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
