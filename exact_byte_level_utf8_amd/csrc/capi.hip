@@ -483,6 +483,7 @@ int tok_set_added_tokens(tok_ctx* ctx, const uint8_t* bytes, const uint64_t* off
     blob.insert(blob.end(), lit[i].begin(), lit[i].end());
     loff[i + 1] = (uint32_t)blob.size();
   }
+  blob.resize(blob.size() + 72, 0);  // the match kernel reads whole words up to 8 bytes past a literal
   if (hipMalloc((void**)&ctx->d_lit_bytes, blob.size()) != hipSuccess ||
       hipMalloc((void**)&ctx->d_lit_off, loff.size() * 4) != hipSuccess ||
       hipMalloc((void**)&ctx->d_lit_ids, n * 4) != hipSuccess ||

@@ -5,11 +5,13 @@
 // section 4 "Design": a device lookup first finds the literals, emits their
 // IDs directly and passes only the unmatched regions to the family predicate).
 //
-//   lit_match_kernel   one 1 KiB tile per workgroup: at every byte, the
-//                      longest literal that starts there (a 256-bit first-byte
-//                      mask rejects most bytes at once; candidates of two or
-//                      more bytes are grouped by their first two bytes, longest
-//                      first); each tile writes its matches in position order.
+//   lit_match_kernel   one 1 KiB tile per workgroup, its bytes staged in LDS: at
+//                      every byte, the longest literal that starts there (a
+//                      256-bit first-byte mask in LDS rejects most bytes at
+//                      once; candidates of two or more bytes are grouped by
+//                      their first two bytes, longest first, and compared a
+//                      word at a time); each tile writes its matches in
+//                      position order.
 //   lit_select_kernel  one workgroup: the matches of all tiles in order; when
 //                      no match overlaps the next one every match is taken,
 //                      else one lane keeps, in order, each match that starts at
@@ -40,27 +42,44 @@ constexpr uint32_t kScatterThreads = 256;
 
 __device__ inline uint32_t lit_len(const Literals& L, uint32_t li) { return L.off[li + 1] - L.off[li]; }
 
+// Bytes b .. b + 3 of a byte array held as words (little endian), from two
+// aligned word reads.
+__device__ inline uint32_t bytes_at(const uint32_t* w, uint32_t b) {
+  return __builtin_amdgcn_alignbyte(w[(b >> 2) + 1], w[b >> 2], b & 3u);
+}
+
 // The longest literal that starts at byte p of text[0, n) and ends by the end
-// of p's document, or -1.
-__device__ inline int32_t literal_at(const uint8_t* __restrict__ text, uint64_t n, uint64_t p, const Literals& L,
-                                     const uint64_t* __restrict__ doc_off, uint32_t n_docs) {
-  const uint32_t b0 = text[p];
-  if (!((L.first[b0 >> 5] >> (b0 & 31u)) & 1u)) return -1;
+// of p's document, or -1.  b0: the byte at p; q: p's byte in the tile's LDS
+// copy s_text (the tile plus the longest literal's reach).  The literal's
+// bytes are compared a word at a time, every load issued at once.
+__device__ inline int32_t literal_at(const uint32_t* s_text, uint32_t q, uint32_t b0, uint64_t n, uint64_t p,
+                                     const Literals& L, const uint64_t* __restrict__ doc_off, uint32_t n_docs) {
   uint64_t lim = n;  // a literal never reaches into the next document
   if (doc_off) {
     const uint32_t d = first_doc_at_or_after(doc_off, n_docs, p + 1);
     if (d <= n_docs) lim = min(lim, doc_off[d]);
   }
   if (p + 1 < lim) {
-    const uint32_t e = L.key2[b0 | ((uint32_t)text[p + 1] << 8)];
+    const uint32_t b1 = (bytes_at(s_text, q) >> 8) & 0xFFu;
+    const uint32_t e = L.key2[b0 | (b1 << 8)];
     const uint32_t start = e >> 16, cnt = e & 0xFFFFu;
+    const uint32_t* blob = reinterpret_cast<const uint32_t*>(L.bytes);  // word-aligned, padded past its end
     for (uint32_t c = 0; c < cnt; ++c) {  // longest first: the first full match is the longest
       const uint32_t li = L.order[start + c];
       const uint32_t a = L.off[li], len = L.off[li + 1] - a;
       if (p + len > lim) continue;
-      uint32_t k = 2;
-      while (k < len && text[p + k] == L.bytes[a + k]) ++k;
-      if (k == len) return (int32_t)li;
+      const uint32_t w0 = a >> 2, sh = a & 3u;
+      bool eq = true;
+#pragma unroll
+      for (uint32_t j = 0; j < (uint32_t)kLitMax / 4; ++j) {
+        if (4 * j < len) {
+          const uint32_t lw = __builtin_amdgcn_alignbyte(blob[w0 + j + 1], blob[w0 + j], sh);
+          const uint32_t rem = len - 4 * j;
+          const uint32_t mask = rem >= 4 ? 0xFFFFFFFFu : (1u << (8 * rem)) - 1u;
+          eq &= ((lw ^ bytes_at(s_text, q + 4 * j)) & mask) == 0;
+        }
+      }
+      if (eq) return (int32_t)li;
     }
   }
   return L.key1[b0];
@@ -69,14 +88,38 @@ __device__ inline int32_t literal_at(const uint8_t* __restrict__ text, uint64_t 
 __global__ void __launch_bounds__(kMatchThreads)
 lit_match_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off, uint32_t n_docs,
                  Literals L, LitBufs lb) {
+  // the tile's bytes, the longest literal's reach past it, and a guard word
+  constexpr uint32_t kWords = (kLitTile + kLitMax + 8) / 4;
+  __shared__ uint32_t s_text[kWords];
+  __shared__ uint32_t s_first[8];
   __shared__ uint32_t s_scan[kMatchThreads / kWave];
   const uint32_t tile = blockIdx.x, tid = threadIdx.x;
-  const uint64_t p0 = (uint64_t)tile * kLitTile + 4u * tid;
+  const uint64_t base = (uint64_t)tile * kLitTile;
+  {
+    const bool aligned = (reinterpret_cast<uintptr_t>(text) & 3u) == 0;
+    for (uint32_t w = tid; w < kWords; w += kMatchThreads) {
+      const uint64_t p = base + 4u * w;
+      uint32_t v = 0;
+      if (aligned && p + 4 <= n) {
+        v = *reinterpret_cast<const uint32_t*>(text + p);
+      } else {
+        for (uint32_t i = 0; i < 4; ++i)
+          if (p + i < n) v |= (uint32_t)text[p + i] << (8 * i);
+      }
+      s_text[w] = v;
+    }
+    if (tid < 8) s_first[tid] = L.first[tid];
+  }
+  __syncthreads();
+  const uint64_t p0 = base + 4u * tid;
+  const uint32_t cur = s_text[tid];
   int32_t m[4];
   uint32_t c = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    m[j] = p0 + j < n ? literal_at(text, n, p0 + j, L, doc_off, n_docs) : -1;
+    const uint32_t b0 = (cur >> (8 * j)) & 0xFFu;
+    const bool cand = p0 + j < n && ((s_first[b0 >> 5] >> (b0 & 31u)) & 1u);
+    m[j] = cand ? literal_at(s_text, 4u * tid + j, b0, n, p0 + j, L, doc_off, n_docs) : -1;
     c += m[j] >= 0 ? 1u : 0u;
   }
   uint32_t tot = 0;
@@ -185,7 +228,9 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
   }
   for (uint32_t d = tid; d <= nb; d += kSelThreads) {
     const uint64_t x = Db(d);
-    uint32_t lo = 0, hi = k;  // #{j : S_j < x}
+    // #{j : S_j < x}: none before the text, all at its end (so one request
+    // needs no search), else a binary search over the taken literals
+    uint32_t lo = x == 0 ? 0u : x >= n ? k : 0u, hi = x == 0 || x >= n ? lo : k;
     while (lo < hi) {
       const uint32_t mid = (lo + hi) >> 1;
       if ((lb.sel[mid] >> 32) < x) lo = mid + 1;
@@ -230,6 +275,16 @@ lit_insert_kernel(Literals L, LitBufs lb, int32_t* __restrict__ out, uint32_t* _
     carry += tot;
   }
   if (tid == 0) lb.fin[parts] = carry;
+  // for the scatter: the part holding pipeline token 256 b, for every b (the
+  // parts tile the tokens, so each b is written once); the candidate buffer is
+  // free by now and holds it
+  if (parts > 1) {
+    uint32_t* blk = reinterpret_cast<uint32_t*>(lb.cand);
+    for (uint32_t i = tid; i < parts; i += kSelThreads) {
+      const uint32_t o0 = (uint32_t)lb.out_off[i], o1 = (uint32_t)lb.out_off[i + 1];
+      for (uint32_t b = (o0 + kScatterThreads - 1) / kScatterThreads; b * kScatterThreads < o1; ++b) blk[b] = i;
+    }
+  }
   __syncthreads();
   // each document's output offset: that of its first part
   if (out_off)
@@ -246,14 +301,12 @@ __global__ void __launch_bounds__(kScatterThreads)
 lit_scatter_kernel(LitBufs lb, int32_t* __restrict__ out, uint32_t* __restrict__ spans, uint64_t cap) {
   const uint32_t parts = lb.misc[2];
   const uint32_t T = lb.misc[0];
+  const uint32_t* blk = reinterpret_cast<const uint32_t*>(lb.cand);
   for (uint32_t t = blockIdx.x * kScatterThreads + threadIdx.x; t < T; t += gridDim.x * kScatterThreads) {
-    // the part holding pipeline token t: the last i with out_off[i] <= t
-    uint32_t lo = 0, hi = parts - 1;
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi + 1) >> 1;
-      if (lb.out_off[mid] <= t) lo = mid;
-      else hi = mid - 1;
-    }
+    // the part holding pipeline token t: the last i with out_off[i] <= t,
+    // from the part of token 256 floor(t / 256) forward
+    uint32_t lo = parts > 1 ? blk[t / kScatterThreads] : 0u;
+    while (lo + 1 < parts && lb.out_off[lo + 1] <= t) ++lo;
     if (lb.part_lit[lo] >= 0) continue;  // made from a literal's own bytes: replaced by its ID
     const uint64_t at = (uint64_t)lb.fin[lo] + (t - (uint32_t)lb.out_off[lo]);
     if (at < cap) {
