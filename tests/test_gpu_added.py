@@ -298,6 +298,30 @@ def test_batch_workload_with_literals(cfg):
         same(f"doc {i}", ids[a:z], o.encode_added(docs[i].encode(), lits))
 
 
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_random_batches_with_literals(cfg, name):
+    """Seeded random batches: many short documents over an alphabet of
+    literal fragments, letters, digits, spaces and newlines, so literals sit
+    at document edges, straddle them (and must not match), overlap and touch."""
+    t, o, v = cfg[name]
+    lits = lits_from(["<|a|>", "<|ab|>", "ab", "|>", "<|", "é"], v)
+    tokb = vocab.token_bytes(vocab.merges(libs.CONFIGS[name][0]))
+    alpha = ["<|", "a", "b", "|>", "<|a|>", " ", "\n", "1", "é", "x", "'s"]
+    rng = random.Random(404)
+    t.set_added_tokens(lits)
+    try:
+        for trial in range(6):
+            docs = ["".join(rng.choice(alpha) for _ in range(rng.choice([0, 1, 2, 5, 40, 300])))
+                    for _ in range(rng.randint(1, 400))]
+            data, off = textgen.pack_docs(docs)
+            want_ids, want_sp, want_off = batch_expect(o, docs, lits, v, tokb)
+            ids, out_off = t.encode_batch(data, off)
+            same(f"trial {trial} out_off", out_off, want_off)
+            same(f"trial {trial} ids", ids, want_ids)
+    finally:
+        t.set_added_tokens([])
+
+
 def test_hand_worked_cases():
     libs.ensure_built()
     cases = json.load(open(os.path.join(HERE, "golden", "added_tokens.json")))["cases"]
