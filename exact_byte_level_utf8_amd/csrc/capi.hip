@@ -507,6 +507,18 @@ int tok_set_added_tokens(tok_ctx* ctx, const uint8_t* bytes, const uint64_t* off
     return TOK_E_DEVICE;
   }
   ctx->n_lit = (uint32_t)n;
+  ctx->lit_str = lit;
+  ctx->lit_id.assign(ids, ids + n);
+  ctx->lit_by_first.assign(256, {});
+  ctx->lit_max_len = 0;
+  for (size_t i = 0; i < n; ++i) {
+    ctx->lit_by_first[lit[i][0]].push_back((uint32_t)i);
+    ctx->lit_max_len = std::max(ctx->lit_max_len, (uint32_t)lit[i].size());
+  }
+  std::vector<int32_t> sorted_ids(ids, ids + n);
+  std::sort(sorted_ids.begin(), sorted_ids.end());
+  ctx->lit_ids_clash = sorted_ids[0] < (int32_t)ctx->tok_len.size() ||
+                       std::adjacent_find(sorted_ids.begin(), sorted_ids.end()) != sorted_ids.end();
   return TOK_OK;
 }
 

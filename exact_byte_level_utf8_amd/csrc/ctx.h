@@ -110,6 +110,11 @@ struct tok_ctx {
 
   // added-token literals (tok_set_added_tokens); n_lit == 0: none
   uint32_t n_lit = 0;
+  std::vector<std::vector<uint8_t>> lit_str;        // host copy, for the repair
+  std::vector<int32_t> lit_id;
+  std::vector<std::vector<uint32_t>> lit_by_first;  // literal indices by first byte
+  uint32_t lit_max_len = 0;
+  bool lit_ids_clash = false;  // an ID shared with the vocabulary or another literal
   uint8_t* d_lit_bytes = nullptr;
   uint32_t* d_lit_off = nullptr;
   int32_t* d_lit_ids = nullptr;
@@ -226,6 +231,11 @@ struct tok_ctx {
     dfree(d_lit_key1);
     dfree(d_lit_first);
     n_lit = 0;
+    lit_str.clear();
+    lit_id.clear();
+    lit_by_first.clear();
+    lit_max_len = 0;
+    lit_ids_clash = false;
   }
 
   void free_lit_bufs() {

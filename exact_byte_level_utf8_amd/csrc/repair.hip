@@ -112,7 +112,7 @@ int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap,
   inf = tok_repair_info{};
   if (new_len > TOK_MAX_BYTES) return TOK_E_TOOLONG;
   if ((old_len == 0) != (n_session == 0)) return TOK_E_SESSION;
-  if (ctx->n_lit) {  // the splice certificate knows nothing of literals: encode the whole text
+  if (ctx->n_lit && ctx->lit_ids_clash) {  // an ID that names two strings: no walk-back; encode the whole text
     inf.full = 1;
     return tok_encode(ctx, text, new_len, session_ids, cap, n_out);
   }
@@ -123,20 +123,57 @@ int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap,
     return TOK_OK;
   }
 
+  // the bytes of an ID: a vocabulary token, or an added-token literal (their
+  // IDs are distinct here); false for an ID that is neither
+  const size_t vocab = ctx->tok_len.size();
+  auto token_str = [&](int32_t id, const uint8_t** b, uint32_t* L) -> bool {
+    if (id >= 0 && (size_t)id < vocab) {
+      *b = &ctx->tok_bytes[ctx->tok_off[(size_t)id]];
+      *L = ctx->tok_len[(size_t)id];
+      return true;
+    }
+    for (size_t i = 0; i < ctx->lit_id.size(); ++i)
+      if (ctx->lit_id[i] == id) {
+        *b = ctx->lit_str[i].data();
+        *L = (uint32_t)ctx->lit_str[i].size();
+        return true;
+      }
+    return false;
+  };
+  auto token_len = [&](int32_t id) -> uint32_t {
+    const uint8_t* b = nullptr;
+    uint32_t L = 0;
+    return token_str(id, &b, &L) ? L : 0u;
+  };
+  // an added-token literal occurrence (taken or not) that covers bytes b - 1
+  // and b: no cut may fall inside one (Delta Tokenizer, section 3, the cut
+  // guard over every occurrence of every special-token string)
+  auto inside_literal = [&](uint64_t b) -> bool {
+    if (!ctx->n_lit) return false;
+    const uint64_t from = b > ctx->lit_max_len ? b - ctx->lit_max_len + 1 : 0;
+    for (uint64_t p = from; p < b; ++p)
+      for (uint32_t li : ctx->lit_by_first[text[p]]) {
+        const auto& x = ctx->lit_str[li];
+        if (p + x.size() > b && p + x.size() <= new_len && std::memcmp(text + p, x.data(), x.size()) == 0)
+          return true;
+      }
+    return false;
+  };
+  const uint32_t longest = std::max(ctx->max_tok_len, ctx->lit_max_len);
+
   // stored records, walked back from the end of the session as far as needed
   std::vector<Rec> stored;  // in reverse order of offset
   uint64_t pos = old_len;
   size_t j = n_session;
-  const size_t vocab = ctx->tok_len.size();
   auto walk_to = [&](uint64_t target) -> int {
     while (pos > target && j > 0) {
       const int32_t id = session_ids[j - 1];
-      if (id < 0 || (size_t)id >= vocab) return TOK_E_SESSION;
-      const uint32_t L = ctx->tok_len[(size_t)id];
-      if (L > pos) return TOK_E_SESSION;
+      const uint8_t* tb = nullptr;
+      uint32_t L = 0;
+      if (!token_str(id, &tb, &L) || L > pos) return TOK_E_SESSION;
       pos -= L;
       --j;
-      if (std::memcmp(&ctx->tok_bytes[ctx->tok_off[(size_t)id]], text + pos, L) != 0) return TOK_E_SESSION;
+      if (std::memcmp(tb, text + pos, L) != 0) return TOK_E_SESSION;
       stored.push_back(Rec{pos, j, id});
     }
     return pos > target ? TOK_E_SESSION : TOK_OK;  // the IDs must cover the stored text
@@ -172,12 +209,12 @@ int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap,
         continue;
       }
       if (fo < s.off) {
-        fo += ctx->tok_len[(size_t)fresh[k++]];
+        fo += token_len(fresh[k++]);
         continue;
       }
       if (s.id != fresh[k]) {
         --si;
-        fo += ctx->tok_len[(size_t)fresh[k++]];
+        fo += token_len(fresh[k++]);
         continue;
       }
       // an equal run starts here; extend it
@@ -189,17 +226,18 @@ int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap,
       while (si > 0 && k < nf && stored[si - 1].off == fo && stored[si - 1].id == fresh[k]) {
         const uint64_t b = fo;
         if (b >= margin && b < old_len &&
-            sync_transition(ctx->pattern, cp_at(text, new_len, prev_lead(text, b)), cp_at(text, new_len, b)))
+            sync_transition(ctx->pattern, cp_at(text, new_len, prev_lead(text, b)), cp_at(text, new_len, b)) &&
+            !inside_literal(b))
           certified = true;
         last_s = stored[si - 1].idx;
         last_f = k;
-        r1 = fo + ctx->tok_len[(size_t)fresh[k]];
+        r1 = fo + token_len(fresh[k]);
         fo = r1;
         ++k;
         --si;
         ++m;
       }
-      const bool gates = m >= 2 && r1 - r0 > ctx->max_tok_len;
+      const bool gates = m >= 2 && r1 - r0 > longest;
       if (certified && gates) {  // keep the last certified run
         found = true;
         keep_s = last_s + 1;

@@ -306,8 +306,11 @@ int tok_sync_boundary(int pattern, uint32_t prev_cp, uint32_t cp);
  * no whitespace stripping, word-boundary or normalization options.  The
  * literal pass and the insertion of the literal IDs run on the device in the
  * same stream as the pipeline (still one synchronization per call).
- * tok_repair then always encodes the whole text (its
- * splice certificate does not cover literals).  The batch calls apply the
+ * tok_repair also refuses a cut inside any literal occurrence, taken or not
+ * (Delta Tokenizer, section 3, the cut guard), and counts a literal's length
+ * in its gates; it encodes the whole text when a literal's ID is also a
+ * vocabulary ID or another literal's.  tok_repair_dev encodes the whole text
+ * while literals are set.  The batch calls apply the
  * pass within each document (a literal never spans two documents), and span
  * export covers literals (a literal's span is its first byte).
  *

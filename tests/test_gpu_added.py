@@ -160,13 +160,12 @@ def test_no_occurrence_and_repair(cfg):
     t.set_added_tokens(lits)
     try:
         same("no occurrence", dev_encode(t, b), o.encode(b))
-        # repair encodes the whole text and still equals the literal pass
+        # repair splices with literals too, and equals the literal pass
         old = textgen.mix_text(22, 20_000) + "<|endoftext|>"
         new = old + "<|endoftext|> and more"
-        sess = t.encode(old.encode())
-        same("session", sess, o.encode_added(old.encode(), lits))
+        sess = o.encode_added(old.encode(), lits)
         ids, info = t.repair(sess, new.encode(), len(old.encode()))
-        assert info["full"] == 1
+        assert info["full"] == 0
         same("repair", ids, o.encode_added(new.encode(), lits))
     finally:
         t.set_added_tokens([])
@@ -318,6 +317,52 @@ def test_random_batches_with_literals(cfg, name):
             ids, out_off = t.encode_batch(data, off)
             same(f"trial {trial} out_off", out_off, want_off)
             same(f"trial {trial} ids", ids, want_ids)
+    finally:
+        t.set_added_tokens([])
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_repair_with_literals(cfg, name):
+    """Append repair with literals set: a cut never falls inside a literal
+    occurrence, taken or not; the result equals the oracle's literal pass over
+    the whole text.  Covers appends that complete a literal cut by the seam,
+    that begin or end with one, and overlapping literal strings; the device
+    session repair (which encodes the whole text while literals are set) and
+    literal IDs that name vocabulary tokens (whole-text encode) agree."""
+    t, o, v = cfg[name]
+    lits = lits_from(MARKERS + ["ab|>", "|>x"], v)
+    base = textgen.chat_text(90, 60_000, MARKERS)
+    seams = [("<|im_", "end|>\nok"), ("<|im_end|", ">"), ("text ", "<|im_start|>user\n"), ("x<|endoftext|>", " y"),
+             ("ab", "|>x tail"), ("<", "|tool_call|>{}"), ("", "plain words only")]
+    t.set_added_tokens(lits)
+    try:
+        spliced = 0
+        for left, right in seams:
+            old = (base + left).encode()
+            new = old + right.encode()
+            sess = o.encode_added(old, lits)
+            want = o.encode_added(new, lits)
+            ids, info = t.repair(sess, new, len(old))
+            same(f"{left!r}|{right!r}", ids, want)
+            spliced += info["full"] == 0
+            d = torch.from_numpy(np.concatenate([sess, np.zeros(len(right) + 64, np.int32)]).astype(np.int32)).cuda()
+            n, dinfo = t.repair_dev(d, len(sess), new, len(old))
+            same(f"dev {left!r}|{right!r}", d[:n].cpu().numpy(), want)
+        for seed in range(8):
+            old_s, suf = textgen.repair_case(91, 9_100 + seed, old_text=base)
+            suf = suf[: len(suf) // 2] + MARKERS[seed % len(MARKERS)] + suf[len(suf) // 2:]
+            old, new = old_s.encode(), (old_s + suf).encode()
+            ids, info = t.repair(o.encode_added(old, lits), new, len(old))
+            same(f"append {seed}", ids, o.encode_added(new, lits))
+            spliced += info["full"] == 0
+        assert spliced >= 8
+        # a literal ID that is also a vocabulary ID: the walk-back cannot tell them apart
+        clash = [(b"<|im_end|>", 300)]
+        t.set_added_tokens(clash)
+        old, new = base.encode(), (base + "<|im_end|> more").encode()
+        ids, info = t.repair(o.encode_added(old, clash), new, len(old))
+        assert info["full"] == 1
+        same("clash", ids, o.encode_added(new, clash))
     finally:
         t.set_added_tokens([])
 
