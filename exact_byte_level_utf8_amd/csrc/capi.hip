@@ -484,7 +484,11 @@ int tok_set_added_tokens(tok_ctx* ctx, const uint8_t* bytes, const uint64_t* off
     loff[i + 1] = (uint32_t)blob.size();
   }
   blob.resize(blob.size() + 72, 0);  // the match kernel reads whole words up to 8 bytes past a literal
-  if (hipMalloc((void**)&ctx->d_lit_bytes, blob.size()) != hipSuccess ||
+  std::vector<uint64_t> by_id(n);
+  for (size_t i = 0; i < n; ++i) by_id[i] = ((uint64_t)(uint32_t)ids[i] << 32) | i;
+  std::sort(by_id.begin(), by_id.end());
+  if (hipMalloc((void**)&ctx->d_lit_by_id, n * 8) != hipSuccess ||
+      hipMalloc((void**)&ctx->d_lit_bytes, blob.size()) != hipSuccess ||
       hipMalloc((void**)&ctx->d_lit_off, loff.size() * 4) != hipSuccess ||
       hipMalloc((void**)&ctx->d_lit_ids, n * 4) != hipSuccess ||
       hipMalloc((void**)&ctx->d_lit_key2, key2.size() * 4) != hipSuccess ||
@@ -495,7 +499,8 @@ int tok_set_added_tokens(tok_ctx* ctx, const uint8_t* bytes, const uint64_t* off
     ctx->free_lit_tables();
     return TOK_E_NOMEM;
   }
-  if (hipMemcpy(ctx->d_lit_bytes, blob.data(), blob.size(), hipMemcpyHostToDevice) != hipSuccess ||
+  if (hipMemcpy(ctx->d_lit_by_id, by_id.data(), n * 8, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(ctx->d_lit_bytes, blob.data(), blob.size(), hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(ctx->d_lit_off, loff.data(), loff.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(ctx->d_lit_ids, ids, n * 4, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(ctx->d_lit_key2, key2.data(), key2.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||

@@ -11,7 +11,7 @@
 #include <vector>
 
 #include "tok.h"
-#include "tok_internal.h"
+#include "ext_internal.h"
 
 using namespace tok;  // internal header of the library's host sources only
 
@@ -122,6 +122,7 @@ struct tok_ctx {
   uint16_t* d_lit_order = nullptr;
   int32_t* d_lit_key1 = nullptr;
   uint32_t* d_lit_first = nullptr;
+  uint64_t* d_lit_by_id = nullptr;
   LitBufs lb{};
   uint64_t lit_cap = 0;   // input bytes lb covers
   uint64_t lit_docs = 0;  // documents lb covers
@@ -230,6 +231,7 @@ struct tok_ctx {
     dfree(d_lit_order);
     dfree(d_lit_key1);
     dfree(d_lit_first);
+    dfree(d_lit_by_id);
     n_lit = 0;
     lit_str.clear();
     lit_id.clear();
@@ -256,7 +258,8 @@ struct tok_ctx {
   }
 
   Literals literals() const {
-    return Literals{d_lit_bytes, d_lit_off, d_lit_ids, d_lit_key2, d_lit_order, d_lit_key1, d_lit_first, n_lit};
+    return Literals{d_lit_bytes, d_lit_off, d_lit_ids, d_lit_key2, d_lit_order, d_lit_key1, d_lit_first, d_lit_by_id,
+                    n_lit};
   }
 
   // Buffers of the literal pass for the current capacity and n_docs
@@ -295,17 +298,25 @@ struct tok_ctx {
   // literal IDs, all enqueued at once; one synchronization.  doc_off /
   // n_docs / out_off: the caller's documents and their output offsets, or
   // nullptr for one request.  spans (optional): each ID's first byte.
+  // The same, enqueued under call number `call` without waiting (after
+  // ensure_lit_bufs()).
+  void enqueue_added(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, int32_t* out,
+                     uint64_t out_cap, uint64_t* out_off, hipStream_t s, uint64_t call, uint32_t* spans) {
+    Bufs bb = b;
+    bb.gen = call;
+    bb.n_docs_dev = lb.misc + 2;
+    launch_literal_pass(text, n, doc_off, n_docs, literals(), lb, d_ctr, call, s);
+    enqueue(text, n, lb.cut, 1, lb.ids, spans ? lb.spans : nullptr, n, lb.out_off, s, bb, true, nullptr);
+    launch_literal_insert(n, literals(), lb, out, spans, out_cap, out_off, d_ctr, call, s);
+  }
+
   int run_added(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, int32_t* out,
                 uint64_t out_cap, uint64_t* out_off, hipStream_t s, uint32_t* total, uint32_t* spans = nullptr) {
     int rc = ensure_lit_bufs(doc_off ? n_docs : 1);
     if (rc) return rc;
     volatile Counters* c = h_ctr;
-    Bufs bb = b;
-    const uint64_t call = bb.gen = ++gen;
-    bb.n_docs_dev = lb.misc + 2;
-    launch_literal_pass(text, n, doc_off, n_docs, literals(), lb, d_ctr, call, s);
-    enqueue(text, n, lb.cut, 1, lb.ids, spans ? lb.spans : nullptr, n, lb.out_off, s, bb, true, nullptr);
-    launch_literal_insert(n, literals(), lb, out, spans, out_cap, out_off, d_ctr, call, s);
+    const uint64_t call = ++gen;
+    enqueue_added(text, n, doc_off, n_docs, out, out_cap, out_off, s, call, spans);
     HIP_OK(hipGetLastError());
     HIP_OK(hipStreamSynchronize(s));
     if (prof) {

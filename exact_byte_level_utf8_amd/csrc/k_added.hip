@@ -30,7 +30,7 @@
 // With span export the pipeline also gives each segment token's first byte
 // (counted from the start of the text, as the parts are), the literal's first
 // byte goes with its ID, and the scatter moves both.
-#include "tok_internal.h"
+#include "ext_internal.h"
 #include "wg_scan.h"
 
 namespace tok {

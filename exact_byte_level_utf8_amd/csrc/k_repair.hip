@@ -13,11 +13,12 @@
 //   - a window record is equal when a stored record starts at the same byte
 //     with the same ID; runs of consecutive equal records are the candidates;
 //   - a run qualifies with at least two records, more bytes than the longest
-//     token, and a record starting at a synchronizing transition at least
-//     8 code points into the window and before old_len;
+//     token (or added-token literal), and a record starting at a
+//     synchronizing transition at least 8 code points into the window and
+//     before old_len, with no literal occurrence across it;
 //   - the last qualifying run is kept: stored IDs up to its end, then the
 //     window's IDs after it.
-#include "tok_internal.h"
+#include "ext_internal.h"
 #include "pretok_rules.h"
 #include "sync_rules.h"
 #include "wg_scan.h"
@@ -44,6 +45,55 @@ __device__ inline uint32_t rp_cp(const uint8_t* w, uint64_t n, uint64_t i) {
   uint32_t cp = b0 & (0x7Fu >> len);
   for (uint32_t k = 1; k < len && i + k < n; ++k) cp = (cp << 6) | (w[i + k] & 0x3Fu);
   return cp;
+}
+
+// Bytes of an ID: a vocabulary token, or an added-token literal (A.L.n > 0;
+// literal IDs name no token).  False for an ID that is neither.
+__device__ inline bool id_bytes(const RepairArgs& A, int32_t id, const uint8_t** b, uint32_t* len) {
+  if (id >= 0 && (uint32_t)id < A.vocab) {
+    *b = A.tok_bytes + A.tok_off[id];
+    *len = A.tok_len[id];
+    return true;
+  }
+  if (id < 0 || A.L.n == 0) return false;
+  uint32_t lo = 0, hi = A.L.n;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if ((uint32_t)(A.L.by_id[mid] >> 32) < (uint32_t)id) lo = mid + 1;
+    else hi = mid;
+  }
+  if (lo == A.L.n || (uint32_t)(A.L.by_id[lo] >> 32) != (uint32_t)id) return false;
+  const uint32_t li = (uint32_t)A.L.by_id[lo];
+  *b = A.L.bytes + A.L.off[li];
+  *len = A.L.off[li + 1] - A.L.off[li];
+  return true;
+}
+
+__device__ inline uint32_t id_len(const RepairArgs& A, int32_t id) {
+  const uint8_t* b = nullptr;
+  uint32_t len = 0;
+  return id_bytes(A, id, &b, &len) ? len : 0u;
+}
+
+// Some added-token literal occurrence, taken or not, covers bytes b - 1 and b
+// (a cut there is refused: Delta Tokenizer, section 3, the cut guard).  The
+// window starts at least the longest literal before any b asked about.
+__device__ inline bool inside_literal(const RepairArgs& A, uint64_t b) {
+  const Literals& L = A.L;
+  for (uint64_t p = b - min(b - A.ws0, (uint64_t)kLitMax - 1); p < b; ++p) {
+    const uint32_t b0 = A.win[p - A.ws0];
+    if (!((L.first[b0 >> 5] >> (b0 & 31u)) & 1u) || p + 1 >= A.new_len) continue;
+    const uint32_t e = L.key2[b0 | ((uint32_t)A.win[p + 1 - A.ws0] << 8)];
+    for (uint32_t c = 0; c < (e & 0xFFFFu); ++c) {
+      const uint32_t li = L.order[(e >> 16) + c];
+      const uint32_t a = L.off[li], len = L.off[li + 1] - a;
+      if (p + len <= b || p + len > A.new_len) continue;
+      uint32_t k = 2;
+      while (k < len && A.win[p + k - A.ws0] == L.bytes[a + k]) ++k;
+      if (k == len) return true;
+    }
+  }
+  return false;
 }
 
 struct MaxOp {
@@ -83,9 +133,10 @@ __global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) 
   for (uint32_t r0 = 0;; r0 += kRpThreads) {  // uniform: s_nst and carry are shared
     const uint32_t r = r0 + tid;
     const bool have = r < A.n_session;
-    int32_t id = have ? A.session[A.n_session - 1 - r] : 0;
-    const bool id_ok = id >= 0 && (uint32_t)id < A.vocab;
-    const uint32_t len = have && id_ok ? A.tok_len[id] : 0u;
+    const int32_t id = have ? A.session[A.n_session - 1 - r] : 0;
+    const uint8_t* tb = nullptr;
+    uint32_t len = 0;
+    const bool id_ok = have && id_bytes(A, id, &tb, &len);
     uint32_t tot = 0;
     const uint32_t before = wg_excl_scan<kRpThreads>(len, 0u, AddOp(), s_scan, &tot);
     const uint64_t s_end = (uint64_t)carry + before;  // bytes after this record
@@ -94,7 +145,6 @@ __global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) 
       if (!bad) {
         const uint64_t off = A.old_len - s_end - len;
         A.st_off[r] = (uint32_t)off;
-        const uint8_t* tb = A.tok_bytes + A.tok_off[id];
         for (uint32_t k = 0; k < len && !bad; ++k) bad = tb[k] != A.win[off - A.ws0 + k];
         if (s_end + len >= need) atomicMin(&s_nst, r + 1);
       }
@@ -138,7 +188,8 @@ __global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) 
         uint64_t j = i - 1;
         while (j > 0 && (A.win[j] & 0xC0u) == 0x80u) --j;
         const uint32_t x = rp_cp(A.win, wn, j), y = rp_cp(A.win, wn, i);
-        cert = sync_transition_of(A.gpt2 != 0, x, rp_class(x), y, rp_class(y));
+        cert = sync_transition_of(A.gpt2 != 0, x, rp_class(x), y, rp_class(y)) &&
+               (A.L.n == 0 || !inside_literal(A, off));
       }
     }
     uint32_t t1 = 0, t2 = 0;
@@ -148,7 +199,7 @@ __global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) 
       const uint32_t s = start ? k + 1 : ls;  // 1 + index of this run's first record
       const uint32_t c = cert ? k + 1 : lc;
       const uint32_t m = k + 2 - s;
-      const uint64_t bytes = off + A.tok_len[A.fresh[k]] - (A.ws + A.fspan[s - 1]);
+      const uint64_t bytes = off + id_len(A, A.fresh[k]) - (A.ws + A.fspan[s - 1]);
       if (c >= s && m >= 2 && bytes > A.max_tok_len) atomicMax(&s_best, k + 1);
     }
     c_start = MaxOp()(c_start, t1);
@@ -165,7 +216,7 @@ __global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) 
     return;
   }
   const uint32_t kl = best - 1;
-  const uint64_t end_off = A.ws + A.fspan[kl] + A.tok_len[A.fresh[kl]];
+  const uint64_t end_off = A.ws + A.fspan[kl] + id_len(A, A.fresh[kl]);
   const int32_t r = find_stored(A.st_off, n_st, A.ws + A.fspan[kl]);
   const uint64_t keep_s = A.n_session - (uint32_t)r;  // stored IDs through the run's last record
   const uint64_t total = keep_s + (F - best);

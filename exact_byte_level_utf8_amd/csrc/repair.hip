@@ -281,10 +281,13 @@ int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_
   DeviceGuard g(ctx->device);
   hipStream_t s = ctx->stream;
   volatile Counters* c = ctx->h_ctr;
-  if (!ctx->n_lit) {
+  if (!ctx->n_lit || !ctx->lit_ids_clash) {
     int rc = ctx->ensure_tok_bytes();
     if (rc) return rc;
-    const uint64_t pad = (ctx->max_tok_len + 3u) & ~3ull;  // keeps the window start word-aligned
+    // the window reaches back the longest token or literal before its start
+    // (the straddling stored token, the literal cut guard), word-aligned
+    const uint32_t longest = std::max(ctx->max_tok_len, ctx->n_lit ? ctx->lit_max_len : 0u);
+    const uint64_t pad = (longest + 3u) & ~3ull;
     uint64_t w = kFirstWindow;
     for (uint32_t widen = 0; widen <= kMaxWidenings; ++widen, w *= 2) {
       inf.widenings = widen;
@@ -299,10 +302,18 @@ int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_
       if (rc) return rc;
       std::memcpy(ctx->h_text, text + ws0, new_len - ws0);
       HIP_OK(hipMemcpyAsync(ctx->d_text, ctx->h_text, new_len - ws0, hipMemcpyHostToDevice, s));
-      Bufs bb = ctx->b;
-      const uint64_t call = bb.gen = ++ctx->gen;
-      ctx->enqueue(ctx->d_text + (ws - ws0), wlen, nullptr, 0, ctx->d_ids, ctx->d_spans, wlen, nullptr, s, bb, true,
-                   nullptr);
+      const uint64_t call = ++ctx->gen;
+      if (ctx->n_lit) {
+        rc = ctx->ensure_lit_bufs(1);
+        if (rc) return rc;
+        ctx->enqueue_added(ctx->d_text + (ws - ws0), wlen, nullptr, 0, ctx->d_ids, wlen, nullptr, s, call,
+                           ctx->d_spans);
+      } else {
+        Bufs bb = ctx->b;
+        bb.gen = call;
+        ctx->enqueue(ctx->d_text + (ws - ws0), wlen, nullptr, 0, ctx->d_ids, ctx->d_spans, wlen, nullptr, s, bb,
+                     true, nullptr);
+      }
       RepairArgs a{};
       a.win = ctx->d_text;
       a.ws0 = ws0;
@@ -320,7 +331,8 @@ int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_
       a.tok_bytes = ctx->d_tok_bytes;
       a.tok_off = ctx->d_tok_off;
       a.vocab = (uint32_t)ctx->tok_len.size();
-      a.max_tok_len = ctx->max_tok_len;
+      a.max_tok_len = longest;
+      a.L = ctx->literals();
       a.gpt2 = ctx->pattern == TOK_PAT_GPT2 ? 1 : 0;
       a.st_off = ctx->b.ws_rk;  // free once the window encode is done
       a.out = &ctx->d_ctr->rp;
@@ -329,7 +341,7 @@ int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_
       HIP_OK(hipGetLastError());
       HIP_OK(hipStreamSynchronize(s));
       if (c->err_utf8 == call) return TOK_E_UTF8;
-      if (c->done != call || c->rp.gen != call) return TOK_E_DEVICE;
+      if (c->done != call || c->rp.gen != call || (ctx->n_lit && c->ins_done != call)) return TOK_E_DEVICE;
       const uint32_t st = c->rp.status;
       if (st == kRepairSession) return TOK_E_SESSION;
       if (st == kRepairNone) continue;

@@ -264,7 +264,7 @@ int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap,
  * matches the (byte offset, ID) records, picks the splice exactly as
  * tok_repair does and writes the window's IDs after it: one synchronization
  * per attempt.  The window widening, the gates and the full-encode fallback
- * are tok_repair's; with added-token literals set the whole text is encoded.
+ * are tok_repair's, with added-token literals too.
  * Runs on the context's own stream, ordered after work on the legacy default
  * stream.
  *
@@ -309,8 +309,8 @@ int tok_sync_boundary(int pattern, uint32_t prev_cp, uint32_t cp);
  * tok_repair also refuses a cut inside any literal occurrence, taken or not
  * (Delta Tokenizer, section 3, the cut guard), and counts a literal's length
  * in its gates; it encodes the whole text when a literal's ID is also a
- * vocabulary ID or another literal's.  tok_repair_dev encodes the whole text
- * while literals are set.  The batch calls apply the
+ * vocabulary ID or another literal's.  tok_repair_dev does the same on the
+ * device.  The batch calls apply the
  * pass within each document (a literal never spans two documents), and span
  * export covers literals (a literal's span is its first byte).
  *

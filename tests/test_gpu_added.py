@@ -327,8 +327,8 @@ def test_repair_with_literals(cfg, name):
     occurrence, taken or not; the result equals the oracle's literal pass over
     the whole text.  Covers appends that complete a literal cut by the seam,
     that begin or end with one, and overlapping literal strings; the device
-    session repair (which encodes the whole text while literals are set) and
-    literal IDs that name vocabulary tokens (whole-text encode) agree."""
+    session repair takes the same decisions; literal IDs that name vocabulary
+    tokens make both encode the whole text."""
     t, o, v = cfg[name]
     lits = lits_from(MARKERS + ["ab|>", "|>x"], v)
     base = textgen.chat_text(90, 60_000, MARKERS)
@@ -348,6 +348,7 @@ def test_repair_with_literals(cfg, name):
             d = torch.from_numpy(np.concatenate([sess, np.zeros(len(right) + 64, np.int32)]).astype(np.int32)).cuda()
             n, dinfo = t.repair_dev(d, len(sess), new, len(old))
             same(f"dev {left!r}|{right!r}", d[:n].cpu().numpy(), want)
+            assert dinfo == info, (left, right, dinfo, info)
         for seed in range(8):
             old_s, suf = textgen.repair_case(91, 9_100 + seed, old_text=base)
             suf = suf[: len(suf) // 2] + MARKERS[seed % len(MARKERS)] + suf[len(suf) // 2:]
@@ -360,9 +361,14 @@ def test_repair_with_literals(cfg, name):
         clash = [(b"<|im_end|>", 300)]
         t.set_added_tokens(clash)
         old, new = base.encode(), (base + "<|im_end|> more").encode()
-        ids, info = t.repair(o.encode_added(old, clash), new, len(old))
+        sess = o.encode_added(old, clash)
+        ids, info = t.repair(sess, new, len(old))
         assert info["full"] == 1
         same("clash", ids, o.encode_added(new, clash))
+        d = torch.from_numpy(np.concatenate([sess, np.zeros(64, np.int32)]).astype(np.int32)).cuda()
+        n, dinfo = t.repair_dev(d, len(sess), new, len(old))
+        assert dinfo["full"] == 1
+        same("clash dev", d[:n].cpu().numpy(), o.encode_added(new, clash))
     finally:
         t.set_added_tokens([])
 
