@@ -373,6 +373,39 @@ def test_repair_with_literals(cfg, name):
         t.set_added_tokens([])
 
 
+def test_batch_literal_errors_and_capacity(cfg):
+    """With literals set: malformed UTF-8 in one document rejects the batch;
+    a too-small output reports the full count, fills the per-document offsets
+    and writes the first cap IDs."""
+    t, o, v = cfg["gpt2"]
+    lits = lits_from(MARKERS, v)
+    tokb = vocab.token_bytes(vocab.merges(libs.CONFIGS["gpt2"][0]))
+    t.set_added_tokens(lits)
+    try:
+        bad = ["<|im_start|>ok", "fine<|im_end|>"]
+        data, off = textgen.pack_docs(bad)
+        data = data[:3] + b"\xff" + data[4:]
+        with pytest.raises(tk.TokError) as e:
+            t.encode_batch(data, off)
+        assert e.value.code == tk.TOK_E_UTF8
+        docs = [textgen.chat_text(80 + i, 3000, MARKERS) for i in range(4)]
+        data, off = textgen.pack_docs(docs)
+        want_ids, _, want_off = batch_expect(o, docs, lits, v, tokb)
+        cap = len(want_ids) - 10
+        d = torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda()
+        d_off = torch.tensor(off.astype(np.int64), device="cuda").view(torch.uint64)
+        d_out = torch.zeros(len(off), dtype=torch.int64, device="cuda").view(torch.uint64)
+        d_ids = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+        with pytest.raises(tk.TokError) as e:
+            t.encode_batch_dev(d, d_off, d_ids, d_out)
+        assert e.value.code == tk.TOK_E_CAPACITY
+        torch.cuda.synchronize()
+        same("out_off", d_out.view(torch.int64).cpu().numpy().astype(np.uint64), want_off)
+        same("first cap IDs", d_ids.cpu().numpy(), want_ids[:cap])
+    finally:
+        t.set_added_tokens([])
+
+
 def test_hand_worked_cases():
     libs.ensure_built()
     cases = json.load(open(os.path.join(HERE, "golden", "added_tokens.json")))["cases"]
