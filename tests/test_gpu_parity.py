@@ -431,3 +431,39 @@ def test_random_texts(cfg, name):
         _check(name, t.encode(b), o.encode(b), b, tokb)
     whole = "".join(docs).encode()
     _check(name, t.encode(whole), o.encode(whole), whole, tokb)
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_unaligned_device_text(cfg, name):
+    """Text that starts 1, 2 or 3 bytes into a device buffer: the kernels
+    fall back from word loads to byte loads, with the same result; the batch
+    call and the literal pass too."""
+    t, o, _ = cfg[name]
+    b = textgen.mix_text(66, 50_000).encode()
+    want = o.encode(b)
+    v = t.info()["vocab_size"]
+    lits = [(b"<|x|>", v), (b"=>", v + 1)]
+    data, off = textgen.pack_docs([b[:20_000].decode(errors="ignore"), "", b[20_000:].decode(errors="ignore")])
+    want_b, want_off = o.encode_batch(data, off)
+    for shift in (1, 2, 3):
+        d = torch.frombuffer(bytearray(b"\0" * shift + b), dtype=torch.uint8).cuda()[shift:]
+        assert d.data_ptr() % 4 == shift
+        ids = torch.empty(len(b), dtype=torch.int32, device="cuda")
+        n = t.encode_dev(d, ids)
+        torch.cuda.synchronize()
+        _check(f"{name}+{shift}", ids[:n].cpu().numpy(), want, b, None)
+        db = torch.frombuffer(bytearray(b"\0" * shift + data), dtype=torch.uint8).cuda()[shift:]
+        d_off = torch.tensor(off.astype(np.int64), device="cuda").view(torch.uint64)
+        d_out = torch.empty(len(off), dtype=torch.int64, device="cuda").view(torch.uint64)
+        d_ids = torch.empty(len(data), dtype=torch.int32, device="cuda")
+        n = t.encode_batch_dev(db, d_off, d_ids, d_out)
+        torch.cuda.synchronize()
+        _check(f"{name}+{shift} batch", d_ids[:n].cpu().numpy(), want_b, data, None)
+        assert np.array_equal(d_out.view(torch.int64).cpu().numpy().astype(np.uint64), want_off)
+        t.set_added_tokens(lits)
+        try:
+            n = t.encode_dev(d, ids)
+            torch.cuda.synchronize()
+            _check(f"{name}+{shift} literals", ids[:n].cpu().numpy(), o.encode_added(b, lits), b, None)
+        finally:
+            t.set_added_tokens([])
