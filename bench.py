@@ -148,6 +148,43 @@ def algorithmic_bytes(stage: str, n_bytes: int, n_tokens: int) -> int:
     return 0
 
 
+def large_appends(tok, base: str, seed: int, reps: int = 5) -> list:
+    """Appends of 50K characters and more, where TokTier's delta-aware routing
+    re-encodes the whole request: median ms of the window repair (session
+    in host and in device memory) beside a full encode of the whole text,
+    all from host memory."""
+    import torch
+
+    from synth import textgen
+
+    rows = []
+    for app_chars in (50_000, 200_000, 1_000_000):
+        ob = base.encode()
+        text = ob + textgen.mix_text(seed + 1 + app_chars, app_chars).encode()
+        sess = tok.encode(ob)
+        want = tok.encode(text)
+        buf = np.zeros(want.size + 64, dtype=np.int32)
+        t_rep, t_dev, t_full = [], [], []
+        for _ in range(reps + 1):
+            buf[: sess.size] = sess
+            d_sess = torch.from_numpy(buf).cuda()
+            torch.cuda.synchronize()
+            s0 = time.perf_counter()
+            n, info = tok.repair_into(buf, sess.size, text, len(ob))
+            t_rep.append(time.perf_counter() - s0)
+            s0 = time.perf_counter()
+            dn, dinfo = tok.repair_dev(d_sess, sess.size, text, len(ob))
+            t_dev.append(time.perf_counter() - s0)
+            s0 = time.perf_counter()
+            full = tok.encode(text)
+            t_full.append(time.perf_counter() - s0)
+            assert n == dn == full.size and np.array_equal(buf[:n], want) and dinfo == info
+        ms = lambda v: round(1e3 * statistics.median(v[1:]), 4)  # noqa: E731
+        rows.append({"append_chars": app_chars, "repair_ms": ms(t_rep), "repair_dev_ms": ms(t_dev),
+                     "full_encode_ms": ms(t_full), "full_fallback": info["full"]})
+    return rows
+
+
 def bench_repair(args, desc, merges_name, pattern, seed, n_chars) -> int:
     """Latency of tok_repair over seeded appends (host text and IDs, one GPU
     window encode per call).  Each case's stored IDs are prepared in a
@@ -183,6 +220,7 @@ def bench_repair(args, desc, merges_name, pattern, seed, n_chars) -> int:
             full += info["full"]
             widen += info["widenings"]
     p50 = statistics.median(lat)
+    large = large_appends(tok, base, seed)
     out = {"metric": "tok_repair latency (ms, P50)", "value": round(1e3 * p50, 4), "unit": "ms", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
            "latency_ms": {"p50": round(1e3 * p50, 4), "p90": round(1e3 * float(np.percentile(lat, 90)), 4),
@@ -190,7 +228,7 @@ def bench_repair(args, desc, merges_name, pattern, seed, n_chars) -> int:
            "device_session_ms": {"p50": round(1e3 * statistics.median(dlat), 4),
                                  "p90": round(1e3 * float(np.percentile(dlat, 90)), 4),
                                  "note": "tok_repair_dev: session IDs in device memory, match and splice on the device"},
-           "full_encodes": full, "widenings": widen, "dtype": "u8->int32",
+           "full_encodes": full, "widenings": widen, "large_appends": large, "dtype": "u8->int32",
            "data": "synthetic (seeded generator; host text and IDs)",
            "config": {"workload": desc, "context_chars": n_chars, "append_chars": 1400, "merges": merges_name,
                       "pattern": pattern, "seed": seed}}

@@ -59,6 +59,9 @@ struct RepairArgs {
   int gpt2;                      // 1: GPT-2 style family, 0: Llama-3 style
   Literals L;                    // added-token literals (L.n == 0: none); their IDs name no token
   uint32_t* st_off;              // scratch: first byte of the r-th stored record from the end
+  uint64_t* splice;              // device words: [0] first window record to copy, [1] session
+                                 // index it goes to, [2] how many (0: nothing to copy)
+  uint64_t max_fresh;            // bound on the window's record count (its byte count)
   RepairOut* out;                // host-mapped result
   uint64_t gen;
 };
@@ -68,6 +71,8 @@ void launch_literal_pass(const uint8_t* text, uint64_t n, const uint64_t* doc_of
                          LitBufs lb, Counters* ctr, uint64_t gen, hipStream_t s);
 void launch_literal_insert(uint64_t n, Literals L, LitBufs lb, int32_t* out, uint32_t* spans, uint64_t cap,
                            uint64_t* out_off, Counters* ctr, uint64_t gen, hipStream_t s);
+// The match kernel, then, for a window of more than a few thousand records,
+// the copy of the window's IDs after the splice (a grid sized by a.max_fresh).
 void launch_repair_match(const RepairArgs& a, hipStream_t s);
 
 }  // namespace tok

@@ -18,6 +18,9 @@
 //     before old_len, with no literal occurrence across it;
 //   - the last qualifying run is kept: stored IDs up to its end, then the
 //     window's IDs after it.
+// Only window records that start before old_len can equal a stored one, so
+// the match passes stop there; a long tail of window IDs after the splice
+// (a long append) is copied by a second, grid-wide kernel.
 #include "ext_internal.h"
 #include "pretok_rules.h"
 #include "sync_rules.h"
@@ -28,6 +31,9 @@ namespace tok {
 namespace {
 
 constexpr uint32_t kRpThreads = 1024;
+// Window IDs after the splice up to this many are copied by the match
+// kernel itself; longer tails (a long append) by a grid-wide copy.
+constexpr uint32_t kInlineCopy = 8 * kRpThreads;
 
 __device__ inline uint32_t rp_class(uint32_t cp) {
   if (cp < 0x80) return ascii_class(cp);
@@ -114,16 +120,26 @@ __device__ inline int32_t find_stored(const uint32_t* st_off, uint32_t n_st, uin
 
 __global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) {
   __shared__ uint32_t s_scan[kRpThreads / kWave];
-  __shared__ uint32_t s_bad, s_nst, s_best, s_F;
+  __shared__ uint32_t s_bad, s_nst, s_best, s_F, s_Fo;
   const uint32_t tid = threadIdx.x;
   if (tid == 0) {
     s_bad = 0;
     s_nst = 0xFFFFFFFFu;
     s_best = 0;
-    s_F = *(volatile const uint32_t*)A.fresh_total;  // host-mapped: one read
+    const uint32_t F = *(volatile const uint32_t*)A.fresh_total;  // host-mapped: one read
+    // records starting before old_len: fspan rises with k
+    uint32_t lo = 0, hi = F;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (A.ws + A.fspan[mid] < A.old_len) lo = mid + 1;
+      else hi = mid;
+    }
+    s_F = F;
+    s_Fo = lo;
+    A.splice[2] = 0;
   }
   __syncthreads();
-  const uint32_t F = s_F;
+  const uint32_t F = s_F, Fo = s_Fo;
   const uint64_t wn = A.new_len - A.ws0;  // bytes in the device window
   const uint64_t need = A.old_len - A.ws;  // stored bytes to cover
 
@@ -168,13 +184,13 @@ __global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) 
 
   // equal records, runs, certificates; best = 1 + the last qualifying run end
   auto equal_at = [&](int64_t k) -> bool {
-    if (k < 0 || k >= (int64_t)F) return false;
+    if (k < 0 || k >= (int64_t)Fo) return false;
     const uint64_t off = A.ws + A.fspan[k];
     const int32_t r = find_stored(A.st_off, n_st, off);
     return r >= 0 && A.session[A.n_session - 1 - (uint32_t)r] == A.fresh[k];
   };
   uint32_t c_start = 0, c_cert = 0;  // 1 + index of the last run start / certified record so far
-  for (uint32_t k0 = 0; k0 < F; k0 += kRpThreads) {
+  for (uint32_t k0 = 0; k0 < Fo; k0 += kRpThreads) {
     const uint32_t k = k0 + tid;
     const bool eq = equal_at(k);
     const bool start = eq && !equal_at((int64_t)k - 1);
@@ -220,10 +236,14 @@ __global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) 
   const int32_t r = find_stored(A.st_off, n_st, A.ws + A.fspan[kl]);
   const uint64_t keep_s = A.n_session - (uint32_t)r;  // stored IDs through the run's last record
   const uint64_t total = keep_s + (F - best);
-  if (total <= A.cap)
+  if (total <= A.cap && F - best <= kInlineCopy)  // a short tail: copied here
     for (uint32_t i = tid; i < F - best; i += kRpThreads) A.session[keep_s + i] = A.fresh[best + i];
-  __syncthreads();
   if (tid == 0) {
+    if (total <= A.cap && F - best > kInlineCopy) {  // the copy kernel after this one moves them
+      A.splice[0] = best;
+      A.splice[1] = keep_s;
+      A.splice[2] = F - best;
+    }
     A.out->status = total <= A.cap ? kRepairSpliced : kRepairCapacity;
     A.out->total = total;
     A.out->kept = keep_s;
@@ -233,10 +253,26 @@ __global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) 
   }
 }
 
+// session[at + i] = fresh[from + i] for i < count, with (from, at, count)
+// as the match kernel left them; 16 IDs per thread.
+constexpr uint32_t kCopyThreads = 256, kCopyPer = 16;
+
+__global__ void __launch_bounds__(kCopyThreads) repair_copy_kernel(const int32_t* fresh, int32_t* session,
+                                                                   const uint64_t* splice) {
+  const uint64_t from = splice[0], at = splice[1], count = splice[2];
+  const uint64_t base = (uint64_t)blockIdx.x * kCopyThreads * kCopyPer;
+  if (base >= count) return;
+  const uint64_t end = min(count, base + (uint64_t)kCopyThreads * kCopyPer);
+  for (uint64_t i = base + threadIdx.x; i < end; i += kCopyThreads) session[at + i] = fresh[from + i];
+}
+
 }  // namespace
 
 void launch_repair_match(const RepairArgs& a, hipStream_t s) {
   repair_match_kernel<<<1, kRpThreads, 0, s>>>(a);
+  const uint64_t per = (uint64_t)kCopyThreads * kCopyPer;
+  const uint32_t grid = (uint32_t)((a.max_fresh + per - 1) / per);
+  if (a.max_fresh > kInlineCopy) repair_copy_kernel<<<grid, kCopyThreads, 0, s>>>(a.fresh, a.session, a.splice);
 }
 
 }  // namespace tok

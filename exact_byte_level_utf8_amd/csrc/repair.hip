@@ -334,7 +334,12 @@ int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_
       a.max_tok_len = longest;
       a.L = ctx->literals();
       a.gpt2 = ctx->pattern == TOK_PAT_GPT2 ? 1 : 0;
-      a.st_off = ctx->b.ws_rk;  // free once the window encode is done
+      // free once the window encode is done: 6 words of splice parameters,
+      // then the stored offsets (at most one per window byte; the buffer
+      // holds the capacity plus 64 words)
+      a.splice = (uint64_t*)ctx->b.ws_rk;
+      a.st_off = ctx->b.ws_rk + 6;
+      a.max_fresh = new_len - ws;
       a.out = &ctx->d_ctr->rp;
       a.gen = call;
       launch_repair_match(a, s);

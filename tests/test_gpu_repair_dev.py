@@ -149,3 +149,17 @@ def test_empty_session_and_literals(cfg, name):
         assert t.repair(sess, new, len(old))[1] == info  # the host repair decides the same
     finally:
         t.set_added_tokens([])
+
+
+@pytest.mark.parametrize("app_chars", [60_000, 250_000, 1_200_000])
+def test_large_appends(cfg, app_chars):
+    """Appends of 50K characters and more (where TokTier's delta-aware routing
+    would re-encode the whole request): the window repair still runs, and its
+    result and decisions match the host repair and the full encode, also for
+    an append longer than the stored context."""
+    t, o = cfg["gpt2"]
+    old = textgen.mix_text(520, 300_000)
+    app = textgen.mix_text(521 + app_chars, app_chars)
+    for cut in (0, 7):  # append starting at a block edge, and mid-word
+        info = check(t, o, (old + app[:cut]).encode(), app[cut:].encode(), f"append {app_chars} cut {cut}")
+        assert info["full"] == 0
