@@ -120,28 +120,37 @@ __device__ inline int32_t find_stored(const uint32_t* st_off, uint32_t n_st, uin
 
 __global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) {
   __shared__ uint32_t s_scan[kRpThreads / kWave];
-  __shared__ uint32_t s_bad, s_nst, s_best, s_F, s_Fo;
+  __shared__ uint32_t s_bad, s_nst, s_best, s_F;
   const uint32_t tid = threadIdx.x;
   if (tid == 0) {
     s_bad = 0;
     s_nst = 0xFFFFFFFFu;
     s_best = 0;
-    const uint32_t F = *(volatile const uint32_t*)A.fresh_total;  // host-mapped: one read
-    // records starting before old_len: fspan rises with k
-    uint32_t lo = 0, hi = F;
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi) >> 1;
-      if (A.ws + A.fspan[mid] < A.old_len) lo = mid + 1;
-      else hi = mid;
-    }
-    s_F = F;
-    s_Fo = lo;
+    s_F = *(volatile const uint32_t*)A.fresh_total;  // host-mapped: one read
     A.splice[2] = 0;
   }
   __syncthreads();
-  const uint32_t F = s_F, Fo = s_Fo;
+  const uint32_t F = s_F;
   const uint64_t wn = A.new_len - A.ws0;  // bytes in the device window
   const uint64_t need = A.old_len - A.ws;  // stored bytes to cover
+
+  // Fo = the window records starting before old_len (fspan rises with k;
+  // records start on distinct bytes, so at most `need` of them): the
+  // answer lies in [lo, hi]; each step samples the range at 1,024 evenly
+  // spaced records at once and keeps the gap after the last one before
+  // old_len.
+  uint32_t lo = 0, hi = (uint32_t)min((uint64_t)F, need);
+  while (lo < hi) {  // uniform: every thread gets the same count
+    const uint32_t step = (hi - lo + kRpThreads - 1) / kRpThreads;
+    const uint64_t k = lo + (uint64_t)tid * step;
+    const int below = k < hi && A.ws + A.fspan[k] < A.old_len;
+    const uint32_t c = (uint32_t)__syncthreads_count(below);
+    if (c == 0) break;  // record lo starts at or after old_len
+    const uint32_t nlo = lo + (c - 1) * step + 1;
+    hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + (uint64_t)c * step);
+    lo = nlo;
+  }
+  const uint32_t Fo = lo;
 
   // stored records, from the session's end: r-th from the end has session
   // index n_session - 1 - r and starts at old_len - (bytes of the last r + 1)
