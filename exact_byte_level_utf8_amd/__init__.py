@@ -20,6 +20,7 @@ PATTERNS = {"gpt2": 0, "llama3": 1}
 
 TOK_OK, TOK_E_ARG, TOK_E_BADMERGES, TOK_E_PATTERN, TOK_E_UTF8 = 0, 1, 2, 3, 4
 TOK_E_CAPACITY, TOK_E_TOOLONG, TOK_E_DEVICE, TOK_E_NOMEM, TOK_E_SESSION = 5, 6, 7, 8, 9
+TOK_MAX_BYTES = 0xFFFF0000  # longest input, in bytes
 
 # every function declared in include/tok.h
 EXPORTS = (

@@ -467,3 +467,53 @@ def test_unaligned_device_text(cfg, name):
             _check(f"{name}+{shift} literals", ids[:n].cpu().numpy(), o.encode_added(b, lits), b, None)
         finally:
             t.set_added_tokens([])
+
+
+def test_too_long_rejected(cfg):
+    """A length past TOK_MAX_BYTES is refused with TOK_E_TOOLONG by every entry
+    point before any buffer is read or written (the buffers here are small;
+    only the stated length is out of range)."""
+    t, _, _ = cfg["gpt2"]
+    big = tk.TOK_MAX_BYTES + 1
+    s = torch.cuda.current_stream().cuda_stream
+    d_text = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    d_ids = torch.full((64,), -1, dtype=torch.int32, device="cuda")
+    d_spans = torch.zeros(64, dtype=torch.int32, device="cuda")
+    d_flags = torch.zeros(64, dtype=torch.int16, device="cuda")
+    d_doc = torch.tensor([0, big], dtype=torch.int64, device="cuda")
+    d_out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    host_text = bytes(64)
+    host_ids = np.full(64, -1, dtype=np.int32)
+    host_spans = np.zeros(64, dtype=np.uint32)
+    doc = np.array([0, big], dtype=np.uint64)
+    out = np.zeros(2, dtype=np.uint64)
+    n = ctypes.c_size_t(7)
+    L = tk.lib()
+    calls = {
+        "tok_encode": lambda: L.tok_encode(t._h, host_text, big, host_ids.ctypes.data, 64, ctypes.byref(n)),
+        "tok_encode_dev": lambda: L.tok_encode_dev(t._h, d_text.data_ptr(), big, d_ids.data_ptr(), 64,
+                                                   ctypes.byref(n), s),
+        "tok_encode_batch": lambda: L.tok_encode_batch(t._h, host_text, doc.ctypes.data, 1, host_ids.ctypes.data,
+                                                       64, out.ctypes.data),
+        "tok_encode_batch_dev": lambda: L.tok_encode_batch_dev(t._h, d_text.data_ptr(), big, d_doc.data_ptr(), 1,
+                                                               d_ids.data_ptr(), 64, d_out.data_ptr(),
+                                                               ctypes.byref(n), s),
+        "tok_encode_spans": lambda: L.tok_encode_spans(t._h, host_text, big, host_ids.ctypes.data,
+                                                       host_spans.ctypes.data, 64, ctypes.byref(n)),
+        "tok_encode_spans_dev": lambda: L.tok_encode_spans_dev(t._h, d_text.data_ptr(), big, None, 0,
+                                                               d_ids.data_ptr(), d_spans.data_ptr(), 64, None,
+                                                               ctypes.byref(n), s),
+        "tok_pretokenize_dev": lambda: L.tok_pretokenize_dev(t._h, d_text.data_ptr(), big, None, 0,
+                                                             d_flags.data_ptr(), s),
+        "tok_repair": lambda: L.tok_repair(t._h, host_ids.ctypes.data, 0, 64, host_text, 0, big, ctypes.byref(n),
+                                           None),
+        "tok_repair_dev": lambda: L.tok_repair_dev(t._h, d_ids.data_ptr(), 0, 64, host_text, 0, big,
+                                                   ctypes.byref(n), None),
+    }
+    for name, call in calls.items():
+        n.value = 7
+        assert call() == tk.TOK_E_TOOLONG, name
+        if name not in ("tok_encode_batch", "tok_pretokenize_dev"):  # these have no count argument
+            assert n.value == 0, name
+    torch.cuda.synchronize()
+    assert (host_ids == -1).all() and (d_ids.cpu().numpy() == -1).all()
