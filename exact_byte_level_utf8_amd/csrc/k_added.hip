@@ -39,6 +39,7 @@ namespace {
 constexpr uint32_t kMatchThreads = 256;  // 4 consecutive positions per thread
 constexpr uint32_t kSelThreads = 1024;
 constexpr uint32_t kScatterThreads = 256;
+constexpr uint32_t kInsPer = 4;  // parts per thread in one pass of the insertion
 
 __device__ inline uint32_t lit_len(const Literals& L, uint32_t li) { return L.off[li + 1] - L.off[li]; }
 
@@ -256,21 +257,33 @@ lit_insert_kernel(Literals L, LitBufs lb, int32_t* __restrict__ out, uint32_t* _
                   uint64_t* __restrict__ out_off, Counters* ctr, uint64_t gen) {
   __shared__ uint32_t s_scan[kSelThreads / kWave];
   const uint32_t tid = threadIdx.x, parts = lb.misc[2], nb = lb.misc[3];
+  // kInsPer consecutive parts per thread, so that a pass covers 4,096 parts
+  // with all their loads in flight before the one scan
   uint32_t carry = 0;
-  for (uint32_t i0 = 0; i0 < parts; i0 += kSelThreads) {
-    const uint32_t i = i0 + tid;
-    const int32_t lj = i < parts ? lb.part_lit[i] : -1;
-    uint32_t v = 0;
-    if (i < parts) v = lj >= 0 ? 1u : (uint32_t)(lb.out_off[i + 1] - lb.out_off[i]);
+  for (uint32_t i0 = 0; i0 < parts; i0 += kSelThreads * kInsPer) {
+    const uint32_t ib = i0 + tid * kInsPer;
+    int32_t lj[kInsPer];
+    uint32_t v[kInsPer], sum = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kInsPer; ++j) {
+      const uint32_t i = ib + j;
+      lj[j] = i < parts ? lb.part_lit[i] : -1;
+      v[j] = i >= parts ? 0u : lj[j] >= 0 ? 1u : (uint32_t)(lb.out_off[i + 1] - lb.out_off[i]);
+      sum += v[j];
+    }
     uint32_t tot = 0;
-    const uint32_t ex = wg_excl_scan<kSelThreads>(v, 0u, AddOp(), s_scan, &tot);
-    if (i < parts) {
-      const uint32_t at = carry + ex;
-      lb.fin[i] = at;
-      if (lj >= 0 && at < cap) {
-        out[at] = L.ids[(uint32_t)lb.sel[lj]];
-        if (spans) spans[at] = (uint32_t)lb.cut[i];  // the literal starts its part
+    uint32_t at = carry + wg_excl_scan<kSelThreads>(sum, 0u, AddOp(), s_scan, &tot);
+#pragma unroll
+    for (uint32_t j = 0; j < kInsPer; ++j) {
+      const uint32_t i = ib + j;
+      if (i < parts) {
+        lb.fin[i] = at;
+        if (lj[j] >= 0 && at < cap) {
+          out[at] = L.ids[(uint32_t)lb.sel[lj[j]]];
+          if (spans) spans[at] = (uint32_t)lb.cut[i];  // the literal starts its part
+        }
       }
+      at += v[j];
     }
     carry += tot;
   }
