@@ -243,7 +243,6 @@ struct tok_ctx {
   void free_lit_bufs() {
     dfree(lb.cand);
     dfree(lb.tile_cnt);
-    dfree(lb.tile_base);
     dfree(lb.sel);
     dfree(lb.cut);
     dfree(lb.part_lit);
@@ -273,7 +272,6 @@ struct tok_ctx {
     const uint64_t parts = docs + 2 * cap;
     if (hipMalloc((void**)&lb.cand, cap * 8) != hipSuccess ||
         hipMalloc((void**)&lb.tile_cnt, tiles * 4) != hipSuccess ||
-        hipMalloc((void**)&lb.tile_base, tiles * 4) != hipSuccess ||
         hipMalloc((void**)&lb.sel, cap * 8) != hipSuccess ||
         hipMalloc((void**)&lb.cut, (parts + 2) * 8) != hipSuccess ||
         hipMalloc((void**)&lb.part_lit, (parts + 2) * 4) != hipSuccess ||

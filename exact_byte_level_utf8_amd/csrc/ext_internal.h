@@ -27,7 +27,6 @@ struct Literals {
 struct LitBufs {
   uint64_t* cand;       // per tile: up to kLitTile (position << 32 | literal) in position order
   uint32_t* tile_cnt;   // candidates found in each tile
-  uint32_t* tile_base;  // candidates before each tile
   uint64_t* sel;        // taken literals, in order
   uint64_t* cut;        // parts + 1 cut points: document boundaries, literal starts and ends, merged
   int32_t* part_lit;    // per part: the taken literal it is, or -1

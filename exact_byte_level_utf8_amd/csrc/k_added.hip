@@ -149,23 +149,19 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
   bool bad = false;
   for (uint32_t d = tid; d < nd; d += kSelThreads) bad |= D(d) > D(d + 1);
   if (tid == 0) bad |= D(0) != 0 || D(nd) != n;
-  // matches before each tile (uniform trip count: the scan holds barriers)
+  // matches before each tile, and each tile's matches copied after them in
+  // the same pass (uniform trip count: the scan holds barriers)
   uint32_t carry = 0;
   for (uint32_t t0 = 0; t0 < tiles; t0 += kSelThreads) {
     const uint32_t t = t0 + tid;
     const uint32_t v = t < tiles ? lb.tile_cnt[t] : 0u;
     uint32_t tot = 0;
-    const uint32_t ex = wg_excl_scan<kSelThreads>(v, 0u, AddOp(), s_scan, &tot);
-    if (t < tiles) lb.tile_base[t] = carry + ex;
+    const uint32_t b = carry + wg_excl_scan<kSelThreads>(v, 0u, AddOp(), s_scan, &tot);
+    for (uint32_t j = 0; j < v; ++j) lb.sel[b + j] = lb.cand[(uint64_t)t * kLitTile + j];
     carry += tot;
   }
   if (bad) s_bad = 1u;
   const uint32_t K = carry;
-  __syncthreads();
-  for (uint32_t t = tid; t < tiles; t += kSelThreads) {
-    const uint32_t c = lb.tile_cnt[t], b = lb.tile_base[t];
-    for (uint32_t j = 0; j < c; ++j) lb.sel[b + j] = lb.cand[(uint64_t)t * kLitTile + j];
-  }
   __syncthreads();
   bool over = false;
   for (uint32_t i = tid; i + 1 < K; i += kSelThreads) {
