@@ -9,7 +9,8 @@ Covers the session-append workload (1,000,000-character context, seeded
 log-normal appends, 30% starting mid-word or mid-whitespace), seam shapes of
 both families, widening and the full-encode fallback, stored IDs that do not
 spell the text or do not cover it, capacity overflow (session untouched), an
-empty session, and added-token literals.
+empty session, added-token literals, and appends of 60K to 1.2M characters
+(the long tail copied by a grid-wide kernel), with and without room.
 """
 import numpy as np
 import pytest
@@ -163,3 +164,34 @@ def test_large_appends(cfg, app_chars):
     for cut in (0, 7):  # append starting at a block edge, and mid-word
         info = check(t, o, (old + app[:cut]).encode(), app[cut:].encode(), f"append {app_chars} cut {cut}")
         assert info["full"] == 0
+
+
+def test_large_append_capacity_and_repeat(cfg):
+    """A long tail (copied by the grid-wide kernel) that does not fit the
+    session buffer is reported with the required count and leaves the
+    session untouched; the same append then fits a larger buffer, and a short
+    append after it (inline copy) still matches the full encode."""
+    t, o = cfg["gpt2"]
+    old = textgen.mix_text(530, 100_000).encode()
+    app = textgen.mix_text(531, 120_000).encode()
+    sess = np.asarray(o.encode(old), dtype=np.int32)
+    want = o.encode(old + app)
+    pad = np.full(64, -9, dtype=np.int32)
+    buf = torch.from_numpy(np.concatenate([sess, pad])).cuda()
+    with pytest.raises(tk.TokError) as e:
+        t.repair_dev(buf, len(sess), old + app, len(old))
+    assert e.value.code == tk.TOK_E_CAPACITY
+    assert np.array_equal(buf.cpu().numpy(), np.concatenate([sess, pad]))
+    big = torch.full((len(want) + 16,), -9, dtype=torch.int32)
+    big[: len(sess)] = torch.from_numpy(sess)
+    d = big.cuda()
+    n, info = t.repair_dev(d, len(sess), old + app, len(old))
+    assert n == len(want) and info["full"] == 0
+    assert np.array_equal(d.cpu().numpy()[:n], want)
+    more = b" and a short tail"
+    want2 = o.encode(old + app + more)
+    d2 = torch.full((len(want2) + 16,), -9, dtype=torch.int32)
+    d2[:n] = d[:n].cpu()
+    d2 = d2.cuda()
+    n2, _ = t.repair_dev(d2, n, old + app + more, len(old + app))
+    assert np.array_equal(d2.cpu().numpy()[:n2], want2)
