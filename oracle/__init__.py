@@ -14,8 +14,8 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
-PAT_GPT2, PAT_LLAMA3 = 0, 1
-PATTERNS = {"gpt2": PAT_GPT2, "llama3": PAT_LLAMA3}
+PAT_GPT2, PAT_LLAMA3, PAT_O200K = 0, 1, 2
+PATTERNS = {"gpt2": PAT_GPT2, "llama3": PAT_LLAMA3, "o200k": PAT_O200K}
 
 
 class OracleError(RuntimeError):
@@ -43,6 +43,10 @@ def lib():
         vp, sz, u8p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
         L.orc_class.argtypes = [ctypes.c_uint32]
         L.orc_class.restype = ctypes.c_int
+        L.orc_class_range.argtypes = [ctypes.c_uint32, ctypes.c_uint32, vp]
+        L.orc_class_range.restype = None
+        L.orc_subclass_range.argtypes = [ctypes.c_uint32, ctypes.c_uint32, vp]
+        L.orc_subclass_range.restype = None
         L.orc_new.argtypes = [vp, sz, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
         L.orc_new.restype = vp
         L.orc_free.argtypes = [vp]
@@ -63,6 +67,21 @@ def lib():
 def char_class(cp: int) -> int:
     """0 = L, 1 = N, 2 = W, 3 = O."""
     return lib().orc_class(cp)
+
+
+def class_range(lo: int, n: int) -> np.ndarray:
+    """Classes of code points lo .. lo + n - 1 (uint8: 0 = L, 1 = N, 2 = W, 3 = O)."""
+    out = np.zeros(n, dtype=np.uint8)
+    lib().orc_class_range(lo, n, out.ctypes.data)
+    return out
+
+
+def subclass_range(lo: int, n: int) -> np.ndarray:
+    """Subclasses of code points lo .. lo + n - 1 (uint8: 0 = U (Lu, Lt), 1 = D (Ll),
+    2 = C (Lm, Lo), 3 = M (marks), 4 = N, 5 = W, 6 = O)."""
+    out = np.zeros(n, dtype=np.uint8)
+    lib().orc_subclass_range(lo, n, out.ctypes.data)
+    return out
 
 
 def load_merges(path: str) -> np.ndarray:

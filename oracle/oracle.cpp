@@ -16,7 +16,9 @@
 //
 //   C-1 decode UTF-8, rejecting malformed input;
 //   C-2 classify code points (L letter, N number, W whitespace, O other)
-//       with the frozen table in unicode_classes.inc;
+//       with the frozen table in unicode_classes.inc (and, for the
+//       case-splitting family, letters by case and marks from
+//       unicode_subclasses.inc);
 //   C-3 pre-tokenize with a direct leftmost-first matcher that tries the
 //       pattern's alternatives in order at a cursor and moves the cursor to the
 //       end of the first match (TokTier, section 4, "Removing the sequential
@@ -41,11 +43,15 @@
 #include <vector>
 
 #include "unicode_classes.inc"
+#include "unicode_subclasses.inc"
 
 namespace {
 
 enum { CL = 0, CN = 1, CW = 2, CO = 3 };
-enum { PAT_GPT2 = 0, PAT_LLAMA3 = 1 };
+enum { PAT_GPT2 = 0, PAT_LLAMA3 = 1, PAT_O200K = 2 };
+// letters by case and marks (the case-splitting family): U = Lu or Lt,
+// D = Ll, C = Lm or Lo, M = marks; SN / SW / SO: numbers, whitespace, others
+enum { SU = 0, SD = 1, SC = 2, SM = 3, SN = 4, SW = 5, SO = 6 };
 enum { ORC_OK = 0, ORC_UTF8 = 1, ORC_CAP = 2, ORC_ARG = 3 };
 
 // ---------------------------------------------------------------- C-2 classes
@@ -59,6 +65,19 @@ int class_of(uint32_t cp) {
   if (lo < kOrcNumRanges && kOrcRanges[lo][0] <= cp && cp <= kOrcRanges[lo][1])
     return int(kOrcRanges[lo][2]);
   return CO;
+}
+
+int subclass_of(uint32_t cp) {
+  size_t lo = 0, hi = kOrcNumSubRanges;
+  while (lo < hi) {
+    size_t mid = (lo + hi) / 2;
+    if (kOrcSubRanges[mid][1] < cp) lo = mid + 1;
+    else hi = mid;
+  }
+  if (lo < kOrcNumSubRanges && kOrcSubRanges[lo][0] <= cp && cp <= kOrcSubRanges[lo][1])
+    return int(kOrcSubRanges[lo][2]);
+  const int c = class_of(cp);
+  return c == CN ? SN : c == CW ? SW : SO;  // a letter always has a case class above
 }
 
 // case-insensitive equality with an ASCII lowercase letter
@@ -113,6 +132,7 @@ bool decode_utf8(const uint8_t* s, size_t n, std::vector<uint32_t>& cps,
 struct Text {
   std::vector<uint32_t> cp;
   std::vector<int> cls;
+  std::vector<int> sub;  // subclass_of, for the case-splitting family only
   size_t n() const { return cp.size(); }
 };
 
@@ -214,17 +234,119 @@ size_t llama3_next(const Text& t, size_t p) {
   return 0;
 }
 
+// Case-splitting (o200k-style) family, as read from TokTier, section 4
+// "Removing the sequential regex scan": the Llama-3-style alternatives, with
+// the letter alternative split at case boundaries, marks joining letters,
+// and the contractions moved to an optional suffix of a letter piece:
+//   P? H* T+ S? | P? H+ T* S? | N{1,3} | " "?[^\s L N]+[\r\n]* | \s*[\r\n]+
+//   | \s+(?!\S) | \s+
+// with H = U|C|M (upper, caseless, marks), T = D|C|M (lower, caseless,
+// marks), P = one char that is not CR, LF, a letter or a number, and S =
+// (?i:'s|'t|'re|'ve|'m|'ll|'d).  Each alternative is matched as a
+// backtracking engine would: the optional prefix is tried first taken, then
+// not; H* gives back one char at a time until T+ can start.
+bool in_h(int k) { return k == SU || k == SC || k == SM; }
+bool in_t(int k) { return k == SD || k == SC || k == SM; }
+bool in_p(const Text& t, size_t i) { return !is_crlf(t.cp[i]) && t.cls[i] != CL && t.cls[i] != CN; }
+
+// optional contraction suffix at q (case-insensitive), greedy
+size_t contraction_suffix(const Text& t, size_t q) {
+  if (q < t.n()) {
+    size_t e = match_contraction(t, q, true);
+    if (e) return e;
+  }
+  return q;
+}
+
+// P? H* T+ S? from cursor p; 0 if it does not match
+size_t match_split_lower(const Text& t, size_t p) {
+  const size_t n = t.n();
+  for (int pre = 1; pre >= 0; --pre) {
+    if (pre && !in_p(t, p)) continue;
+    const size_t q = p + pre;
+    size_t h = q;
+    while (h < n && in_h(t.sub[h])) ++h;
+    for (size_t x = h + 1; x-- > q;) {  // H* takes [q, x); T+ starts at x
+      if (x < n && in_t(t.sub[x])) {
+        size_t e = x;
+        while (e < n && in_t(t.sub[e])) ++e;
+        return contraction_suffix(t, e);
+      }
+    }
+  }
+  return 0;
+}
+
+// P? H+ T* S? from cursor p; 0 if it does not match
+size_t match_split_upper(const Text& t, size_t p) {
+  const size_t n = t.n();
+  for (int pre = 1; pre >= 0; --pre) {
+    if (pre && !in_p(t, p)) continue;
+    const size_t q = p + pre;
+    if (q >= n || !in_h(t.sub[q])) continue;
+    size_t h = q;
+    while (h < n && in_h(t.sub[h])) ++h;
+    size_t e = h;
+    while (e < n && in_t(t.sub[e])) ++e;
+    return contraction_suffix(t, e);
+  }
+  return 0;
+}
+
+size_t o200k_next(const Text& t, size_t p) {
+  const size_t n = t.n();
+  size_t q;
+  if ((q = match_split_lower(t, p))) return q;
+  if ((q = match_split_upper(t, p))) return q;
+  // \p{N}{1,3}
+  if (t.cls[p] == CN) {
+    q = p;
+    while (q < n && q < p + 3 && t.cls[q] == CN) ++q;
+    return q;
+  }
+  // " ?[^\s\p{L}\p{N}]+[\r\n]*": marks are not letters, so they count here
+  if ((q = match_space_run(t, p, CO))) {
+    while (q < n && is_crlf(t.cp[q])) ++q;
+    return q;
+  }
+  // \s*[\r\n]+
+  if (t.cls[p] == CW) {
+    size_t e = run_of(t, p, CW);
+    for (size_t k = e + 1; k-- > p;) {
+      if (k < n && is_crlf(t.cp[k])) {
+        q = k;
+        while (q < n && is_crlf(t.cp[q])) ++q;
+        return q;
+      }
+    }
+  }
+  if ((q = match_ws_lookahead(t, p))) return q;
+  if ((q = match_ws(t, p))) return q;
+  return 0;
+}
+
 // Pieces as code-point index boundaries [b_0=0, b_1, ..., b_m = n].
 std::vector<size_t> pretokenize(const Text& t, int pattern) {
   std::vector<size_t> starts;
   size_t p = 0;
   while (p < t.n()) {
     starts.push_back(p);
-    size_t q = pattern == PAT_GPT2 ? gpt2_next(t, p) : llama3_next(t, p);
+    size_t q = pattern == PAT_GPT2 ? gpt2_next(t, p) : pattern == PAT_LLAMA3 ? llama3_next(t, p) : o200k_next(t, p);
     if (q <= p) q = p + 1;  // unreachable: every class has an alternative
     p = q;
   }
   return starts;
+}
+
+// C-2 for a decoded text: classes, and for the case-splitting family the
+// letter-case and mark subclasses
+void classify(Text& t, int pattern) {
+  t.cls.resize(t.cp.size());
+  for (size_t i = 0; i < t.cp.size(); ++i) t.cls[i] = class_of(t.cp[i]);
+  if (pattern == PAT_O200K) {
+    t.sub.resize(t.cp.size());
+    for (size_t i = 0; i < t.cp.size(); ++i) t.sub[i] = subclass_of(t.cp[i]);
+  }
 }
 
 // ---------------------------------------------------------------- C-4 BPE
@@ -267,8 +389,7 @@ int encode_one(const Oracle& o, const uint8_t* s, size_t n, std::vector<int32_t>
   Text t;
   std::vector<size_t> offs;
   if (!decode_utf8(s, n, t.cp, offs)) return ORC_UTF8;
-  t.cls.resize(t.cp.size());
-  for (size_t i = 0; i < t.cp.size(); ++i) t.cls[i] = class_of(t.cp[i]);
+  classify(t, o.pattern);
   std::vector<size_t> st = pretokenize(t, o.pattern);
   std::vector<size_t> at;
   for (size_t k = 0; k < st.size(); ++k) {
@@ -288,10 +409,20 @@ extern "C" {
 
 int orc_class(uint32_t cp) { return class_of(cp); }
 
+// Classes of the code points lo .. lo + n - 1, one byte each.
+void orc_class_range(uint32_t lo, uint32_t n, uint8_t* out) {
+  for (uint32_t i = 0; i < n; ++i) out[i] = uint8_t(class_of(lo + i));
+}
+
+// Subclasses (U=0 D=1 C=2 M=3 N=4 W=5 O=6) of the code points lo .. lo + n - 1.
+void orc_subclass_range(uint32_t lo, uint32_t n, uint8_t* out) {
+  for (uint32_t i = 0; i < n; ++i) out[i] = uint8_t(subclass_of(lo + i));
+}
+
 // merges: n x (left, right); operands must precede their merge; pairs unique.
 void* orc_new(const uint32_t* merges, size_t n, int pattern, int* err) {
   *err = ORC_ARG;
-  if (pattern != PAT_GPT2 && pattern != PAT_LLAMA3) return nullptr;
+  if (pattern != PAT_GPT2 && pattern != PAT_LLAMA3 && pattern != PAT_O200K) return nullptr;
   Oracle* o = new Oracle();
   o->pattern = pattern;
   for (size_t r = 0; r < n; ++r) {
@@ -315,8 +446,7 @@ int orc_pieces(void* h, const uint8_t* text, size_t len, uint64_t* starts, size_
   std::vector<size_t> offs;
   *n_out = 0;
   if (!decode_utf8(text, len, t.cp, offs)) return ORC_UTF8;
-  t.cls.resize(t.cp.size());
-  for (size_t i = 0; i < t.cp.size(); ++i) t.cls[i] = class_of(t.cp[i]);
+  classify(t, o.pattern);
   std::vector<size_t> st = pretokenize(t, o.pattern);
   *n_out = st.size();
   if (st.size() > cap) return ORC_CAP;

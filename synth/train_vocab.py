@@ -36,6 +36,17 @@ CORPUS_DIR = os.path.join(HERE, "_corpus")
 PATTERNS = {
     "gpt2": r"""'s|'t|'re|'ve|'m|'ll|'d| ?\p{L}+| ?\p{N}+| ?[^\s\p{L}\p{N}]+|\s+(?!\S)|\s+""",
     "llama3": r"""(?i:'s|'t|'re|'ve|'m|'ll|'d)|[^\r\n\p{L}\p{N}]?\p{L}+|\p{N}{1,3}| ?[^\s\p{L}\p{N}]+[\r\n]*|\s*[\r\n]+|\s+(?!\S)|\s+""",
+    # case-splitting style, composed from TokTier's description of the o200k
+    # lineage (section 4, "Removing the sequential regex scan"): the Llama-3
+    # style with letter runs split at case boundaries (an optional run of
+    # upper-case or caseless letters or marks, then lower-case or caseless
+    # letters or marks), marks joining letters, and the contractions as an
+    # optional suffix of a letter piece
+    "o200k": (r"""[^\r\n\p{L}\p{N}]?[\p{Lu}\p{Lt}\p{Lm}\p{Lo}\p{M}]*[\p{Ll}\p{Lm}\p{Lo}\p{M}]+"""
+              r"""(?i:'s|'t|'re|'ve|'m|'ll|'d)?"""
+              r"""|[^\r\n\p{L}\p{N}]?[\p{Lu}\p{Lt}\p{Lm}\p{Lo}\p{M}]+[\p{Ll}\p{Lm}\p{Lo}\p{M}]*"""
+              r"""(?i:'s|'t|'re|'ve|'m|'ll|'d)?"""
+              r"""|\p{N}{1,3}| ?[^\s\p{L}\p{N}]+[\r\n]*|\s*[\r\n]+|\s+(?!\S)|\s+"""),
 }
 
 # name -> (generator, corpus seeds, chars per doc, pattern, merges)
