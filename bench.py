@@ -1,38 +1,48 @@
 """Benchmark: exact encode of one 1,000,000-character request on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_1m|llama3_3m|batch64|chat_1m|repair]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra]
 
-One step = one tok_encode_dev call over the whole request (pre-tokenization,
-piece pass with merges, count scan + scatter), with the UTF-8 text already
-resident in HBM and the int32 IDs left in HBM.  W untimed steps, then exactly
-K timed steps between two device synchronizations.  Prints one JSON line:
-value = input MB/s (UTF-8 bytes / s / 1e6), ms_per_step = ms per request.
+Headline (default workload gpt2_1m): one step = one tok_encode_dev call over a
+whole request (pre-tokenization, piece pass with merges, count scan +
+scatter), with the UTF-8 text already resident in HBM and the int32 IDs left
+in HBM.  Every step encodes a different seeded request of the same shape
+(fresh inputs, as in TokTier's Table 3 protocol): W + K distinct requests are
+generated and copied to HBM before the clock starts; W untimed steps, then
+exactly K timed steps between two device synchronizations.  Prints one JSON
+line: value = input MB/s (UTF-8 bytes / s / 1e6), ms_per_step = ms per request.
 
 Also reported, outside the headline value:
-  - roofline: the dominant kernel's algorithmic bytes per launch over its
-    average duration, timed with HIP events on the stream the kernels run on
-    during the timed steps (only that stage is bracketed by events there; the
-    warm-up steps time every stage to find it and give stages_ms), against the
-    8 TB/s HBM peak, with the counter-measured HBM traffic of that kernel from
-    the committed rocprofv3 summary when it matches the kernel's sources;
+  - roofline: the dominant kernel's algorithmic bytes per launch (input bytes
+    read once plus 4 bytes per output ID written once) over its average
+    duration, timed with HIP events on the stream the kernels run on during
+    the timed steps (only that stage is bracketed by events there; the
+    warm-up steps time every stage to find it and give stages_ms), against
+    the 8 TB/s HBM peak, with the counter-measured HBM traffic of that kernel
+    from the committed rocprofv3 summary when it matches the kernel's sources;
+  - steady_input: the same request encoded on every step;
   - complete_call: host bytes -> host int32 IDs through tok_encode (or
     tok_encode_batch for the batch; pinned staging, both transfers), the
     PCIe-inclusive rate;
   - graph_ab: median call time without stage timing, eager launches against
     a replayed HIP graph of the same call (tok_set_graph);
-  - fresh_inputs: median call time over distinct seeded requests of the same
-    shape (a new text on every call; the headline repeats one text);
   - span_export: median call time of the same encode with each token's first
     byte exported next to its ID (tok_encode_spans_dev);
-  - cpu_baseline: the CPU oracle on the same request, single-threaded; for
-    the batch, a pool of worker processes (one per core share, up to 16), one
-    document prefix each, timed in parallel.
+  - cpu_baseline: the CPU oracle on a bounded sample of the same workload,
+    single-threaded (for the batch, a pool of worker processes, one document
+    each), with the host's CPU model and core count;
+  - configs: the other workloads (tiny 10K-char request, 3M-char Llama-3-style
+    request, 64 x 500K batch, CJK-dense 1M request, chat transcript with
+    added-token literals, append repair), each with its own rate, roofline
+    fraction, complete call and oracle rate (skipped with --no-extra).
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures
 import json
+import multiprocessing
 import os
+import platform
 import statistics
 import sys
 import time
@@ -45,22 +55,29 @@ import numpy as np  # noqa: E402
 METRIC = "ms per 1M-char request encode (input MB/s) + % HBM roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 
+CHAT_MARKERS = ["<|im_start|>", "<|im_end|>", "<|endoftext|>", "<|tool_call|>", "<|im_sep|>"]
+
 WORKLOADS = {
-    # name: (description, merges, pattern, generator seed, chars, docs)
-    "gpt2_1m": ("1M-char agent-transcript request, GPT-2-style pattern, 50K merges", "gpt2_50k", "gpt2", 2,
+    # name: (description, merges, pattern, generator, seed, chars per request, documents)
+    "tiny_10k": ("10,000-char ASCII request, GPT-2-style pattern, 1,000 merges", "tiny_1k", "gpt2", "tiny", 1,
+                 10_000, 1),
+    "gpt2_1m": ("1M-char agent-transcript request, GPT-2-style pattern, 50K merges", "gpt2_50k", "gpt2", "mix", 2,
                 1_000_000, 1),
     "llama3_3m": ("3M-char agent-transcript request, Llama-3-style pattern, 127,744 merges", "llama3_128k",
-                  "llama3", 3, 3_000_000, 1),
+                  "llama3", "mix", 3, 3_000_000, 1),
     "batch64": ("64 requests x 500K chars, Llama-3-style pattern, 127,744 merges, one batch call",
-                "llama3_128k", "llama3", 40_000, 500_000, 64),
+                "llama3_128k", "llama3", "mix", 40_000, 500_000, 64),
+    # CJK-dense text: every ideograph run is one long letter piece (the long-piece merge path)
+    "cjk_1m": ("1M-char CJK-dense request (ideograph runs of 50-2,000 chars), GPT-2-style pattern, 50K merges",
+               "gpt2_50k", "gpt2", "cjk", 5, 1_000_000, 1),
     # chat transcript with added-token markers taken ahead of the pattern (tok_set_added_tokens)
     "chat_1m": ("1M-char chat transcript with 5 added-token markers, GPT-2-style pattern, 50K merges",
-                "gpt2_50k", "gpt2", 7, 1_000_000, 1),
-    # append repair: stored 1M-char context + 1,400-char appends (a latency, not a bench headline)
+                "gpt2_50k", "gpt2", "chat", 7, 1_000_000, 1),
+    # append repair: stored 1M-char context + 1,400-char appends (a latency)
     "repair": ("tok_repair: 1M-char stored context + 1,400-char append, GPT-2-style pattern, 50K merges",
-               "gpt2_50k", "gpt2", 2, 1_000_000, 1),
+               "gpt2_50k", "gpt2", "mix", 2, 1_000_000, 1),
 }
-
+EXTRA = ["tiny_10k", "llama3_3m", "batch64", "cjk_1m", "chat_1m", "repair"]
 
 # dominant-stage kernel and the sources its code comes from (for matching
 # committed counter summaries to the kernel that produced them)
@@ -72,16 +89,108 @@ STAGE_KERNELS = {
 }
 
 
-CHAT_MARKERS = ["<|im_start|>", "<|im_end|>", "<|endoftext|>", "<|tool_call|>", "<|im_sep|>"]
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
 
 
-def request_text(workload: str, seed: int, n_chars: int) -> bytes:
+# ------------------------------------------------------------------ inputs
+
+def gen_request(job) -> bytes:
+    """One seeded request (a pool job: (generator, seed, chars))."""
+    kind, seed, n_chars = job
     from synth import textgen
 
-    if workload == "chat_1m":
+    if kind == "tiny":
+        return textgen.tiny_text(seed, n_chars).encode()
+    if kind == "chat":
         return textgen.chat_text(seed, n_chars, CHAT_MARKERS).encode()
+    if kind == "cjk":
+        return textgen.cjk_text(seed, n_chars).encode()
     return textgen.mix_text(seed, n_chars).encode()
 
+
+def fresh_seed(seed: int, k: int) -> int:
+    """Seed of the k-th fresh request of a workload (k = 0 is the workload's own request)."""
+    return seed if k == 0 else seed + 1000 * k
+
+
+def cpu_facts() -> dict:
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": usable, "logical_cpus": os.cpu_count()}
+
+
+def pool_size() -> int:
+    return max(1, min(16, cpu_facts()["nproc"]))
+
+
+def generate(jobs: list) -> list:
+    """Texts of the jobs, generated in parallel (spawned processes: this runs
+    before the GPU is touched)."""
+    with concurrent.futures.ProcessPoolExecutor(pool_size(), mp_context=multiprocessing.get_context("spawn")) as ex:
+        return list(ex.map(gen_request, jobs))
+
+
+def _pool_worker(job):
+    """One process of the batch's CPU-baseline pool: build the oracle and the
+    document outside the clock, then time its encode three times."""
+    merges_name, pattern, kind, seed, n_chars = job
+    import oracle
+    from tests import vocab
+
+    o = oracle.Oracle(vocab.merges(merges_name), pattern)
+    b = gen_request((kind, seed, n_chars))
+    s0 = time.perf_counter()
+    for _ in range(3):
+        o.encode(b)
+    return 3 * len(b), time.perf_counter() - s0
+
+
+def pool_baseline(merges_name, pattern, kind, base_seed, n_docs, n_chars):
+    """The CPU oracle over a batch with a process pool (one worker per core
+    share, at most one per document), started before this process touches the
+    GPU: aggregate and per-core MB/s."""
+    workers = max(1, min(n_docs, pool_size()))
+    jobs = [(merges_name, pattern, kind, base_seed + i, n_chars) for i in range(workers)]
+    with concurrent.futures.ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("spawn")) as ex:
+        res = list(ex.map(_pool_worker, jobs))
+    total = sum(r[0] for r in res)
+    wall = max(r[1] for r in res)
+    per_core = sum(r[0] / r[1] for r in res) / len(res)
+    return {"value": round(total / wall / 1e6, 3), "unit": "MB/s", "cores": workers, "kind": "oracle",
+            "per_core_mbps": round(per_core / 1e6, 3),
+            "sample": f"{workers} documents of the batch ({n_chars} characters each), one per worker process in "
+                      f"parallel, each encoded 3 times; aggregate = their bytes over the slowest worker's time",
+            **cpu_facts()}
+
+
+def oracle_rate(merges, pattern, sample: bytes, seconds: float, literals=None, what="") -> dict:
+    """The CPU oracle as it stands, single thread, on a bounded sample."""
+    import oracle
+
+    o = oracle.Oracle(merges, pattern)
+    reps, t_cpu = 0, 0.0
+    while t_cpu < seconds and reps < 200:
+        s0 = time.perf_counter()
+        o.encode(sample) if literals is None else o.encode_added(sample, literals)
+        t_cpu += time.perf_counter() - s0
+        reps += 1
+    return {"value": round(len(sample) * reps / t_cpu / 1e6, 3), "unit": "MB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{what} ({len(sample)} bytes) {reps} times, single thread ({t_cpu:.1f} s)", **cpu_facts()}
+
+
+# ---------------------------------------------------------------- measures
 
 def source_digest(stage: str) -> str:
     import hashlib
@@ -109,44 +218,162 @@ def profiled(workload: str, stage: str, field: str):
     return int(k[field])
 
 
-def measured_traffic(workload: str, stage: str):
-    return profiled(workload, stage, "bytes_per_launch")
-
-
-# VALU issue peak: the published fp32 vector peak, 157.3 TFLOP/s = 256 CUs x
-# 4 SIMDs x 32 lanes x 2 flops (FMA) x 2.4 GHz, is one wave64 instruction per
-# 2 cycles per SIMD: 1228.8 G wave64 instructions/s
+# Vector-issue rate used as the ALU reference.  The published fp32 vector
+# peak, 157.3 TFLOP/s = 256 CUs x 4 SIMDs x 32 lanes x 2 flops x 2.4 GHz, read
+# as one wave64 instruction per 2 cycles per SIMD: 1228.8 G wave64
+# instructions/s.  That reading is inferred (the fp32 figure counts packed
+# math), kept because the counted instructions of the batch's pre-tokenization
+# kernel exceed a 4-cycle issue model; it is an upper bound, not a measured
+# issue rate.
 VALU_PEAK_G = 256 * 4 * 2.4e9 / 2 / 1e9
 
 
 def valu_issue(workload: str, stage: str, avg_ms: float):
-    """Vector-instruction issue rate of the kernel: its counted wave64 VALU
-    instructions per launch (committed counter summary) over the live average
-    duration, against the chip's issue peak."""
     v = profiled(workload, stage, "valu_wave_instr")
     if v is None or avg_ms <= 0:
         return None
     g = v / (avg_ms * 1e-3) / 1e9
     return {"achieved": round(g, 1), "peak": round(VALU_PEAK_G, 1), "unit": "G wave64 VALU instr/s",
-            "frac": round(g / VALU_PEAK_G, 4), "instr_per_launch": v}
+            "frac": round(g / VALU_PEAK_G, 4), "instr_per_launch": v,
+            "peak_basis": "inferred: 1 wave64 VALU instruction per 2 cycles per SIMD (an upper bound consistent "
+                          "with the counters, not a published issue rate)"}
 
 
-def log(*a):
-    print(*a, file=sys.stderr, flush=True)
+def algorithmic_bytes(n_bytes: int, n_tokens: int) -> int:
+    """What the path must move per request: the input read once and 4 bytes
+    per output ID written once (intermediates are implementation overhead)."""
+    return n_bytes + 4 * n_tokens
 
 
-def algorithmic_bytes(stage: str, n_bytes: int, n_tokens: int) -> int:
-    """Bytes a stage must move through its interface buffers, once each."""
-    chunks = (n_bytes + 15) // 16
-    flags = 2 * chunks
-    if stage == "pretokenize":      # text in, piece-start flags out
-        return n_bytes + flags
-    if stage == "pieces":           # text and flags in, each tile's run of int32 IDs out
-        return n_bytes + flags + 4 * n_tokens
-    if stage == "assemble":         # runs in, IDs out
-        return 8 * n_tokens
-    return 0
+def pct(v, q):
+    return round(1e3 * float(np.percentile(v, q)), 4)
 
+
+class Leg:
+    """Device buffers of one workload on one tokenizer and its encode step."""
+
+    def __init__(self, tok, texts: list, doc_off=None, stream=None):
+        import torch
+
+        self.tok = tok
+        self.stream = stream
+        self.texts = texts
+        self.doc_off = doc_off
+        self.d_texts = [torch.frombuffer(bytearray(t), dtype=torch.uint8).cuda() for t in texts]
+        self.d_ids = torch.empty(max(len(t) for t in texts), dtype=torch.int32, device="cuda")
+        if doc_off is not None:
+            n_docs = len(doc_off) - 1
+            self.d_off = torch.tensor(doc_off.astype(np.int64), device="cuda").view(torch.uint64)
+            self.d_out = torch.empty(n_docs + 1, dtype=torch.int64, device="cuda").view(torch.uint64)
+        torch.cuda.synchronize()
+
+    def step(self, k: int) -> int:
+        d = self.d_texts[k % len(self.d_texts)]
+        if self.doc_off is None:
+            return self.tok.encode_dev(d, self.d_ids, stream=self.stream)
+        return self.tok.encode_batch_dev(d, self.d_off, self.d_ids, self.d_out, stream=self.stream)
+
+    def run(self, warmup: int, steps: int, first: int = 0) -> dict:
+        """W warm-up steps with every stage timed (to find the dominant one),
+        then K timed steps with only that stage bracketed by events.  Step i
+        encodes text (first + i) of the leg's list (cycled)."""
+        import torch
+
+        import exact_byte_level_utf8_amd as tk
+
+        tok = self.tok
+        tok.set_profiling(True)
+        warm = []
+        for i in range(max(warmup, 2)):
+            self.step(first + i)
+            if i > 0 or warmup <= 1:
+                warm.append(tok.stage_ms())
+        torch.cuda.synchronize()
+        stage_avg = np.mean(np.asarray(warm), axis=0)
+        stages = {name: round(float(v), 5) for name, v in zip(tk.STAGES, stage_avg)}
+        dom = max(("pretokenize", "pieces", "assemble"), key=lambda s: stages[s])
+        dom_i = tk.STAGES.index(dom)
+        tok.set_profiling(1 << dom_i)
+        dom_sum, per_step, alg, nbytes, ntok = 0.0, [], 0, 0, 0
+        base = first + max(warmup, 2)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            s0 = time.perf_counter()
+            n = self.step(base + i)
+            per_step.append(time.perf_counter() - s0)
+            dom_sum += tok.stage_ms()[dom_i]
+            nb = len(self.texts[(base + i) % len(self.texts)])
+            alg += algorithmic_bytes(nb, n)
+            nbytes += nb
+            ntok += n
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        tok.set_profiling(False)
+        dom_ms = dom_sum / steps
+        achieved = (alg / steps) / (dom_ms * 1e-3) / 1e9 if dom_ms > 0 else 0.0
+        return {"ms_per_step": round(1e3 * elapsed / steps, 5), "mbps": round(nbytes / elapsed / 1e6, 2),
+                "latency_ms": {"p50": round(1e3 * statistics.median(per_step), 4), "p90": pct(per_step, 90),
+                               "p99": pct(per_step, 99)},
+                "stages_ms": stages, "dominant": dom, "dom_ms": round(dom_ms, 5),
+                "alg_bytes_per_launch": int(alg / steps), "achieved_gbs": round(achieved, 2),
+                "frac": round(achieved / HBM_PEAK_GBS, 6), "tokens_per_step": int(ntok / steps),
+                "bytes_per_step": int(nbytes / steps), "distinct_inputs": min(steps, len(self.texts))}
+
+    def complete_call(self, reps: int) -> dict:
+        """Host bytes in, host IDs out (text 0 of the leg)."""
+        tok, text = self.tok, self.texts[0]
+        cc = []
+        for _ in range(reps):
+            s0 = time.perf_counter()
+            tok.encode(text) if self.doc_off is None else tok.encode_batch(text, self.doc_off)
+            cc.append(time.perf_counter() - s0)
+        med = statistics.median(cc)
+        call = "tok_encode" if self.doc_off is None else "tok_encode_batch"
+        return {"p50_ms": round(1e3 * med, 4), "mbps": round(len(text) / med / 1e6, 1),
+                "note": f"{call}: pinned staging + H2D text + pipeline + D2H IDs"}
+
+    def median_step(self, k: int) -> float:
+        v = []
+        for _ in range(k):
+            s0 = time.perf_counter()
+            self.step(0)
+            v.append(time.perf_counter() - s0)
+        return statistics.median(v)
+
+    def graph_ab(self, k: int) -> dict:
+        eager = self.median_step(k)
+        self.tok.set_graph(True)
+        self.step(0)
+        self.step(0)  # the second call of a shape captures its graph
+        graph = self.median_step(k)
+        held = self.tok.graph_count()
+        self.tok.set_graph(False)
+        return {"eager_p50_ms": round(1e3 * eager, 4), "graph_p50_ms": round(1e3 * graph, 4), "graphs": held,
+                "steps": k}
+
+    def span_export(self, k: int) -> dict:
+        import torch
+
+        d_spans = torch.empty(self.d_ids.numel(), dtype=torch.int32, device="cuda")
+        d = self.d_texts[0]
+
+        def span_step():
+            if self.doc_off is None:
+                return self.tok.encode_spans_dev(d, self.d_ids, d_spans, stream=self.stream)
+            return self.tok.encode_spans_dev(d, self.d_ids, d_spans, self.d_off, self.d_out, stream=self.stream)
+
+        span_step()
+        sv = []
+        for _ in range(k):
+            s0 = time.perf_counter()
+            span_step()
+            sv.append(time.perf_counter() - s0)
+        return {"p50_ms": round(1e3 * statistics.median(sv), 4), "steps": k,
+                "note": "tok_encode_spans_dev: IDs plus each token's first byte, device-resident"}
+
+
+# ------------------------------------------------------------------ repair
 
 def large_appends(tok, base: str, seed: int, reps: int = 5) -> list:
     """Appends of 50K characters and more, where TokTier's delta-aware routing
@@ -185,21 +412,17 @@ def large_appends(tok, base: str, seed: int, reps: int = 5) -> list:
     return rows
 
 
-def bench_repair(args, desc, merges_name, pattern, seed, n_chars) -> int:
-    """Latency of tok_repair over seeded appends (host text and IDs, one GPU
-    window encode per call).  Each case's stored IDs are prepared in a
-    caller-owned buffer outside the timed call; only the C call is timed."""
+def repair_leg(tok, base: str, seed: int, warmup: int, steps: int, with_large: bool) -> dict:
+    """Latency of tok_repair and tok_repair_dev over seeded 1,400-char appends
+    to the 1M-char context (host text; IDs in a caller-owned host buffer, or
+    in device memory).  Each case's stored IDs are prepared outside the timed
+    call; only the C call is timed."""
     import torch
 
-    import exact_byte_level_utf8_amd as tk
     from synth import textgen
-    from tests import vocab
 
-    torch.cuda.set_device(0)
-    tok = tk.Tokenizer(vocab.merges(merges_name), pattern, device=0)
-    base = textgen.mix_text(seed, n_chars)
     lat, dlat, full, widen = [], [], 0, 0
-    for i in range(args.warmup + args.steps):
+    for i in range(warmup + steps):
         old, suf = textgen.repair_case(seed, 70_000 + i, old_text=base, append_chars=1_400)
         ob, text = old.encode(), (old + suf).encode()
         sess = tok.encode(ob)
@@ -214,76 +437,32 @@ def bench_repair(args, desc, merges_name, pattern, seed, n_chars) -> int:
         dn, dinfo = tok.repair_dev(d_sess, sess.size, text, len(ob))
         ddt = time.perf_counter() - s0
         assert dn == n and dinfo == info
-        if i >= args.warmup:
+        if i >= warmup:
             lat.append(dt)
             dlat.append(ddt)
             full += info["full"]
             widen += info["widenings"]
-    p50 = statistics.median(lat)
-    large = large_appends(tok, base, seed)
-    out = {"metric": "tok_repair latency (ms, P50)", "value": round(1e3 * p50, 4), "unit": "ms", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
-           "latency_ms": {"p50": round(1e3 * p50, 4), "p90": round(1e3 * float(np.percentile(lat, 90)), 4),
-                          "p99": round(1e3 * float(np.percentile(lat, 99)), 4)},
-           "device_session_ms": {"p50": round(1e3 * statistics.median(dlat), 4),
-                                 "p90": round(1e3 * float(np.percentile(dlat, 90)), 4),
-                                 "note": "tok_repair_dev: session IDs in device memory, match and splice on the device"},
-           "full_encodes": full, "widenings": widen, "large_appends": large, "dtype": "u8->int32",
-           "data": "synthetic (seeded generator; host text and IDs)",
-           "config": {"workload": desc, "context_chars": n_chars, "append_chars": 1400, "merges": merges_name,
-                      "pattern": pattern, "seed": seed}}
-    print(json.dumps(out), flush=True)
-    tok.close()
-    return 0
+    out = {"latency_ms": {"p50": round(1e3 * statistics.median(lat), 4), "p90": pct(lat, 90), "p99": pct(lat, 99)},
+           "device_session_ms": {"p50": round(1e3 * statistics.median(dlat), 4), "p90": pct(dlat, 90),
+                                 "note": "tok_repair_dev: session IDs in device memory, match and splice on the "
+                                         "device"},
+           "appends": steps, "full_encodes": full, "widenings": widen}
+    if with_large:
+        out["large_appends"] = large_appends(tok, base, seed)
+    return out
 
 
-def _pool_worker(job):
-    """One process of the batch's CPU-baseline pool: build the oracle and the
-    document's sample outside the clock, then time its encode."""
-    merges_name, pattern, seed, n_chars = job
-    import oracle
-    from synth import textgen
-    from tests import vocab
-
-    o = oracle.Oracle(vocab.merges(merges_name), pattern)
-    b = textgen.mix_text(seed, n_chars).encode()
-    s0 = time.perf_counter()
-    for _ in range(3):
-        o.encode(b)
-    return 3 * len(b), time.perf_counter() - s0
-
-
-def pool_baseline(merges_name, pattern, base_seed, n_docs, n_chars):
-    """The CPU oracle over a batch with a process pool (one worker per core
-    share, at most one per document), started before this process touches the
-    GPU: aggregate and per-core MB/s."""
-    import concurrent.futures
-    import multiprocessing
-
-    workers = max(1, min(n_docs, 16, os.cpu_count() or 1))
-    jobs = [(merges_name, pattern, base_seed + i, n_chars) for i in range(workers)]
-    with concurrent.futures.ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("spawn")) as ex:
-        res = list(ex.map(_pool_worker, jobs))
-    total = sum(r[0] for r in res)
-    wall = max(r[1] for r in res)
-    per_core = sum(r[0] / r[1] for r in res) / len(res)
-    return {"value": round(total / wall / 1e6, 3), "unit": "MB/s", "cores": workers, "kind": "oracle",
-            "per_core_mbps": round(per_core / 1e6, 3),
-            "sample": f"{workers} documents of the batch ({n_chars} characters each), one per worker process in "
-                      f"parallel, each encoded 3 times; aggregate = their bytes over the slowest worker's time"}
-
+# -------------------------------------------------------------------- main
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gpt2_1m", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-extra", action="store_true", help="only the chosen workload (profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--fresh", type=int, default=-1,
-                    help="distinct seeded requests of the same shape for the fresh-input leg (default: 4 for a "
-                         "single request, 0 for the batch)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one device-to-device copy of this many MiB: a kernel of "
                          "known traffic that scales the HBM byte counters of a profiler run")
@@ -293,76 +472,111 @@ def main() -> int:
               "(the tokenizer runs on a single MI355X)", file=sys.stderr)
         return 2
 
+    from synth import textgen
+
+    head = args.workload
+    names = [head] + ([] if args.no_extra else [w for w in EXTRA if w != head])
+    # every text, generated before the GPU is touched: the headline's W + K
+    # fresh requests (a single request) and each other workload's request
+    jobs, where = [], {}
+    for w in names:
+        desc, merges_name, pattern, kind, seed, n_chars, n_docs = WORKLOADS[w]
+        if n_docs > 1:
+            ks = [(kind, seed + i, n_chars) for i in range(n_docs)]
+        elif w == head and w != "repair":
+            ks = [(kind, fresh_seed(seed, k), n_chars) for k in range(max(args.warmup, 2) + args.steps)]
+        else:
+            ks = [(kind, seed, n_chars)]
+        where[w] = (len(jobs), len(ks))
+        jobs += ks
+    t0 = time.time()
+    texts_all = generate(jobs)
+    log(f"[bench] {len(jobs)} texts generated in {time.time() - t0:.1f}s ({pool_size()} processes)")
+    pools = {}
+    if not args.no_cpu_baseline:
+        for w in names:
+            desc, merges_name, pattern, kind, seed, n_chars, n_docs = WORKLOADS[w]
+            if n_docs > 1:  # worker processes: started before the GPU is touched
+                pools[w] = pool_baseline(merges_name, pattern, kind, seed, n_docs, n_chars)
+                log(f"[bench] cpu oracle pool ({w}): {pools[w]}")
+
     import torch
 
     import exact_byte_level_utf8_amd as tk
-    from synth import textgen
     from tests import vocab
 
-    desc, merges_name, pattern, seed, n_chars, n_docs = WORKLOADS[args.workload]
-    if args.workload == "repair":
-        return bench_repair(args, desc, merges_name, pattern, seed, n_chars)
-    pool_cpu = None
-    if n_docs > 1 and not args.no_cpu_baseline:  # before the GPU is touched: workers are fresh processes
-        pool_cpu = pool_baseline(merges_name, pattern, seed, n_docs, n_chars)
-        log(f"[bench] cpu oracle pool: {pool_cpu}")
-    t0 = time.time()
-    if n_docs == 1:
-        text = request_text(args.workload, seed, n_chars)
-        doc_off = None
-    else:
-        text, doc_off = textgen.pack_docs(textgen.batch_texts(seed, n_docs, n_chars))
-    n_bytes = len(text)
-    log(f"[bench] workload {args.workload}: {n_bytes} bytes generated in {time.time() - t0:.1f}s")
-
-    merges = vocab.merges(merges_name)
     torch.cuda.set_device(0)
-    tok = tk.Tokenizer(merges, pattern, device=0)
-    literals = None
-    if args.workload == "chat_1m":
-        literals = [(m.encode(), 256 + len(merges) + i) for i, m in enumerate(CHAT_MARKERS)]
-        tok.set_added_tokens(literals)
     stream = torch.cuda.current_stream()
-    d_text = torch.frombuffer(bytearray(text), dtype=torch.uint8).cuda()
-    d_ids = torch.empty(n_bytes, dtype=torch.int32, device="cuda")
-    if doc_off is not None:
-        d_off = torch.tensor(doc_off.astype(np.int64), device="cuda").view(torch.uint64)
-        d_out = torch.empty(n_docs + 1, dtype=torch.int64, device="cuda").view(torch.uint64)
+    toks = {}
 
-    def step() -> int:
-        if doc_off is None:
-            return tok.encode_dev(d_text, d_ids, stream=stream)
-        return tok.encode_batch_dev(d_text, d_off, d_ids, d_out, stream=stream)
+    def tokenizer(merges_name, pattern):
+        if (merges_name, pattern) not in toks:
+            toks[(merges_name, pattern)] = tk.Tokenizer(vocab.merges(merges_name), pattern, device=0)
+        return toks[(merges_name, pattern)]
 
-    # warm-up: every stage timed, to find the dominant one
-    tok.set_profiling(True)
-    warm_stages = []
-    for i in range(max(args.warmup, 2)):
-        n_tokens = step()
-        if i > 0:
-            warm_stages.append(tok.stage_ms())
-    torch.cuda.synchronize()
-    stage_avg = np.mean(np.asarray(warm_stages), axis=0)
-    stages = {name: round(float(v), 5) for name, v in zip(tk.STAGES, stage_avg)}
-    dom = max(("pretokenize", "pieces", "assemble"), key=lambda s: stages[s])
-    dom_i = tk.STAGES.index(dom)
-    log(f"[bench] warmup done: {n_tokens} tokens; stages {stages}")
-
-    # timed region: K steps; HIP events inside the library time the dominant
-    # stage on the stream it runs on
-    tok.set_profiling(1 << dom_i)
-    dom_sum = 0.0
-    per_step = []
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        s0 = time.perf_counter()
-        n_tokens = step()
-        per_step.append(time.perf_counter() - s0)
-        dom_sum += tok.stage_ms()[dom_i]
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    tok.set_profiling(False)
+    results = {}
+    for w in names:
+        desc, merges_name, pattern, kind, seed, n_chars, n_docs = WORKLOADS[w]
+        i0, cnt = where[w]
+        texts = texts_all[i0:i0 + cnt]
+        merges = vocab.merges(merges_name)
+        tok = tokenizer(merges_name, pattern)
+        literals = None
+        if kind == "chat":
+            literals = [(m.encode(), 256 + len(merges) + i) for i, m in enumerate(CHAT_MARKERS)]
+        tok.set_added_tokens(literals or [])
+        r = {"workload": desc, "merges": merges_name, "pattern": pattern, "seed": seed}
+        if w == "repair":
+            base = texts[0].decode()
+            steps = args.steps if w == head else 20
+            r.update(repair_leg(tok, base, seed, args.warmup, steps, with_large=True))
+            results[w] = r
+            log(f"[bench] {w}: {r['latency_ms']}")
+            continue
+        if n_docs > 1:
+            data, doc_off = textgen.pack_docs([t.decode() for t in texts])
+            leg = Leg(tok, [data], doc_off, stream)
+        else:
+            leg = Leg(tok, texts, None, stream)
+        steps = args.steps if w == head else (5 if n_docs > 1 else 10)
+        main_run = leg.run(args.warmup, steps)
+        r.update(main_run)
+        r["bytes"] = len(leg.texts[0])
+        r["docs"] = n_docs
+        r["chars"] = n_chars * n_docs
+        r["protocol"] = ("fresh: a distinct seeded request on every step, all resident in HBM before the clock"
+                         if len(leg.texts) > 1 else "steady: the same input on every step")
+        if w == head and len(leg.texts) > 1:
+            steady = Leg(tok, [leg.texts[0]], None, stream)
+            r["steady_input"] = steady.run(args.warmup, args.steps)
+            del steady
+        r["complete_call"] = leg.complete_call(max(3, steps // 4) if w == head else 3)
+        if w == head:
+            k_ab = max(20, args.steps)
+            r["graph_ab"] = leg.graph_ab(k_ab)
+            r["span_export"] = leg.span_export(k_ab) if literals is None else None
+        # the oracle on a bounded sample of the same workload
+        if not args.no_cpu_baseline:
+            if w in pools:
+                r["cpu_baseline"] = pools[w]
+            else:
+                sample = leg.texts[0]
+                what = "the whole request"
+                if kind == "cjk":  # textbook BPE is quadratic in a piece's length: a prefix
+                    cut = 20_000
+                    while cut < len(sample) and (sample[cut] & 0xC0) == 0x80:
+                        cut += 1
+                    sample, what = sample[:cut], "the request's first 20,000 bytes"
+                secs = args.cpu_seconds if w == head else 1.0
+                r["cpu_baseline"] = oracle_rate(merges, pattern, sample, secs, literals, what)
+        r["roofline"] = {"bound": "hbm", "kernel": main_run["dominant"], "achieved": main_run["achieved_gbs"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": main_run["frac"],
+                         "traffic": profiled(w, main_run["dominant"], "bytes_per_launch"),
+                         "algorithmic_bytes": main_run["alg_bytes_per_launch"], "avg_ms": main_run["dom_ms"],
+                         "valu_issue": valu_issue(w, main_run["dominant"], main_run["dom_ms"])}
+        results[w] = r
+        log(f"[bench] {w}: {r['ms_per_step']} ms/step, {r['mbps']} MB/s, frac {r['frac']}")
+        del leg
     if args.copy_probe_mib > 0:
         src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -371,145 +585,44 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"[bench] copy probe: {args.copy_probe_mib} MiB device-to-device")
         del src, dst
-    ms_per_step = 1e3 * elapsed / args.steps
-    mbps = n_bytes * args.steps / elapsed / 1e6
-    log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step, {mbps:.1f} MB/s")
-    dom_ms = round(dom_sum / args.steps, 5)
-    alg = algorithmic_bytes(dom, n_bytes, n_tokens)
-    achieved = alg / (dom_ms * 1e-3) / 1e9 if dom_ms > 0 else 0.0
 
-    # complete call: host bytes in, host IDs out
-    cc = []
-    for i in range(max(5, args.steps // 5)):
-        s0 = time.perf_counter()
-        ids_host = tok.encode(text) if doc_off is None else tok.encode_batch(text, doc_off)[0]
-        cc.append(time.perf_counter() - s0)
-    assert len(ids_host) == n_tokens
-    med = statistics.median(cc)
-    call = "tok_encode" if doc_off is None else "tok_encode_batch"
-    complete = {"p50_ms": round(1e3 * med, 4), "mbps": round(n_bytes / med / 1e6, 1),
-                "note": f"{call}: pinned staging + H2D text + pipeline + D2H IDs"}
-
-    # graph replay A/B (outside the timed region): the same step without stage
-    # timing, three launches per call against one replayed graph per call
-    def median_step(k: int) -> float:
-        v = []
-        for _ in range(k):
-            s0 = time.perf_counter()
-            assert step() == n_tokens
-            v.append(time.perf_counter() - s0)
-        return statistics.median(v)
-
-    # fresh inputs (outside the timed region): a different seeded request of
-    # the same shape on every call, each resident in HBM before its call
-    fresh = None
-    n_fresh = args.fresh if args.fresh >= 0 else (4 if doc_off is None else 0)
-    if n_fresh > 0 and doc_off is None:
-        texts = [request_text(args.workload, seed + 1000 * (k + 1), n_chars) for k in range(n_fresh)]
-        d_texts = [torch.frombuffer(bytearray(t), dtype=torch.uint8).cuda() for t in texts]
-        d_fids = torch.empty(max(len(t) for t in texts), dtype=torch.int32, device="cuda")
-        torch.cuda.synchronize()
-        fv, fb = [], 0
-        for rep in range(4):
-            for t, d in zip(texts, d_texts):
-                s0 = time.perf_counter()
-                tok.encode_dev(d, d_fids, stream=stream)
-                dt = time.perf_counter() - s0
-                if rep > 0:  # the first pass over the set is warm-up
-                    fv.append(dt)
-                    fb += len(t)
-        fresh = {"p50_ms": round(1e3 * statistics.median(fv), 4),
-                 "p90_ms": round(1e3 * float(np.percentile(fv, 90)), 4),
-                 "mbps": round(fb / sum(fv) / 1e6, 1), "requests": n_fresh, "calls": len(fv),
-                 "note": f"{n_fresh} distinct seeded requests of {n_chars} chars, cycled; device-resident"}
-        log(f"[bench] fresh inputs: {fresh}")
-        del d_texts, d_fids
-
-    k_ab = max(20, args.steps)
-    # span export (outside the timed region): the same call that also writes
-    # each token's first byte (a second int32 per token)
-    d_spans = torch.empty(n_bytes, dtype=torch.int32, device="cuda")
-
-    def span_step() -> int:
-        if doc_off is None:
-            return tok.encode_spans_dev(d_text, d_ids, d_spans, stream=stream)
-        return tok.encode_spans_dev(d_text, d_ids, d_spans, d_off, d_out, stream=stream)
-
-    span_export = None
-    if literals is None:  # span export refuses added-token literals
-        span_step()
-        sv = []
-        for _ in range(k_ab):
-            s0 = time.perf_counter()
-            assert span_step() == n_tokens
-            sv.append(time.perf_counter() - s0)
-        span_export = {"p50_ms": round(1e3 * statistics.median(sv), 4), "steps": k_ab,
-                       "note": "tok_encode_spans_dev: IDs plus each token's first byte, device-resident"}
-    del d_spans
-    eager_p50 = median_step(k_ab)
-    tok.set_graph(True)
-    step()
-    step()  # the second call of a shape captures its graph
-    graph_p50 = median_step(k_ab)
-    graphs_held = tok.graph_count()
-    tok.set_graph(False)
-    graph_ab = {"eager_p50_ms": round(1e3 * eager_p50, 4), "graph_p50_ms": round(1e3 * graph_p50, 4),
-                "graphs": graphs_held, "steps": k_ab}
-    log(f"[bench] graph A/B: {graph_ab}")
-
-    cpu = pool_cpu
-    if not args.no_cpu_baseline and cpu is None:
-        import oracle
-
-        o = oracle.Oracle(merges, pattern)
-        if doc_off is None:
-            sample, what = text, f"the whole {n_bytes}-byte request, repeated"
-        else:
-            sample = text[int(doc_off[0]):int(doc_off[1])]
-            what = f"document 0 of the batch ({len(sample)} bytes), repeated"
-        reps, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds and reps < 200:
-            s0 = time.perf_counter()
-            o.encode(sample) if literals is None else o.encode_added(sample, literals)
-            t_cpu += time.perf_counter() - s0
-            reps += 1
-        cpu = {"value": round(len(sample) * reps / t_cpu / 1e6, 3), "unit": "MB/s", "cores": 1,
-               "kind": "oracle", "sample": f"{what} {reps} times, single thread ({t_cpu:.1f} s)"}
-        log(f"[bench] cpu oracle: {cpu['value']} MB/s")
-
-    out = {
-        "metric": METRIC,
-        "value": round(mbps, 2),
-        "unit": "MB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "strong",
-        "vs_baseline": None,
-        "dtype": "u8->int32",
-        "data": "synthetic (seeded generator, inputs resident in HBM)",
-        "config": {"workload": desc, "bytes": n_bytes,
-                   "chars": len(text.decode("utf-8")) if doc_off is None else n_chars * n_docs, "docs": n_docs,
-                   "tokens": n_tokens, "merges": merges_name, "pattern": pattern, "seed": seed},
-        "latency_ms": {"p50": round(1e3 * statistics.median(per_step), 4),
-                       "p90": round(1e3 * float(np.percentile(per_step, 90)), 4),
-                       "p99": round(1e3 * float(np.percentile(per_step, 99)), 4)},
-        "stages_ms": stages,  # warm-up steps, every stage timed
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6),
-                     "traffic": measured_traffic(args.workload, dom),
-                     "algorithmic_bytes": alg, "avg_ms": dom_ms,
-                     "valu_issue": valu_issue(args.workload, dom, dom_ms)},
-        "complete_call": complete,
-        "graph_ab": graph_ab,
-        "span_export": span_export,
-        "fresh_inputs": fresh,
-        "cpu_baseline": cpu,
-    }
+    h = results[head]
+    if head == "repair":
+        out = {"metric": "tok_repair latency (ms, P50)", "value": h["latency_ms"]["p50"], "unit": "ms", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "higher_is_better": False, "vs_baseline": None,
+               "dtype": "u8->int32", "data": "synthetic (seeded generator; host text and IDs)",
+               "config": {"workload": h["workload"], "context_chars": 1_000_000, "append_chars": 1400}, **h}
+    else:
+        out = {
+            "metric": METRIC,
+            "value": h["mbps"],
+            "unit": "MB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": h["ms_per_step"],
+            "higher_is_better": True,
+            "scaling": "strong",
+            "vs_baseline": None,
+            "dtype": "u8->int32",
+            "data": "synthetic (seeded generator, inputs resident in HBM)",
+            "config": {"workload": h["workload"], "bytes": h["bytes"], "chars": h["chars"], "docs": h["docs"],
+                       "tokens": h["tokens_per_step"], "merges": h["merges"], "pattern": h["pattern"],
+                       "seed": h["seed"], "protocol": h["protocol"]},
+            "latency_ms": h["latency_ms"],
+            "stages_ms": h["stages_ms"],
+            "roofline": h["roofline"],
+            "steady_input": h.get("steady_input"),
+            "complete_call": h.get("complete_call"),
+            "graph_ab": h.get("graph_ab"),
+            "span_export": h.get("span_export"),
+            "cpu_baseline": h.get("cpu_baseline"),
+        }
+    if len(names) > 1:
+        out["configs"] = {w: results[w] for w in names[1:]}
     print(json.dumps(out), flush=True)
-    tok.close()
+    for t in toks.values():
+        t.close()
     return 0
 
 

@@ -24,10 +24,11 @@ TOK_MAX_BYTES = 0xFFFF0000  # longest input, in bytes
 
 # every function declared in include/tok.h
 EXPORTS = (
-    "tok_load", "tok_free", "tok_strerror", "tok_encode", "tok_encode_dev", "tok_encode_batch",
+    "tok_opts_default", "tok_load", "tok_free", "tok_strerror", "tok_encode", "tok_encode_dev", "tok_encode_batch",
     "tok_encode_batch_dev", "tok_encode_spans_dev", "tok_encode_spans", "tok_pretokenize_dev", "tok_repair",
     "tok_repair_dev", "tok_sync_boundary", "tok_get_info",
     "tok_token_lengths", "tok_set_added_tokens", "tok_set_graph", "tok_graph_count", "tok_set_profiling", "tok_stage_ms",
+    "tok_fill_scratch",
 )
 
 
@@ -42,6 +43,19 @@ class TokInfo(ctypes.Structure):
                 ("vocab_size", ctypes.c_uint32), ("max_token_len", ctypes.c_uint32),
                 ("n_whole", ctypes.c_uint32), ("n_not_self", ctypes.c_uint32),
                 ("config_hash", ctypes.c_uint64)]
+
+
+class TokOpts(ctypes.Structure):
+    """tok_opts: load options (device, initial scratch, repair window, doublings, margin)."""
+    _fields_ = [("device", ctypes.c_int32), ("repair_window", ctypes.c_uint32),
+                ("initial_bytes", ctypes.c_uint64), ("repair_doublings", ctypes.c_uint32),
+                ("repair_margin", ctypes.c_uint32)]
+
+
+def default_opts() -> TokOpts:
+    o = TokOpts()
+    lib().tok_opts_default(ctypes.byref(o))
+    return o
 
 
 class RepairInfo(ctypes.Structure):
@@ -61,7 +75,9 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
         szp = ctypes.POINTER(ctypes.c_size_t)
-        L.tok_load.argtypes = [vp, sz, i32, i32, ctypes.POINTER(vp)]
+        L.tok_opts_default.argtypes = [ctypes.POINTER(TokOpts)]
+        L.tok_opts_default.restype = None
+        L.tok_load.argtypes = [vp, sz, i32, ctypes.POINTER(TokOpts), ctypes.POINTER(vp)]
         L.tok_free.argtypes = [vp]
         L.tok_free.restype = None
         L.tok_strerror.argtypes = [i32]
@@ -85,10 +101,11 @@ def lib() -> ctypes.CDLL:
         L.tok_graph_count.restype = sz
         L.tok_set_profiling.argtypes = [vp, i32]
         L.tok_stage_ms.argtypes = [vp, vp, i32]
+        L.tok_fill_scratch.argtypes = [vp, i32]
         for name in ("tok_load", "tok_encode", "tok_encode_dev", "tok_encode_batch", "tok_encode_batch_dev",
                      "tok_encode_spans_dev", "tok_encode_spans", "tok_pretokenize_dev", "tok_repair",
                      "tok_repair_dev", "tok_sync_boundary", "tok_get_info", "tok_set_added_tokens",
-                     "tok_set_graph", "tok_set_profiling", "tok_stage_ms"):
+                     "tok_set_graph", "tok_set_profiling", "tok_stage_ms", "tok_fill_scratch"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -135,11 +152,19 @@ def _stream_handle(stream) -> int | None:
 class Tokenizer:
     """One loaded configuration (merge list + pre-tokenizer pattern) on one GPU."""
 
-    def __init__(self, merges, pattern: str | int, device: int = 0):
+    def __init__(self, merges, pattern: str | int, device: int = 0, **opts):
+        """opts: any tok_opts field other than device (initial_bytes, repair_window,
+        repair_doublings, repair_margin); the rest keep their defaults."""
         m = np.ascontiguousarray(np.asarray(merges, dtype=np.uint32).reshape(-1, 2))
         pat = PATTERNS[pattern] if isinstance(pattern, str) else int(pattern)
+        o = default_opts()
+        o.device = device
+        for k, v in opts.items():
+            if k == "device" or k not in dict(TokOpts._fields_):
+                raise TypeError(f"unknown tok_opts field {k!r}")
+            setattr(o, k, v)
         h = ctypes.c_void_p()
-        _check(lib().tok_load(m.ctypes.data if m.size else None, m.shape[0], pat, device, ctypes.byref(h)),
+        _check(lib().tok_load(m.ctypes.data if m.size else None, m.shape[0], pat, ctypes.byref(o), ctypes.byref(h)),
                "tok_load")
         self._h = h
         self.device = device
@@ -295,6 +320,10 @@ class Tokenizer:
         _check(lib().tok_set_added_tokens(self._h, blob if lits else None, off.ctypes.data if lits else None,
                                           len(lits), ids.ctypes.data if lits else None), "tok_set_added_tokens")
 
+    def fill_scratch(self, value: int) -> None:
+        """tok_fill_scratch: poison the context's per-call device buffers (a diagnostic)."""
+        _check(lib().tok_fill_scratch(self._h, int(value)), "tok_fill_scratch")
+
     def set_graph(self, on: bool = True) -> None:
         """Replay a captured HIP graph for call shapes met before (tok_set_graph)."""
         _check(lib().tok_set_graph(self._h, 1 if on else 0), "tok_set_graph")
@@ -313,7 +342,7 @@ class Tokenizer:
         return list(out[:k])
 
 
-STAGES = ("pretokenize", "pieces", "assemble")
+STAGES = ("pretokenize", "pieces", "assemble", "long_pieces")
 
 
 def flags_to_starts(flags: np.ndarray, n: int) -> np.ndarray:

@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtok.so")
 RULES_LIB = os.path.join(HERE, "librules_cpu.so")
-SOURCES = ["capi.hip", "repair.hip", "k_pretok.hip", "k_bpe.hip", "k_assemble.hip", "k_added.hip", "k_repair.hip"]
+SOURCES = ["capi.hip", "repair.hip", "k_pretok.hip", "k_bpe.hip", "k_long.hip", "k_assemble.hip", "k_added.hip",
+           "k_repair.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
@@ -27,7 +28,7 @@ def hipcc_cmd(out: str) -> list[str]:
     return [
         HIPCC, "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", "-Wno-unused-function",
+        "-Wall", "-Wno-unused-function", "-Wl,--no-undefined",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,

@@ -140,9 +140,26 @@ const char* tok_strerror(int code) {
   }
 }
 
-int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, tok_ctx** out) {
+void tok_opts_default(tok_opts* opts) {
+  if (!opts) return;
+  *opts = tok_opts{};
+  opts->device = 0;
+  opts->initial_bytes = 0;
+  opts->repair_window = 512;
+  opts->repair_doublings = 5;
+  opts->repair_margin = 8;
+}
+
+int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opts* opts, tok_ctx** out) {
   if (!out || (!merges && n_merges)) return TOK_E_ARG;
   *out = nullptr;
+  tok_opts o;
+  tok_opts_default(&o);
+  if (opts) o = *opts;
+  if (o.device < 0 || o.repair_window < 1 || o.repair_window > (1u << 24) || o.repair_doublings > 24 ||
+      o.repair_margin > (1u << 20) || o.initial_bytes > TOK_MAX_BYTES)
+    return TOK_E_ARG;
+  const int device = o.device;
   if (pattern != TOK_PAT_GPT2 && pattern != TOK_PAT_LLAMA3) return TOK_E_PATTERN;
   if (n_merges > TOK_MAX_MERGES) return TOK_E_BADMERGES;
   // operands precede their merge, and each ordered pair has one rank
@@ -184,6 +201,9 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
   if (!ctx) return TOK_E_NOMEM;
   ctx->device = device;
   ctx->pattern = pattern;
+  ctx->repair_window = o.repair_window;
+  ctx->repair_doublings = o.repair_doublings;
+  ctx->repair_margin = o.repair_margin;
   ctx->n_merges = (uint32_t)n_merges;
   ctx->tok_len.resize(tok.size());
   ctx->tok_off.resize(tok.size() + 1);
@@ -238,6 +258,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
     ctx->b.ctr = ctx->d_ctr;
     ctx->merge_buckets = bmask;
     rc = build_word_table(ctx, tok);
+    if (rc == TOK_OK && o.initial_bytes) rc = ctx->ensure(o.initial_bytes);
   } while (false);
   if (rc != TOK_OK) {
     (void)hipGetLastError();
@@ -246,6 +267,12 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, t
   }
   *out = ctx;
   return TOK_OK;
+}
+
+int tok_fill_scratch(tok_ctx* ctx, int value) {
+  if (!ctx || value < 0 || value > 255) return TOK_E_ARG;
+  DeviceGuard g(ctx->device);
+  return ctx->fill_scratch((uint8_t)value);
 }
 
 void tok_free(tok_ctx* ctx) {

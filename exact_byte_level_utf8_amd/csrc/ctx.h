@@ -53,7 +53,7 @@ inline void hfree(T*& p) {
   p = nullptr;
 }
 
-constexpr int kStages = 3;
+constexpr int kStages = 4;  // pre-tokenization, piece pass, assembly, long pieces
 
 // Key of a captured pipeline: every argument baked into its kernel launches.
 struct GraphKey {
@@ -89,6 +89,9 @@ struct tok_ctx {
   uint32_t max_tok_len = 1;
   uint32_t n_whole = 0, n_not_self = 0;
   uint64_t config_hash = 0;
+  uint32_t repair_window = 512;    // first repair window, code points
+  uint32_t repair_doublings = 5;   // window doublings before the full encode
+  uint32_t repair_margin = 8;      // code points into the window of a certifying boundary
   std::vector<uint32_t> tok_len;  // host copy
   std::vector<uint8_t> tok_bytes;  // host copy of every token's bytes, concatenated
   std::vector<uint64_t> tok_off;   // token i is tok_bytes[tok_off[i] .. tok_off[i + 1])
@@ -188,6 +191,11 @@ struct tok_ctx {
     dfree(b.ws_sym);
     dfree(b.ws_rk);
     dfree(b.ws_sel);
+    dfree(b.tile_run);
+    dfree(b.lq_ctr);
+    dfree(b.lq_start);
+    dfree(b.lq_len);
+    dfree(b.lq_cnt);
     free_lit_bufs();
     dfree(d_text);
     dfree(d_ids);
@@ -213,13 +221,49 @@ struct tok_ctx {
         hipMalloc((void**)&b.ws_rk, (c + 64) * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&b.ws_sel, (c + 64) * sizeof(uint64_t)) != hipSuccess ||
         hipMalloc((void**)&b.sum1, ((tiles >> kSum1Shift) + 1) * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.sum2, ((tiles >> kSum2Shift) + 1) * sizeof(uint32_t)) != hipSuccess) {
+        hipMalloc((void**)&b.sum2, ((tiles >> kSum2Shift) + 1) * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc((void**)&b.tile_run, tiles * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc((void**)&b.lq_ctr, 16 * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc((void**)&b.lq_start, (c / 64 + 64) * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc((void**)&b.lq_len, (c / 64 + 64) * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc((void**)&b.lq_cnt, (c / 64 + 64) * sizeof(uint32_t)) != hipSuccess) {
       (void)hipGetLastError();
       free_scratch();
       return TOK_E_NOMEM;
     }
     b.ctr = d_ctr;
     cap = c;
+    return TOK_OK;
+  }
+
+  // Fill every per-call device buffer with byte v and wait (a diagnostic:
+  // no call may depend on what an earlier one left in them).
+  int fill_scratch(uint8_t v) {
+    auto fill = [&](void* p, uint64_t bytes) { return !p || hipMemsetAsync(p, v, bytes, stream) == hipSuccess; };
+    bool ok = true;
+    if (b.flags) {
+      const uint64_t chunks = cap / kChunk, tiles = cap / kPieceTile;
+      ok = fill(b.flags, (chunks + 8) * 2) && fill(b.staging, (cap + 64) * 4) && fill(b.tile_cnt, tiles * 4) &&
+           fill(b.tile_first, tiles * 4) && fill(b.ws_sym, (cap + 64) * 4) && fill(b.ws_rk, (cap + 64) * 4) &&
+           fill(b.ws_sel, (cap + 64) * 8) && fill(b.sum1, ((tiles >> kSum1Shift) + 1) * 4) &&
+           fill(b.sum2, ((tiles >> kSum2Shift) + 1) * 4) && fill(d_text, cap + 64) && fill(d_ids, (cap + 64) * 4) &&
+           fill(d_spans, (cap + 64) * 4) && fill(b.tile_run, tiles * 4) && fill(b.lq_ctr, 64) &&
+           fill(b.lq_start, (cap / 64 + 64) * 4) && fill(b.lq_len, (cap / 64 + 64) * 4) &&
+           fill(b.lq_cnt, (cap / 64 + 64) * 4);
+    }
+    if (ok && lb.cand) {
+      const uint64_t parts = lit_docs + 2 * lit_cap;
+      ok = fill(lb.cand, lit_cap * 8) && fill(lb.tile_cnt, lit_cap / kLitTile * 4) && fill(lb.sel, lit_cap * 8) &&
+           fill(lb.cut, (parts + 2) * 8) && fill(lb.part_lit, (parts + 2) * 4) &&
+           fill(lb.doc_part, (lit_docs + 2) * 4) && fill(lb.out_off, (parts + 2) * 8) &&
+           fill(lb.fin, (parts + 2) * 4) && fill(lb.misc, 16) && fill(lb.ids, (lit_cap + 64) * 4) &&
+           fill(lb.spans, (lit_cap + 64) * 4);
+    }
+    if (ok && d_doc) ok = fill(d_doc, doc_cap * 8) && fill(d_outoff, doc_cap * 8);
+    if (!ok || hipStreamSynchronize(stream) != hipSuccess) {
+      (void)hipGetLastError();
+      return TOK_E_DEVICE;
+    }
     return TOK_OK;
   }
 
@@ -419,6 +463,7 @@ struct tok_ctx {
     launch_pretok(text, n, doc_off, n_docs, pattern, bb, s, e0(0), e1(0));
     if (out_flags) return;
     launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s, e0(1), e1(1));
+    launch_long(text, n, t, bb, s, e0(3), e1(3));
     launch_assemble(n, bb, out, spans, d_tok_len, out_cap, doc_off, n_docs, out_off, s, e0(2), e1(2));
   }
 
@@ -518,11 +563,13 @@ struct tok_ctx {
     Bufs bb = b;
     bb.gen = ++gen;
     const uint32_t tiles = (uint32_t)((n + kPieceTile - 1) / kPieceTile);
-    std::vector<uint32_t> zero((tiles >> kSum1Shift) + 1, 0);  // group sums start at zero
+    std::vector<uint32_t> zero(std::max<size_t>((tiles >> kSum1Shift) + 1, 2), 0);  // group sums start at zero
     HIP_OK(hipMemcpyAsync(bb.sum1, zero.data(), zero.size() * 4, hipMemcpyHostToDevice, stream));
     HIP_OK(hipMemcpyAsync(bb.sum2, zero.data(), ((tiles >> kSum2Shift) + 1) * 4, hipMemcpyHostToDevice, stream));
+    HIP_OK(hipMemcpyAsync(bb.lq_ctr, zero.data(), 2 * 4, hipMemcpyHostToDevice, stream));  // empty long-piece queue
     const Tables t = tables(false);
     launch_pieces(d_text, n, t, bb, nullptr, 0, nullptr, stream);
+    launch_long(d_text, n, t, bb, stream);
     launch_assemble(n, bb, d_ids, nullptr, nullptr, n, nullptr, 0, nullptr, stream);
     HIP_OK(hipGetLastError());
     HIP_OK(hipStreamSynchronize(stream));

@@ -62,6 +62,8 @@ struct RepairArgs {
                                  // index it goes to, [2] how many (0: nothing to copy)
   uint64_t max_fresh;            // bound on the window's record count (its byte count)
   RepairOut* out;                // host-mapped result
+  const uint64_t* err_utf8;      // host-mapped error words of the window encode: when either holds
+  const uint64_t* err_docs;      // gen, the window's IDs are not a result and the session is left alone
   uint64_t gen;
 };
 

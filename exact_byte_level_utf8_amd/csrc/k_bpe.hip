@@ -14,18 +14,20 @@
 //      into lists in LDS, one per table, and then run one per lane, so a wave
 //      waits for one memory round trip.  Every other piece goes to a work
 //      list in LDS by length.
-//   2. The workgroup's waves merge the listed pieces: pieces longer than
-//      64 bytes first, then 33..64-byte pieces (one wave per piece, one symbol
-//      per lane), then 17..32-byte pieces (two per wave, one 32-lane row
-//      each), then 2..16-byte pieces (four per wave, one 16-lane row each).
+//      A piece longer than 64 bytes is deferred to the long-piece kernel
+//      (k_long.hip): its first byte goes to a device work queue and one
+//      marker entry (-1 - its queue index) stands for its tokens in the run.
+//   2. The workgroup's waves merge the listed pieces: 33..64-byte pieces
+//      first (one wave per piece, one symbol per lane), then 17..32-byte
+//      pieces (two per wave, one 32-lane row each), then 2..16-byte pieces
+//      (four per wave, one 16-lane row each).
 //      A round takes the row minimum of (rank, position), chooses every
 //      leftmost non-overlapping occurrence of that pair value at once,
 //      compacts the row with a lane permute, and re-probes only the pairs next
 //      to a merge (TokTier: merging all leftmost non-overlapping occurrences of
 //      the minimum-rank pair equals iterated single merges, and only pairs
 //      adjacent to a completed merge are re-probed; GraphTok: a round takes
-//      every other pair of a chain).  Pieces longer than 64 bytes run the same
-//      rounds over arrays in global memory.
+//      every other pair of a chain).
 //   3. The tile's tokens are compacted in order (in LDS) and written as one
 //      run from the tile's first piece start, with the tile's count, which is
 //      also added to the sums of its groups of 64 and 4096 tiles; the
@@ -304,106 +306,6 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
   }
 }
 
-// Byte offset of the first piece start after s, or n.
-__device__ inline uint64_t next_start(const uint16_t* flags, uint64_t n, uint64_t s) {
-  const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint64_t c = s / kChunk;
-  const uint32_t own = flags[c] & ~((2u << (s % kChunk)) - 1u);
-  if (own) return c * kChunk + __builtin_ctz(own);
-  for (uint64_t cb = c + 1; cb < n_chunks; cb += 64) {
-    const uint64_t ci = cb + lane;
-    const uint32_t wv = ci < n_chunks ? flags[ci] : 0u;
-    const uint64_t mask = __ballot(wv != 0);
-    if (mask) {
-      const uint32_t l = __builtin_ctzll(mask);
-      const uint32_t wl = __builtin_amdgcn_readfirstlane(__shfl(wv, l, 64));
-      return (cb + l) * kChunk + __builtin_ctz(wl);
-    }
-  }
-  return n;
-}
-
-// One wave merges a piece longer than 64 bytes with the same rounds, its
-// symbols and pair ranks in global memory (workspace indexed by the piece's
-// bytes, so pieces never share it), compacting in place.  Its tokens stay in
-// ws_sym[s ..]; cnt_out gets 0 to mark the piece as long.
-__device__ void merge_long(const Tables& T, const uint8_t* __restrict__ text, uint64_t n, uint64_t s,
-                           const Bufs& B, uint8_t* cnt_out, uint32_t* chunk_total) {
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-  const uint64_t e = next_start(B.flags, n, s);
-  uint32_t* sym = B.ws_sym + s;
-  uint32_t* rk = B.ws_rk + s;
-  uint64_t* sel = B.ws_sel + s;
-  uint32_t cur = __builtin_amdgcn_readfirstlane((uint32_t)(e - s));
-  for (uint32_t k = lane; k < cur; k += 64) {
-    const uint32_t a = text[s + k];
-    sym[k] = a;
-    rk[k] = k + 1 < cur ? T.pair_rank[(a << 8) | text[s + k + 1]] : kNoRank;
-  }
-  for (;;) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    uint32_t m = kNoRank;
-    for (uint32_t k = lane; k + 1 < cur; k += 64) m = min(m, rk[k]);
-    m = wave_min(m);
-    if (m == kNoRank) break;
-    const uint32_t groups = (cur + 63) / 64;
-    uint32_t carry = 0, chosen = 0;
-    for (uint32_t g = 0; g < groups; ++g) {
-      const uint32_t k = g * 64 + lane;
-      const uint64_t S = select_leftmost(__ballot(k + 1 < cur && rk[k] == m), carry);
-      carry = (uint32_t)(S >> 63);
-      chosen += (uint32_t)__popcll(S);
-      if (lane == 0) sel[g] = S;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const uint32_t nid = 256u + m;
-    uint32_t removed = 0;
-    uint64_t prev_S = 0;
-    for (uint32_t g = 0; g < groups; ++g) {
-      const uint64_t S = sel[g];
-      const uint64_t S_next = g + 1 < groups ? sel[g + 1] : 0ull;
-      const uint64_t R = (S << 1) | (prev_S >> 63);  // bit j: position 64g + j is absorbed
-      const uint32_t k = g * 64 + lane;
-      const bool alive = k < cur && !((R >> lane) & 1ull);
-      uint32_t nsym = 0, nrk = kNoRank;
-      if (alive) {
-        const bool chose = (S >> lane) & 1ull;
-        nsym = chose ? nid : sym[k];
-        const uint32_t kn = chose ? k + 2 : k + 1;
-        if (kn < cur) {
-          const uint32_t jn = kn - g * 64;  // 1..65
-          const bool chose_n = jn < 64 ? ((S >> jn) & 1ull) : ((S_next >> (jn - 64)) & 1ull);
-          if (chose || chose_n) nrk = merge_rank(T, nsym, chose_n ? nid : sym[kn]);
-          else nrk = rk[k];
-        }
-      }
-      const uint32_t idx = k - removed - (uint32_t)__popcll(R & lt_mask);
-      __builtin_amdgcn_wave_barrier();
-      if (alive) {
-        sym[idx] = nsym;
-        rk[idx] = nrk;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      removed += (uint32_t)__popcll(__ballot(k < cur && ((R >> lane) & 1ull)));
-      prev_S = S;
-    }
-    cur -= chosen;
-  }
-  if (lane == 0) {
-    *cnt_out = 0;  // marks a long piece: its tokens are in ws_sym
-    atomicAdd(chunk_total, cur);
-  }
-}
-
-
 constexpr uint32_t kXcds = 8;    // XCDs of the device; workgroups are dealt to them in turn
 constexpr uint32_t kXcdCus = 32;  // compute units per XCD
 constexpr uint32_t kLine = 128;   // L2 line bytes
@@ -447,21 +349,23 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   constexpr int kCapA = kPieceTile / 13 + 1, kCapB = kPieceTile / 9 + 1, kCapC = kPieceTile / 5 + 1;
   constexpr int kCapD = kPieceTile / 2;
   constexpr int kCapH = kPieceTile / (kRowMax + 1) + 1, kCap1 = kPieceTile / (kHalfMax + 1) + 1;
-  constexpr int kCap2 = kPieceTile / (kWaveMax + 1) + 1;
   __shared__ __attribute__((aligned(16))) uint8_t s_text[kTextLds];
   __shared__ uint16_t s_flags[kFlagLds];
   __shared__ uint32_t s_tok[kTokLds];
   __shared__ uint8_t s_cnt8[kPieceTile];
   __shared__ uint32_t s_la[kCapA], s_lb[kCapB], s_lc[kCapC], s_ld[kCapD];
-  __shared__ uint32_t s_lh[kCapH], s_list1[kCap1], s_list2[kCap2];
+  __shared__ uint32_t s_lh[kCapH], s_list1[kCap1];
   // probe lists of 2..13-byte and 14..28-byte pieces
   __shared__ uint32_t s_probe_s[kPieceTile / 2], s_probe_l[kPieceTile / (kWordMax + 1) + 1];
   __shared__ uint32_t s_cnt[kChunksPerWg], s_excl[kChunksPerWg];
-  __shared__ uint32_t s_n[9], s_next, s_first, s_doc0;
+  __shared__ uint32_t s_n[9], s_next, s_first, s_doc0, s_marks;
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   if (tid < 9) s_n[tid] = 0;
-  if (tid == 0) s_next = 0;
+  if (tid == 0) {
+    s_next = 0;
+    s_marks = 0;
+  }
   const uint32_t tile = blockIdx.x;
   const uint64_t base = (uint64_t)tile * kPieceTile;
   const uint64_t c0 = (uint64_t)tile * kChunksPerWg;
@@ -497,11 +401,11 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
                         touch_lines<NT>(T.pair_rank, 256u * 256u * 4u, 1);
   __syncthreads();
 
-  // a piece that needs the merge loop goes to the list of its length class
+  // a piece of 2..64 bytes that needs the merge loop goes to the list of its
+  // length class
   auto list_piece = [&](uint32_t item) {
     const uint32_t len = item >> 16;
-    if (len > (uint32_t)kWaveMax) s_list2[atomicAdd(&s_n[5], 1u)] = item & 0xFFFFu;
-    else if (len > (uint32_t)kHalfMax) s_list1[atomicAdd(&s_n[4], 1u)] = item;
+    if (len > (uint32_t)kHalfMax) s_list1[atomicAdd(&s_n[4], 1u)] = item;
     else if (len > (uint32_t)kRowMax) s_lh[atomicAdd(&s_n[8], 1u)] = item;
     else if (len >= 13u) s_la[atomicAdd(&s_n[0], 1u)] = item;
     else if (len >= 9u) s_lb[atomicAdd(&s_n[1], 1u)] = item;
@@ -542,6 +446,14 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
         s_probe_s[atomicAdd(&s_n[6], 1u)] = item;
       } else if (T.long_slots && len <= (uint32_t)kLongMax) {
         s_probe_l[atomicAdd(&s_n[7], 1u)] = item;
+      } else if (len > (uint32_t)kWaveMax) {
+        // deferred to the long-piece kernel: a queue entry and one marker
+        const uint32_t j = atomicAdd(&B.lq_ctr[0], 1u);
+        B.lq_start[j] = (uint32_t)s0;
+        s_tok[off] = ~j;
+        s_cnt8[off] = 1;
+        s_marks = 1u;
+        ++hits;
       } else {
         list_piece(item);
       }
@@ -575,34 +487,30 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   }
   __syncthreads();
 
-  // phase 2: the waves take items in order, longest pieces first: pieces
-  // over 64 bytes, then 33..64 bytes (a wave each), then pairs of 17..32-byte
+  // phase 2: the waves take items in order, longest pieces first: 33..64
+  // bytes (a wave each), then pairs of 17..32-byte
   // pieces (a 32-lane row each), then groups of four 2..16-byte pieces by
   // length class (a 16-lane row each).  The item index comes from an LDS
   // counter through readfirstlane, so every branch on it is uniform across
   // the wave.
   {
-    const uint32_t n2 = __builtin_amdgcn_readfirstlane(s_n[5]);
     const uint32_t n1 = __builtin_amdgcn_readfirstlane(s_n[4]);
     const uint32_t nh = __builtin_amdgcn_readfirstlane(s_n[8]);
     const uint32_t ca = __builtin_amdgcn_readfirstlane(s_n[0]), cb = __builtin_amdgcn_readfirstlane(s_n[1]);
     const uint32_t cc = __builtin_amdgcn_readfirstlane(s_n[2]), cd = __builtin_amdgcn_readfirstlane(s_n[3]);
-    const uint32_t eh = n2 + n1 + (nh + 1) / 2;
+    const uint32_t eh = n1 + (nh + 1) / 2;
     const uint32_t ea = eh + (ca + 3) / 4, eb = ea + (cb + 3) / 4, ec = eb + (cc + 3) / 4;
     const uint32_t items = ec + (cd + 3) / 4;
     for (;;) {
       // every lane adds 1, so a grab moves the counter by 64
       const uint32_t item = __builtin_amdgcn_readfirstlane(atomicAdd(&s_next, 1u)) / (uint32_t)kWave;
       if (item >= items) break;
-      if (item < n2) {
-        const uint32_t off = s_list2[item];
-        merge_long(T, text, n, base + off, B, &s_cnt8[off], &s_cnt[off / kChunk]);
-      } else if (item < n2 + n1) {
-        const uint32_t it = s_list1[item - n2];
+      if (item < n1) {
+        const uint32_t it = s_list1[item];
         const uint32_t off = it & 0xFFFFu;
         merge_rows<64>(T, s_text + off, it >> 16, true, s_tok + off, &s_cnt8[off], &s_cnt[off / kChunk]);
       } else if (item < eh) {
-        const uint32_t i = (item - n2 - n1) * 2 + (lane >> 5);
+        const uint32_t i = (item - n1) * 2 + (lane >> 5);
         const bool act = i < nh;
         const uint32_t it = act ? s_lh[i] : 0u;
         const uint32_t off = it & 0xFFFFu;
@@ -641,7 +549,8 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
     }
     if (t2 == 0) {
       s_first = (uint32_t)first;
-      B.tile_cnt[tile] = total;
+      B.tile_cnt[tile] = total;  // the long-piece kernel adds the deferred pieces' tokens
+      B.tile_run[tile] = total | (s_marks << 31);
       B.tile_first[tile] = (uint32_t)first;
       atomicAdd(&B.sum1[tile >> kSum1Shift], total);
       atomicAdd(&B.sum2[tile >> kSum2Shift], total);
@@ -654,8 +563,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   // every thread writes the tokens of the pieces that start in its two bytes:
   // its position in the run is its chunk's offset plus the counts of the
   // earlier pieces of the chunk (a scan over the chunk's eight threads).  A
-  // piece longer than 64 bytes is its chunk's last piece; its count is what
-  // the chunk's total leaves, and its tokens are in the long-piece workspace.
+  // deferred piece writes its one marker.
   {
     int32_t* run = B.staging + __builtin_amdgcn_readfirstlane(s_first);
     // this thread's piece starts, read again from LDS rather than kept live
@@ -677,19 +585,13 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
       if (q >= (uint32_t)d) incl += up;
     }
     uint32_t at = s_excl[lc] + (incl - own);
-    const uint32_t chunk_end = s_excl[lc] + s_cnt[lc];
 #pragma unroll
     for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
       if (!((mine >> b) & 1u)) continue;
       const uint32_t off = lc * kChunk + kBytesPer * q + b;
       const uint32_t k = s_cnt8[off];
-      if (k == 0) {  // long piece
-        for (uint32_t j = 0; at + j < chunk_end; ++j) run[at + j] = (int32_t)B.ws_sym[base + off + j];
-        at = chunk_end;
-      } else {
-        for (uint32_t j = 0; j < k; ++j) run[at + j] = (int32_t)s_tok[off + j];
-        at += k;
-      }
+      for (uint32_t j = 0; j < k; ++j) run[at + j] = (int32_t)s_tok[off + j];
+      at += k;
     }
   }
 

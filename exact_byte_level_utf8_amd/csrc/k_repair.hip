@@ -127,9 +127,23 @@ __global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) 
     s_nst = 0xFFFFFFFFu;
     s_best = 0;
     s_F = *(volatile const uint32_t*)A.fresh_total;  // host-mapped: one read
-    A.splice[2] = 0;
+    A.splice[2] = 0;  // the copy kernel after this one moves nothing unless a splice sets it
+    // the window encode found malformed UTF-8 (or bad part offsets): its IDs
+    // are no result, so nothing is matched and the session stays as it was
+    const uint64_t e1 = __hip_atomic_load(A.err_utf8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const uint64_t e2 = __hip_atomic_load(A.err_docs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (e1 == A.gen || e2 == A.gen) s_bad = 2;
   }
   __syncthreads();
+  if (s_bad == 2) {  // uniform: read after the barrier
+    if (tid == 0) {
+      A.out->status = kRepairEncodeError;
+      __threadfence_system();
+      report(&A.out->gen, A.gen);
+    }
+    return;
+  }
+  __syncthreads();  // every lane has read s_bad before the stored-record pass may set it
   const uint32_t F = s_F;
   const uint64_t wn = A.new_len - A.ws0;  // bytes in the device window
   const uint64_t need = A.old_len - A.ws;  // stored bytes to cover

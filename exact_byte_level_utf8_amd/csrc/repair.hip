@@ -88,10 +88,6 @@ struct Rec {
   int32_t id;
 };
 
-constexpr uint64_t kFirstWindow = 512;  // code points
-constexpr uint32_t kMaxWidenings = 5;
-constexpr uint64_t kMarginCodePoints = 8;
-
 }  // namespace
 
 extern "C" {
@@ -180,8 +176,8 @@ int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap,
   };
 
   std::vector<int32_t> fresh;
-  uint64_t w = kFirstWindow;
-  for (uint32_t widen = 0; widen <= kMaxWidenings; ++widen, w *= 2) {
+  uint64_t w = ctx->repair_window;
+  for (uint32_t widen = 0; widen <= ctx->repair_doublings; ++widen, w *= 2) {
     inf.widenings = widen;
     const uint64_t ws = back_code_points(text, old_len, w);
     if (ws == 0) break;  // the window would be the whole text
@@ -192,7 +188,7 @@ int tok_repair(tok_ctx* ctx, int32_t* session_ids, size_t n_session, size_t cap,
     size_t nf = 0;
     rc = tok_encode(ctx, text + ws, wlen, fresh.data(), wlen, &nf);
     if (rc) return rc;
-    const uint64_t margin = fwd_code_points(text, ws, new_len, kMarginCodePoints);
+    const uint64_t margin = fwd_code_points(text, ws, new_len, ctx->repair_margin);
 
     // match stored records (offset >= ws) against the window's records
     size_t si = stored.size();  // stored[si - 1] is the first stored record at or after ws
@@ -288,13 +284,13 @@ int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_
     // (the straddling stored token, the literal cut guard), word-aligned
     const uint32_t longest = std::max(ctx->max_tok_len, ctx->n_lit ? ctx->lit_max_len : 0u);
     const uint64_t pad = (longest + 3u) & ~3ull;
-    uint64_t w = kFirstWindow;
-    for (uint32_t widen = 0; widen <= kMaxWidenings; ++widen, w *= 2) {
+    uint64_t w = ctx->repair_window;
+    for (uint32_t widen = 0; widen <= ctx->repair_doublings; ++widen, w *= 2) {
       inf.widenings = widen;
       const uint64_t ws = back_code_points(text, old_len, w);
       if (ws == 0) break;  // the window would be the whole text
       const uint64_t ws0 = ws > pad ? ws - pad : 0;
-      const uint64_t margin = fwd_code_points(text, ws, new_len, kMarginCodePoints);
+      const uint64_t margin = fwd_code_points(text, ws, new_len, ctx->repair_margin);
       const uint64_t wlen = new_len - ws;
       rc = ctx->ensure(new_len - ws0);
       if (!rc) rc = ctx->ensure_host();
@@ -341,13 +337,17 @@ int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_
       a.st_off = ctx->b.ws_rk + 6;
       a.max_fresh = new_len - ws;
       a.out = &ctx->d_ctr->rp;
+      a.err_utf8 = &ctx->d_ctr->err_utf8;
+      a.err_docs = &ctx->d_ctr->err_docs;
       a.gen = call;
       launch_repair_match(a, s);
       HIP_OK(hipGetLastError());
       HIP_OK(hipStreamSynchronize(s));
-      if (c->err_utf8 == call) return TOK_E_UTF8;
-      if (c->done != call || c->rp.gen != call || (ctx->n_lit && c->ins_done != call)) return TOK_E_DEVICE;
+      if (c->rp.gen != call) return TOK_E_DEVICE;
       const uint32_t st = c->rp.status;
+      if (c->err_utf8 == call) return TOK_E_UTF8;  // the match kernel wrote nothing (kRepairEncodeError)
+      if (c->err_docs == call || st == kRepairEncodeError) return TOK_E_DEVICE;
+      if (c->done != call || (ctx->n_lit && c->ins_done != call)) return TOK_E_DEVICE;
       if (st == kRepairSession) return TOK_E_SESSION;
       if (st == kRepairNone) continue;
       *n_out = c->rp.total;

@@ -38,6 +38,18 @@ uint32_t fold_extra(uint32_t cp) {
 
 extern "C" int rules_cpu_class(uint32_t cp) { return (int)table_class(cp); }
 
+// Classes of the code points lo .. lo + n - 1, one byte each.
+extern "C" void rules_cpu_class_range(uint32_t lo, uint32_t n, uint8_t* out) {
+  for (uint32_t i = 0; i < n; ++i) out[i] = (uint8_t)table_class(lo + i);
+}
+
+// The contraction-letter code of a non-ASCII code point (0: none), from the
+// fold table the kernels use.
+extern "C" int rules_cpu_fold_extra(uint32_t cp) { return (int)fold_extra(cp); }
+
+// The contraction-letter code of an ASCII lowercase letter (0: not one).
+extern "C" int rules_cpu_letter_code(uint32_t cp) { return (int)ascii_letter_code(cp); }
+
 // Piece-start byte offsets of valid UTF-8 text (documents split at doc_off,
 // n_docs + 1 offsets, or one document when doc_off is null).  Returns 0, or 1
 // on malformed input (this harness only decodes; it does not fully validate).

@@ -72,12 +72,45 @@ typedef struct tok_ctx tok_ctx;
 #define TOK_MAX_MERGES 1040000ull
 
 /*
+ * tok_opts -- per-context options of tok_load (the survey's load options;
+ * the repair parameters are per-tokenizer values in the pages: TokTier,
+ * section 3 "Incremental repair", a first window of w = 512 characters
+ * doubled at most five times before the full re-encode; Delta Tokenizer,
+ * Table S1, the certificate's margin and bound).  A NULL opts means the
+ * defaults below; tok_opts_default fills a struct with them.
+ *
+ * device:           HIP device ordinal the context runs on (default 0).
+ * initial_bytes:    input bytes the per-call device scratch covers from the
+ *                   start (0, the default: allocated by the first call and
+ *                   grown in powers of two, as every call does when its input
+ *                   is larger).
+ * repair_window:    code points of the stored text in the first repair
+ *                   window (default 512; 1 .. 2^24).
+ * repair_doublings: window doublings before the whole text is encoded
+ *                   (default 5; at most 24).
+ * repair_margin:    code points into the window that a certifying boundary
+ *                   must lie (default 8; at most 2^20).  Any value is exact
+ *                   (the certificate holds for every left context); a margin
+ *                   keeps the splice away from the window's cut.
+ */
+typedef struct tok_opts {
+  int32_t device;
+  uint32_t repair_window;
+  uint64_t initial_bytes;
+  uint32_t repair_doublings;
+  uint32_t repair_margin;
+} tok_opts;
+
+void tok_opts_default(tok_opts* opts);
+
+/*
  * tok_load -- validate a configuration and build its device tables.
  *
  * merges:   host array of 2 * n_merges uint32: (left, right) of merge r at
  *           [2r, 2r+1].  Copied; the caller may free it on return.
- * pattern:  TOK_PAT_GPT2 or TOK_PAT_LLAMA3.
- * device:   HIP device ordinal the context runs on.
+ * pattern:  TOK_PAT_GPT2, TOK_PAT_LLAMA3 or TOK_PAT_O200K.
+ * opts:     load options (above), or NULL for the defaults.  Read during the
+ *           call only.
  * out:      receives the context (NULL on error).
  *
  * Builds, on the device: the (left, right) -> rank open-addressing table, a
@@ -87,11 +120,11 @@ typedef struct tok_ctx tok_ctx;
  * provably cannot change an ID: each string is checked by running the GPU
  * merge kernels on it once at load).
  *
- * Errors: TOK_E_ARG (null out or merges with n_merges > 0), TOK_E_BADMERGES
- * (left or right >= 256 + r, a repeated pair, n_merges > TOK_MAX_MERGES),
- * TOK_E_PATTERN, TOK_E_DEVICE, TOK_E_NOMEM.
+ * Errors: TOK_E_ARG (null out, merges NULL with n_merges > 0, an option out
+ * of its range), TOK_E_BADMERGES (left or right >= 256 + r, a repeated pair,
+ * n_merges > TOK_MAX_MERGES), TOK_E_PATTERN, TOK_E_DEVICE, TOK_E_NOMEM.
  */
-int tok_load(const uint32_t* merges, size_t n_merges, int pattern, int device, tok_ctx** out);
+int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opts* opts, tok_ctx** out);
 
 /* Release the context and all its device and pinned memory.  NULL is a no-op. */
 void tok_free(tok_ctx* ctx);
@@ -320,6 +353,18 @@ int tok_sync_boundary(int pattern, uint32_t prev_cp, uint32_t cp);
  */
 int tok_set_added_tokens(tok_ctx* ctx, const uint8_t* bytes, const uint64_t* off, size_t n, const int32_t* ids);
 
+/*
+ * tok_fill_scratch -- diagnostic: fill every per-call device buffer the
+ * context holds (pipeline scratch, literal-pass buffers, staging of the
+ * host-memory calls) with the byte value (0..255) and wait for it.  No call's
+ * result depends on what an earlier call left in those buffers; tests poison
+ * them between calls of different sizes to show it (GraphTok, section 6.2,
+ * stale state across replays).  Device tables and the caller's buffers are
+ * not touched.  Errors: TOK_E_ARG (null context, value out of range),
+ * TOK_E_DEVICE.
+ */
+int tok_fill_scratch(tok_ctx* ctx, int value);
+
 /* Context facts. */
 typedef struct tok_info {
   uint32_t pattern;
@@ -347,8 +392,10 @@ size_t tok_token_lengths(const tok_ctx* ctx, uint32_t* len_out, size_t n);
  * system-scope fence).  tok_stage_ms writes the last call's stage durations in ms, 0 for
  * stages not timed: [0] pre-tokenization (with the per-call set-up of the
  * later passes), [1] piece pass (single bytes, whole-piece hits, merge
- * rounds of the remaining pieces, one run of IDs per 1 KiB tile), [2]
- * assembly (output offsets of the runs and their copy).  Returns the number
+ * rounds of pieces of up to 64 bytes, one run of IDs per 1 KiB tile), [2]
+ * assembly (output offsets of the runs and their copy, with the long pieces'
+ * tokens put in place), [3] long pieces (merge rounds of every piece longer
+ * than 64 bytes, one workgroup per piece; it runs between [1] and [2]).  Returns the number
  * of stages written (at most n).  tok_set_profiling: TOK_E_ARG for a null
  * context or a negative mask.
  */
@@ -373,7 +420,8 @@ size_t tok_graph_count(const tok_ctx* ctx);
 #define TOK_STAGE_PRETOK 1
 #define TOK_STAGE_PIECES 2
 #define TOK_STAGE_ASSEMBLE 4
-#define TOK_STAGES_ALL 7
+#define TOK_STAGE_LONG 8
+#define TOK_STAGES_ALL 15
 int tok_set_profiling(tok_ctx* ctx, int stages);
 int tok_stage_ms(const tok_ctx* ctx, float* ms, int n);
 

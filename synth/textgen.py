@@ -395,6 +395,30 @@ def chat_text(seed: int, n_chars: int, markers: list[str]) -> str:
     return "".join(parts)
 
 
+def cjk_text(seed: int, n_chars: int) -> str:
+    """CJK-dense text of exactly ``n_chars`` characters (the CJK corpora that
+    TokTier's Table 9 reports apart): runs of 50-2,000 ideographs from
+    U+4E00-U+9FFF (log-uniform lengths, each character uniform as in the mix's
+    CJK runs), each followed by ASCII punctuation, a newline, or a short
+    phrase of lexicon words.  A run is one letter piece of up to 6,000 bytes
+    under both patterns, so this text exercises the long-piece merge path."""
+    g = _MixGen(seed)
+    seps = [", ", ". ", ":", "! ", "? ", "\n", "\n\n", "; ", " (", ") "]
+    parts: list[str] = []
+    total = 0
+    while total < n_chars:
+        n = int(round(math.exp(math.log(50.0) + g.s.u() * (math.log(2000.0) - math.log(50.0)))))
+        run = "".join(chr(g.s.randint(0x4E00, 0x9FFF)) for _ in range(n))
+        u = g.s.u()
+        if u < 0.7:
+            tail = g.s.pick(seps)
+        else:
+            tail = " " + " ".join(g.word() for _ in range(g.s.randint(1, 6))) + g.s.pick(seps)
+        parts.append(run + tail)
+        total += len(run) + len(tail)
+    return "".join(parts)[:n_chars]
+
+
 # ----------------------------------------------------------------- workloads
 
 def batch_texts(base_seed: int, n_docs: int, n_chars: int) -> list[str]:

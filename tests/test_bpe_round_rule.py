@@ -16,6 +16,13 @@ Equal-rank runs keep the leftmost non-overlapping pairs.  The claim is
 pinned here against oracle.Oracle.bpe on random merge tables over small
 alphabets (many interacting merges, long chains) and on the pieces of the
 synthetic workloads under the trained vocabularies.
+
+The long-piece kernel uses the same rule with walks of up to 64 pairs (the
+argument does not depend on the walk's length); that rule is pinned the same
+way, on longer random pieces and on the CJK-dense workload's pieces, where it
+cuts the rounds from hundreds to under twenty.  Rules with a planted mistake
+(a walk that does not stop at a pair ranked at or below r, or a walk that
+takes any token as a barrier) must fail these checks.
 """
 import random
 
@@ -32,7 +39,9 @@ WALK = 2  # pairs walked past the pair itself on each side
 class RuleBPE:
     """BPE of single pieces by rounds of the piece pass's rule."""
 
-    def __init__(self, merges):
+    def __init__(self, merges, walk: int = WALK, mistake: str | None = None):
+        self.walk = walk
+        self.mistake = mistake
         self.rank = {(int(a), int(b)): r for r, (a, b) in enumerate(merges)}
         n_tok = 256 + len(merges)
         self.min_l = [INF] * n_tok  # lowest rank of a merge with the token as right operand
@@ -60,28 +69,30 @@ class RuleBPE:
                 if r == low:
                     safe.append(True)
                     continue
-                ok_l = min_l[sym[i]] > r
-                for d in range(1, WALK + 1):
+                stops = self.mistake != "no_stop"
+                barrier = (lambda t, m: True) if self.mistake == "any_barrier" else (lambda t, m: m[t] > r)
+                ok_l = barrier(sym[i], min_l)
+                for d in range(1, self.walk + 1):
                     if ok_l:
                         break
                     j = i - d
                     if j < 0:
                         ok_l = True
                         break
-                    if pr[j] <= r:
+                    if stops and pr[j] <= r:
                         break
-                    ok_l = min_l[sym[j]] > r
-                ok_r = min_r[sym[i + 1]] > r
-                for d in range(1, WALK + 1):
+                    ok_l = barrier(sym[j], min_l)
+                ok_r = barrier(sym[i + 1], min_r)
+                for d in range(1, self.walk + 1):
                     if ok_r:
                         break
                     j = i + d
                     if j >= len(pr):
                         ok_r = True
                         break
-                    if pr[j] <= r:
+                    if stops and pr[j] <= r:
                         break
-                    ok_r = min_r[sym[j + 1]] > r
+                    ok_r = barrier(sym[j + 1], min_r)
                 safe.append(ok_l and ok_r)
             # adjacent sheltered pairs always have equal rank; keep the
             # leftmost non-overlapping ones
@@ -174,3 +185,60 @@ def test_rule_matches_textbook_bpe_on_workload_pieces():
             _, r_text = rule(p, shelter=False)
             fewer += r_rule < r_text
         assert fewer > 100  # the rule shortens many of the longest pieces' chains
+
+
+LONG_WALK = 64  # the long-piece kernel's walk bound
+
+
+def test_long_walk_rule_matches_textbook_bpe_on_random_tables():
+    rng = random.Random(2027)
+    for t in range(80):
+        alphabet = bytes(rng.sample(b"abcdefgh", rng.randint(2, 7)))
+        merges = random_merges(rng, alphabet, rng.randint(5, 300))
+        toks = token_bytes(merges, 256)[256:]
+        orc = oracle.Oracle(merges, "gpt2")
+        rule = RuleBPE(merges, walk=LONG_WALK)
+        for i in range(30):
+            if i % 2:
+                piece = bytes(rng.choice(alphabet) for _ in range(rng.randint(65, 400)))
+            else:
+                piece = b"".join(rng.choice(toks) for _ in range(rng.randint(8, 40)))[:400]
+            assert rule(piece)[0] == orc.bpe(piece), (t, piece, merges.tolist())
+
+
+def test_long_walk_rule_on_cjk_pieces():
+    """The CJK-dense workload's long pieces: the 64-pair walk gives textbook
+    BPE's tokens in far fewer rounds than the two-pair walk."""
+    m = vocab.merges("gpt2_50k")
+    orc = oracle.Oracle(m, "gpt2")
+    short, long_ = RuleBPE(m), RuleBPE(m, walk=LONG_WALK)
+    text = textgen.cjk_text(5, 40_000).encode()
+    pieces = sorted((p for p in orc.piece_strings(text) if 64 < len(p) <= 1600), key=len)
+    assert len(pieces) >= 20
+    most_long = most_short = 0
+    for p in pieces[:: max(1, len(pieces) // 20)]:
+        want = orc.bpe(p)
+        got, r_long = long_(p)
+        assert got == want, len(p)
+        got2, r_short = short(p)
+        assert got2 == want
+        most_long, most_short = max(most_long, r_long), max(most_short, r_short)
+    assert most_long <= 20 < most_short
+
+
+def test_planted_rule_mistakes_fail():
+    """Each planted mistake in the walk gives a wrong result on some random
+    table, so the checks above would catch it."""
+    for mistake in ("no_stop", "any_barrier"):
+        rng = random.Random(2028)
+        wrong = 0
+        for t in range(80):
+            alphabet = bytes(rng.sample(b"abcdefgh", rng.randint(2, 5)))
+            merges = random_merges(rng, alphabet, rng.randint(20, 200))
+            toks = token_bytes(merges, 256)[256:]
+            orc = oracle.Oracle(merges, "gpt2")
+            rule = RuleBPE(merges, walk=LONG_WALK, mistake=mistake)
+            for _ in range(20):
+                piece = b"".join(rng.choice(toks) for _ in range(rng.randint(4, 20)))[:200]
+                wrong += rule(piece)[0] != orc.bpe(piece)
+        assert wrong > 0, mistake

@@ -40,7 +40,7 @@ def test_library_exports_every_symbol():
 def _load(merges, pattern=0):
     m = np.ascontiguousarray(np.asarray(merges, dtype=np.uint32).reshape(-1, 2))
     h = ctypes.c_void_p()
-    rc = tk.lib().tok_load(m.ctypes.data if m.size else None, m.shape[0], pattern, 0, ctypes.byref(h))
+    rc = tk.lib().tok_load(m.ctypes.data if m.size else None, m.shape[0], pattern, None, ctypes.byref(h))
     return rc, h
 
 
@@ -53,8 +53,26 @@ def test_load_rejects_bad_merges_and_pattern():
     assert _load([[97, 98], [97, 98]])[0] == tk.TOK_E_BADMERGES
     assert _load([[97, 98]], pattern=7)[0] == tk.TOK_E_PATTERN
     h = ctypes.c_void_p()
-    assert tk.lib().tok_load(None, 3, 0, 0, ctypes.byref(h)) == tk.TOK_E_ARG
-    assert tk.lib().tok_load(None, 0, 0, 0, None) == tk.TOK_E_ARG
+    assert tk.lib().tok_load(None, 3, 0, None, ctypes.byref(h)) == tk.TOK_E_ARG
+    assert tk.lib().tok_load(None, 0, 0, None, None) == tk.TOK_E_ARG
+
+
+def test_load_options():
+    """tok_opts_default gives the documented defaults; an option outside its
+    range is refused before any device work."""
+    libs.ensure_built()
+    o = tk.default_opts()
+    assert (o.device, o.initial_bytes, o.repair_window, o.repair_doublings, o.repair_margin) == (0, 0, 512, 5, 8)
+    m = np.asarray([[97, 98]], dtype=np.uint32)
+    for field, bad in (("repair_window", 0), ("repair_window", (1 << 24) + 1), ("repair_doublings", 25),
+                       ("repair_margin", (1 << 20) + 1), ("device", -1), ("initial_bytes", tk.TOK_MAX_BYTES + 1)):
+        x = tk.default_opts()
+        setattr(x, field, bad)
+        h = ctypes.c_void_p()
+        assert tk.lib().tok_load(m.ctypes.data, 1, 0, ctypes.byref(x), ctypes.byref(h)) == tk.TOK_E_ARG, field
+        assert not h.value
+    with pytest.raises(TypeError):
+        tk.Tokenizer(m, "gpt2", bogus=1)
 
 
 def test_null_arguments():

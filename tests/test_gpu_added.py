@@ -23,7 +23,7 @@ import pytest
 import exact_byte_level_utf8_amd as tk
 import oracle
 from synth import textgen
-from tests import libs, vocab
+from tests import libs, oracle_par, vocab
 
 pytestmark = pytest.mark.gpu
 
@@ -276,8 +276,9 @@ def test_batch_with_literals(cfg, name):
 
 
 def test_batch_workload_with_literals(cfg):
-    """64 chat transcripts of 200,000 characters in one batch call: sampled
-    documents equal the oracle; every document's IDs cover its bytes."""
+    """64 chat transcripts of 200,000 characters in one batch call: every
+    document's IDs and output offsets equal the oracle's encode with the
+    literals; every document's IDs cover its bytes."""
     t, o, v = cfg["llama3"]
     lits = lits_from(MARKERS, v)
     tokb = vocab.token_bytes(vocab.merges(libs.CONFIGS["llama3"][0]))
@@ -292,9 +293,12 @@ def test_batch_workload_with_literals(cfg):
     lens = np.asarray([lit_len[i] if i >= v else len(tokb[i]) for i in ids.tolist()], dtype=np.int64)
     doc_bytes = np.add.reduceat(lens, out_off[:-1].astype(np.int64))
     assert np.array_equal(doc_bytes, np.diff(off.astype(np.int64)))
-    for i in (0, 33, 63):
+    want = oracle_par.map_docs(lambda d: o.encode_added(d.encode(), lits), docs)
+    want_ids, want_off = oracle_par.concat(want)
+    same("output offsets", out_off, want_off)
+    for i in range(64):
         a, z = int(out_off[i]), int(out_off[i + 1])
-        same(f"doc {i}", ids[a:z], o.encode_added(docs[i].encode(), lits))
+        same(f"doc {i}", ids[a:z], want[i])
 
 
 @pytest.mark.parametrize("name", ["gpt2", "llama3"])

@@ -21,7 +21,7 @@ import pytest
 import exact_byte_level_utf8_amd as tk
 import oracle
 from synth import textgen
-from tests import libs, vocab
+from tests import libs, oracle_par, vocab
 
 pytestmark = pytest.mark.gpu
 
@@ -183,7 +183,7 @@ def test_long_pieces(cfg, name):
     t, o, tokb = cfg[name]
     rng = random.Random(7)
     cases = []
-    for L in [33, 63, 64, 65, 100, 128, 129, 511, 512, 513, 4097, 10_000]:
+    for L in [33, 63, 64, 65, 100, 128, 129, 511, 512, 513, 4095, 4096, 4097, 10_000]:
         cases += ["a" * L, " " * L + "x", "=" * L, "é" * L, "\n" * L + "x", "中" * L,
                   "".join(rng.choice("abcdefghij") for _ in range(L)),
                   "".join(rng.choice("aab") for _ in range(L)), "7" * L, "x" + "1" * L]
@@ -194,6 +194,26 @@ def test_long_pieces(cfg, name):
     for s in cases[::7]:
         bb = s.encode()
         _check(name, t.encode(bb), o.encode(bb), bb, tokb)
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_long_pieces_in_batches(cfg, name):
+    """Pieces over 64 bytes (merged by the long-piece kernel and expanded from
+    one marker by the assembly) at document starts and ends, several in one
+    tile, across tiles, on both sides of the 4,096-symbol LDS capacity: IDs and
+    output offsets equal the oracle's per document."""
+    t, o, tokb = cfg[name]
+    rng = random.Random(99)
+    cjk = lambda k: "".join(chr(rng.randint(0x4E00, 0x9FFF)) for _ in range(k))  # noqa: E731
+    docs = ["a" * 65, " " * 200 + "x", cjk(40) + ". " + cjk(30), "x", "", "=" * 70 + " " + "-" * 66 + "\n",
+            cjk(1365), cjk(1366) + "!", "ab" * 2100, "q " + "7" * 300, " " * 64 + "y", "é" * 33 + "z" * 64]
+    docs += [cjk(rng.randint(20, 90)) + rng.choice([", ", ".\n", " ok "]) for _ in range(40)]
+    data, off = textgen.pack_docs(docs)
+    ids, out_off = t.encode_batch(data, off)
+    want = [o.encode(d.encode()) for d in docs]
+    want_ids, want_off = oracle_par.concat(want)
+    assert np.array_equal(out_off, want_off), "output offsets differ"
+    _check(name, ids, want_ids, data, tokb)
 
 
 def test_empty_and_tiny_inputs(cfg):
@@ -295,21 +315,21 @@ def test_batch_rejects_bad_offsets(cfg):
         t.encode_batch(data, np.asarray([1, 11], dtype=np.uint64))
 
 
-def test_batch_workload_sampled(cfg):
+def test_batch_workload(cfg):
     """64 documents of 500,000 characters in one call (the batch workload):
-    every document's tokens spell its bytes, and sampled documents equal the
-    oracle exactly."""
+    every document's IDs and output offsets equal the oracle's encode of that
+    document, element by element."""
     t, o, tokb = cfg["llama3"]
     texts = textgen.batch_texts(40_000, 64, 500_000)
     data, off = textgen.pack_docs(texts)
     ids, out_off = t.encode_batch(data, off)
-    assert out_off[0] == 0 and np.all(np.diff(out_off.astype(np.int64)) > 0)
-    lens = np.asarray([len(x) for x in tokb], dtype=np.int64)
-    doc_bytes = np.add.reduceat(lens[ids], out_off[:-1].astype(np.int64))
-    assert np.array_equal(doc_bytes, np.diff(off.astype(np.int64)))
-    for i in (0, 17, 63):
-        s, e = int(off[i]), int(off[i + 1])
-        _check(f"doc {i}", ids[int(out_off[i]):int(out_off[i + 1])], o.encode(data[s:e]), data[s:e], tokb)
+    docs = [data[int(off[i]):int(off[i + 1])] for i in range(64)]
+    want_ids, want_off = oracle_par.concat(oracle_par.map_docs(o.encode, docs))
+    assert np.array_equal(out_off, want_off), "output offsets differ"
+    for i in range(64):
+        a, z = int(out_off[i]), int(out_off[i + 1])
+        _check(f"doc {i}", ids[a:z], want_ids[a:z], docs[i], tokb)
+    assert np.array_equal(ids, want_ids)
 
 
 def test_repair_seams(cfg):
@@ -326,15 +346,31 @@ def test_repair_seams(cfg):
         _check(s, t.encode(b), o.encode(b), b, tokb)
 
 
-def test_stale_state_across_sizes(cfg):
+@pytest.mark.parametrize("poison", [None, 0xFF, 0x00, 0x5A])
+def test_stale_state_across_sizes(cfg, poison):
+    """Calls of different sizes on one context, with every per-call device
+    buffer filled with a poison byte before each call (GraphTok, section 6.2:
+    stale state across replays): the results never depend on what an earlier
+    call or the poison left in the scratch."""
     t, o, tokb = cfg["llama3"]
     small = "x12345 it's\n\n  fine".encode()
     big = textgen.mix_text(12, 3_000_000).encode()
     want_small, want_big = o.encode(small), o.encode(big)
+    docs = [big[:5000], b"", small, big[5000:90_000]]
+    data, off = b"".join(docs), np.cumsum([0] + [len(d) for d in docs]).astype(np.uint64)
+    want_batch = np.concatenate([o.encode(d) for d in docs])
     for b, w in ((small, want_small), (big, want_big), (small, want_small), (big[:777], o.encode(big[:777])),
                  (big, want_big)):
+        if poison is not None:
+            t.fill_scratch(poison)
         _check("stale", t.encode(b), w, b, tokb)
+        if poison is not None:
+            t.fill_scratch(poison)
         _check("stale-dev", gpu_encode_dev(t, b), w, b, tokb)
+        if poison is not None:
+            t.fill_scratch(poison)
+        got, got_off = t.encode_batch(data, off)
+        _check("stale-batch", got, want_batch, data, tokb)
 
 
 def test_deterministic(cfg):

@@ -140,3 +140,37 @@ def test_capacity_is_reported_and_ids_untouched(cfg):
     assert rc == tk.TOK_E_CAPACITY
     assert need == len(o.encode(old + app))
     assert np.array_equal(buf[: len(sess)], sess)
+
+
+@pytest.mark.parametrize("opts", [
+    dict(repair_window=16, repair_doublings=0, repair_margin=0),
+    dict(repair_window=64, repair_doublings=2, repair_margin=0),
+    dict(repair_window=2048, repair_doublings=5, repair_margin=64),
+    dict(repair_window=1, repair_doublings=24, repair_margin=1000, initial_bytes=1 << 22),
+])
+def test_repair_options(cfg, opts):
+    """Load options (tok_opts) change only how much work a repair does, never
+    its result: every window, doubling count and margin gives the full
+    encode, on the host and the device session; the first window and the
+    doublings bound where the window starts."""
+    merges_name, pattern = libs.CONFIGS["gpt2"]
+    t = tk.Tokenizer(vocab.merges(merges_name), pattern, **opts)
+    o = cfg["gpt2"][1]
+    base = textgen.mix_text(531, 60_000)
+    try:
+        for seed in range(10):
+            old, suf = textgen.repair_case(531, 9_500 + seed, old_text=base)
+            ob, text = old.encode(), (old + suf).encode()
+            sess = o.encode(ob)
+            want = o.encode(text)
+            got, info = t.repair(sess, text, len(ob))
+            assert np.array_equal(got, want), (seed, info)
+            assert info["widenings"] <= opts["repair_doublings"]
+            if not info["full"]:
+                w = opts["repair_window"] << info["widenings"]
+                assert len(old) - len(text[: info["window_start"]].decode()) <= w
+            buf = torch.from_numpy(np.concatenate([sess, np.zeros(len(want) + 8, np.int32)])).cuda()
+            n, dinfo = t.repair_dev(buf, len(sess), text, len(ob))
+            assert dinfo == info and np.array_equal(buf[:n].cpu().numpy(), want)
+    finally:
+        t.close()

@@ -132,6 +132,33 @@ def test_session_errors_leave_the_session_alone(cfg):
     assert cap == buf.numel()
 
 
+@pytest.mark.parametrize("with_literals", [False, True])
+def test_malformed_append_leaves_the_session_alone(cfg, with_literals):
+    """Malformed UTF-8 in the appended bytes, after a stored text cut mid-word:
+    the window encode reports it, the match kernel writes nothing, and the
+    call returns TOK_E_UTF8 with the device session bit-identical (the window
+    IDs after a mid-word cut would otherwise overwrite the stored tail)."""
+    t, o = cfg["gpt2"]
+    v = t.info()["vocab_size"]
+    lits = [(b"<|endoftext|>", v)]
+    if with_literals:
+        t.set_added_tokens(lits)
+    try:
+        old = (textgen.mix_text(511, 20_000) + " the wor").encode()
+        sess = np.asarray(o.encode_added(old, lits) if with_literals else o.encode(old), dtype=np.int32)
+        for app in (b"ld\xff", b"ld and more \xc3", b"ld \xed\xa0\x80 x"):
+            buf = torch.from_numpy(np.concatenate([sess, np.full(64, -7, dtype=np.int32)])).cuda()
+            with pytest.raises(tk.TokError) as e:
+                t.repair_dev(buf, len(sess), old + app, len(old))
+            assert e.value.code == tk.TOK_E_UTF8, app
+            torch.cuda.synchronize()
+            got = buf.cpu().numpy()
+            assert np.array_equal(got[:len(sess)], sess) and np.all(got[len(sess):] == -7), app
+    finally:
+        if with_literals:
+            t.set_added_tokens([])
+
+
 @pytest.mark.parametrize("name", ["gpt2", "llama3"])
 def test_empty_session_and_literals(cfg, name):
     t, o = cfg[name]

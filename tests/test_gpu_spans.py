@@ -19,7 +19,7 @@ import pytest
 import exact_byte_level_utf8_amd as tk
 import oracle
 from synth import textgen
-from tests import libs, vocab
+from tests import libs, oracle_par, vocab
 
 pytestmark = pytest.mark.gpu
 
@@ -177,9 +177,10 @@ def test_graph_replay_with_spans(cfg):
 
 
 def test_batch_workload_spans(cfg):
-    """64 documents of 500,000 characters: sampled documents equal the oracle;
-    in every document the spans start at its first byte and step by the
-    token lengths up to its last byte."""
+    """64 documents of 500,000 characters: every document's IDs and spans
+    equal the oracle's (spans counted from the batch's first byte), and in
+    every document the spans start at its first byte and step by the token
+    lengths up to its last byte."""
     t, o, tokb = cfg["llama3"]
     texts = textgen.batch_texts(40_000, 64, 500_000)
     data, off = textgen.pack_docs(texts)
@@ -190,9 +191,33 @@ def test_batch_workload_spans(cfg):
         assert sp[a] == off[i]
         assert np.array_equal(sp[a + 1:z], sp[a:z - 1] + lens[a:z - 1])
         assert sp[z - 1] + lens[z - 1] == off[i + 1]
-    for i in (0, 40):
-        s, e = int(off[i]), int(off[i + 1])
-        want_ids, want_sp = o.encode_spans(data[s:e])
+    docs = [data[int(off[i]):int(off[i + 1])] for i in range(64)]
+    want = oracle_par.map_docs(o.encode_spans, docs)
+    want_ids, want_off = oracle_par.concat([w[0] for w in want])
+    same("output offsets", out_off, want_off)
+    for i in range(64):
         a, z = int(out_off[i]), int(out_off[i + 1])
-        same(f"doc {i} ids", ids[a:z], want_ids)
-        same(f"doc {i} spans", sp[a:z], want_sp + np.uint64(s))
+        same(f"doc {i} ids", ids[a:z], want[i][0])
+        same(f"doc {i} spans", sp[a:z], want[i][1] + np.uint64(off[i]))
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_long_pieces_spans(cfg, name):
+    """Spans of pieces over 64 bytes (the long-piece kernel's tokens), single
+    request and batch, with documents starting at a long piece: equal to the
+    oracle's merge-tracked spans."""
+    t, o, _ = cfg[name]
+    rng = random.Random(5)
+    cjk = lambda k: "".join(chr(rng.randint(0x4E00, 0x9FFF)) for _ in range(k))  # noqa: E731
+    docs = [" " * 300 + "x", cjk(500) + ", " + cjk(66), "ab" * 2049, "w" * 65 + " " + cjk(1400), "é" * 80]
+    b = "".join(docs).encode()
+    ids, sp = dev_spans(t, b)
+    want_ids, want_sp = o.encode_spans(b)
+    same("single ids", ids, want_ids)
+    same("single spans", sp, want_sp)
+    data, off = textgen.pack_docs(docs)
+    ids, sp, out_off = dev_spans(t, data, off)
+    want_ids, want_sp, want_off = o.encode_batch_spans(data, off)
+    same("batch ids", ids, want_ids)
+    same("batch spans", sp, want_sp)
+    same("batch offsets", out_off, want_off)

@@ -32,6 +32,10 @@ def rules():
     L.rules_cpu_select.restype = ctypes.c_uint64
     L.rules_cpu_select.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
     L.rules_cpu_class.argtypes = [ctypes.c_uint32]
+    L.rules_cpu_class_range.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    L.rules_cpu_class_range.restype = None
+    L.rules_cpu_fold_extra.argtypes = [ctypes.c_uint32]
+    L.rules_cpu_letter_code.argtypes = [ctypes.c_uint32]
 
     def pieces(b: bytes, pat: int, doc_off=None):
         out = np.zeros(max(len(b), 1), dtype=np.uint64)
@@ -54,12 +58,37 @@ def orcs():
 
 
 def test_device_class_table_matches_oracle_table(rules):
-    rng = random.Random(0)
-    cps = list(range(0, 0x3400)) + rng.sample(range(0x3400, 0x110000), 60000)
-    for cp in cps:
+    """Every Unicode scalar value (U+0000..U+10FFFF without the surrogates):
+    the kernels' class table equals the oracle's, which is pinned against the
+    regex module code point by code point."""
+    n = 0x110000
+    dev = np.zeros(n, dtype=np.uint8)
+    rules.rules_cpu_class_range(0, n, dev.ctypes.data)
+    want = oracle.class_range(0, n)
+    scalar = np.ones(n, dtype=bool)
+    scalar[0xD800:0xE000] = False
+    bad = np.nonzero((dev != want) & scalar)[0]
+    assert bad.size == 0, [hex(int(c)) for c in bad[:10]]
+
+
+def test_device_fold_table(rules):
+    """The kernels' non-ASCII contraction letters are exactly the code points
+    that the regex module's case-insensitive matching takes for one of the
+    contraction letters s t r e v m l d, each mapped to that letter; checked
+    over every scalar value outside ASCII."""
+    import regex
+    any_letter = regex.compile("(?i)[strevmld]")
+    singles = {a: regex.compile("(?i)" + a) for a in "strevmld"}
+    for cp in range(0x80, 0x110000):
         if 0xD800 <= cp <= 0xDFFF:
             continue
-        assert rules.rules_cpu_class(cp) == oracle.char_class(cp), hex(cp)
+        ch = chr(cp)
+        code = rules.rules_cpu_fold_extra(cp)
+        if not any_letter.fullmatch(ch):
+            assert code == 0, hex(cp)
+            continue
+        letter = next(a for a, r in singles.items() if r.fullmatch(ch))
+        assert code != 0 and code == rules.rules_cpu_letter_code(ord(letter)), hex(cp)
 
 
 @pytest.mark.parametrize("pat", [0, 1])
