@@ -342,7 +342,7 @@ class Tokenizer:
         return list(out[:k])
 
 
-STAGES = ("pretokenize", "pieces", "assemble", "long_pieces")
+STAGES = ("pretokenize", "pieces", "assemble")
 
 
 def flags_to_starts(flags: np.ndarray, n: int) -> np.ndarray:

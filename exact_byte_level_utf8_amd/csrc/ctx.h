@@ -53,7 +53,7 @@ inline void hfree(T*& p) {
   p = nullptr;
 }
 
-constexpr int kStages = 4;  // pre-tokenization, piece pass, assembly, long pieces
+constexpr int kStages = 3;  // pre-tokenization, piece pass, assembly
 
 // Key of a captured pipeline: every argument baked into its kernel launches.
 struct GraphKey {
@@ -191,11 +191,6 @@ struct tok_ctx {
     dfree(b.ws_sym);
     dfree(b.ws_rk);
     dfree(b.ws_sel);
-    dfree(b.tile_run);
-    dfree(b.lq_ctr);
-    dfree(b.lq_start);
-    dfree(b.lq_len);
-    dfree(b.lq_cnt);
     free_lit_bufs();
     dfree(d_text);
     dfree(d_ids);
@@ -221,12 +216,7 @@ struct tok_ctx {
         hipMalloc((void**)&b.ws_rk, (c + 64) * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&b.ws_sel, (c + 64) * sizeof(uint64_t)) != hipSuccess ||
         hipMalloc((void**)&b.sum1, ((tiles >> kSum1Shift) + 1) * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.sum2, ((tiles >> kSum2Shift) + 1) * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.tile_run, tiles * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.lq_ctr, 16 * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.lq_start, (c / 64 + 64) * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.lq_len, (c / 64 + 64) * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.lq_cnt, (c / 64 + 64) * sizeof(uint32_t)) != hipSuccess) {
+        hipMalloc((void**)&b.sum2, ((tiles >> kSum2Shift) + 1) * sizeof(uint32_t)) != hipSuccess) {
       (void)hipGetLastError();
       free_scratch();
       return TOK_E_NOMEM;
@@ -247,9 +237,7 @@ struct tok_ctx {
            fill(b.tile_first, tiles * 4) && fill(b.ws_sym, (cap + 64) * 4) && fill(b.ws_rk, (cap + 64) * 4) &&
            fill(b.ws_sel, (cap + 64) * 8) && fill(b.sum1, ((tiles >> kSum1Shift) + 1) * 4) &&
            fill(b.sum2, ((tiles >> kSum2Shift) + 1) * 4) && fill(d_text, cap + 64) && fill(d_ids, (cap + 64) * 4) &&
-           fill(d_spans, (cap + 64) * 4) && fill(b.tile_run, tiles * 4) && fill(b.lq_ctr, 64) &&
-           fill(b.lq_start, (cap / 64 + 64) * 4) && fill(b.lq_len, (cap / 64 + 64) * 4) &&
-           fill(b.lq_cnt, (cap / 64 + 64) * 4);
+           fill(d_spans, (cap + 64) * 4);
     }
     if (ok && lb.cand) {
       const uint64_t parts = lit_docs + 2 * lit_cap;
@@ -463,7 +451,6 @@ struct tok_ctx {
     launch_pretok(text, n, doc_off, n_docs, pattern, bb, s, e0(0), e1(0));
     if (out_flags) return;
     launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s, e0(1), e1(1));
-    launch_long(text, n, t, bb, s, e0(3), e1(3));
     launch_assemble(n, bb, out, spans, d_tok_len, out_cap, doc_off, n_docs, out_off, s, e0(2), e1(2));
   }
 
@@ -563,13 +550,11 @@ struct tok_ctx {
     Bufs bb = b;
     bb.gen = ++gen;
     const uint32_t tiles = (uint32_t)((n + kPieceTile - 1) / kPieceTile);
-    std::vector<uint32_t> zero(std::max<size_t>((tiles >> kSum1Shift) + 1, 2), 0);  // group sums start at zero
+    std::vector<uint32_t> zero((tiles >> kSum1Shift) + 1, 0);  // group sums start at zero
     HIP_OK(hipMemcpyAsync(bb.sum1, zero.data(), zero.size() * 4, hipMemcpyHostToDevice, stream));
     HIP_OK(hipMemcpyAsync(bb.sum2, zero.data(), ((tiles >> kSum2Shift) + 1) * 4, hipMemcpyHostToDevice, stream));
-    HIP_OK(hipMemcpyAsync(bb.lq_ctr, zero.data(), 2 * 4, hipMemcpyHostToDevice, stream));  // empty long-piece queue
     const Tables t = tables(false);
     launch_pieces(d_text, n, t, bb, nullptr, 0, nullptr, stream);
-    launch_long(d_text, n, t, bb, stream);
     launch_assemble(n, bb, d_ids, nullptr, nullptr, n, nullptr, 0, nullptr, stream);
     HIP_OK(hipGetLastError());
     HIP_OK(hipStreamSynchronize(stream));

@@ -17,12 +17,6 @@
 // a cumulative sum gives the offsets).  A tile's run covers the text
 // contiguously from its first piece start, so the offsets are that byte plus
 // a workgroup scan of the lengths along the run: no scan crosses tiles.
-//
-// A piece longer than 64 bytes is one marker entry in its tile's run; the
-// long-piece kernel (k_long.hip) left its tokens, their first bytes relative
-// to the piece and their count, and added the count (less the marker's one)
-// to the tile counts.  The marker expands here: later entries move on by that
-// count, and the piece's tokens are copied in at the marker's place.
 #include "tok_internal.h"
 #include "wg_scan.h"
 
@@ -38,8 +32,7 @@ assemble_kernel(uint64_t n, Bufs B, int32_t* __restrict__ out, uint32_t* __restr
                 uint32_t n_docs, uint64_t* __restrict__ out_off) {
   __shared__ uint32_t s_part[kAsmThreads / kWave];
   __shared__ uint32_t s_scan[kAsmThreads / kWave];
-  __shared__ uint32_t s_doc0, s_nmk;
-  __shared__ uint32_t s_mk_out[16], s_mk_j[16], s_mk_run[16];  // markers of the tile's run
+  __shared__ uint32_t s_doc0;
   if (B.n_docs_dev) n_docs = *B.n_docs_dev;
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   const uint32_t tile = blockIdx.x;
@@ -63,56 +56,8 @@ assemble_kernel(uint64_t n, Bufs B, int32_t* __restrict__ out, uint32_t* __restr
   const uint32_t base = __builtin_amdgcn_readfirstlane(s_part[0] + s_part[1] + s_part[2] + s_part[3]);
   const uint32_t cnt = __builtin_amdgcn_readfirstlane(B.tile_cnt[tile]);
   const uint32_t first = __builtin_amdgcn_readfirstlane(B.tile_first[tile]);
-  const uint32_t runw = __builtin_amdgcn_readfirstlane(B.tile_run[tile]);
-  const uint32_t run_len = runw & 0x7FFFFFFFu;
-  const bool marks = (runw >> 31) != 0u;
   const int32_t* run = B.staging + first;
-  if (marks) {
-    // the run holds markers (-1 - queue index) of pieces merged by the
-    // long-piece kernel: each stands for that piece's tokens, so every later
-    // entry moves on by the piece's count less one (a workgroup scan per pass)
-    if (tid == 0) s_nmk = 0;
-    uint32_t extra = 0, at = first;
-    for (uint32_t i0 = 0; i0 < run_len; i0 += kAsmThreads) {  // uniform trip count: the scans hold barriers
-      const uint32_t i = i0 + tid;
-      const int32_t v = i < run_len ? run[i] : 0;
-      const bool mk = v < 0;
-      const uint32_t j = mk ? (uint32_t)~v : 0u;
-      const uint32_t x = mk ? B.lq_cnt[j] - 1u : 0u;
-      uint32_t xs = 0;
-      const uint32_t xb = wg_excl_scan<kAsmThreads>(x, 0u, AddOp(), s_scan, &xs);
-      const uint32_t o = base + i + extra + xb;  // this entry's (or the piece's first token's) output index
-      uint32_t sp = 0;
-      if constexpr (SPANS) {
-        const uint32_t len = i >= run_len ? 0u : mk ? B.lq_len[j] : tok_len[v];
-        uint32_t chunk = 0;
-        sp = at + wg_excl_scan<kAsmThreads>(len, 0u, AddOp(), s_scan, &chunk);
-        at += chunk;
-      }
-      if (i < run_len && !mk && (uint64_t)o < cap) {
-        out[o] = v;
-        if constexpr (SPANS) spans[o] = sp;
-      }
-      if (mk) {
-        const uint32_t m = atomicAdd(&s_nmk, 1u);  // at most 16 pieces over 64 bytes start in a tile
-        s_mk_out[m] = o;
-        s_mk_j[m] = j;
-        s_mk_run[m] = i;
-      }
-      extra = __builtin_amdgcn_readfirstlane(extra + xs);
-    }
-    __syncthreads();
-    const uint32_t nmk = __builtin_amdgcn_readfirstlane(s_nmk);
-    for (uint32_t m = 0; m < nmk; ++m) {
-      const uint32_t j = s_mk_j[m], o = s_mk_out[m];
-      const uint32_t c = B.lq_cnt[j], st = B.lq_start[j];
-      for (uint32_t k = tid; k < c; k += kAsmThreads) {
-        if ((uint64_t)o + k >= cap) break;
-        out[o + k] = (int32_t)B.ws_sym[st + k];
-        if constexpr (SPANS) spans[o + k] = st + B.ws_rk[st + k];
-      }
-    }
-  } else if constexpr (SPANS) {
+  if constexpr (SPANS) {
     // uniform trip count: the scan inside holds barriers
     uint32_t at = first;
     for (uint32_t i0 = 0; i0 < cnt; i0 += kAsmThreads) {
@@ -138,7 +83,6 @@ assemble_kernel(uint64_t n, Bufs B, int32_t* __restrict__ out, uint32_t* __restr
   }
   if (doc_off) {
     const uint64_t t0 = (uint64_t)tile * kPieceTile;
-    const uint32_t nmk = marks ? __builtin_amdgcn_readfirstlane(s_nmk) : 0u;
     for (uint32_t d = s_doc0 + tid; d <= n_docs; d += kAsmThreads) {
       const uint64_t p = doc_off[d];
       if (p >= n) {
@@ -148,12 +92,7 @@ assemble_kernel(uint64_t n, Bufs B, int32_t* __restrict__ out, uint32_t* __restr
       }
       if (p >= t0 + kPieceTile) break;
       if (p < t0) continue;  // only with unordered offsets, which the call rejects
-      // the piece pass stored the offset within the tile's run; markers before
-      // it stand for more than one token
-      uint64_t o = out_off[d] + base;
-      for (uint32_t m = 0; m < nmk; ++m)
-        if (s_mk_run[m] < out_off[d]) o += B.lq_cnt[s_mk_j[m]] - 1u;
-      out_off[d] = o;
+      out_off[d] += base;    // the piece pass stored the offset within the tile's run
     }
   }
 }

@@ -14,13 +14,10 @@
 //      into lists in LDS, one per table, and then run one per lane, so a wave
 //      waits for one memory round trip.  Every other piece goes to a work
 //      list in LDS by length.
-//      A piece longer than 64 bytes is deferred to the long-piece kernel
-//      (k_long.hip): its first byte goes to a device work queue and one
-//      marker entry (-1 - its queue index) stands for its tokens in the run.
-//   2. The workgroup's waves merge the listed pieces: 33..64-byte pieces
-//      first (one wave per piece, one symbol per lane), then 17..32-byte
-//      pieces (two per wave, one 32-lane row each), then 2..16-byte pieces
-//      (four per wave, one 16-lane row each).
+//   2. The workgroup's waves merge the listed pieces of up to 64 bytes:
+//      33..64-byte pieces first (one wave per piece, one symbol per lane),
+//      then 17..32-byte pieces (two per wave, one 32-lane row each), then
+//      2..16-byte pieces (four per wave, one 16-lane row each).
 //      A round takes the row minimum of (rank, position), chooses every
 //      leftmost non-overlapping occurrence of that pair value at once,
 //      compacts the row with a lane permute, and re-probes only the pairs next
@@ -28,6 +25,11 @@
 //      the minimum-rank pair equals iterated single merges, and only pairs
 //      adjacent to a completed merge are re-probed; GraphTok: a round takes
 //      every other pair of a chain).
+//   2b. Then the whole workgroup merges each piece longer than 64 bytes in
+//      turn (long_merge.h): its symbols in an LDS pool that overlays the
+//      length-class and probe lists (dead by then), or in the byte-indexed
+//      workspace in global memory for pieces larger than the pool.  Its
+//      tokens end in that workspace.
 //   3. The tile's tokens are compacted in order (in LDS) and written as one
 //      run from the tile's first piece start, with the tile's count, which is
 //      also added to the sums of its groups of 64 and 4096 tiles; the
@@ -35,6 +37,7 @@
 //      The assembly kernel then places the runs (k_assemble.hip).
 #include "tok_internal.h"
 #include "bpe_util.h"
+#include "long_merge.h"
 #include "wg_scan.h"
 
 #pragma clang diagnostic ignored "-Wbitwise-instead-of-logical"
@@ -306,6 +309,26 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
   }
 }
 
+// Byte offset of the first piece start after s, or n (one wave).
+__device__ inline uint64_t next_start(const uint16_t* flags, uint64_t n, uint64_t s) {
+  const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint64_t c = s / kChunk;
+  const uint32_t own = flags[c] & ~((2u << (s % kChunk)) - 1u);
+  if (own) return c * kChunk + __builtin_ctz(own);
+  for (uint64_t cb = c + 1; cb < n_chunks; cb += 64) {
+    const uint64_t ci = cb + lane;
+    const uint32_t wv = ci < n_chunks ? flags[ci] : 0u;
+    const uint64_t mask = __ballot(wv != 0);
+    if (mask) {
+      const uint32_t l = __builtin_ctzll(mask);
+      const uint32_t wl = __builtin_amdgcn_readfirstlane(__shfl(wv, l, 64));
+      return (cb + l) * kChunk + __builtin_ctz(wl);
+    }
+  }
+  return n;
+}
+
 constexpr uint32_t kXcds = 8;    // XCDs of the device; workgroups are dealt to them in turn
 constexpr uint32_t kXcdCus = 32;  // compute units per XCD
 constexpr uint32_t kLine = 128;   // L2 line bytes
@@ -349,23 +372,38 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   constexpr int kCapA = kPieceTile / 13 + 1, kCapB = kPieceTile / 9 + 1, kCapC = kPieceTile / 5 + 1;
   constexpr int kCapD = kPieceTile / 2;
   constexpr int kCapH = kPieceTile / (kRowMax + 1) + 1, kCap1 = kPieceTile / (kHalfMax + 1) + 1;
+  constexpr int kCap2 = kPieceTile / (kWaveMax + 1) + 1;  // pieces over 64 bytes: at most 16 start in a tile
+  constexpr int kCapPS = kPieceTile / 2, kCapPL = kPieceTile / (kWordMax + 1) + 1;
+  // the length-class lists and the probe lists of 2..13-byte and 14..28-byte
+  // pieces live in one pool; once phase 2 is done the pool holds the
+  // symbols of one long piece at a time (16 bytes per symbol: as many as the
+  // workgroup's LDS share allows at full occupancy)
+  constexpr int kListWords = kCapA + kCapB + kCapC + kCapD + kCapH + kCap1 + kCapPS + kCapPL;
+  constexpr int kLongE = NT == 512 ? 2 : 3;                // long-piece symbols per thread and chunk
+  constexpr int kLongSyms = NT == 512 ? 2048 : NT * kLongE;  // long-piece symbols held in LDS (whole chunks)
+  constexpr int kPoolWords = kListWords > 4 * kLongSyms ? kListWords : 4 * kLongSyms;
   __shared__ __attribute__((aligned(16))) uint8_t s_text[kTextLds];
   __shared__ uint16_t s_flags[kFlagLds];
   __shared__ uint32_t s_tok[kTokLds];
   __shared__ uint8_t s_cnt8[kPieceTile];
-  __shared__ uint32_t s_la[kCapA], s_lb[kCapB], s_lc[kCapC], s_ld[kCapD];
-  __shared__ uint32_t s_lh[kCapH], s_list1[kCap1];
-  // probe lists of 2..13-byte and 14..28-byte pieces
-  __shared__ uint32_t s_probe_s[kPieceTile / 2], s_probe_l[kPieceTile / (kWordMax + 1) + 1];
+  __shared__ __attribute__((aligned(16))) uint32_t s_pool[kPoolWords];
+  uint32_t* const s_la = s_pool;
+  uint32_t* const s_lb = s_la + kCapA;
+  uint32_t* const s_lc = s_lb + kCapB;
+  uint32_t* const s_ld = s_lc + kCapC;
+  uint32_t* const s_lh = s_ld + kCapD;
+  uint32_t* const s_list1 = s_lh + kCapH;
+  uint32_t* const s_probe_s = s_list1 + kCap1;
+  uint32_t* const s_probe_l = s_probe_s + kCapPS;
+  __shared__ uint32_t s_list2[kCap2];
   __shared__ uint32_t s_cnt[kChunksPerWg], s_excl[kChunksPerWg];
-  __shared__ uint32_t s_n[9], s_next, s_first, s_doc0, s_marks;
+  __shared__ uint32_t s_n[9], s_next, s_first, s_doc0, s_lend;
+  __shared__ uint32_t s_lscan[NT / kWave];
+  __shared__ uint32_t s_lat[kCap2];  // phase 3: run position of each long piece
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   if (tid < 9) s_n[tid] = 0;
-  if (tid == 0) {
-    s_next = 0;
-    s_marks = 0;
-  }
+  if (tid == 0) s_next = 0;
   const uint32_t tile = blockIdx.x;
   const uint64_t base = (uint64_t)tile * kPieceTile;
   const uint64_t c0 = (uint64_t)tile * kChunksPerWg;
@@ -401,11 +439,11 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
                         touch_lines<NT>(T.pair_rank, 256u * 256u * 4u, 1);
   __syncthreads();
 
-  // a piece of 2..64 bytes that needs the merge loop goes to the list of its
-  // length class
+  // a piece that needs the merge loop goes to the list of its length class
   auto list_piece = [&](uint32_t item) {
     const uint32_t len = item >> 16;
-    if (len > (uint32_t)kHalfMax) s_list1[atomicAdd(&s_n[4], 1u)] = item;
+    if (len > (uint32_t)kWaveMax) s_list2[atomicAdd(&s_n[5], 1u)] = item & 0xFFFFu;
+    else if (len > (uint32_t)kHalfMax) s_list1[atomicAdd(&s_n[4], 1u)] = item;
     else if (len > (uint32_t)kRowMax) s_lh[atomicAdd(&s_n[8], 1u)] = item;
     else if (len >= 13u) s_la[atomicAdd(&s_n[0], 1u)] = item;
     else if (len >= 9u) s_lb[atomicAdd(&s_n[1], 1u)] = item;
@@ -446,14 +484,6 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
         s_probe_s[atomicAdd(&s_n[6], 1u)] = item;
       } else if (T.long_slots && len <= (uint32_t)kLongMax) {
         s_probe_l[atomicAdd(&s_n[7], 1u)] = item;
-      } else if (len > (uint32_t)kWaveMax) {
-        // deferred to the long-piece kernel: a queue entry and one marker
-        const uint32_t j = atomicAdd(&B.lq_ctr[0], 1u);
-        B.lq_start[j] = (uint32_t)s0;
-        s_tok[off] = ~j;
-        s_cnt8[off] = 1;
-        s_marks = 1u;
-        ++hits;
       } else {
         list_piece(item);
       }
@@ -488,11 +518,11 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   __syncthreads();
 
   // phase 2: the waves take items in order, longest pieces first: 33..64
-  // bytes (a wave each), then pairs of 17..32-byte
-  // pieces (a 32-lane row each), then groups of four 2..16-byte pieces by
-  // length class (a 16-lane row each).  The item index comes from an LDS
-  // counter through readfirstlane, so every branch on it is uniform across
-  // the wave.
+  // bytes (a wave each), then pairs of 17..32-byte pieces (a 32-lane row
+  // each), then groups of four 2..16-byte pieces by length class (a 16-lane
+  // row each).  The item index comes from an LDS counter through
+  // readfirstlane, so every branch on it is uniform across the wave.
+  const uint32_t n2 = __builtin_amdgcn_readfirstlane(s_n[5]);
   {
     const uint32_t n1 = __builtin_amdgcn_readfirstlane(s_n[4]);
     const uint32_t nh = __builtin_amdgcn_readfirstlane(s_n[8]);
@@ -531,6 +561,34 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   }
   __syncthreads();
 
+  // phase 2b: every piece over 64 bytes, merged by the whole workgroup in
+  // turn (uniform loop: the rounds hold barriers).  Its symbols go to the LDS
+  // pool when they fit, else to the workspace at the piece's bytes; its
+  // tokens end in ws_sym[start ..] and its count in the chunk total, with a
+  // count byte of 0 marking it for phase 3.
+  for (uint32_t k = 0; k < n2; ++k) {
+    const uint32_t off = s_list2[k];
+    const uint64_t s = base + off;
+    if (tid < (uint32_t)kWave) {
+      const uint64_t e = next_start(B.flags, n, s);
+      if (tid == 0) s_lend = (uint32_t)(e - s);
+    }
+    __syncthreads();
+    const uint32_t len = __builtin_amdgcn_readfirstlane(s_lend);
+    uint32_t cnt;
+    if (len <= (uint32_t)kLongSyms)
+      cnt = longp::long_piece<NT, kLongE>(text, s, len, T, s_pool, s_pool + kLongSyms,
+                                          reinterpret_cast<uint2*>(s_pool + 2 * kLongSyms), B.ws_sym + s, s_lscan);
+    else
+      cnt = longp::long_piece<NT, kLongE>(text, s, len, T, B.ws_sym + s, B.ws_rk + s,
+                                          reinterpret_cast<uint2*>(B.ws_sel + s), B.ws_sym + s, s_lscan);
+    if (tid == 0) {
+      s_cnt8[off] = 0;
+      s_cnt[off / kChunk] += cnt;
+    }
+    __syncthreads();  // the pool and s_lend are reused by the next piece
+  }
+
   // phase 3: the tile's tokens as one run from its first piece start (the
   // thread index again through an empty asm, so that no address computed
   // before the merge phase is kept, and spilled, across it)
@@ -549,8 +607,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
     }
     if (t2 == 0) {
       s_first = (uint32_t)first;
-      B.tile_cnt[tile] = total;  // the long-piece kernel adds the deferred pieces' tokens
-      B.tile_run[tile] = total | (s_marks << 31);
+      B.tile_cnt[tile] = total;
       B.tile_first[tile] = (uint32_t)first;
       atomicAdd(&B.sum1[tile >> kSum1Shift], total);
       atomicAdd(&B.sum2[tile >> kSum2Shift], total);
@@ -563,7 +620,8 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   // every thread writes the tokens of the pieces that start in its two bytes:
   // its position in the run is its chunk's offset plus the counts of the
   // earlier pieces of the chunk (a scan over the chunk's eight threads).  A
-  // deferred piece writes its one marker.
+  // piece longer than 64 bytes is its chunk's last piece; its count is what
+  // the chunk's total leaves, and its tokens are in the long-piece workspace.
   {
     int32_t* run = B.staging + __builtin_amdgcn_readfirstlane(s_first);
     // this thread's piece starts, read again from LDS rather than kept live
@@ -585,13 +643,32 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
       if (q >= (uint32_t)d) incl += up;
     }
     uint32_t at = s_excl[lc] + (incl - own);
+    const uint32_t chunk_end = s_excl[lc] + s_cnt[lc];
 #pragma unroll
     for (uint32_t b = 0; b < (uint32_t)kBytesPer; ++b) {
       if (!((mine >> b) & 1u)) continue;
       const uint32_t off = lc * kChunk + kBytesPer * q + b;
       const uint32_t k = s_cnt8[off];
-      for (uint32_t j = 0; j < k; ++j) run[at + j] = (int32_t)s_tok[off + j];
-      at += k;
+      if (k == 0) {  // long piece: its chunk's last; copied below by the whole workgroup
+        uint32_t m = 0;
+        while (s_list2[m] != off) ++m;
+        s_lat[m] = at;
+        at = chunk_end;
+      } else {
+        for (uint32_t j = 0; j < k; ++j) run[at + j] = (int32_t)s_tok[off + j];
+        at += k;
+      }
+    }
+  }
+
+  if (n2) {  // uniform
+    __syncthreads();
+    int32_t* run = B.staging + __builtin_amdgcn_readfirstlane(s_first);
+    for (uint32_t m = 0; m < n2; ++m) {
+      const uint32_t off = s_list2[m], at = s_lat[m];
+      const uint32_t lc = off / kChunk, c = s_excl[lc] + s_cnt[lc] - at;  // the chunk's tokens from `at` on
+      const uint32_t* src = B.ws_sym + base + off;
+      for (uint32_t j = threadIdx.x; j < c; j += NT) run[at + j] = (int32_t)src[j];
     }
   }
 

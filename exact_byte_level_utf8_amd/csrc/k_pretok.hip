@@ -148,15 +148,11 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
   const int64_t base = (int64_t)blockIdx.x * kPT;
   uint16_t* __restrict__ flags = B.flags;
   // per-call set-up for the later passes: clear the group sums of the tile
-  // counts and the long-piece queue, and check the batch's document offsets
+  // counts, and check the batch's document offsets
   if (tid == 0) {
     const uint32_t tiles = gridDim.x;
     if (blockIdx.x < ((tiles + 63u) >> kSum1Shift)) B.sum1[blockIdx.x] = 0;
     if (blockIdx.x < ((tiles + 4095u) >> kSum2Shift)) B.sum2[blockIdx.x] = 0;
-    if (blockIdx.x == 0) {  // the long-piece queue starts empty
-      B.lq_ctr[0] = 0;
-      B.lq_ctr[1] = 0;
-    }
     if (doc_off && blockIdx.x == 0 && (doc_off[0] != 0 || doc_off[n_docs] != n)) report(&B.ctr->err_docs, B.gen);
   }
   if (doc_off) {

@@ -10,13 +10,11 @@
 //   tile_first uint32[G]       byte offset of tile t's first piece start
 //   sum1       uint32[G / 64]  tile counts summed over aligned groups of 64 tiles
 //   sum2       uint32[G / 4096] the same over groups of 4096 tiles
-//   tile_run   uint32[G]       entries of tile t's run (bit 31: it holds markers)
-//   lq_*       uint32[N/64+64] queue of pieces longer than 64 bytes: first
-//                              byte, byte length, token count (+ 2 counters)
-//   ws_sym/rk  uint32[N + 64]  the long pieces' tokens and their first bytes
-//                              (relative), indexed by the piece's bytes; the
-//                              merge workspace of pieces over 4,096 bytes
-//   ws_sel     uint64[N + 64]  the latter's per-token operand ranks
+//   ws_sym     uint32[N + 64]  tokens of the pieces longer than 64 bytes,
+//                              indexed by the piece's bytes; with ws_rk
+//                              uint32[N + 64] and ws_sel uint64[N + 64] (per
+//                              token: lowest operand ranks) the merge
+//                              workspace of pieces too long for the LDS pool
 // and, in pinned host memory mapped into the device, one Counters block that
 // the host reads after its one synchronization of the call.
 // Everything else a tile needs (its bytes, piece lists, tokens, counts) lives
@@ -109,11 +107,6 @@ struct Bufs {
   uint32_t* ws_sym;
   uint32_t* ws_rk;
   uint64_t* ws_sel;
-  uint32_t* tile_run;  // per tile: entries of its run (a deferred piece is one marker), bit 31: has markers
-  uint32_t* lq_ctr;    // long-piece queue: [0] pieces queued, [1] next to take (cleared by pre-tokenization)
-  uint32_t* lq_start;  // per queued piece: its first byte
-  uint32_t* lq_len;    // its byte length (written by the long-piece kernel)
-  uint32_t* lq_cnt;    // its token count (written by the long-piece kernel)
   Counters* ctr;  // device address of the host-mapped counters
   uint64_t gen;   // this call's number
   const uint32_t* n_docs_dev;  // if set, the document count, read on the device (overrides n_docs)
@@ -170,8 +163,6 @@ void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uin
 void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, const uint64_t* doc_off,
                    uint32_t n_docs, uint64_t* out_off, hipStream_t s, hipEvent_t e0 = nullptr,
                    hipEvent_t e1 = nullptr);
-void launch_long(const uint8_t* text, uint64_t n, Tables t, Bufs b, hipStream_t s, hipEvent_t e0 = nullptr,
-                 hipEvent_t e1 = nullptr);
 // spans: optional uint32 per output ID, the byte where its token starts
 // (tok_len is read only when spans is set).
 void launch_assemble(uint64_t n, Bufs b, int32_t* out, uint32_t* spans, const uint32_t* tok_len, uint64_t cap,

@@ -392,10 +392,9 @@ size_t tok_token_lengths(const tok_ctx* ctx, uint32_t* len_out, size_t n);
  * system-scope fence).  tok_stage_ms writes the last call's stage durations in ms, 0 for
  * stages not timed: [0] pre-tokenization (with the per-call set-up of the
  * later passes), [1] piece pass (single bytes, whole-piece hits, merge
- * rounds of pieces of up to 64 bytes, one run of IDs per 1 KiB tile), [2]
- * assembly (output offsets of the runs and their copy, with the long pieces'
- * tokens put in place), [3] long pieces (merge rounds of every piece longer
- * than 64 bytes, one workgroup per piece; it runs between [1] and [2]).  Returns the number
+ * rounds of the remaining pieces, the longer ones by the whole workgroup,
+ * one run of IDs per 1 KiB tile), [2] assembly (output offsets of the runs
+ * and their copy).  Returns the number
  * of stages written (at most n).  tok_set_profiling: TOK_E_ARG for a null
  * context or a negative mask.
  */
@@ -420,8 +419,7 @@ size_t tok_graph_count(const tok_ctx* ctx);
 #define TOK_STAGE_PRETOK 1
 #define TOK_STAGE_PIECES 2
 #define TOK_STAGE_ASSEMBLE 4
-#define TOK_STAGE_LONG 8
-#define TOK_STAGES_ALL 15
+#define TOK_STAGES_ALL 7
 int tok_set_profiling(tok_ctx* ctx, int stages);
 int tok_stage_ms(const tok_ctx* ctx, float* ms, int n);
 
