@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtok.so")
 
-PATTERNS = {"gpt2": 0, "llama3": 1}
+PATTERNS = {"gpt2": 0, "llama3": 1, "o200k": 2}
 
 TOK_OK, TOK_E_ARG, TOK_E_BADMERGES, TOK_E_PATTERN, TOK_E_UTF8 = 0, 1, 2, 3, 4
 TOK_E_CAPACITY, TOK_E_TOOLONG, TOK_E_DEVICE, TOK_E_NOMEM, TOK_E_SESSION = 5, 6, 7, 8, 9

@@ -160,7 +160,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
       o.repair_margin > (1u << 20) || o.initial_bytes > TOK_MAX_BYTES)
     return TOK_E_ARG;
   const int device = o.device;
-  if (pattern != TOK_PAT_GPT2 && pattern != TOK_PAT_LLAMA3) return TOK_E_PATTERN;
+  if (pattern != TOK_PAT_GPT2 && pattern != TOK_PAT_LLAMA3 && pattern != TOK_PAT_O200K) return TOK_E_PATTERN;
   if (n_merges > TOK_MAX_MERGES) return TOK_E_BADMERGES;
   // operands precede their merge, and each ordered pair has one rank
   // open addressing over buckets of kBucket slots, at most half full; a key

@@ -435,6 +435,18 @@ struct tok_ctx {
     return TOK_OK;
   }
 
+  // After a call's synchronization: the durations of its timed stages (the
+  // first `last` stages ran), 0 for the others.
+  void collect_stage_times(int last) {
+    if (!prof) return;
+    for (int i = 0; i < kStages; ++i) {
+      float ms = 0.f;
+      const bool timed = i < last && ((prof >> i) & 1u);
+      if (timed && hipEventElapsedTime(&ms, ev0[i], ev1[i]) != hipSuccess) ms = 0.f;
+      stage_ms[i] = timed ? ms : 0.f;
+    }
+  }
+
   // start and end events for stage i when it is timed, else none
   hipEvent_t e0(int i) const { return (prof >> i) & 1u ? ev0[i] : nullptr; }
   hipEvent_t e1(int i) const { return (prof >> i) & 1u ? ev1[i] : nullptr; }
@@ -521,15 +533,7 @@ struct tok_ctx {
     }
     HIP_OK(hipGetLastError());
     HIP_OK(hipStreamSynchronize(s));
-    if (prof) {
-      const int last = n == 0 ? 0 : out_flags ? 1 : kStages;
-      for (int i = 0; i < kStages; ++i) {
-        float ms = 0.f;
-        const bool timed = i < last && ((prof >> i) & 1u);
-        if (timed && hipEventElapsedTime(&ms, ev0[i], ev1[i]) != hipSuccess) ms = 0.f;
-        stage_ms[i] = timed ? ms : 0.f;
-      }
-    }
+    collect_stage_times(n == 0 ? 0 : out_flags ? 1 : kStages);
     if (c->err_docs == call) return TOK_E_ARG;
     if (c->err_utf8 == call) return TOK_E_UTF8;
     if (out_flags) return TOK_OK;

@@ -55,7 +55,7 @@ struct RepairArgs {
   const uint8_t* tok_bytes;      // token t is tok_bytes[tok_off[t] .. + tok_len[t])
   const uint64_t* tok_off;
   uint32_t vocab, max_tok_len;  // max_tok_len: the longest token or literal
-  int gpt2;                      // 1: GPT-2 style family, 0: Llama-3 style
+  int pattern;                   // TOK_PAT_GPT2, TOK_PAT_LLAMA3 or TOK_PAT_O200K
   Literals L;                    // added-token literals (L.n == 0: none); their IDs name no token
   uint32_t* st_off;              // scratch: first byte of the r-th stored record from the end
   uint64_t* splice;              // device words: [0] first window record to copy, [1] session

@@ -466,7 +466,9 @@ void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uin
   // up to one tile per workgroup slot of the device, 8 waves per tile; larger
   // inputs use 4-wave workgroups, which pack the CUs better
   const bool small = tiles <= (uint32_t)kPretokSmallGrid;
-  if (pattern == 0) {
+  if (pattern == 2) {  // the case-splitting family: segments between synchronizing cuts
+    launch_pretok_case(text, n, doc_off, n_docs, b, s, e0, e1);
+  } else if (pattern == 0) {
     if (small) launch_on(pretok_kernel<0, 512>, dim3(tiles), dim3(512), s, e0, e1, text, n, doc_off, n_docs, b);
     else launch_on(pretok_kernel<0, 256>, dim3(tiles), dim3(256), s, e0, e1, text, n, doc_off, n_docs, b);
   } else {

@@ -26,6 +26,7 @@
 #include "sync_rules.h"
 #include "wg_scan.h"
 #include "uniclass.inc"
+#include "uniclass_case.inc"
 
 namespace tok {
 namespace {
@@ -41,6 +42,13 @@ __device__ inline uint32_t rp_class(uint32_t cp) {
   if (cp >= 0x110000) return kO;
   const uint32_t blk = kClsBlock[cp >> 8];
   return (kClsBits[blk * 64 + ((cp & 255u) >> 2)] >> (2 * (cp & 3u))) & 3u;
+}
+
+__device__ inline uint32_t rp_case(uint32_t cp) {
+  if (cp < TOK_CLS_LOW) return (kCaseLow[cp >> 1] >> (4 * (cp & 1u))) & 15u;
+  if (cp >= 0x110000) return 6u;
+  const uint32_t blk = kCaseBlock[cp >> 8];
+  return (kCaseBits[blk * 128 + ((cp & 255u) >> 1)] >> (4 * (cp & 1u))) & 15u;
 }
 
 // Code point whose lead byte is at index i of w[0, n) (valid UTF-8 there).
@@ -227,7 +235,8 @@ __global__ void __launch_bounds__(kRpThreads) repair_match_kernel(RepairArgs A) 
         uint64_t j = i - 1;
         while (j > 0 && (A.win[j] & 0xC0u) == 0x80u) --j;
         const uint32_t x = rp_cp(A.win, wn, j), y = rp_cp(A.win, wn, i);
-        cert = sync_transition_of(A.gpt2 != 0, x, rp_class(x), y, rp_class(y)) &&
+        cert = (A.pattern == 2 ? sync_transition_case(x, rp_case(x), y, rp_case(y))
+                               : sync_transition_of(A.pattern == 0, x, rp_class(x), y, rp_class(y))) &&
                (A.L.n == 0 || !inside_literal(A, off));
       }
     }

@@ -25,6 +25,7 @@ namespace {
 
 #define TOK_CLS_QUAL static
 #include "uniclass.inc"
+#include "uniclass_case.inc"
 #undef TOK_CLS_QUAL
 
 uint32_t host_class(uint32_t cp) {
@@ -33,6 +34,13 @@ uint32_t host_class(uint32_t cp) {
   if (cp >= 0x110000) return kO;
   const uint32_t blk = kClsBlock[cp >> 8];
   return (kClsBits[blk * 64 + ((cp & 255u) >> 2)] >> (2 * (cp & 3u))) & 3u;
+}
+
+uint32_t host_case(uint32_t cp) {
+  if (cp < TOK_CLS_LOW) return (kCaseLow[cp >> 1] >> (4 * (cp & 1u))) & 15u;
+  if (cp >= 0x110000) return 6u;
+  const uint32_t blk = kCaseBlock[cp >> 8];
+  return (kCaseBits[blk * 128 + ((cp & 255u) >> 1)] >> (4 * (cp & 1u))) & 15u;
 }
 
 bool is_cont(uint8_t b) { return (b & 0xC0) == 0x80; }
@@ -79,6 +87,7 @@ uint64_t fwd_code_points(const uint8_t* t, uint64_t start, uint64_t end, uint64_
 }
 
 bool sync_transition(int pattern, uint32_t x, uint32_t y) {
+  if (pattern == TOK_PAT_O200K) return sync_transition_case(x, host_case(x), y, host_case(y));
   return sync_transition_of(pattern == TOK_PAT_GPT2, x, host_class(x), y, host_class(y));
 }
 
@@ -93,7 +102,7 @@ struct Rec {
 extern "C" {
 
 int tok_sync_boundary(int pattern, uint32_t prev_cp, uint32_t cp) {
-  if (pattern != TOK_PAT_GPT2 && pattern != TOK_PAT_LLAMA3) return 0;
+  if (pattern != TOK_PAT_GPT2 && pattern != TOK_PAT_LLAMA3 && pattern != TOK_PAT_O200K) return 0;
   return sync_transition(pattern, prev_cp, cp) ? 1 : 0;
 }
 
@@ -329,7 +338,7 @@ int tok_repair_dev(tok_ctx* ctx, int32_t* d_session_ids, size_t n_session, size_
       a.vocab = (uint32_t)ctx->tok_len.size();
       a.max_tok_len = longest;
       a.L = ctx->literals();
-      a.gpt2 = ctx->pattern == TOK_PAT_GPT2 ? 1 : 0;
+      a.pattern = ctx->pattern;
       // free once the window encode is done: 6 words of splice parameters,
       // then the stored offsets (at most one per window byte; the buffer
       // holds the capacity plus 64 words)

@@ -1,0 +1,223 @@
+// Pre-tokenization of the case-splitting (o200k-style) family by segments.
+//
+// TokTier, section 4 "Removing the sequential regex scan", describes this
+// lineage as the cl100k/Llama-3 rules plus a case-boundary rule inside letter
+// runs, a contraction path, and a narrow fallback for marks.  Here the family
+// is: an optional prefix char P (not CR, LF, a letter or a number), then
+// either H* T+ or H+ T* (H = upper-case or caseless letters or marks, T =
+// lower-case or caseless letters or marks), then an optional case-insensitive
+// contraction suffix; digit groups of 1-3; an optional space, a run of other
+// chars and marks, and trailing CR/LF; whitespace up to the last CR/LF of its
+// run; whitespace not followed by non-whitespace; whitespace.
+//
+// Instead of a per-code-point predicate with run aggregates, the text is cut
+// at synchronizing transitions (sync_rules.h: for every left context, a piece
+// starts there, the pieces after it are those of the text from there alone,
+// and the pieces before it do not depend on the text after it).  Between two
+// such cuts the pieces are found by matching the alternatives in order from
+// the cut, one piece after another.  Cuts come at nearly every word edge, so
+// a segment is short, and each segment is independent of every other.
+//
+// This header holds the matching logic only; the text is read through an
+// accessor (a.at(p): the info word of the code point at byte p), so the same
+// code runs in the pre-tokenization kernel and in a CPU build for the tests.
+#pragma once
+
+#include <stdint.h>
+
+#include "sync_rules.h"
+
+#ifndef TOK_HD
+#define TOK_HD __host__ __device__
+#endif
+// the matcher's steps are inlined into the one loop that calls them
+#define TOK_SEG_INLINE __attribute__((always_inline)) inline
+
+namespace tok {
+namespace seg {
+
+// letter-case classes
+enum : uint32_t { kSU = 0, kSD = 1, kSC = 2, kSM = 3, kSN = 4, kSW = 5, kSO = 6 };
+
+// info word of the code point at a byte
+enum : uint32_t {
+  kQSub = 7u,             // bits 0-2: letter-case class
+  kQLead = 1u << 3,       // a code point starts at this byte
+  kQLenShift = 4,         // bits 4-6: its UTF-8 length
+  kQCrlf = 1u << 7,       // U+000D or U+000A
+  kQSpace = 1u << 8,      // U+0020
+  kQApos = 1u << 9,       // U+0027
+  kQFoldShift = 10,       // bits 10-13: contraction letter under case folding (s t r e v m l d = 1..8)
+  kQDocStart = 1u << 14,  // a document starts at this byte
+  kQEnd = 1u << 15,       // no code point: past the text
+  kQCpShift = 16,         // bits 16-31: the code point if below U+10000, else 0xFFFF
+};
+enum : uint32_t { kFS = 1, kFT, kFR, kFE, kFV, kFM, kFL, kFD };
+
+TOK_HD inline uint32_t sub_of(uint32_t q) { return q & kQSub; }
+TOK_HD inline uint32_t len_of(uint32_t q) { return (q >> kQLenShift) & 7u; }
+TOK_HD inline uint32_t fold_of(uint32_t q) { return (q >> kQFoldShift) & 15u; }
+TOK_HD inline bool in_h(uint32_t s) { return s == kSU || s == kSC || s == kSM; }
+TOK_HD inline bool in_t(uint32_t s) { return s == kSD || s == kSC || s == kSM; }
+TOK_HD inline bool in_om(uint32_t s) { return s == kSO || s == kSM; }
+// the optional prefix char of a letter piece: not CR, LF, a letter or a number
+TOK_HD inline bool is_prefix(uint32_t q) { return !(q & kQCrlf) && sub_of(q) >= kSM && sub_of(q) != kSN; }
+
+// Info word of a decoded code point.
+TOK_HD inline uint32_t make_q(uint32_t cp, uint32_t sub, uint32_t len, uint32_t fold) {
+  uint32_t q = sub | kQLead | (len << kQLenShift) | (fold << kQFoldShift);
+  q |= (cp == 0x0D || cp == 0x0A) ? kQCrlf : 0u;
+  q |= cp == 0x20 ? kQSpace : 0u;
+  q |= cp == 0x27 ? kQApos : 0u;
+  q |= (cp < 0xFFFFu ? cp : 0xFFFFu) << kQCpShift;
+  return q;
+}
+
+// Contraction letter of a code point under simple case folding (ASCII letters
+// either case; fold_extra: the code for a non-ASCII code point that folds to
+// one of them, else 0).
+TOK_HD inline uint32_t fold_code(uint32_t cp, uint32_t fold_extra) {
+  if (cp >= 0x80) return fold_extra;
+  switch (cp | 0x20u) {
+    case 's': return kFS;
+    case 't': return kFT;
+    case 'r': return kFR;
+    case 'e': return kFE;
+    case 'v': return kFV;
+    case 'm': return kFM;
+    case 'l': return kFL;
+    case 'd': return kFD;
+    default: return 0;
+  }
+}
+
+// The pieces of a segment are matched from a cursor p.  Within a match,
+// any position past p where a document starts, or past the text, ends the
+// text (documents are hard boundaries).
+template <typename Acc>
+struct Matcher {
+  const Acc a;  // held by value, so a device accessor stays in registers
+  uint64_t p;  // the cursor: the current piece's first byte
+
+  TOK_HD TOK_SEG_INLINE uint32_t q(uint64_t i) const {
+    const uint32_t v = a.at(i);
+    return (i > p && (v & kQDocStart)) ? kQEnd : v;
+  }
+  TOK_HD static bool end(uint32_t v) { return (v & kQEnd) != 0; }
+
+  // optional contraction suffix at e: 's 't 're 've 'm 'll 'd, any case
+  TOK_HD TOK_SEG_INLINE uint64_t suffix(uint64_t e) const {
+    const uint32_t v = q(e);
+    if (end(v) || !(v & kQApos)) return e;
+    const uint64_t e1 = e + 1;
+    const uint32_t v1 = q(e1);
+    if (end(v1)) return e;
+    const uint32_t f1 = fold_of(v1);
+    const uint64_t e2 = e1 + len_of(v1);
+    if (f1 == kFS || f1 == kFT || f1 == kFM || f1 == kFD) return e2;
+    if (f1 == kFR || f1 == kFV || f1 == kFL) {
+      const uint32_t v2 = q(e2);
+      if (end(v2)) return e;
+      const uint32_t f2 = fold_of(v2);
+      if ((f1 == kFL && f2 == kFL) || (f1 != kFL && f2 == kFE)) return e2 + len_of(v2);
+    }
+    return e;
+  }
+
+  // First byte after the piece that starts at the cursor.
+  TOK_HD TOK_SEG_INLINE uint64_t piece_end() const {
+    const uint32_t v0 = q(p);
+    const uint32_t s0 = sub_of(v0);
+    const uint64_t n0 = p + len_of(v0);
+    // P? H* T+ S?: the prefix taken if possible, then H* as long as it goes;
+    // T+ starts at the first char after H* that is in T, else at the last
+    // char of the H* stretch that is also in T
+    for (int pre = 1; pre >= 0; --pre) {
+      if (pre && !is_prefix(v0)) continue;
+      uint64_t h = pre ? n0 : p, last_t = ~0ull;
+      uint32_t vh = q(h);
+      while (!end(vh) && in_h(sub_of(vh))) {
+        if (in_t(sub_of(vh))) last_t = h;
+        h += len_of(vh);
+        vh = q(h);
+      }
+      if (!end(vh) && in_t(sub_of(vh))) {
+        uint64_t e = h;
+        uint32_t ve = vh;
+        while (!end(ve) && in_t(sub_of(ve))) {
+          e += len_of(ve);
+          ve = q(e);
+        }
+        return suffix(e);
+      }
+      if (last_t != ~0ull) return suffix(last_t + len_of(q(last_t)));
+    }
+    // P? H+ T* S?
+    for (int pre = 1; pre >= 0; --pre) {
+      if (pre && !is_prefix(v0)) continue;
+      uint64_t h = pre ? n0 : p;
+      uint32_t vh = q(h);
+      if (end(vh) || !in_h(sub_of(vh))) continue;
+      while (!end(vh) && in_h(sub_of(vh))) {
+        h += len_of(vh);
+        vh = q(h);
+      }
+      while (!end(vh) && in_t(sub_of(vh))) {
+        h += len_of(vh);
+        vh = q(h);
+      }
+      return suffix(h);
+    }
+    // digits in groups of one to three
+    if (s0 == kSN) {
+      uint64_t e = p;
+      uint32_t ve = v0;
+      for (int k = 0; k < 3 && !end(ve) && sub_of(ve) == kSN; ++k) {
+        e += len_of(ve);
+        ve = q(e);
+      }
+      return e;
+    }
+    // an optional space, other chars and marks, then CR/LF
+    {
+      uint64_t e = ~0ull;
+      if ((v0 & kQSpace) && !end(q(n0)) && in_om(sub_of(q(n0)))) e = n0;
+      else if (in_om(s0)) e = p;
+      if (e != ~0ull) {
+        uint32_t ve = q(e);
+        while (!end(ve) && in_om(sub_of(ve))) {
+          e += len_of(ve);
+          ve = q(e);
+        }
+        while (!end(ve) && (ve & kQCrlf)) {
+          e += len_of(ve);
+          ve = q(e);
+        }
+        return e;
+      }
+    }
+    // whitespace: up to its last CR/LF; else not followed by non-whitespace;
+    // else all of it
+    uint64_t e = p, last_crlf = ~0ull, last_start = p;
+    uint32_t count = 0, ve = v0;
+    while (!end(ve) && sub_of(ve) == kSW) {
+      if (ve & kQCrlf) last_crlf = e;
+      last_start = e;
+      ++count;
+      e += len_of(ve);
+      ve = q(e);
+    }
+    if (last_crlf != ~0ull) return last_crlf + 1;  // CR and LF are one byte each
+    if (end(ve)) return e;
+    return count >= 2 ? last_start : e;
+  }
+};
+
+// Synchronizing transition from the code point with info x to the one with
+// info y (both decoded, both in one document).
+TOK_HD inline bool sync_at(uint32_t x, uint32_t y) {
+  return sync_transition_case(x >> kQCpShift, sub_of(x), y >> kQCpShift, sub_of(y));
+}
+
+}  // namespace seg
+}  // namespace tok

@@ -22,7 +22,18 @@
 //   prefixes a letter run, or a contraction), and other -> CR/LF (the other
 //   piece takes trailing CR/LF).
 //
-// Per-code-point logic only, for the host repair and the device repair.
+//   Case-splitting (o200k-style) family, over letter-case classes (U upper or
+//   title case, D lower case, C caseless letters, M marks, N, W, O): a number
+//   after anything else, and from a number to anything else; a letter before
+//   whitespace, before an other char that is not the apostrophe (which may
+//   begin a contraction suffix), and D -> U (the case boundary) except inside
+//   a mixed-case contraction suffix ('rE 'vE 'lL); a mark or an
+//   other char before whitespace that is not CR/LF (an other-run may take
+//   marks and trailing CR/LF); CR/LF before a letter or mark; and whitespace
+//   before an other char unless the whitespace is U+0020.
+//
+// Per-code-point logic only, for the host repair, the device repair and the
+// segment pre-tokenizer of the case-splitting family.
 #pragma once
 
 #include <stdint.h>
@@ -49,6 +60,27 @@ TOK_HD inline bool sync_transition_of(bool gpt2, uint32_t x, uint32_t cx, uint32
   if (cx == 3u && cy == 0u) return false;             // O -> L
   if (cx == 3u && y_crlf) return false;               // O -> CR/LF
   return true;
+}
+
+// Case-splitting family.  sx, sy: letter-case classes of x and y (U=0 D=1
+// C=2 M=3 N=4 W=5 O=6).
+TOK_HD inline bool sync_transition_case(uint32_t x, uint32_t sx, uint32_t y, uint32_t sy) {
+  constexpr uint32_t U = 0, D = 1, M = 3, N = 4, W = 5, O = 6;
+  if (sy == N) return sx != N;
+  if (sx == N) return true;
+  const bool x_crlf = x == 0x0D || x == 0x0A, y_crlf = y == 0x0D || y == 0x0A;
+  if (sx < M) {  // a letter
+    if (sy == W) return true;
+    if (sy == O) return y != 0x27;
+    // D -> U, unless it is the middle of a two-letter contraction suffix in
+    // mixed case ('rE 'vE 'lL)
+    return sx == D && sy == U && !(((x == 'r' || x == 'v') && y == 'E') || (x == 'l' && y == 'L'));
+  }
+  if (sx == M || sx == O) return sy == W && !y_crlf;
+  // x is whitespace
+  if (sy == W) return false;
+  if (sy == O) return x != 0x20;
+  return x_crlf;  // a letter or a mark
 }
 
 }  // namespace tok

@@ -160,6 +160,10 @@ inline void launch_on(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
 void launch_empty_batch(Bufs b, const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s);
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
                    int pattern, Bufs b, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+// The case-splitting family's pre-tokenization (k_pretok_case.hip), called by
+// launch_pretok for that pattern.
+void launch_pretok_case(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, Bufs b,
+                        hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, const uint64_t* doc_off,
                    uint32_t n_docs, uint64_t* out_off, hipStream_t s, hipEvent_t e0 = nullptr,
                    hipEvent_t e1 = nullptr);

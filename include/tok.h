@@ -17,7 +17,7 @@
  *     IDs 0..255 are the single bytes; merge r creates ID 256 + r.  Ranks are
  *     keyed by the ordered ID pair (GraphTok, section 4: the lowest rank wins,
  *     the leftmost pair on equal rank).
- *   - pattern: the pre-tokenizer family, TOK_PAT_GPT2 or TOK_PAT_LLAMA3.
+ *   - pattern: the pre-tokenizer family, TOK_PAT_GPT2, TOK_PAT_LLAMA3 or TOK_PAT_O200K.
  *     encode(x) = concatenation over the pre-tokenization pieces p of x, in
  *     order, of bpe(bytes(p)) (TokTier, Appendix A, Definition A.2 and
  *     Lemma A.3).
@@ -64,6 +64,14 @@ typedef struct tok_ctx tok_ctx;
 /* Pre-tokenizer families. */
 #define TOK_PAT_GPT2 0   /* 's|'t|'re|'ve|'m|'ll|'d| ?L+| ?N+| ?[^\s L N]+|\s+(?!\S)|\s+ */
 #define TOK_PAT_LLAMA3 1 /* (?i:contractions)|[^\r\n L N]?L+|N{1,3}| ?[^\s L N]+[\r\n]*|\s*[\r\n]+|\s+(?!\S)|\s+ */
+/* Case-splitting family (the o200k lineage as TokTier, section 4, describes it:
+ * the Llama-3 style with a case-boundary rule inside letter runs, marks
+ * joining letters and contractions as a suffix of a letter piece):
+ * P?H*T+S?|P?H+T*S?|N{1,3}| ?[^\s L N]+[\r\n]*|\s*[\r\n]+|\s+(?!\S)|\s+ with H = upper-case or
+ * caseless letters or marks, T = lower-case or caseless letters or marks,
+ * P = one char that is not CR, LF, a letter or a number, S = an optional
+ * case-insensitive 's 't 're 've 'm 'll 'd. */
+#define TOK_PAT_O200K 2
 
 /* Largest input of one call, in bytes (token counts and offsets are 32-bit
  * on the device). */

@@ -1,6 +1,6 @@
-"""Train the three seeded merge lists (the frozen tokenizer configurations).
+"""Train the seeded merge lists (the frozen tokenizer configurations).
 
-    python -m synth.train_vocab [--only tiny|gpt2_50k|llama3_128k]
+    python -m synth.train_vocab [--only tiny_1k|gpt2_50k|llama3_128k|o200k_64k]
 
 For each vocabulary: generate the seeded training corpus (synth.textgen),
 split it into pieces with the third-party ``regex`` module running the
@@ -54,6 +54,7 @@ VOCABS = {
     "tiny_1k": ("tiny", [101], 200_000, "gpt2", 1_000),
     "gpt2_50k": ("mix", list(range(20_000, 20_020)), 1_000_000, "gpt2", 50_000),
     "llama3_128k": ("mix", list(range(50_000, 50_050)), 1_000_000, "llama3", 127_744),
+    "o200k_64k": ("mix", list(range(80_000, 80_020)), 1_000_000, "o200k", 64_000),
 }
 
 

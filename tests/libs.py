@@ -10,6 +10,7 @@ CONFIGS = {
     "tiny": ("tiny_1k", "gpt2"),
     "gpt2": ("gpt2_50k", "gpt2"),
     "llama3": ("llama3_128k", "llama3"),
+    "o200k": ("o200k_64k", "o200k"),
 }
 
 

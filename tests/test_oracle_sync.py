@@ -51,14 +51,15 @@ def _fails(orc, C: str, x: str, y: str, R: str) -> bool:
     return False
 
 
-def _derive(pattern: str):
+def _derive(pattern: str, alpha=ALPHA, small=SMALL, klass=lambda c: oracle.char_class(ord(c))):
     orc = oracle.Oracle(vocab.merges("tiny_1k"), pattern)
-    cls = {c: oracle.char_class(ord(c)) for c in ALPHA}
-    pairs = [(x, y) for x in ALPHA for y in ALPHA if cls[x] != cls[y]]
+    cls = {c: klass(c) for c in alpha}
+    pairs = [(x, y) for x in alpha for y in alpha if cls[x] != cls[y]]
+    ALPHA_, SMALL_ = alpha, small
     rng = random.Random(12345)
     failing = set()
-    small_ctx = ["".join(t) for n in range(3) for t in itertools.product(SMALL, repeat=n)]
-    small_right = ["".join(t) for n in range(2) for t in itertools.product(SMALL, repeat=n)]
+    small_ctx = ["".join(t) for n in range(3) for t in itertools.product(SMALL_, repeat=n)]
+    small_right = ["".join(t) for n in range(2) for t in itertools.product(SMALL_, repeat=n)]
     for x, y in pairs:
         done = False
         # exhaustive over short contexts from a smaller alphabet
@@ -74,18 +75,28 @@ def _derive(pattern: str):
             continue
         # random longer contexts from the full alphabet, with runs
         for _ in range(150):
-            C = "".join(rng.choice(ALPHA) * rng.choice([1, 1, 2, 4]) for _ in range(rng.randint(0, 4)))
-            R = "".join(rng.choice(ALPHA) * rng.choice([1, 1, 2, 4]) for _ in range(rng.randint(0, 4)))
+            C = "".join(rng.choice(ALPHA_) * rng.choice([1, 1, 2, 4]) for _ in range(rng.randint(0, 4)))
+            R = "".join(rng.choice(ALPHA_) * rng.choice([1, 1, 2, 4]) for _ in range(rng.randint(0, 4)))
             if _fails(orc, C, x, y, R):
                 failing.add((x, y))
                 break
     return pairs, failing
 
 
-@pytest.mark.parametrize("pattern", ["gpt2", "llama3"])
+# the case-splitting family: letters of every case kind, the letters that end
+# two-letter contractions in either case, and marks
+CASE_ALPHA = ["s", "e", "l", "r", "v", "a", "S", "E", "L", "A", "ǅ", "ʰ", "中", "́", "ः", "é", "1", "²", " ", "\t",
+              "\n", "\r", "\u00a0", "'", ".", "!", "\U0001F600"]
+CASE_SMALL = ["s", "l", "A", "L", "中", "́", "1", " ", "\n", "'", "."]
+
+
+@pytest.mark.parametrize("pattern", ["gpt2", "llama3", "o200k"])
 def test_sync_set_is_sound_and_exact(pattern):
     libs.ensure_built()
-    pairs, failing = _derive(pattern)
+    if pattern == "o200k":
+        pairs, failing = _derive(pattern, CASE_ALPHA, CASE_SMALL, lambda c: int(oracle.subclass_range(ord(c), 1)[0]))
+    else:
+        pairs, failing = _derive(pattern)
     claimed = {(x, y) for x, y in pairs if sync_boundary(pattern, ord(x), ord(y))}
     unsound = sorted(claimed & failing)
     assert not unsound, f"declared synchronizing but the oracle finds a failure: {unsound}"
@@ -97,6 +108,6 @@ def test_sync_set_is_sound_and_exact(pattern):
 
 def test_same_class_is_never_a_certificate():
     libs.ensure_built()
-    for pattern in ("gpt2", "llama3"):
+    for pattern in ("gpt2", "llama3", "o200k"):
         for x, y in [("a", "b"), (" ", " "), ("1", "2"), (".", "!"), ("\n", " ")]:
             assert not sync_boundary(pattern, ord(x), ord(y))

@@ -146,3 +146,72 @@ def test_round_selection_closed_form(rules):
         m = sum(1 << j for j in range(64) if rng.random() < p)
         c = rng.randint(0, 1)
         assert rules.rules_cpu_select(m, c) == ref(m, c)
+
+
+# ---------------------------------------------------------------- case-splitting family
+# The segment pre-tokenizer (seg_rules.h), built for the CPU and run the way
+# the kernel runs it (1 KiB tiles, segments between synchronizing cuts),
+# against the oracle's direct matcher.
+
+CASE_ALPHA = ["A", "S", "ǅ", "a", "s", "t", "e", "ʰ", "中", "́", "ः", "ſ", "'", " ", "\t", "\n", "\r", "1", "."]
+CASE_WIDE = CASE_ALPHA + ["T", "L", "D", "r", "v", "m", "l", "d", "E", "R", "V", "M", "é", "É", "ß", "ǈ", "Ω",
+                          "ω", "²", "_", '"', "(", " ", "\u0085", "\U0001F600", "⃝", "ー", "ｱ"]
+
+
+@pytest.fixture(scope="module")
+def case_orc():
+    return oracle.Oracle(np.zeros((0, 2), dtype=np.uint32), "o200k")
+
+
+def test_case_table_matches_oracle(rules):
+    """The kernels' letter-case table equals the oracle's (which is pinned
+    against the regex module) over every scalar value."""
+    rules.rules_cpu_case_range.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    rules.rules_cpu_case_range.restype = None
+    dev = np.zeros(0x110000, dtype=np.uint8)
+    rules.rules_cpu_case_range(0, 0x110000, dev.ctypes.data)
+    want = oracle.subclass_range(0, 0x110000)
+    scalar = np.ones(0x110000, dtype=bool)
+    scalar[0xD800:0xE000] = False
+    bad = np.nonzero((dev != want) & scalar)[0]
+    assert bad.size == 0, [hex(int(c)) for c in bad[:10]]
+
+
+def test_case_exhaustive_short_strings(rules, case_orc):
+    for n in range(1, 5):
+        for tup in itertools.product(CASE_ALPHA, repeat=n):
+            b = "".join(tup).encode()
+            assert rules.pieces(b, 2) == case_orc.pieces(b), b
+
+
+def test_case_random_strings(rules, case_orc):
+    rng = random.Random(21)
+    for _ in range(30000):
+        b = "".join(rng.choice(CASE_WIDE) * rng.choice([1, 1, 1, 2, 5]) for _ in range(rng.randint(1, 40))).encode()
+        assert rules.pieces(b, 2) == case_orc.pieces(b), b
+
+
+def test_case_long_runs_across_tiles(rules, case_orc):
+    texts = ["A" * 3000 + "b" * 2000 + " x", "ab" * 2000 + "C", "中" * 777 + "A", "7" * 5000 + "x",
+             " " * 3000 + "y", "x" + "\n" * 2050 + "  y", "Aa" * 1500, "a" + "́" * 1300 + "B", "DON'T" * 400,
+             "'" * 3000 + "s", "!" + "́" * 2000 + "a", "x'd" * 900, textgen.cjk_text(8, 5000)]
+    for t in texts:
+        b = t.encode()
+        assert rules.pieces(b, 2) == case_orc.pieces(b), t[:30]
+
+
+@pytest.mark.parametrize("seed,n", [(2, 150_000), (3, 60_000)])
+def test_case_workload_text(rules, case_orc, seed, n):
+    b = textgen.mix_text(seed, n).encode()
+    assert rules.pieces(b, 2) == case_orc.pieces(b)
+
+
+def test_case_documents_are_hard_boundaries(rules, case_orc):
+    rng = random.Random(4)
+    docs = ["".join(rng.choice(CASE_WIDE) for _ in range(rng.randint(0, 30))) for _ in range(300)]
+    data = "".join(docs).encode()
+    off = np.cumsum([0] + [len(d.encode()) for d in docs])
+    want = []
+    for d, s in zip(docs, off[:-1]):
+        want += [int(s) + p for p in case_orc.pieces(d.encode())]
+    assert rules.pieces(data, 2, off) == want
