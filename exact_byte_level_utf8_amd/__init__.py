@@ -21,6 +21,7 @@ PATTERNS = {"gpt2": 0, "llama3": 1, "o200k": 2}
 TOK_OK, TOK_E_ARG, TOK_E_BADMERGES, TOK_E_PATTERN, TOK_E_UTF8 = 0, 1, 2, 3, 4
 TOK_E_CAPACITY, TOK_E_TOOLONG, TOK_E_DEVICE, TOK_E_NOMEM, TOK_E_SESSION = 5, 6, 7, 8, 9
 TOK_MAX_BYTES = 0xFFFF0000  # longest input, in bytes
+TOK_NOALLOC_MAX_BYTES = 1 << 20  # longest input of tok_encode_dev_noalloc
 
 # every function declared in include/tok.h
 EXPORTS = (
@@ -28,7 +29,7 @@ EXPORTS = (
     "tok_encode_batch_dev", "tok_encode_spans_dev", "tok_encode_spans", "tok_pretokenize_dev", "tok_repair",
     "tok_repair_dev", "tok_sync_boundary", "tok_get_info",
     "tok_token_lengths", "tok_set_added_tokens", "tok_set_graph", "tok_graph_count", "tok_set_profiling", "tok_stage_ms",
-    "tok_fill_scratch",
+    "tok_fill_scratch", "tok_encode_dev_noalloc",
 )
 
 
@@ -102,10 +103,12 @@ def lib() -> ctypes.CDLL:
         L.tok_set_profiling.argtypes = [vp, i32]
         L.tok_stage_ms.argtypes = [vp, vp, i32]
         L.tok_fill_scratch.argtypes = [vp, i32]
+        L.tok_encode_dev_noalloc.argtypes = [vp, vp, sz, vp, sz, szp, vp]
         for name in ("tok_load", "tok_encode", "tok_encode_dev", "tok_encode_batch", "tok_encode_batch_dev",
                      "tok_encode_spans_dev", "tok_encode_spans", "tok_pretokenize_dev", "tok_repair",
                      "tok_repair_dev", "tok_sync_boundary", "tok_get_info", "tok_set_added_tokens",
-                     "tok_set_graph", "tok_set_profiling", "tok_stage_ms", "tok_fill_scratch"):
+                     "tok_set_graph", "tok_set_profiling", "tok_stage_ms", "tok_fill_scratch",
+                     "tok_encode_dev_noalloc"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -262,6 +265,16 @@ class Tokenizer:
         _check(lib().tok_encode_dev(self._h, _dev_ptr(d_text, "uint8", "text"), n_bytes,
                                     _dev_ptr(d_ids, "int32", "ids"), d_ids.numel(), ctypes.byref(n),
                                     _stream_handle(stream)), "tok_encode_dev")
+        return n.value
+
+    def encode_dev_noalloc(self, d_text, d_ids, length: int | None = None, stream=None) -> int:
+        """tok_encode_dev_noalloc: as encode_dev, with no allocation during the call (inputs up to
+        TOK_NOALLOC_MAX_BYTES)."""
+        n_bytes = d_text.numel() if length is None else int(length)
+        n = ctypes.c_size_t(0)
+        _check(lib().tok_encode_dev_noalloc(self._h, _dev_ptr(d_text, "uint8", "text"), n_bytes,
+                                            _dev_ptr(d_ids, "int32", "ids"), d_ids.numel(), ctypes.byref(n),
+                                            _stream_handle(stream)), "tok_encode_dev_noalloc")
         return n.value
 
     def encode_batch_dev(self, d_text, d_doc_off, d_ids, d_out_off, stream=None) -> int:

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtok.so")
 RULES_LIB = os.path.join(HERE, "librules_cpu.so")
 SOURCES = ["capi.hip", "repair.hip", "k_pretok.hip", "k_pretok_case.hip", "k_bpe.hip", "k_assemble.hip",
-           "k_added.hip", "k_repair.hip"]
+           "k_added.hip", "k_repair.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

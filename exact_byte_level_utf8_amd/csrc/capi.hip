@@ -255,6 +255,9 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
         hipHostGetDevicePointer((void**)&ctx->d_ctr, ctx->h_ctr, 0) != hipSuccess)
       break;
     std::memset(ctx->h_ctr, 0, sizeof(Counters));
+    // the no-allocation entry point's array: its address on this device, once
+    // per device (a failed lookup only disables that entry point)
+    (void)noalloc_scratch(device);
     ctx->b.ctr = ctx->d_ctr;
     ctx->merge_buckets = bmask;
     rc = build_word_table(ctx, tok);

@@ -15,6 +15,11 @@
 
 using namespace tok;  // internal header of the library's host sources only
 
+// Device address of the no-allocation scratch array on `device` (current),
+// looked up on the first call for that device (noalloc.hip); nullptr if the
+// lookup failed.
+uint8_t* noalloc_scratch(int device);
+
 #define HIP_OK(expr)                       \
   do {                                     \
     if ((expr) != hipSuccess) {            \

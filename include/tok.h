@@ -170,6 +170,25 @@ int tok_encode_dev(tok_ctx* ctx, const uint8_t* d_text, size_t len, int32_t* d_i
                    size_t* n_out, void* stream);
 
 /*
+ * tok_encode_dev_noalloc -- tok_encode_dev that allocates nothing, for
+ * callers that cannot allocate device memory during a call (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, results and errors as tok_encode_dev, for len up to
+ * TOK_NOALLOC_MAX_BYTES (else TOK_E_TOOLONG, before any device work).  Every
+ * per-call device buffer comes from one fixed array that the library holds on
+ * each GPU it runs on until the process ends (about 20 MiB); the call makes
+ * no hipMalloc, hipFree or other allocation.  All calls on one GPU share that
+ * array, so calls that overlap on one GPU (from any context or thread) race:
+ * the caller must serialize them.  Added-token literals are not supported
+ * here (TOK_E_ARG when the context has any): their pass needs more buffers.
+ * The array's address is looked up at tok_load; TOK_E_DEVICE if that failed.
+ */
+#define TOK_NOALLOC_MAX_BYTES 0x100000ull
+int tok_encode_dev_noalloc(tok_ctx* ctx, const uint8_t* d_text, size_t len, int32_t* d_ids, size_t cap,
+                           size_t* n_out, void* stream);
+
+/*
  * tok_encode_batch -- encode n_docs independent documents in one pipeline
  * pass (GraphTok, section 5 "Implementation", the batch entry point; TokTier,
  * section 4 "GPU BPE", multi-document batches).  Document i is text[doc_off[i] .. doc_off[i+1]);

@@ -108,5 +108,6 @@ def test_constants_match_the_header():
     defs = {m.group(1): int(m.group(2).rstrip("uUlL"), 0)
             for m in re.finditer(r"#define\s+(TOK_\w+)\s+(0x[0-9A-Fa-f]+[uUlL]*|\d+)", text)}
     for name in ("TOK_OK", "TOK_E_ARG", "TOK_E_BADMERGES", "TOK_E_PATTERN", "TOK_E_UTF8", "TOK_E_CAPACITY",
-                 "TOK_E_TOOLONG", "TOK_E_DEVICE", "TOK_E_NOMEM", "TOK_E_SESSION", "TOK_MAX_BYTES"):
+                 "TOK_E_TOOLONG", "TOK_E_DEVICE", "TOK_E_NOMEM", "TOK_E_SESSION", "TOK_MAX_BYTES",
+                 "TOK_NOALLOC_MAX_BYTES"):
         assert defs[name] == getattr(tk, name), name
