@@ -70,6 +70,11 @@ WORKLOADS = {
     # CJK-dense text: every ideograph run is one long letter piece (the long-piece merge path)
     "cjk_1m": ("1M-char CJK-dense request (ideograph runs of 50-2,000 chars), GPT-2-style pattern, 50K merges",
                "gpt2_50k", "gpt2", "cjk", 5, 1_000_000, 1),
+    # the case-splitting (o200k-style) family: segment pre-tokenization
+    "o200k_1m": ("1M-char agent-transcript request, case-splitting (o200k-style) pattern, 64K merges",
+                 "o200k_64k", "o200k", "mix", 8, 1_000_000, 1),
+    "cjk_o200k_1m": ("1M-char CJK-dense request, case-splitting (o200k-style) pattern, 64K merges",
+                     "o200k_64k", "o200k", "cjk", 9, 1_000_000, 1),
     # chat transcript with added-token markers taken ahead of the pattern (tok_set_added_tokens)
     "chat_1m": ("1M-char chat transcript with 5 added-token markers, GPT-2-style pattern, 50K merges",
                 "gpt2_50k", "gpt2", "chat", 7, 1_000_000, 1),
@@ -77,7 +82,7 @@ WORKLOADS = {
     "repair": ("tok_repair: 1M-char stored context + 1,400-char append, GPT-2-style pattern, 50K merges",
                "gpt2_50k", "gpt2", "mix", 2, 1_000_000, 1),
 }
-EXTRA = ["tiny_10k", "llama3_3m", "batch64", "cjk_1m", "chat_1m", "repair"]
+EXTRA = ["tiny_10k", "llama3_3m", "batch64", "cjk_1m", "chat_1m", "o200k_1m", "cjk_o200k_1m", "repair"]
 
 # dominant-stage kernel and the sources its code comes from (for matching
 # committed counter summaries to the kernel that produced them)

@@ -175,6 +175,9 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
   std::vector<uint32_t> tmin(2 * (256 + n_merges), kNoRank);
   std::vector<std::vector<uint8_t>> tok(256 + n_merges);
   for (uint32_t i = 0; i < 256; ++i) tok[i] = {(uint8_t)i};
+  // byte pairs that some token spans, one bit per (first << 8 | second): the
+  // junction of each merge (the pairs inside its operands are set already)
+  std::vector<uint32_t> join(kJoinWords, 0u);
   for (size_t r = 0; r < n_merges; ++r) {
     const uint32_t a = merges[2 * r], bb = merges[2 * r + 1];
     if (a >= 256 + r || bb >= 256 + r) return TOK_E_BADMERGES;
@@ -194,6 +197,8 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
     if ((a | bb) < 256) pr[(a << 8) | bb] = (uint32_t)r;
     tmin[2 * (size_t)bb] = std::min(tmin[2 * (size_t)bb], (uint32_t)r);
     tmin[2 * (size_t)a + 1] = std::min(tmin[2 * (size_t)a + 1], (uint32_t)r);
+    const uint32_t jp = ((uint32_t)tok[a].back() << 8) | tok[bb].front();
+    join[jp >> 5] |= 1u << (jp & 31u);
     tok[256 + r] = tok[a];
     tok[256 + r].insert(tok[256 + r].end(), tok[bb].begin(), tok[bb].end());
   }
@@ -243,6 +248,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
         hipMalloc((void**)&ctx->d_pair_rank, pr.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_tok_len, ctx->tok_len.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_tok_min, tmin.size() * 4) != hipSuccess ||
+        hipMalloc((void**)&ctx->d_joinable, join.size() * 4) != hipSuccess ||
         hipHostMalloc((void**)&ctx->h_ctr, sizeof(Counters), hipHostMallocMapped) != hipSuccess) {
       rc = TOK_E_NOMEM;
       break;
@@ -252,6 +258,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
         hipMemcpy(ctx->d_tok_len, ctx->tok_len.data(), ctx->tok_len.size() * 4, hipMemcpyHostToDevice) !=
             hipSuccess ||
         hipMemcpy(ctx->d_tok_min, tmin.data(), tmin.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(ctx->d_joinable, join.data(), join.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipHostGetDevicePointer((void**)&ctx->d_ctr, ctx->h_ctr, 0) != hipSuccess)
       break;
     std::memset(ctx->h_ctr, 0, sizeof(Counters));

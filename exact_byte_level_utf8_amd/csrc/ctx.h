@@ -111,6 +111,7 @@ struct tok_ctx {
   uint32_t long_buckets = 0;
   uint32_t* d_tok_len = nullptr;
   uint2* d_tok_min = nullptr;
+  uint32_t* d_joinable = nullptr;  // kJoinWords: bit (a << 8 | b) set iff some token spans the byte pair a b
 
   // every token's bytes on the device, made on first use (device repair)
   uint8_t* d_tok_bytes = nullptr;
@@ -465,7 +466,9 @@ struct tok_ctx {
       launch_empty_batch(bb, doc_off, n_docs, out_off, s);
       return;
     }
-    launch_pretok(text, n, doc_off, n_docs, pattern, bb, s, e0(0), e1(0));
+    // the pre-tokenization alone (out_flags) gives piece starts; the pipeline
+    // also starts a unit of BPE between bytes that no token spans
+    launch_pretok(text, n, doc_off, n_docs, pattern, out_flags ? nullptr : d_joinable, bb, s, e0(0), e1(0));
     if (out_flags) return;
     launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s, e0(1), e1(1));
     launch_assemble(n, bb, out, spans, d_tok_len, out_cap, doc_off, n_docs, out_off, s, e0(2), e1(2));
@@ -583,6 +586,7 @@ struct tok_ctx {
     dfree(d_long_slots);
     dfree(d_tok_len);
     dfree(d_tok_min);
+    dfree(d_joinable);
     free_lit_tables();
     dfree(d_tok_bytes);
     dfree(d_tok_off);

@@ -10,7 +10,9 @@
 // thread, with NT = 512 threads for grids of up to 1024 tiles and 256 above),
 // so a wave touches 64 consecutive LDS entries at every step and a wave
 // ballot yields four flag words at once: bit i of word c is set iff byte
-// 16c + i starts a piece.
+// 16c + i starts a piece.  Ahead of the merge stage (a byte-pair table is
+// given) a bit is also set where no token spans the pair of the byte and the
+// one before it: BPE cannot join the two sides, so each merges on its own.
 //
 // The Llama-3 style needs three run aggregates whose runs may cross the tile
 // edge.  They are (reset, value) scan elements: one workgroup pass of wave
@@ -127,7 +129,7 @@ __device__ inline bool is_cont(uint32_t byte) { return (byte & 0xC0u) == 0x80u; 
 template <int PATTERN, int NT>
 __global__ void __launch_bounds__(NT, NT >= 512 ? 8 : 6)
 pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off,
-              uint32_t n_docs, Bufs B) {
+              uint32_t n_docs, const uint32_t* __restrict__ joinable, Bufs B) {
   constexpr int kRounds = kPT / NT;                    // tile positions per thread
   constexpr int kPer = kRounds;                        // consecutive positions per thread in the aggregate pass
   static_assert(kPer == 2 || kPer == 4, "aggregate states are packed as 2 or 4 bytes per thread");
@@ -446,7 +448,12 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     const bool rule = PATTERN == 0 ? piece_start_gpt2(c, p[0], p[1], p[2], p[3], n1)
                                    : piece_start_llama3(c, p[0], p[1], p[2], p[3], n1, agg & 3u, (agg >> 2) & 1u,
                                                         (agg >> 3) & 1u);
-    const bool st = (c & kILead) && rule;
+    bool st = (c & kILead) && rule;
+    if (joinable) {  // a unit of BPE also starts where no token spans the byte pair
+      const uint32_t g = (uint32_t)(k + kGuard) - 1u;
+      const uint32_t two = lds_word(s_raw32, g), out = lds_word(s_fl32, g);
+      if (!((out | (out >> 8)) & kBOut)) st = st || !pair_joinable(joinable, two & 0xFFu, (two >> 8) & 0xFFu);
+    }
     // this wave holds 64 consecutive positions: four flag words
     const uint64_t m = __ballot(st);
     const uint64_t p0 = (uint64_t)base + (uint64_t)j * NT + wv * kWave;
@@ -460,20 +467,24 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
 }  // namespace
 
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
-                   int pattern, Bufs b, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                   int pattern, const uint32_t* joinable, Bufs b, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const uint32_t tiles = (uint32_t)((n + kPretokTile - 1) / kPretokTile);
   if (!tiles) return;
   // up to one tile per workgroup slot of the device, 8 waves per tile; larger
   // inputs use 4-wave workgroups, which pack the CUs better
   const bool small = tiles <= (uint32_t)kPretokSmallGrid;
   if (pattern == 2) {  // the case-splitting family: segments between synchronizing cuts
-    launch_pretok_case(text, n, doc_off, n_docs, b, s, e0, e1);
+    launch_pretok_case(text, n, doc_off, n_docs, joinable, b, s, e0, e1);
   } else if (pattern == 0) {
-    if (small) launch_on(pretok_kernel<0, 512>, dim3(tiles), dim3(512), s, e0, e1, text, n, doc_off, n_docs, b);
-    else launch_on(pretok_kernel<0, 256>, dim3(tiles), dim3(256), s, e0, e1, text, n, doc_off, n_docs, b);
+    if (small)
+      launch_on(pretok_kernel<0, 512>, dim3(tiles), dim3(512), s, e0, e1, text, n, doc_off, n_docs, joinable, b);
+    else
+      launch_on(pretok_kernel<0, 256>, dim3(tiles), dim3(256), s, e0, e1, text, n, doc_off, n_docs, joinable, b);
   } else {
-    if (small) launch_on(pretok_kernel<1, 512>, dim3(tiles), dim3(512), s, e0, e1, text, n, doc_off, n_docs, b);
-    else launch_on(pretok_kernel<1, 256>, dim3(tiles), dim3(256), s, e0, e1, text, n, doc_off, n_docs, b);
+    if (small)
+      launch_on(pretok_kernel<1, 512>, dim3(tiles), dim3(512), s, e0, e1, text, n, doc_off, n_docs, joinable, b);
+    else
+      launch_on(pretok_kernel<1, 256>, dim3(tiles), dim3(256), s, e0, e1, text, n, doc_off, n_docs, joinable, b);
   }
 }
 

@@ -18,7 +18,8 @@
 // the one running into the tile from the last cut before it; a segment that
 // runs past the loaded window reads the text from global memory.  The
 // result is the same flag words as the other families' pre-tokenization:
-// bit i of word c set iff byte 16c + i starts a piece.
+// bit i of word c set iff byte 16c + i starts a piece, or, ahead of the
+// merge stage, a unit of BPE (no token spans the byte pair there).
 #include "tok_internal.h"
 #include "seg_rules.h"
 #include "wg_scan.h"
@@ -100,7 +101,7 @@ struct DevAcc {
 
 __global__ void __launch_bounds__(kCaseNT)
 pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off,
-                   uint32_t n_docs, Bufs B) {
+                   uint32_t n_docs, const uint32_t* __restrict__ joinable, Bufs B) {
   __shared__ uint8_t s_raw[kCaseWin + 4];
   __shared__ uint8_t s_ds[kCaseWin];        // a document starts at this byte
   __shared__ uint32_t s_q[kCaseWin];        // info per window byte
@@ -269,6 +270,13 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
       if ((int64_t)p >= t0 && ((s_cut[(p - t0) >> 5] >> ((p - t0) & 31)) & 1u)) break;
     }
   }
+  if (joinable) {  // a unit of BPE also starts where no token spans the byte pair
+    for (int64_t p = max(t0, (int64_t)1) + tid; p < t1; p += kCaseNT) {
+      const int i = (int)(p - lo);
+      if (!pair_joinable(joinable, s_raw[i - 1], s_raw[i]))
+        atomicOr(&s_start[(p - t0) >> 5], 1u << ((p - t0) & 31));
+    }
+  }
   __syncthreads();
   // flag words of the tile's chunks
   for (int c = tid; c < kCaseTile / kChunk; c += kCaseNT)
@@ -277,11 +285,11 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
 
 }  // namespace
 
-void launch_pretok_case(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, Bufs b,
-                        hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+void launch_pretok_case(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
+                        const uint32_t* joinable, Bufs b, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const uint32_t tiles = (uint32_t)((n + kCaseTile - 1) / kCaseTile);
   if (!tiles) return;
-  launch_on(pretok_case_kernel, dim3(tiles), dim3(kCaseNT), s, e0, e1, text, n, doc_off, n_docs, b);
+  launch_on(pretok_case_kernel, dim3(tiles), dim3(kCaseNT), s, e0, e1, text, n, doc_off, n_docs, joinable, b);
 }
 
 }  // namespace tok

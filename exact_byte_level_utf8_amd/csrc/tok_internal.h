@@ -38,6 +38,19 @@ constexpr int kPretokTile = 1024;    // bytes per workgroup of the pre-tokenizat
 constexpr int kPieceTile = 1024;     // bytes per workgroup of the piece pass
 constexpr uint32_t kPieceSmallGrid = 1024;  // piece-pass grids up to this use 512-thread workgroups
 constexpr uint32_t kNoRank = 0xFFFFFFFFu;
+constexpr int kJoinWords = 65536 / 32;  // byte-pair bits: some token spans the pair
+
+// Whether some token spans the byte pair (a, b).  A merge joins two tokens,
+// so a token that spans a byte boundary has the boundary's two bytes inside
+// it.  Where no token spans the pair, every token sequence BPE passes through
+// has a boundary there, the pair straddling it never has a rank, and the
+// rounds on each side are those of each side alone: BPE of the piece is the
+// BPE of the bytes before the boundary followed by that of the bytes from it.
+// So a piece splits there into units of BPE that merge independently.
+__device__ inline bool pair_joinable(const uint32_t* __restrict__ joinable, uint32_t a, uint32_t b) {
+  const uint32_t k = (a << 8) | b;
+  return (joinable[k >> 5] >> (k & 31u)) & 1u;
+}
 constexpr uint64_t kEmptySlot = ~0ull;
 constexpr uint32_t kBucket = 4;      // hash-table slots probed with one set of loads
 
@@ -158,12 +171,16 @@ inline void launch_on(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
 // Kernel launchers (defined in the .hip files); e0 / e1: optional events
 // around the stage's kernel.
 void launch_empty_batch(Bufs b, const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s);
+// joinable: nullptr for piece starts only; else the byte-pair bits (bit
+// a << 8 | b set iff some token spans the pair a b), and a flag also marks
+// every byte whose pair with the byte before it no token spans.
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
-                   int pattern, Bufs b, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+                   int pattern, const uint32_t* joinable, Bufs b, hipStream_t s, hipEvent_t e0 = nullptr,
+                   hipEvent_t e1 = nullptr);
 // The case-splitting family's pre-tokenization (k_pretok_case.hip), called by
 // launch_pretok for that pattern.
-void launch_pretok_case(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, Bufs b,
-                        hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+void launch_pretok_case(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
+                        const uint32_t* joinable, Bufs b, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, const uint64_t* doc_off,
                    uint32_t n_docs, uint64_t* out_off, hipStream_t s, hipEvent_t e0 = nullptr,
                    hipEvent_t e1 = nullptr);

@@ -1,7 +1,8 @@
 """GPU parity on CJK-dense text, where every ideograph run is one letter
 piece of up to 6,000 bytes (TokTier, Table 9 reports CJK corpora apart;
-GraphTok, section 6.2: long pre-tokens).  These pieces take the long-piece
-merge path.
+GraphTok, section 6.2: long pre-tokens).  The pipeline cuts them into units
+of BPE where no token spans the byte pair; the units over 64 bytes take the
+long-piece merge path.
 
 The oracle's textbook BPE is quadratic in a piece's length, so whole texts
 are compared element by element at sizes it finishes in seconds (runs still
@@ -86,3 +87,17 @@ def test_cjk_workload_sampled_pieces(cfg, name):
     for i, want in zip(pick, wants):
         a, z = np.searchsorted(sp, [starts[i], starts[i + 1]])
         same(f"piece {i} ({plen[i]} bytes at {starts[i]})", ids[a:z], want)
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_cjk_split_is_the_pattern_alone(cfg, name):
+    """The pipeline cuts long ideograph runs into units of BPE where no token
+    spans the byte pair; the pre-tokenization entry point still returns the
+    pattern's pieces alone."""
+    t, o, _ = cfg[name]
+    b = textgen.cjk_text(13, 200_000).encode()
+    d = torch.frombuffer(bytearray(b), dtype=torch.uint8).cuda()
+    flags = torch.zeros((len(b) + 15) // 16 + 8, dtype=torch.int16, device="cuda")
+    t.pretokenize_dev(d, flags)
+    torch.cuda.synchronize()
+    same("pieces", tk.flags_to_starts(flags.cpu().numpy().view(np.uint16), len(b)), o.pieces(b))
