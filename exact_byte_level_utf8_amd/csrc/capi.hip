@@ -163,11 +163,13 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
   if (pattern != TOK_PAT_GPT2 && pattern != TOK_PAT_LLAMA3 && pattern != TOK_PAT_O200K) return TOK_E_PATTERN;
   if (n_merges > TOK_MAX_MERGES) return TOK_E_BADMERGES;
   // operands precede their merge, and each ordered pair has one rank
-  // open addressing over buckets of kBucket slots, at most half full; a key
-  // lives in the first bucket of its probe sequence with a free slot, taking
-  // the bucket's first free slot (lookups stop at a bucket with a free slot)
+  // open addressing over buckets of kBucket slots, at most half full (denser
+  // tables send more lookups of absent pairs on to a second bucket, and the
+  // merge rounds wait on those loads); a key lives in the first bucket of its
+  // probe sequence with a free slot, taking the bucket's first free slot
+  // (lookups stop at a bucket with a free slot)
   const uint64_t slots = std::max<uint64_t>(next_pow2(2 * n_merges), 1024);
-  const uint32_t bmask = (uint32_t)(slots / kBucket - 1);
+  const uint32_t nbk = (uint32_t)(slots / kBucket);
   std::vector<uint64_t> mtab(slots, kEmptySlot);
   std::vector<uint32_t> pr(65536, kNoRank);
   // per token: lowest rank of a merge taking it as right operand (x), as
@@ -182,8 +184,8 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
     const uint32_t a = merges[2 * r], bb = merges[2 * r + 1];
     if (a >= 256 + r || bb >= 256 + r) return TOK_E_BADMERGES;
     const uint64_t key = ((uint64_t)a << 20) | bb;
-    uint32_t h = merge_hash(a, bb) & bmask;
-    for (bool placed = false; !placed; h = (h + 1) & bmask) {
+    uint32_t h = merge_bucket(a, bb, nbk);
+    for (bool placed = false; !placed; h = next_bucket(h, nbk)) {
       for (uint32_t j = 0; j < kBucket && !placed; ++j) {
         uint64_t& slot = mtab[(size_t)h * kBucket + j];
         if (slot == kEmptySlot) {
@@ -202,6 +204,16 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
     tok[256 + r] = tok[a];
     tok[256 + r].insert(tok[256 + r].end(), tok[bb].begin(), tok[bb].end());
   }
+  // the same ranks, 16 bits each in one word per token: the rank shifted
+  // right so that every rank fits below 0xFFFF (which stands for none).  A
+  // floor only makes the shelter test stricter, so merging stays exact.
+  uint32_t min_shift = 0;
+  while (n_merges && ((uint64_t)(n_merges - 1) >> min_shift) >= 0xFFFFu) ++min_shift;
+  std::vector<uint32_t> tmin16(256 + n_merges);
+  for (size_t t = 0; t < tmin16.size(); ++t) {
+    auto q = [&](uint32_t r) { return r == kNoRank ? 0xFFFFu : r >> min_shift; };
+    tmin16[t] = (q(tmin[2 * t]) << 16) | q(tmin[2 * t + 1]);
+  }
   tok_ctx* ctx = new (std::nothrow) tok_ctx();
   if (!ctx) return TOK_E_NOMEM;
   ctx->device = device;
@@ -210,6 +222,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
   ctx->repair_doublings = o.repair_doublings;
   ctx->repair_margin = o.repair_margin;
   ctx->n_merges = (uint32_t)n_merges;
+  ctx->min_shift = min_shift;
   ctx->tok_len.resize(tok.size());
   ctx->tok_off.resize(tok.size() + 1);
   ctx->tok_off[0] = 0;
@@ -247,7 +260,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
     if (hipMalloc((void**)&ctx->d_merge_slots, slots * 8) != hipSuccess ||
         hipMalloc((void**)&ctx->d_pair_rank, pr.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_tok_len, ctx->tok_len.size() * 4) != hipSuccess ||
-        hipMalloc((void**)&ctx->d_tok_min, tmin.size() * 4) != hipSuccess ||
+        hipMalloc((void**)&ctx->d_tok_min, tmin16.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_joinable, join.size() * 4) != hipSuccess ||
         hipHostMalloc((void**)&ctx->h_ctr, sizeof(Counters), hipHostMallocMapped) != hipSuccess) {
       rc = TOK_E_NOMEM;
@@ -257,7 +270,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
         hipMemcpy(ctx->d_pair_rank, pr.data(), pr.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(ctx->d_tok_len, ctx->tok_len.data(), ctx->tok_len.size() * 4, hipMemcpyHostToDevice) !=
             hipSuccess ||
-        hipMemcpy(ctx->d_tok_min, tmin.data(), tmin.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(ctx->d_tok_min, tmin16.data(), tmin16.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(ctx->d_joinable, join.data(), join.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipHostGetDevicePointer((void**)&ctx->d_ctr, ctx->h_ctr, 0) != hipSuccess)
       break;
@@ -266,7 +279,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
     // per device (a failed lookup only disables that entry point)
     (void)noalloc_scratch(device);
     ctx->b.ctr = ctx->d_ctr;
-    ctx->merge_buckets = bmask;
+    ctx->merge_buckets = nbk;
     rc = build_word_table(ctx, tok);
     if (rc == TOK_OK && o.initial_bytes) rc = ctx->ensure(o.initial_bytes);
   } while (false);

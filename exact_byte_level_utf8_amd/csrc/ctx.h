@@ -110,7 +110,8 @@ struct tok_ctx {
   uint64_t* d_long_slots = nullptr;
   uint32_t long_buckets = 0;
   uint32_t* d_tok_len = nullptr;
-  uint2* d_tok_min = nullptr;
+  uint32_t* d_tok_min = nullptr;  // per token: (x >> min_shift) << 16 | (y >> min_shift), see Tables
+  uint32_t min_shift = 0;
   uint32_t* d_joinable = nullptr;  // kJoinWords: bit (a << 8 | b) set iff some token spans the byte pair a b
 
   // every token's bytes on the device, made on first use (device repair)
@@ -183,6 +184,7 @@ struct tok_ctx {
     t.long_buckets = words ? long_buckets : 0;
     t.tok_len = d_tok_len;
     t.tok_min = d_tok_min;
+    t.min_shift = min_shift;
     return t;
   }
 

@@ -71,13 +71,13 @@ __device__ inline uint32_t bucket_rank(ulonglong2 s01, ulonglong2 s23, uint32_t 
 // bucket without the key goes on to the next ones.
 __device__ inline uint32_t merge_rank(const Tables& T, uint32_t a, uint32_t b) {
   const uint32_t khi = (a << 12) | (b >> 8), klo = b & 0xFFu;
-  uint32_t h = merge_hash(a, b) & T.merge_buckets;
+  uint32_t h = merge_bucket(a, b, T.merge_buckets);
   const ulonglong2* bk = reinterpret_cast<const ulonglong2*>(T.merge_slots + (size_t)h * kBucket);
   const ulonglong2 s01 = bk[0], s23 = bk[1];
   uint32_t r = bucket_rank(s01, s23, khi, klo);
   if (r == kNoRank && s23.y != kEmptySlot) {  // slots fill in order within a bucket
-    for (uint32_t probe = 1; probe <= T.merge_buckets; ++probe) {
-      h = (h + 1) & T.merge_buckets;
+    for (uint32_t probe = 1; probe < T.merge_buckets; ++probe) {
+      h = next_bucket(h, T.merge_buckets);
       bk = reinterpret_cast<const ulonglong2*>(T.merge_slots + (size_t)h * kBucket);
       const ulonglong2 t01 = bk[0], t23 = bk[1];
       r = bucket_rank(t01, t23, khi, klo);
@@ -242,9 +242,10 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
   uint32_t rk = k + 1 < cur ? T.pair_rank[(sym << 8) | nx] : kNoRank;
   // held across the rounds (the empty asm keeps the compiler from reloading
   // it from the kernel arguments in every round)
-  const uint2* __restrict__ tok_min = T.tok_min;
+  const uint32_t* __restrict__ tok_min = T.tok_min;
   __asm__ volatile("" : "+s"(tok_min));
-  const uint2 m0 = tok_min[sym];
+  const uint32_t min_shift = T.min_shift;
+  const uint2 m0 = token_mins(tok_min, min_shift, sym);
   uint32_t ml = m0.x, mr = m0.y;
   for (;;) {
     if (k + 1 >= cur) rk = kNoRank;
@@ -284,7 +285,7 @@ __device__ void merge_rows(const Tables& T, const uint8_t* p, uint32_t len, bool
     const uint32_t nsym = chose ? 256u + rk : sym;
     uint32_t nml = ml, nmr = mr;
     if (chose) {
-      const uint2 m = tok_min[nsym];
+      const uint2 m = token_mins(tok_min, min_shift, nsym);
       nml = m.x;
       nmr = m.y;
     }
@@ -384,6 +385,8 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   constexpr int kListWords = kCapA + kCapB + kCapC + kCapD + kCapH + kCap1 + kCapPS + kCapPL;
   constexpr int kLongE = NT == 512 ? 2 : 3;                // long-piece symbols per thread and chunk
   constexpr int kLongSyms = NT == 512 ? 2048 : NT * kLongE;  // long-piece symbols held in LDS (whole chunks)
+  constexpr int kWaveSyms = kLongSyms / (NT / kWave);        // a wave's share of them (256 or 192)
+  static_assert(kWaveSyms % (kWave * kLongE) == 0, "a wave's share is whole chunks");
   constexpr int kPoolWords = kListWords > 4 * kLongSyms ? kListWords : 4 * kLongSyms;
   __shared__ __attribute__((aligned(16))) uint8_t s_text[kTextLds];
   __shared__ uint16_t s_flags[kFlagLds];
@@ -400,13 +403,18 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   uint32_t* const s_probe_l = s_probe_s + kCapPS;
   __shared__ uint32_t s_list2[kCap2];
   __shared__ uint32_t s_cnt[kChunksPerWg], s_excl[kChunksPerWg];
-  __shared__ uint32_t s_n[9], s_next, s_first, s_doc0, s_lend;
+  __shared__ uint32_t s_n[9], s_next, s_next2, s_nbig, s_first, s_doc0;
+  __shared__ uint32_t s_big[kCap2], s_biglen[kCap2];  // long pieces set aside for the whole workgroup
   __shared__ uint32_t s_lscan[NT / kWave];
   __shared__ uint32_t s_lat[kCap2];  // phase 3: run position of each long piece
 
   const uint32_t tid = threadIdx.x, lane = tid & 63u;
   if (tid < 9) s_n[tid] = 0;
-  if (tid == 0) s_next = 0;
+  if (tid == 0) {
+    s_next = 0;
+    s_next2 = 0;
+    s_nbig = 0;
+  }
   const uint32_t tile = blockIdx.x;
   const uint64_t base = (uint64_t)tile * kPieceTile;
   const uint64_t c0 = (uint64_t)tile * kChunksPerWg;
@@ -438,7 +446,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
     s_flags[k] = c < n_chunks ? B.flags[c] : 0;
   }
   // the merge and byte-pair tables into this XCD's L2 while phase 1 runs
-  const uint32_t warm = touch_lines<NT>(T.merge_slots, (uint64_t)(T.merge_buckets + 1) * kBucket * 8, 2) ^
+  const uint32_t warm = touch_lines<NT>(T.merge_slots, (uint64_t)T.merge_buckets * kBucket * 8, 2) ^
                         touch_lines<NT>(T.pair_rank, 256u * 256u * 4u, 1);
   __syncthreads();
 
@@ -564,32 +572,60 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   }
   __syncthreads();
 
-  // phase 2b: every piece over 64 bytes, merged by the whole workgroup in
-  // turn (uniform loop: the rounds hold barriers).  Its symbols go to the LDS
-  // pool when they fit, else to the workspace at the piece's bytes; its
-  // tokens end in ws_sym[start ..] and its count in the chunk total, with a
-  // count byte of 0 marking it for phase 3.
-  for (uint32_t k = 0; k < n2; ++k) {
-    const uint32_t off = s_list2[k];
-    const uint64_t s = base + off;
-    if (tid < (uint32_t)kWave) {
-      const uint64_t e = next_start(B.flags, n, s);
-      if (tid == 0) s_lend = (uint32_t)(e - s);
+  // phase 2b: every piece over 64 bytes.  Its tokens end in ws_sym[start ..]
+  // and its count in the chunk total (a long piece is its chunk's last), with
+  // a count byte of 0 marking it for phase 3.  First the waves take the
+  // pieces in turn, each merging one that fits its share of the LDS pool
+  // (kWaveSyms symbols) with wave scans, all waves at once; a longer piece is
+  // set aside, and those are then merged by the whole workgroup one after
+  // another (uniform loop: the rounds hold barriers), in the pool when they
+  // fit it, else in the workspace at the piece's bytes.
+  if (n2) {  // uniform
+    uint32_t* const s_wpool = s_pool + (tid / kWave) * (4u * kWaveSyms);  // this wave's share
+    for (;;) {
+      // every lane adds 1, so a grab moves the counter by 64
+      const uint32_t k = __builtin_amdgcn_readfirstlane(atomicAdd(&s_next2, 1u)) / (uint32_t)kWave;
+      if (k >= n2) break;
+      const uint32_t off = s_list2[k];
+      const uint64_t s = base + off;
+      const uint32_t len = __builtin_amdgcn_readfirstlane((uint32_t)(next_start(B.flags, n, s) - s));
+      if (len > (uint32_t)kWaveSyms) {
+        if (lane == 0) {
+          const uint32_t j = atomicAdd(&s_nbig, 1u);
+          s_big[j] = k;
+          s_biglen[j] = len;
+        }
+        continue;
+      }
+      const uint32_t cnt = longp::long_piece<longp::WaveGroup, kLongE>(
+          text, s, len, T, s_wpool, s_wpool + kWaveSyms, reinterpret_cast<uint2*>(s_wpool + 2 * kWaveSyms),
+          B.ws_sym + s, nullptr);
+      if (lane == 0) {
+        s_cnt8[off] = 0;
+        atomicAdd(&s_cnt[off / kChunk], cnt);
+      }
     }
-    __syncthreads();
-    const uint32_t len = __builtin_amdgcn_readfirstlane(s_lend);
-    uint32_t cnt;
-    if (len <= (uint32_t)kLongSyms)
-      cnt = longp::long_piece<NT, kLongE>(text, s, len, T, s_pool, s_pool + kLongSyms,
-                                          reinterpret_cast<uint2*>(s_pool + 2 * kLongSyms), B.ws_sym + s, s_lscan);
-    else
-      cnt = longp::long_piece<NT, kLongE>(text, s, len, T, B.ws_sym + s, B.ws_rk + s,
-                                          reinterpret_cast<uint2*>(B.ws_sel + s), B.ws_sym + s, s_lscan);
-    if (tid == 0) {
-      s_cnt8[off] = 0;
-      s_cnt[off / kChunk] += cnt;
+    __syncthreads();  // the pool is free, and the set-aside list complete
+    const uint32_t nbig = __builtin_amdgcn_readfirstlane(s_nbig);
+    for (uint32_t j = 0; j < nbig; ++j) {
+      const uint32_t off = s_list2[s_big[j]];
+      const uint64_t s = base + off;
+      const uint32_t len = __builtin_amdgcn_readfirstlane(s_biglen[j]);
+      uint32_t cnt;
+      if (len <= (uint32_t)kLongSyms)
+        cnt = longp::long_piece<longp::WgGroup<NT>, kLongE>(text, s, len, T, s_pool, s_pool + kLongSyms,
+                                                            reinterpret_cast<uint2*>(s_pool + 2 * kLongSyms),
+                                                            B.ws_sym + s, s_lscan);
+      else
+        cnt = longp::long_piece<longp::WgGroup<NT>, kLongE>(text, s, len, T, B.ws_sym + s, B.ws_rk + s,
+                                                            reinterpret_cast<uint2*>(B.ws_sel + s), B.ws_sym + s,
+                                                            s_lscan);
+      if (tid == 0) {
+        s_cnt8[off] = 0;
+        s_cnt[off / kChunk] += cnt;
+      }
+      __syncthreads();  // the pool is reused by the next piece
     }
-    __syncthreads();  // the pool and s_lend are reused by the next piece
   }
 
   // phase 3: the tile's tokens as one run from its first piece start (the

@@ -110,10 +110,6 @@ __device__ inline bool inside_literal(const RepairArgs& A, uint64_t b) {
   return false;
 }
 
-struct MaxOp {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
-};
-
 // Stored record whose first byte is `off`, as its distance r from the
 // session's end (st_off[r] falls as r grows), or -1.
 __device__ inline int32_t find_stored(const uint32_t* st_off, uint32_t n_st, uint64_t off) {

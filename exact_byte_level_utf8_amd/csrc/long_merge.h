@@ -20,8 +20,11 @@
 // occurrences).
 //
 // The piece's symbols live in sym / rk / mm, in LDS or in global memory; the
-// round processes them in chunks of NT * E symbols, E consecutive symbols
-// per thread, with carries from chunk to chunk.
+// round processes them in chunks of G::kSize * E symbols, E consecutive
+// symbols per thread, with carries from chunk to chunk.  G is the group of
+// threads that merges the piece: the whole workgroup (WgGroup), or one wave
+// (WaveGroup), so that the waves of a workgroup merge several pieces at
+// once with wave scans and no workgroup barrier.
 #pragma once
 
 #include "tok_internal.h"
@@ -36,19 +39,47 @@ constexpr uint32_t kChosen = 0x40000000u;  // marks a chosen pair's rank within 
 __device__ inline uint32_t rank_of(uint32_t v) { return v == kNoRank ? kNoRank : (v & ~kChosen); }
 __device__ inline bool chosen_bit(uint32_t v) { return (v >> 30) == 1u; }
 
-struct MinOp {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+
+// The whole workgroup of NT threads: workgroup scans and barriers.
+template <int NT>
+struct WgGroup {
+  static constexpr uint32_t kSize = NT;
+  static constexpr bool kScanSyncs = true;  // a scan holds barriers
+  __device__ static uint32_t rank() { return threadIdx.x; }
+  __device__ static void sync() { __syncthreads(); }
+  template <typename Op>
+  __device__ static uint32_t excl_scan(uint32_t v, uint32_t id, Op op, uint32_t* scratch, uint32_t* total) {
+    return wg_excl_scan<NT>(v, id, op, scratch, total);
+  }
 };
-struct MaxOp {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+
+// One wave: DPP scans; a wave's LDS accesses take effect in issue order, so
+// a wavefront fence (which keeps the compiler from moving memory accesses
+// across it) stands in for the barrier.
+struct WaveGroup {
+  static constexpr uint32_t kSize = kWave;
+  static constexpr bool kScanSyncs = false;
+  __device__ static uint32_t rank() { return lane_id(); }
+  __device__ static void sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+  template <typename Op>
+  __device__ static uint32_t excl_scan(uint32_t v, uint32_t id, Op op, uint32_t*, uint32_t* total) {
+    const uint32_t incl = wave_incl_scan(v, op, id);
+    // lane i - 1 across the whole wave (wave_shr:1); lane 0 takes the identity
+    const uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)incl, 0x138, 0xF, 0xF, false);
+    if (total) *total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+    return lane_id() == 0 ? id : prev;
+  }
 };
 
 // Rank of the merge (a, b), or kNoRank: open addressing over buckets of
 // kBucket slots (left << 44 | right << 24 | rank).
 __device__ inline uint32_t long_merge_rank(const Tables& T, uint32_t a, uint32_t b) {
   const uint32_t khi = (a << 12) | (b >> 8), klo = b & 0xFFu;
-  uint32_t h = merge_hash(a, b) & T.merge_buckets;
-  for (uint32_t probe = 0; probe <= T.merge_buckets; ++probe) {
+  uint32_t h = merge_bucket(a, b, T.merge_buckets);
+  for (uint32_t probe = 0; probe < T.merge_buckets; ++probe) {
     const ulonglong2* bk = reinterpret_cast<const ulonglong2*>(T.merge_slots + (size_t)h * kBucket);
     const ulonglong2 s01 = bk[0], s23 = bk[1];
     const uint64_t v[4] = {s01.x, s01.y, s23.x, s23.y};
@@ -58,7 +89,7 @@ __device__ inline uint32_t long_merge_rank(const Tables& T, uint32_t a, uint32_t
       if (hi == khi && (lo >> 24) == klo) return lo & 0xFFFFFFu;
     }
     if (s23.y == kEmptySlot) return kNoRank;  // slots fill in order within a bucket
-    h = (h + 1) & T.merge_buckets;
+    h = next_bucket(h, T.merge_buckets);
   }
   return kNoRank;
 }
@@ -90,11 +121,11 @@ __device__ inline bool sheltered(const uint32_t* rk, const uint2* mm, uint32_t n
 // uniform arguments.  sym[i]: token i; rk[i]: rank of the pair (i, i + 1)
 // (kNoRank for the last); mm[i]: the token's lowest ranks as right operand
 // (x) and as left operand (y).
-template <int NT, int E>
+template <typename G, int E>
 __device__ __forceinline__ uint32_t merge_piece(const Tables& T, uint32_t* sym, uint32_t* rk, uint2* mm,
                                                 uint32_t n, uint32_t low, uint32_t* s_scan) {
-  constexpr uint32_t kCap = NT * E;  // symbols per chunk
-  const uint32_t tid = threadIdx.x;
+  constexpr uint32_t kCap = G::kSize * E;  // symbols per chunk
+  const uint32_t tid = G::rank();
   while (low != kNoRank) {  // uniform
     // pass A: which pairs merge; mark the chosen ones in rk
     uint32_t rs_carry = 0;  // 1 + the last pair before this chunk that does not merge (0: none)
@@ -114,7 +145,7 @@ __device__ __forceinline__ uint32_t merge_piece(const Tables& T, uint32_t* sym, 
         }
       }
       uint32_t total = 0;
-      const uint32_t before = MaxOp()(rs_carry, wg_excl_scan<NT>(last_stop, 0u, MaxOp(), s_scan, &total));
+      const uint32_t before = MaxOp()(rs_carry, G::excl_scan(last_stop, 0u, MaxOp(), s_scan, &total));
       uint32_t rs = before;  // run start of this thread's first pair
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -125,7 +156,7 @@ __device__ __forceinline__ uint32_t merge_piece(const Tables& T, uint32_t* sym, 
         }
       }
       rs_carry = __builtin_amdgcn_readfirstlane(MaxOp()(rs_carry, total));
-      __syncthreads();  // marks visible before the next chunk's walks
+      G::sync();  // marks visible before the next chunk's walks
     }
     // pass B: compaction, chunk by chunk in place (a symbol only moves down);
     // pairs next to a merge are probed again
@@ -151,7 +182,7 @@ __device__ __forceinline__ uint32_t merge_piece(const Tables& T, uint32_t* sym, 
           alive[e] = !pc;
           if (alive[e]) {
             ns[e] = ch ? 256u + rank_of(v) : sym[i];
-            nm[e] = ch ? T.tok_min[ns[e]] : mm[i];
+            nm[e] = ch ? token_mins(T.tok_min, T.min_shift, ns[e]) : mm[i];
             const uint32_t kn = ch ? i + 2 : i + 1;
             nr[e] = kNoRank;
             if (kn < n) {
@@ -166,12 +197,12 @@ __device__ __forceinline__ uint32_t merge_piece(const Tables& T, uint32_t* sym, 
         }
       }
       uint32_t chunk_chosen = 0;
-      const uint32_t before = wg_excl_scan<NT>(mine, 0u, AddOp(), s_scan, &chunk_chosen);
+      const uint32_t before = G::excl_scan(mine, 0u, AddOp(), s_scan, &chunk_chosen);
       // the last pair of this chunk, for the next chunk's first symbol (read
       // before any write of this chunk: the scan above holds barriers)
       const uint32_t last = min(c0 + kCap, n) - 1;
       const bool last_chosen = last + 1 < n && chosen_bit(rk[last]);
-      __syncthreads();
+      G::sync();
       // symbol i moves to i less the chosen pairs before it; a symbol absorbed
       // by the pair before it is not written (its index is its partner's)
       uint32_t q = i0 - removed - before;
@@ -188,40 +219,42 @@ __device__ __forceinline__ uint32_t merge_piece(const Tables& T, uint32_t* sym, 
       }
       removed = __builtin_amdgcn_readfirstlane(removed + chunk_chosen);
       prev_chosen = __builtin_amdgcn_readfirstlane((uint32_t)last_chosen) != 0u;
-      __syncthreads();
+      G::sync();
     }
     n -= removed;
     uint32_t all = 0;
-    (void)wg_excl_scan<NT>(new_low, kNoRank, MinOp(), s_scan, &all);
+    (void)G::excl_scan(new_low, kNoRank, MinOp(), s_scan, &all);
     low = __builtin_amdgcn_readfirstlane(all);
   }
   return n;
 }
 
 
-// BPE of the long piece text[s .. s + len) by the workgroup: its bytes become
+// BPE of the long piece text[s .. s + len) by the group G: its bytes become
 // the symbols in sym / rk / mm, the rounds run, and its tokens are left in
 // out[0 ..] (the global workspace at the piece's bytes; when the arrays are
 // that workspace already, nothing moves).  Returns the token count.  Called
-// by every thread with uniform arguments.
-template <int NT, int E>
+// by every thread of the group with uniform arguments.
+template <typename G, int E>
 __device__ __forceinline__ uint32_t long_piece(const uint8_t* __restrict__ text, uint64_t s, uint32_t len,
                                                const Tables& T, uint32_t* sym, uint32_t* rk, uint2* mm,
                                                uint32_t* out, uint32_t* s_scan) {
-  const uint32_t tid = threadIdx.x;
+  constexpr uint32_t NT = G::kSize;
+  const uint32_t tid = G::rank();
   uint32_t low = kNoRank;
   for (uint32_t i = tid; i < len; i += NT) {
     const uint32_t a = text[s + i];
     sym[i] = a;
     const uint32_t r = i + 1 < len ? T.pair_rank[(a << 8) | text[s + i + 1]] : kNoRank;
     rk[i] = r;
-    mm[i] = T.tok_min[a];
+    mm[i] = token_mins(T.tok_min, T.min_shift, a);
     low = min(low, r);
   }
   uint32_t all = 0;
-  (void)wg_excl_scan<NT>(low, kNoRank, MinOp(), s_scan, &all);  // its barriers order the stores above
+  if (!G::kScanSyncs) G::sync();  // the stores above before any read of them
+  (void)G::excl_scan(low, kNoRank, MinOp(), s_scan, &all);
   const uint32_t cnt = __builtin_amdgcn_readfirstlane(
-      merge_piece<NT, E>(T, sym, rk, mm, len, __builtin_amdgcn_readfirstlane(all), s_scan));
+      merge_piece<G, E>(T, sym, rk, mm, len, __builtin_amdgcn_readfirstlane(all), s_scan));
   if (sym != out)
     for (uint32_t i = tid; i < cnt; i += NT) out[i] = sym[i];
   return cnt;

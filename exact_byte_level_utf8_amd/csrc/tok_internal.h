@@ -99,14 +99,16 @@ constexpr uint32_t kSum2Shift = 12;  // tiles per sum2 group: 4096
 // Read-only device tables built by tok_load.
 struct Tables {
   const uint64_t* merge_slots;  // (left << 44 | right << 24 | rank), kEmptySlot = empty
-  uint32_t merge_buckets;       // buckets - 1 (power of two), kBucket slots each
+  uint32_t merge_buckets;       // buckets, kBucket slots each (at most half the slots hold a merge)
   const uint32_t* pair_rank;    // [256 * 256] rank of byte pair (a, b), or kNoRank
   const uint64_t* word_slots;   // 2 x uint64 per slot, see word_hash()
   uint32_t word_buckets;        // buckets - 1; word_slots == nullptr disables the table
   const uint64_t* long_slots;   // 4 x uint64 per slot, see long_hash()
   uint32_t long_buckets;        // buckets - 1; long_slots == nullptr disables the table
   const uint32_t* tok_len;      // bytes of each token ID
-  const uint2* tok_min;         // per token: lowest rank of a merge taking it as right operand (x), as left (y)
+  const uint32_t* tok_min;      // per token: lowest rank of a merge taking it as right operand (x), as left (y),
+                                // 16 bits each (x high), shifted right by min_shift; 0xFFFF: none
+  uint32_t min_shift;
 };
 
 // Per-call device buffers.
@@ -125,12 +127,28 @@ struct Bufs {
   const uint32_t* n_docs_dev;  // if set, the document count, read on the device (overrides n_docs)
 };
 
-// Bucket of the merge pair (left, right): multiplicative hashing of the
+// A token's lowest ranks as right operand (x) and as left operand (y), or
+// kNoRank: from the packed table, floored to a multiple of 2^shift.  A floor
+// never exceeds the rank, so a test "lowest rank > r" that passes on it
+// passes on the rank too.
+__device__ inline uint2 token_mins(const uint32_t* __restrict__ tok_min, uint32_t shift, uint32_t t) {
+  const uint32_t v = tok_min[t], x = v >> 16, y = v & 0xFFFFu;
+  return make_uint2(x == 0xFFFFu ? kNoRank : x << shift, y == 0xFFFFu ? kNoRank : y << shift);
+}
+
+// Hash of the merge pair (left, right): multiplicative hashing of the
 // 40-bit key, high bits.
 __host__ __device__ inline uint32_t merge_hash(uint32_t left, uint32_t right) {
   const uint64_t key = ((uint64_t)left << 20) | right;
   return (uint32_t)((key * 0x9E3779B97F4A7C15ull) >> 32);
 }
+
+// First bucket of the pair among nb buckets (the hash scaled to [0, nb), so
+// nb need not be a power of two), and the bucket probed after h.
+__host__ __device__ inline uint32_t merge_bucket(uint32_t left, uint32_t right, uint32_t nb) {
+  return (uint32_t)(((uint64_t)merge_hash(left, right) * nb) >> 32);
+}
+__host__ __device__ inline uint32_t next_bucket(uint32_t h, uint32_t nb) { return h + 1 == nb ? 0u : h + 1; }
 
 // Whole-piece key of a byte string of 2..13 bytes: a = bytes 0..7 (little
 // endian, zero padded), b = bytes 8..12 | len << 40.  A stored slot adds the

@@ -105,5 +105,11 @@ __device__ inline uint32_t wg_excl_suffix(uint32_t v, uint32_t id, Op op, uint32
 struct AddOp {
   __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; }
 };
+struct MinOp {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+};
+struct MaxOp {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
 
 }  // namespace tok

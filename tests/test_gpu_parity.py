@@ -132,6 +132,27 @@ def test_workload_parity(cfg, name, gen, seed, n_chars):
 
 
 @pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_high_id_vocabulary_strings(cfg, name):
+    """Text made of the latest merges' strings (IDs from 33,024 on), each a
+    piece of its own: whole-piece table hits for nearly all of them, beside
+    pieces that are not vocabulary strings (the newlines between), must come
+    out as the oracle encodes them."""
+    t, o, tokb = cfg[name]
+    def utf8(x):
+        try:
+            x.decode("utf-8")
+            return True
+        except UnicodeDecodeError:
+            return False
+
+    picks = [x for i, x in enumerate(tokb) if i >= 256 + 32768 and 2 <= len(x) <= 28 and utf8(x)]
+    whole = [x for x in picks if o.pieces(x) == [0]]
+    assert len(whole) > 1000
+    b = b"\n".join(whole)
+    _check(name, t.encode(b), o.encode(b), b, tokb)
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
 def test_adversarial_parity(cfg, name):
     t, o, tokb = cfg[name]
     for s in adversarial_texts():
