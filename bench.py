@@ -56,6 +56,8 @@ METRIC = "ms per 1M-char request encode (input MB/s) + % HBM roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 
 CHAT_MARKERS = ["<|im_start|>", "<|im_end|>", "<|endoftext|>", "<|tool_call|>", "<|im_sep|>"]
+# operators and indentation of code text: dense matches that overlap one another
+CODE_LITERALS = ["==", "===", "!=", "!==", "=>", "->", "::", "  ", "    ", "\n    ", "\n        ", "();"]
 
 WORKLOADS = {
     # name: (description, merges, pattern, generator, seed, chars per request, documents)
@@ -78,11 +80,15 @@ WORKLOADS = {
     # chat transcript with added-token markers taken ahead of the pattern (tok_set_added_tokens)
     "chat_1m": ("1M-char chat transcript with 5 added-token markers, GPT-2-style pattern, 50K merges",
                 "gpt2_50k", "gpt2", "chat", 7, 1_000_000, 1),
+    # code text with dense, overlapping added-token literals (the selection's cluster path)
+    "code_lit_1m": ("1M-char code/JSON request with 12 overlapping operator and indentation literals, GPT-2-style "
+                    "pattern, 50K merges", "gpt2_50k", "gpt2", "codelit", 11, 1_000_000, 1),
     # append repair: stored 1M-char context + 1,400-char appends (a latency)
     "repair": ("tok_repair: 1M-char stored context + 1,400-char append, GPT-2-style pattern, 50K merges",
                "gpt2_50k", "gpt2", "mix", 2, 1_000_000, 1),
 }
-EXTRA = ["tiny_10k", "llama3_3m", "batch64", "cjk_1m", "chat_1m", "o200k_1m", "cjk_o200k_1m", "repair"]
+EXTRA = ["tiny_10k", "llama3_3m", "batch64", "cjk_1m", "chat_1m", "code_lit_1m", "o200k_1m", "cjk_o200k_1m",
+         "repair"]
 
 # dominant-stage kernel and the sources its code comes from (for matching
 # committed counter summaries to the kernel that produced them)
@@ -111,6 +117,8 @@ def gen_request(job) -> bytes:
         return textgen.chat_text(seed, n_chars, CHAT_MARKERS).encode()
     if kind == "cjk":
         return textgen.cjk_text(seed, n_chars).encode()
+    if kind == "codelit":
+        return textgen.tool_text(seed, n_chars).encode()
     return textgen.mix_text(seed, n_chars).encode()
 
 
@@ -527,8 +535,9 @@ def main() -> int:
         merges = vocab.merges(merges_name)
         tok = tokenizer(merges_name, pattern)
         literals = None
-        if kind == "chat":
-            literals = [(m.encode(), 256 + len(merges) + i) for i, m in enumerate(CHAT_MARKERS)]
+        if kind in ("chat", "codelit"):
+            strings = CHAT_MARKERS if kind == "chat" else CODE_LITERALS
+            literals = [(m.encode(), 256 + len(merges) + i) for i, m in enumerate(strings)]
         tok.set_added_tokens(literals or [])
         r = {"workload": desc, "merges": merges_name, "pattern": pattern, "seed": seed}
         if w == "repair":

@@ -29,7 +29,7 @@ struct LitBufs {
   uint32_t* tile_cnt;   // candidates found in each tile
   uint64_t* sel;        // taken literals, in order
   uint64_t* cut;        // parts + 1 cut points: document boundaries, literal starts and ends, merged
-  int32_t* part_lit;    // per part: the taken literal it is, or -1
+  int32_t* part_lit;    // per part: the ID of the taken literal it is, or -1
   uint32_t* doc_part;   // per document boundary: its index among the cut points
   uint64_t* out_off;    // the parts' output offsets from the pipeline
   uint32_t* fin;        // final output offset of each part (and the total)

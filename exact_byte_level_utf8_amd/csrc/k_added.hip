@@ -10,15 +10,19 @@
 //                      256-bit first-byte mask in LDS rejects most bytes at
 //                      once; candidates of two or more bytes are grouped by
 //                      their first two bytes, longest first, and compared a
-//                      word at a time); each tile writes its matches in
+//                      word at a time).  The cursor scan of the definition
+//                      keeps each match that starts at or after the end of
+//                      the last one kept; each tile resolves that for its own
+//                      matches (clusters of overlapping matches, one thread
+//                      each, decided exactly from the matches of the 256
+//                      bytes before the tile) and writes the kept ones in
 //                      position order.
-//   lit_select_kernel  one workgroup: the matches of all tiles in order; when
-//                      no match overlaps the next one every match is taken,
-//                      else one lane keeps, in order, each match that starts at
-//                      or after the end of the last one kept (the cursor scan
-//                      of the definition, over the matches only).  The taken
-//                      literals cut the text into 2k + 1 parts: segment,
-//                      literal, segment, ..., segment.
+//   lit_select_kernel  one workgroup: the kept matches of all tiles in order
+//                      (a tile whose first cluster began too far back lists
+//                      all its matches, and then the cursor scan runs here
+//                      over the whole list).  The taken literals cut the
+//                      text into 2k + 1 parts: segment, literal, segment,
+//                      ..., segment.
 // The parts then run through the usual pipeline as documents (their count
 // read on the device, so the host enqueues everything without waiting),
 // which are hard boundaries for code points, pieces and merges, exactly as
@@ -39,7 +43,14 @@ namespace {
 constexpr uint32_t kMatchThreads = 256;  // 4 consecutive positions per thread
 constexpr uint32_t kSelThreads = 1024;
 constexpr uint32_t kScatterThreads = 256;
-constexpr uint32_t kInsPer = 4;  // parts per thread in one pass of the insertion
+constexpr uint32_t kInsPer = 6;  // parts per thread in one pass of the insertion (48 KiB of LDS)
+constexpr uint32_t kLitBack = 256;        // bytes before its tile whose matches the match kernel also finds
+constexpr uint32_t kTileRaw = 1u << 31;   // tile count flag: every match of the tile listed, unresolved
+constexpr uint8_t kMarkHead = 1, kMarkKept = 2;
+// marks of the selection in the literal half of a match word
+constexpr uint64_t kSelKeep = 1ull << 31, kSelHead = 1ull << 30;
+constexpr uint32_t kSelIndex = kLitMaxCount - 1;  // the literal index bits
+static_assert((kLitMaxCount & (kLitMaxCount - 1)) == 0 && kLitMaxCount <= (1u << 30), "index bits below the marks");
 
 __device__ inline uint32_t lit_len(const Literals& L, uint32_t li) { return L.off[li + 1] - L.off[li]; }
 
@@ -89,54 +100,145 @@ __device__ inline int32_t literal_at(const uint32_t* s_text, uint32_t q, uint32_
 __global__ void __launch_bounds__(kMatchThreads)
 lit_match_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off, uint32_t n_docs,
                  Literals L, LitBufs lb) {
-  // the tile's bytes, the longest literal's reach past it, and a guard word
-  constexpr uint32_t kWords = (kLitTile + kLitMax + 8) / 4;
+  // the window: kLitBack bytes before the tile, the tile, the longest
+  // literal's reach past it, and a guard word; at most one match per position
+  constexpr uint32_t kWords = (kLitBack + kLitTile + kLitMax + 8) / 4;
+  constexpr uint32_t kList = kLitBack + kLitTile;
+  constexpr uint32_t kPer = (kList + kMatchThreads - 1) / kMatchThreads;
+  static_assert(kLitBack == kMatchThreads && kLitTile == 4 * kMatchThreads, "one window-front and four tile positions per thread");
+  static_assert(kLitBack >= 2 * kLitMax, "the front of the window decides the cluster heads of the tile's matches");
   __shared__ uint32_t s_text[kWords];
   __shared__ uint32_t s_first[8];
   __shared__ uint32_t s_scan[kMatchThreads / kWave];
+  __shared__ uint32_t s_pos[kList];  // each match's start and end, counted from the window's first byte
+  __shared__ uint32_t s_end[kList];
+  __shared__ uint16_t s_lit[kList];
+  __shared__ uint8_t s_mark[kList];  // kMarkHead, kMarkKept
+  __shared__ uint32_t s_first_exact, s_raw;
   const uint32_t tile = blockIdx.x, tid = threadIdx.x;
   const uint64_t base = (uint64_t)tile * kLitTile;
+  const int64_t w0 = (int64_t)base - (int64_t)kLitBack;  // the window's first byte (before the text for tile 0)
   {
     const bool aligned = (reinterpret_cast<uintptr_t>(text) & 3u) == 0;
     for (uint32_t w = tid; w < kWords; w += kMatchThreads) {
-      const uint64_t p = base + 4u * w;
+      const int64_t p = w0 + 4 * (int64_t)w;
       uint32_t v = 0;
-      if (aligned && p + 4 <= n) {
+      if (aligned && p >= 0 && p + 4 <= (int64_t)n) {
         v = *reinterpret_cast<const uint32_t*>(text + p);
       } else {
         for (uint32_t i = 0; i < 4; ++i)
-          if (p + i < n) v |= (uint32_t)text[p + i] << (8 * i);
+          if (p + i >= 0 && p + i < (int64_t)n) v |= (uint32_t)text[p + i] << (8 * i);
       }
       s_text[w] = v;
     }
     if (tid < 8) s_first[tid] = L.first[tid];
   }
   __syncthreads();
-  const uint64_t p0 = base + 4u * tid;
-  const uint32_t cur = s_text[tid];
+  // the longest literal at window-front position tid and at tile positions
+  // 4 tid .. 4 tid + 3
+  auto match = [&](uint32_t q) -> int32_t {  // q: window byte
+    const int64_t p = w0 + (int64_t)q;
+    if (p < 0 || p >= (int64_t)n) return -1;
+    const uint32_t b0 = (s_text[q >> 2] >> (8 * (q & 3u))) & 0xFFu;
+    if (!((s_first[b0 >> 5] >> (b0 & 31u)) & 1u)) return -1;
+    return literal_at(s_text, q, b0, n, (uint64_t)p, L, doc_off, n_docs);
+  };
+  const int32_t mf = match(tid);
   int32_t m[4];
   uint32_t c = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t b0 = (cur >> (8 * j)) & 0xFFu;
-    const bool cand = p0 + j < n && ((s_first[b0 >> 5] >> (b0 & 31u)) & 1u);
-    m[j] = cand ? literal_at(s_text, 4u * tid + j, b0, n, p0 + j, L, doc_off, n_docs) : -1;
+    m[j] = match(kLitBack + 4u * tid + j);
     c += m[j] >= 0 ? 1u : 0u;
   }
+  uint32_t nf = 0, nt = 0;
+  const uint32_t af = wg_excl_scan<kMatchThreads>(mf >= 0 ? 1u : 0u, 0u, AddOp(), s_scan, &nf);
+  const uint32_t at0 = nf + wg_excl_scan<kMatchThreads>(c, 0u, AddOp(), s_scan, &nt);
+  auto put = [&](uint32_t i, uint32_t q, int32_t li) {
+    s_pos[i] = q;
+    s_end[i] = q + lit_len(L, (uint32_t)li);
+    s_lit[i] = (uint16_t)li;
+    s_mark[i] = 0;
+  };
+  if (mf >= 0) put(af, tid, mf);
+  {
+    uint32_t i = at0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (m[j] >= 0) put(i++, kLitBack + 4u * tid + j, m[j]);
+  }
+  __syncthreads();
+  // Cluster heads: a match that no earlier match reaches (the cursor keeps it
+  // whatever came before; the selection kernel describes the clusters).  A
+  // match before the window reaches at most kLitMax - 1 bytes into it, so a
+  // head decided at a window byte from kLitMax on is exact.
+  const uint32_t nl = nf + nt;
+  const uint32_t i0 = min(nl, tid * kPer), i1 = min(nl, i0 + kPer);
+  uint32_t mx = 0;
+  for (uint32_t i = i0; i < i1; ++i) mx = max(mx, s_end[i]);
+  uint32_t reach = wg_excl_scan<kMatchThreads>(mx, 0u, MaxOp(), s_scan, nullptr);
+  for (uint32_t i = i0; i < i1; ++i) {
+    if (reach <= s_pos[i]) s_mark[i] = kMarkHead;
+    reach = max(reach, s_end[i]);
+  }
+  if (tid == 0) {
+    s_raw = 0;
+    s_first_exact = nl;
+  }
+  __syncthreads();
+  // the head that governs the tile's first match: resolved when it is exact
+  if (tid == 0 && nt > 0) {
+    uint32_t g = nf;
+    while (g > 0 && !(s_mark[g] & kMarkHead)) --g;
+    const bool exact = (s_mark[g] & kMarkHead) && s_pos[g] >= kLitMax;
+    s_raw = exact ? 0u : 1u;
+    s_first_exact = g;
+  }
+  __syncthreads();
+  // every cluster from the governing head on, one thread per head, in order
+  const uint32_t g = s_first_exact;
+  for (uint32_t h = max(i0, g); h < i1; ++h) {
+    if (!(s_mark[h] & kMarkHead)) continue;
+    uint32_t end = 0, j = h;
+    do {
+      if (s_pos[j] >= end) {
+        s_mark[j] |= kMarkKept;
+        end = s_end[j];
+      }
+      ++j;
+    } while (j < nl && !(s_mark[j] & kMarkHead));
+  }
+  __syncthreads();
+  // the tile's matches in order: only the kept ones once resolved, else all
+  // of them (the selection kernel then resolves them with the rest)
+  const bool raw = s_raw != 0;
+  uint32_t keep[4], k = 0;
+  {
+    uint32_t i = at0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      keep[j] = 0;
+      if (m[j] >= 0) {
+        keep[j] = raw || (s_mark[i] & kMarkKept) ? 1u : 0u;
+        ++i;
+      }
+      k += keep[j];
+    }
+  }
   uint32_t tot = 0;
-  uint32_t at = wg_excl_scan<kMatchThreads>(c, 0u, AddOp(), s_scan, &tot);
+  uint32_t at = wg_excl_scan<kMatchThreads>(k, 0u, AddOp(), s_scan, &tot);
   uint64_t* out = lb.cand + (uint64_t)tile * kLitTile;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    if (m[j] >= 0) out[at++] = ((p0 + j) << 32) | (uint32_t)m[j];
-  if (tid == 0) lb.tile_cnt[tile] = tot;
+    if (keep[j]) out[at++] = ((base + 4u * tid + j) << 32) | (uint32_t)m[j];
+  if (tid == 0) lb.tile_cnt[tile] = tot | (raw ? kTileRaw : 0u);
 }
 
 __global__ void __launch_bounds__(kSelThreads)
 lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_off, uint32_t n_docs, Literals L,
                   LitBufs lb, Counters* ctr, uint64_t gen) {
   __shared__ uint32_t s_scan[kSelThreads / kWave];
-  __shared__ uint32_t s_over, s_kept, s_bad;
+  __shared__ uint32_t s_over, s_bad;
   const uint32_t tid = threadIdx.x;
   if (tid == 0) {
     s_over = 0;
@@ -152,43 +254,95 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
   // matches before each tile, and each tile's matches copied after them in
   // the same pass (uniform trip count: the scan holds barriers)
   uint32_t carry = 0;
+  bool raw = false;  // a tile listed all its matches, unresolved
   for (uint32_t t0 = 0; t0 < tiles; t0 += kSelThreads) {
     const uint32_t t = t0 + tid;
-    const uint32_t v = t < tiles ? lb.tile_cnt[t] : 0u;
+    const uint32_t w = t < tiles ? lb.tile_cnt[t] : 0u, v = w & ~kTileRaw;
+    raw |= (w & kTileRaw) != 0;
     uint32_t tot = 0;
     const uint32_t b = carry + wg_excl_scan<kSelThreads>(v, 0u, AddOp(), s_scan, &tot);
-    for (uint32_t j = 0; j < v; ++j) lb.sel[b + j] = lb.cand[(uint64_t)t * kLitTile + j];
+    const uint64_t* src = lb.cand + (uint64_t)t * kLitTile;
+    for (uint32_t j = 0; j < v; j += 4) {  // four loads in flight before the stores
+      uint64_t x[4];
+#pragma unroll
+      for (uint32_t u = 0; u < 4; ++u) x[u] = j + u < v ? src[j + u] : 0ull;
+#pragma unroll
+      for (uint32_t u = 0; u < 4; ++u)
+        if (j + u < v) lb.sel[b + j + u] = x[u];
+    }
     carry += tot;
   }
+  if (raw) s_over = 1u;  // (a possible overlap: checked below)
   if (bad) s_bad = 1u;
   const uint32_t K = carry;
   __syncthreads();
-  bool over = false;
-  for (uint32_t i = tid; i + 1 < K; i += kSelThreads) {
-    const uint64_t a = lb.sel[i], b = lb.sel[i + 1];
-    over |= (a >> 32) + lit_len(L, (uint32_t)a) > (b >> 32);
+  // Tiles resolve their own clusters (lit_match_kernel), so the list holds
+  // only taken matches, which never overlap, unless a tile was left
+  // unresolved: then the cursor scan runs here over the whole list.
+  if (s_over) {  // uniform: some tile was left unresolved; do its matches overlap?
+    __syncthreads();
+    if (tid == 0) s_over = 0;
+    __syncthreads();
+    bool over = false;
+    for (uint32_t i = tid; i + 1 < K; i += kSelThreads) {
+      const uint64_t a = lb.sel[i], b = lb.sel[i + 1];
+      over |= (a >> 32) + lit_len(L, (uint32_t)a) > (b >> 32);
+    }
+    if (over) s_over = 1u;
+    __syncthreads();
   }
-  if (over) s_over = 1u;
-  __syncthreads();
   // malformed offsets: report, and fall back to one part with no literal
   // (the call fails; everything below stays in bounds)
   const bool bad_docs = s_bad != 0;
   uint32_t k = bad_docs ? 0u : K;
   if (!bad_docs && s_over) {  // uniform: LDS words read after a barrier
-    if (tid == 0) {
-      uint64_t end = 0;
-      uint32_t w = 0;
-      for (uint32_t i = 0; i < K; ++i) {
-        const uint64_t a = lb.sel[i];
-        if ((a >> 32) >= end) {
-          lb.sel[w++] = a;
-          end = (a >> 32) + lit_len(L, (uint32_t)a);
+    // The cursor keeps a match iff it starts at or after the end of the last
+    // match kept.  Where no earlier match reaches the next one's start (the
+    // running maximum of the ends, a scan), the last kept match has ended
+    // too, so that match is kept whatever came before: the matches split
+    // there into clusters that are resolved independently, one thread
+    // walking each in order.  Marks go into the literal half of the words
+    // (indexes stay below kLitMaxCount); then the kept matches move down in
+    // order.  Positions fit 32 bits (inputs are under 2^32 bytes).
+    uint32_t reach = 0;  // the largest end before this chunk
+    for (uint32_t c0 = 0; c0 < K; c0 += kSelThreads) {  // uniform trip count: the scan holds barriers
+      const uint32_t i = c0 + tid;
+      const uint64_t a = i < K ? lb.sel[i] : 0ull;
+      const uint32_t S = (uint32_t)(a >> 32), E = S + lit_len(L, (uint32_t)a & kSelIndex);
+      uint32_t tot = 0;
+      const uint32_t before = max(reach, wg_excl_scan<kSelThreads>(i < K ? E : 0u, 0u, MaxOp(), s_scan, &tot));
+      if (i < K && (i == 0 || before <= S)) lb.sel[i] = a | kSelHead;
+      reach = max(reach, tot);
+    }
+    __syncthreads();  // every cluster head marked
+    for (uint32_t h = tid; h < K; h += kSelThreads) {
+      if (!(lb.sel[h] & kSelHead)) continue;
+      uint32_t end = 0, j = h;
+      do {
+        const uint64_t a = lb.sel[j];
+        const uint32_t S = (uint32_t)(a >> 32);
+        if (S >= end) {
+          lb.sel[j] = a | kSelKeep;
+          end = S + lit_len(L, (uint32_t)a & kSelIndex);
         }
-      }
-      s_kept = w;
+        ++j;
+      } while (j < K && !(lb.sel[j] & kSelHead));
+    }
+    __syncthreads();  // every kept match marked
+    uint32_t kept = 0;
+    for (uint32_t c0 = 0; c0 < K; c0 += kSelThreads) {
+      const uint32_t i = c0 + tid;
+      const uint64_t a = i < K ? lb.sel[i] : 0ull;
+      const uint32_t keep = (a & kSelKeep) ? 1u : 0u;
+      uint32_t tot = 0;
+      // the scan's barriers put every read of this chunk before any write; a
+      // match only moves down, and later chunks are read after
+      const uint32_t at = kept + wg_excl_scan<kSelThreads>(keep, 0u, AddOp(), s_scan, &tot);
+      if (keep) lb.sel[at] = a & ~(kSelHead | kSelKeep);
+      kept += tot;
     }
     __syncthreads();
-    k = s_kept;
+    k = kept;
   }
   // cut points: the document boundaries merged with each literal's start and
   // end.  A boundary comes before a literal starting on it and after a
@@ -201,9 +355,24 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
   const uint32_t parts = nb + 2 * k;
   for (uint32_t i = tid; i < parts; i += kSelThreads) lb.part_lit[i] = -1;
   __syncthreads();
-  for (uint32_t j = tid; j < k; j += kSelThreads) {
-    const uint64_t a = lb.sel[j];
-    const uint64_t S = a >> 32, E = S + lit_len(L, (uint32_t)a);
+  for (uint32_t j0 = tid; j0 < k; j0 += 4 * kSelThreads) {
+    uint64_t a4[4];  // four literals per pass, their loads in flight together
+    uint32_t len4[4];
+    int32_t id4[4];
+#pragma unroll
+    for (uint32_t u = 0; u < 4; ++u) a4[u] = j0 + u * kSelThreads < k ? lb.sel[j0 + u * kSelThreads] : 0ull;
+#pragma unroll
+    for (uint32_t u = 0; u < 4; ++u) {
+      const bool in = j0 + u * kSelThreads < k;
+      len4[u] = in ? lit_len(L, (uint32_t)a4[u]) : 0u;
+      id4[u] = in ? L.ids[(uint32_t)a4[u]] : -1;
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < 4; ++u) {
+    const uint32_t j = j0 + u * kSelThreads;
+    if (j >= k) break;
+    const uint64_t a = a4[u];
+    const uint64_t S = a >> 32, E = S + len4[u];
     uint32_t lo = 0, hi = nb + 1;  // #{d : D(d) <= S}
     while (lo < hi) {
       const uint32_t mid = (lo + hi) >> 1;
@@ -221,7 +390,8 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
     const uint32_t ie = 2 * j + 1 + lo;
     lb.cut[is] = S;
     lb.cut[ie] = E;
-    lb.part_lit[is] = (int32_t)j;
+    lb.part_lit[is] = id4[u];  // the literal's ID (IDs are never negative)
+    }
   }
   for (uint32_t d = tid; d <= nb; d += kSelThreads) {
     const uint64_t x = Db(d);
@@ -252,19 +422,30 @@ __global__ void __launch_bounds__(kSelThreads)
 lit_insert_kernel(Literals L, LitBufs lb, int32_t* __restrict__ out, uint32_t* __restrict__ spans, uint64_t cap,
                   uint64_t* __restrict__ out_off, Counters* ctr, uint64_t gen) {
   __shared__ uint32_t s_scan[kSelThreads / kWave];
+  __shared__ int32_t s_plit[kSelThreads * kInsPer];     // a pass's part words: the literal ID, or -1
+  __shared__ uint32_t s_poff[kSelThreads * kInsPer + 1];  // and the pipeline's output offsets
   const uint32_t tid = threadIdx.x, parts = lb.misc[2], nb = lb.misc[3];
-  // kInsPer consecutive parts per thread, so that a pass covers 4,096 parts
-  // with all their loads in flight before the one scan
+  // kInsPer consecutive parts per thread, so that a pass covers 6,144 parts
+  // with one scan.  The pass's part words are read coalesced into LDS first
+  // and each thread then takes its own run of them.  The same pass writes,
+  // for the scatter, the part that holds pipeline token 256 b for every b
+  // (the parts tile the pipeline's tokens, so each b is written once; the
+  // candidate buffer is free by now and holds it).
+  uint32_t* blk = reinterpret_cast<uint32_t*>(lb.cand);
   uint32_t carry = 0;
   for (uint32_t i0 = 0; i0 < parts; i0 += kSelThreads * kInsPer) {
-    const uint32_t ib = i0 + tid * kInsPer;
-    int32_t lj[kInsPer];
+    for (uint32_t r = tid; r <= kSelThreads * kInsPer; r += kSelThreads) {
+      const uint32_t i = i0 + r;
+      if (r < kSelThreads * kInsPer) s_plit[r] = i < parts ? lb.part_lit[i] : -1;
+      s_poff[r] = i <= parts ? (uint32_t)lb.out_off[i] : 0u;
+    }
+    __syncthreads();
+    const uint32_t rb = tid * kInsPer, ib = i0 + rb;
     uint32_t v[kInsPer], sum = 0;
 #pragma unroll
     for (uint32_t j = 0; j < kInsPer; ++j) {
       const uint32_t i = ib + j;
-      lj[j] = i < parts ? lb.part_lit[i] : -1;
-      v[j] = i >= parts ? 0u : lj[j] >= 0 ? 1u : (uint32_t)(lb.out_off[i + 1] - lb.out_off[i]);
+      v[j] = i >= parts ? 0u : s_plit[rb + j] >= 0 ? 1u : s_poff[rb + j + 1] - s_poff[rb + j];
       sum += v[j];
     }
     uint32_t tot = 0;
@@ -274,26 +455,21 @@ lit_insert_kernel(Literals L, LitBufs lb, int32_t* __restrict__ out, uint32_t* _
       const uint32_t i = ib + j;
       if (i < parts) {
         lb.fin[i] = at;
-        if (lj[j] >= 0 && at < cap) {
-          out[at] = L.ids[(uint32_t)lb.sel[lj[j]]];
+        const int32_t id = s_plit[rb + j];
+        if (id >= 0 && at < cap) {
+          out[at] = id;
           if (spans) spans[at] = (uint32_t)lb.cut[i];  // the literal starts its part
         }
+        const uint32_t o0 = s_poff[rb + j], o1 = s_poff[rb + j + 1];
+        if (parts > 1)
+          for (uint32_t bk = (o0 + kScatterThreads - 1) / kScatterThreads; bk * kScatterThreads < o1; ++bk) blk[bk] = i;
       }
       at += v[j];
     }
     carry += tot;
+    __syncthreads();  // the LDS words are reloaded by the next pass
   }
   if (tid == 0) lb.fin[parts] = carry;
-  // for the scatter: the part holding pipeline token 256 b, for every b (the
-  // parts tile the tokens, so each b is written once); the candidate buffer is
-  // free by now and holds it
-  if (parts > 1) {
-    uint32_t* blk = reinterpret_cast<uint32_t*>(lb.cand);
-    for (uint32_t i = tid; i < parts; i += kSelThreads) {
-      const uint32_t o0 = (uint32_t)lb.out_off[i], o1 = (uint32_t)lb.out_off[i + 1];
-      for (uint32_t b = (o0 + kScatterThreads - 1) / kScatterThreads; b * kScatterThreads < o1; ++b) blk[b] = i;
-    }
-  }
   __syncthreads();
   // each document's output offset: that of its first part
   if (out_off)

@@ -119,6 +119,30 @@ def test_overlapping_literals(cfg):
             t.set_added_tokens([])
 
 
+# operators and indentation that code text holds everywhere, many of them
+# overlapping one another (the selection resolves clusters of overlaps)
+CODE_LITERALS = ["==", "===", "!=", "!==", "=>", "->", "::", "  ", "    ", "\n    ", "\n        ", "();"]
+
+
+@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+def test_dense_overlapping_literals_on_code(cfg, name):
+    t, o, v = cfg[name]
+    lits = lits_from(CODE_LITERALS, v)
+    b = textgen.tool_text(19, 1_000_000).encode()
+    t.set_added_tokens(lits)
+    try:
+        want = check(t, o, b, lits, name)
+        assert sum(1 for i in want if i >= v) > 20_000
+        docs = [textgen.tool_text(200 + i, 30_000 + 777 * i) for i in range(8)] + ["", "===", "a ===  b"]
+        data, off = textgen.pack_docs(docs)
+        ids, out_off = t.encode_batch(data, off)
+        want_ids, want_off = oracle_par.concat(oracle_par.map_docs(lambda d: o.encode_added(d.encode(), lits), docs))
+        same(f"{name} batch", ids, want_ids)
+        same(f"{name} batch offsets", out_off, want_off)
+    finally:
+        t.set_added_tokens([])
+
+
 def test_edges(cfg):
     t, o, v = cfg["llama3"]
     long_lit = "<|" + "x" * 60 + "|>"
