@@ -41,51 +41,13 @@
 #include "tok_internal.h"
 #include "bpe_util.h"
 #include "long_merge.h"
+#include "merge_table.h"
 #include "wg_scan.h"
 
 #pragma clang diagnostic ignored "-Wbitwise-instead-of-logical"
 
 namespace tok {
 namespace {
-
-// Rank held by one merge-table slot, or kNoRank.  A slot is left << 44 |
-// right << 24 | rank, so its high dword is left << 12 | right >> 8 (khi) and
-// the top byte of its low dword is right & 0xFF (klo); an empty slot (all
-// ones) never matches, since token IDs stay below 2^20 - 1 (TOK_MAX_MERGES)
-// and khi is then never all ones.
-__device__ inline uint32_t slot_rank(ulonglong2 two, int which, uint32_t khi, uint32_t klo) {
-  const uint64_t v = which ? two.y : two.x;
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  return hi == khi && (lo >> 24) == klo ? (lo & 0xFFFFFFu) : kNoRank;
-}
-
-__device__ inline uint32_t bucket_rank(ulonglong2 s01, ulonglong2 s23, uint32_t khi, uint32_t klo) {
-  return min(min(slot_rank(s01, 0, khi, klo), slot_rank(s01, 1, khi, klo)),
-             min(slot_rank(s23, 0, khi, klo), slot_rank(s23, 1, khi, klo)));
-}
-
-// Rank of the merge (a, b), or kNoRank, for a pair next to a merge: a or b is
-// a merged token (>= 256), so the byte-pair table never applies.  Open
-// addressing over buckets of kBucket slots, each read with two 16-byte loads;
-// the first bucket is compared without branches, and only a full first
-// bucket without the key goes on to the next ones.
-__device__ inline uint32_t merge_rank(const Tables& T, uint32_t a, uint32_t b) {
-  const uint32_t khi = (a << 12) | (b >> 8), klo = b & 0xFFu;
-  uint32_t h = merge_bucket(a, b, T.merge_buckets);
-  const ulonglong2* bk = reinterpret_cast<const ulonglong2*>(T.merge_slots + (size_t)h * kBucket);
-  const ulonglong2 s01 = bk[0], s23 = bk[1];
-  uint32_t r = bucket_rank(s01, s23, khi, klo);
-  if (r == kNoRank && s23.y != kEmptySlot) {  // slots fill in order within a bucket
-    for (uint32_t probe = 1; probe < T.merge_buckets; ++probe) {
-      h = next_bucket(h, T.merge_buckets);
-      bk = reinterpret_cast<const ulonglong2*>(T.merge_slots + (size_t)h * kBucket);
-      const ulonglong2 t01 = bk[0], t23 = bk[1];
-      r = bucket_rank(t01, t23, khi, klo);
-      if (r != kNoRank || t23.y == kEmptySlot) break;
-    }
-  }
-  return r;
-}
 
 // NW dwords holding the LDS bytes text[off .. off + 4 NW), read with NW + 1
 // aligned dword loads and byte funnel shifts; bytes at or past len are zero.
@@ -597,9 +559,15 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
         }
         continue;
       }
-      const uint32_t cnt = longp::long_piece<longp::WaveGroup, kLongE>(
-          text, s, len, T, s_wpool, s_wpool + kWaveSyms, reinterpret_cast<uint2*>(s_wpool + 2 * kWaveSyms),
-          B.ws_sym + s, nullptr);
+      // a round costs the wave the same whatever its active lanes: pieces of
+      // up to 128 symbols take two per lane, longer ones kLongE
+      uint32_t* const w_rk = s_wpool + kWaveSyms;
+      uint2* const w_mm = reinterpret_cast<uint2*>(s_wpool + 2 * kWaveSyms);
+      const uint32_t cnt =
+          kLongE > 2 && len <= 2u * kWave
+              ? longp::long_piece<longp::WaveGroup, 2>(text, s, len, T, s_wpool, w_rk, w_mm, B.ws_sym + s, nullptr)
+              : longp::long_piece<longp::WaveGroup, kLongE>(text, s, len, T, s_wpool, w_rk, w_mm, B.ws_sym + s,
+                                                            nullptr);
       if (lane == 0) {
         s_cnt8[off] = 0;
         atomicAdd(&s_cnt[off / kChunk], cnt);

@@ -28,6 +28,7 @@
 #pragma once
 
 #include "tok_internal.h"
+#include "merge_table.h"
 #include "wg_scan.h"
 
 namespace tok {
@@ -73,26 +74,6 @@ struct WaveGroup {
     return lane_id() == 0 ? id : prev;
   }
 };
-
-// Rank of the merge (a, b), or kNoRank: open addressing over buckets of
-// kBucket slots (left << 44 | right << 24 | rank).
-__device__ inline uint32_t long_merge_rank(const Tables& T, uint32_t a, uint32_t b) {
-  const uint32_t khi = (a << 12) | (b >> 8), klo = b & 0xFFu;
-  uint32_t h = merge_bucket(a, b, T.merge_buckets);
-  for (uint32_t probe = 0; probe < T.merge_buckets; ++probe) {
-    const ulonglong2* bk = reinterpret_cast<const ulonglong2*>(T.merge_slots + (size_t)h * kBucket);
-    const ulonglong2 s01 = bk[0], s23 = bk[1];
-    const uint64_t v[4] = {s01.x, s01.y, s23.x, s23.y};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = (uint32_t)v[j], hi = (uint32_t)(v[j] >> 32);
-      if (hi == khi && (lo >> 24) == klo) return lo & 0xFFFFFFu;
-    }
-    if (s23.y == kEmptySlot) return kNoRank;  // slots fill in order within a bucket
-    h = next_bucket(h, T.merge_buckets);
-  }
-  return kNoRank;
-}
 
 // Shelter walks of the pair k (symbols k, k + 1) of rank r among n symbols.
 __device__ inline bool sheltered(const uint32_t* rk, const uint2* mm, uint32_t n, uint32_t k, uint32_t r) {
@@ -188,7 +169,7 @@ __device__ __forceinline__ uint32_t merge_piece(const Tables& T, uint32_t* sym, 
             if (kn < n) {
               const uint32_t vn = rk[kn];
               const bool chn = chosen_bit(vn);
-              if (ch || chn) nr[e] = long_merge_rank(T, ns[e], chn ? 256u + rank_of(vn) : sym[kn]);
+              if (ch || chn) nr[e] = merge_rank(T, ns[e], chn ? 256u + rank_of(vn) : sym[kn]);
               else nr[e] = rank_of(v);
             }
           }
