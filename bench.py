@@ -94,8 +94,10 @@ EXTRA = ["tiny_10k", "llama3_3m", "batch64", "cjk_1m", "chat_1m", "code_lit_1m",
 # committed counter summaries to the kernel that produced them)
 CSRC = os.path.join(ROOT, "exact_byte_level_utf8_amd", "csrc")
 STAGE_KERNELS = {
-    "pretokenize": ("pretok_kernel", ["k_pretok.hip", "pretok_rules.h", "wg_scan.h", "tok_internal.h", "uniclass.inc"]),
-    "pieces": ("piece_kernel", ["k_bpe.hip", "bpe_util.h", "wg_scan.h", "tok_internal.h"]),
+    "pretokenize": ("pretok_kernel", ["k_pretok.hip", "pretok_rules.h", "wg_scan.h", "tok_internal.h", "uniclass.inc",
+                                      "k_pretok_case.hip", "seg_rules.h", "sync_rules.h", "uniclass_case.inc"]),
+    "pieces": ("piece_kernel", ["k_bpe.hip", "bpe_util.h", "long_merge.h", "merge_table.h", "wg_scan.h",
+                                "tok_internal.h"]),
     "assemble": ("assemble_kernel", ["k_assemble.hip", "wg_scan.h", "tok_internal.h"]),
 }
 
@@ -569,6 +571,8 @@ def main() -> int:
             k_ab = max(20, args.steps)
             r["graph_ab"] = leg.graph_ab(k_ab)
             r["span_export"] = leg.span_export(k_ab) if literals is None else None
+        elif literals is not None:  # the literal path: seven kernels per call, eager or one replayed graph
+            r["graph_ab"] = leg.graph_ab(20)
         # the oracle on a bounded sample of the same workload
         if not args.no_cpu_baseline:
             if w in pools:

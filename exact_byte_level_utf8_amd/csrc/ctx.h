@@ -72,9 +72,11 @@ struct GraphKey {
   uint64_t* out_off;
   hipStream_t s;
   bool words;
+  bool lits;  // the added-token literal pass ahead of the pipeline
   bool operator==(const GraphKey& o) const {
     return text == o.text && n == o.n && doc_off == o.doc_off && n_docs == o.n_docs && out == o.out &&
-           spans == o.spans && out_cap == o.out_cap && out_off == o.out_off && s == o.s && words == o.words;
+           spans == o.spans && out_cap == o.out_cap && out_off == o.out_off && s == o.s && words == o.words &&
+           lits == o.lits;
   }
 };
 
@@ -264,6 +266,7 @@ struct tok_ctx {
   }
 
   void free_lit_tables() {
+    drop_graphs();  // their launches carry these tables
     dfree(d_lit_bytes);
     dfree(d_lit_off);
     dfree(d_lit_ids);
@@ -281,6 +284,7 @@ struct tok_ctx {
   }
 
   void free_lit_bufs() {
+    drop_graphs();  // their launches point into these buffers
     dfree(lb.cand);
     dfree(lb.tile_cnt);
     dfree(lb.sel);
@@ -353,8 +357,22 @@ struct tok_ctx {
     int rc = ensure_lit_bufs(doc_off ? n_docs : 1);
     if (rc) return rc;
     volatile Counters* c = h_ctr;
-    const uint64_t call = ++gen;
-    enqueue_added(text, n, doc_off, n_docs, out, out_cap, out_off, s, call, spans);
+    uint64_t call = 0;
+    GraphEntry* g = nullptr;
+    if (graph_mode && !prof && n > 0)
+      g = graph_for(GraphKey{text, n, doc_off, n_docs, out, spans, out_cap, out_off, s, true, true});
+    if (g) {  // a replay reports the call number baked in at capture: clear its words first
+      call = g->gen;
+      c->err_utf8 = 0;
+      c->err_docs = 0;
+      c->done = 0;
+      c->lit_done = 0;
+      c->ins_done = 0;
+      HIP_OK(hipGraphLaunch(g->exec, s));
+    } else {
+      call = ++gen;
+      enqueue_added(text, n, doc_off, n_docs, out, out_cap, out_off, s, call, spans);
+    }
     HIP_OK(hipGetLastError());
     HIP_OK(hipStreamSynchronize(s));
     if (prof) {
@@ -498,7 +516,10 @@ struct tok_ctx {
     hipGraph_t gr = nullptr;
     hipGraphExec_t ex = nullptr;
     if (hipStreamBeginCapture(k.s, hipStreamCaptureModeThreadLocal) != hipSuccess) return nullptr;
-    enqueue(k.text, k.n, k.doc_off, k.n_docs, k.out, k.spans, k.out_cap, k.out_off, k.s, bb, k.words, nullptr);
+    if (k.lits)
+      enqueue_added(k.text, k.n, k.doc_off, k.n_docs, k.out, k.out_cap, k.out_off, k.s, bb.gen, k.spans);
+    else
+      enqueue(k.text, k.n, k.doc_off, k.n_docs, k.out, k.spans, k.out_cap, k.out_off, k.s, bb, k.words, nullptr);
     const bool captured = hipStreamEndCapture(k.s, &gr) == hipSuccess && gr;
     const bool made = captured && hipGraphInstantiate(&ex, gr, nullptr, nullptr, 0) == hipSuccess;
     if (gr) (void)hipGraphDestroy(gr);
@@ -528,7 +549,7 @@ struct tok_ctx {
     uint64_t call = 0;
     GraphEntry* g = nullptr;
     if (graph_mode && !prof && !out_flags && n > 0)
-      g = graph_for(GraphKey{text, n, doc_off, n_docs, out, spans, out_cap, out_off, s, words});
+      g = graph_for(GraphKey{text, n, doc_off, n_docs, out, spans, out_cap, out_off, s, words, false});
     if (g) {
       call = g->gen;
       c->err_utf8 = 0;

@@ -186,3 +186,59 @@ def test_repair_with_graphs_on(graph_on):
         old_b, full_b = old.encode(), (old + suf).encode()
         got, info = t.repair(o.encode(old_b), full_b, len(old_b))
         assert np.array_equal(got, o.encode(full_b)), info
+
+
+MARKERS = ["<|im_start|>", "<|im_end|>", "<|endoftext|>", "<|tool_call|>", "<|im_sep|>"]
+
+
+def test_literal_path_replay(graph_on):
+    """The literal pass and the pipeline after it captured as one graph: the
+    parts' count is read on the device, so replays with other texts of the
+    same length (other literal counts) match the oracle; a new literal set
+    drops the graphs, and batches replay too."""
+    t, o = graph_on["gpt2"]
+    v = t.info()["vocab_size"]
+    lits = [(m.encode(), v + i) for i, m in enumerate(MARKERS)]
+    t.set_added_tokens(lits)
+    try:
+        n = 120_000
+        d_text = torch.empty(n, dtype=torch.uint8, device="cuda")
+        d_ids = torch.empty(n, dtype=torch.int32, device="cuda")
+        counts = []
+        for rep in range(6):
+            b = textgen.chat_text(900 + rep, n, MARKERS).encode()[:n].decode("utf-8", "ignore").encode()
+            b = b + b" " * (n - len(b))
+            d_text.copy_(torch.frombuffer(bytearray(b), dtype=torch.uint8))
+            d_ids.fill_(-1)
+            k = t.encode_dev(d_text, d_ids)
+            counts.append(t.graph_count())
+            got = d_ids[:k].cpu().numpy()
+            torch.cuda.synchronize()
+            assert np.array_equal(got, o.encode_added(b, lits)), f"replay {rep}"
+        assert counts[0] == 0 and all(c == 1 for c in counts[1:]), counts
+        # a new literal set: no graph survives, and the next shape captures again
+        lits2 = lits + [(b"==", v + 7)]
+        t.set_added_tokens(lits2)
+        assert t.graph_count() == 0
+        for rep in range(3):
+            b = (textgen.tool_text(950 + rep, n).encode()[:n].decode("utf-8", "ignore").encode())
+            b = b + b" " * (n - len(b))
+            d_text.copy_(torch.frombuffer(bytearray(b), dtype=torch.uint8))
+            k = t.encode_dev(d_text, d_ids)
+            assert np.array_equal(d_ids[:k].cpu().numpy(), o.encode_added(b, lits2)), f"after reset {rep}"
+        assert t.graph_count() == 1
+        # a batch with literals
+        docs = [textgen.chat_text(960 + i, 9_000, MARKERS) for i in range(5)]
+        data, off = textgen.pack_docs(docs)
+        d_b = torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda()
+        d_doc = torch.from_numpy(off.astype(np.int64)).cuda().view(torch.uint64)
+        d_bid = torch.empty(len(data), dtype=torch.int32, device="cuda")
+        d_out = torch.empty(len(docs) + 1, dtype=torch.int64, device="cuda").view(torch.uint64)
+        want = [o.encode_added(d.encode(), lits2) for d in docs]
+        for rep in range(3):
+            k = t.encode_batch_dev(d_b, d_doc, d_bid, d_out)
+            assert np.array_equal(d_bid[:k].cpu().numpy(), np.concatenate(want)), f"batch {rep}"
+            offs = d_out.view(torch.int64).cpu().numpy()
+            assert np.array_equal(np.diff(offs), [len(w) for w in want]), f"batch offsets {rep}"
+    finally:
+        t.set_added_tokens([])
