@@ -452,7 +452,10 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
     if (joinable) {  // a unit of BPE also starts where no token spans the byte pair
       const uint32_t g = (uint32_t)(k + kGuard) - 1u;
       const uint32_t two = lds_word(s_raw32, g), out = lds_word(s_fl32, g);
-      if (!((out | (out >> 8)) & kBOut)) st = st || !pair_joinable(joinable, two & 0xFFu, (two >> 8) & 0xFFu);
+      // (ASCII pairs are left alone: a cut is never required, and byte-level
+      // vocabularies join nearly every ASCII pair)
+      if (!((out | (out >> 8)) & kBOut) && (two & 0x8080u))
+        st = st || !pair_joinable(joinable, two & 0xFFu, (two >> 8) & 0xFFu);
     }
     // this wave holds 64 consecutive positions: four flag words
     const uint64_t m = __ballot(st);

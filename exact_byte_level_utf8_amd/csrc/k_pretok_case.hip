@@ -273,7 +273,7 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
   if (joinable) {  // a unit of BPE also starts where no token spans the byte pair
     for (int64_t p = max(t0, (int64_t)1) + tid; p < t1; p += kCaseNT) {
       const int i = (int)(p - lo);
-      if (!pair_joinable(joinable, s_raw[i - 1], s_raw[i]))
+      if (((s_raw[i - 1] | s_raw[i]) & 0x80u) && !pair_joinable(joinable, s_raw[i - 1], s_raw[i]))
         atomicOr(&s_start[(p - t0) >> 5], 1u << ((p - t0) & 31));
     }
   }

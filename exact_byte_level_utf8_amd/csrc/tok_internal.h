@@ -127,13 +127,14 @@ struct Bufs {
   const uint32_t* n_docs_dev;  // if set, the document count, read on the device (overrides n_docs)
 };
 
-// A token's lowest ranks as right operand (x) and as left operand (y), or
-// kNoRank: from the packed table, floored to a multiple of 2^shift.  A floor
-// never exceeds the rank, so a test "lowest rank > r" that passes on it
-// passes on the rank too.
+// A token's lowest ranks as right operand (x) and as left operand (y), from
+// the packed table, floored to a multiple of 2^shift.  A floor never exceeds
+// the rank, so a test "lowest rank > r" that passes on it passes on the rank
+// too.  "None" (0xFFFF) comes out as 0xFFFF << shift, which the table's shift
+// keeps above every rank, so it needs no case of its own.
 __device__ inline uint2 token_mins(const uint32_t* __restrict__ tok_min, uint32_t shift, uint32_t t) {
-  const uint32_t v = tok_min[t], x = v >> 16, y = v & 0xFFFFu;
-  return make_uint2(x == 0xFFFFu ? kNoRank : x << shift, y == 0xFFFFu ? kNoRank : y << shift);
+  const uint32_t v = tok_min[t];
+  return make_uint2((v >> 16) << shift, (v & 0xFFFFu) << shift);
 }
 
 // Hash of the merge pair (left, right): multiplicative hashing of the
