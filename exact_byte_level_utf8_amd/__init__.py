@@ -47,10 +47,10 @@ class TokInfo(ctypes.Structure):
 
 
 class TokOpts(ctypes.Structure):
-    """tok_opts: load options (device, initial scratch, repair window, doublings, margin)."""
+    """tok_opts: load options (device, initial scratch, repair window, doublings, margin, hand-over wait)."""
     _fields_ = [("device", ctypes.c_int32), ("repair_window", ctypes.c_uint32),
                 ("initial_bytes", ctypes.c_uint64), ("repair_doublings", ctypes.c_uint32),
-                ("repair_margin", ctypes.c_uint32)]
+                ("repair_margin", ctypes.c_uint32), ("handoff_wait_us", ctypes.c_uint32)]
 
 
 def default_opts() -> TokOpts:

@@ -148,6 +148,7 @@ void tok_opts_default(tok_opts* opts) {
   opts->repair_window = 512;
   opts->repair_doublings = 5;
   opts->repair_margin = 8;
+  opts->handoff_wait_us = 1000000;
 }
 
 int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opts* opts, tok_ctx** out) {
@@ -157,7 +158,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
   tok_opts_default(&o);
   if (opts) o = *opts;
   if (o.device < 0 || o.repair_window < 1 || o.repair_window > (1u << 24) || o.repair_doublings > 24 ||
-      o.repair_margin > (1u << 20) || o.initial_bytes > TOK_MAX_BYTES)
+      o.repair_margin > (1u << 20) || o.initial_bytes > TOK_MAX_BYTES || o.handoff_wait_us > 10000000u)
     return TOK_E_ARG;
   const int device = o.device;
   if (pattern != TOK_PAT_GPT2 && pattern != TOK_PAT_LLAMA3 && pattern != TOK_PAT_O200K) return TOK_E_PATTERN;
@@ -262,6 +263,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
         hipMalloc((void**)&ctx->d_tok_len, ctx->tok_len.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_tok_min, tmin16.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_joinable, join.size() * 4) != hipSuccess ||
+        hipMalloc((void**)&ctx->d_hand_tick, 16) != hipSuccess ||
         hipHostMalloc((void**)&ctx->h_ctr, sizeof(Counters), hipHostMallocMapped) != hipSuccess) {
       rc = TOK_E_NOMEM;
       break;
@@ -272,8 +274,15 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
             hipSuccess ||
         hipMemcpy(ctx->d_tok_min, tmin16.data(), tmin16.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(ctx->d_joinable, join.data(), join.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemset(ctx->d_hand_tick, 0, 16) != hipSuccess ||
         hipHostGetDevicePointer((void**)&ctx->d_ctr, ctx->h_ctr, 0) != hipSuccess)
       break;
+    // the hand-over wait in wall-clock ticks (the clock's rate is in kHz)
+    int clock_khz = 0;
+    if (hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeWallClockRate, device) != hipSuccess || clock_khz <= 0)
+      break;
+    ctx->b.hand_tick = ctx->d_hand_tick;
+    ctx->b.hand_wait = (uint64_t)o.handoff_wait_us * (uint64_t)clock_khz / 1000u;
     std::memset(ctx->h_ctr, 0, sizeof(Counters));
     // the no-allocation entry point's array: its address on this device, once
     // per device (a failed lookup only disables that entry point)

@@ -115,6 +115,7 @@ struct tok_ctx {
   uint32_t* d_tok_min = nullptr;  // per token: (x >> min_shift) << 16 | (y >> min_shift), see Tables
   uint32_t min_shift = 0;
   uint32_t* d_joinable = nullptr;  // kJoinWords: bit (a << 8 | b) set iff some token spans the byte pair a b
+  uint64_t* d_hand_tick = nullptr;  // Bufs::hand_tick, for the context's life (never cleared after load)
 
   // every token's bytes on the device, made on first use (device repair)
   uint8_t* d_tok_bytes = nullptr;
@@ -201,6 +202,7 @@ struct tok_ctx {
     dfree(b.ws_sym);
     dfree(b.ws_rk);
     dfree(b.ws_sel);
+    dfree(b.hand_state);
     free_lit_bufs();
     dfree(d_text);
     dfree(d_ids);
@@ -226,7 +228,9 @@ struct tok_ctx {
         hipMalloc((void**)&b.ws_rk, (c + 64) * sizeof(uint32_t)) != hipSuccess ||
         hipMalloc((void**)&b.ws_sel, (c + 64) * sizeof(uint64_t)) != hipSuccess ||
         hipMalloc((void**)&b.sum1, ((tiles >> kSum1Shift) + 1) * sizeof(uint32_t)) != hipSuccess ||
-        hipMalloc((void**)&b.sum2, ((tiles >> kSum2Shift) + 1) * sizeof(uint32_t)) != hipSuccess) {
+        hipMalloc((void**)&b.sum2, ((tiles >> kSum2Shift) + 1) * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc((void**)&b.hand_state, (c / kPretokTile + 1) * sizeof(uint64_t)) != hipSuccess ||
+        hipMemsetAsync(b.hand_state, 0, (c / kPretokTile + 1) * sizeof(uint64_t), stream) != hipSuccess) {
       (void)hipGetLastError();
       free_scratch();
       return TOK_E_NOMEM;
@@ -237,7 +241,9 @@ struct tok_ctx {
   }
 
   // Fill every per-call device buffer with byte v and wait (a diagnostic:
-  // no call may depend on what an earlier one left in them).
+  // no call may depend on what an earlier one left in them).  The hand-over
+  // words of the case-splitting pre-tokenization are not per-call data: they
+  // carry the numbering of the calls, and are left as they are.
   int fill_scratch(uint8_t v) {
     auto fill = [&](void* p, uint64_t bytes) { return !p || hipMemsetAsync(p, v, bytes, stream) == hipSuccess; };
     bool ok = true;
@@ -610,6 +616,7 @@ struct tok_ctx {
     dfree(d_tok_len);
     dfree(d_tok_min);
     dfree(d_joinable);
+    dfree(d_hand_tick);
     free_lit_tables();
     dfree(d_tok_bytes);
     dfree(d_tok_off);

@@ -630,7 +630,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   // piece longer than 64 bytes is its chunk's last piece; its count is what
   // the chunk's total leaves, and its tokens are in the long-piece workspace.
   {
-    int32_t* run = B.staging + __builtin_amdgcn_readfirstlane(s_first);
+    int32_t* run = B.staging + (uint32_t)__builtin_amdgcn_readfirstlane(s_first);  // unsigned: the builtin is signed
     // this thread's piece starts, read again from LDS rather than kept live
     // across the merge phase (the empty asm keeps the compiler from reusing,
     // and so spilling, addresses computed before it)
@@ -670,7 +670,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
 
   if (n2) {  // uniform
     __syncthreads();
-    int32_t* run = B.staging + __builtin_amdgcn_readfirstlane(s_first);
+    int32_t* run = B.staging + (uint32_t)__builtin_amdgcn_readfirstlane(s_first);  // unsigned: the builtin is signed
     for (uint32_t m = 0; m < n2; ++m) {
       const uint32_t off = s_list2[m], at = s_lat[m];
       const uint32_t lc = off / kChunk, c = s_excl[lc] + s_cnt[lc] - at;  // the chunk's tokens from `at` on

@@ -10,16 +10,37 @@
 // Cuts fall at nearly every word edge, so the segments are short and all of
 // them are matched at once, one per thread.
 //
-// One workgroup per 1 KiB tile: the tile and 256 bytes on each side are
-// loaded into LDS and decoded (code point, letter-case class, CR/LF, space,
-// apostrophe, contraction letter, document start).  The tile's own bytes are
-// checked as well-formed UTF-8 (Unicode Table 3-7; no sequence may cross a
-// document boundary).  The segments that start in the tile are matched, plus
-// the one running into the tile from the last cut before it; a segment that
-// runs past the loaded window reads the text from global memory.  The
-// result is the same flag words as the other families' pre-tokenization:
-// bit i of word c set iff byte 16c + i starts a piece, or, ahead of the
-// merge stage, a unit of BPE (no token spans the byte pair there).
+// One workgroup per 1 KiB tile: the tile, 16 bytes before it and 240 after it
+// are loaded into LDS and decoded (code point, letter-case class, CR/LF,
+// space, apostrophe, contraction letter, document start).  The tile's own
+// bytes are checked as well-formed UTF-8 (Unicode Table 3-7; no sequence may
+// cross a document boundary).  The result is the same flag words as the
+// other families' pre-tokenization: bit i of word c set iff byte 16c + i
+// starts a piece, or, ahead of the merge stage, a unit of BPE (no token spans
+// the byte pair there).
+//
+// Long stretches without a cut (an ideograph run, a digit string, a wall of
+// whitespace) cost time linear in their length:
+//  - the segment running into a tile from an earlier cut is not re-matched
+//    from that cut.  Each tile publishes its cursor past its end (the first
+//    piece start at or after it), and the next tile continues from there.
+//    A tile with a cut of its own publishes before it waits, so only runs of
+//    tiles without a cut wait on one another, each for its predecessor
+//    alone.  Workgroups start in index order on each XCD, so the earliest
+//    unfinished tile is always running and never waits on anything
+//    unfinished; a wait is also bounded in time, after which the tile finds
+//    the cursor itself (walking back to the segment's cut).  The cursors are
+//    tagged with the call's number, read once per workgroup; the last
+//    workgroup to read it advances it for the next call.
+//  - while it waits, a tile matches speculatively from its first four code
+//    points; once the handed-over cursor meets a piece start of one of these
+//    matches, the rest of that match is the tile's (matching from a piece
+//    start does not depend on how it was reached).
+//  - every loop of the pattern is a run of code points of given kinds.  In
+//    the window, a table of where each stretch of one kind ends lets a
+//    thread's match cross a stretch in one step; a match that needs the text
+//    past the window is finished by the whole workgroup, which finds a run's
+//    end 1 KiB per step.
 #include "tok_internal.h"
 #include "seg_rules.h"
 #include "wg_scan.h"
@@ -32,10 +53,16 @@ namespace {
 using namespace seg;
 
 constexpr int kCaseNT = 256;
-constexpr int kCaseTile = kPretokTile;                     // 1024 bytes
-constexpr int kCaseHalo = 256;                             // context bytes on each side
-constexpr int kCaseWin = kCaseTile + 2 * kCaseHalo;        // loaded bytes
-constexpr uint32_t kNotLead = 0;                           // info of a continuation byte
+constexpr int kCaseTile = kPretokTile;          // 1024 bytes
+constexpr int kCaseLeft = 16;                   // bytes before the tile: the code point before it, for cuts and checks
+constexpr int kCaseWin = 1280;                  // loaded bytes: [t0 - 16, t0 + 1264)
+constexpr int kCaseValid = kCaseWin - 4;        // decoded window bytes (a lead reads the 3 bytes after it)
+constexpr int kCand = 4;                        // speculative starts of the segment running into a tile
+constexpr int kJobs = kCaseTile + kCand;        // segments (one per cut) and speculative starts
+constexpr int kStage = 4 * kCaseNT;             // bytes per step of the workgroup-wide run search
+constexpr uint32_t kNotLead = 0;                // info of a continuation byte
+constexpr uint32_t kNone32 = 0xFFFFFFFFu;       // no position (positions are below TOK_MAX_BYTES < 2^32)
+static_assert(kCaseWin % kCaseNT == 0 && kCaseTile % 32 == 0, "window and tile shapes");
 
 __device__ inline uint32_t case_class(uint32_t cp) {
   if (cp < TOK_CLS_LOW) return (kCaseLow[cp >> 1] >> (4 * (cp & 1u))) & 15u;
@@ -53,122 +80,274 @@ __device__ inline uint32_t case_fold_extra(uint32_t cp) {
 
 __device__ inline uint32_t seq_len(uint32_t b0) { return b0 < 0x80 ? 1u : b0 >= 0xF0 ? 4u : b0 >= 0xE0 ? 3u : 2u; }
 
+__device__ inline uint32_t decode_cp(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3, uint32_t len) {
+  if (len == 2) return ((b0 & 0x1Fu) << 6) | (b1 & 0x3Fu);
+  if (len == 3) return ((b0 & 0x0Fu) << 12) | ((b1 & 0x3Fu) << 6) | (b2 & 0x3Fu);
+  if (len == 4) return ((b0 & 0x07u) << 18) | ((b1 & 0x3Fu) << 12) | ((b2 & 0x3Fu) << 6) | (b3 & 0x3Fu);
+  return b0;
+}
+
 // Info word of the code point whose bytes are b[0 .. len) (taken as given;
 // validation is separate).
 __device__ inline uint32_t decode_q(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3, uint32_t len) {
-  uint32_t cp = b0;
-  if (len == 2) cp = ((b0 & 0x1Fu) << 6) | (b1 & 0x3Fu);
-  else if (len == 3) cp = ((b0 & 0x0Fu) << 12) | ((b1 & 0x3Fu) << 6) | (b2 & 0x3Fu);
-  else if (len == 4) cp = ((b0 & 0x07u) << 18) | ((b1 & 0x3Fu) << 12) | ((b2 & 0x3Fu) << 6) | (b3 & 0x3Fu);
+  const uint32_t cp = decode_cp(b0, b1, b2, b3, len);
   return make_q(cp, case_class(cp), len, fold_code(cp, case_fold_extra(cp)));
 }
 
-// The text as the matcher reads it: decoded info from LDS inside the window,
-// decoded from global memory outside it.
-struct DevAcc {
-  const uint32_t* q;      // info per window byte (LDS)
-  int64_t lo;             // absolute position of window byte 0
-  const uint8_t* text;
-  uint64_t n;
-  const uint64_t* doc_off;
-  uint32_t n_docs;
+// Info word of the code point at byte p of the text (kNotLead inside one),
+// without a document-start mark.
+__device__ inline uint32_t text_q(const uint8_t* text, uint64_t n, uint64_t p) {
+  const uint32_t b0 = text[p];
+  if ((b0 & 0xC0u) == 0x80u) return kNotLead;
+  const uint32_t len = seq_len(b0);
+  const uint32_t b1 = len > 1 && p + 1 < n ? text[p + 1] : 0u;
+  const uint32_t b2 = len > 2 && p + 2 < n ? text[p + 2] : 0u;
+  const uint32_t b3 = len > 3 && p + 3 < n ? text[p + 3] : 0u;
+  return decode_q(b0, b1, b2, b3, len);
+}
 
-  __device__ __forceinline__ uint32_t global_q(uint64_t p) const {
-    const uint32_t b0 = text[p];
-    if ((b0 & 0xC0u) == 0x80u) return kNotLead;
-    const uint32_t len = seq_len(b0);
-    const uint32_t b1 = len > 1 && p + 1 < n ? text[p + 1] : 0u;
-    const uint32_t b2 = len > 2 && p + 2 < n ? text[p + 2] : 0u;
-    const uint32_t b3 = len > 3 && p + 3 < n ? text[p + 3] : 0u;
-    uint32_t v = decode_q(b0, b1, b2, b3, len);
-    if (doc_off) {
-      const uint32_t d = first_doc_at_or_after(doc_off, n_docs, p);
-      if (d <= n_docs && doc_off[d] == p) v |= kQDocStart;
-    } else if (p == 0) {
-      v |= kQDocStart;
-    }
-    return v;
+// The value of the first active lane, as a scalar (the builtin works on
+// signed 32-bit values: cast back before any widening).
+__device__ __forceinline__ uint32_t uni32(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {
+  return ((uint64_t)uni32((uint32_t)(v >> 32)) << 32) | uni32((uint32_t)v);
+}
+
+struct CaseShared {
+  uint8_t raw[kCaseWin + 4];
+  uint16_t rend[kCaseWin];       // at a lead: where its stretch of one kind ends (window index, at most kCaseValid)
+  uint8_t ds[kCaseWin];          // a document starts at this byte
+  uint8_t stage[kStage + 4];     // text bytes of one step of a run search
+  uint32_t q[kCaseWin];          // info per window byte
+  uint32_t cut[kCaseTile / 32];    // cut bit per tile byte
+  uint32_t start[kCaseTile / 32];  // piece-start bit per tile byte
+  uint32_t job[kJobs];           // a segment's cut; a job that needs the text past the window leaves its cursor here
+  uint32_t far[(kJobs + 31) / 32];  // jobs that need the text past the window
+  uint32_t cmask[kCand][kCaseTile / 32];  // piece starts of each speculative match
+  uint32_t cstart[kCand], cexit[kCand], cok[kCand];
+  uint32_t red[2 * kCaseNT / kWave];
+  uint32_t nseg, ncand, doc0, bad, first, first_cut, exit, hand, back;
+};
+
+// Workgroup-wide minimum, and maximum of two values.  Contain barriers.
+__device__ inline uint32_t wg_min(CaseShared* S, uint32_t v) {
+  constexpr int NW = kCaseNT / kWave;
+  v = __builtin_amdgcn_readlane((int)wave_incl_scan(v, MinOp{}, kNone32), kWave - 1);
+  if (lane_id() == 0) S->red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  uint32_t r = S->red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = min(r, S->red[i]);
+  __syncthreads();
+  return uni32(r);
+}
+__device__ inline uint2 wg_max2(CaseShared* S, uint32_t a, uint32_t b) {
+  constexpr int NW = kCaseNT / kWave;
+  a = __builtin_amdgcn_readlane((int)wave_incl_scan(a, MaxOp{}, 0u), kWave - 1);
+  b = __builtin_amdgcn_readlane((int)wave_incl_scan(b, MaxOp{}, 0u), kWave - 1);
+  if (lane_id() == 0) {
+    S->red[threadIdx.x / kWave] = a;
+    S->red[NW + threadIdx.x / kWave] = b;
   }
+  __syncthreads();
+  uint32_t ra = S->red[0], rb = S->red[NW];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    ra = max(ra, S->red[i]);
+    rb = max(rb, S->red[NW + i]);
+  }
+  __syncthreads();
+  return make_uint2(uni32(ra), uni32(rb));
+}
 
-  // info of the code point at byte p
-  __device__ __forceinline__ uint32_t at(uint64_t p) const {
-    if (p >= n) return kQEnd;
-    const int64_t i = (int64_t)p - lo;
-    if (i >= 0 && i < kCaseWin - 4) return q[i];
-    return global_q(p);
+// The run (seg_rules.h) from the code point start h, found by the whole
+// workgroup, 1 KiB of text per step; lim: the end of the text as the match
+// sees it (the text's end or the first document start past the cursor).
+// Call from all threads with the same arguments.
+__device__ Run coop_run(CaseShared* S, const uint8_t* __restrict__ text, uint64_t n, uint64_t lim, uint64_t h,
+                        uint32_t mask, uint32_t tmask) {
+  const uint32_t tid = threadIdx.x;
+  uint32_t tend = 0, last = 0;  // a byte position + 0 / + 1; 0: none yet
+  for (uint64_t base = h;; base += kStage) {
+    for (int i = tid; i < kStage + 4; i += kCaseNT) {
+      const uint64_t x = base + i;
+      S->stage[i] = x < n ? text[x] : 0;
+    }
+    __syncthreads();
+    const uint64_t x0 = base + 4 * tid;
+    uint32_t stop = kNone32, my_tend = 0, my_last = 0;
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t x = x0 + j;
+      if (x >= lim) {  // the first such x over all threads is max(lim, h), as a serial run finds it
+        stop = (uint32_t)x;
+        break;
+      }
+      const uint32_t b0 = S->stage[4 * tid + j];
+      if ((b0 & 0xC0u) == 0x80u) continue;
+      const uint32_t len = seq_len(b0);
+      const uint32_t cp = decode_cp(b0, S->stage[4 * tid + j + 1], S->stage[4 * tid + j + 2],
+                                    S->stage[4 * tid + j + 3], len);
+      const uint32_t k = (cp == 0x0A || cp == 0x0D) ? (uint32_t)kKCrlf : case_class(cp);
+      if (!((mask >> k) & 1u)) {
+        stop = (uint32_t)x;
+        break;
+      }
+      my_last = (uint32_t)x + 1;
+      if ((tmask >> k) & 1u) my_tend = (uint32_t)(x + len);
+    }
+    const uint32_t f = wg_min(S, stop);
+    if (f != kNone32 && x0 > f) my_tend = my_last = 0;  // past the run's end
+    const uint2 tl = wg_max2(S, my_tend, my_last);
+    tend = max(tend, tl.x);
+    last = max(last, tl.y);
+    if (f != kNone32) return Run{f, tend ? (uint64_t)tend : kNoPos, last ? (uint64_t)(last - 1) : kNoPos};
+  }
+}
+
+// The text as a thread's own match reads it: the loaded window only; a read
+// at or past its end marks the match as needing the workgroup.
+struct WinAcc {
+  const uint32_t* q;
+  const uint16_t* rend;
+  int64_t lo;
+  uint64_t n;
+  uint64_t wend;
+  mutable bool far;
+  __device__ __forceinline__ uint32_t at(uint64_t i) const {
+    if (i >= n) return kQEnd;
+    if (i >= wend) {
+      far = true;
+      return kQEnd;
+    }
+    return q[i - lo];
+  }
+  __device__ __forceinline__ uint64_t run_end(uint64_t i) const { return (uint64_t)(lo + rend[i - lo]); }
+  __device__ __forceinline__ uint64_t prev_lead(uint64_t i) const {
+    int64_t k = (int64_t)i - 1 - lo;
+    while (q[k] == kNotLead) --k;
+    return (uint64_t)(lo + k);
+  }
+  __device__ __forceinline__ Run run(uint64_t p, uint64_t h, uint32_t mask, uint32_t tmask) const {
+    return run_jump(*this, p, h, mask, tmask);
   }
 };
+
+// The text as the workgroup's match reads it: the window from LDS, the rest
+// from global memory, runs found by coop_run.  Every value is the same in
+// every lane (read as scalars), so the match's branches are uniform and the
+// barriers inside coop_run are reached by all threads.
+struct CoopAcc {
+  CaseShared* S;
+  int64_t lo;
+  const uint8_t* text;
+  uint64_t n;
+  uint64_t lim;  // the text's end, or the first document start past the entry cursor
+  __device__ __forceinline__ uint32_t at(uint64_t i) const {
+    uint32_t v;
+    const int64_t w = (int64_t)i - lo;
+    if (i >= lim) v = kQEnd;
+    else if (w >= 0 && w < kCaseValid) v = S->q[w];
+    else v = text_q(text, n, i);
+    return uni32(v);
+  }
+  __device__ __forceinline__ Run run(uint64_t p, uint64_t h, uint32_t mask, uint32_t tmask) const {
+    const Run r = coop_run(S, text, n, lim, h, mask, tmask);
+    return Run{uni64(r.stop), uni64(r.tend), uni64(r.last)};
+  }
+};
+
+// The first document start after byte p (or the text's end).
+__device__ inline uint64_t doc_limit(const uint64_t* doc_off, uint32_t n_docs, uint64_t n, uint64_t p) {
+  if (!doc_off) return n;
+  const uint32_t d = first_doc_at_or_after(doc_off, n_docs, p + 1);
+  return uni64(d <= n_docs ? min(doc_off[d], n) : n);
+}
+
+__device__ inline void publish(const Bufs& B, uint32_t tile, uint32_t tag, uint64_t cursor) {
+  __hip_atomic_store(&B.hand_state[tile], ((uint64_t)tag << 32) | (uint32_t)cursor, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __global__ void __launch_bounds__(kCaseNT)
 pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off,
                    uint32_t n_docs, const uint32_t* __restrict__ joinable, Bufs B) {
-  __shared__ uint8_t s_raw[kCaseWin + 4];
-  __shared__ uint8_t s_ds[kCaseWin];        // a document starts at this byte
-  __shared__ uint32_t s_q[kCaseWin];        // info per window byte
-  __shared__ uint32_t s_cut[kCaseTile / 32];    // cut bit per tile byte
-  __shared__ uint32_t s_start[kCaseTile / 32];  // piece-start bit per tile byte
-  __shared__ uint32_t s_seg[kCaseTile + 1];     // segment starts (byte positions)
-  __shared__ uint32_t s_nseg, s_doc0, s_bad;
-
+  __shared__ CaseShared sh;
+  CaseShared* S = &sh;
   if (B.n_docs_dev) n_docs = *B.n_docs_dev;
   const uint32_t tid = threadIdx.x;
-  const int64_t t0 = (int64_t)blockIdx.x * kCaseTile;
-  const int64_t lo = t0 - kCaseHalo;
-  const int64_t t1 = min((int64_t)n, t0 + kCaseTile);
-  // per-call set-up for the later passes: clear the group sums of the tile
-  // counts, and check the batch's document offsets
+  const uint32_t tiles = gridDim.x;
+  const uint32_t tile = blockIdx.x;
+  // the call's number (thread 0 only: it publishes and waits); the count of
+  // workgroups that have read it is taken later, off the critical path
+  uint64_t epoch = 0;
   if (tid == 0) {
-    const uint32_t tiles = gridDim.x;
+    epoch = __hip_atomic_load(&B.hand_tick[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // per-call set-up for the later passes: clear the group sums of the tile
+    // counts, and check the batch's document offsets
     if (blockIdx.x < ((tiles + 63u) >> kSum1Shift)) B.sum1[blockIdx.x] = 0;
     if (blockIdx.x < ((tiles + 4095u) >> kSum2Shift)) B.sum2[blockIdx.x] = 0;
     if (doc_off && blockIdx.x == 0 && (doc_off[0] != 0 || doc_off[n_docs] != n)) report(&B.ctr->err_docs, B.gen);
-    s_nseg = 0;
-    s_bad = 0;
-    s_doc0 = doc_off ? first_doc_at_or_after(doc_off, n_docs, (uint64_t)max(lo, (int64_t)0)) : 0u;
   }
+  const uint32_t tag = (uint32_t)(epoch % 0xFFFFFFFFull) + 1u;  // meaningful in thread 0
   if (doc_off) {
     bool bad_doc = false;
     for (uint32_t d = blockIdx.x * kCaseNT + tid; d < n_docs; d += gridDim.x * kCaseNT)
       bad_doc |= doc_off[d] > doc_off[d + 1];
     if (bad_doc) report(&B.ctr->err_docs, B.gen);
   }
-  for (int i = tid; i < kCaseWin; i += kCaseNT) {
+  const int64_t t0 = (int64_t)tile * kCaseTile;
+  const int64_t lo = t0 - kCaseLeft;
+  const int64_t t1 = min((int64_t)n, t0 + kCaseTile);
+  if (tid == 0) {
+    S->nseg = 0;
+    S->ncand = 0;
+    S->bad = 0;
+    S->first_cut = (uint32_t)t1;
+    S->exit = (uint32_t)t1;
+    S->doc0 = doc_off ? first_doc_at_or_after(doc_off, n_docs, (uint64_t)max(lo, (int64_t)0)) : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < kCaseWin / kCaseNT; ++r) {  // all loads in flight at once
+    const int i = tid + r * kCaseNT;
     const int64_t p = lo + i;
-    s_raw[i] = p >= 0 && p < (int64_t)n ? text[p] : 0;
-    s_ds[i] = 0;
+    S->raw[i] = p >= 0 && p < (int64_t)n ? text[p] : 0;
+    S->ds[i] = 0;
   }
-  if (tid < 4) s_raw[kCaseWin + tid] = 0;
+  if (tid < 4) S->raw[kCaseWin + tid] = 0;
   for (int i = tid; i < kCaseTile / 32; i += kCaseNT) {
-    s_cut[i] = 0;
-    s_start[i] = 0;
+    S->cut[i] = 0;
+    S->start[i] = 0;
   }
+  for (int i = tid; i < kCand * (kCaseTile / 32); i += kCaseNT) S->cmask[i / (kCaseTile / 32)][i % (kCaseTile / 32)] = 0;
+  for (int i = tid; i < (kJobs + 31) / 32; i += kCaseNT) S->far[i] = 0;
   __syncthreads();
   // document starts inside the window
   if (doc_off) {
-    for (uint32_t d = s_doc0 + tid; d <= n_docs; d += kCaseNT) {
+    for (uint32_t d = S->doc0 + tid; d <= n_docs; d += kCaseNT) {
       const uint64_t p = doc_off[d];
       if ((int64_t)p >= lo + kCaseWin || p >= n) break;
-      if ((int64_t)p >= lo) s_ds[p - lo] = 1;
+      if ((int64_t)p >= lo) S->ds[p - lo] = 1;
     }
   } else if (lo <= 0 && tid == 0) {
-    s_ds[-lo] = 1;
+    S->ds[-lo] = 1;
   }
   __syncthreads();
   // decode every window byte
-  for (int i = tid; i < kCaseWin; i += kCaseNT) {
+#pragma unroll
+  for (int r = 0; r < kCaseWin / kCaseNT; ++r) {
+    const int i = tid + r * kCaseNT;
     const int64_t p = lo + i;
     uint32_t v = kQEnd;
     if (p >= 0 && p < (int64_t)n) {
-      const uint32_t b0 = s_raw[i];
+      const uint32_t b0 = S->raw[i];
       if ((b0 & 0xC0u) == 0x80u) {
         v = kNotLead;
       } else {
-        const uint32_t len = seq_len(b0);
-        v = decode_q(b0, s_raw[i + 1], s_raw[i + 2], s_raw[i + 3], len);
-        if (s_ds[i]) v |= kQDocStart;
+        v = decode_q(b0, S->raw[i + 1], S->raw[i + 2], S->raw[i + 3], seq_len(b0));
+        if (S->ds[i]) v |= kQDocStart;
       }
     }
-    s_q[i] = v;
+    S->q[i] = v;
   }
   // well-formed UTF-8 over the tile's own bytes (Unicode Table 3-7): a lead
   // is ASCII or C2..F4 with the right continuation bytes, all in its
@@ -176,111 +355,316 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
   // it in the same document
   for (int64_t p = t0 + tid; p < t1; p += kCaseNT) {
     const int i = (int)(p - lo);
-    const uint32_t b0 = s_raw[i];
+    const uint32_t b0 = S->raw[i];
     bool bad = false;
     if ((b0 & 0xC0u) == 0x80u) {
-      if (s_ds[i]) {
+      if (S->ds[i]) {
         bad = true;
       } else {
         int k = 1;
-        while (k <= 3 && (s_raw[i - k] & 0xC0u) == 0x80u && !s_ds[i - k]) ++k;
-        const uint32_t lead = s_raw[i - k];
+        while (k <= 3 && (S->raw[i - k] & 0xC0u) == 0x80u && !S->ds[i - k]) ++k;
+        const uint32_t lead = S->raw[i - k];
         bad = k > 3 || lo + i - k < 0 || (lead & 0xC0u) == 0x80u || lead < 0xC2u || lead > 0xF4u ||
               (int)seq_len(lead) <= k;
       }
     } else if (b0 >= 0x80u) {
       const uint32_t len = seq_len(b0);
       bad = b0 < 0xC2u || b0 > 0xF4u || p + (int64_t)len > (int64_t)n;
-      for (uint32_t k = 1; k < len && !bad; ++k) bad = (s_raw[i + k] & 0xC0u) != 0x80u || s_ds[i + k];
+      for (uint32_t k = 1; k < len && !bad; ++k) bad = (S->raw[i + k] & 0xC0u) != 0x80u || S->ds[i + k];
       if (!bad && len > 2) {
-        const uint32_t b1 = s_raw[i + 1];
+        const uint32_t b1 = S->raw[i + 1];
         bad = (b0 == 0xE0u && b1 < 0xA0u) || (b0 == 0xEDu && b1 > 0x9Fu) || (b0 == 0xF0u && b1 < 0x90u) ||
               (b0 == 0xF4u && b1 > 0x8Fu);
       }
     }
-    if (bad) s_bad = 1;
+    if (bad) S->bad = 1;
   }
+  // count this workgroup among those that have read the call's number (the
+  // add waits for the read: its operand depends on it; never more than 1)
+  uint64_t counted = 0;
+  if (tid == 0) counted = atomicAdd((unsigned long long*)&B.hand_tick[1], 1ull + (epoch >> 63));
+  // the last workgroup to be counted starts the next call's number
+  auto finish = [&]() {
+    if (tid == 0 && counted == tiles - 1) {
+      __hip_atomic_store(&B.hand_tick[1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&B.hand_tick[0], epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
   __syncthreads();
-  const uint64_t c0 = (uint64_t)blockIdx.x * (kCaseTile / kChunk);
+  const uint64_t c0 = (uint64_t)tile * (kCaseTile / kChunk);
   const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
-  if (s_bad) {  // uniform: the call reports malformed input; the flags are zero
-    if (tid == 0) report(&B.ctr->err_utf8, B.gen);
+  if (S->bad) {  // uniform: the call reports malformed input; the flags are zero
+    if (tid == 0) {
+      report(&B.ctr->err_utf8, B.gen);
+      publish(B, tile, tag, (uint64_t)t1);  // a cursor all the same, so no successor waits
+    }
     for (int c = tid; c < kCaseTile / kChunk; c += kCaseNT)
       if (c0 + c < n_chunks) B.flags[c0 + c] = 0;
+    finish();
     return;
   }
 
-  // cuts at the tile's code points, and the segments that start at them
-  for (int64_t p = t0 + tid; p < t1; p += kCaseNT) {
+  // cuts at the tile's code points (a wave's ballot is two words of the cut
+  // bits), and the segments that start at them
+#pragma unroll
+  for (int r = 0; r < kCaseTile / kCaseNT; ++r) {
+    const int64_t p = t0 + r * kCaseNT + tid;
     const int i = (int)(p - lo);
-    const uint32_t v = s_q[i];
-    if (v == kNotLead) continue;
-    bool cut = p == 0 || (v & kQDocStart);
-    if (!cut) {
-      // the previous lead is at most 3 bytes back in well-formed text; the
-      // bound keeps a malformed halo (reported by its own tile) in the window
-      int k = 1;
-      while (k < i && s_q[i - k] == kNotLead) ++k;
-      cut = sync_at(s_q[i - k], v);
+    const uint32_t v = S->q[i];
+    bool cut = false;
+    if (p < t1 && v != kNotLead) {
+      cut = p == 0 || (v & kQDocStart);
+      if (!cut) {
+        // the previous lead is at most 3 bytes back in well-formed text; the
+        // bound keeps a malformed halo (reported by its own tile) in the window
+        int k = 1;
+        while (k < i && S->q[i - k] == kNotLead) ++k;
+        cut = sync_at(S->q[i - k], v);
+      }
     }
-    if (cut) {
-      atomicOr(&s_cut[(p - t0) >> 5], 1u << ((p - t0) & 31));
-      s_seg[atomicAdd(&s_nseg, 1u)] = (uint32_t)p;
+    const uint64_t m = __ballot(cut);
+    const uint32_t lane = lane_id();
+    const uint32_t w0 = (uint32_t)(r * kCaseNT + (tid - lane)) / 32;
+    uint32_t base = 0;
+    if (lane == 0) {
+      S->cut[w0] = (uint32_t)m;
+      S->cut[w0 + 1] = (uint32_t)(m >> 32);
+      if (m) base = atomicAdd(&S->nseg, (uint32_t)__popcll(m));
+    }
+    base = __shfl(base, 0, kWave);
+    if (cut) S->job[base + __popcll(m & ((1ull << lane) - 1))] = (uint32_t)p;
+  }
+  __syncthreads();
+  auto is_cut = [&](uint64_t p) { return (S->cut[(p - t0) >> 5] >> ((p - t0) & 31)) & 1u; };
+  // the tile's first code point, its first cut, and speculative starts
+  // before its first cut
+  if (tid == 0) {
+    uint32_t fc = (uint32_t)t1;
+    for (int w = 0; w < kCaseTile / 32; ++w)
+      if (S->cut[w]) {
+        fc = (uint32_t)(t0 + 32 * w + __builtin_ctz(S->cut[w]));
+        break;
+      }
+    S->first_cut = fc;
+    int64_t f = t0;
+    while (f < t1 && S->q[f - lo] == kNotLead) ++f;
+    S->first = (uint32_t)f;
+    uint32_t nc = 0;
+    for (int64_t j = f; j < (int64_t)S->first_cut && nc < (uint32_t)kCand; ++j) {
+      if (S->q[j - lo] == kNotLead) continue;
+      S->cstart[nc] = (uint32_t)j;
+      S->cexit[nc] = (uint32_t)t1;
+      S->cok[nc] = 1;
+      ++nc;
+    }
+    S->ncand = nc;
+  }
+  // where each stretch of one kind ends: a boundary at every code point
+  // whose kind differs from the one before it, where a document starts or
+  // the text ends, and at the window's decoded end; each thread takes 5
+  // consecutive bytes, and the first boundary after them comes from a suffix
+  // minimum over the workgroup
+  {
+    constexpr int kPer = kCaseWin / kCaseNT;
+    uint32_t bmask = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid * kPer + j;
+      bool b;
+      if (i >= kCaseValid) {
+        b = i == kCaseValid;
+      } else {
+        const uint32_t v = S->q[i];
+        if (v == kNotLead) {
+          b = false;
+        } else if (i == 0 || (v & (kQDocStart | kQEnd))) {
+          b = true;
+        } else {
+          int k = i - 1;
+          while (k > 0 && S->q[k] == kNotLead) --k;
+          b = kind_of(S->q[k]) != kind_of(v);
+        }
+      }
+      bmask |= (uint32_t)b << j;
+    }
+    const uint32_t mine = bmask ? (uint32_t)(tid * kPer + __builtin_ctz(bmask)) : kNone32;
+    uint32_t next = wg_excl_suffix<kCaseNT>(mine, kNone32, MinOp{}, S->red, nullptr);
+#pragma unroll
+    for (int j = kPer - 1; j >= 0; --j) {
+      const int i = tid * kPer + j;
+      S->rend[i] = (uint16_t)min(next, (uint32_t)kCaseValid);
+      if ((bmask >> j) & 1u) next = (uint32_t)i;
     }
   }
-  const DevAcc acc{s_q, lo, text, n, doc_off, n_docs};
   __syncthreads();
-  // the segment running into the tile: from the last cut at or before the
-  // tile's first code point (walking back, through global memory if the
-  // cut lies before the window)
-  if (tid == 0) {
-    int64_t f = t0;
-    while (f < t1 && s_q[f - lo] == kNotLead) ++f;
-    if (f < t1 && !((s_cut[(f - t0) >> 5] >> ((f - t0) & 31)) & 1u)) {
-      uint64_t j = (uint64_t)f;
-      uint32_t vj = s_q[f - lo];
-      for (;;) {
-        if (j == 0 || (vj & kQDocStart)) break;
-        uint64_t k = j - 1;
-        while (k > 0 && ((int64_t)k - lo >= 0 && (int64_t)k - lo < kCaseWin ? s_q[k - lo] == kNotLead
-                                                                           : (text[k] & 0xC0u) == 0x80u))
-          --k;
-        const uint32_t vk = acc.at(k);
-        if (sync_at(vk, vj)) break;
-        j = k;
-        vj = vk;
+  const WinAcc wacc{S->q, S->rend, lo, n, (uint64_t)(lo + kCaseValid), false};
+
+  // every job, one per thread: a segment from its cut, or a speculative
+  // start, matched until the next cut or the tile's end
+  const uint32_t nseg = S->nseg, njobs = nseg + S->ncand;
+  for (uint32_t jb = tid; jb < njobs; jb += kCaseNT) {
+    const bool cand = jb >= nseg;
+    const uint32_t c = jb - nseg;
+    uint64_t p = cand ? S->cstart[c] : S->job[jb];
+    uint32_t* mark = cand ? S->cmask[c] : S->start;
+    for (;;) {
+      atomicOr(&mark[(p - t0) >> 5], 1u << ((p - t0) & 31));
+      const Matcher<WinAcc> m{wacc, p};
+      const uint64_t e = m.piece_end();
+      if (m.a.far) {  // the workgroup finishes it
+        if (cand) {
+          S->cok[c] = 0;
+        } else {
+          S->job[jb] = (uint32_t)p;
+          atomicOr(&S->far[jb >> 5], 1u << (jb & 31));
+        }
+        break;
       }
-      s_seg[s_nseg] = (uint32_t)j;
-      s_nseg = s_nseg + 1;
+      p = e > p ? e : p + 1;  // a match always advances; the guard keeps the loop finite regardless
+      if ((int64_t)p >= t1) {
+        if (cand) S->cexit[c] = (uint32_t)p;
+        else S->exit = (uint32_t)p;
+        break;
+      }
+      if (is_cut(p)) {
+        if (cand) S->cexit[c] = (uint32_t)p;
+        break;
+      }
     }
   }
   __syncthreads();
 
-  // every segment from its cut, one per thread: the pieces until the next
-  // cut or the tile's end
-  const uint32_t nseg = s_nseg;
-  for (uint32_t k = tid; k < nseg; k += kCaseNT) {
-    uint64_t p = s_seg[k];
+  // the segments whose matches need the text past the window, one at a time
+  // by the whole workgroup, from where the thread stopped
+  auto coop_walk = [&](uint64_t p) {
+    const CoopAcc acc{S, lo, text, n, doc_limit(doc_off, n_docs, n, p)};
     for (;;) {
-      if ((int64_t)p >= t0) atomicOr(&s_start[(p - t0) >> 5], 1u << ((p - t0) & 31));
-      const Matcher<DevAcc> m{acc, p};
-      const uint64_t e = m.piece_end();
-      p = e > p ? e : p + 1;  // a match always advances; the guard keeps the loop finite regardless
-      if ((int64_t)p >= t1) break;
-      if ((int64_t)p >= t0 && ((s_cut[(p - t0) >> 5] >> ((p - t0) & 31)) & 1u)) break;
+      if (tid == 0) atomicOr(&S->start[(p - t0) >> 5], 1u << ((p - t0) & 31));
+      const Matcher<CoopAcc> m{acc, p};
+      const uint64_t e = uni64(m.piece_end());
+      p = e > p ? e : p + 1;
+      if ((int64_t)p >= t1) return p;
+      if (is_cut(p)) return p;
+    }
+  };
+  for (uint32_t w = 0; w < (njobs + 31) / 32; ++w) {
+    uint32_t bits = uni32(S->far[w]);
+    while (bits) {
+      const uint32_t jb = w * 32 + __builtin_ctz(bits);
+      bits &= bits - 1;
+      const uint64_t e = coop_walk(uni32(S->job[jb]));
+      if ((int64_t)e >= t1 && tid == 0) S->exit = (uint32_t)e;
     }
   }
+  __syncthreads();
+
+  // a tile with a cut knows its cursor past its end: the last segment's
+  const uint32_t first = uni32(S->first);
+  const uint32_t first_cut = uni32(S->first_cut);
+  if ((int64_t)first_cut < t1 && tid == 0) publish(B, tile, tag, S->exit);
+
+  // the segment running into the tile, from the predecessor's cursor
+  if (tile > 0 && (first < first_cut || (int64_t)first_cut == t1)) {
+    if (tid == 0) {
+      const uint64_t* word = &B.hand_state[tile - 1];
+      const uint64_t t_start = B.hand_wait ? (uint64_t)wall_clock64() : 0;
+      uint32_t r = kNone32;
+      for (;;) {
+        const uint64_t v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(v >> 32) == tag) {
+          r = (uint32_t)v;
+          break;
+        }
+        if (!B.hand_wait || (uint64_t)wall_clock64() - t_start > B.hand_wait) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      S->hand = r;
+    }
+    __syncthreads();
+    uint64_t R = uni32(S->hand);
+    if (R == kNone32) {
+      // the wait ran out: walk back to the segment's cut (a document start
+      // at the latest), then match forward to the tile
+      if (tid == 0) {
+        uint64_t dstart = 0;
+        if (doc_off) {
+          const uint32_t d = first_doc_at_or_after(doc_off, n_docs, (uint64_t)first + 1);
+          dstart = d > 0 ? doc_off[d - 1] : 0;
+        }
+        auto info = [&](uint64_t p) {
+          const int64_t w = (int64_t)p - lo;
+          return w >= 0 && w < kCaseValid ? S->q[w] : text_q(text, n, p);
+        };
+        uint64_t j = first;
+        uint32_t vj = info(j);
+        while (j > dstart) {
+          uint64_t k = j - 1;
+          while (k > dstart && info(k) == kNotLead) --k;
+          const uint32_t vk = info(k);
+          if (sync_at(vk, vj)) break;
+          j = k;
+          vj = vk;
+        }
+        S->back = (uint32_t)j;
+      }
+      __syncthreads();
+      uint64_t p = uni32(S->back);
+      const CoopAcc acc{S, lo, text, n, doc_limit(doc_off, n_docs, n, p)};
+      while ((int64_t)p < t0) {
+        const Matcher<CoopAcc> m{acc, p};
+        const uint64_t e = uni64(m.piece_end());
+        p = e > p ? e : p + 1;
+      }
+      R = p;
+    }
+    uint64_t in_exit = R;
+    if (R < first_cut) {
+      uint64_t p = R;
+      for (;;) {
+        // a piece start of a speculative match: the rest of that match
+        uint32_t hit = kNone32;
+        for (uint32_t c = 0; c < S->ncand && hit == kNone32; ++c)
+          if (S->cok[c] && ((S->cmask[c][(p - t0) >> 5] >> ((p - t0) & 31)) & 1u)) hit = c;
+        hit = uni32(hit);
+        if (hit != kNone32) {
+          if (tid < kCaseTile / 32) {
+            const uint32_t b = (uint32_t)(p - t0);
+            const uint32_t keep = tid < (b >> 5) ? 0u : tid == (b >> 5) ? ~0u << (b & 31) : ~0u;
+            atomicOr(&S->start[tid], S->cmask[hit][tid] & keep);
+          }
+          in_exit = uni32(S->cexit[hit]);
+          break;
+        }
+        if (tid == 0) atomicOr(&S->start[(p - t0) >> 5], 1u << ((p - t0) & 31));
+        const Matcher<WinAcc> m{wacc, p};
+        uint64_t e = uni64(m.piece_end());
+        if (uni32((uint32_t)m.a.far)) {
+          const CoopAcc acc{S, lo, text, n, doc_limit(doc_off, n_docs, n, p)};
+          const Matcher<CoopAcc> mc{acc, p};
+          e = uni64(mc.piece_end());
+        }
+        p = e > p ? e : p + 1;
+        if ((int64_t)p >= t1 || is_cut(p)) {
+          in_exit = p;
+          break;
+        }
+      }
+    }
+    if ((int64_t)first_cut == t1 && tid == 0) publish(B, tile, tag, in_exit);
+  }
+
   if (joinable) {  // a unit of BPE also starts where no token spans the byte pair
     for (int64_t p = max(t0, (int64_t)1) + tid; p < t1; p += kCaseNT) {
       const int i = (int)(p - lo);
-      if (((s_raw[i - 1] | s_raw[i]) & 0x80u) && !pair_joinable(joinable, s_raw[i - 1], s_raw[i]))
-        atomicOr(&s_start[(p - t0) >> 5], 1u << ((p - t0) & 31));
+      if (((S->raw[i - 1] | S->raw[i]) & 0x80u) && !pair_joinable(joinable, S->raw[i - 1], S->raw[i]))
+        atomicOr(&S->start[(p - t0) >> 5], 1u << ((p - t0) & 31));
     }
   }
   __syncthreads();
   // flag words of the tile's chunks
   for (int c = tid; c < kCaseTile / kChunk; c += kCaseNT)
-    if (c0 + c < n_chunks) B.flags[c0 + c] = (uint16_t)(s_start[c >> 1] >> (16 * (c & 1)));
+    if (c0 + c < n_chunks) B.flags[c0 + c] = (uint16_t)(S->start[c >> 1] >> (16 * (c & 1)));
+  finish();
 }
 
 }  // namespace

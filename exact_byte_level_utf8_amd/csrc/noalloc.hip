@@ -10,7 +10,10 @@
 // address is looked up once per device, at the first tok_load on that device
 // (with the device current), and kept per device.  All calls on one GPU share
 // the array, so calls that overlap on one GPU race; the kernels clear what
-// must start at zero (the group sums) in every call.
+// must start at zero (the group sums) in every call.  The hand-over words of
+// the case-splitting pre-tokenization (a call counter, a count of the
+// workgroups that read it, and per-tile cursors tagged with it) start at zero with the array and are kept consistent by
+// every call.
 #include <mutex>
 
 #include "ctx.h"
@@ -32,7 +35,9 @@ constexpr uint64_t kOffSum2 = up256(kOffSum1 + ((kNaTiles >> kSum1Shift) + 1) * 
 constexpr uint64_t kOffWsSym = up256(kOffSum2 + ((kNaTiles >> kSum2Shift) + 1) * 4);
 constexpr uint64_t kOffWsRk = up256(kOffWsSym + (kNaMax + 64) * 4);
 constexpr uint64_t kOffWsSel = up256(kOffWsRk + (kNaMax + 64) * 4);
-constexpr uint64_t kScratchBytes = up256(kOffWsSel + (kNaMax + 64) * 8);
+constexpr uint64_t kOffHandTick = up256(kOffWsSel + (kNaMax + 64) * 8);
+constexpr uint64_t kOffHandState = up256(kOffHandTick + 16);
+constexpr uint64_t kScratchBytes = up256(kOffHandState + (kNaMax / kPretokTile + 1) * 8);
 static_assert(kScratchBytes < (24ull << 20), "the no-allocation scratch stays near 20 MiB");
 
 __device__ __align__(256) uint8_t scratch[kScratchBytes];
@@ -85,6 +90,9 @@ int tok_encode_dev_noalloc(tok_ctx* ctx, const uint8_t* d_text, size_t len, int3
   bb.ws_sym = reinterpret_cast<uint32_t*>(base + kOffWsSym);
   bb.ws_rk = reinterpret_cast<uint32_t*>(base + kOffWsRk);
   bb.ws_sel = reinterpret_cast<uint64_t*>(base + kOffWsSel);
+  bb.hand_tick = reinterpret_cast<uint64_t*>(base + kOffHandTick);  // zero at load, kept by every call
+  bb.hand_state = reinterpret_cast<uint64_t*>(base + kOffHandState);
+  bb.hand_wait = ctx->b.hand_wait;
   bb.ctr = ctx->d_ctr;
   bb.n_docs_dev = nullptr;
   bb.gen = ++ctx->gen;

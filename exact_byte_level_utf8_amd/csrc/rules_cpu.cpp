@@ -48,13 +48,55 @@ struct HostAcc {
   const std::vector<uint32_t>* q;
   size_t n;
   uint32_t at(uint64_t i) const { return i >= n ? (uint32_t)seg::kQEnd : (*q)[i]; }
+  seg::Run run(uint64_t p, uint64_t h, uint32_t mask, uint32_t tmask) const {
+    return seg::run_serial(*this, p, h, mask, tmask);
+  }
 };
 
-// The case-splitting family the way the kernel does it: 1 KiB tiles; in each
-// tile, segments from the last synchronizing cut at or before its first code
-// point and from every cut inside it, each matched from its cut until the
-// cursor reaches another cut or the tile's end.
-int case_pieces(const uint8_t* s, size_t n, const std::vector<char>& docstart, std::vector<uint64_t>& out) {
+// The same text seen through a tile's loaded window: a read at or past wend
+// marks the match as needing the text beyond the window.  Runs go a stretch
+// of one kind at a time (rend: the text's run ends, cut at the window's end),
+// as the kernel's per-thread matches do.
+struct WinAcc {
+  const std::vector<uint32_t>* q;
+  const std::vector<uint64_t>* rend;
+  size_t n;
+  uint64_t wend;
+  mutable bool far = false;
+  uint32_t at(uint64_t i) const {
+    if (i >= n) return seg::kQEnd;
+    if (i >= wend) {
+      far = true;
+      return seg::kQEnd;
+    }
+    return (*q)[i];
+  }
+  uint64_t run_end(uint64_t i) const { return std::min<uint64_t>((*rend)[i], wend); }
+  uint64_t prev_lead(uint64_t i) const {
+    uint64_t k = i - 1;
+    while (!((*q)[k] & seg::kQLead)) --k;
+    return k;
+  }
+  seg::Run run(uint64_t p, uint64_t h, uint32_t mask, uint32_t tmask) const {
+    return seg::run_jump(*this, p, h, mask, tmask);
+  }
+};
+
+// The case-splitting family the way the kernel does it, tile by tile (1 KiB
+// tiles, a window of 16 bytes before and 236 valid bytes after each).  A
+// tile matches the segments that start at its cuts, each until the cursor
+// reaches another cut or the tile's end, reading only its window; a match
+// that needs more is finished by the unbounded matcher (the kernel's
+// workgroup-wide one).  The cursor past the tile's end (the first piece
+// start at or after it) goes to the next tile, which continues the segment
+// running into it from there: directly if that start is past its first cut,
+// else by matching forward, where the piece starts already found from up to
+// four of the tile's first code points (speculatively, before the
+// predecessor's cursor was known) are taken over as soon as the cursor meets
+// one of them.  fallback: ignore the predecessor and find the segment's cut
+// by walking back (the kernel's path when a wait runs out).
+int case_pieces(const uint8_t* s, size_t n, const std::vector<char>& docstart, std::vector<uint64_t>& out,
+                bool fallback) {
   std::vector<uint32_t> q(n, 0);
   std::vector<uint64_t> leads;
   for (size_t i = 0; i < n;) {
@@ -68,38 +110,147 @@ int case_pieces(const uint8_t* s, size_t n, const std::vector<char>& docstart, s
     leads.push_back(i);
     i += len;
   }
-  std::vector<char> cut(n, 0);
+  std::vector<char> cut(n + 1, 0);
   for (size_t k = 0; k < leads.size(); ++k) {
     const uint64_t j = leads[k];
     cut[j] = k == 0 || docstart[j] || seg::sync_at(q[leads[k - 1]], q[j]);
   }
-  HostAcc acc{&q, n};
+  // run ends: the next code point start where the kind changes, a document
+  // starts or the text ends
+  std::vector<uint64_t> rend(n + 1, n);
+  {
+    uint64_t next = n;
+    for (size_t k = leads.size(); k-- > 0;) {
+      const uint64_t j = leads[k];
+      rend[j] = next;
+      if (k == 0 || docstart[j] || seg::kind_of(q[j]) != seg::kind_of(q[leads[k - 1]])) next = j;
+    }
+  }
+  const HostAcc full{&q, n};
   std::vector<char> start(n, 0);
-  constexpr size_t kTile = 1024;
+  constexpr size_t kTile = 1024, kLeft = 16, kWin = 1280, kCand = 4;
+  uint64_t carry = 0;  // the first piece start at or after the previous tile's end
   for (size_t t0 = 0; t0 < n; t0 += kTile) {
     const size_t t1 = std::min(n, t0 + kTile);
+    const WinAcc win{&q, &rend, n, t0 - kLeft + kWin - 4};  // window [t0 - 16, t0 + 1264), decoded up to 4 bytes short
     size_t first = t0;
     while (first < t1 && !(q[first] & seg::kQLead)) ++first;
-    if (first == t1) continue;
-    size_t a0 = first;
-    while (!cut[a0]) {
-      --a0;
-      while (!(q[a0] & seg::kQLead)) --a0;
-    }
-    std::vector<size_t> segs{a0};
-    for (size_t j = first + 1; j < t1; ++j)
-      if ((q[j] & seg::kQLead) && cut[j]) segs.push_back(j);
-    for (size_t a : segs) {
-      uint64_t p = a;
+    size_t first_cut = first;
+    while (first_cut < t1 && !((q[first_cut] & seg::kQLead) && cut[first_cut])) ++first_cut;
+    // match from a piece start until a cut or the tile's end; returns the
+    // cursor there, or kNoPos if the window did not suffice (mark: the
+    // starts found, which stay valid)
+    auto walk = [&](uint64_t p, const auto& acc, std::vector<char>& mark, bool& far) -> uint64_t {
+      far = false;
       for (;;) {
-        if (p >= t0) start[p] = 1;
-        seg::Matcher<HostAcc> m{acc, p};
+        if (p >= t0 && p < t1) mark[p - t0] = 1;
+        seg::Matcher<std::decay_t<decltype(acc)>> m{acc, p};
+        m.a.far = false;
         const uint64_t e = m.piece_end();
-        if (e <= p) return 2;  // no progress: a matcher bug
+        if (m.a.far) {  // the matcher holds its own copy of the accessor
+          far = true;
+          return p;
+        }
+        if (e <= p) return seg::kNoPos - 1;  // no progress: a matcher bug
         p = e;
-        if (p >= t1 || cut[p]) break;
+        if (p >= t1 || cut[p]) return p;
       }
+    };
+    struct Unbounded {  // the unbounded matcher behind the WinAcc interface
+      const HostAcc* f;
+      mutable bool far = false;
+      uint32_t at(uint64_t i) const { return f->at(i); }
+      seg::Run run(uint64_t p, uint64_t h, uint32_t mask, uint32_t tmask) const { return f->run(p, h, mask, tmask); }
+    };
+    const Unbounded unb{&full};
+    std::vector<char> tmark(t1 - t0, 0);
+    auto walk_any = [&](uint64_t p, std::vector<char>& mark) -> uint64_t {
+      bool far = false;
+      WinAcc w = win;
+      uint64_t r = walk(p, w, mark, far);
+      if (r == seg::kNoPos - 1) return r;
+      if (far) r = walk(r, unb, mark, far);
+      return r;
+    };
+    // the segments that start at the tile's cuts
+    uint64_t exit = seg::kNoPos;
+    for (size_t j = first_cut; j < t1; ++j) {
+      if (!((q[j] & seg::kQLead) && cut[j])) continue;
+      const uint64_t r = walk_any(j, tmark);
+      if (r == seg::kNoPos - 1) return 2;
+      if (r >= t1) exit = r;
     }
+    // the segment running into the tile
+    if (first < first_cut) {
+      // speculative matches from the first code points
+      std::vector<std::vector<char>> cmark;
+      std::vector<uint64_t> cstart, cexit;
+      for (size_t j = first; j < first_cut && cstart.size() < kCand; ++j) {
+        if (!(q[j] & seg::kQLead)) continue;
+        std::vector<char> mk(t1 - t0, 0);
+        bool far = false;
+        WinAcc w = win;
+        const uint64_t r = walk(j, w, mk, far);
+        if (r == seg::kNoPos - 1) return 2;
+        if (far) continue;  // a candidate that needs the text past the window is dropped
+        cmark.push_back(mk);
+        cstart.push_back(j);
+        cexit.push_back(r);
+      }
+      uint64_t R = carry;
+      if (fallback) {
+        // walk back to the segment's cut, then forward to the first piece
+        // start at or after t0
+        uint64_t c = first;
+        while (!cut[c]) {
+          --c;
+          while (!(q[c] & seg::kQLead)) --c;
+        }
+        uint64_t p = c;
+        while (p < t0) {
+          const seg::Matcher<HostAcc> m{full, p};
+          const uint64_t e = m.piece_end();
+          if (e <= p) return 2;
+          p = e;
+        }
+        R = p;
+      }
+      uint64_t in_exit = R;
+      if (R < first_cut) {
+        uint64_t p = R;
+        for (;;) {
+          size_t hit = cstart.size();
+          for (size_t c = 0; c < cstart.size() && hit == cstart.size(); ++c)
+            if (cmark[c][p - t0]) hit = c;
+          if (hit < cstart.size()) {
+            for (size_t i = p - t0; i < t1 - t0; ++i) tmark[i] |= cmark[hit][i];
+            in_exit = cexit[hit];
+            break;
+          }
+          // one piece, through the window if it suffices
+          tmark[p - t0] = 1;
+          seg::Matcher<WinAcc> m{win, p};
+          m.a.far = false;
+          uint64_t e = m.piece_end();
+          if (m.a.far) {
+            const seg::Matcher<HostAcc> mf{full, p};
+            e = mf.piece_end();
+          }
+          if (e <= p) return 2;
+          p = e;
+          if (p >= t1 || cut[p]) {
+            in_exit = p;
+            break;
+          }
+        }
+      }
+      if (first_cut == t1) exit = in_exit;
+    } else if (first == t1) {
+      exit = carry;  // no code point starts in the tile
+    }
+    for (size_t i = 0; i < t1 - t0; ++i)
+      if (tmark[i]) start[t0 + i] = 1;
+    carry = exit;
   }
   for (size_t i = 0; i < n; ++i)
     if (start[i]) out.push_back(i);
@@ -147,9 +298,9 @@ extern "C" int rules_cpu_pieces(const uint8_t* s, size_t n, const uint64_t* doc_
     docstart[0] = 1;
   }
   docstart[n] = 1;
-  if (pattern == 2) {
+  if (pattern == 2 || pattern == 3) {  // 3: every tile takes the fallback path
     std::vector<uint64_t> st;
-    const int rc = case_pieces(s, n, docstart, st);
+    const int rc = case_pieces(s, n, docstart, st, pattern == 3);
     if (rc) return rc;
     *n_out = st.size();
     for (size_t k = 0; k < st.size() && k < cap; ++k) starts[k] = st[k];

@@ -91,9 +91,67 @@ TOK_HD inline uint32_t fold_code(uint32_t cp, uint32_t fold_extra) {
   }
 }
 
+// Kinds of code point for the matcher's runs: the letter-case class, with
+// CR and LF (whitespace) apart, and the sets the pattern's loops take.
+enum : uint32_t { kKCrlf = 7 };
+enum : uint32_t {
+  kMaskH = (1u << kSU) | (1u << kSC) | (1u << kSM),      // upper, caseless, marks
+  kMaskT = (1u << kSD) | (1u << kSC) | (1u << kSM),      // lower, caseless, marks
+  kMaskOM = (1u << kSO) | (1u << kSM),                   // other chars and marks
+  kMaskW = (1u << kSW) | (1u << kKCrlf),                 // whitespace
+  kMaskCrlf = 1u << kKCrlf,                              // CR, LF
+};
+TOK_HD inline uint32_t kind_of(uint32_t q) { return (q & kQCrlf) ? (uint32_t)kKCrlf : sub_of(q); }
+
+constexpr uint64_t kNoPos = ~0ull;
+
+// A run of code points whose kinds lie in a set, from a code point start h:
+// stop = the first code point start at or after h that ends it (past the
+// text, a document start past the cursor, or a kind outside the set); tend =
+// the byte after the last code point in [h, stop) whose kind lies in a second
+// set (kNoPos if none); last = the first byte of the last code point in
+// [h, stop) (kNoPos if the run is empty).
+struct Run {
+  uint64_t stop, tend, last;
+};
+
+// The run, one code point at a time through the accessor's at().
+template <typename Acc>
+TOK_HD TOK_SEG_INLINE Run run_serial(const Acc& a, uint64_t p, uint64_t h, uint32_t mask, uint32_t tmask) {
+  Run r{h, kNoPos, kNoPos};
+  for (;;) {
+    const uint32_t v = a.at(r.stop);
+    if ((v & kQEnd) || (r.stop > p && (v & kQDocStart)) || !((mask >> kind_of(v)) & 1u)) return r;
+    r.last = r.stop;
+    r.stop += len_of(v);
+    if ((tmask >> kind_of(v)) & 1u) r.tend = r.stop;
+  }
+}
+
+// The same run, a stretch of one kind at a time: the accessor also gives
+// run_end(i), the first code point start after the code point at i where the
+// kind changes, a document starts or the text ends (or the end of what the
+// accessor can read), and prev_lead(i), the first byte of the code point
+// before i.  A run of one kind costs one step however long it is.
+template <typename Acc>
+TOK_HD TOK_SEG_INLINE Run run_jump(const Acc& a, uint64_t p, uint64_t h, uint32_t mask, uint32_t tmask) {
+  uint64_t stop = h, tend = kNoPos;
+  for (;;) {
+    const uint32_t v = a.at(stop);
+    if ((v & kQEnd) || (stop > p && (v & kQDocStart)) || !((mask >> kind_of(v)) & 1u)) break;
+    const uint64_t e = a.run_end(stop);
+    if ((tmask >> kind_of(v)) & 1u) tend = e;
+    stop = e;
+  }
+  return Run{stop, tend, stop > h ? a.prev_lead(stop) : kNoPos};
+}
+
 // The pieces of a segment are matched from a cursor p.  Within a match,
 // any position past p where a document starts, or past the text, ends the
-// text (documents are hard boundaries).
+// text (documents are hard boundaries).  The accessor gives the info word of
+// a byte (at) and the extent of a run (run, as run_serial defines it); every
+// loop of the pattern is one run, so an accessor that finds long runs in
+// parallel matches long pieces in parallel.
 template <typename Acc>
 struct Matcher {
   const Acc a;  // held by value, so a device accessor stays in registers
@@ -104,6 +162,9 @@ struct Matcher {
     return (i > p && (v & kQDocStart)) ? kQEnd : v;
   }
   TOK_HD static bool end(uint32_t v) { return (v & kQEnd) != 0; }
+  TOK_HD TOK_SEG_INLINE Run run(uint64_t h, uint32_t mask, uint32_t tmask = 0) const {
+    return a.run(p, h, mask, tmask);
+  }
 
   // optional contraction suffix at e: 's 't 're 've 'm 'll 'd, any case
   TOK_HD TOK_SEG_INLINE uint64_t suffix(uint64_t e) const {
@@ -134,39 +195,18 @@ struct Matcher {
     // char of the H* stretch that is also in T
     for (int pre = 1; pre >= 0; --pre) {
       if (pre && !is_prefix(v0)) continue;
-      uint64_t h = pre ? n0 : p, last_t = ~0ull;
-      uint32_t vh = q(h);
-      while (!end(vh) && in_h(sub_of(vh))) {
-        if (in_t(sub_of(vh))) last_t = h;
-        h += len_of(vh);
-        vh = q(h);
-      }
-      if (!end(vh) && in_t(sub_of(vh))) {
-        uint64_t e = h;
-        uint32_t ve = vh;
-        while (!end(ve) && in_t(sub_of(ve))) {
-          e += len_of(ve);
-          ve = q(e);
-        }
-        return suffix(e);
-      }
-      if (last_t != ~0ull) return suffix(last_t + len_of(q(last_t)));
+      const Run h = run(pre ? n0 : p, kMaskH, kMaskT);
+      const uint32_t vh = q(h.stop);
+      if (!end(vh) && in_t(sub_of(vh))) return suffix(run(h.stop, kMaskT).stop);
+      if (h.tend != kNoPos) return suffix(h.tend);
     }
     // P? H+ T* S?
     for (int pre = 1; pre >= 0; --pre) {
       if (pre && !is_prefix(v0)) continue;
-      uint64_t h = pre ? n0 : p;
-      uint32_t vh = q(h);
+      const uint64_t h0 = pre ? n0 : p;
+      const uint32_t vh = q(h0);
       if (end(vh) || !in_h(sub_of(vh))) continue;
-      while (!end(vh) && in_h(sub_of(vh))) {
-        h += len_of(vh);
-        vh = q(h);
-      }
-      while (!end(vh) && in_t(sub_of(vh))) {
-        h += len_of(vh);
-        vh = q(h);
-      }
-      return suffix(h);
+      return suffix(run(run(h0, kMaskH).stop, kMaskT).stop);
     }
     // digits in groups of one to three
     if (s0 == kSN) {
@@ -180,36 +220,17 @@ struct Matcher {
     }
     // an optional space, other chars and marks, then CR/LF
     {
-      uint64_t e = ~0ull;
+      uint64_t e = kNoPos;
       if ((v0 & kQSpace) && !end(q(n0)) && in_om(sub_of(q(n0)))) e = n0;
       else if (in_om(s0)) e = p;
-      if (e != ~0ull) {
-        uint32_t ve = q(e);
-        while (!end(ve) && in_om(sub_of(ve))) {
-          e += len_of(ve);
-          ve = q(e);
-        }
-        while (!end(ve) && (ve & kQCrlf)) {
-          e += len_of(ve);
-          ve = q(e);
-        }
-        return e;
-      }
+      if (e != kNoPos) return run(run(e, kMaskOM).stop, kMaskCrlf).stop;
     }
     // whitespace: up to its last CR/LF; else not followed by non-whitespace;
     // else all of it
-    uint64_t e = p, last_crlf = ~0ull, last_start = p;
-    uint32_t count = 0, ve = v0;
-    while (!end(ve) && sub_of(ve) == kSW) {
-      if (ve & kQCrlf) last_crlf = e;
-      last_start = e;
-      ++count;
-      e += len_of(ve);
-      ve = q(e);
-    }
-    if (last_crlf != ~0ull) return last_crlf + 1;  // CR and LF are one byte each
-    if (end(ve)) return e;
-    return count >= 2 ? last_start : e;
+    const Run w = run(p, kMaskW, kMaskCrlf);
+    if (w.tend != kNoPos) return w.tend;  // CR and LF are one byte each
+    if (end(q(w.stop))) return w.stop;
+    return w.last != kNoPos && w.last > p ? w.last : w.stop;
   }
 };
 

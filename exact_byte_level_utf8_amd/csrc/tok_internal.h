@@ -124,6 +124,18 @@ struct Bufs {
   uint64_t* ws_sel;
   Counters* ctr;  // device address of the host-mapped counters
   uint64_t gen;   // this call's number
+  // Hand-over of the case-splitting pre-tokenization (k_pretok_case.hip):
+  // hand_tick: two words, the calls so far and the workgroups of the current
+  // call that have read that number; zero when allocated, and the count is
+  // back to zero after every call, so they persist across calls and are not
+  // per-call scratch.  hand_state: per tile, (tag << 32 | cursor), the first
+  // piece start at or after the tile's end, tagged with the call's number
+  // (1 + calls so far, modulo 2^32 - 1); zeroed when allocated.  hand_wait:
+  // wall-clock ticks a tile waits for its predecessor's word before finding
+  // the cursor itself (0: it never waits).
+  uint64_t* hand_tick;
+  uint64_t* hand_state;
+  uint64_t hand_wait;
   const uint32_t* n_docs_dev;  // if set, the document count, read on the device (overrides n_docs)
 };
 

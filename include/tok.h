@@ -100,6 +100,14 @@ typedef struct tok_ctx tok_ctx;
  *                   must lie (default 8; at most 2^20).  Any value is exact
  *                   (the certificate holds for every left context); a margin
  *                   keeps the splice away from the window's cut.
+ * handoff_wait_us:  TOK_PAT_O200K only: microseconds a 1 KiB tile of the
+ *                   pre-tokenization waits for the previous tile's cursor
+ *                   (the first piece start past that tile) before finding it
+ *                   itself by walking back to the cut its segment started at
+ *                   (default 1000000; at most 10^7).  The wait always ends
+ *                   well before this in practice; 0 makes every tile walk
+ *                   back (slow on long stretches without a cut, for tests).
+ *                   Results never depend on it.
  */
 typedef struct tok_opts {
   int32_t device;
@@ -107,6 +115,7 @@ typedef struct tok_opts {
   uint64_t initial_bytes;
   uint32_t repair_doublings;
   uint32_t repair_margin;
+  uint32_t handoff_wait_us;
 } tok_opts;
 
 void tok_opts_default(tok_opts* opts);

@@ -167,3 +167,70 @@ def test_repair(cfg):
         n, dinfo = t.repair_dev(buf, len(sess), text, len(ob))
         assert dinfo == info
         same(f"device repair {suf[:10]!r}", buf[:n].cpu().numpy(), want)
+
+
+# Stretches without a synchronizing cut, a megabyte and more: each tile takes
+# the cursor its predecessor hands over, and pieces past the loaded window are
+# matched by the whole workgroup.  Split-level parity (the oracle's textbook
+# BPE of a megabyte-long piece is quadratic); the IDs of such pieces are
+# covered by the long-piece tests of the merge stage.
+@pytest.mark.parametrize("text", [
+    "中" * 350_000, "7" * 1_000_001, " " * 700_000 + "x", "x'd" * 300_000, "!" * 900_000 + "\n" * 3000 + "a",
+    "A" * 600_000 + "b" * 400_000, "中" + "A" * 800_000 + " y", " " * 400_000 + "z",
+])
+def test_megabyte_stretches_without_a_cut(cfg, text):
+    t, o, _ = cfg
+    b = ("pre " + text + " post").encode()
+    same("pieces", gpu_pieces(t, b), o.pieces(b))
+
+
+def test_long_runs_inside_batch_documents(cfg):
+    """Cut-free runs that start and end inside documents of a batch, cross
+    tiles, and meet document boundaries (hard boundaries for the hand-over)."""
+    t, o, _ = cfg
+    rng = random.Random(33)
+    kinds = ["中", "7", " ", "x'd", "A", "!", "\n", "ab"]
+    docs = []
+    for i in range(60):
+        k = rng.choice(kinds)
+        docs.append(rng.choice(["", "q ", "中"]) + k * rng.randint(0, 3000) + rng.choice(["", " z", "b"]))
+    docs += [textgen.cjk_text(300 + i, 2000) for i in range(4)]
+    rng.shuffle(docs)
+    data, off = textgen.pack_docs(docs)
+    want = []
+    for d, s in zip(docs, off[:-1]):
+        want += [int(s) + p for p in o.pieces(d.encode())]
+    same("pieces", gpu_pieces(t, data, off), want)
+    ids, out_off = t.encode_batch(data, off)
+    want_ids, want_off = oracle_par.concat(oracle_par.map_docs(lambda d: o.encode(d.encode()), docs))
+    same("ids", ids, want_ids)
+    same("offsets", out_off, want_off)
+
+
+@pytest.fixture(scope="module")
+def walk_back(cfg):
+    """The same configuration with no hand-over wait: every tile finds the
+    cursor into it by walking back to its segment's cut."""
+    merges_name, pattern = libs.CONFIGS["o200k"]
+    return tk.Tokenizer(vocab.merges(merges_name), pattern, handoff_wait_us=0)
+
+
+@pytest.mark.parametrize("text", ["A" * 3000 + "b" * 2000 + " x", "中" * 2777 + "A", "7" * 5000 + "x",
+                                  " " * 3000 + "y", "x'd" * 1900, "!" + "́" * 2000 + "a", "DON'T" * 600])
+def test_walk_back_path(cfg, walk_back, text):
+    _, o, _ = cfg
+    b = ("pre " + text + " post").encode()
+    same("pieces", gpu_pieces(walk_back, b), o.pieces(b))
+    same("ids", walk_back.encode(b), o.encode(b))
+
+
+def test_walk_back_path_workload_and_batch(cfg, walk_back):
+    t, o, _ = cfg
+    b = textgen.cjk_text(96, 30_000).encode()
+    same("pieces", gpu_pieces(walk_back, b), gpu_pieces(t, b))
+    docs = random_docs(34, 3000, 40) + ["中" * 1500, "7" * 2100]
+    data, off = textgen.pack_docs(docs)
+    want = []
+    for d, s in zip(docs, off[:-1]):
+        want += [int(s) + p for p in o.pieces(d.encode())]
+    same("pieces", gpu_pieces(walk_back, data, off), want)

@@ -191,27 +191,39 @@ def test_case_random_strings(rules, case_orc):
         assert rules.pieces(b, 2) == case_orc.pieces(b), b
 
 
-def test_case_long_runs_across_tiles(rules, case_orc):
-    texts = ["A" * 3000 + "b" * 2000 + " x", "ab" * 2000 + "C", "中" * 777 + "A", "7" * 5000 + "x",
+LONG_RUNS = ["A" * 3000 + "b" * 2000 + " x", "ab" * 2000 + "C", "中" * 777 + "A", "7" * 5000 + "x",
              " " * 3000 + "y", "x" + "\n" * 2050 + "  y", "Aa" * 1500, "a" + "́" * 1300 + "B", "DON'T" * 400,
-             "'" * 3000 + "s", "!" + "́" * 2000 + "a", "x'd" * 900, textgen.cjk_text(8, 5000)]
-    for t in texts:
-        b = t.encode()
-        assert rules.pieces(b, 2) == case_orc.pieces(b), t[:30]
+             "'" * 3000 + "s", "!" + "́" * 2000 + "a", "x'd" * 900, "中" + "A" * 4000 + " ", "AB" * 700 + "cd" * 700,
+             "\u00a0" * 2000 + "x", " " + "!" * 3000 + "\r\n" * 700 + "z", "中A" * 1500 + "b", "7" * 4001,
+             "x" + " " * 1500 + "\n" + " " * 1500 + "y", "a" * 1261 + "B", "A" * 1258 + "'LL x"]
+
+
+@pytest.mark.parametrize("pat", [2, 3])
+def test_case_long_runs_across_tiles(rules, case_orc, pat):
+    """Pieces and runs longer than a tile's window, with the tile's cursor
+    handed over (2) and recomputed by walking back (3)."""
+    for t in LONG_RUNS + [textgen.cjk_text(8, 5000)]:
+        for pre in ["", "q", " ", "中" * 5, "x" * 1019, "x" * 1020, "x" * 1021, "x" * 1023]:
+            b = (pre + t).encode()
+            assert rules.pieces(b, pat) == case_orc.pieces(b), (pre[:3], len(pre), t[:30])
 
 
 @pytest.mark.parametrize("seed,n", [(2, 150_000), (3, 60_000)])
 def test_case_workload_text(rules, case_orc, seed, n):
     b = textgen.mix_text(seed, n).encode()
     assert rules.pieces(b, 2) == case_orc.pieces(b)
+    assert rules.pieces(b, 3) == case_orc.pieces(b)
 
 
 def test_case_documents_are_hard_boundaries(rules, case_orc):
     rng = random.Random(4)
     docs = ["".join(rng.choice(CASE_WIDE) for _ in range(rng.randint(0, 30))) for _ in range(300)]
+    docs += ["中" * 900, "7" * 2500, " " * 1800, "A" * 700] * 3
+    rng.shuffle(docs)
     data = "".join(docs).encode()
     off = np.cumsum([0] + [len(d.encode()) for d in docs])
     want = []
     for d, s in zip(docs, off[:-1]):
         want += [int(s) + p for p in case_orc.pieces(d.encode())]
     assert rules.pieces(data, 2, off) == want
+    assert rules.pieces(data, 3, off) == want
