@@ -263,7 +263,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
         hipMalloc((void**)&ctx->d_tok_len, ctx->tok_len.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_tok_min, tmin16.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_joinable, join.size() * 4) != hipSuccess ||
-        hipMalloc((void**)&ctx->d_hand_tick, 16) != hipSuccess ||
+        hipMalloc((void**)&ctx->d_hand_tick, kHandTickWords * 8) != hipSuccess ||
         hipHostMalloc((void**)&ctx->h_ctr, sizeof(Counters), hipHostMallocMapped) != hipSuccess) {
       rc = TOK_E_NOMEM;
       break;
@@ -274,7 +274,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
             hipSuccess ||
         hipMemcpy(ctx->d_tok_min, tmin16.data(), tmin16.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(ctx->d_joinable, join.data(), join.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemset(ctx->d_hand_tick, 0, 16) != hipSuccess ||
+        hipMemset(ctx->d_hand_tick, 0, kHandTickWords * 8) != hipSuccess ||
         hipHostGetDevicePointer((void**)&ctx->d_ctr, ctx->h_ctr, 0) != hipSuccess)
       break;
     // the hand-over wait in wall-clock ticks (the clock's rate is in kHz)

@@ -59,12 +59,14 @@ constexpr int kCaseWin = 1280;                  // loaded bytes: [t0 - 16, t0 + 
 constexpr int kCaseValid = kCaseWin - 4;        // decoded window bytes (a lead reads the 3 bytes after it)
 constexpr int kCand = 4;                        // speculative starts of the segment running into a tile
 constexpr int kJobs = kCaseTile + kCand;        // segments (one per cut) and speculative starts
-constexpr int kStage = 4 * kCaseNT;             // bytes per step of the workgroup-wide run search
+constexpr int kStagePer = 16;                   // bytes per thread and step of the workgroup-wide run search
+constexpr int kStage = kStagePer * kCaseNT;     // bytes per step: 4 KiB
 constexpr uint32_t kNotLead = 0;                // info of a continuation byte
 constexpr uint32_t kNone32 = 0xFFFFFFFFu;       // no position (positions are below TOK_MAX_BYTES < 2^32)
 static_assert(kCaseWin % kCaseNT == 0 && kCaseTile % 32 == 0, "window and tile shapes");
 
 __device__ inline uint32_t case_class(uint32_t cp) {
+  if (cp < 0x80) return ascii_case(cp);
   if (cp < TOK_CLS_LOW) return (kCaseLow[cp >> 1] >> (4 * (cp & 1u))) & 15u;
   if (cp >= 0x110000) return kSO;
   const uint32_t blk = kCaseBlock[cp >> 8];
@@ -97,13 +99,13 @@ __device__ inline uint32_t decode_q(uint32_t b0, uint32_t b1, uint32_t b2, uint3
 // Info word of the code point at byte p of the text (kNotLead inside one),
 // without a document-start mark.
 __device__ inline uint32_t text_q(const uint8_t* text, uint64_t n, uint64_t p) {
+  // all four bytes in one round trip
   const uint32_t b0 = text[p];
+  const uint32_t b1 = p + 1 < n ? text[p + 1] : 0u;
+  const uint32_t b2 = p + 2 < n ? text[p + 2] : 0u;
+  const uint32_t b3 = p + 3 < n ? text[p + 3] : 0u;
   if ((b0 & 0xC0u) == 0x80u) return kNotLead;
-  const uint32_t len = seq_len(b0);
-  const uint32_t b1 = len > 1 && p + 1 < n ? text[p + 1] : 0u;
-  const uint32_t b2 = len > 2 && p + 2 < n ? text[p + 2] : 0u;
-  const uint32_t b3 = len > 3 && p + 3 < n ? text[p + 3] : 0u;
-  return decode_q(b0, b1, b2, b3, len);
+  return decode_q(b0, b1, b2, b3, seq_len(b0));
 }
 
 // The value of the first active lane, as a scalar (the builtin works on
@@ -117,7 +119,7 @@ struct CaseShared {
   uint8_t raw[kCaseWin + 4];
   uint16_t rend[kCaseWin];       // at a lead: where its stretch of one kind ends (window index, at most kCaseValid)
   uint8_t ds[kCaseWin];          // a document starts at this byte
-  uint8_t stage[kStage + 4];     // text bytes of one step of a run search
+  alignas(16) uint8_t stage[kStage + 32];  // 16-byte chunks of the text around one step of a run search
   uint32_t q[kCaseWin];          // info per window byte
   uint32_t cut[kCaseTile / 32];    // cut bit per tile byte
   uint32_t start[kCaseTile / 32];  // piece-start bit per tile byte
@@ -125,11 +127,16 @@ struct CaseShared {
   uint32_t far[(kJobs + 31) / 32];  // jobs that need the text past the window
   uint32_t cmask[kCand][kCaseTile / 32];  // piece starts of each speculative match
   uint32_t cstart[kCand], cexit[kCand], cok[kCand];
-  uint32_t red[2 * kCaseNT / kWave];
+  uint32_t red[3 * kCaseNT / kWave];
+  uint64_t stage_base;           // text position of the step's first byte (kNoPos before the first run search)
+  uint32_t stage_off;            // its index in stage
   uint32_t nseg, ncand, doc0, bad, first, first_cut, exit, hand, back;
 };
 
-// Workgroup-wide minimum, and maximum of two values.  Contain barriers.
+// Workgroup-wide minimum (scratch red[0 .. 4)), and maximum of two values
+// (red[4 .. 12)), for one step of a run search.  One barrier each: a step
+// writes its scratch again only after the next step's staging barrier, which
+// every thread reaches after reading this step's results.
 __device__ inline uint32_t wg_min(CaseShared* S, uint32_t v) {
   constexpr int NW = kCaseNT / kWave;
   v = __builtin_amdgcn_readlane((int)wave_incl_scan(v, MinOp{}, kNone32), kWave - 1);
@@ -138,62 +145,90 @@ __device__ inline uint32_t wg_min(CaseShared* S, uint32_t v) {
   uint32_t r = S->red[0];
 #pragma unroll
   for (int i = 1; i < NW; ++i) r = min(r, S->red[i]);
-  __syncthreads();
   return uni32(r);
 }
 __device__ inline uint2 wg_max2(CaseShared* S, uint32_t a, uint32_t b) {
   constexpr int NW = kCaseNT / kWave;
+  uint32_t* red = S->red + NW;
   a = __builtin_amdgcn_readlane((int)wave_incl_scan(a, MaxOp{}, 0u), kWave - 1);
   b = __builtin_amdgcn_readlane((int)wave_incl_scan(b, MaxOp{}, 0u), kWave - 1);
   if (lane_id() == 0) {
-    S->red[threadIdx.x / kWave] = a;
-    S->red[NW + threadIdx.x / kWave] = b;
+    red[threadIdx.x / kWave] = a;
+    red[NW + threadIdx.x / kWave] = b;
   }
   __syncthreads();
-  uint32_t ra = S->red[0], rb = S->red[NW];
+  uint32_t ra = red[0], rb = red[NW];
 #pragma unroll
   for (int i = 1; i < NW; ++i) {
-    ra = max(ra, S->red[i]);
-    rb = max(rb, S->red[NW + i]);
+    ra = max(ra, red[i]);
+    rb = max(rb, red[NW + i]);
   }
-  __syncthreads();
   return make_uint2(uni32(ra), uni32(rb));
 }
 
 // The run (seg_rules.h) from the code point start h, found by the whole
-// workgroup, 1 KiB of text per step; lim: the end of the text as the match
+// workgroup, 4 KiB of text per step; lim: the end of the text as the match
 // sees it (the text's end or the first document start past the cursor).
 // Call from all threads with the same arguments.
 __device__ Run coop_run(CaseShared* S, const uint8_t* __restrict__ text, uint64_t n, uint64_t lim, uint64_t h,
                         uint32_t mask, uint32_t tmask) {
   const uint32_t tid = threadIdx.x;
   uint32_t tend = 0, last = 0;  // a byte position + 0 / + 1; 0: none yet
+  __syncthreads();  // every wave is done reading the previous step's block (CoopAcc::at)
+  const uintptr_t end = (uintptr_t)(text + n);
   for (uint64_t base = h;; base += kStage) {
-    for (int i = tid; i < kStage + 4; i += kCaseNT) {
-      const uint64_t x = base + i;
-      S->stage[i] = x < n ? text[x] : 0;
+    // the step's bytes as aligned 16-byte chunks, one per thread (threads 0
+    // and 1 take one more for the tail), a single load each: a chunk that
+    // starts before the text's end holds a byte of the text, so, aligned, it
+    // lies in a page the text uses; a later one is zeros.  Bytes around the
+    // text's ends are read but never used.
+    const uintptr_t al = (uintptr_t)(text + base) & ~(uintptr_t)15;
+    const uint32_t off = (uint32_t)((uintptr_t)(text + base) - al);
+    for (uint32_t c = tid; c < (uint32_t)(kStage / 16 + 2); c += kCaseNT) {
+      const uintptr_t ca = al + 16u * c;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (ca < end) v = *reinterpret_cast<const uint4*>(ca);
+      *reinterpret_cast<uint4*>(&S->stage[16 * c]) = v;
+    }
+    if (tid == 0) {
+      S->stage_base = base;
+      S->stage_off = off;
     }
     __syncthreads();
-    const uint64_t x0 = base + 4 * tid;
+    const uint64_t x0 = base + kStagePer * tid;
     uint32_t stop = kNone32, my_tend = 0, my_last = 0;
-    for (int j = 0; j < 4; ++j) {
-      const uint64_t x = x0 + j;
-      if (x >= lim) {  // the first such x over all threads is max(lim, h), as a serial run finds it
-        stop = (uint32_t)x;
-        break;
+    // two halves of 8 bytes: their code points, every class-table read at
+    // once, then the run's test in order
+    for (int half = 0; half < kStagePer / 8 && stop == kNone32; ++half) {
+      uint32_t cps[8], lens[8], low[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t si = off + kStagePer * tid + 8 * half + j;
+        const uint32_t b0 = S->stage[si];
+        lens[j] = (b0 & 0xC0u) == 0x80u ? 0u : seq_len(b0);  // 0: inside a code point
+        cps[j] = decode_cp(b0, S->stage[si + 1], S->stage[si + 2], S->stage[si + 3], seq_len(b0));
       }
-      const uint32_t b0 = S->stage[4 * tid + j];
-      if ((b0 & 0xC0u) == 0x80u) continue;
-      const uint32_t len = seq_len(b0);
-      const uint32_t cp = decode_cp(b0, S->stage[4 * tid + j + 1], S->stage[4 * tid + j + 2],
-                                    S->stage[4 * tid + j + 3], len);
-      const uint32_t k = (cp == 0x0A || cp == 0x0D) ? (uint32_t)kKCrlf : case_class(cp);
-      if (!((mask >> k) & 1u)) {
-        stop = (uint32_t)x;
-        break;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) low[j] = kCaseLow[min(cps[j], (uint32_t)TOK_CLS_LOW - 1u) >> 1];
+      for (int j = 0; j < 8; ++j) {
+        const uint64_t x = x0 + 8 * half + j;
+        if (x >= lim) {  // the first such x over all threads is max(lim, h), as a serial run finds it
+          stop = (uint32_t)x;
+          break;
+        }
+        if (!lens[j]) continue;
+        const uint32_t cp = cps[j];
+        const uint32_t cls = cp < 0x80 ? ascii_case(cp)
+                             : cp < TOK_CLS_LOW ? (low[j] >> (4 * (cp & 1u))) & 15u
+                                                : case_class(cp);
+        const uint32_t k = (cp == 0x0A || cp == 0x0D) ? (uint32_t)kKCrlf : cls;
+        if (!((mask >> k) & 1u)) {
+          stop = (uint32_t)x;
+          break;
+        }
+        my_last = (uint32_t)x + 1;
+        if ((tmask >> k) & 1u) my_tend = (uint32_t)(x + lens[j]);
       }
-      my_last = (uint32_t)x + 1;
-      if ((tmask >> k) & 1u) my_tend = (uint32_t)(x + len);
     }
     const uint32_t f = wg_min(S, stop);
     if (f != kNone32 && x0 > f) my_tend = my_last = 0;  // past the run's end
@@ -245,9 +280,18 @@ struct CoopAcc {
   __device__ __forceinline__ uint32_t at(uint64_t i) const {
     uint32_t v;
     const int64_t w = (int64_t)i - lo;
-    if (i >= lim) v = kQEnd;
-    else if (w >= 0 && w < kCaseValid) v = S->q[w];
-    else v = text_q(text, n, i);
+    const uint64_t sb = S->stage_base;
+    if (i >= lim) {
+      v = kQEnd;
+    } else if (w >= 0 && w < kCaseValid) {
+      v = S->q[w];
+    } else if (i >= sb && i - sb < (uint64_t)kStage) {  // the last block a run search staged
+      const uint32_t k = (uint32_t)(i - sb) + S->stage_off, b0 = S->stage[k];
+      v = (b0 & 0xC0u) == 0x80u ? kNotLead
+                                : decode_q(b0, S->stage[k + 1], S->stage[k + 2], S->stage[k + 3], seq_len(b0));
+    } else {
+      v = text_q(text, n, i);
+    }
     return uni32(v);
   }
   __device__ __forceinline__ Run run(uint64_t p, uint64_t h, uint32_t mask, uint32_t tmask) const {
@@ -304,6 +348,7 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
     S->bad = 0;
     S->first_cut = (uint32_t)t1;
     S->exit = (uint32_t)t1;
+    S->stage_base = kNoPos;
     S->doc0 = doc_off ? first_doc_at_or_after(doc_off, n_docs, (uint64_t)max(lo, (int64_t)0)) : 0u;
   }
 #pragma unroll
@@ -332,22 +377,39 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
     S->ds[-lo] = 1;
   }
   __syncthreads();
-  // decode every window byte
+  // decode every window byte: the code points, then all their class-table
+  // reads at once (one round trip), then the info words
+  {
+    constexpr int kPer = kCaseWin / kCaseNT;
+    uint32_t cps[kPer], lens[kPer], low[kPer];
 #pragma unroll
-  for (int r = 0; r < kCaseWin / kCaseNT; ++r) {
-    const int i = tid + r * kCaseNT;
-    const int64_t p = lo + i;
-    uint32_t v = kQEnd;
-    if (p >= 0 && p < (int64_t)n) {
+    for (int r = 0; r < kPer; ++r) {
+      const int i = tid + r * kCaseNT;
       const uint32_t b0 = S->raw[i];
-      if ((b0 & 0xC0u) == 0x80u) {
-        v = kNotLead;
-      } else {
-        v = decode_q(b0, S->raw[i + 1], S->raw[i + 2], S->raw[i + 3], seq_len(b0));
-        if (S->ds[i]) v |= kQDocStart;
-      }
+      lens[r] = seq_len(b0);
+      cps[r] = decode_cp(b0, S->raw[i + 1], S->raw[i + 2], S->raw[i + 3], lens[r]);
     }
-    S->q[i] = v;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) low[r] = kCaseLow[min(cps[r], (uint32_t)TOK_CLS_LOW - 1u) >> 1];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = tid + r * kCaseNT;
+      const int64_t p = lo + i;
+      const uint32_t b0 = S->raw[i], cp = cps[r];
+      uint32_t v = kQEnd;
+      if (p >= 0 && p < (int64_t)n) {
+        if ((b0 & 0xC0u) == 0x80u) {
+          v = kNotLead;
+        } else {
+          const uint32_t cls = cp < 0x80 ? ascii_case(cp)
+                               : cp < TOK_CLS_LOW ? (low[r] >> (4 * (cp & 1u))) & 15u
+                                                  : case_class(cp);
+          v = make_q(cp, cls, lens[r], fold_code(cp, case_fold_extra(cp)));
+          if (S->ds[i]) v |= kQDocStart;
+        }
+      }
+      S->q[i] = v;
+    }
   }
   // well-formed UTF-8 over the tile's own bytes (Unicode Table 3-7): a lead
   // is ASCII or C2..F4 with the right continuation bytes, all in its
@@ -379,15 +441,18 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
     }
     if (bad) S->bad = 1;
   }
-  // count this workgroup among those that have read the call's number (the
-  // add waits for the read: its operand depends on it; never more than 1)
-  uint64_t counted = 0;
-  if (tid == 0) counted = atomicAdd((unsigned long long*)&B.hand_tick[1], 1ull + (epoch >> 63));
-  // the last workgroup to be counted starts the next call's number
+  // at the end, after the last barrier (a barrier waits for every memory
+  // operation in flight, and this one is contended): count this workgroup
+  // among those that have read the call's number (the add waits for the
+  // read: its operand depends on it; never more than 1), and the last one
+  // counted starts the next call's number
   auto finish = [&]() {
-    if (tid == 0 && counted == tiles - 1) {
-      __hip_atomic_store(&B.hand_tick[1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&B.hand_tick[0], epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      const uint64_t counted = atomicAdd((unsigned long long*)&B.hand_tick[kHandCountWord], 1ull + (epoch >> 63));
+      if (counted == tiles - 1) {
+        __hip_atomic_store(&B.hand_tick[kHandCountWord], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&B.hand_tick[0], epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   };
   __syncthreads();
@@ -565,20 +630,30 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
 
   // the segment running into the tile, from the predecessor's cursor
   if (tile > 0 && (first < first_cut || (int64_t)first_cut == t1)) {
-    if (tid == 0) {
-      const uint64_t* word = &B.hand_state[tile - 1];
+    // wave 0 reads the words of the 64 tiles before this one at once: the
+    // nearest published one decides if it is the predecessor's, or if its
+    // cursor already lies at or past this tile's start (then no tile in
+    // between has a piece start, and the cursor passes through them)
+    if (tid < kWave) {
+      const uint32_t wtag = uni32(tag);
+      const int64_t j = (int64_t)tile - 1 - tid;
       const uint64_t t_start = B.hand_wait ? (uint64_t)wall_clock64() : 0;
       uint32_t r = kNone32;
       for (;;) {
-        const uint64_t v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((uint32_t)(v >> 32) == tag) {
-          r = (uint32_t)v;
-          break;
+        const uint64_t v = j >= 0 ? __hip_atomic_load(&B.hand_state[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        const uint64_t pub = __ballot(j >= 0 && (uint32_t)(v >> 32) == wtag);
+        if (pub) {
+          const int l = __builtin_ctzll(pub);
+          const uint32_t c = (uint32_t)__shfl((int)(uint32_t)v, l, kWave);
+          if (l == 0 || (int64_t)c >= t0) {
+            r = c;
+            break;
+          }
         }
         if (!B.hand_wait || (uint64_t)wall_clock64() - t_start > B.hand_wait) break;
         __builtin_amdgcn_s_sleep(2);
       }
-      S->hand = r;
+      if (tid == 0) S->hand = r;
     }
     __syncthreads();
     uint64_t R = uni32(S->hand);

@@ -36,7 +36,7 @@ constexpr uint64_t kOffWsSym = up256(kOffSum2 + ((kNaTiles >> kSum2Shift) + 1) *
 constexpr uint64_t kOffWsRk = up256(kOffWsSym + (kNaMax + 64) * 4);
 constexpr uint64_t kOffWsSel = up256(kOffWsRk + (kNaMax + 64) * 4);
 constexpr uint64_t kOffHandTick = up256(kOffWsSel + (kNaMax + 64) * 8);
-constexpr uint64_t kOffHandState = up256(kOffHandTick + 16);
+constexpr uint64_t kOffHandState = up256(kOffHandTick + kHandTickWords * 8);
 constexpr uint64_t kScratchBytes = up256(kOffHandState + (kNaMax / kPretokTile + 1) * 8);
 static_assert(kScratchBytes < (24ull << 20), "the no-allocation scratch stays near 20 MiB");
 

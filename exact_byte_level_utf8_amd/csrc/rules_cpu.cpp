@@ -266,6 +266,9 @@ extern "C" void rules_cpu_case_range(uint32_t lo, uint32_t n, uint8_t* out) {
   for (uint32_t i = 0; i < n; ++i) out[i] = (uint8_t)table_case(lo + i);
 }
 
+// The kernels' table-free letter-case class of an ASCII byte.
+extern "C" int rules_cpu_ascii_case(uint32_t b) { return (int)seg::ascii_case(b); }
+
 // The case-splitting family's synchronizing transition (the library's rule).
 extern "C" int rules_cpu_sync_case(uint32_t x, uint32_t y) {
   return tok::sync_transition_case(x, table_case(x), y, table_case(y)) ? 1 : 0;

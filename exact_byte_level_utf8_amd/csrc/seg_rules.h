@@ -63,6 +63,17 @@ TOK_HD inline bool in_om(uint32_t s) { return s == kSO || s == kSM; }
 // the optional prefix char of a letter piece: not CR, LF, a letter or a number
 TOK_HD inline bool is_prefix(uint32_t q) { return !(q & kQCrlf) && sub_of(q) >= kSM && sub_of(q) != kSN; }
 
+// Letter-case class of an ASCII code point (b < 0x80) without the table:
+// A-Z upper, a-z lower, 0-9 numbers, TAB..CR and space whitespace, the rest
+// other (the table's values there; a test checks all 128).
+TOK_HD inline uint32_t ascii_case(uint32_t b) {
+  const uint32_t l = b | 0x20u;
+  if (l - 'a' < 26u) return b < 'a' ? kSU : kSD;
+  if (b - '0' < 10u) return kSN;
+  if (b - 9u < 5u || b == 0x20u) return kSW;
+  return kSO;
+}
+
 // Info word of a decoded code point.
 TOK_HD inline uint32_t make_q(uint32_t cp, uint32_t sub, uint32_t len, uint32_t fold) {
   uint32_t q = sub | kQLead | (len << kQLenShift) | (fold << kQFoldShift);

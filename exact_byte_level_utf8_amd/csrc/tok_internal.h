@@ -35,6 +35,8 @@ constexpr int kRowMax = 16;          // longest piece merged by one 16-lane row
 constexpr int kHalfMax = 32;         // longest piece merged by one 32-lane row
 constexpr int kWaveMax = 64;         // longest piece merged by one wave in registers
 constexpr int kPretokTile = 1024;    // bytes per workgroup of the pre-tokenization pass
+constexpr int kHandCountWord = 16;   // Bufs::hand_tick: the count's word, 128 bytes after the call number
+constexpr int kHandTickWords = 32;
 constexpr int kPieceTile = 1024;     // bytes per workgroup of the piece pass
 constexpr uint32_t kPieceSmallGrid = 1024;  // piece-pass grids up to this use 512-thread workgroups
 constexpr uint32_t kNoRank = 0xFFFFFFFFu;
@@ -125,7 +127,8 @@ struct Bufs {
   Counters* ctr;  // device address of the host-mapped counters
   uint64_t gen;   // this call's number
   // Hand-over of the case-splitting pre-tokenization (k_pretok_case.hip):
-  // hand_tick: two words, the calls so far and the workgroups of the current
+  // hand_tick: kHandTickWords words; [0] the calls so far, and
+  // [kHandCountWord] (on its own cache line) the workgroups of the current
   // call that have read that number; zero when allocated, and the count is
   // back to zero after every call, so they persist across calls and are not
   // per-call scratch.  hand_state: per tile, (tag << 32 | cursor), the first

@@ -177,6 +177,18 @@ def test_case_table_matches_oracle(rules):
     assert bad.size == 0, [hex(int(c)) for c in bad[:10]]
 
 
+def test_ascii_case_without_the_table(rules):
+    """The kernels classify ASCII by arithmetic: equal to the table (and so
+    to the oracle) on all 128 code points."""
+    rules.rules_cpu_case_range.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    rules.rules_cpu_case_range.restype = None
+    tab = np.zeros(128, dtype=np.uint8)
+    rules.rules_cpu_case_range(0, 128, tab.ctypes.data)
+    got = [rules.rules_cpu_ascii_case(b) for b in range(128)]
+    assert got == tab.tolist()
+    assert got == [int(c) for c in oracle.subclass_range(0, 128)]
+
+
 def test_case_exhaustive_short_strings(rules, case_orc):
     for n in range(1, 5):
         for tup in itertools.product(CASE_ALPHA, repeat=n):
