@@ -215,6 +215,13 @@ def walk_back(cfg):
     return tk.Tokenizer(vocab.merges(merges_name), pattern, handoff_wait_us=0)
 
 
+def test_handoff_wait_range(cfg):
+    merges_name, pattern = libs.CONFIGS["o200k"]
+    with pytest.raises(tk.TokError) as e:
+        tk.Tokenizer(vocab.merges(merges_name), pattern, handoff_wait_us=10_000_001)
+    assert e.value.code == tk.TOK_E_ARG
+
+
 @pytest.mark.parametrize("text", ["A" * 3000 + "b" * 2000 + " x", "中" * 2777 + "A", "7" * 5000 + "x",
                                   " " * 3000 + "y", "x'd" * 1900, "!" + "́" * 2000 + "a", "DON'T" * 600])
 def test_walk_back_path(cfg, walk_back, text):

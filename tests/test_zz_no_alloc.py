@@ -23,7 +23,7 @@ def cfg():
     libs.ensure_built()
     assert torch.cuda.is_available(), "GPU tests need a HIP device"
     out = {}
-    for name in ("gpt2", "llama3"):
+    for name in ("gpt2", "llama3", "o200k"):
         merges_name, pattern = libs.CONFIGS[name]
         m = vocab.merges(merges_name)
         out[name] = (tk.Tokenizer(m, pattern), oracle.Oracle(m, pattern))
@@ -40,7 +40,7 @@ def run_both(t, b: bytes):
     return a[:n1].cpu().numpy(), z[:n2].cpu().numpy(), z[n2:].cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+@pytest.mark.parametrize("name", ["gpt2", "llama3", "o200k"])
 def test_noalloc_matches_encode_dev(cfg, name):
     t, o = cfg[name]
     big = textgen.mix_text(61, 1_100_000).encode()[: tk.TOK_NOALLOC_MAX_BYTES]
@@ -50,7 +50,10 @@ def test_noalloc_matches_encode_dev(cfg, name):
         big = big[:-1]
     cjk = textgen.cjk_text(62, 40_000).encode()
     small = textgen.mix_text(63, 3_000).encode()
-    for b in (big, small, cjk, b"x", small[:1000]):
+    # stretches without a cut across tiles: under the case-splitting family the
+    # tiles hand their cursors over through words in the shared array
+    stretch = ("q " + "7" * 20_000 + " " * 5_000 + "x'd" * 3_000 + " z").encode()
+    for b in (big, small, cjk, b"x", stretch, small[:1000]):
         ref, got, tail = run_both(t, b)
         assert np.array_equal(got, ref), len(b)
         assert np.all(tail == -5), "nothing written past the count"
