@@ -28,7 +28,7 @@ def pairs():
     libs.ensure_built()
     assert torch.cuda.is_available(), "GPU tests need a HIP device"
     out = {}
-    for name in ("gpt2", "llama3"):
+    for name in ("gpt2", "llama3", "o200k"):
         merges_name, pattern = libs.CONFIGS[name]
         m = vocab.merges(merges_name)
         out[name] = (tk.Tokenizer(m, pattern), oracle.Oracle(m, pattern))
@@ -57,7 +57,7 @@ def raw_encode_dev(t, d_text, n, d_ids, cap):
     return rc, out.value
 
 
-@pytest.mark.parametrize("name", ["gpt2", "llama3"])
+@pytest.mark.parametrize("name", ["gpt2", "llama3", "o200k"])
 def test_replay_follows_buffer_contents(graph_on, name):
     t, o = graph_on[name]
     n = 200_000
@@ -80,6 +80,56 @@ def test_replay_follows_buffer_contents(graph_on, name):
             assert np.array_equal(got, want), f"replay {rep}/{i} differs from the oracle"
             assert np.all(d_ids[k:].cpu().numpy() == -1), "wrote past the count"
     assert counts[0] == 0 and all(c == 1 for c in counts[1:]), counts
+
+
+def stretch_text(seed: int, n: int) -> bytes:
+    """Mixed text of n bytes with stretches that hold no synchronizing cut of
+    the case-splitting family (digits, spaces, contractions, an ideograph
+    run) placed by the seed, so that the cursors the tiles hand over differ
+    from text to text."""
+    rng = np.random.default_rng(seed)
+    parts, size = [], 0
+    while size < n:
+        k = int(rng.integers(0, 5))
+        if k == 0:
+            s = textgen.mix_text(int(rng.integers(1 << 30)), int(rng.integers(200, 3000)))
+        elif k == 1:
+            s = " 7" + "7" * int(rng.integers(1000, 6000))
+        elif k == 2:
+            s = "x" + " " * int(rng.integers(1000, 5000)) + "y"
+        elif k == 3:
+            s = " " + "x'd" * int(rng.integers(300, 2000))
+        else:
+            s = "，" + "中" * int(rng.integers(200, 400)) + "。"
+        parts.append(s)
+        size += len(s.encode())
+    return fixed_len_text_from("".join(parts).encode(), n)
+
+
+def fixed_len_text_from(b: bytes, n: int) -> bytes:
+    b = b[:n].decode("utf-8", "ignore").encode()
+    return b + b"q" * (n - len(b))
+
+
+def test_replay_hands_over_fresh_cursors(graph_on):
+    """Under the case-splitting family each tile takes the cursor its
+    predecessor publishes in the call; a replay bakes in the call number it
+    was captured with, so the words must be told apart by a number the
+    device advances itself.  Texts with cut-free stretches in different
+    places, replayed twice each, against the oracle."""
+    t, o = graph_on["o200k"]
+    n = 150_000
+    texts = [stretch_text(900 + i, n) for i in range(5)]
+    src = torch.frombuffer(bytearray(b"".join(texts)), dtype=torch.uint8).cuda()
+    d_text = torch.empty(n, dtype=torch.uint8, device="cuda")
+    d_ids = torch.empty(n, dtype=torch.int32, device="cuda")
+    wants = [o.encode(b) for b in texts]
+    for rep in range(2):
+        for i in range(len(texts)):
+            d_text.copy_(src[i * n:(i + 1) * n])
+            k = t.encode_dev(d_text, d_ids)
+            assert np.array_equal(d_ids[:k].cpu().numpy(), wants[i]), f"replay {rep}/{i} differs from the oracle"
+    assert t.graph_count() == 1
 
 
 def test_replay_reports_errors_and_capacity(graph_on):
