@@ -188,6 +188,7 @@ struct tok_ctx {
     t.tok_len = d_tok_len;
     t.tok_min = d_tok_min;
     t.min_shift = min_shift;
+    t.max_tok_len = max_tok_len;
     return t;
   }
 

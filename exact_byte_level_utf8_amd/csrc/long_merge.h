@@ -7,7 +7,11 @@
 // counts) or the piece start, and likewise walking right from y with left
 // operands.  Then no merge ranked below r can ever change x or y: any merge
 // touching the walked stretch first has the rank of a pair on it or of a
-// barrier token's operand, both above r.  So textbook BPE merges (x, y)
+// barrier token's operand, both above r.  A walk also ends sheltered once the
+// stretch it has crossed, x included, is longer than the longest token: no
+// pair on it ranks below r, so a change could only enter at its far end and
+// reach x as one token spanning the whole stretch (each merge on the way
+// joins the changed token with the next symbol), and no token is that long.  So textbook BPE merges (x, y)
 // before anything changes them, and merging it now cannot change the result
 // (GraphTok, section 4 "Warp-cooperative BPE": lowest rank wins, leftmost on
 // equal rank; TokTier, "Exact GPU Tokenization": all leftmost non-overlapping
@@ -75,12 +79,22 @@ struct WaveGroup {
   }
 };
 
-// Shelter walks of the pair k (symbols k, k + 1) of rank r among n symbols.
-__device__ inline bool sheltered(const uint32_t* rk, const uint2* mm, uint32_t n, uint32_t k, uint32_t r) {
+// A symbol's entry in mm: its token's lowest ranks as right and as left
+// operand, packed as in Tables::tok_min, and its first byte's offset in the
+// piece.
+__device__ inline uint32_t low_right(uint2 v, uint32_t shift) { return (v.x >> 16) << shift; }
+__device__ inline uint32_t low_left(uint2 v, uint32_t shift) { return (v.x & 0xFFFFu) << shift; }
+
+// Shelter walks of the pair k (symbols k, k + 1) of rank r among n symbols;
+// maxlen: bytes of the longest token.
+__device__ inline bool sheltered(const uint32_t* rk, const uint2* mm, uint32_t n, uint32_t k, uint32_t r,
+                                 uint32_t shift, uint32_t maxlen) {
   bool left = false;
   uint32_t i = k;
+  const uint32_t end_x = mm[k + 1].y;  // the byte after x
   for (uint32_t s = 0; s <= kWalkMax; ++s) {
-    if (mm[i].x > r || i == 0) {
+    const uint2 v = mm[i];
+    if (low_right(v, shift) > r || i == 0 || end_x - v.y > maxlen) {  // symbols i .. k span more than a token
       left = true;
       break;
     }
@@ -89,8 +103,10 @@ __device__ inline bool sheltered(const uint32_t* rk, const uint2* mm, uint32_t n
   }
   if (!left) return false;
   i = k + 1;
+  const uint32_t start_y = mm[k + 1].y;
   for (uint32_t s = 0; s <= kWalkMax; ++s) {
-    if (mm[i].y > r || i == n - 1) return true;
+    const uint2 v = mm[i];
+    if (low_left(v, shift) > r || i == n - 1 || v.y - start_y > maxlen) return true;  // k + 1 .. i - 1 do
     if (rank_of(rk[i]) <= r) return false;
     ++i;
   }
@@ -100,8 +116,8 @@ __device__ inline bool sheltered(const uint32_t* rk, const uint2* mm, uint32_t n
 // BPE of the n-symbol piece held in sym / rk / mm (LDS or global memory), in
 // rounds; returns the final symbol count.  Called by every thread with
 // uniform arguments.  sym[i]: token i; rk[i]: rank of the pair (i, i + 1)
-// (kNoRank for the last); mm[i]: the token's lowest ranks as right operand
-// (x) and as left operand (y).
+// (kNoRank for the last); mm[i]: the token's lowest ranks as right and left
+// operand (packed) and its first byte's offset in the piece.
 template <typename G, int E>
 __device__ __forceinline__ uint32_t merge_piece(const Tables& T, uint32_t* sym, uint32_t* rk, uint2* mm,
                                                 uint32_t n, uint32_t low, uint32_t* s_scan) {
@@ -121,7 +137,7 @@ __device__ __forceinline__ uint32_t merge_piece(const Tables& T, uint32_t* sym, 
         take[e] = false;
         if (k < pairs) {
           const uint32_t r = rank_of(rk[k]);
-          take[e] = r != kNoRank && (r == low || sheltered(rk, mm, n, k, r));
+          take[e] = r != kNoRank && (r == low || sheltered(rk, mm, n, k, r, T.min_shift, T.max_tok_len));
           if (!take[e]) last_stop = k + 1;
         }
       }
@@ -163,7 +179,7 @@ __device__ __forceinline__ uint32_t merge_piece(const Tables& T, uint32_t* sym, 
           alive[e] = !pc;
           if (alive[e]) {
             ns[e] = ch ? 256u + rank_of(v) : sym[i];
-            nm[e] = ch ? token_mins(T.tok_min, T.min_shift, ns[e]) : mm[i];
+            nm[e] = ch ? make_uint2(T.tok_min[ns[e]], mm[i].y) : mm[i];  // a merged token starts where its left part did
             const uint32_t kn = ch ? i + 2 : i + 1;
             nr[e] = kNoRank;
             if (kn < n) {
@@ -228,7 +244,7 @@ __device__ __forceinline__ uint32_t long_piece(const uint8_t* __restrict__ text,
     sym[i] = a;
     const uint32_t r = i + 1 < len ? T.pair_rank[(a << 8) | text[s + i + 1]] : kNoRank;
     rk[i] = r;
-    mm[i] = token_mins(T.tok_min, T.min_shift, a);
+    mm[i] = make_uint2(T.tok_min[a], i);
     low = min(low, r);
   }
   uint32_t all = 0;

@@ -111,6 +111,7 @@ struct Tables {
   const uint32_t* tok_min;      // per token: lowest rank of a merge taking it as right operand (x), as left (y),
                                 // 16 bits each (x high), shifted right by min_shift; 0xFFFF: none
   uint32_t min_shift;
+  uint32_t max_tok_len;         // bytes of the longest token
 };
 
 // Per-call device buffers.
