@@ -180,7 +180,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
   for (uint32_t i = 0; i < 256; ++i) tok[i] = {(uint8_t)i};
   // byte pairs that some token spans, one bit per (first << 8 | second): the
   // junction of each merge (the pairs inside its operands are set already)
-  std::vector<uint32_t> join(kJoinWords, 0u);
+  std::vector<uint32_t> join(kUnitTabWords, 0u);  // the unit table: pairs, two-byte tokens, three-byte strings
   for (size_t r = 0; r < n_merges; ++r) {
     const uint32_t a = merges[2 * r], bb = merges[2 * r + 1];
     if (a >= 256 + r || bb >= 256 + r) return TOK_E_BADMERGES;
@@ -204,6 +204,19 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
     join[jp >> 5] |= 1u << (jp & 31u);
     tok[256 + r] = tok[a];
     tok[256 + r].insert(tok[256 + r].end(), tok[bb].begin(), tok[bb].end());
+  }
+  // the rest of the unit table: two-byte tokens, and every three-byte string
+  // inside a token (hashed)
+  for (size_t t = 256; t < tok.size(); ++t) {
+    const std::vector<uint8_t>& b = tok[t];
+    if (b.size() == 2) {
+      const uint32_t k = ((uint32_t)b[0] << 8) | b[1];
+      join[kJoinWords + (k >> 5)] |= 1u << (k & 31u);
+    }
+    for (size_t i = 0; i + 2 < b.size(); ++i) {
+      const uint32_t h = tri_slot((uint32_t)b[i] | (uint32_t)b[i + 1] << 8 | (uint32_t)b[i + 2] << 16);
+      join[2 * kJoinWords + (h >> 5)] |= 1u << (h & 31u);
+    }
   }
   // the same ranks, 16 bits each in one word per token: the rank shifted
   // right so that every rank fits below 0xFFFF (which stands for none).  A
@@ -262,7 +275,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
         hipMalloc((void**)&ctx->d_pair_rank, pr.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_tok_len, ctx->tok_len.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_tok_min, tmin16.size() * 4) != hipSuccess ||
-        hipMalloc((void**)&ctx->d_joinable, join.size() * 4) != hipSuccess ||
+        hipMalloc((void**)&ctx->d_unit_tab, join.size() * 4) != hipSuccess ||
         hipMalloc((void**)&ctx->d_hand_tick, kHandTickWords * 8) != hipSuccess ||
         hipHostMalloc((void**)&ctx->h_ctr, sizeof(Counters), hipHostMallocMapped) != hipSuccess) {
       rc = TOK_E_NOMEM;
@@ -273,7 +286,7 @@ int tok_load(const uint32_t* merges, size_t n_merges, int pattern, const tok_opt
         hipMemcpy(ctx->d_tok_len, ctx->tok_len.data(), ctx->tok_len.size() * 4, hipMemcpyHostToDevice) !=
             hipSuccess ||
         hipMemcpy(ctx->d_tok_min, tmin16.data(), tmin16.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(ctx->d_joinable, join.data(), join.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(ctx->d_unit_tab, join.data(), join.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemset(ctx->d_hand_tick, 0, kHandTickWords * 8) != hipSuccess ||
         hipHostGetDevicePointer((void**)&ctx->d_ctr, ctx->h_ctr, 0) != hipSuccess)
       break;

@@ -114,7 +114,7 @@ struct tok_ctx {
   uint32_t* d_tok_len = nullptr;
   uint32_t* d_tok_min = nullptr;  // per token: (x >> min_shift) << 16 | (y >> min_shift), see Tables
   uint32_t min_shift = 0;
-  uint32_t* d_joinable = nullptr;  // kJoinWords: bit (a << 8 | b) set iff some token spans the byte pair a b
+  uint32_t* d_unit_tab = nullptr;  // kUnitTabWords: where no token can span a byte boundary (tok_internal.h)
   uint64_t* d_hand_tick = nullptr;  // Bufs::hand_tick, for the context's life (never cleared after load)
 
   // every token's bytes on the device, made on first use (device repair)
@@ -495,7 +495,7 @@ struct tok_ctx {
     }
     // the pre-tokenization alone (out_flags) gives piece starts; the pipeline
     // also starts a unit of BPE between bytes that no token spans
-    launch_pretok(text, n, doc_off, n_docs, pattern, out_flags ? nullptr : d_joinable, bb, s, e0(0), e1(0));
+    launch_pretok(text, n, doc_off, n_docs, pattern, out_flags ? nullptr : d_unit_tab, bb, s, e0(0), e1(0));
     if (out_flags) return;
     launch_pieces(text, n, t, bb, doc_off, n_docs, out_off, s, e0(1), e1(1));
     launch_assemble(n, bb, out, spans, d_tok_len, out_cap, doc_off, n_docs, out_off, s, e0(2), e1(2));
@@ -616,7 +616,7 @@ struct tok_ctx {
     dfree(d_long_slots);
     dfree(d_tok_len);
     dfree(d_tok_min);
-    dfree(d_joinable);
+    dfree(d_unit_tab);
     dfree(d_hand_tick);
     free_lit_tables();
     dfree(d_tok_bytes);

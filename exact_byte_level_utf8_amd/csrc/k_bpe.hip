@@ -4,8 +4,8 @@
 // piece the merges are ordered: while some adjacent pair has a rank, the
 // lowest rank wins, the leftmost pair on equal rank, and the pair becomes ID
 // 256 + rank (GraphTok, section 4 "Warp-cooperative BPE").  The flag words
-// this stage reads also cut pieces where no token spans the byte pair
-// (pair_joinable): the parts are independent units of BPE, and below
+// this stage reads also cut pieces where no token can span a byte boundary
+// (no_token_spans): the parts are independent units of BPE, and below
 // "piece" means such a unit.
 //
 // piece_kernel: one workgroup per 1 KiB of piece starts, in three phases.

@@ -129,7 +129,7 @@ __device__ inline bool is_cont(uint32_t byte) { return (byte & 0xC0u) == 0x80u; 
 template <int PATTERN, int NT>
 __global__ void __launch_bounds__(NT, NT >= 512 ? 8 : 6)
 pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off,
-              uint32_t n_docs, const uint32_t* __restrict__ joinable, Bufs B) {
+              uint32_t n_docs, const uint32_t* __restrict__ unit_tab, Bufs B) {
   constexpr int kRounds = kPT / NT;                    // tile positions per thread
   constexpr int kPer = kRounds;                        // consecutive positions per thread in the aggregate pass
   static_assert(kPer == 2 || kPer == 4, "aggregate states are packed as 2 or 4 bytes per thread");
@@ -449,13 +449,12 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
                                    : piece_start_llama3(c, p[0], p[1], p[2], p[3], n1, agg & 3u, (agg >> 2) & 1u,
                                                         (agg >> 3) & 1u);
     bool st = (c & kILead) && rule;
-    if (joinable) {  // a unit of BPE also starts where no token spans the byte pair
-      const uint32_t g = (uint32_t)(k + kGuard) - 1u;
-      const uint32_t two = lds_word(s_raw32, g), out = lds_word(s_fl32, g);
+    if (unit_tab) {  // a unit of BPE also starts where no token can span the boundary
+      const uint32_t g = (uint32_t)(k + kGuard) - 2u;
+      const uint32_t four = lds_word(s_raw32, g), out = lds_word(s_fl32, g + 1u);  // bytes i - 2 .. i + 1
       // (ASCII pairs are left alone: a cut is never required, and byte-level
       // vocabularies join nearly every ASCII pair)
-      if (!((out | (out >> 8)) & kBOut) && (two & 0x8080u))
-        st = st || !pair_joinable(joinable, two & 0xFFu, (two >> 8) & 0xFFu);
+      if (!((out | (out >> 8)) & kBOut) && (four & 0x808000u)) st = st || no_token_spans(unit_tab, four);
     }
     // this wave holds 64 consecutive positions: four flag words
     const uint64_t m = __ballot(st);
@@ -470,24 +469,24 @@ pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __re
 }  // namespace
 
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
-                   int pattern, const uint32_t* joinable, Bufs b, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                   int pattern, const uint32_t* unit_tab, Bufs b, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const uint32_t tiles = (uint32_t)((n + kPretokTile - 1) / kPretokTile);
   if (!tiles) return;
   // up to one tile per workgroup slot of the device, 8 waves per tile; larger
   // inputs use 4-wave workgroups, which pack the CUs better
   const bool small = tiles <= (uint32_t)kPretokSmallGrid;
   if (pattern == 2) {  // the case-splitting family: segments between synchronizing cuts
-    launch_pretok_case(text, n, doc_off, n_docs, joinable, b, s, e0, e1);
+    launch_pretok_case(text, n, doc_off, n_docs, unit_tab, b, s, e0, e1);
   } else if (pattern == 0) {
     if (small)
-      launch_on(pretok_kernel<0, 512>, dim3(tiles), dim3(512), s, e0, e1, text, n, doc_off, n_docs, joinable, b);
+      launch_on(pretok_kernel<0, 512>, dim3(tiles), dim3(512), s, e0, e1, text, n, doc_off, n_docs, unit_tab, b);
     else
-      launch_on(pretok_kernel<0, 256>, dim3(tiles), dim3(256), s, e0, e1, text, n, doc_off, n_docs, joinable, b);
+      launch_on(pretok_kernel<0, 256>, dim3(tiles), dim3(256), s, e0, e1, text, n, doc_off, n_docs, unit_tab, b);
   } else {
     if (small)
-      launch_on(pretok_kernel<1, 512>, dim3(tiles), dim3(512), s, e0, e1, text, n, doc_off, n_docs, joinable, b);
+      launch_on(pretok_kernel<1, 512>, dim3(tiles), dim3(512), s, e0, e1, text, n, doc_off, n_docs, unit_tab, b);
     else
-      launch_on(pretok_kernel<1, 256>, dim3(tiles), dim3(256), s, e0, e1, text, n, doc_off, n_docs, joinable, b);
+      launch_on(pretok_kernel<1, 256>, dim3(tiles), dim3(256), s, e0, e1, text, n, doc_off, n_docs, unit_tab, b);
   }
 }
 

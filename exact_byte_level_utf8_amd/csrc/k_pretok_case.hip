@@ -314,7 +314,7 @@ __device__ inline void publish(const Bufs& B, uint32_t tile, uint32_t tag, uint6
 
 __global__ void __launch_bounds__(kCaseNT)
 pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off,
-                   uint32_t n_docs, const uint32_t* __restrict__ joinable, Bufs B) {
+                   uint32_t n_docs, const uint32_t* __restrict__ unit_tab, Bufs B) {
   __shared__ CaseShared sh;
   CaseShared* S = &sh;
   if (B.n_docs_dev) n_docs = *B.n_docs_dev;
@@ -728,10 +728,12 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
     if ((int64_t)first_cut == t1 && tid == 0) publish(B, tile, tag, in_exit);
   }
 
-  if (joinable) {  // a unit of BPE also starts where no token spans the byte pair
+  if (unit_tab) {  // a unit of BPE also starts where no token can span the boundary
     for (int64_t p = max(t0, (int64_t)1) + tid; p < t1; p += kCaseNT) {
       const int i = (int)(p - lo);
-      if (((S->raw[i - 1] | S->raw[i]) & 0x80u) && !pair_joinable(joinable, S->raw[i - 1], S->raw[i]))
+      const uint32_t four = (uint32_t)S->raw[i - 2] | (uint32_t)S->raw[i - 1] << 8 | (uint32_t)S->raw[i] << 16 |
+                            (uint32_t)S->raw[i + 1] << 24;  // bytes past either end of the text are 0
+      if ((four & 0x808000u) && no_token_spans(unit_tab, four))
         atomicOr(&S->start[(p - t0) >> 5], 1u << ((p - t0) & 31));
     }
   }
@@ -745,10 +747,10 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
 }  // namespace
 
 void launch_pretok_case(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
-                        const uint32_t* joinable, Bufs b, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                        const uint32_t* unit_tab, Bufs b, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const uint32_t tiles = (uint32_t)((n + kCaseTile - 1) / kCaseTile);
   if (!tiles) return;
-  launch_on(pretok_case_kernel, dim3(tiles), dim3(kCaseNT), s, e0, e1, text, n, doc_off, n_docs, joinable, b);
+  launch_on(pretok_case_kernel, dim3(tiles), dim3(kCaseNT), s, e0, e1, text, n, doc_off, n_docs, unit_tab, b);
 }
 
 }  // namespace tok

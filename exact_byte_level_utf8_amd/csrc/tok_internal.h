@@ -40,18 +40,42 @@ constexpr int kHandTickWords = 32;
 constexpr int kPieceTile = 1024;     // bytes per workgroup of the piece pass
 constexpr uint32_t kPieceSmallGrid = 1024;  // piece-pass grids up to this use 512-thread workgroups
 constexpr uint32_t kNoRank = 0xFFFFFFFFu;
-constexpr int kJoinWords = 65536 / 32;  // byte-pair bits: some token spans the pair
 
-// Whether some token spans the byte pair (a, b).  A merge joins two tokens,
-// so a token that spans a byte boundary has the boundary's two bytes inside
-// it.  Where no token spans the pair, every token sequence BPE passes through
-// has a boundary there, the pair straddling it never has a rank, and the
-// rounds on each side are those of each side alone: BPE of the piece is the
-// BPE of the bytes before the boundary followed by that of the bytes from it.
-// So a piece splits there into units of BPE that merge independently.
-__device__ inline bool pair_joinable(const uint32_t* __restrict__ joinable, uint32_t a, uint32_t b) {
-  const uint32_t k = (a << 8) | b;
-  return (joinable[k >> 5] >> (k & 31u)) & 1u;
+// Units of BPE.  A merge joins two tokens, so a token that spans a byte
+// boundary has the boundary's two bytes inside it.  Where no token can span
+// the boundary, every token sequence BPE passes through has a boundary
+// there, the pair straddling it never has a rank, and the rounds on each
+// side are those of each side alone: BPE of the piece is the BPE of the bytes
+// before the boundary followed by that of the bytes from it.  So a piece
+// splits there into units of BPE that merge independently.
+//
+// The unit table (kUnitTabWords words, built at load) decides it from the
+// four bytes around the boundary before byte i: bits [0, 65536) are set for
+// every byte pair (a, b) some token holds; bits [65536, 131072) for every
+// two-byte token; then kTriBits bits hold, hashed, every three-byte string
+// inside some token.  A token spanning the boundary is the two bytes i - 1,
+// i alone, or it holds the bytes i - 2 .. i or i - 1 .. i + 1; with none of
+// these in the vocabulary nothing spans it.  A hash collision only keeps a
+// boundary that could have been cut, so the cuts stay exact.
+constexpr int kJoinWords = 65536 / 32;
+constexpr int kTriLog = 20;
+constexpr uint32_t kTriBits = 1u << kTriLog;
+constexpr int kUnitTabWords = 2 * kJoinWords + (int)(kTriBits / 32);
+
+// Bit of the three bytes x, y, z (key x | y << 8 | z << 16) in the table.
+__host__ __device__ inline uint32_t tri_slot(uint32_t key) { return (key * 0x9E3779B1u) >> (32 - kTriLog); }
+
+// w: bytes i - 2, i - 1, i, i + 1 (low to high; bytes past either end of
+// the text are 0, which can only keep a boundary).
+__device__ inline bool no_token_spans(const uint32_t* __restrict__ tab, uint32_t w) {
+  const uint32_t pair = ((w >> 8) & 0xFFu) << 8 | ((w >> 16) & 0xFFu);
+  const uint32_t h1 = tri_slot(w & 0xFFFFFFu), h2 = tri_slot(w >> 8);
+  const uint32_t* tri = tab + 2 * kJoinWords;
+  const uint32_t held = tab[pair >> 5], two = tab[kJoinWords + (pair >> 5)];  // all four reads at once
+  const uint32_t t1 = tri[h1 >> 5], t2 = tri[h2 >> 5];
+  if (!((held >> (pair & 31u)) & 1u)) return true;
+  if ((two >> (pair & 31u)) & 1u) return false;
+  return !((t1 >> (h1 & 31u)) & 1u) && !((t2 >> (h2 & 31u)) & 1u);
 }
 constexpr uint64_t kEmptySlot = ~0ull;
 constexpr uint32_t kBucket = 4;      // hash-table slots probed with one set of loads
@@ -206,16 +230,16 @@ inline void launch_on(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
 // Kernel launchers (defined in the .hip files); e0 / e1: optional events
 // around the stage's kernel.
 void launch_empty_batch(Bufs b, const uint64_t* doc_off, uint32_t n_docs, uint64_t* out_off, hipStream_t s);
-// joinable: nullptr for piece starts only; else the byte-pair bits (bit
-// a << 8 | b set iff some token spans the pair a b), and a flag also marks
-// every byte whose pair with the byte before it no token spans.
+// unit_tab: nullptr for piece starts only; else the unit table, and a flag
+// also marks every byte before which no token can span the boundary (at
+// non-ASCII byte pairs).
 void launch_pretok(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
-                   int pattern, const uint32_t* joinable, Bufs b, hipStream_t s, hipEvent_t e0 = nullptr,
+                   int pattern, const uint32_t* unit_tab, Bufs b, hipStream_t s, hipEvent_t e0 = nullptr,
                    hipEvent_t e1 = nullptr);
 // The case-splitting family's pre-tokenization (k_pretok_case.hip), called by
 // launch_pretok for that pattern.
 void launch_pretok_case(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs,
-                        const uint32_t* joinable, Bufs b, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
+                        const uint32_t* unit_tab, Bufs b, hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, const uint64_t* doc_off,
                    uint32_t n_docs, uint64_t* out_off, hipStream_t s, hipEvent_t e0 = nullptr,
                    hipEvent_t e1 = nullptr);
