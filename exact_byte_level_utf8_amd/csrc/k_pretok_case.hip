@@ -117,7 +117,9 @@ __device__ __forceinline__ uint64_t uni64(uint64_t v) {
 
 struct CaseShared {
   uint8_t raw[kCaseWin + 4];
-  uint16_t rend[kCaseWin];       // at a lead: where its stretch of one kind ends (window index, at most kCaseValid)
+  uint16_t rend[kCaseWin];       // at a lead i: where its stretch of one kind ends (window index, at most
+                                 // kCaseValid) << 2 | the byte length - 1 of the code point before i,
+                                 // and bit 15: i is a cut
   uint8_t ds[kCaseWin];          // a document starts at this byte
   alignas(16) uint8_t stage[kStage + 32];  // 16-byte chunks of the text around one step of a run search
   uint32_t q[kCaseWin];          // info per window byte
@@ -125,9 +127,11 @@ struct CaseShared {
   uint32_t start[kCaseTile / 32];  // piece-start bit per tile byte
   uint32_t job[kJobs];           // a segment's cut; a job that needs the text past the window leaves its cursor here
   uint32_t far[(kJobs + 31) / 32];  // jobs that need the text past the window
+  uint32_t hard[(kJobs + 31) / 32];  // jobs at a piece that starts with a mark (the matcher's)
   uint32_t cmask[kCand][kCaseTile / 32];  // piece starts of each speculative match
   uint32_t cstart[kCand], cexit[kCand], cok[kCand];
   uint32_t red[3 * kCaseNT / kWave];
+  uint32_t act[kScanStages * kScanKinds];  // the forward scan's action per (stage, kind)
   uint64_t stage_base;           // text position of the step's first byte (kNoPos before the first run search)
   uint32_t stage_off;            // its index in stage
   uint32_t nseg, ncand, doc0, bad, first, first_cut, exit, hand, back;
@@ -256,7 +260,7 @@ struct WinAcc {
     }
     return q[i - lo];
   }
-  __device__ __forceinline__ uint64_t run_end(uint64_t i) const { return (uint64_t)(lo + rend[i - lo]); }
+  __device__ __forceinline__ uint64_t run_end(uint64_t i) const { return (uint64_t)(lo + ((rend[i - lo] >> 2) & 0x1FFFu)); }
   __device__ __forceinline__ uint64_t prev_lead(uint64_t i) const {
     int64_t k = (int64_t)i - 1 - lo;
     while (q[k] == kNotLead) --k;
@@ -364,7 +368,11 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
     S->start[i] = 0;
   }
   for (int i = tid; i < kCand * (kCaseTile / 32); i += kCaseNT) S->cmask[i / (kCaseTile / 32)][i % (kCaseTile / 32)] = 0;
-  for (int i = tid; i < (kJobs + 31) / 32; i += kCaseNT) S->far[i] = 0;
+  for (int i = tid; i < (kJobs + 31) / 32; i += kCaseNT) {
+    S->far[i] = 0;
+    S->hard[i] = 0;
+  }
+  for (int i = tid; i < kScanStages * kScanKinds; i += kCaseNT) S->act[i] = scan_action(i / kScanKinds, i % kScanKinds);
   __syncthreads();
   // document starts inside the window
   if (doc_off) {
@@ -378,68 +386,75 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
   }
   __syncthreads();
   // decode every window byte: the code points, then all their class-table
-  // reads at once (one round trip), then the info words
+  // reads at once (one round trip; none in a wave without a non-ASCII
+  // byte), then the info words
   {
     constexpr int kPer = kCaseWin / kCaseNT;
     uint32_t cps[kPer], lens[kPer], low[kPer];
+    bool hi = false, big = false;
 #pragma unroll
     for (int r = 0; r < kPer; ++r) {
       const int i = tid + r * kCaseNT;
       const uint32_t b0 = S->raw[i];
       lens[r] = seq_len(b0);
       cps[r] = decode_cp(b0, S->raw[i + 1], S->raw[i + 2], S->raw[i + 3], lens[r]);
+      hi |= cps[r] >= 0x80u;
+      big |= cps[r] >= (uint32_t)TOK_CLS_LOW;
+      low[r] = 0;
     }
+    if (__ballot(hi)) {
 #pragma unroll
-    for (int r = 0; r < kPer; ++r) low[r] = kCaseLow[min(cps[r], (uint32_t)TOK_CLS_LOW - 1u) >> 1];
+      for (int r = 0; r < kPer; ++r) low[r] = kCaseLow[min(cps[r], (uint32_t)TOK_CLS_LOW - 1u) >> 1];
+    }
+    const bool any_big = __ballot(big) != 0;
 #pragma unroll
     for (int r = 0; r < kPer; ++r) {
       const int i = tid + r * kCaseNT;
       const int64_t p = lo + i;
       const uint32_t b0 = S->raw[i], cp = cps[r];
-      uint32_t v = kQEnd;
-      if (p >= 0 && p < (int64_t)n) {
-        if ((b0 & 0xC0u) == 0x80u) {
-          v = kNotLead;
-        } else {
-          const uint32_t cls = cp < 0x80 ? ascii_case(cp)
-                               : cp < TOK_CLS_LOW ? (low[r] >> (4 * (cp & 1u))) & 15u
-                                                  : case_class(cp);
-          v = make_q(cp, cls, lens[r], fold_code(cp, case_fold_extra(cp)));
-          if (S->ds[i]) v |= kQDocStart;
-        }
-      }
-      S->q[i] = v;
+      uint32_t cls = cp < 0x80 ? ascii_case(cp) : (low[r] >> (4 * (cp & 1u))) & 15u;
+      if (any_big) cls = cp >= (uint32_t)TOK_CLS_LOW ? case_class(cp) : cls;
+      const uint32_t q = make_q(cp, cls, lens[r], fold_code(cp, case_fold_extra(cp))) | (S->ds[i] ? kQDocStart : 0u);
+      S->q[i] = (p < 0 || p >= (int64_t)n) ? kQEnd : (b0 & 0xC0u) == 0x80u ? kNotLead : q;
     }
   }
   // well-formed UTF-8 over the tile's own bytes (Unicode Table 3-7): a lead
   // is ASCII or C2..F4 with the right continuation bytes, all in its
   // document; a continuation byte belongs to a lead at most 3 bytes before
-  // it in the same document
-  for (int64_t p = t0 + tid; p < t1; p += kCaseNT) {
-    const int i = (int)(p - lo);
-    const uint32_t b0 = S->raw[i];
-    bool bad = false;
-    if ((b0 & 0xC0u) == 0x80u) {
-      if (S->ds[i]) {
-        bad = true;
-      } else {
-        int k = 1;
-        while (k <= 3 && (S->raw[i - k] & 0xC0u) == 0x80u && !S->ds[i - k]) ++k;
-        const uint32_t lead = S->raw[i - k];
-        bad = k > 3 || lo + i - k < 0 || (lead & 0xC0u) == 0x80u || lead < 0xC2u || lead > 0xF4u ||
-              (int)seq_len(lead) <= k;
+  // it in the same document.  A wave whose bytes are all ASCII has nothing
+  // to check.
+  {
+    constexpr int kRounds = kCaseTile / kCaseNT;
+    bool hi = false;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) hi |= S->raw[kCaseLeft + r * kCaseNT + tid] >= 0x80u;
+    if (__ballot(hi)) {
+      bool bad = false;
+      auto cont = [](uint32_t b) { return (b & 0xC0u) == 0x80u; };
+#pragma unroll
+      for (int r = 0; r < kRounds; ++r) {
+        const int i = kCaseLeft + r * kCaseNT + tid;
+        const int64_t p = lo + i;
+        const uint32_t b0 = S->raw[i], b1 = S->raw[i + 1], b2 = S->raw[i + 2], b3 = S->raw[i + 3];
+        const uint32_t r1 = S->raw[i - 1], r2 = S->raw[i - 2], r3 = S->raw[i - 3];
+        // a continuation byte: back over continuation bytes of the same
+        // document to the lead
+        const bool c1 = cont(r1) && !S->ds[i - 1], c2 = cont(r2) && !S->ds[i - 2], c3 = cont(r3) && !S->ds[i - 3];
+        const int k = !c1 ? 1 : !c2 ? 2 : !c3 ? 3 : 4;
+        const uint32_t lead = k == 1 ? r1 : k == 2 ? r2 : r3;
+        const bool bad_cont = S->ds[i] || k > 3 || p - k < 0 || cont(lead) || lead < 0xC2u || lead > 0xF4u ||
+                              (int)seq_len(lead) <= k;
+        // a lead: its continuation bytes, in the text and the document, and
+        // the narrower second-byte ranges after E0, ED, F0 and F4
+        const uint32_t len = seq_len(b0);
+        const bool bad_lead = b0 < 0xC2u || b0 > 0xF4u || p + (int64_t)len > (int64_t)n ||
+                              (len > 1 && (!cont(b1) || S->ds[i + 1])) || (len > 2 && (!cont(b2) || S->ds[i + 2])) ||
+                              (len > 3 && (!cont(b3) || S->ds[i + 3])) || (b0 == 0xE0u && b1 < 0xA0u) ||
+                              (b0 == 0xEDu && b1 > 0x9Fu) || (b0 == 0xF0u && b1 < 0x90u) || (b0 == 0xF4u && b1 > 0x8Fu);
+        bad |= p < t1 && (cont(b0) ? bad_cont : b0 >= 0x80u && bad_lead);
       }
-    } else if (b0 >= 0x80u) {
-      const uint32_t len = seq_len(b0);
-      bad = b0 < 0xC2u || b0 > 0xF4u || p + (int64_t)len > (int64_t)n;
-      for (uint32_t k = 1; k < len && !bad; ++k) bad = (S->raw[i + k] & 0xC0u) != 0x80u || S->ds[i + k];
-      if (!bad && len > 2) {
-        const uint32_t b1 = S->raw[i + 1];
-        bad = (b0 == 0xE0u && b1 < 0xA0u) || (b0 == 0xEDu && b1 > 0x9Fu) || (b0 == 0xF0u && b1 < 0x90u) ||
-              (b0 == 0xF4u && b1 > 0x8Fu);
-      }
+      if (bad) S->bad = 1;
     }
-    if (bad) S->bad = 1;
   }
   // at the end, after the last barrier (a barrier waits for every memory
   // operation in flight, and this one is contended): count this workgroup
@@ -476,17 +491,11 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
     const int64_t p = t0 + r * kCaseNT + tid;
     const int i = (int)(p - lo);
     const uint32_t v = S->q[i];
-    bool cut = false;
-    if (p < t1 && v != kNotLead) {
-      cut = p == 0 || (v & kQDocStart);
-      if (!cut) {
-        // the previous lead is at most 3 bytes back in well-formed text; the
-        // bound keeps a malformed halo (reported by its own tile) in the window
-        int k = 1;
-        while (k < i && S->q[i - k] == kNotLead) ++k;
-        cut = sync_at(S->q[i - k], v);
-      }
-    }
+    // the code point before starts 1 to 4 bytes back in well-formed text (in
+    // malformed text, which its own tile reports, any value will do)
+    const uint32_t v1 = S->q[i - 1], v2 = S->q[i - 2], v3 = S->q[i - 3], v4 = S->q[i - 4];
+    const uint32_t prev = v1 != kNotLead ? v1 : v2 != kNotLead ? v2 : v3 != kNotLead ? v3 : v4;
+    const bool cut = p < t1 && v != kNotLead && (p == 0 || (v & kQDocStart) || sync_at(prev, v));
     const uint64_t m = __ballot(cut);
     const uint32_t lane = lane_id();
     const uint32_t w0 = (uint32_t)(r * kCaseNT + (tid - lane)) / 32;
@@ -527,37 +536,38 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
   // where each stretch of one kind ends: a boundary at every code point
   // whose kind differs from the one before it, where a document starts or
   // the text ends, and at the window's decoded end; each thread takes 5
-  // consecutive bytes, and the first boundary after them comes from a suffix
-  // minimum over the workgroup
+  // consecutive bytes (and the 4 before them, for the code point before
+  // each), and the first boundary after them comes from a suffix minimum
+  // over the workgroup
   {
     constexpr int kPer = kCaseWin / kCaseNT;
-    uint32_t bmask = 0;
+    const int i0 = tid * kPer;
+    uint32_t w[kPer + 4];  // info of bytes i0 - 4 .. i0 + kPer - 1
+#pragma unroll
+    for (int j = 0; j < kPer + 4; ++j) w[j] = S->q[max(i0 + j - 4, 0)];
+    uint32_t bmask = 0, plen[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int i = tid * kPer + j;
+      const int i = i0 + j;
+      const uint32_t v = w[j + 4];
+      // the code point before i starts 1 to 4 bytes back in well-formed text
+      const uint32_t back = w[j + 3] != kNotLead ? 1u : w[j + 2] != kNotLead ? 2u : w[j + 1] != kNotLead ? 3u : 4u;
+      const uint32_t prev = back == 1u ? w[j + 3] : back == 2u ? w[j + 2] : back == 3u ? w[j + 1] : w[j];
+      plen[j] = back;
       bool b;
-      if (i >= kCaseValid) {
-        b = i == kCaseValid;
-      } else {
-        const uint32_t v = S->q[i];
-        if (v == kNotLead) {
-          b = false;
-        } else if (i == 0 || (v & (kQDocStart | kQEnd))) {
-          b = true;
-        } else {
-          int k = i - 1;
-          while (k > 0 && S->q[k] == kNotLead) --k;
-          b = kind_of(S->q[k]) != kind_of(v);
-        }
-      }
+      if (i >= kCaseValid) b = i == kCaseValid;
+      else if (v == kNotLead) b = false;
+      else b = i == 0 || (v & (kQDocStart | kQEnd)) || kind_of(prev) != kind_of(v);
       bmask |= (uint32_t)b << j;
     }
-    const uint32_t mine = bmask ? (uint32_t)(tid * kPer + __builtin_ctz(bmask)) : kNone32;
+    const uint32_t mine = bmask ? (uint32_t)(i0 + __builtin_ctz(bmask)) : kNone32;
     uint32_t next = wg_excl_suffix<kCaseNT>(mine, kNone32, MinOp{}, S->red, nullptr);
 #pragma unroll
     for (int j = kPer - 1; j >= 0; --j) {
-      const int i = tid * kPer + j;
-      S->rend[i] = (uint16_t)min(next, (uint32_t)kCaseValid);
+      const int i = i0 + j;
+      const uint32_t ti = (uint32_t)(i - kCaseLeft);  // the tile byte, if in the tile
+      const uint32_t cut = ti < (uint32_t)kCaseTile ? (S->cut[ti >> 5] >> (ti & 31)) & 1u : 0u;
+      S->rend[i] = (uint16_t)(cut << 15 | min(next, (uint32_t)kCaseValid) << 2 | (plen[j] - 1u));
       if ((bmask >> j) & 1u) next = (uint32_t)i;
     }
   }
@@ -565,12 +575,73 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
   const WinAcc wacc{S->q, S->rend, lo, n, (uint64_t)(lo + kCaseValid), false};
 
   // every job, one per thread: a segment from its cut, or a speculative
-  // start, matched until the next cut or the tile's end
+  // start, matched until the next cut or the tile's end by the forward scan
+  // (seg_rules.h), one step per iteration; a lane that finishes a job takes
+  // its next one at once
   const uint32_t nseg = S->nseg, njobs = nseg + S->ncand;
+  auto tile_bit = [&](uint32_t* words, uint32_t w) {  // w: a window index in the tile
+    atomicOr(&words[(w - kCaseLeft) >> 5], 1u << ((w - kCaseLeft) & 31));
+  };
+  {
+    const uint32_t tw1 = (uint32_t)(t1 - lo);                  // the tile's end as a window index
+    // the kind past the decoded window: more text, or its end
+    const uint32_t kpast = lo + kCaseValid < (int64_t)n ? (uint32_t)kKFar : (uint32_t)kKEnd;
+    uint32_t jb = tid;
+    uint32_t* mark = S->start;
+    uint32_t js = 0;  // the job's first byte
+    Scan<uint32_t> sc{0u, 0u, 0u, 0u, kStStart, 0u};
+    auto open = [&]() {
+      const bool cand = jb >= nseg;
+      js = (uint32_t)((int64_t)(cand ? S->cstart[jb - nseg] : S->job[jb]) - lo);
+      mark = cand ? S->cmask[jb - nseg] : S->start;
+      sc = Scan<uint32_t>{js, js, 0u, 0u, kStStart, 0u};
+    };
+    if (jb < njobs) open();
+    while (jb < njobs) {
+      const uint32_t x = sc.x;
+      const uint32_t xi = min(x, (uint32_t)kCaseValid - 1u);
+      const uint32_t v = S->q[xi];
+      const uint32_t rr = S->rend[xi];
+      const uint32_t kin = ((v & kQEnd) || (x > sc.p && (v & kQDocStart))) ? (uint32_t)kKEnd : kind_of(v);
+      const uint32_t k = x >= (uint32_t)kCaseValid ? kpast : kin;
+      const uint32_t act = S->act[sc.st * kScanKinds + k];
+      // at a piece's first code point: the job ends at the tile's end or at
+      // another cut; else the piece starts here
+      const bool at_start = sc.st == kStStart;
+      const bool seg_end = at_start && (x >= tw1 || ((rr >> 15) && x != js));
+      if (at_start && !seg_end) tile_bit(mark, x);
+      sc.sp = at_start ? (uint32_t)((v & kQSpace) != 0) : sc.sp;
+      const uint32_t res = scan_apply(sc, act, v, k, (rr >> 2) & 0x1FFFu, x - 1u - (rr & 3u));
+      if (!seg_end && res < kScanFar) {
+        const bool piece = res == kScanPiece;
+        const uint32_t e = sc.x > sc.p ? sc.x : sc.p + 1u;  // a piece always advances; the guard keeps the loop finite regardless
+        sc.x = piece ? e : sc.x;
+        sc.p = piece ? e : sc.p;
+        sc.st = piece ? (uint32_t)kStStart : sc.st;
+        continue;
+      }
+      const bool cand = jb >= nseg;
+      if (seg_end) {
+        if (cand) S->cexit[jb - nseg] = (uint32_t)(lo + x);
+        else if (x >= tw1) S->exit = (uint32_t)(lo + x);
+      } else {  // the matcher's (a mark) or the workgroup's (the text past the window), from this piece
+        S->job[jb] = (uint32_t)(lo + sc.p);
+        if (res == kScanHard) atomicOr(&S->hard[jb >> 5], 1u << (jb & 31));
+        else if (cand) S->cok[jb - nseg] = 0;  // a speculative match that needs more is dropped
+        else atomicOr(&S->far[jb >> 5], 1u << (jb & 31));
+      }
+      jb += kCaseNT;
+      if (jb < njobs) open();
+    }
+  }
+  __syncthreads();
+
+  // jobs at a piece that starts with a mark: the matcher, one thread each
   for (uint32_t jb = tid; jb < njobs; jb += kCaseNT) {
+    if (!((S->hard[jb >> 5] >> (jb & 31)) & 1u)) continue;
     const bool cand = jb >= nseg;
     const uint32_t c = jb - nseg;
-    uint64_t p = cand ? S->cstart[c] : S->job[jb];
+    uint64_t p = S->job[jb];
     uint32_t* mark = cand ? S->cmask[c] : S->start;
     for (;;) {
       atomicOr(&mark[(p - t0) >> 5], 1u << ((p - t0) & 31));

@@ -85,7 +85,8 @@ struct WinAcc {
 // The case-splitting family the way the kernel does it, tile by tile (1 KiB
 // tiles, a window of 16 bytes before and 236 valid bytes after each).  A
 // tile matches the segments that start at its cuts, each until the cursor
-// reaches another cut or the tile's end, reading only its window; a match
+// reaches another cut or the tile's end, reading only its window (by the
+// forward scan, with the matcher from a piece that starts with a mark); a match
 // that needs more is finished by the unbounded matcher (the kernel's
 // workgroup-wide one).  The cursor past the tile's end (the first piece
 // start at or after it) goes to the next tile, which continues the segment
@@ -156,6 +157,48 @@ int case_pieces(const uint8_t* s, size_t n, const std::vector<char>& docstart, s
         if (p >= t1 || cut[p]) return p;
       }
     };
+    // the kernel's per-thread match: the forward scan (seg::scan_step), one
+    // code point or one stretch of one kind per step; from a piece that
+    // starts with a mark the matcher takes the rest of the segment
+    auto walk_scan = [&](uint64_t p, std::vector<char>& mark, bool& far) -> uint64_t {
+      far = false;
+      const uint64_t wend = win.wend;
+      if (p >= t0 && p < t1) mark[p - t0] = 1;
+      seg::Scan<uint64_t> sc{p, p, 0, 0, seg::kStStart, 0};
+      for (;;) {
+        const uint64_t x = sc.x;
+        uint32_t v = 0, k;
+        uint64_t r = x, pl = x;
+        if (x >= n) {
+          k = seg::kKEnd;
+        } else if (x >= wend) {
+          k = seg::kKFar;
+        } else {
+          v = q[x];
+          k = ((v & seg::kQEnd) || (x > sc.p && (v & seg::kQDocStart))) ? (uint32_t)seg::kKEnd : seg::kind_of(v);
+          r = std::min<uint64_t>(rend[x], wend);
+          if (x > 0) {
+            pl = x - 1;
+            while (!(q[pl] & seg::kQLead)) --pl;
+          }
+        }
+        const uint32_t res = seg::scan_step(sc, v, k, r, pl);
+        if (res == seg::kScanGo) continue;
+        if (res == seg::kScanFar) {
+          far = true;
+          return sc.p;
+        }
+        if (res == seg::kScanHard) {
+          WinAcc w = win;
+          return walk(sc.p, w, mark, far);
+        }
+        const uint64_t e = sc.x;
+        if (e <= sc.p) return seg::kNoPos - 1;  // no progress: a scan bug
+        if (e >= t1 || cut[e]) return e;
+        mark[e - t0] = 1;
+        sc = seg::Scan<uint64_t>{e, e, 0, 0, seg::kStStart, 0};
+      }
+    };
     struct Unbounded {  // the unbounded matcher behind the WinAcc interface
       const HostAcc* f;
       mutable bool far = false;
@@ -166,8 +209,7 @@ int case_pieces(const uint8_t* s, size_t n, const std::vector<char>& docstart, s
     std::vector<char> tmark(t1 - t0, 0);
     auto walk_any = [&](uint64_t p, std::vector<char>& mark) -> uint64_t {
       bool far = false;
-      WinAcc w = win;
-      uint64_t r = walk(p, w, mark, far);
+      uint64_t r = walk_scan(p, mark, far);
       if (r == seg::kNoPos - 1) return r;
       if (far) r = walk(r, unb, mark, far);
       return r;
@@ -189,8 +231,7 @@ int case_pieces(const uint8_t* s, size_t n, const std::vector<char>& docstart, s
         if (!(q[j] & seg::kQLead)) continue;
         std::vector<char> mk(t1 - t0, 0);
         bool far = false;
-        WinAcc w = win;
-        const uint64_t r = walk(j, w, mk, far);
+        const uint64_t r = walk_scan(j, mk, far);
         if (r == seg::kNoPos - 1) return 2;
         if (far) continue;  // a candidate that needs the text past the window is dropped
         cmark.push_back(mk);

@@ -65,13 +65,11 @@ TOK_HD inline bool is_prefix(uint32_t q) { return !(q & kQCrlf) && sub_of(q) >= 
 
 // Letter-case class of an ASCII code point (b < 0x80) without the table:
 // A-Z upper, a-z lower, 0-9 numbers, TAB..CR and space whitespace, the rest
-// other (the table's values there; a test checks all 128).
+// other (the table's values there; a test checks all 128).  Selects only.
 TOK_HD inline uint32_t ascii_case(uint32_t b) {
-  const uint32_t l = b | 0x20u;
-  if (l - 'a' < 26u) return b < 'a' ? kSU : kSD;
-  if (b - '0' < 10u) return kSN;
-  if (b - 9u < 5u || b == 0x20u) return kSW;
-  return kSO;
+  const bool letter = (b | 0x20u) - 'a' < 26u, digit = b - '0' < 10u, ws = b - 9u < 5u || b == 0x20u;
+  const uint32_t other = digit ? (uint32_t)kSN : ws ? (uint32_t)kSW : (uint32_t)kSO;
+  return letter ? (b < 'a' ? (uint32_t)kSU : (uint32_t)kSD) : other;
 }
 
 // Info word of a decoded code point.
@@ -84,22 +82,25 @@ TOK_HD inline uint32_t make_q(uint32_t cp, uint32_t sub, uint32_t len, uint32_t 
   return q;
 }
 
+// Contraction-letter codes of a..p and q..z as nibbles.
+constexpr uint64_t contraction_nibbles(char first, char last) {
+  uint64_t v = 0;
+  for (char ch = first; ch <= last; ++ch) {
+    const uint64_t code = ch == 's' ? kFS : ch == 't' ? kFT : ch == 'r' ? kFR : ch == 'e' ? kFE
+                        : ch == 'v' ? kFV : ch == 'm' ? kFM : ch == 'l' ? kFL : ch == 'd' ? kFD : 0;
+    v |= code << (4 * (ch - first));
+  }
+  return v;
+}
+constexpr uint64_t kFoldLo = contraction_nibbles('a', 'p'), kFoldHi = contraction_nibbles('q', 'z');
+
 // Contraction letter of a code point under simple case folding (ASCII letters
 // either case; fold_extra: the code for a non-ASCII code point that folds to
-// one of them, else 0).
+// one of them, else 0).  Selects only.
 TOK_HD inline uint32_t fold_code(uint32_t cp, uint32_t fold_extra) {
-  if (cp >= 0x80) return fold_extra;
-  switch (cp | 0x20u) {
-    case 's': return kFS;
-    case 't': return kFT;
-    case 'r': return kFR;
-    case 'e': return kFE;
-    case 'v': return kFV;
-    case 'm': return kFM;
-    case 'l': return kFL;
-    case 'd': return kFD;
-    default: return 0;
-  }
+  const uint32_t t = (cp | 0x20u) - 'a';
+  const uint32_t ascii = (uint32_t)((t < 16u ? kFoldLo >> (4 * (t & 15u)) : kFoldHi >> (4 * ((t - 16u) & 15u))) & 15u);
+  return cp >= 0x80 ? fold_extra : t < 26u ? ascii : 0u;
 }
 
 // Kinds of code point for the matcher's runs: the letter-case class, with
@@ -244,6 +245,203 @@ struct Matcher {
     return w.last != kNoPos && w.last > p ? w.last : w.stop;
   }
 };
+
+// The same matches as one forward scan, for a matcher that runs in lockstep
+// with others (a wave's lanes): each step reads one code point (or crosses
+// one stretch of one kind) and moves a small state machine, so every lane
+// does the same work per step whatever alternative its piece takes.  The
+// pattern's loops never need to look back, except for two things the scan
+// carries along: the end of the last letter in both H and T (where H* T+
+// falls back to when T+ finds nothing after H*), and the end of the last
+// CR/LF of a whitespace run.  A piece that starts with a mark (a prefix char
+// and a letter at once) is left to Matcher.
+enum : uint32_t { kKEnd = 8, kKFar = 9 };  // kinds past kind_of's: no code point; past the readable text
+enum : uint32_t {
+  kStStart,  // at the piece's first code point
+  kStPreO,   // after a prefix char that is an other char
+  kStPreW,   // after a prefix char that is whitespace (sp: U+0020)
+  kStH,      // H* (a: end of the last code point in H and T, or none)
+  kStT,      // T+
+  kStSuf,    // the contraction suffix at e: its apostrophe
+  kStSuf1,   // its first letter
+  kStSuf2,   // its second letter (a: the first one's code)
+  kStOM,     // other chars and marks
+  kStCrlf,   // CR/LF after them
+  kStW,      // whitespace (a: end of the last CR/LF, or none)
+  kStDig,    // digits (a: how many so far)
+};
+enum : uint32_t { kScanGo, kScanPiece, kScanFar, kScanHard };
+
+template <typename P>
+struct Scan {
+  P x;          // the code point the next step reads; after kScanPiece, the piece's end
+  P p;          // the piece's first byte
+  P a;          // per stage, as above
+  P e;          // a letter piece's end before its suffix
+  uint32_t st;  // stage
+  uint32_t sp;  // the piece's first code point is U+0020
+};
+
+// A step as an action word for each (stage, kind): the next stage, how the
+// cursor moves, how the stage's position a changes, the outcome, and a few
+// cases that look at more than the kind (the apostrophe, the contraction
+// letters, the digit count, the ends of letter and whitespace runs).  A
+// stage that a step enters takes the stretch at the cursor at once when it
+// can, and a run that ends checks the suffix's apostrophe at its end when
+// that is where the cursor is, so a typical piece takes three steps.
+enum : uint32_t {
+  kAxKeep = 0u << 4, kAxLen = 1u << 4, kAxRun = 2u << 4, kAxE = 3u << 4,       // x stays, x += len, x = r, x = e
+  kAaKeep = 0u << 6, kAaNone = 1u << 6, kAaRun = 2u << 6, kAaOne = 3u << 6,    // a stays, none, r, 1
+  kArGo = 0u << 8, kArPiece = 1u << 8, kArFar = 2u << 8, kArHard = 3u << 8,    // the outcome
+  kAfSpO = 1u << 10,   // PreW before an other char: other chars after a space, else the piece ends
+  kAfExit = 1u << 11,  // end of H* or T+ (e = a if set, else x), then the suffix from e
+  kAfApos = 1u << 12,  // the suffix's apostrophe, or the piece ends at e
+  kAfSuf1 = 1u << 13,  // the suffix's first letter
+  kAfSuf2 = 1u << 14,  // its second letter
+  kAfWEnd = 1u << 15,  // end of a whitespace run
+  kAfDig = 1u << 16,   // one more digit, if fewer than three so far
+};
+constexpr int kScanStages = 12, kScanKinds = 16;  // action table: stage * kScanKinds + kind
+
+TOK_HD constexpr TOK_SEG_INLINE uint32_t scan_action(uint32_t st, uint32_t k) {
+  if (k == kKFar) return kArFar;
+  if (k > kKFar) return kArHard;  // no such kind
+  // entering a letter piece at the cursor: H* takes U, C and M (C and M
+  // are in T as well); a lower-case letter starts T+
+  const uint32_t letter = (k == kSU)                ? (kStH | kAxRun | kAaNone)
+                          : (k == kSC || k == kSM) ? (kStH | kAxRun | kAaRun)
+                          : (k == kSD)             ? (kStT | kAxRun | kAaNone)
+                                                   : 0u;
+  switch (st) {
+    case kStStart:
+      if (k == kSM) return kArHard;  // a mark is a prefix char and a letter: the matcher's
+      if (letter) return letter;
+      if (k == kSN) return kStDig | kAxLen | kAaOne;
+      if (k == kSO) return kStPreO | kAxLen;
+      if (k == kSW) return kStPreW | kAxLen;
+      if (k == kKCrlf) return kStW | kAxRun | kAaRun;
+      return kArHard;  // no code point
+    case kStPreO:  // a letter piece with the prefix, else other chars from the piece's start
+      if (letter) return letter;
+      if (k == kSO) return kStOM | kAxRun;
+      if (k == kKCrlf) return kStCrlf | kAxRun;
+      return kArPiece;
+    case kStPreW:  // a letter piece with the prefix, a space before other chars, else whitespace
+      if (letter) return letter;
+      if (k == kSO) return kStOM | kAxRun | kAfSpO;
+      if (k == kSW) return kStW | kAxRun | kAaNone;
+      if (k == kKCrlf) return kStW | kAxRun | kAaRun;
+      return kArPiece;  // the whitespace run is the prefix char alone
+    case kStH:
+      if (k == kSU) return kStH | kAxRun;
+      if (k == kSC || k == kSM) return kStH | kAxRun | kAaRun;
+      if (k == kSD) return kStT | kAxRun | kAaNone;
+      return kAfExit;
+    case kStT:
+      if (k == kSD || k == kSC || k == kSM) return kStT | kAxRun;
+      return kAfExit;
+    case kStSuf:
+      return k == kSO ? (uint32_t)kAfApos : (kAxE | kArPiece);
+    case kStSuf1:
+      return k < kKEnd ? (uint32_t)kAfSuf1 : (kAxE | kArPiece);
+    case kStSuf2:
+      return k < kKEnd ? (uint32_t)kAfSuf2 : (kAxE | kArPiece);
+    case kStOM:
+      if (k == kSO || k == kSM) return kStOM | kAxRun;
+      if (k == kKCrlf) return kStCrlf | kAxRun;
+      return kArPiece;
+    case kStCrlf:
+      return k == kKCrlf ? (kStCrlf | kAxRun) : (uint32_t)kArPiece;
+    case kStW:
+      if (k == kKCrlf) return kStW | kAxRun | kAaRun;  // CR and LF are one byte each
+      if (k == kSW) return kStW | kAxRun;
+      return kAfWEnd;
+    case kStDig:
+      return k == kSN ? (kStDig | kAfDig) : (uint32_t)kArPiece;
+    default:
+      return kArHard;
+  }
+}
+
+// Applies action act to s.  v: the info word at s.x; k: its kind (kind_of,
+// or kKEnd past the text or at a document start after s.p, or kKFar past
+// what the reader holds); r: the end of the stretch of one kind that starts
+// at s.x (capped at what the reader holds); pl: the first byte of the code
+// point before s.x.  Returns kScanGo (step again), kScanPiece (s.x: where
+// the piece ends), kScanFar (the piece at s.p needs the text past the
+// reader) or kScanHard (the piece at s.p starts with a mark).  Written as
+// selects only, so lanes in different stages take the same instructions.
+template <typename P>
+TOK_HD TOK_SEG_INLINE uint32_t scan_apply(Scan<P>& s, uint32_t act, uint32_t v, uint32_t k, P r, P pl) {
+  constexpr P kNone = ~P(0);
+  const P x = s.x, len = (P)len_of(v);
+  const uint32_t xop = act & (3u << 4), aop = act & (3u << 6);
+  uint32_t st = act & 15u, res = (act >> 8) & 3u;
+  // two independent selects per field (the codes' low and high bits)
+  const P x_lo = (xop & kAxLen) ? x + len : x, x_hi = (xop & kAxLen) ? s.e : r;
+  P nx = (xop & kAxRun) ? x_hi : x_lo;
+  const P a_lo = (aop & kAaNone) ? kNone : s.a, a_hi = (aop & kAaNone) ? P(1) : r;
+  P na = (aop & kAaRun) ? a_hi : a_lo;
+  P ne = s.e;
+  const bool apos = k == kSO && (v & kQApos) != 0;
+  if (act & kAfSpO) {  // a space before other chars, else the prefix char alone
+    nx = s.sp ? nx : x;
+    res = s.sp ? res : (uint32_t)kScanPiece;
+  }
+  // end of H* or T+: the piece reaches e; a suffix may follow
+  if (act & kAfExit) {
+    const P e = s.a != kNone ? s.a : x;
+    const bool here = e == x;
+    ne = e;
+    nx = here ? (apos ? x + 1 : x) : e;
+    st = here ? (uint32_t)kStSuf1 : (uint32_t)kStSuf;
+    res = (here && !apos) ? (uint32_t)kScanPiece : (uint32_t)kScanGo;
+  }
+  // the suffix: its apostrophe, then one or two letters under case folding
+  const uint32_t f = fold_of(v);
+  const bool one = f == kFS || f == kFT || f == kFM || f == kFD, two = f == kFR || f == kFV || f == kFL;
+  const bool fin = s.a == kFL ? f == kFL : f == kFE;
+  if (act & kAfApos) {
+    nx = apos ? x + 1 : s.e;
+    st = kStSuf1;
+    res = apos ? (uint32_t)kScanGo : (uint32_t)kScanPiece;
+  }
+  if (act & kAfSuf1) {
+    nx = (one || two) ? x + len : s.e;
+    na = two ? (P)f : na;
+    st = kStSuf2;
+    res = two ? (uint32_t)kScanGo : (uint32_t)kScanPiece;
+  }
+  if (act & kAfSuf2) {
+    nx = fin ? x + len : s.e;
+    res = kScanPiece;
+  }
+  // end of a whitespace run: up to its last CR/LF; else all of it at the
+  // text's end; else all but its last code point, if that leaves one
+  if (act & kAfWEnd) {
+    nx = s.a != kNone ? s.a : (k != kKEnd && pl > s.p) ? pl : x;
+    res = kScanPiece;
+  }
+  // digits in groups of at most three
+  if (act & kAfDig) {
+    const bool more = s.a < 3;
+    na = more ? s.a + 1 : s.a;
+    nx = more ? x + len : x;
+    res = more ? (uint32_t)kScanGo : (uint32_t)kScanPiece;
+  }
+  s.x = nx;
+  s.a = na;
+  s.e = ne;
+  s.st = st;
+  return res;
+}
+
+// One step: the action for the stage and kind, applied.
+template <typename P>
+TOK_HD TOK_SEG_INLINE uint32_t scan_step(Scan<P>& s, uint32_t v, uint32_t k, P r, P pl) {
+  if (s.st == kStStart) s.sp = (v & kQSpace) != 0;
+  return scan_apply(s, scan_action(s.st, k), v, k, r, pl);
+}
 
 // Synchronizing transition from the code point with info x to the one with
 // info y (both decoded, both in one document).

@@ -66,21 +66,22 @@ TOK_HD inline bool sync_transition_of(bool gpt2, uint32_t x, uint32_t cx, uint32
 // C=2 M=3 N=4 W=5 O=6).
 TOK_HD inline bool sync_transition_case(uint32_t x, uint32_t sx, uint32_t y, uint32_t sy) {
   constexpr uint32_t U = 0, D = 1, M = 3, N = 4, W = 5, O = 6;
-  if (sy == N) return sx != N;
-  if (sx == N) return true;
+  // written as selects: the kernels evaluate it for every code point at once
   const bool x_crlf = x == 0x0D || x == 0x0A, y_crlf = y == 0x0D || y == 0x0A;
-  if (sx < M) {  // a letter
-    if (sy == W) return true;
-    if (sy == O) return y != 0x27;
-    // D -> U, unless it is the middle of a two-letter contraction suffix in
-    // mixed case ('rE 'vE 'lL)
-    return sx == D && sy == U && !(((x == 'r' || x == 'v') && y == 'E') || (x == 'l' && y == 'L'));
-  }
-  if (sx == M || sx == O) return sy == W && !y_crlf;
-  // x is whitespace
-  if (sy == W) return false;
-  if (sy == O) return x != 0x20;
-  return x_crlf;  // a letter or a mark
+  // after a letter: whitespace; an other char unless it is the apostrophe
+  // (which may begin a contraction suffix); D -> U (the case boundary),
+  // unless it is the middle of a two-letter contraction suffix in mixed case
+  // ('rE 'vE 'lL)
+  const bool mixed_suffix = ((x == 'r' || x == 'v') && y == 'E') || (x == 'l' && y == 'L');
+  const bool after_letter = sy == W || (sy == O ? y != 0x27 : (sx == D && sy == U && !mixed_suffix));
+  // after a mark or an other char: whitespace that is not CR/LF
+  const bool after_mo = sy == W && !y_crlf;
+  // after whitespace: an other char unless the whitespace is U+0020; a
+  // letter or a mark after CR/LF
+  const bool after_ws = sy != W && (sy == O ? x != 0x20 : x_crlf);
+  const bool by_x = sx < M ? after_letter : (sx == M || sx == O) ? after_mo : after_ws;
+  // a number after anything else, and from a number to anything else
+  return sy == N ? sx != N : sx == N ? true : by_x;
 }
 
 }  // namespace tok
