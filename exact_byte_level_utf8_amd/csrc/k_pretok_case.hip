@@ -485,28 +485,40 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
   }
 
   // cuts at the tile's code points (a wave's ballot is two words of the cut
-  // bits), and the segments that start at them
-#pragma unroll
-  for (int r = 0; r < kCaseTile / kCaseNT; ++r) {
-    const int64_t p = t0 + r * kCaseNT + tid;
-    const int i = (int)(p - lo);
-    const uint32_t v = S->q[i];
-    // the code point before starts 1 to 4 bytes back in well-formed text (in
-    // malformed text, which its own tile reports, any value will do)
-    const uint32_t v1 = S->q[i - 1], v2 = S->q[i - 2], v3 = S->q[i - 3], v4 = S->q[i - 4];
-    const uint32_t prev = v1 != kNotLead ? v1 : v2 != kNotLead ? v2 : v3 != kNotLead ? v3 : v4;
-    const bool cut = p < t1 && v != kNotLead && (p == 0 || (v & kQDocStart) || sync_at(prev, v));
-    const uint64_t m = __ballot(cut);
+  // bits), and the segments that start at them: the ballots of all rounds
+  // first, then one slot reservation per wave
+  {
+    constexpr int kRounds = kCaseTile / kCaseNT;
     const uint32_t lane = lane_id();
-    const uint32_t w0 = (uint32_t)(r * kCaseNT + (tid - lane)) / 32;
-    uint32_t base = 0;
-    if (lane == 0) {
-      S->cut[w0] = (uint32_t)m;
-      S->cut[w0 + 1] = (uint32_t)(m >> 32);
-      if (m) base = atomicAdd(&S->nseg, (uint32_t)__popcll(m));
+    const uint64_t below = (1ull << lane) - 1;
+    uint64_t m[kRounds];
+    uint32_t total = 0;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int64_t p = t0 + r * kCaseNT + tid;
+      const int i = (int)(p - lo);
+      const uint32_t v = S->q[i];
+      // the code point before starts 1 to 4 bytes back in well-formed text (in
+      // malformed text, which its own tile reports, any value will do)
+      const uint32_t v1 = S->q[i - 1], v2 = S->q[i - 2], v3 = S->q[i - 3], v4 = S->q[i - 4];
+      const uint32_t prev = v1 != kNotLead ? v1 : v2 != kNotLead ? v2 : v3 != kNotLead ? v3 : v4;
+      const bool cut = p < t1 && v != kNotLead && (p == 0 || (v & kQDocStart) || sync_at(prev, v));
+      m[r] = __ballot(cut);
+      total += (uint32_t)__popcll(m[r]);
+      if (lane == 0) {
+        const uint32_t w0 = (uint32_t)(r * kCaseNT + (tid - lane)) / 32;
+        S->cut[w0] = (uint32_t)m[r];
+        S->cut[w0 + 1] = (uint32_t)(m[r] >> 32);
+      }
     }
+    uint32_t base = 0;
+    if (lane == 0 && total) base = atomicAdd(&S->nseg, total);
     base = __shfl(base, 0, kWave);
-    if (cut) S->job[base + __popcll(m & ((1ull << lane) - 1))] = (uint32_t)p;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      if ((m[r] >> lane) & 1u) S->job[base + __popcll(m[r] & below)] = (uint32_t)(t0 + r * kCaseNT + tid);
+      base += (uint32_t)__popcll(m[r]);
+    }
   }
   __syncthreads();
   auto is_cut = [&](uint64_t p) { return (S->cut[(p - t0) >> 5] >> ((p - t0) & 31)) & 1u; };
@@ -602,14 +614,15 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
       const uint32_t xi = min(x, (uint32_t)kCaseValid - 1u);
       const uint32_t v = S->q[xi];
       const uint32_t rr = S->rend[xi];
-      const uint32_t kin = ((v & kQEnd) || (x > sc.p && (v & kQDocStart))) ? (uint32_t)kKEnd : kind_of(v);
+      const bool gone = ((v & kQEnd) != 0) | ((x > sc.p) & ((v & kQDocStart) != 0));  // bitwise: no branches
+      const uint32_t kin = gone ? (uint32_t)kKEnd : kind_of(v);
       const uint32_t k = x >= (uint32_t)kCaseValid ? kpast : kin;
       const uint32_t act = S->act[sc.st * kScanKinds + k];
       // at a piece's first code point: the job ends at the tile's end or at
       // another cut; else the piece starts here
       const bool at_start = sc.st == kStStart;
-      const bool seg_end = at_start && (x >= tw1 || ((rr >> 15) && x != js));
-      if (at_start && !seg_end) tile_bit(mark, x);
+      const bool seg_end = at_start & ((x >= tw1) | (((rr >> 15) != 0) & (x != js)));
+      if (at_start & !seg_end) tile_bit(mark, x);
       sc.sp = at_start ? (uint32_t)((v & kQSpace) != 0) : sc.sp;
       const uint32_t res = scan_apply(sc, act, v, k, (rr >> 2) & 0x1FFFu, x - 1u - (rr & 3u));
       if (!seg_end && res < kScanFar) {

@@ -397,24 +397,27 @@ TOK_HD TOK_SEG_INLINE uint32_t scan_apply(Scan<P>& s, uint32_t act, uint32_t v, 
     st = here ? (uint32_t)kStSuf1 : (uint32_t)kStSuf;
     res = (here && !apos) ? (uint32_t)kScanPiece : (uint32_t)kScanGo;
   }
-  // the suffix: its apostrophe, then one or two letters under case folding
-  const uint32_t f = fold_of(v);
-  const bool one = f == kFS || f == kFT || f == kFM || f == kFD, two = f == kFR || f == kFV || f == kFL;
-  const bool fin = s.a == kFL ? f == kFL : f == kFE;
-  if (act & kAfApos) {
-    nx = apos ? x + 1 : s.e;
-    st = kStSuf1;
-    res = apos ? (uint32_t)kScanGo : (uint32_t)kScanPiece;
-  }
-  if (act & kAfSuf1) {
-    nx = (one || two) ? x + len : s.e;
-    na = two ? (P)f : na;
-    st = kStSuf2;
-    res = two ? (uint32_t)kScanGo : (uint32_t)kScanPiece;
-  }
-  if (act & kAfSuf2) {
-    nx = fin ? x + len : s.e;
-    res = kScanPiece;
+  // the suffix after an apostrophe that is not where the run ended, and its
+  // letters under case folding: rare, so apart from the rest
+  if (act & (kAfApos | kAfSuf1 | kAfSuf2)) {
+    const uint32_t f = fold_of(v);
+    const bool one = f == kFS || f == kFT || f == kFM || f == kFD, two = f == kFR || f == kFV || f == kFL;
+    const bool fin = s.a == kFL ? f == kFL : f == kFE;
+    if (act & kAfApos) {
+      nx = apos ? x + 1 : s.e;
+      st = kStSuf1;
+      res = apos ? (uint32_t)kScanGo : (uint32_t)kScanPiece;
+    }
+    if (act & kAfSuf1) {
+      nx = (one || two) ? x + len : s.e;
+      na = two ? (P)f : na;
+      st = kStSuf2;
+      res = two ? (uint32_t)kScanGo : (uint32_t)kScanPiece;
+    }
+    if (act & kAfSuf2) {
+      nx = fin ? x + len : s.e;
+      res = kScanPiece;
+    }
   }
   // end of a whitespace run: up to its last CR/LF; else all of it at the
   // text's end; else all but its last code point, if that leaves one
