@@ -300,6 +300,69 @@ int case_pieces(const uint8_t* s, size_t n, const std::vector<char>& docstart, s
 
 }  // namespace
 
+// The forward scan of the case-splitting family alone (seg::scan_step) over
+// a whole text of one document, with no window and no fallback: the piece
+// starts in order, until the first piece the scan leaves to the matcher (one
+// that starts with a mark).  Returns the number of starts found, and in
+// *hard_at that piece's first byte (n if the scan matched the whole text);
+// -1 on malformed input or a step that does not advance.
+extern "C" long rules_cpu_scan_pieces(const uint8_t* s, size_t n, uint64_t* starts, size_t cap, uint64_t* hard_at) {
+  std::vector<uint32_t> q(n, 0);
+  std::vector<uint64_t> leads;
+  for (size_t i = 0; i < n;) {
+    const uint8_t b = s[i];
+    const uint32_t len = b < 0x80 ? 1 : b >= 0xF0 ? 4 : b >= 0xE0 ? 3 : 2;
+    if ((b & 0xC0) == 0x80 || i + len > n) return -1;
+    uint32_t cp = len == 1 ? b : len == 2 ? (b & 0x1Fu) : len == 3 ? (b & 0x0Fu) : (b & 0x07u);
+    for (uint32_t k = 1; k < len; ++k) cp = (cp << 6) | (s[i + k] & 0x3Fu);
+    q[i] = seg::make_q(cp, table_case(cp), len, seg::fold_code(cp, fold_extra(cp)));
+    leads.push_back(i);
+    i += len;
+  }
+  if (n) q[0] |= seg::kQDocStart;
+  // where each stretch of one kind ends
+  std::vector<uint64_t> rend(n + 1, n);
+  uint64_t next = n;
+  for (size_t k = leads.size(); k-- > 0;) {
+    const uint64_t j = leads[k];
+    rend[j] = next;
+    if (k == 0 || seg::kind_of(q[j]) != seg::kind_of(q[leads[k - 1]])) next = j;
+  }
+  size_t count = 0;
+  *hard_at = n;
+  uint64_t p = 0;
+  while (p < n) {
+    if (count < cap) starts[count] = p;
+    ++count;
+    seg::Scan<uint64_t> sc{p, p, 0, 0, seg::kStStart, 0};
+    for (int steps = 0;; ++steps) {
+      if (steps > (int)(4 * n + 16)) return -1;
+      const uint64_t x = sc.x;
+      uint32_t v = 0, k = seg::kKEnd;
+      uint64_t r = x, pl = x;
+      if (x < n) {
+        v = q[x];
+        k = (x > sc.p && (v & seg::kQDocStart)) ? (uint32_t)seg::kKEnd : seg::kind_of(v);
+        r = rend[x];
+        if (x > 0) {
+          pl = x - 1;
+          while (!(q[pl] & seg::kQLead)) --pl;
+        }
+      }
+      const uint32_t res = seg::scan_step(sc, v, k, r, pl);
+      if (res == seg::kScanGo) continue;
+      if (res != seg::kScanPiece) {
+        *hard_at = sc.p;
+        return (long)count - 1;
+      }
+      break;
+    }
+    if (sc.x <= p) return -1;
+    p = sc.x;
+  }
+  return (long)count;
+}
+
 extern "C" int rules_cpu_class(uint32_t cp) { return (int)table_class(cp); }
 
 // Letter-case classes (U=0 D=1 C=2 M=3 N=4 W=5 O=6) of lo .. lo + n - 1.

@@ -239,3 +239,41 @@ def test_case_documents_are_hard_boundaries(rules, case_orc):
         want += [int(s) + p for p in case_orc.pieces(d.encode())]
     assert rules.pieces(data, 2, off) == want
     assert rules.pieces(data, 3, off) == want
+
+
+def test_case_scan_alone_matches_the_oracle(rules, case_orc):
+    """The forward scan by itself (seg_rules.h: one text, no window, no
+    fallback) gives the oracle's pieces, and leaves to the matcher only a
+    piece that starts with a mark: on workload text, CJK text, long runs and
+    random strings over a case-rich alphabet.  The tile emulation above
+    would pass even if the scan handed every piece to the matcher; this
+    pins the scan itself."""
+    f = rules.rules_cpu_scan_pieces
+    f.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.POINTER(ctypes.c_uint64)]
+    f.restype = ctypes.c_long
+
+    def check(b: bytes) -> bool:
+        out = np.zeros(len(b) + 1, dtype=np.uint64)
+        hard = ctypes.c_uint64(0)
+        k = f(b, len(b), out.ctypes.data, len(out), ctypes.byref(hard))
+        assert k >= 0, b[:60]
+        want = case_orc.pieces(b)
+        h = hard.value
+        assert out[:k].tolist() == [p for p in want if p < h], b[:60]
+        if h == len(b):
+            return True
+        assert h in want, b[:60]
+        cp = ord(b[h:h + 4].decode("utf-8", errors="ignore")[0])
+        assert int(oracle.subclass_range(cp, 1)[0]) == 3, (hex(cp), b[:60])  # a mark
+        return False
+
+    for b in [textgen.mix_text(2, 100_000).encode(), textgen.cjk_text(8, 20_000).encode()] + \
+             [t.encode() for t in LONG_RUNS if "\u0301" not in t]:
+        check(b)
+    rng = random.Random(23)
+    whole = 0
+    for _ in range(20000):
+        b = "".join(rng.choice(CASE_WIDE) * rng.choice([1, 1, 1, 2, 5]) for _ in range(rng.randint(1, 40))).encode()
+        whole += check(b)
+    assert whole > 5000  # most strings have no piece that starts with a mark
