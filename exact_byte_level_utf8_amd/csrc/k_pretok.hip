@@ -126,8 +126,12 @@ __device__ inline uint32_t lds_word(const uint32_t* a, uint32_t b) {
 
 __device__ inline bool is_cont(uint32_t byte) { return (byte & 0xC0u) == 0x80u; }
 
+// Occupancy: 8 workgroups per CU for 8-wave workgroups, and for 4-wave ones
+// of the Llama-3 style (its register spills cost less than fewer waves: 393
+// -> 375 us on the 64 x 500K batch); 6 for the GPT-2 style's 4-wave ones,
+// which would spill for nothing.
 template <int PATTERN, int NT>
-__global__ void __launch_bounds__(NT, NT >= 512 ? 8 : 6)
+__global__ void __launch_bounds__(NT, NT >= 512 || PATTERN == 1 ? 8 : 6)
 pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off,
               uint32_t n_docs, const uint32_t* __restrict__ unit_tab, Bufs B) {
   constexpr int kRounds = kPT / NT;                    // tile positions per thread
