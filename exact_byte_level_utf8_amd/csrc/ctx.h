@@ -262,7 +262,7 @@ struct tok_ctx {
            fill(lb.cut, (parts + 2) * 8) && fill(lb.part_lit, (parts + 2) * 4) &&
            fill(lb.doc_part, (lit_docs + 2) * 4) && fill(lb.out_off, (parts + 2) * 8) &&
            fill(lb.fin, (parts + 2) * 4) && fill(lb.misc, 16) && fill(lb.ids, (lit_cap + 64) * 4) &&
-           fill(lb.spans, (lit_cap + 64) * 4);
+           fill(lb.spans, (lit_cap + 64) * 4) && fill(lb.lmark, lit_cap + 64) && fill(lb.lid_at, lit_cap * 4);
     }
     if (ok && d_doc) ok = fill(d_doc, doc_cap * 8) && fill(d_outoff, doc_cap * 8);
     if (!ok || hipStreamSynchronize(stream) != hipSuccess) {
@@ -303,6 +303,8 @@ struct tok_ctx {
     dfree(lb.misc);
     dfree(lb.ids);
     dfree(lb.spans);
+    dfree(lb.lmark);
+    dfree(lb.lid_at);
     lit_cap = 0;
     lit_docs = 0;
   }
@@ -331,7 +333,8 @@ struct tok_ctx {
         hipMalloc((void**)&lb.fin, (parts + 2) * 4) != hipSuccess ||
         hipMalloc((void**)&lb.misc, 16) != hipSuccess ||
         hipMalloc((void**)&lb.ids, (cap + 64) * 4) != hipSuccess ||
-        hipMalloc((void**)&lb.spans, (cap + 64) * 4) != hipSuccess) {
+        hipMalloc((void**)&lb.spans, (cap + 64) * 4) != hipSuccess ||
+        hipMalloc((void**)&lb.lmark, cap + 64) != hipSuccess || hipMalloc((void**)&lb.lid_at, cap * 4) != hipSuccess) {
       (void)hipGetLastError();
       free_lit_bufs();
       return TOK_E_NOMEM;
@@ -347,16 +350,34 @@ struct tok_ctx {
   // literal IDs, all enqueued at once; one synchronization.  doc_off /
   // n_docs / out_off: the caller's documents and their output offsets, or
   // nullptr for one request.  spans (optional): each ID's first byte.
+  // Whether a call folds the literal IDs into the piece pass: every call but
+  // those with span export (whose assembly scans token byte lengths, which a
+  // literal's ID does not give) and empty ones.
+  static bool folds_literals(uint64_t n, const uint32_t* spans) { return n > 0 && !spans; }
+
   // The same, enqueued under call number `call` without waiting (after
-  // ensure_lit_bufs()).
+  // ensure_lit_bufs()).  Folded: the literal pass marks the taken literals,
+  // the pipeline over the parts takes each as one piece with its ID and
+  // writes the result, and only a batch's document offsets are mapped after
+  // it.  Otherwise the pipeline encodes the literals' own bytes too, and the
+  // insertion puts the literal IDs in place of those tokens.
   void enqueue_added(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, int32_t* out,
                      uint64_t out_cap, uint64_t* out_off, hipStream_t s, uint64_t call, uint32_t* spans) {
     Bufs bb = b;
     bb.gen = call;
     bb.n_docs_dev = lb.misc + 2;
-    launch_literal_pass(text, n, doc_off, n_docs, literals(), lb, d_ctr, call, s);
+    LitBufs l = lb;
+    l.fold = folds_literals(n, spans) ? 1u : 0u;
+    launch_literal_pass(text, n, doc_off, n_docs, literals(), l, d_ctr, call, s);
+    if (l.fold) {
+      const Literals L = literals();
+      bb.lit = LitMarks{lb.sel, lb.misc + 1, L.off, L.ids, lb.lmark, lb.lid_at};
+      enqueue(text, n, lb.cut, 1, out, nullptr, out_cap, lb.out_off, s, bb, true, nullptr);
+      if (out_off) launch_literal_doc_offsets(l, out_off, doc_off ? n_docs : 1u, s);
+      return;
+    }
     enqueue(text, n, lb.cut, 1, lb.ids, spans ? lb.spans : nullptr, n, lb.out_off, s, bb, true, nullptr);
-    launch_literal_insert(n, literals(), lb, out, spans, out_cap, out_off, d_ctr, call, s);
+    launch_literal_insert(n, literals(), l, out, spans, out_cap, out_off, d_ctr, call, s);
   }
 
   int run_added(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, int32_t* out,
@@ -391,7 +412,8 @@ struct tok_ctx {
     }
     if (c->err_docs == call) return TOK_E_ARG;  // the caller's document offsets (the parts are well formed)
     if (c->err_utf8 == call) return TOK_E_UTF8;
-    if (c->lit_done != call || c->done != call || c->ins_done != call) return TOK_E_DEVICE;
+    if (c->lit_done != call || c->done != call || (!folds_literals(n, spans) && c->ins_done != call))
+      return TOK_E_DEVICE;
     *total = c->total;
     return TOK_OK;
   }

@@ -36,6 +36,15 @@ struct LitBufs {
   uint32_t* misc;       // [0] tokens the pipeline produced, [1] literals taken k, [2] parts, [3] documents
   int32_t* ids;         // the pipeline's output, before the literal IDs go in
   uint32_t* spans;      // with span export: the first byte of each of those IDs
+  // Literal IDs folded into the piece pass (calls without span export): a
+  // taken literal is then one piece whose token is its ID, and the pipeline's
+  // output is the result.  lmark[b]: 1 where a taken literal starts, 2 on
+  // its later bytes, else 0 (the match kernel clears its tile's bytes, the
+  // selection writes the marks); lid_at[b]: the ID of the literal that
+  // starts at b (meaningful only where lmark[b] is 1).
+  uint8_t* lmark;
+  int32_t* lid_at;
+  uint32_t fold;        // this call folds the literal IDs in
 };
 
 constexpr int kLitTile = 1024;  // bytes per workgroup of the literal match
@@ -72,6 +81,9 @@ void launch_literal_pass(const uint8_t* text, uint64_t n, const uint64_t* doc_of
                          LitBufs lb, Counters* ctr, uint64_t gen, hipStream_t s);
 void launch_literal_insert(uint64_t n, Literals L, LitBufs lb, int32_t* out, uint32_t* spans, uint64_t cap,
                            uint64_t* out_off, Counters* ctr, uint64_t gen, hipStream_t s);
+// With the literal IDs folded into the piece pass: the caller's document
+// offsets (n_docs + 1 of them) from the pipeline's part offsets.
+void launch_literal_doc_offsets(LitBufs lb, uint64_t* out_off, uint32_t n_docs, hipStream_t s);
 // The match kernel, then, for a window of more than a few thousand records,
 // the copy of the window's IDs after the splice (a grid sized by a.max_fresh).
 void launch_repair_match(const RepairArgs& a, hipStream_t s);

@@ -26,7 +26,14 @@
 // The parts then run through the usual pipeline as documents (their count
 // read on the device, so the host enqueues everything without waiting),
 // which are hard boundaries for code points, pieces and merges, exactly as
-// the segments between literals must be.  Then:
+// the segments between literals must be.  Without span export the literal
+// IDs are folded into that pipeline: the match kernel clears its tile's
+// literal marks, the pre-tokenization kernel marks the taken literals on
+// its way in (1 on the first byte, 2 on the others, and the ID at the first
+// byte), and the piece pass takes each marked literal as one piece whose
+// token is its ID, so the pipeline's output is the result; only a batch's
+// document offsets are mapped afterwards (lit_doc_offsets_kernel).  With
+// span export the literals' own bytes go through the pipeline too, and:
 //   lit_insert_kernel  one workgroup: output offsets of the parts, where a
 //                      literal part counts one ID; writes the literal IDs.
 //   lit_scatter_kernel every ID of a segment part to its final place; the IDs
@@ -132,6 +139,9 @@ lit_match_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* _
       s_text[w] = v;
     }
     if (tid < 8) s_first[tid] = L.first[tid];
+    if (lb.fold)  // this tile's literal marks start clear (the selection writes them)
+      for (uint32_t w = tid; w < kLitTile / 4; w += kMatchThreads)
+        reinterpret_cast<uint32_t*>(lb.lmark + base)[w] = 0;
   }
   __syncthreads();
   // the longest literal at window-front position tid and at tile positions
@@ -501,7 +511,21 @@ lit_scatter_kernel(LitBufs lb, int32_t* __restrict__ out, uint32_t* __restrict__
   }
 }
 
+// The caller's document offsets when the literal IDs are folded into the
+// piece pass: the pipeline's offset of each document's first part.
+__global__ void __launch_bounds__(kScatterThreads)
+lit_doc_offsets_kernel(LitBufs lb, uint64_t* __restrict__ out_off) {
+  const uint32_t nb = lb.misc[3];
+  for (uint32_t d = blockIdx.x * kScatterThreads + threadIdx.x; d <= nb; d += gridDim.x * kScatterThreads)
+    out_off[d] = lb.out_off[lb.doc_part[d]];
+}
+
 }  // namespace
+
+void launch_literal_doc_offsets(LitBufs lb, uint64_t* out_off, uint32_t n_docs, hipStream_t s) {
+  const uint32_t blocks = (uint32_t)std::min<uint64_t>(((uint64_t)n_docs + kScatterThreads) / kScatterThreads, 1024);
+  lit_doc_offsets_kernel<<<blocks, kScatterThreads, 0, s>>>(lb, out_off);
+}
 
 void launch_literal_pass(const uint8_t* text, uint64_t n, const uint64_t* doc_off, uint32_t n_docs, Literals L,
                          LitBufs lb, Counters* ctr, uint64_t gen, hipStream_t s) {

@@ -16,7 +16,9 @@
 //      BPE": whole-piece vocabulary hits).  The probes are first compacted
 //      into lists in LDS, one per table, and then run one per lane, so a wave
 //      waits for one memory round trip.  Every other piece goes to a work
-//      list in LDS by length.
+//      list in LDS by length.  With added-token literals folded in, a taken
+//      literal is one piece (the flags inside it are masked) whose token is
+//      the literal's ID.
 //   2. The workgroup's waves merge the listed pieces of up to 64 bytes:
 //      33..64-byte pieces first (one wave per piece, one symbol per lane),
 //      then 17..32-byte pieces (two per wave, one 32-lane row each), then
@@ -352,6 +354,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   constexpr int kPoolWords = kListWords > 4 * kLongSyms ? kListWords : 4 * kLongSyms;
   __shared__ __attribute__((aligned(16))) uint8_t s_text[kTextLds];
   __shared__ uint16_t s_flags[kFlagLds];
+  __shared__ uint16_t s_litst[kFlagLds];  // taken literals' first bytes (literal IDs folded in)
   __shared__ uint32_t s_tok[kTokLds];
   __shared__ uint8_t s_cnt8[kPieceTile];
   __shared__ __attribute__((aligned(16))) uint32_t s_pool[kPoolWords];
@@ -405,7 +408,21 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   }
   for (int k = tid; k < kFlagLds; k += NT) {
     const uint64_t c = c0 + k;
-    s_flags[k] = c < n_chunks ? B.flags[c] : 0;
+    uint32_t f = c < n_chunks ? B.flags[c] : 0u, ls = 0;
+    if (B.lit.mark && c < n_chunks) {  // a taken literal is one piece: no start inside it
+      const uint4 mk = reinterpret_cast<const uint4*>(B.lit.mark)[c];  // the chunk's 16 marks
+      const uint32_t w[4] = {mk.x, mk.y, mk.z, mk.w};
+      uint32_t inside = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t v = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        ls |= (uint32_t)(v == 1u) << i;
+        inside |= (uint32_t)(v == 2u) << i;
+      }
+      f &= ~inside;
+    }
+    s_flags[k] = (uint16_t)f;
+    s_litst[k] = (uint16_t)ls;
   }
   // the merge and byte-pair tables into this XCD's L2 while phase 1 runs
   const uint32_t warm = touch_lines<NT>(T.merge_slots, (uint64_t)T.merge_buckets * kBucket * 8, 2) ^
@@ -449,7 +466,11 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
       const uint32_t len = (uint32_t)min(e - s0, (uint64_t)0xFFFF);
       const uint32_t off = (uint32_t)(s0 - base);
       const uint32_t item = off | (len << 16);
-      if (len == 1u) {
+      if ((s_litst[lc] >> bit) & 1u) {  // a taken literal: its ID
+        s_tok[off] = (uint32_t)B.lit.id_at[s0];
+        s_cnt8[off] = 1;
+        ++hits;
+      } else if (len == 1u) {
         s_tok[off] = s_text[off];
         s_cnt8[off] = 1;
         ++hits;

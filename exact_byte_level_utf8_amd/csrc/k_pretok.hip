@@ -134,6 +134,7 @@ template <int PATTERN, int NT>
 __global__ void __launch_bounds__(NT, NT >= 512 || PATTERN == 1 ? 8 : 6)
 pretok_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* __restrict__ doc_off,
               uint32_t n_docs, const uint32_t* __restrict__ unit_tab, Bufs B) {
+  mark_literals(B.lit);  // for the piece pass, when literal IDs are folded in
   constexpr int kRounds = kPT / NT;                    // tile positions per thread
   constexpr int kPer = kRounds;                        // consecutive positions per thread in the aggregate pass
   static_assert(kPer == 2 || kPer == 4, "aggregate states are packed as 2 or 4 bytes per thread");

@@ -321,6 +321,7 @@ pretok_case_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t*
                    uint32_t n_docs, const uint32_t* __restrict__ unit_tab, Bufs B) {
   __shared__ CaseShared sh;
   CaseShared* S = &sh;
+  mark_literals(B.lit);  // for the piece pass, when literal IDs are folded in
   if (B.n_docs_dev) n_docs = *B.n_docs_dev;
   const uint32_t tid = threadIdx.x;
   const uint32_t tiles = gridDim.x;

@@ -139,6 +139,32 @@ struct Tables {
 };
 
 // Per-call device buffers.
+// Added-token literals folded into the piece pass (k_added.hip): the taken
+// literals, marked by the pre-tokenization kernels on their way in (one
+// literal per thread over the grid, before anything else) and read by the
+// piece pass.  mark == nullptr: no literals to fold.
+struct LitMarks {
+  const uint64_t* sel;    // the taken literals in order, (first byte << 32 | literal index)
+  const uint32_t* count;  // how many (on the device)
+  const uint32_t* off;    // literal i's bytes are off[i] .. off[i + 1]
+  const int32_t* ids;     // literal i's ID
+  uint8_t* mark;          // 1 at a taken literal's first byte, 2 on its others (0 elsewhere: cleared before)
+  int32_t* id_at;         // the literal's ID at its first byte
+};
+
+__device__ inline void mark_literals(const LitMarks& m) {
+  if (!m.mark) return;
+  const uint32_t k = *m.count;
+  for (uint32_t j = blockIdx.x * blockDim.x + threadIdx.x; j < k; j += gridDim.x * blockDim.x) {
+    const uint64_t a = m.sel[j];
+    const uint32_t li = (uint32_t)a;
+    const uint64_t S = a >> 32, E = S + (m.off[li + 1] - m.off[li]);
+    m.id_at[S] = m.ids[li];
+    m.mark[S] = 1;
+    for (uint64_t b = S + 1; b < E; ++b) m.mark[b] = 2;
+  }
+}
+
 struct Bufs {
   uint16_t* flags;
   int32_t* staging;
@@ -165,6 +191,7 @@ struct Bufs {
   uint64_t* hand_state;
   uint64_t hand_wait;
   const uint32_t* n_docs_dev;  // if set, the document count, read on the device (overrides n_docs)
+  LitMarks lit;  // added-token literals folded into the piece pass (lit.mark == nullptr: none)
 };
 
 // A token's lowest ranks as right operand (x) and as left operand (y), from
