@@ -244,6 +244,8 @@ lit_match_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* _
   if (tid == 0) lb.tile_cnt[tile] = tot | (raw ? kTileRaw : 0u);
 }
 
+constexpr uint32_t kSelBatch = 16;  // global loads one selection thread keeps in flight
+
 __global__ void __launch_bounds__(kSelThreads)
 lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_off, uint32_t n_docs, Literals L,
                   LitBufs lb, Counters* ctr, uint64_t gen) {
@@ -272,12 +274,12 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
     uint32_t tot = 0;
     const uint32_t b = carry + wg_excl_scan<kSelThreads>(v, 0u, AddOp(), s_scan, &tot);
     const uint64_t* src = lb.cand + (uint64_t)t * kLitTile;
-    for (uint32_t j = 0; j < v; j += 4) {  // four loads in flight before the stores
-      uint64_t x[4];
+    for (uint32_t j = 0; j < v; j += kSelBatch) {  // kSelBatch loads in flight before the stores
+      uint64_t x[kSelBatch];
 #pragma unroll
-      for (uint32_t u = 0; u < 4; ++u) x[u] = j + u < v ? src[j + u] : 0ull;
+      for (uint32_t u = 0; u < kSelBatch; ++u) x[u] = j + u < v ? src[j + u] : 0ull;
 #pragma unroll
-      for (uint32_t u = 0; u < 4; ++u)
+      for (uint32_t u = 0; u < kSelBatch; ++u)
         if (j + u < v) lb.sel[b + j + u] = x[u];
     }
     carry += tot;
@@ -363,44 +365,46 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
   const uint32_t nb = bad_docs ? 1u : nd;  // boundaries 0..nb
   auto Db = [&](uint32_t d) -> uint64_t { return bad_docs ? (d == 0 ? 0ull : n) : D(d); };
   const uint32_t parts = nb + 2 * k;
-  for (uint32_t i = tid; i < parts; i += kSelThreads) lb.part_lit[i] = -1;
+  // the parts' literal IDs, for the insertion (unused when the IDs are folded
+  // into the piece pass)
+  if (!lb.fold)
+    for (uint32_t i = tid; i < parts; i += kSelThreads) lb.part_lit[i] = -1;
   __syncthreads();
-  for (uint32_t j0 = tid; j0 < k; j0 += 4 * kSelThreads) {
-    uint64_t a4[4];  // four literals per pass, their loads in flight together
-    uint32_t len4[4];
-    int32_t id4[4];
+  for (uint32_t j0 = tid; j0 < k; j0 += kSelBatch * kSelThreads) {
+    uint64_t aa[kSelBatch];  // kSelBatch literals per pass, their loads in flight together
+    uint32_t len[kSelBatch];
+    int32_t id[kSelBatch];
 #pragma unroll
-    for (uint32_t u = 0; u < 4; ++u) a4[u] = j0 + u * kSelThreads < k ? lb.sel[j0 + u * kSelThreads] : 0ull;
+    for (uint32_t u = 0; u < kSelBatch; ++u) aa[u] = j0 + u * kSelThreads < k ? lb.sel[j0 + u * kSelThreads] : 0ull;
 #pragma unroll
-    for (uint32_t u = 0; u < 4; ++u) {
+    for (uint32_t u = 0; u < kSelBatch; ++u) {
       const bool in = j0 + u * kSelThreads < k;
-      len4[u] = in ? lit_len(L, (uint32_t)a4[u]) : 0u;
-      id4[u] = in ? L.ids[(uint32_t)a4[u]] : -1;
+      len[u] = in ? lit_len(L, (uint32_t)aa[u]) : 0u;
+      id[u] = in && !lb.fold ? L.ids[(uint32_t)aa[u]] : -1;
     }
 #pragma unroll
-    for (uint32_t u = 0; u < 4; ++u) {
-    const uint32_t j = j0 + u * kSelThreads;
-    if (j >= k) break;
-    const uint64_t a = a4[u];
-    const uint64_t S = a >> 32, E = S + len4[u];
-    uint32_t lo = 0, hi = nb + 1;  // #{d : D(d) <= S}
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi) >> 1;
-      if (Db(mid) <= S) lo = mid + 1;
-      else hi = mid;
-    }
-    const uint32_t is = 2 * j + lo;
-    lo = 0;
-    hi = nb + 1;  // #{d : D(d) < E}
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi) >> 1;
-      if (Db(mid) < E) lo = mid + 1;
-      else hi = mid;
-    }
-    const uint32_t ie = 2 * j + 1 + lo;
-    lb.cut[is] = S;
-    lb.cut[ie] = E;
-    lb.part_lit[is] = id4[u];  // the literal's ID (IDs are never negative)
+    for (uint32_t u = 0; u < kSelBatch; ++u) {
+      const uint32_t j = j0 + u * kSelThreads;
+      if (j >= k) break;
+      const uint64_t S = aa[u] >> 32, E = S + len[u];
+      uint32_t lo = 0, hi = nb + 1;  // #{d : D(d) <= S}
+      while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (Db(mid) <= S) lo = mid + 1;
+        else hi = mid;
+      }
+      const uint32_t is = 2 * j + lo;
+      lo = 0;
+      hi = nb + 1;  // #{d : D(d) < E}
+      while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (Db(mid) < E) lo = mid + 1;
+        else hi = mid;
+      }
+      const uint32_t ie = 2 * j + 1 + lo;
+      lb.cut[is] = S;
+      lb.cut[ie] = E;
+      if (!lb.fold) lb.part_lit[is] = id[u];  // the literal's ID (IDs are never negative)
     }
   }
   for (uint32_t d = tid; d <= nb; d += kSelThreads) {
