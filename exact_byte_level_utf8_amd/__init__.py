@@ -132,12 +132,20 @@ def sync_boundary(pattern: str | int, prev_cp: int, cp: int) -> bool:
     return bool(lib().tok_sync_boundary(pat, prev_cp, cp))
 
 
+_DTYPES: dict = {}  # dtype_name -> the torch dtypes it names (filled on first use)
+
+
 def _dev_ptr(t, dtype_name: str, what: str) -> int:
     """Device pointer of a contiguous CUDA/HIP torch tensor of the given dtype
     (dtype_name may list alternatives separated by '|')."""
+    want = _DTYPES.get(dtype_name)
+    if want is None:
+        import torch
+
+        want = _DTYPES[dtype_name] = tuple(getattr(torch, d) for d in dtype_name.split("|"))
     if not t.is_cuda:
         raise ValueError(f"{what} must be a device tensor")
-    if str(t.dtype) not in [f"torch.{d}" for d in dtype_name.split("|")]:
+    if t.dtype not in want:
         raise ValueError(f"{what} must be {dtype_name}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
@@ -145,9 +153,15 @@ def _dev_ptr(t, dtype_name: str, what: str) -> int:
 
 
 def _stream_handle(stream) -> int | None:
+    """The HIP stream to enqueue on: torch's current stream of the current
+    device when stream is None (its raw handle, without building a Stream
+    object: that costs about 2.5 us per call), else the given stream."""
     if stream is None:
         import torch
 
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return raw(torch.cuda.current_device())
         return torch.cuda.current_stream().cuda_stream
     return getattr(stream, "cuda_stream", stream)
 
