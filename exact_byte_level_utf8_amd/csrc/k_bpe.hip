@@ -323,7 +323,9 @@ __device__ inline uint32_t touch_lines(const void* table, uint64_t bytes, uint32
   return x;
 }
 
-template <int NT>
+// LIT: added-token literals folded in (B.lit); a separate instantiation keeps
+// their checks out of every other call.
+template <int NT, bool LIT>
 __global__ void __launch_bounds__(NT, 8)
 piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, const uint64_t* __restrict__ doc_off,
              uint32_t n_docs, uint64_t* __restrict__ out_off) {
@@ -409,7 +411,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
   for (int k = tid; k < kFlagLds; k += NT) {
     const uint64_t c = c0 + k;
     uint32_t f = c < n_chunks ? B.flags[c] : 0u, ls = 0;
-    if (B.lit.mark && c < n_chunks) {  // a taken literal is one piece: no start inside it
+    if (LIT && c < n_chunks) {  // a taken literal is one piece: no start inside it
       const uint4 mk = reinterpret_cast<const uint4*>(B.lit.mark)[c];  // the chunk's 16 marks
       const uint32_t w[4] = {mk.x, mk.y, mk.z, mk.w};
       uint32_t inside = 0;
@@ -422,7 +424,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
       f &= ~inside;
     }
     s_flags[k] = (uint16_t)f;
-    s_litst[k] = (uint16_t)ls;
+    if (LIT) s_litst[k] = (uint16_t)ls;
   }
   // the merge and byte-pair tables into this XCD's L2 while phase 1 runs
   const uint32_t warm = touch_lines<NT>(T.merge_slots, (uint64_t)T.merge_buckets * kBucket * 8, 2) ^
@@ -466,7 +468,7 @@ piece_kernel(const uint8_t* __restrict__ text, uint64_t n, Tables T, Bufs B, con
       const uint32_t len = (uint32_t)min(e - s0, (uint64_t)0xFFFF);
       const uint32_t off = (uint32_t)(s0 - base);
       const uint32_t item = off | (len << 16);
-      if ((s_litst[lc] >> bit) & 1u) {  // a taken literal: its ID
+      if (LIT && ((s_litst[lc] >> bit) & 1u)) {  // a taken literal: its ID
         s_tok[off] = (uint32_t)B.lit.id_at[s0];
         s_cnt8[off] = 1;
         ++hits;
@@ -728,10 +730,14 @@ void launch_pieces(const uint8_t* text, uint64_t n, Tables t, Bufs b, const uint
   // up to one tile per workgroup slot of the device (four 512-thread
   // workgroups per CU) every tile starts at once with 8 waves; larger inputs
   // use 4-wave workgroups, so twice as many tiles are in flight per CU
-  if (blocks <= kPieceSmallGrid)
-    launch_on(piece_kernel<512>, dim3(blocks), dim3(512), s, e0, e1, text, n, t, b, doc_off, n_docs, out_off);
-  else
-    launch_on(piece_kernel<256>, dim3(blocks), dim3(256), s, e0, e1, text, n, t, b, doc_off, n_docs, out_off);
+  const bool lit = b.lit.mark != nullptr;
+  if (blocks <= kPieceSmallGrid) {
+    auto k = lit ? piece_kernel<512, true> : piece_kernel<512, false>;
+    launch_on(k, dim3(blocks), dim3(512), s, e0, e1, text, n, t, b, doc_off, n_docs, out_off);
+  } else {
+    auto k = lit ? piece_kernel<256, true> : piece_kernel<256, false>;
+    launch_on(k, dim3(blocks), dim3(256), s, e0, e1, text, n, t, b, doc_off, n_docs, out_off);
+  }
 }
 
 }  // namespace tok
