@@ -261,7 +261,7 @@ struct tok_ctx {
       ok = fill(lb.cand, lit_cap * 8) && fill(lb.tile_cnt, lit_cap / kLitTile * 4) && fill(lb.sel, lit_cap * 8) &&
            fill(lb.cut, (parts + 2) * 8) && fill(lb.part_lit, (parts + 2) * 4) &&
            fill(lb.doc_part, (lit_docs + 2) * 4) && fill(lb.out_off, (parts + 2) * 8) &&
-           fill(lb.fin, (parts + 2) * 4) && fill(lb.misc, 16) && fill(lb.ids, (lit_cap + 64) * 4) &&
+           fill(lb.fin, (parts + 2) * 4) && fill(lb.misc, 32) && fill(lb.ids, (lit_cap + 64) * 4) &&
            fill(lb.spans, (lit_cap + 64) * 4) && fill(lb.lmark, lit_cap + 64) && fill(lb.lid_at, lit_cap * 4);
     }
     if (ok && d_doc) ok = fill(d_doc, doc_cap * 8) && fill(d_outoff, doc_cap * 8);
@@ -331,7 +331,7 @@ struct tok_ctx {
         hipMalloc((void**)&lb.doc_part, (docs + 2) * 4) != hipSuccess ||
         hipMalloc((void**)&lb.out_off, (parts + 2) * 8) != hipSuccess ||
         hipMalloc((void**)&lb.fin, (parts + 2) * 4) != hipSuccess ||
-        hipMalloc((void**)&lb.misc, 16) != hipSuccess ||
+        hipMalloc((void**)&lb.misc, 32) != hipSuccess ||
         hipMalloc((void**)&lb.ids, (cap + 64) * 4) != hipSuccess ||
         hipMalloc((void**)&lb.spans, (cap + 64) * 4) != hipSuccess ||
         hipMalloc((void**)&lb.lmark, cap + 64) != hipSuccess || hipMalloc((void**)&lb.lid_at, cap * 4) != hipSuccess) {

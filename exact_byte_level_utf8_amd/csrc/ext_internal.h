@@ -33,15 +33,17 @@ struct LitBufs {
   uint32_t* doc_part;   // per document boundary: its index among the cut points
   uint64_t* out_off;    // the parts' output offsets from the pipeline
   uint32_t* fin;        // final output offset of each part (and the total)
-  uint32_t* misc;       // [0] tokens the pipeline produced, [1] literals taken k, [2] parts, [3] documents
+  uint32_t* misc;       // [0] tokens the pipeline produced, [1] literals taken k, [2] parts, [3] documents,
+                        // [4] selection workgroups finished (zeroed by the match kernel)
   int32_t* ids;         // the pipeline's output, before the literal IDs go in
   uint32_t* spans;      // with span export: the first byte of each of those IDs
   // Literal IDs folded into the piece pass (calls without span export): a
   // taken literal is then one piece whose token is its ID, and the pipeline's
   // output is the result.  lmark[b]: 1 where a taken literal starts, 2 on
   // its later bytes, else 0 (the match kernel clears its tile's bytes, the
-  // selection writes the marks); lid_at[b]: the ID of the literal that
-  // starts at b (meaningful only where lmark[b] is 1).
+  // pre-tokenization kernel marks the taken literals on its way in);
+  // lid_at[b]: the ID of the literal that starts at b (meaningful only where
+  // lmark[b] is 1).
   uint8_t* lmark;
   int32_t* lid_at;
   uint32_t fold;        // this call folds the literal IDs in

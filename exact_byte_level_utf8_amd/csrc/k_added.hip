@@ -17,12 +17,13 @@
 //                      each, decided exactly from the matches of the 256
 //                      bytes before the tile) and writes the kept ones in
 //                      position order.
-//   lit_select_kernel  one workgroup: the kept matches of all tiles in order
-//                      (a tile whose first cluster began too far back lists
-//                      all its matches, and then the cursor scan runs here
-//                      over the whole list).  The taken literals cut the
-//                      text into 2k + 1 parts: segment, literal, segment,
-//                      ..., segment.
+//   lit_select_kernel  the kept matches of all tiles in order: workgroups
+//                      copy shares of the tiles and place the cut points;
+//                      the last one to finish checks the offsets and, if a
+//                      tile whose first cluster began too far back listed
+//                      all its matches, runs the cursor scan over the whole
+//                      list.  The taken literals cut the text into 2k + 1
+//                      parts: segment, literal, segment, ..., segment.
 // The parts then run through the usual pipeline as documents (their count
 // read on the device, so the host enqueues everything without waiting),
 // which are hard boundaries for code points, pieces and merges, exactly as
@@ -125,6 +126,7 @@ lit_match_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* _
   const uint32_t tile = blockIdx.x, tid = threadIdx.x;
   const uint64_t base = (uint64_t)tile * kLitTile;
   const int64_t w0 = (int64_t)base - (int64_t)kLitBack;  // the window's first byte (before the text for tile 0)
+  if (tile == 0 && tid == 0) lb.misc[4] = 0;  // the selection's count of finished workgroups
   {
     const bool aligned = (reinterpret_cast<uintptr_t>(text) & 3u) == 0;
     for (uint32_t w = tid; w < kWords; w += kMatchThreads) {
@@ -245,26 +247,80 @@ lit_match_kernel(const uint8_t* __restrict__ text, uint64_t n, const uint64_t* _
 }
 
 constexpr uint32_t kSelBatch = 16;  // global loads one selection thread keeps in flight
+constexpr uint32_t kSelWaves = kSelThreads / kWave;
+constexpr uint32_t kCopyTiles = 4;     // tiles whose matches one selection wave loads at once
+constexpr uint32_t kSelDocs = 2048;    // document boundaries a selection workgroup holds in LDS
+constexpr uint32_t kSelTilesPerWg = 32;  // selection workgroups: about one per this many tiles,
+constexpr uint32_t kSelMaxWgs = 64;      // at most this many
 
 __global__ void __launch_bounds__(kSelThreads)
 lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_off, uint32_t n_docs, Literals L,
                   LitBufs lb, Counters* ctr, uint64_t gen) {
-  __shared__ uint32_t s_scan[kSelThreads / kWave];
-  __shared__ uint32_t s_over, s_bad;
-  const uint32_t tid = threadIdx.x;
+  __shared__ uint32_t s_scan[kSelWaves];
+  __shared__ uint32_t s_over, s_bad, s_last;
+  __shared__ uint32_t s_tb[kSelThreads], s_tv[kSelThreads];  // a chunk's tiles: first output index, match count
+  __shared__ uint8_t s_len[kLitMaxCount];                      // the literals' lengths
+  __shared__ uint64_t s_doc[kSelDocs];                         // the document boundaries, where they fit
+  const uint32_t tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const uint32_t G = gridDim.x, g = blockIdx.x;
   if (tid == 0) {
     s_over = 0;
     s_bad = 0;
+    s_last = 0;
   }
+  for (uint32_t i = tid; i < L.n; i += kSelThreads) s_len[i] = (uint8_t)lit_len(L, i);
   // the caller's documents (one document [0, n) without offsets): the
   // pipeline sees only the parts, so their offsets are checked here
   const uint32_t nd = doc_off ? n_docs : 1u;
+  const bool doc_lds = nd < kSelDocs;
   auto D = [&](uint32_t d) -> uint64_t { return doc_off ? doc_off[d] : (d == 0 ? 0ull : n); };
-  bool bad = false;
-  for (uint32_t d = tid; d < nd; d += kSelThreads) bad |= D(d) > D(d + 1);
-  if (tid == 0) bad |= D(0) != 0 || D(nd) != n;
-  // matches before each tile, and each tile's matches copied after them in
-  // the same pass (uniform trip count: the scan holds barriers)
+  if (doc_lds)
+    for (uint32_t d = tid; d <= nd; d += kSelThreads) s_doc[d] = D(d);
+  __syncthreads();
+  auto Dc = [&](uint32_t d) -> uint64_t { return doc_lds ? s_doc[d] : D(d); };
+  // cut points: the document boundaries merged with each literal's start and
+  // end.  A boundary comes before a literal starting on it and after a
+  // literal ending on it; literals never straddle a boundary.
+  //   index of start j = 2j + #{d : D(d) <= S_j}
+  //   index of end j   = 2j + 1 + #{d : D(d) < E_j}
+  //   index of D(d)    = d + 2 #{j : S_j < D(d)}
+  // With one boundary pair, 0 and n, literal j's start and end are cut
+  // points 2j + 1 and 2j + 2.
+  auto place = [&](uint32_t j, uint64_t a) {
+    const uint32_t li = (uint32_t)a & kSelIndex;
+    const uint64_t S = a >> 32, E = S + s_len[li];
+    if (nd == 1) {
+      lb.cut[2 * j + 1] = S;
+      lb.cut[2 * j + 2] = E;
+      if (!lb.fold) {
+        lb.part_lit[2 * j] = -1;  // the stretch before the literal
+        lb.part_lit[2 * j + 1] = L.ids[li];
+      }
+      return;
+    }
+    uint32_t lo = 0, hi = nd + 1;  // #{d : D(d) <= S}
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (Dc(mid) <= S) lo = mid + 1;
+      else hi = mid;
+    }
+    const uint32_t is = 2 * j + lo;
+    lo = 0;
+    hi = nd + 1;  // #{d : D(d) < E}
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (Dc(mid) < E) lo = mid + 1;
+      else hi = mid;
+    }
+    lb.cut[is] = S;
+    lb.cut[2 * j + 1 + lo] = E;
+  };
+  // Matches before each tile (a scan of the tile counts, a chunk of tiles at
+  // a time; uniform trip count: the scan holds barriers).  Every workgroup
+  // scans all counts and copies its share of each chunk's tiles into the
+  // list, placing each match's cut points as it goes: a wave per tile, its
+  // lanes on consecutive matches so that loads and stores coalesce,
+  // kCopyTiles tiles in flight.
   uint32_t carry = 0;
   bool raw = false;  // a tile listed all its matches, unresolved
   for (uint32_t t0 = 0; t0 < tiles; t0 += kSelThreads) {
@@ -272,21 +328,60 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
     const uint32_t w = t < tiles ? lb.tile_cnt[t] : 0u, v = w & ~kTileRaw;
     raw |= (w & kTileRaw) != 0;
     uint32_t tot = 0;
-    const uint32_t b = carry + wg_excl_scan<kSelThreads>(v, 0u, AddOp(), s_scan, &tot);
-    const uint64_t* src = lb.cand + (uint64_t)t * kLitTile;
-    for (uint32_t j = 0; j < v; j += kSelBatch) {  // kSelBatch loads in flight before the stores
-      uint64_t x[kSelBatch];
+    s_tb[tid] = carry + wg_excl_scan<kSelThreads>(v, 0u, AddOp(), s_scan, &tot);
+    s_tv[tid] = v;
+    __syncthreads();
+    const uint32_t nt = min(tiles - t0, kSelThreads);
+    const uint32_t qa = (uint32_t)((uint64_t)nt * g / G), qb = (uint32_t)((uint64_t)nt * (g + 1) / G);
+    for (uint32_t q0 = qa + wave; q0 < qb; q0 += kCopyTiles * kSelWaves) {
+      uint32_t vmax = 0;  // the most matches of the wave's tiles (the same on every lane)
 #pragma unroll
-      for (uint32_t u = 0; u < kSelBatch; ++u) x[u] = j + u < v ? src[j + u] : 0ull;
+      for (uint32_t u = 0; u < kCopyTiles; ++u) {
+        const uint32_t q = q0 + u * kSelWaves;
+        vmax = max(vmax, q < qb ? s_tv[q] : 0u);
+      }
+      for (uint32_t e0 = 0; e0 < vmax; e0 += kWave) {
+        const uint32_t e = e0 + lane;
+        uint64_t x[kCopyTiles];
 #pragma unroll
-      for (uint32_t u = 0; u < kSelBatch; ++u)
-        if (j + u < v) lb.sel[b + j + u] = x[u];
+        for (uint32_t u = 0; u < kCopyTiles; ++u) {
+          const uint32_t q = q0 + u * kSelWaves;
+          x[u] = q < qb && e < s_tv[q] ? lb.cand[(uint64_t)(t0 + q) * kLitTile + e] : 0ull;
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < kCopyTiles; ++u) {
+          const uint32_t q = q0 + u * kSelWaves;
+          if (q < qb && e < s_tv[q]) {
+            const uint32_t j = s_tb[q] + e;
+            lb.sel[j] = x[u];
+            place(j, x[u]);
+          }
+        }
+      }
     }
     carry += tot;
+    __syncthreads();  // the next chunk rewrites s_tb and s_tv
   }
   if (raw) s_over = 1u;  // (a possible overlap: checked below)
-  if (bad) s_bad = 1u;
   const uint32_t K = carry;
+  // The last workgroup to finish its share completes the selection (the
+  // match kernel zeroed the count word); the others are done.
+  if (G > 1) {
+    __syncthreads();
+    if (tid == 0) {
+      __threadfence();  // this workgroup's list entries and cut points, before its count
+      if (atomicAdd(&lb.misc[4], 1u) == G - 1) {
+        __threadfence();  // every other workgroup's writes, before the reads below
+        s_last = 1u;
+      }
+    }
+    __syncthreads();
+    if (!s_last) return;
+  }
+  bool bad = false;
+  for (uint32_t d = tid; d < nd; d += kSelThreads) bad |= Dc(d) > Dc(d + 1);
+  if (tid == 0) bad |= Dc(0) != 0 || Dc(nd) != n;
+  if (bad) s_bad = 1u;
   __syncthreads();
   // Tiles resolve their own clusters (lit_match_kernel), so the list holds
   // only taken matches, which never overlap, unless a tile was left
@@ -298,7 +393,7 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
     bool over = false;
     for (uint32_t i = tid; i + 1 < K; i += kSelThreads) {
       const uint64_t a = lb.sel[i], b = lb.sel[i + 1];
-      over |= (a >> 32) + lit_len(L, (uint32_t)a) > (b >> 32);
+      over |= (a >> 32) + s_len[(uint32_t)a & kSelIndex] > (b >> 32);
     }
     if (over) s_over = 1u;
     __syncthreads();
@@ -307,7 +402,8 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
   // (the call fails; everything below stays in bounds)
   const bool bad_docs = s_bad != 0;
   uint32_t k = bad_docs ? 0u : K;
-  if (!bad_docs && s_over) {  // uniform: LDS words read after a barrier
+  const bool resolve = !bad_docs && s_over;  // uniform: LDS words read after a barrier
+  if (resolve) {
     // The cursor keeps a match iff it starts at or after the end of the last
     // match kept.  Where no earlier match reaches the next one's start (the
     // running maximum of the ends, a scan), the last kept match has ended
@@ -320,7 +416,7 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
     for (uint32_t c0 = 0; c0 < K; c0 += kSelThreads) {  // uniform trip count: the scan holds barriers
       const uint32_t i = c0 + tid;
       const uint64_t a = i < K ? lb.sel[i] : 0ull;
-      const uint32_t S = (uint32_t)(a >> 32), E = S + lit_len(L, (uint32_t)a & kSelIndex);
+      const uint32_t S = (uint32_t)(a >> 32), E = S + s_len[(uint32_t)a & kSelIndex];
       uint32_t tot = 0;
       const uint32_t before = max(reach, wg_excl_scan<kSelThreads>(i < K ? E : 0u, 0u, MaxOp(), s_scan, &tot));
       if (i < K && (i == 0 || before <= S)) lb.sel[i] = a | kSelHead;
@@ -335,7 +431,7 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
         const uint32_t S = (uint32_t)(a >> 32);
         if (S >= end) {
           lb.sel[j] = a | kSelKeep;
-          end = S + lit_len(L, (uint32_t)a & kSelIndex);
+          end = S + s_len[(uint32_t)a & kSelIndex];
         }
         ++j;
       } while (j < K && !(lb.sel[j] & kSelHead));
@@ -356,55 +452,77 @@ lit_select_kernel(uint64_t n, uint32_t tiles, const uint64_t* __restrict__ doc_o
     __syncthreads();
     k = kept;
   }
-  // cut points: the document boundaries merged with each literal's start and
-  // end.  A boundary comes before a literal starting on it and after a
-  // literal ending on it; literals never straddle a boundary.
-  //   index of start j = 2j + #{d : D(d) <= S_j}
-  //   index of end j   = 2j + 1 + #{d : D(d) < E_j}
-  //   index of D(d)    = d + 2 #{j : S_j < D(d)}
   const uint32_t nb = bad_docs ? 1u : nd;  // boundaries 0..nb
-  auto Db = [&](uint32_t d) -> uint64_t { return bad_docs ? (d == 0 ? 0ull : n) : D(d); };
+  auto Db = [&](uint32_t d) -> uint64_t { return bad_docs ? (d == 0 ? 0ull : n) : Dc(d); };
   const uint32_t parts = nb + 2 * k;
-  // the parts' literal IDs, for the insertion (unused when the IDs are folded
-  // into the piece pass)
-  if (!lb.fold)
-    for (uint32_t i = tid; i < parts; i += kSelThreads) lb.part_lit[i] = -1;
-  __syncthreads();
-  for (uint32_t j0 = tid; j0 < k; j0 += kSelBatch * kSelThreads) {
-    uint64_t aa[kSelBatch];  // kSelBatch literals per pass, their loads in flight together
-    uint32_t len[kSelBatch];
-    int32_t id[kSelBatch];
+  // The cut points and literal IDs placed with the copy stand, unless the
+  // list was resolved here, the offsets were malformed (one part, no
+  // literal), or literal IDs go to parts among several documents: those are
+  // placed here, after every part is marked as no literal.  (The parts'
+  // literal IDs serve the insertion; they are unused when the IDs are folded
+  // into the piece pass.)
+  if (!lb.fold && !(bad_docs || resolve || nb > 1) && tid == 0)
+    lb.part_lit[2 * k] = -1;  // the stretch after the last literal
+  if (bad_docs || resolve || (!lb.fold && nb > 1)) {  // uniform
+    if (!lb.fold)
+      for (uint32_t i = tid; i < parts; i += kSelThreads) lb.part_lit[i] = -1;
+    __syncthreads();
+    if (nb == 1) {
+      // one boundary pair, 0 and n (one document, or the fallback): literal j's
+      // start and end are cut points 2j + 1 and 2j + 2
+      for (uint32_t j0 = tid; j0 < k; j0 += kSelBatch * kSelThreads) {
+        uint64_t aa[kSelBatch];
 #pragma unroll
-    for (uint32_t u = 0; u < kSelBatch; ++u) aa[u] = j0 + u * kSelThreads < k ? lb.sel[j0 + u * kSelThreads] : 0ull;
+        for (uint32_t u = 0; u < kSelBatch; ++u) aa[u] = j0 + u * kSelThreads < k ? lb.sel[j0 + u * kSelThreads] : 0ull;
 #pragma unroll
-    for (uint32_t u = 0; u < kSelBatch; ++u) {
-      const bool in = j0 + u * kSelThreads < k;
-      len[u] = in ? lit_len(L, (uint32_t)aa[u]) : 0u;
-      id[u] = in && !lb.fold ? L.ids[(uint32_t)aa[u]] : -1;
-    }
-#pragma unroll
-    for (uint32_t u = 0; u < kSelBatch; ++u) {
-      const uint32_t j = j0 + u * kSelThreads;
-      if (j >= k) break;
-      const uint64_t S = aa[u] >> 32, E = S + len[u];
-      uint32_t lo = 0, hi = nb + 1;  // #{d : D(d) <= S}
-      while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (Db(mid) <= S) lo = mid + 1;
-        else hi = mid;
+        for (uint32_t u = 0; u < kSelBatch; ++u) {
+          const uint32_t j = j0 + u * kSelThreads, li = (uint32_t)aa[u] & kSelIndex;
+          if (j < k) {
+            const uint64_t S = aa[u] >> 32;
+            lb.cut[2 * j + 1] = S;
+            lb.cut[2 * j + 2] = S + s_len[li];
+            if (!lb.fold) lb.part_lit[2 * j + 1] = L.ids[li];
+          }
+        }
       }
-      const uint32_t is = 2 * j + lo;
-      lo = 0;
-      hi = nb + 1;  // #{d : D(d) < E}
-      while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (Db(mid) < E) lo = mid + 1;
-        else hi = mid;
+    } else {
+      for (uint32_t j0 = tid; j0 < k; j0 += kSelBatch * kSelThreads) {
+        uint64_t aa[kSelBatch];  // kSelBatch literals per pass, their loads in flight together
+        uint32_t len[kSelBatch];
+        int32_t id[kSelBatch];
+#pragma unroll
+        for (uint32_t u = 0; u < kSelBatch; ++u) aa[u] = j0 + u * kSelThreads < k ? lb.sel[j0 + u * kSelThreads] : 0ull;
+#pragma unroll
+        for (uint32_t u = 0; u < kSelBatch; ++u) {
+          const bool in = j0 + u * kSelThreads < k;
+          len[u] = in ? s_len[(uint32_t)aa[u] & kSelIndex] : 0u;
+          id[u] = in && !lb.fold ? L.ids[(uint32_t)aa[u]] : -1;
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < kSelBatch; ++u) {
+          const uint32_t j = j0 + u * kSelThreads;
+          if (j >= k) break;
+          const uint64_t S = aa[u] >> 32, E = S + len[u];
+          uint32_t lo = 0, hi = nb + 1;  // #{d : D(d) <= S}
+          while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (Db(mid) <= S) lo = mid + 1;
+            else hi = mid;
+          }
+          const uint32_t is = 2 * j + lo;
+          lo = 0;
+          hi = nb + 1;  // #{d : D(d) < E}
+          while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (Db(mid) < E) lo = mid + 1;
+            else hi = mid;
+          }
+          const uint32_t ie = 2 * j + 1 + lo;
+          lb.cut[is] = S;
+          lb.cut[ie] = E;
+          if (!lb.fold) lb.part_lit[is] = id[u];  // the literal's ID (IDs are never negative)
+        }
       }
-      const uint32_t ie = 2 * j + 1 + lo;
-      lb.cut[is] = S;
-      lb.cut[ie] = E;
-      if (!lb.fold) lb.part_lit[is] = id[u];  // the literal's ID (IDs are never negative)
     }
   }
   for (uint32_t d = tid; d <= nb; d += kSelThreads) {
@@ -535,7 +653,8 @@ void launch_literal_pass(const uint8_t* text, uint64_t n, const uint64_t* doc_of
                          LitBufs lb, Counters* ctr, uint64_t gen, hipStream_t s) {
   const uint32_t tiles = (uint32_t)((n + kLitTile - 1) / kLitTile);
   lit_match_kernel<<<tiles, kMatchThreads, 0, s>>>(text, n, doc_off, n_docs, L, lb);
-  lit_select_kernel<<<1, kSelThreads, 0, s>>>(n, tiles, doc_off, n_docs, L, lb, ctr, gen);
+  const uint32_t wgs = std::max(1u, std::min(tiles / kSelTilesPerWg, kSelMaxWgs));
+  lit_select_kernel<<<wgs, kSelThreads, 0, s>>>(n, tiles, doc_off, n_docs, L, lb, ctr, gen);
 }
 
 void launch_literal_insert(uint64_t n, Literals L, LitBufs lb, int32_t* out, uint32_t* spans, uint64_t cap,

@@ -114,7 +114,10 @@ def test_overlapping_literals(cfg):
             for k in range(3):
                 b = "".join(rng.choice(alpha) for _ in range(20_000)).encode()
                 check(t, o, b, lits, f"{strings} #{k}")
-            check(t, o, (strings[0] * 30_000).encode(), lits, f"{strings} run")
+            # one cluster over 200K bytes and more: every tile after the first lists all
+            # its matches and the cursor scan runs over the whole list, on a selection
+            # grid of several workgroups
+            check(t, o, (strings[0] * 100_000).encode(), lits, f"{strings} run")
         finally:
             t.set_added_tokens([])
 
@@ -397,6 +400,53 @@ def test_repair_with_literals(cfg, name):
         n, dinfo = t.repair_dev(d, len(sess), new, len(old))
         assert dinfo["full"] == 1
         same("clash dev", d[:n].cpu().numpy(), o.encode_added(new, clash))
+    finally:
+        t.set_added_tokens([])
+
+
+def test_many_documents_with_literals(cfg):
+    """More document boundaries than a selection workgroup holds in LDS (3,000
+    short documents, about 120 KB: a selection grid of several workgroups):
+    IDs, output offsets and spans as the oracle's per-document encode; then
+    malformed offsets on the same text are rejected, and the next call is
+    right again."""
+    t, o, v = cfg["gpt2"]
+    lits = lits_from(["<|a|>", "==", "===", "ab", "  "], v)
+    tokb = vocab.token_bytes(vocab.merges(libs.CONFIGS["gpt2"][0]))
+    alpha = ["<|a|>", "=", "==", "a", "b", " ", "  ", "\n", "x", "1", "é"]
+    rng = random.Random(2048)
+    docs = ["".join(rng.choice(alpha) for _ in range(rng.choice([0, 1, 3, 20, 40, 60]))) for _ in range(3000)]
+    data, off = textgen.pack_docs(docs)
+    assert len(data) >= 64 * 1024
+    want_ids, want_sp, want_off = batch_expect(o, docs, lits, v, tokb)
+    t.set_added_tokens(lits)
+    try:
+        ids, out_off = t.encode_batch(data, off)
+        same("out_off", out_off, want_off)
+        same("ids", ids, want_ids)
+        d = torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda()
+        d_off = torch.tensor(off.astype(np.int64), device="cuda").view(torch.uint64)
+        d_out = torch.zeros(len(off), dtype=torch.int64, device="cuda").view(torch.uint64)
+        d_ids = torch.full((len(data),), -7, dtype=torch.int32, device="cuda")
+        d_sp = torch.full((len(data),), -7, dtype=torch.int32, device="cuda")
+        n = t.encode_spans_dev(d, d_ids, d_sp, d_off, d_out)
+        torch.cuda.synchronize()
+        same("spans ids", d_ids[:n].cpu().numpy(), want_ids)
+        same("spans", d_sp[:n].cpu().numpy().view(np.uint32).astype(np.uint64), want_sp)
+        same("spans out_off", d_out.view(torch.int64).cpu().numpy().astype(np.uint64), want_off)
+        bad = off.astype(np.int64).copy()
+        bad[1500], bad[1501] = bad[1501] + 1, bad[1500]
+        assert bad[1500] > bad[1501]
+        d_bad = torch.tensor(bad, device="cuda").view(torch.uint64)
+        with pytest.raises(tk.TokError) as e:
+            t.encode_batch_dev(d, d_bad, d_ids, d_out)
+        assert e.value.code == tk.TOK_E_ARG
+        d_out.zero_()
+        d_ids.fill_(-7)
+        n = t.encode_batch_dev(d, d_off, d_ids, d_out)
+        torch.cuda.synchronize()
+        same("ids after the rejected call", d_ids[:n].cpu().numpy(), want_ids)
+        same("out_off after the rejected call", d_out.view(torch.int64).cpu().numpy().astype(np.uint64), want_off)
     finally:
         t.set_added_tokens([])
 
