@@ -227,7 +227,9 @@ def profiled(workload: str, stage: str, field: str):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    k = rec.get("kernels", {}).get(STAGE_KERNELS[stage][0])
+    # the stage's record (its kernel is pretok_kernel or pretok_case_kernel by
+    # pattern family)
+    k = next((v for v in rec.get("kernels", {}).values() if v.get("stage") == stage), None)
     if not k or k.get("source_sha256") != source_digest(stage) or field not in k:
         return None
     return int(k[field])
