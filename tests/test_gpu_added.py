@@ -404,6 +404,27 @@ def test_repair_with_literals(cfg, name):
         t.set_added_tokens([])
 
 
+@pytest.mark.parametrize("count,lo,hi", [(700, 2, 9), (120, 40, 64), (500, 2, 9)])
+def test_large_literal_sets(cfg, count, lo, hi):
+    """Large literal sets: 700 short literals, 120 of 40-64 bytes (over 6 KiB
+    of literal bytes), 500 short ones, with many sharing their first two
+    bytes, on text made of them and of their bytes."""
+    t, o, v = cfg["gpt2"]
+    rng = random.Random(count * 100 + hi)
+    alpha = "abcd =\n"
+    strings = set()
+    while len(strings) < count:
+        strings.add("".join(rng.choice(alpha) for _ in range(rng.randint(lo, hi))))
+    strings = sorted(strings)
+    lits = lits_from(strings, v)
+    t.set_added_tokens(lits)
+    try:
+        pieces = [rng.choice(strings) if rng.random() < 0.3 else rng.choice(alpha) for _ in range(40_000)]
+        check(t, o, "".join(pieces).encode(), lits, f"{count} literals of {lo}-{hi} bytes")
+    finally:
+        t.set_added_tokens([])
+
+
 def test_many_documents_with_literals(cfg):
     """More document boundaries than a selection workgroup holds in LDS (3,000
     short documents, about 120 KB: a selection grid of several workgroups):
